@@ -1,0 +1,238 @@
+"""TEST INFRASTRUCTURE ONLY: the fp64 CPU oracle for the Gated DeltaNet-2 core.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package. The GPU library never imports, links or calls it, and it
+shares no code with the GPU library: the only thing both sides consume is the
+seeded input generator, which holds none of the method's arithmetic.
+
+Two independent evaluations of the method live here:
+
+* ``recurrent`` -- the per-token recurrence of the burn-gdn2 0.1.5 docs page
+  (section "Architecture"), written out in plain C (``gdn2_oracle.c``), fp64, one
+  (sequence, value head) pair at a time. ``decode_step`` is one token of it.
+* ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
+  mode) and on the FG^2-GDN summary (section 2C, DPLR structure and the WY
+  representation), in numpy fp64. It exists to pin the recurrence: the two are
+  different algorithms and agree only if both are right.
+
+Conventions (taken where the pages are silent; each listed in the design doc):
+
+* packed token layout: ``q, k`` are ``[T_total, H_k, d_k]``, ``v, w`` are
+  ``[T_total, H_v, d_v]``, ``log_alpha, b`` are ``[T_total, H_v, d_k]``;
+  sequence ``n`` owns tokens ``cu_seqlens[n] .. cu_seqlens[n+1]-1``;
+* value head ``h`` reads key head ``h // (H_v // H_k)`` (contiguous groups);
+* ``log_alpha`` carries ``log(alpha) <= 0``; the output reads the state after the
+  update of its own token; there is no query scale;
+* ``S0 is None`` means a zero initial state.
+
+Parity of these functions is pinned by ``tests/test_oracle_pins.py`` (closed forms,
+invariants, the formulas of the other pages, brute force, chunked-vs-recurrent).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn2_oracle.c")
+_LIB_DIR = os.path.join(_HERE, "_build")
+_LIB = os.path.join(_LIB_DIR, "libgdn2_oracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the C oracle with gcc (-O2, no fast-math). Returns the library path."""
+    os.makedirs(_LIB_DIR, exist_ok=True)
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+           "-shared", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.gdn2_oracle_sequence.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.gdn2_oracle_sequence.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def sequence(q, k, v, w, log_alpha, b, S0):
+    """One (sequence, value head) pair: q,k,log_alpha,b [T,d_k]; v,w [T,d_v]; S0 [d_k,d_v].
+
+    Returns (o [T,d_v], S_T [d_k,d_v]) in fp64.
+    """
+    lib = _load()
+    q, k, v, w, la, b = (_f64(x) for x in (q, k, v, w, log_alpha, b))
+    T, d_k = k.shape
+    d_v = v.shape[1]
+    S = _f64(S0).copy()
+    o = np.zeros((T, d_v), dtype=np.float64)
+    rc = lib.gdn2_oracle_sequence(T, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(w),
+                                  _ptr(la), _ptr(b), _ptr(S), _ptr(o))
+    if rc != 0:
+        raise MemoryError("gdn2_oracle_sequence failed")
+    return o, S
+
+
+def recurrent(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, pairs=None, threads=None):
+    """Token-by-token recurrence over packed sequences.
+
+    q, k: [T_total, H_k, d_k]; v, w: [T_total, H_v, d_v]; log_alpha, b: [T_total, H_v, d_k];
+    S0: [N, H_v, d_k, d_v] or None (zeros); cu_seqlens: [N+1] offsets, or None for one
+    sequence of T_total tokens. ``pairs`` restricts the work to a list of (n, h); entries of
+    other pairs are left NaN. Returns (o [T_total, H_v, d_v], S_T [N, H_v, d_k, d_v]) fp64.
+    """
+    q, k, v, w, la, b = (np.asarray(x) for x in (q, k, v, w, log_alpha, b))
+    T_total, H_k, d_k = k.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    if H_v % H_k:
+        raise ValueError("H_v must be a multiple of H_k")
+    G = H_v // H_k
+    cu = np.array([0, T_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    if pairs is None:
+        pairs = [(n, h) for n in range(N) for h in range(H_v)]
+    o = np.full((T_total, H_v, d_v), np.nan)
+    S_T = np.full((N, H_v, d_k, d_v), np.nan)
+
+    def run(pair):
+        n, h = pair
+        s, e = int(cu[n]), int(cu[n + 1])
+        hk = h // G
+        S_init = np.zeros((d_k, d_v)) if S0 is None else np.asarray(S0)[n, h]
+        on, Sn = sequence(q[s:e, hk], k[s:e, hk], v[s:e, h], w[s:e, h], la[s:e, h], b[s:e, h],
+                          S_init)
+        o[s:e, h] = on
+        S_T[n, h] = Sn
+
+    nthr = threads or default_threads()
+    if nthr <= 1 or len(pairs) <= 1:
+        for p in pairs:
+            run(p)
+    else:
+        with ThreadPoolExecutor(max_workers=nthr) as ex:
+            list(ex.map(run, pairs))
+    return o, S_T
+
+
+def decode_step(q, k, v, log_alpha, b, w, S, pairs=None, threads=None):
+    """One token per sequence: q,k [N,H_k,d_k]; v,w [N,H_v,d_v]; log_alpha,b [N,H_v,d_k];
+    S [N,H_v,d_k,d_v]. Returns (o [N,H_v,d_v], S_new)."""
+    N = np.asarray(k).shape[0]
+    cu = np.arange(N + 1)
+    return recurrent(q, k, v, log_alpha, b, w, S0=S, cu_seqlens=cu, pairs=pairs,
+                     threads=threads)
+
+
+def _unit_lower_inverse(L: np.ndarray) -> np.ndarray:
+    """Inverse of a unit lower-triangular matrix by forward substitution on the identity."""
+    n = L.shape[0]
+    Tm = np.zeros_like(L)
+    for r in range(n):
+        row = np.zeros(n)
+        row[r] = 1.0
+        for i in range(r):
+            row -= L[r, i] * Tm[i]
+        Tm[r] = row
+    return Tm
+
+
+def chunked_sequence(q, k, v, w, log_alpha, b, S0, chunk_size):
+    """Chunked WY form of the recurrence for one (sequence, value head) pair, fp64.
+
+    Within a chunk of L tokens entering with state S (all vectors per token are rows):
+      g_r        = sum_{i<=r} log alpha_i                    (cumulative log decay, per key channel)
+      A[r,i]     = sum_c b_r[c] k_r[c] k_i[c] exp(g_r[c]-g_i[c]),  i < r   (0 elsewhere)
+      T          = (I + A)^{-1}
+      W~         = T (exp(g) . b . k),   U~ = T (w . v)       (the WY factors)
+      U          = U~ - W~ S                                  (the per-token erase-corrected writes)
+      Mqk[r,i]   = sum_c q_r[c] k_i[c] exp(g_r[c]-g_i[c]),     i <= r
+      O          = (exp(g) . q) S + Mqk U
+      S_next     = diag(exp(g_L)) S + (exp(g_L - g) . k)^T U
+    Returns (o [T,d_v], S_T).
+    """
+    q, k, v, w, la, b = (_f64(x) for x in (q, k, v, w, log_alpha, b))
+    T = k.shape[0]
+    S = _f64(S0).copy()
+    o = np.zeros((T, v.shape[1]))
+    for c0 in range(0, T, chunk_size):
+        sl = slice(c0, min(T, c0 + chunk_size))
+        qc, kc, vc, wc, lac, bc = q[sl], k[sl], v[sl], w[sl], la[sl], b[sl]
+        L = kc.shape[0]
+        g = np.cumsum(lac, axis=0)
+        A = np.zeros((L, L))
+        Mqk = np.zeros((L, L))
+        for r in range(L):
+            for i in range(r + 1):
+                dec = np.exp(g[r] - g[i])
+                Mqk[r, i] = np.sum(qc[r] * kc[i] * dec)
+                if i < r:
+                    A[r, i] = np.sum(bc[r] * kc[r] * kc[i] * dec)
+        Tm = _unit_lower_inverse(np.eye(L) + A)
+        W_t = Tm @ (np.exp(g) * bc * kc)
+        U_t = Tm @ (wc * vc)
+        U = U_t - W_t @ S
+        o[sl] = (np.exp(g) * qc) @ S + Mqk @ U
+        S = np.exp(g[-1])[:, None] * S + (np.exp(g[-1][None, :] - g) * kc).T @ U
+    return o, S
+
+
+def chunked(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size=64):
+    """Chunked WY form over packed sequences; same layout and result as ``recurrent``."""
+    q, k, v, w, la, b = (np.asarray(x) for x in (q, k, v, w, log_alpha, b))
+    T_total, H_k, d_k = k.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    G = H_v // H_k
+    cu = np.array([0, T_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    o = np.zeros((T_total, H_v, d_v))
+    S_T = np.zeros((N, H_v, d_k, d_v))
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        for h in range(H_v):
+            hk = h // G
+            S_init = np.zeros((d_k, d_v)) if S0 is None else np.asarray(S0)[n, h]
+            on, Sn = chunked_sequence(q[s:e, hk], k[s:e, hk], v[s:e, h], w[s:e, h],
+                                      la[s:e, h], b[s:e, h], S_init, chunk_size)
+            o[s:e, h] = on
+            S_T[n, h] = Sn
+    return o, S_T
+
+
+def rel_l2(x, ref) -> float:
+    """Relative L2 error ||x - ref|| / ||ref|| (0 when both are zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(x - ref)
+    if den == 0.0:
+        return float(num)
+    return float(num / den)

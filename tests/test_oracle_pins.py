@@ -1,0 +1,302 @@
+"""Pins of the fp64 CPU oracle against facts fixed by the pages and by mathematics.
+
+No page prints a worked numeric example of the recurrence, so each pin below is a
+closed form, an invariant, another page's formula for a special case, brute force on
+the definition, or agreement between the two independent algorithms in ``oracle``
+(token-by-token recurrence in C, chunked WY form in numpy). Every pin uses d_k != d_v
+where the case allows it, so a transposed operand or a swapped axis cannot pass.
+
+Method: burn-gdn2 0.1.5 docs page, section "Architecture":
+    S_t = (I - k_t (b_t . k_t)^T) diag(alpha_t) S_{t-1} + k_t (w_t . v_t)^T,  o_t = q_t^T S_t
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+TOL = 1e-11
+
+
+def rand_case(rng, T, Hk=1, Hv=1, dk=5, dv=3, b_scale=2.0, unit_k=True):
+    q = rng.standard_normal((T, Hk, dk))
+    k = rng.standard_normal((T, Hk, dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, Hv, dv))
+    la = -np.logaddexp(0.0, rng.standard_normal((T, Hv, dk)))
+    b = b_scale / (1.0 + np.exp(-rng.standard_normal((T, Hv, dk))))
+    w = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, Hv, dv))))
+    return q, k, v, la, b, w
+
+
+def close(a, b, tol=TOL):
+    a, b = np.asarray(a), np.asarray(b)
+    scale = max(1.0, float(np.max(np.abs(b))))
+    return float(np.max(np.abs(a - b))) <= tol * scale
+
+
+# ---- P1: brute force on the definition (explicit d_k x d_k transition matrices) ----------
+
+def test_explicit_matrix_definition():
+    rng = np.random.default_rng(1)
+    T, dk, dv = 9, 5, 3
+    q, k, v, la, b, w = rand_case(rng, T, dk=dk, dv=dv)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    S = S0[0, 0].copy()
+    for t in range(T):
+        kt, bt = k[t, 0], b[t, 0]
+        P = np.zeros((dk, dk))
+        for i in range(dk):
+            for j in range(dk):
+                P[i, j] = (1.0 if i == j else 0.0) - kt[i] * bt[j] * kt[j]
+        D = np.diag(np.exp(la[t, 0]))
+        write = np.zeros((dk, dv))
+        for i in range(dk):
+            for j in range(dv):
+                write[i, j] = kt[i] * w[t, 0, j] * v[t, 0, j]
+        S = P @ D @ S + write
+        ot = np.array([sum(q[t, 0, i] * S[i, j] for i in range(dk)) for j in range(dv)])
+        assert close(o[t, 0], ot)
+    assert close(ST[0, 0], S)
+
+
+# ---- P2: chunked WY form (independent algorithm) equals the recurrence -------------------
+
+@pytest.mark.parametrize("C", [1, 2, 3, 8, 16, 64])
+def test_chunked_equals_recurrent(C):
+    rng = np.random.default_rng(100 + C)
+    for T in sorted({1, C - 1 if C > 1 else 1, C, C + 1, 2 * C + 3, 3 * C + 5}):
+        q, k, v, la, b, w = rand_case(rng, T, Hk=2, Hv=4, dk=6, dv=4)
+        S0 = rng.standard_normal((1, 4, 6, 4))
+        o_r, S_r = oracle.recurrent(q, k, v, la, b, w, S0=S0, threads=1)
+        o_c, S_c = oracle.chunked(q, k, v, la, b, w, S0=S0, chunk_size=C)
+        assert close(o_c, o_r, 1e-10), (C, T)
+        assert close(S_c, S_r, 1e-10), (C, T)
+
+
+def test_chunked_equals_recurrent_varlen_with_empty_sequence():
+    rng = np.random.default_rng(7)
+    cu = np.array([0, 5, 5, 21, 40])
+    q, k, v, la, b, w = rand_case(rng, 40, Hk=1, Hv=2, dk=4, dv=6)
+    S0 = rng.standard_normal((4, 2, 4, 6))
+    o_r, S_r = oracle.recurrent(q, k, v, la, b, w, S0=S0, cu_seqlens=cu)
+    o_c, S_c = oracle.chunked(q, k, v, la, b, w, S0=S0, cu_seqlens=cu, chunk_size=8)
+    assert close(o_c, o_r, 1e-10) and close(S_c, S_r, 1e-10)
+    assert close(S_r[1], S0[1], 0.0)          # a zero-length sequence returns its S0
+
+
+# ---- P3: alpha = 1, b = 0 is causal linear attention (O(T^2) brute force) ---------------
+
+def test_linear_attention_closed_form():
+    rng = np.random.default_rng(3)
+    T, dk, dv = 13, 5, 3
+    q, k, v, la, b, w = rand_case(rng, T, dk=dk, dv=dv, unit_k=False)
+    la[:] = 0.0
+    b[:] = 0.0
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    for t in range(T):
+        ref = S0[0, 0].T @ q[t, 0]
+        for i in range(t + 1):
+            ref = ref + np.dot(q[t, 0], k[i, 0]) * (w[i, 0] * v[i, 0])
+        assert close(o[t, 0], ref)
+    S_ref = S0[0, 0] + sum(np.outer(k[i, 0], w[i, 0] * v[i, 0]) for i in range(T))
+    assert close(ST[0, 0], S_ref)
+
+
+# ---- P4: exact delta-rule retrieval ----------------------------------------------------
+
+def test_exact_retrieval():
+    rng = np.random.default_rng(4)
+    T, d = 20, 8
+    q, k, v, la, b, w = rand_case(rng, T, dk=d, dv=d)
+    la[:] = 0.0
+    b[:] = 1.0
+    w[:] = 1.0
+    q = k.copy()                                     # read out along the key just written
+    S0 = rng.standard_normal((1, 1, d, d))
+    o, _ = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    assert np.max(np.abs(o[:, 0] - v[:, 0])) < 1e-13 * 10
+
+
+# ---- P5: the scalar-gate rule of the llama.cpp decode notes (section 2) ----------------
+
+def test_scalar_gate_rule_of_llama_cpp_notes():
+    """Decay s *= exp(g); sk = S^T k; delta d = (v - sk) * beta; s += k d^T; o = S^T q."""
+    rng = np.random.default_rng(5)
+    T, dk, dv = 11, 6, 4
+    q, k, v, _, _, _ = rand_case(rng, T, dk=dk, dv=dv)
+    g = -np.logaddexp(0.0, rng.standard_normal(T))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(T)))
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    la = np.broadcast_to(g[:, None, None], (T, 1, dk)).copy()
+    b = np.broadcast_to(beta[:, None, None], (T, 1, dk)).copy()
+    w = np.broadcast_to(beta[:, None, None], (T, 1, dv)).copy()
+    o, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    s = S0[0, 0].copy()
+    for t in range(T):
+        s = s * np.exp(g[t])
+        sk = s.T @ k[t, 0]
+        d = (v[t, 0] - sk) * beta[t]
+        s = s + np.outer(k[t, 0], d)
+        assert close(o[t, 0], s.T @ q[t, 0])
+    assert close(ST[0, 0], s)
+
+
+# ---- P6: FG^2-GDN symmetric vector beta (gist.science summary, section 2A) -------------
+
+def test_fg2_gdn_mapping():
+    """S = (I - k~ k~^T) Diag(alpha) S + k~ v~^T with k~ = sqrt(beta).k, v~ = sqrt(beta).v
+    equals the GDN-2 rule with k := k~, b := 1, w := 1, v := v~ (d_k = d_v for this variant)."""
+    rng = np.random.default_rng(6)
+    T, d = 10, 5
+    q, k, v, la, _, _ = rand_case(rng, T, dk=d, dv=d)
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, 1, d))))
+    kt, vt = np.sqrt(beta) * k, np.sqrt(beta) * v
+    S0 = rng.standard_normal((1, 1, d, d))
+    o, ST = oracle.recurrent(q, kt, vt, la, np.ones((T, 1, d)), np.ones((T, 1, d)), S0=S0)
+    S = S0[0, 0].copy()
+    for t in range(T):
+        S = (np.eye(d) - np.outer(kt[t, 0], kt[t, 0])) @ np.diag(np.exp(la[t, 0])) @ S \
+            + np.outer(kt[t, 0], vt[t, 0])
+        assert close(o[t, 0], S.T @ q[t, 0])
+    assert close(ST[0, 0], S)
+
+
+# ---- P7: b = 0 is gated linear attention with channel-wise decay (closed form) ---------
+
+def test_gated_linear_attention_closed_form():
+    rng = np.random.default_rng(8)
+    T, dk, dv = 12, 4, 7
+    q, k, v, la, b, w = rand_case(rng, T, dk=dk, dv=dv)
+    b[:] = 0.0
+    alpha = np.exp(la[:, 0])                     # [T, dk]
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    for t in range(T):
+        St = np.prod(alpha[: t + 1], axis=0)[:, None] * S0[0, 0]
+        for i in range(t + 1):
+            decay_after_i = np.prod(alpha[i + 1: t + 1], axis=0)   # alpha_{i+1} ... alpha_t
+            St = St + (decay_after_i * k[i, 0])[:, None] * (w[i, 0] * v[i, 0])[None, :]
+        assert close(o[t, 0], St.T @ q[t, 0])
+    assert close(ST[0, 0], St)
+
+
+# ---- the asymmetric rank-1 erase: k on the left, b.k on the right ----------------------
+
+def test_erase_eigenvalue_along_k():
+    """With alpha = 1 and no write, S0 = k x^T maps to (1 - sum_c b_c k_c^2) k x^T."""
+    rng = np.random.default_rng(9)
+    dk, dv = 6, 3
+    q, k, v, la, b, w = rand_case(rng, 1, dk=dk, dv=dv)
+    la[:] = 0.0
+    w[:] = 0.0
+    x = rng.standard_normal(dv)
+    S0 = np.outer(k[0, 0], x)[None, None]
+    _, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    lam = 1.0 - np.sum(b[0, 0] * k[0, 0] ** 2)
+    assert close(ST[0, 0], lam * S0[0, 0])
+    assert -1.0 < lam < 1.0                      # b in (0,2), |k| = 1: negative eigenvalue allowed
+
+
+def test_erase_fixes_directions_orthogonal_to_gated_key():
+    """E x = x when (b.k)^T x = 0, and q^T E = q^T when q^T k = 0 (E = I - k (b.k)^T)."""
+    rng = np.random.default_rng(10)
+    dk, dv = 6, 3
+    q, k, v, la, b, w = rand_case(rng, 1, dk=dk, dv=dv)
+    la[:] = 0.0
+    w[:] = 0.0
+    bk = b[0, 0] * k[0, 0]
+    x = rng.standard_normal(dk)
+    x -= bk * (x @ bk) / (bk @ bk)
+    S0 = np.outer(x, rng.standard_normal(dv))[None, None]
+    _, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    assert close(ST[0, 0], S0[0, 0])
+    qq = rng.standard_normal(dk)
+    qq -= k[0, 0] * (qq @ k[0, 0])
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    o, _ = oracle.recurrent(qq[None, None], k, v, la, b, w, S0=S0)
+    assert close(o[0, 0], S0[0, 0].T @ qq)
+
+
+# ---- P8: linearity in (w.v, S0); only the product w.v matters --------------------------
+
+def test_linearity_and_write_gate_product():
+    rng = np.random.default_rng(11)
+    T, dk, dv = 15, 5, 4
+    q, k, v1, la, b, w = rand_case(rng, T, dk=dk, dv=dv)
+    v2 = rng.standard_normal(v1.shape)
+    S1, S2 = rng.standard_normal((2, 1, 1, dk, dv))
+    c = -1.7
+    o1, T1 = oracle.recurrent(q, k, v1, la, b, w, S0=S1)
+    o2, T2 = oracle.recurrent(q, k, v2, la, b, w, S0=S2)
+    o3, T3 = oracle.recurrent(q, k, v1 + c * v2, la, b, w, S0=S1 + c * S2)
+    assert close(o3, o1 + c * o2, 1e-10) and close(T3, T1 + c * T2, 1e-10)
+    o4, T4 = oracle.recurrent(q, k, v1 / 3.0, la, b, w * 3.0, S0=S1)
+    assert close(o4, o1, 1e-12) and close(T4, T1, 1e-12)
+
+
+# ---- P9: split / resume, packing, decode steps ------------------------------------------
+
+def test_split_resume_pack_and_decode_steps():
+    rng = np.random.default_rng(12)
+    T, dk, dv = 23, 4, 5
+    q, k, v, la, b, w = rand_case(rng, T, Hk=1, Hv=3, dk=dk, dv=dv)
+    S0 = rng.standard_normal((1, 3, dk, dv))
+    o, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    t = 9
+    oa, Sa = oracle.recurrent(q[:t], k[:t], v[:t], la[:t], b[:t], w[:t], S0=S0)
+    ob, Sb = oracle.recurrent(q[t:], k[t:], v[t:], la[t:], b[t:], w[t:], S0=Sa)
+    assert close(np.concatenate([oa, ob]), o) and close(Sb, ST)
+    # decode: T single steps with the state carried
+    S = S0.copy()
+    for i in range(T):
+        oi, S = oracle.decode_step(q[i:i + 1], k[i:i + 1], v[i:i + 1], la[i:i + 1],
+                                   b[i:i + 1], w[i:i + 1], S)
+        assert close(oi[0], o[i])
+    assert close(S, ST)
+    # packing two sequences equals two separate calls
+    cu = np.array([0, t, T])
+    S0p = np.concatenate([S0, rng.standard_normal((1, 3, dk, dv))])
+    op, Sp = oracle.recurrent(q, k, v, la, b, w, S0=S0p, cu_seqlens=cu)
+    assert close(op[:t], oa) and close(Sp[0], Sa[0])
+    oc, Sc = oracle.recurrent(q[t:], k[t:], v[t:], la[t:], b[t:], w[t:], S0=S0p[1:])
+    assert close(op[t:], oc) and close(Sp[1], Sc[0])
+
+
+def test_gva_value_head_reads_key_head_group():
+    """Value head h uses key head h // (H_v / H_k): contiguous groups."""
+    rng = np.random.default_rng(13)
+    T, dk, dv = 7, 4, 3
+    q, k, v, la, b, w = rand_case(rng, T, Hk=2, Hv=6, dk=dk, dv=dv)
+    o, ST = oracle.recurrent(q, k, v, la, b, w)
+    for h in range(6):
+        hk = h // 3
+        oh, Sh = oracle.recurrent(q[:, hk:hk + 1], k[:, hk:hk + 1], v[:, h:h + 1],
+                                  la[:, h:h + 1], b[:, h:h + 1], w[:, h:h + 1])
+        assert close(o[:, h], oh[:, 0]) and close(ST[0, h], Sh[0, 0])
+
+
+# ---- P10: boundedness over a long run with the negative-eigenvalue gates ----------------
+
+def test_state_stays_bounded():
+    rng = np.random.default_rng(14)
+    T, d = 3000, 8
+    q, k, v, la, b, w = rand_case(rng, T, dk=d, dv=d, b_scale=2.0)
+    o, ST = oracle.recurrent(q, k, v, la, b, w)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(ST))
+    assert np.max(np.abs(ST)) < 100.0
+
+
+def test_identity_token_leaves_state_unchanged():
+    """k = 0, w.v = 0, log alpha = 0 is the identity step (used for padding)."""
+    rng = np.random.default_rng(15)
+    q, k, v, la, b, w = rand_case(rng, 1, dk=4, dv=6)
+    k[:] = 0.0
+    la[:] = 0.0
+    w[:] = 0.0
+    S0 = rng.standard_normal((1, 1, 4, 6))
+    o, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    assert close(ST, S0, 0.0)
+    assert close(o[0, 0], S0[0, 0].T @ q[0, 0])
