@@ -1,0 +1,187 @@
+"""MI355X (gfx950) Gated DeltaNet-2 core -- Python binding of libgdn2.so.
+
+This module only marshals arguments: it checks tensor shapes, allocates outputs and the
+workspace with torch, and calls the C ABI (``include/gdn2.h``) on torch's current HIP
+stream. Every step of the computation runs in the library's HIP kernels; there is no
+CPU or PyTorch fallback, and the calls raise if the library is not built or the tensors
+are not on a GPU.
+
+    o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size=64)
+    o      = recurrent_step(q, k, v, log_alpha, b, w, S)      # S updated in place
+
+Layouts: q, k [B,T,H_k,d_k]; v, w [B,T,H_v,d_v]; log_alpha, b [B,T,H_v,d_k];
+states [N,H_v,d_k,d_v] fp32. ``log_alpha`` is log of the decay (<= 0). Decode inputs drop
+the T axis: q, k [N,H_k,d_k], v, w [N,H_v,d_v], log_alpha, b [N,H_v,d_k].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_build", "libgdn2.so")
+
+GDN2_F32, GDN2_BF16 = 0, 1
+STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL_ARG", 2: "GDN2_ERR_BAD_SHAPE",
+          3: "GDN2_ERR_UNSUPPORTED", 4: "GDN2_ERR_WORKSPACE", 5: "GDN2_ERR_HIP"}
+CHUNK_SIZE = 64
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("h_k", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class GDN2Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgdn2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m gated_delta_rule_gdn_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        dp = ctypes.POINTER(Dims)
+        L.gdn2_abi_version.restype = i32
+        L.gdn2_abi_version.argtypes = []
+        L.gdn2_status_string.restype = ctypes.c_char_p
+        L.gdn2_status_string.argtypes = [i32]
+        L.gdn2_last_error.restype = ctypes.c_char_p
+        L.gdn2_last_error.argtypes = []
+        L.gdn2_chunk_fwd_workspace_bytes.restype = sz
+        L.gdn2_chunk_fwd_workspace_bytes.argtypes = [dp, i32]
+        L.gdn2_chunk_fwd.restype = i32
+        L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i32, vp, vp, dp, vp, sz, vp]
+        L.gdn2_recurrent_step.restype = i32
+        L.gdn2_recurrent_step.argtypes = [vp] * 8 + [dp, vp]
+        L.gdn2_check_cu_seqlens.restype = i32
+        L.gdn2_check_cu_seqlens.argtypes = [vp, i32, i32]
+        _lib = L
+    return _lib
+
+
+def _raise_on(status: int) -> None:
+    if status != 0:
+        msg = lib().gdn2_last_error().decode(errors="replace")
+        raise GDN2Error(status, msg)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return GDN2_F32
+    if t == torch.bfloat16:
+        return GDN2_BF16
+    raise TypeError(f"unsupported dtype {t}; use torch.float32 or torch.bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need_gpu(name: str, t: torch.Tensor, device) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_fwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: int, d_v: int,
+                              dtype: torch.dtype, num_seqs: int = 0,
+                              chunk_size: int = CHUNK_SIZE) -> int:
+    d = Dims(batch, seqlen, num_seqs, h_k, h_v, d_k, d_v, _dtype_code(dtype))
+    return int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), chunk_size))
+
+
+def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: int = CHUNK_SIZE,
+              output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked WY forward. Returns (o [B,T,H_v,d_v], S_T [N,H_v,d_k,d_v] fp32 or None)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
+        _need_gpu(name, t, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError("q and k must both be [B,T,H_k,d_k]")
+    B, T, Hk, dk = q.shape
+    if v.dim() != 4 or v.shape[:2] != (B, T) or w.shape != v.shape:
+        raise ValueError("v and w must both be [B,T,H_v,d_v]")
+    Hv, dv = v.shape[2], v.shape[3]
+    if log_alpha.shape != (B, T, Hv, dk) or b.shape != (B, T, Hv, dk):
+        raise ValueError("log_alpha and b must be [B,T,H_v,d_k]")
+    if cu_seqlens is not None:
+        _need_gpu("cu_seqlens", cu_seqlens, dev)
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if S0 is not None:
+        _need_gpu("S0", S0, dev)
+        if S0.dtype != torch.float32 or S0.shape != (N, Hv, dk, dv):
+            raise ValueError(f"S0 must be fp32 [{N},{Hv},{dk},{dv}]")
+    code = _dtype_code(q.dtype)
+    dims = Dims(B, T, N if cu_seqlens is not None else 0, Hk, Hv, dk, dv, code)
+    need = int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), chunk_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    o = out if out is not None else torch.empty(B, T, Hv, dv, dtype=q.dtype, device=dev)
+    S_T = None
+    if output_final_state:
+        S_T = final_state if final_state is not None else torch.empty(
+            N, Hv, dk, dv, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                              _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(o), _ptr(S_T),
+                              ctypes.byref(dims), _ptr(workspace), workspace.numel(), stream)
+    _raise_on(st)
+    return o, S_T
+
+
+def recurrent_step(q, k, v, log_alpha, b, w, S, out: Optional[torch.Tensor] = None
+                   ) -> torch.Tensor:
+    """One fused decode step; S [N,H_v,d_k,d_v] fp32 is updated in place. Returns o."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
+        _need_gpu(name, t, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    _need_gpu("S", S, dev)
+    if q.dim() != 3 or k.shape != q.shape:
+        raise ValueError("q and k must both be [N,H_k,d_k]")
+    N, Hk, dk = q.shape
+    if v.dim() != 3 or v.shape[0] != N or w.shape != v.shape:
+        raise ValueError("v and w must both be [N,H_v,d_v]")
+    Hv, dv = v.shape[1], v.shape[2]
+    if log_alpha.shape != (N, Hv, dk) or b.shape != (N, Hv, dk):
+        raise ValueError("log_alpha and b must be [N,H_v,d_k]")
+    if S.dtype != torch.float32 or S.shape != (N, Hv, dk, dv):
+        raise ValueError(f"S must be fp32 [{N},{Hv},{dk},{dv}]")
+    dims = Dims(N, 1, 0, Hk, Hv, dk, dv, _dtype_code(q.dtype))
+    o = out if out is not None else torch.empty(N, Hv, dv, dtype=q.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib().gdn2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                   _ptr(S), _ptr(o), ctypes.byref(dims), stream)
+    _raise_on(st)
+    return o
+
+
+def abi_version() -> int:
+    return int(lib().gdn2_abi_version())

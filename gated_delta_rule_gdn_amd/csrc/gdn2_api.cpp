@@ -1,0 +1,184 @@
+// gdn2_api.cpp -- the extern "C" boundary of libgdn2: argument validation, workspace sizing
+// and dispatch to the gfx950 kernels. Every check runs on the host before anything is
+// enqueued, so a rejected call has no effect on the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "gdn2.h"
+#include "gdn2_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+gdn2_status fail(gdn2_status st, const char *msg) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg);
+    return st;
+}
+
+gdn2_status fail_hip(hipError_t e, const char *where) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+    return GDN2_ERR_HIP;
+}
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Checks shared by both entry points. `tokens` is the token count the layouts span.
+gdn2_status check_heads(const gdn2_dims *d) {
+    if (d->dtype != GDN2_F32 && d->dtype != GDN2_BF16)
+        return fail(GDN2_ERR_UNSUPPORTED, "dtype must be GDN2_F32 or GDN2_BF16");
+    if (d->h_k < 1 || d->h_v < 1) return fail(GDN2_ERR_BAD_SHAPE, "h_k and h_v must be >= 1");
+    if (d->h_v % d->h_k != 0) return fail(GDN2_ERR_BAD_SHAPE, "h_v must be a multiple of h_k");
+    if (d->d_k < 1 || d->d_v < 1) return fail(GDN2_ERR_BAD_SHAPE, "d_k and d_v must be >= 1");
+    if (!head_dim_ok(d->d_k) || !head_dim_ok(d->d_v))
+        return fail(GDN2_ERR_UNSUPPORTED, "d_k and d_v must each be 64 or 128");
+    return GDN2_OK;
+}
+
+constexpr int64_t kMaxElems = (int64_t{1} << 40);   // bound on any tensor's element count
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdn2_abi_version(void) { return GDN2_ABI_VERSION; }
+
+const char *gdn2_status_string(int32_t s) {
+    switch (s) {
+        case GDN2_OK: return "ok";
+        case GDN2_ERR_NULL_ARG: return "a required pointer is NULL";
+        case GDN2_ERR_BAD_SHAPE: return "invalid or inconsistent dimensions";
+        case GDN2_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GDN2_ERR_WORKSPACE: return "workspace missing or too small";
+        case GDN2_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *gdn2_last_error(void) { return g_last_error; }
+
+static gdn2_status check_chunk_dims(const gdn2_dims *d, int32_t chunk_size, bool packed) {
+    if (!d) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
+    gdn2_status st = check_heads(d);
+    if (st != GDN2_OK) return st;
+    if (chunk_size < 1) return fail(GDN2_ERR_BAD_SHAPE, "chunk_size must be >= 1");
+    if (chunk_size != gdn2::kChunk) return fail(GDN2_ERR_UNSUPPORTED, "chunk_size must be 64");
+    if (!gdn2::chunk_dims_built(d->d_k, d->d_v, d->dtype == GDN2_BF16))
+        return fail(GDN2_ERR_UNSUPPORTED,
+                    "fp32 chunk forward is built for d_k = d_v = 64 only");
+    if (d->seqlen < 0) return fail(GDN2_ERR_BAD_SHAPE, "seqlen must be >= 0");
+    if (packed) {
+        if (d->batch != 1) return fail(GDN2_ERR_BAD_SHAPE, "packed batches need batch = 1");
+        if (d->num_seqs < 1) return fail(GDN2_ERR_BAD_SHAPE, "num_seqs must be >= 1");
+    } else if (d->batch < 1) {
+        return fail(GDN2_ERR_BAD_SHAPE, "batch must be >= 1");
+    }
+    const int64_t tokens = static_cast<int64_t>(d->batch) * d->seqlen;
+    if (tokens > INT32_MAX) return fail(GDN2_ERR_BAD_SHAPE, "more than 2^31-1 tokens");
+    const int64_t hd = static_cast<int64_t>(d->h_v) * (d->d_k > d->d_v ? d->d_k : d->d_v);
+    if (tokens * hd > kMaxElems) return fail(GDN2_ERR_BAD_SHAPE, "tensors too large");
+    const int64_t nseq = packed ? d->num_seqs : d->batch;
+    if (nseq * d->h_v * d->d_k * d->d_v > kMaxElems)
+        return fail(GDN2_ERR_BAD_SHAPE, "state tensor too large");
+    return GDN2_OK;
+}
+
+size_t gdn2_chunk_fwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size) {
+    if (!dims) return 0;
+    const bool packed = dims->num_seqs > 0 && dims->batch == 1;
+    // A dense call ignores num_seqs; size for whichever layout the caller may use.
+    if (check_chunk_dims(dims, chunk_size, false) != GDN2_OK &&
+        check_chunk_dims(dims, chunk_size, packed) != GDN2_OK)
+        return 0;
+    const bool bf = dims->dtype == GDN2_BF16;
+    const size_t dense = gdn2::chunk_workspace_bytes(dims->batch, dims->seqlen, dims->num_seqs,
+                                                      dims->h_v, dims->d_k, dims->d_v, bf, false);
+    const size_t pk = packed ? gdn2::chunk_workspace_bytes(dims->batch, dims->seqlen,
+                                                           dims->num_seqs, dims->h_v, dims->d_k,
+                                                           dims->d_v, bf, true)
+                             : 0;
+    return dense > pk ? dense : pk;
+}
+
+gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *b, const void *w, const float *S0,
+                           const int32_t *cu_seqlens, int32_t chunk_size, void *o, float *S_T,
+                           const gdn2_dims *dims, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    const bool packed = cu_seqlens != nullptr;
+    gdn2_status st = check_chunk_dims(dims, chunk_size, packed);
+    if (st != GDN2_OK) return st;
+    const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
+    if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
+        return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w and o are required");
+    const bool bf = dims->dtype == GDN2_BF16;
+    const size_t need = gdn2::chunk_workspace_bytes(dims->batch, dims->seqlen, dims->num_seqs,
+                                                    dims->h_v, dims->d_k, dims->d_v, bf, packed);
+    if (need > 0 && !workspace) return fail(GDN2_ERR_WORKSPACE, "workspace is NULL");
+    if (workspace_bytes < need) return fail(GDN2_ERR_WORKSPACE, "workspace is too small");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(GDN2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (o && (o == q || o == k || o == v || o == log_alpha || o == b || o == w))
+        return fail(GDN2_ERR_BAD_SHAPE, "o must not alias an input");
+
+    gdn2::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.b = b; a.w = w;
+    a.S0 = S0; a.cu_seqlens = cu_seqlens; a.o = o; a.S_T = S_T;
+    a.workspace = static_cast<char *>(workspace);
+    a.batch = dims->batch; a.seqlen = dims->seqlen; a.num_seqs = packed ? dims->num_seqs : 0;
+    a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
+    a.bf16 = bf;
+    const hipError_t e = gdn2::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "gdn2_chunk_fwd launch");
+    g_last_error[0] = '\0';
+    return GDN2_OK;
+}
+
+gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
+                                const void *log_alpha, const void *b, const void *w, float *S,
+                                void *o, const gdn2_dims *dims, void *stream) {
+    if (!dims) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
+    gdn2_status st = check_heads(dims);
+    if (st != GDN2_OK) return st;
+    if (dims->seqlen != 1) return fail(GDN2_ERR_BAD_SHAPE, "recurrent step needs seqlen = 1");
+    if (dims->batch < 0) return fail(GDN2_ERR_BAD_SHAPE, "batch must be >= 0");
+    if (static_cast<int64_t>(dims->batch) * dims->h_v * dims->d_k * dims->d_v > kMaxElems)
+        return fail(GDN2_ERR_BAD_SHAPE, "state tensor too large");
+    if (static_cast<int64_t>(dims->batch) * dims->h_v > INT32_MAX)
+        return fail(GDN2_ERR_BAD_SHAPE, "too many states");
+    if (dims->batch == 0) {
+        g_last_error[0] = '\0';
+        return GDN2_OK;
+    }
+    if (!q || !k || !v || !log_alpha || !b || !w || !S || !o)
+        return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w, S and o are required");
+    if (o == q || o == k || o == v || o == log_alpha || o == b || o == w || o == S)
+        return fail(GDN2_ERR_BAD_SHAPE, "o must not alias an input or the state");
+
+    gdn2::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.b = b; a.w = w;
+    a.S = S; a.o = o;
+    a.num_seqs = dims->batch; a.h_k = dims->h_k; a.h_v = dims->h_v;
+    a.d_k = dims->d_k; a.d_v = dims->d_v;
+    a.bf16 = dims->dtype == GDN2_BF16;
+    const hipError_t e = gdn2::launch_decode(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "gdn2_recurrent_step launch");
+    g_last_error[0] = '\0';
+    return GDN2_OK;
+}
+
+gdn2_status gdn2_check_cu_seqlens(const int32_t *cu, int32_t num_seqs, int32_t total_tokens) {
+    if (!cu) return fail(GDN2_ERR_NULL_ARG, "cu_seqlens is NULL");
+    if (num_seqs < 1) return fail(GDN2_ERR_BAD_SHAPE, "num_seqs must be >= 1");
+    if (cu[0] != 0) return fail(GDN2_ERR_BAD_SHAPE, "cu_seqlens[0] must be 0");
+    for (int32_t n = 0; n < num_seqs; ++n)
+        if (cu[n + 1] < cu[n]) return fail(GDN2_ERR_BAD_SHAPE, "cu_seqlens must not decrease");
+    if (cu[num_seqs] != total_tokens)
+        return fail(GDN2_ERR_BAD_SHAPE, "cu_seqlens[num_seqs] must equal the token count");
+    g_last_error[0] = '\0';
+    return GDN2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// gdn2_internal.h -- host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+constexpr int kChunk = 64;   // chunk size of the chunked forward
+
+struct DecodeArgs {
+    const void *q, *k, *v, *log_alpha, *b, *w;
+    float *S;
+    void *o;
+    int num_seqs, h_k, h_v, d_k, d_v;
+    bool bf16;
+};
+
+struct ChunkArgs {
+    const void *q, *k, *v, *log_alpha, *b, *w;
+    const float *S0;
+    const int32_t *cu_seqlens;   // NULL: dense
+    void *o;
+    float *S_T;
+    char *workspace;
+    int batch, seqlen, num_seqs, h_k, h_v, d_k, d_v;
+    bool bf16;
+};
+
+// Workspace layout of the chunked forward (all offsets 256-byte aligned):
+//   [chunk map: int32[num_seqs + 1], packed batches only]
+//   [per (chunk, value head) record of chunk_record_bytes()]
+size_t chunk_record_bytes(int d_k, int d_v, bool bf16);
+int64_t chunk_upper_bound(int batch, int seqlen, int num_seqs, bool packed);
+size_t chunk_map_bytes(int num_seqs, bool packed);
+size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
+                             bool bf16, bool packed);
+bool chunk_dims_built(int d_k, int d_v, bool bf16);
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st);
+
+}  // namespace gdn2

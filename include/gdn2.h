@@ -1,0 +1,160 @@
+/*
+ * gdn2.h -- C ABI of the MI355X (gfx950) Gated DeltaNet-2 core library, libgdn2.so.
+ *
+ * The method (burn-gdn2 0.1.5 docs page, section "Architecture"): per sequence and per
+ * value head, a matrix state S in R^{d_k x d_v} follows
+ *
+ *     S_t = (I - k_t (b_t . k_t)^T) diag(alpha_t) S_{t-1} + k_t (w_t . v_t)^T
+ *     o_t = q_t^T S_t
+ *
+ * with alpha_t the channel-wise decay and b_t the erase gate on the key axis, and w_t the
+ * write gate on the value axis. The same page names two ways to run it, and this library
+ * exports one call for each:
+ *   - gdn2_chunk_fwd       the chunked WY-decomposition forward ("Chunk" mode, training and
+ *                          prefill; chunk_size defaults to 64 on that page);
+ *   - gdn2_recurrent_step  one fused token-by-token step ("FusedRecurrent" mode, decode),
+ *                          which reads and writes a persistent state in place as the
+ *                          llama.cpp decode notes (LocalAI mirror, section 2) describe.
+ *
+ * Conventions (the pages are silent on these; this is the reading the library implements):
+ *   - o_t reads the state AFTER the update of token t.
+ *   - The decay argument carries log(alpha) <= 0, in the input dtype; the kernels take exp.
+ *   - No query scaling (a caller wanting 1/sqrt(d_k) pre-scales q; o is linear in q).
+ *   - Grouped value attention: value head h reads key head h / (h_v / h_k)
+ *     (burn-gdn2 "num_v_heads"; the llama.cpp notes' 48 value heads over 16 key groups).
+ *   - The negative-eigenvalue option of burn-gdn2 (allow_neg_eigval, "b x 2") is the
+ *     caller's b in (0,2); the library has no flag for it.
+ *
+ * Layouts (all contiguous, last dimension fastest):
+ *   q, k          [B, T, h_k, d_k]      input dtype
+ *   v, w, o       [B, T, h_v, d_v]      input dtype (o is written in the input dtype)
+ *   log_alpha, b  [B, T, h_v, d_k]      input dtype
+ *   S0, S_T, S    [N, h_v, d_k, d_v]    fp32 always, d_v fastest
+ * A packed (variable-length) batch uses B = 1, T = total tokens and cu_seqlens (int32,
+ * N + 1 offsets, device memory): sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1.
+ * Without cu_seqlens the batch is dense: N = B sequences of T tokens each.
+ *
+ * Ownership: the caller allocates every buffer (inputs, outputs, workspace, state). The
+ * library allocates no device memory and keeps no state between calls apart from the
+ * thread-local error message.
+ *
+ * Streams: every call only enqueues work on `stream` (a hipStream_t; NULL is the default
+ * stream) and returns without synchronising. No call reads device memory on the host.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; a failed check
+ * returns a status code and launches nothing. A failed launch returns GDN2_ERR_HIP. A short
+ * message for the last failure of the calling thread is available from gdn2_last_error().
+ * Device-side contents (cu_seqlens values, NaN/Inf in the data) are not checked: NaN and
+ * Inf propagate into the affected (sequence, head) outputs.
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN2_ABI_VERSION 1
+
+typedef enum gdn2_status {
+    GDN2_OK = 0,
+    GDN2_ERR_NULL_ARG = 1,      /* a required pointer is NULL */
+    GDN2_ERR_BAD_SHAPE = 2,     /* a dimension is out of range or inconsistent */
+    GDN2_ERR_UNSUPPORTED = 3,   /* valid but not built: head dims, chunk size, dtype */
+    GDN2_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
+    GDN2_ERR_HIP = 5            /* the HIP runtime reported an error */
+} gdn2_status;
+
+typedef enum gdn2_dtype {
+    GDN2_F32 = 0,               /* fp32 inputs and o; fp32 arithmetic throughout */
+    GDN2_BF16 = 1               /* bf16 inputs and o; bf16 matrix-core operands, fp32
+                                   accumulation, fp32 state */
+} gdn2_dtype;
+
+typedef struct gdn2_dims {
+    int32_t batch;      /* dense: number of sequences B. packed: must be 1.
+                           recurrent step: number of sequences N. */
+    int32_t seqlen;     /* dense: tokens per sequence T (>= 0). packed: total tokens.
+                           recurrent step: must be 1. */
+    int32_t num_seqs;   /* packed: N, the number of sequences (cu_seqlens has N+1 entries).
+                           dense and recurrent step: ignored. */
+    int32_t h_k;        /* key/query heads (>= 1) */
+    int32_t h_v;        /* value heads, a multiple of h_k */
+    int32_t d_k;        /* key head dim: 64 or 128 */
+    int32_t d_v;        /* value head dim: 64 or 128 */
+    int32_t dtype;      /* gdn2_dtype */
+} gdn2_dims;
+
+/* Library ABI version (GDN2_ABI_VERSION of the build). */
+int32_t gdn2_abi_version(void);
+
+/* Static text for a status code. */
+const char *gdn2_status_string(int32_t status);
+
+/* Message of the last failing call made by this thread ("" if none). */
+const char *gdn2_last_error(void);
+
+/*
+ * Bytes of device workspace gdn2_chunk_fwd needs for these dims and chunk size, or 0 if
+ * the dims are invalid. For a packed batch the size uses the upper bound
+ * ceil(T / chunk_size) + N on the number of chunks, so it depends only on the dims.
+ */
+size_t gdn2_chunk_fwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size);
+
+/*
+ * Chunked WY forward over a whole batch (burn-gdn2 docs page, "Chunk" mode of the
+ * Architecture section; chunk_size as in its Configuration table).
+ *
+ *   q, k, v, log_alpha, b, w   device inputs in the layouts above (dims->dtype)
+ *   S0          device fp32 [N, h_v, d_k, d_v] initial states, or NULL for zero states
+ *   cu_seqlens  device int32 [N+1] for a packed batch, or NULL for a dense batch.
+ *               Precondition (not checked on the device): cu_seqlens[0] = 0,
+ *               non-decreasing, cu_seqlens[N] = T. Zero-length sequences are allowed and
+ *               return S_T = S0 (or zeros).
+ *   chunk_size  64 (the only size built)
+ *   o           device output [B, T, h_v, d_v] in the input dtype; must not alias inputs
+ *   S_T         device fp32 [N, h_v, d_k, d_v] final states, or NULL to skip them. S_T may
+ *               be the same buffer as S0 (in-place continuation); no other aliasing.
+ *   workspace   device buffer of at least gdn2_chunk_fwd_workspace_bytes() bytes, 256-byte
+ *               aligned; its contents on entry are ignored and are clobbered.
+ *   stream      hipStream_t the work is enqueued on
+ * Returns GDN2_OK or an error status (nothing is enqueued on a validation error).
+ */
+gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *b, const void *w,
+                           const float *S0, const int32_t *cu_seqlens, int32_t chunk_size,
+                           void *o, float *S_T, const gdn2_dims *dims,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for N sequences, one token each (burn-gdn2 "FusedRecurrent" mode; the
+ * llama.cpp decode notes, section 2, describe the same fused state read-update-write).
+ *
+ *   q, k          device [N, h_k, d_k]   (dims->batch = N, dims->seqlen = 1)
+ *   v, w          device [N, h_v, d_v]
+ *   log_alpha, b  device [N, h_v, d_k]
+ *   S             device fp32 [N, h_v, d_k, d_v], read and updated in place
+ *   o             device [N, h_v, d_v] in the input dtype; must not alias any input or S
+ *   stream        hipStream_t
+ * Each state is read from memory once and written once.
+ */
+gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
+                                const void *log_alpha, const void *b, const void *w,
+                                float *S, void *o, const gdn2_dims *dims, void *stream);
+
+/*
+ * Host helper: checks a HOST copy of cu_seqlens (N+1 entries) against total tokens T.
+ * Returns GDN2_OK when cu[0] = 0, cu is non-decreasing and cu[N] = T, else
+ * GDN2_ERR_BAD_SHAPE (GDN2_ERR_NULL_ARG for a NULL pointer). Touches no device.
+ */
+gdn2_status gdn2_check_cu_seqlens(const int32_t *cu_seqlens_host, int32_t num_seqs,
+                                  int32_t total_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects invalid arguments before touching a device.
+
+Every call made here fails host validation by construction (a NULL dims, a bad shape, a
+too-small workspace, ...), so no kernel is ever launched and no device is needed.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_gdn_amd as g
+from gated_delta_rule_gdn_amd import Dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+FAKE = ctypes.c_void_p(0x1000)       # never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(g.LIB_PATH):
+        from gated_delta_rule_gdn_amd import build
+        build.build()
+    return g.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"gdn2_chunk_fwd", "gdn2_recurrent_step", "gdn2_chunk_fwd_workspace_bytes"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn2_\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_version_and_status_strings(L):
+    assert L.gdn2_abi_version() == 1
+    assert L.gdn2_status_string(0) == b"ok"
+    assert b"workspace" in L.gdn2_status_string(4)
+    assert L.gdn2_status_string(99) == b"unknown status"
+
+
+def chunk(L, dims, chunk_size=64, ws=FAKE, ws_bytes=1 << 40, cu=None, o=FAKE, q=FAKE):
+    # o defaults to the q pointer: a call that passed every other check is still rejected
+    return L.gdn2_chunk_fwd(q, FAKE, FAKE, FAKE, FAKE, FAKE, None, cu, chunk_size, o, None,
+                            None if dims is None else ctypes.byref(dims), ws, ws_bytes, None)
+
+
+def test_chunk_fwd_rejects_bad_arguments(L):
+    ok = dict(batch=2, seqlen=100, num_seqs=0, h_k=2, h_v=4, d_k=128, d_v=128, dtype=1)
+    assert chunk(L, None) == 1
+    assert b"dims" in L.gdn2_last_error()
+    assert chunk(L, Dims(**{**ok, "dtype": 7})) == 3
+    assert chunk(L, Dims(**{**ok, "h_v": 5})) == 2
+    assert chunk(L, Dims(**{**ok, "h_k": 0})) == 2
+    assert chunk(L, Dims(**{**ok, "d_k": 96})) == 3
+    assert chunk(L, Dims(**{**ok, "d_v": 0})) == 2
+    assert chunk(L, Dims(**ok), chunk_size=32) == 3
+    assert chunk(L, Dims(**ok), chunk_size=0) == 2
+    assert chunk(L, Dims(**{**ok, "seqlen": -1})) == 2
+    assert chunk(L, Dims(**{**ok, "batch": 0})) == 2
+    assert chunk(L, Dims(**{**ok, "dtype": 0})) == 3          # fp32 is built for d = 64 only
+    assert chunk(L, Dims(**ok), q=None) == 1
+    assert chunk(L, Dims(**ok), ws=None) == 4
+    assert chunk(L, Dims(**ok), ws_bytes=1024) == 4
+    assert chunk(L, Dims(**ok), ws=ctypes.c_void_p(0x1010)) == 4   # not 256-byte aligned
+    assert chunk(L, Dims(**ok), o=FAKE, q=FAKE) == 2                # o aliases q
+    # packed batches need batch = 1 and num_seqs >= 1
+    assert chunk(L, Dims(**{**ok, "num_seqs": 3}), cu=FAKE) == 2
+    assert chunk(L, Dims(**{**ok, "batch": 1, "num_seqs": 0}), cu=FAKE) == 2
+    # too many tokens
+    assert chunk(L, Dims(**{**ok, "batch": 1 << 20, "seqlen": 1 << 12})) == 2
+
+
+def step(L, dims, S=FAKE, o=FAKE):
+    # o defaults to the q pointer, so even a call that passed every other check would be
+    # rejected by the aliasing check and never launch
+    return L.gdn2_recurrent_step(FAKE, ctypes.c_void_p(0x3000), FAKE, FAKE, FAKE, FAKE, S, o,
+                                 None if dims is None else ctypes.byref(dims), None)
+
+
+def test_recurrent_step_rejects_bad_arguments(L):
+    ok = dict(batch=4, seqlen=1, num_seqs=0, h_k=2, h_v=6, d_k=128, d_v=64, dtype=0)
+    assert step(L, None) == 1
+    assert step(L, Dims(**{**ok, "seqlen": 2})) == 2
+    assert step(L, Dims(**{**ok, "h_v": 5})) == 2
+    assert step(L, Dims(**{**ok, "d_v": 32})) == 3
+    assert step(L, Dims(**{**ok, "dtype": 2})) == 3
+    assert step(L, Dims(**{**ok, "batch": -1})) == 2
+    assert step(L, Dims(**ok), S=None) == 1
+    assert step(L, Dims(**ok), o=FAKE) == 2               # o aliases q
+    assert step(L, Dims(**{**ok, "batch": 0})) == 0       # empty batch: nothing to do
+
+
+def test_workspace_size_formula(L):
+    # per (chunk, value head) record: bf16 operands 2*(3*64*dk + 64*64 + 64*dv) + 4*dk,
+    # rounded up to 256 bytes; dense batches hold B*ceil(T/64) chunks.
+    d = Dims(2, 100, 0, 2, 4, 128, 128, 1)
+    rec = (2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128 + 255) // 256 * 256
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 2 * 2 * 4 * rec
+    # packed: ceil(T/64) + N chunks plus the chunk map
+    d = Dims(1, 1000, 5, 1, 2, 64, 64, 0)
+    rec = (4 * (3 * 64 * 64 + 64 * 64 + 64 * 64) + 4 * 64 + 255) // 256 * 256
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 256 + (16 + 5) * 2 * rec
+    assert L.gdn2_chunk_fwd_workspace_bytes(None, 64) == 0
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(Dims(1, 10, 0, 1, 1, 96, 64, 1)),
+                                            64) == 0
+
+
+def test_cu_seqlens_host_check(L):
+    def chk(vals, n, t):
+        arr = (ctypes.c_int32 * len(vals))(*vals)
+        return L.gdn2_check_cu_seqlens(arr, n, t)
+    assert chk([0, 5, 5, 9], 3, 9) == 0
+    assert chk([1, 5, 9], 2, 9) == 2
+    assert chk([0, 5, 4], 2, 4) == 2
+    assert chk([0, 5, 9], 2, 10) == 2
+    assert L.gdn2_check_cu_seqlens(None, 2, 9) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        g.chunk_fwd(x, x, x, x, x, x)

@@ -1,0 +1,153 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on seeded inputs.
+
+Gate (relative L2 error per output tensor): 1e-4 for fp32 inputs, 2e-2 for bf16 inputs, on
+o and on the final states. Small cases compare every element; the full-size workloads
+compare every element the oracle can afford and otherwise a seeded sample of whole
+(sequence, value head) pairs, each computed over all of its tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_gdn_amd as g
+from gated_delta_rule_gdn_amd import inputs
+from gpu_common import (TOL, assert_chunk_parity, decode_oracle_pair, gpu_chunk, np64,
+                        oracle_chunk, flat_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g.lib()
+
+
+# ---------------------------------------------------------------- decode step -----------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)])
+def test_decode_small(dtype, dk, dv):
+    wl = inputs.DecodeWorkload("decode_small", dtype, 3, 2, 6, dk, dv, steps=5)
+    x = inputs.decode_inputs(wl, seed=11)
+    S = x["S"].cuda()
+    os_ = []
+    for t in range(wl.steps):
+        o = g.recurrent_step(x["q"][t].cuda(), x["k"][t].cuda(), x["v"][t].cuda(),
+                             x["log_alpha"][t].cuda(), x["b"][t].cuda(), x["w"][t].cuda(), S)
+        os_.append(np64(o))
+    torch.cuda.synchronize()
+    o_g = np.stack(os_)                      # [steps, N, Hv, dv]
+    o_r = np.zeros_like(o_g)
+    S_r = np.zeros((3, 6, dk, dv))
+    for n in range(3):
+        for h in range(6):
+            on, Sn = decode_oracle_pair(x, n, h, wl.steps, 3)
+            o_r[:, n, h] = on
+            S_r[n, h] = Sn
+    eo, es = oracle.rel_l2(o_g, o_r), oracle.rel_l2(np64(S), S_r)
+    print(f"[parity] decode {dtype} {dk}x{dv} o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_decode_full_size_256_steps():
+    """64 sequences, 48 value heads over 16 key heads, d=128, fp32 state, 256 steps in place."""
+    wl = inputs.DECODE_F32
+    x = inputs.decode_inputs(wl, seed=3)
+    dev = {n: x[n].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    S = x["S"].cuda()
+    o_all = torch.empty(wl.steps, wl.num_seqs, wl.h_v, wl.d_v, device="cuda")
+    for t in range(wl.steps):
+        g.recurrent_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["log_alpha"][t],
+                         dev["b"][t], dev["w"][t], S, out=o_all[t])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, wl.num_seqs, 24),
+                                              rng.integers(0, wl.h_v, 24))]
+    o_g = np64(o_all)
+    S_g = np64(S)
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(S_g))
+    go, gs, ro, rs = [], [], [], []
+    for n, h in pairs:
+        on, Sn = decode_oracle_pair(x, n, h, wl.steps, wl.h_v // wl.h_k)
+        go.append(o_g[:, n, h].ravel()); ro.append(on.ravel())
+        gs.append(S_g[n, h].ravel()); rs.append(Sn.ravel())
+    eo = oracle.rel_l2(np.concatenate(go), np.concatenate(ro))
+    es = oracle.rel_l2(np.concatenate(gs), np.concatenate(rs))
+    print(f"[parity] decode full 256 steps, 24 sampled states: o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= 1e-4 and es <= 1e-4
+
+
+# ---------------------------------------------------------------- chunk forward ---------
+
+def test_chunk_f32_b1_t256_h4_d64():
+    x = inputs.chunk_inputs(inputs.CHUNK_F32_SMALL, seed=1000)
+    assert_chunk_parity(x, torch.float32, label="chunk f32 B1 T256 H4 d64")
+
+
+def test_chunk_bf16_b8_t2048_h8_d128():
+    x = inputs.chunk_inputs(inputs.CHUNK_BF16_B8, seed=1001)
+    assert_chunk_parity(x, torch.bfloat16, label="chunk bf16 B8 T2048 H8 d128")
+
+
+def test_chunk_bf16_b1_t4096_h16_d128_negeig():
+    x = inputs.chunk_inputs(inputs.CHUNK_BF16_T4096, seed=1002)
+    assert_chunk_parity(x, torch.bfloat16, label="chunk bf16 B1 T4096 H16 d128 neg-eig S0")
+
+
+def test_varlen_bf16_n16_hv32_hk16_d128():
+    x = inputs.chunk_inputs(inputs.VARLEN_BF16, seed=1004)
+    rng = np.random.default_rng(4)
+    pairs = [(n, int(h)) for n in range(16) for h in rng.choice(32, 2, replace=False)]
+    print("[parity] varlen tokens:", int(x["cu_seqlens"][-1]), flush=True)
+    assert_chunk_parity(x, torch.bfloat16, pairs=pairs, label="varlen bf16 16 seqs (32 pairs)")
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [(torch.float32, 64, 64), (torch.bfloat16, 128, 128),
+                                         (torch.bfloat16, 64, 128), (torch.bfloat16, 128, 64),
+                                         (torch.bfloat16, 64, 64)])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
+def test_chunk_tails_gva_and_state(dtype, dk, dv, T):
+    wl = inputs.small_chunk(dtype=dtype, batch=2, seqlen=T, h_k=1, h_v=3, d_k=dk, d_v=dv,
+                            neg_eig=True, s0_std=0.1)
+    x = inputs.chunk_inputs(wl, seed=T)
+    assert_chunk_parity(x, dtype, label=f"tail {dtype} {dk}x{dv} T={T}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_packed_with_empty_and_short_sequences(dtype):
+    wl = inputs.small_chunk(dtype=dtype, h_k=2, h_v=4, d_k=64, d_v=64, num_seqs=6, len_lo=2,
+                            len_hi=150)
+    x = inputs.chunk_inputs(wl, seed=21)
+    cu = x["cu_seqlens"].clone()
+    lens = (cu[1:] - cu[:-1]).tolist()
+    lens[2] = 0                               # force an empty sequence and a 1-token one
+    lens[4] = 1
+    cu[1:] = torch.cumsum(torch.tensor(lens), 0).to(torch.int32)
+    T = int(cu[-1])
+    for n in ("q", "k", "v", "log_alpha", "b", "w"):
+        x[n] = x[n][:, :T].contiguous()
+    x["cu_seqlens"] = cu
+    assert_chunk_parity(x, dtype, label=f"packed {dtype} lens={lens}")
+    _, S_g = gpu_chunk(x)
+    assert np.array_equal(S_g[2], np64(x["S0"][2]))      # empty sequence: S_T = S0
+
+
+def test_chunk_extreme_decay_stress():
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=300, h_k=2, h_v=2, d_k=128,
+                            d_v=128, neg_eig=True)
+    x = inputs.chunk_inputs(wl, seed=5, decay_mu=3.0)
+    assert_chunk_parity(x, torch.bfloat16, label="extreme decay (log alpha ~ -softplus(N(3,1)))")
+
+
+def test_chunk_zero_initial_state_and_no_final_state():
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=100, h_k=1, h_v=1, d_k=128,
+                            d_v=128, s0_std=None)
+    x = inputs.chunk_inputs(wl, seed=8)
+    o_full, _ = gpu_chunk(x)
+    o_only, S_none = gpu_chunk(x, output_final_state=False)
+    assert S_none is None
+    assert np.array_equal(o_full, o_only)
+    o_r, _ = oracle_chunk(x)
+    assert oracle.rel_l2(o_only, o_r) <= 2e-2
