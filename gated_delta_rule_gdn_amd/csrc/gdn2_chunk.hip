@@ -18,13 +18,15 @@
 // Kernels:
 //   K0 chunk_map_kernel    packed batches: chunk offsets per sequence (no host sync).
 //   K1 chunk_prep_kernel   one workgroup per (chunk, value head), fully parallel: the
-//                          cumulative log decay, A and M on the matrix cores, the 16x16
-//                          diagonal inverses of (I + A), a blocked forward substitution for
-//                          W~ and U~, and the per-chunk operands of K2, written to the
-//                          workspace already in matrix-core fragment order.
+//                          cumulative log decay, A and M on the matrix cores, T = (I + A)^{-1}
+//                          by 16x16 blocks (diagonal blocks by forward substitution, the rest
+//                          by fp32 matrix-core products), the WY factors as tile GEMMs, and
+//                          the per-chunk operands of K2, written to the workspace already in
+//                          matrix-core fragment order.
 //   K2 chunk_state_kernel  one wave per (sequence, value head, 16 columns of S), sequential
 //                          over the chunks of its sequence with its slice of S held in
-//                          registers in fp32; writes o and S_T.
+//                          registers in fp32 and the chunk operands prefetched into LDS one
+//                          chunk ahead; writes o and S_T.
 //
 // Numerics: exp(g_r - g_i) is split as exp(g_r - ref) * exp(ref - g_i). For a block of
 // rows r in 16-token sub-chunk R against columns in an earlier sub-chunk, ref is the
@@ -138,304 +140,420 @@ __device__ __forceinline__ u32x4 pack16(const float *v) {
 }
 
 // ---------------------------------------------------------------------------------------
-// K1: per (chunk, value head) WY factors and K2 operands.
+// K1: per (chunk, value head) WY factors and K2 operands, as a persistent kernel.
+//
+// One 512-thread workgroup per CU walks the (chunk, value head) records in chunk-major order
+// (record = chunk * h_v + h, stride = grid size). While a record is computed from LDS, the
+// raw k, q, b, log alpha tiles of the next one are already in flight into registers, and
+// its w.v operands are requested as soon as the current U~ tiles are done, so global memory
+// latency overlaps the math. LDS (about 125 KB at d = 128): raw k, q, b, log alpha with
+// padded rows, g = cumulative log decay (fp32), and the lower 16x16 blocks of A and of
+// T = (I + A)^{-1} (fp32, fragment order).
+//
+// Phases per record:
+//   0  raw tiles -> LDS, cumulative sum of log alpha, gamma_C
+//   1  A^T and M^T blocks (the transposed products leave each lane's results in the
+//      row-per-lane fragment order the consumers read); M goes to the workspace
+//  2a wave 0: 16x16 diagonal inverses T_RR by forward substitution; waves 1-7: Qg, KgT
+//  2b off-diagonal T blocks by levels, T_RI = -T_RR sum_{I<=m<R} A_Rm T_mI (fp32 MFMA)
+//   3  W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) as tile GEMMs, one column tile of
+//      each per wave, written to the workspace in the orders K2 reads
 // ---------------------------------------------------------------------------------------
-template <typename T, bool BF, int DK, int DV>
-__global__ __launch_bounds__(512) void chunk_prep_kernel(ChunkParams p) {
-    using R_ = Rec<DK, DV, BF>;
-    using OT = typename Op<BF>::type;
-    constexpr int C = kChunk, NT = 512, NW = NT / 64;
-    constexpr int KT = Op<BF>::KT, EPL = Op<BF>::EPL;
-    constexpr int VEC = 16 / sizeof(T);          // raw elements per 16-byte load
-    constexpr int CP = C + 1;                    // padded row stride of A and M
-    constexpr int PARTS = NT / DK;               // cumsum: token parts per channel
-    constexpr int RPP = C / PARTS;               // rows per part
-    static_assert(sizeof(T) == sizeof(OT), "raw and operand types share LDS staging");
+__device__ __forceinline__ int lower_blk(int R, int I) { return R * (R + 1) / 2 + I; }
 
-    __shared__ __attribute__((aligned(16))) T s_k[C * DK];
-    __shared__ __attribute__((aligned(16))) T s_q[C * DK];   // later: -W~ staging
-    __shared__ __attribute__((aligned(16))) T s_b[C * DK];
-    __shared__ __attribute__((aligned(16))) T s_v[C * DV];
-    __shared__ __attribute__((aligned(16))) T s_w[C * DV];
-    __shared__ __attribute__((aligned(16))) float s_g[C * DK];
+// Element (r, c) of a 16x16 fp32 block stored in fragment order (lane 16 g + r holds
+// X[r][4 g .. 4 g + 3]).
+__device__ __forceinline__ int frag_idx(int r, int c) { return 4 * (16 * (c >> 2) + r) + (c & 3); }
+
+struct PrepLoc {
+    int64_t t0;     // first token of the chunk
+    int L;          // valid rows
+    int h, hk;
+    size_t rec;     // record index
+};
+
+template <typename T, bool BF, int DK, int DV>
+__global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
+    using R_ = Rec<DK, DV, BF>;
+    constexpr int C = kChunk, NT = 512, NW = NT / 64;
+    constexpr int KT = Op<BF>::KT;            // k per matrix-core tile: 32 (bf16) / 16 (fp32)
+    constexpr int KS = BF ? 8 : 4;            // consecutive k values a lane holds per tile
+    constexpr int VEC = 16 / sizeof(T);
+    constexpr int SK = DK + VEC;              // padded row stride of the raw tiles (elements)
+    constexpr int SG = DK + 4;                // padded row stride of s_g (floats)
+    constexpr int VK = DK / VEC;              // 16-byte vectors per raw row
+    constexpr int RAWV = C * VK / NT;         // raw vectors per thread per tensor
+    constexpr int PARTS = NT / DK;            // cumulative sum: token parts per channel
+    constexpr int RPP = C / PARTS;
+    constexpr int NKC = R_::NKT_C, NKTC = C / KT;
+    constexpr int VV = DV / VEC;              // 16-byte vectors per raw value row
+    constexpr int RAWW = C * VV / NT;         // raw w / v vectors per thread
+    static_assert(RAWV >= 1 && RAWV * NT == C * VK, "raw tile split");
+    static_assert(RAWW >= 1 && RAWW * NT == C * VV, "raw tile split");
+    constexpr int SL = (DK > DV ? DK : DV) + VEC;   // row stride of the log alpha / w.v tile
+
+    __shared__ __attribute__((aligned(16))) T s_k[C * SK];
+    __shared__ __attribute__((aligned(16))) T s_q[C * SK];
+    __shared__ __attribute__((aligned(16))) T s_b[C * SK];
+    __shared__ __attribute__((aligned(16))) T s_la[C * SL];  // log alpha, then w.v
+    __shared__ __attribute__((aligned(16))) float s_g[C * SG];
+    __shared__ __attribute__((aligned(16))) float s_A[10 * 256];
+    __shared__ __attribute__((aligned(16))) float s_T[10 * 256];
     __shared__ float s_part[PARTS * DK];
-    __shared__ float s_A[C * CP];
-    __shared__ float s_M[C * CP];
-    __shared__ float s_T[4 * 16 * 16];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const int chunk = blockIdx.x, h = blockIdx.y, hk = h / p.group;
-    int n, j;
-    int64_t start, end;
-    if (!locate_chunk(p, chunk, n, j, start, end)) return;
-    const int64_t t0 = start + static_cast<int64_t>(j) * C;
-    const int L = static_cast<int>(min<int64_t>(C, end - t0));
-    char *rec = p.rec + (static_cast<size_t>(chunk) * p.h_v + h) * R_::bytes;
+    const T *kp = static_cast<const T *>(p.k), *qp = static_cast<const T *>(p.q);
+    const T *bp = static_cast<const T *>(p.b), *lap = static_cast<const T *>(p.log_alpha);
+    const T *vp = static_cast<const T *>(p.v), *wp = static_cast<const T *>(p.w);
 
-    // ---- phase 0: stage raw tiles, zero A/M, cumulative log decay ----
-    {
-        const T *kp = static_cast<const T *>(p.k), *qp = static_cast<const T *>(p.q);
-        const T *bp = static_cast<const T *>(p.b);
-        const T *vp = static_cast<const T *>(p.v), *wp = static_cast<const T *>(p.w);
-        constexpr int VK = DK / VEC, VV = DV / VEC;
-        for (int idx = tid; idx < C * VK; idx += NT) {
-            const int r = idx / VK, cv = idx - r * VK;
-            u32x4 kv = {0u, 0u, 0u, 0u}, qv = kv, bv = kv;
-            if (r < L) {
-                const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + cv * VEC;
-                const size_t ob = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + cv * VEC;
-                kv = *reinterpret_cast<const u32x4 *>(kp + ok);
-                qv = *reinterpret_cast<const u32x4 *>(qp + ok);
-                bv = *reinterpret_cast<const u32x4 *>(bp + ob);
+    const int total_chunks = p.cu ? p.map[p.num_seqs] : p.num_seqs * p.nc_dense;
+    const int nitems = total_chunks * p.h_v;
+
+    auto locate = [&](int item, PrepLoc &lc) {
+        const int chunk = item / p.h_v;
+        lc.h = item - chunk * p.h_v;
+        lc.hk = lc.h / p.group;
+        int n, j;
+        int64_t start, end;
+        locate_chunk(p, chunk, n, j, start, end);
+        lc.t0 = start + static_cast<int64_t>(j) * C;
+        lc.L = static_cast<int>(min<int64_t>(C, end - lc.t0));
+        lc.rec = static_cast<size_t>(item);
+    };
+    // raw k, q, b, log alpha vectors of a record (rows >= L are zero: identity tokens)
+    u32x4 rk[RAWV], rq[RAWV], rb[RAWV], rl[RAWV], rw[RAWW], rv[RAWW];
+    auto load_raw = [&](const PrepLoc &lc) {
+#pragma unroll
+        for (int e = 0; e < RAWW; ++e) {
+            const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            rw[e] = z; rv[e] = z;
+            if (r < lc.L) {
+                const size_t ov = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DV + cv * VEC;
+                rw[e] = *reinterpret_cast<const u32x4 *>(wp + ov);
+                rv[e] = *reinterpret_cast<const u32x4 *>(vp + ov);
             }
-            *reinterpret_cast<u32x4 *>(&s_k[r * DK + cv * VEC]) = kv;
-            *reinterpret_cast<u32x4 *>(&s_q[r * DK + cv * VEC]) = qv;
-            *reinterpret_cast<u32x4 *>(&s_b[r * DK + cv * VEC]) = bv;
         }
-        for (int idx = tid; idx < C * VV; idx += NT) {
-            const int r = idx / VV, cv = idx - r * VV;
-            u32x4 vv = {0u, 0u, 0u, 0u}, wv = vv;
-            if (r < L) {
-                const size_t ov = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + cv * VEC;
-                vv = *reinterpret_cast<const u32x4 *>(vp + ov);
-                wv = *reinterpret_cast<const u32x4 *>(wp + ov);
+#pragma unroll
+        for (int e = 0; e < RAWV; ++e) {
+            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            rk[e] = z; rq[e] = z; rb[e] = z; rl[e] = z;
+            if (r < lc.L) {
+                const size_t ok = (static_cast<size_t>(lc.t0 + r) * p.h_k + lc.hk) * DK + cv * VEC;
+                const size_t og = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DK + cv * VEC;
+                rk[e] = *reinterpret_cast<const u32x4 *>(kp + ok);
+                rq[e] = *reinterpret_cast<const u32x4 *>(qp + ok);
+                rb[e] = *reinterpret_cast<const u32x4 *>(bp + og);
+                rl[e] = *reinterpret_cast<const u32x4 *>(lap + og);
             }
-            *reinterpret_cast<u32x4 *>(&s_v[r * DV + cv * VEC]) = vv;
-            *reinterpret_cast<u32x4 *>(&s_w[r * DV + cv * VEC]) = wv;
         }
-        for (int idx = tid; idx < C * CP; idx += NT) {
-            s_A[idx] = 0.f;
-            s_M[idx] = 0.f;
+    };
+    int item = blockIdx.x;
+    PrepLoc cur;
+    if (item < nitems) {
+        locate(item, cur);
+        load_raw(cur);
+    }
+    for (; item < nitems; item += gridDim.x) {
+        const int next = item + gridDim.x;
+        const bool has_next = next < nitems;
+        PrepLoc nxt = cur;
+        if (has_next) locate(next, nxt);
+        char *rec = p.rec + cur.rec * R_::bytes;
+
+        // ---- phase 0 ----
+#pragma unroll
+        for (int e = 0; e < RAWV; ++e) {
+            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
+            *reinterpret_cast<u32x4 *>(&s_k[r * SK + cv * VEC]) = rk[e];
+            *reinterpret_cast<u32x4 *>(&s_q[r * SK + cv * VEC]) = rq[e];
+            *reinterpret_cast<u32x4 *>(&s_b[r * SK + cv * VEC]) = rb[e];
+            *reinterpret_cast<u32x4 *>(&s_la[r * SL + cv * VEC]) = rl[e];
         }
-        const T *lap = static_cast<const T *>(p.log_alpha);
-        const int c = tid % DK, part = tid / DK;
-        float acc = 0.f;
-        for (int rr = 0; rr < RPP; ++rr) {
-            const int r = part * RPP + rr;
-            const float x = (r < L)
-                ? io<T>::ld(lap + (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c) : 0.f;
-            acc += x;
-            s_g[r * DK + c] = acc;
-        }
-        s_part[part * DK + c] = acc;
         __syncthreads();
-        float pre = 0.f;
-        for (int pp = 0; pp < part; ++pp) pre += s_part[pp * DK + c];
-        for (int rr = 0; rr < RPP; ++rr) s_g[(part * RPP + rr) * DK + c] += pre;
-        __syncthreads();
-        if (tid < DK) {
-            reinterpret_cast<float *>(rec + R_::gC)[tid] = __expf(s_g[(C - 1) * DK + tid]);
-        }
-    }
-
-    // ---- phase 1a: A and M, 16x16 blocks (R >= I) on the matrix cores ----
-    for (int pr = wave; pr < 10; pr += NW) {
-        const int R = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
-        const int I = pr - R * (R + 1) / 2;
-        const bool diag = (R == I);
-        const int refrow = diag ? 16 * R + 7 : 16 * R - 1;   // R >= 1 when off-diagonal
-        const int r = 16 * R + li;                           // A-operand row (token)
-        const int i = 16 * I + li;                           // B-operand column (token)
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
-#pragma unroll
-        for (int kt = 0; kt < DK / KT; ++kt) {
-            if constexpr (BF) {
-                float ak[8], aq[8], bk[8];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int c = kt * 32 + 8 * lg + jj;
-                    const float ref = s_g[refrow * DK + c];
-                    const float ef = __expf(s_g[r * DK + c] - ref);
-                    const float ec = __expf(ref - s_g[i * DK + c]);
-                    const float kr = io<T>::ld(&s_k[r * DK + c]);
-                    ak[jj] = io<T>::ld(&s_b[r * DK + c]) * kr * ef;
-                    aq[jj] = io<T>::ld(&s_q[r * DK + c]) * ef;
-                    bk[jj] = io<T>::ld(&s_k[i * DK + c]) * ec;
-                }
-                const u32x4 B = pack16<true>(bk);
-                accA = mma_k32(pack16<true>(ak), B, accA);
-                accM = mma_k32(pack16<true>(aq), B, accM);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int c = kt * 16 + 4 * lg + s;
-                    const float ref = s_g[refrow * DK + c];
-                    const float ef = __expf(s_g[r * DK + c] - ref);
-                    const float ec = __expf(ref - s_g[i * DK + c]);
-                    const float kr = io<T>::ld(&s_k[r * DK + c]);
-                    const float bk = io<T>::ld(&s_k[i * DK + c]) * ec;
-                    accA = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        io<T>::ld(&s_b[r * DK + c]) * kr * ef, bk, accA, 0, 0, 0);
-                    accM = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        io<T>::ld(&s_q[r * DK + c]) * ef, bk, accM, 0, 0, 0);
-                }
-            }
-        }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int row = 16 * R + 4 * lg + ii, col = 16 * I + li;
-            float a = accA[ii], m = accM[ii];
-            if (diag) {
-                if (col >= row) a = 0.f;
-                if (col > row) m = 0.f;
-            }
-            s_A[row * CP + col] = a;
-            s_M[row * CP + col] = m;
-        }
-    }
-
-    // ---- phase 1b: Qg and KgT fragment blocks (elementwise) ----
-    {
-        constexpr int NBQ = (C / 16) * R_::NKT_DK;      // Qg blocks
-        constexpr int NBK = (DK / 16) * R_::NKT_C;      // KgT blocks
-        u32x4 *qg = reinterpret_cast<u32x4 *>(rec + R_::Qg);
-        u32x4 *kg = reinterpret_cast<u32x4 *>(rec + R_::KgT);
-        for (int idx = tid; idx < (NBQ + NBK) * 64; idx += NT) {
-            const int blk = idx >> 6, l = idx & 63, lli = l & 15, llg = l >> 4;
-            float vals[EPL];
-            if (blk < NBQ) {
-                const int rt = blk / R_::NKT_DK, kt = blk - rt * R_::NKT_DK;
-                const int r = 16 * rt + lli;
-#pragma unroll
-                for (int jj = 0; jj < EPL; ++jj) {
-                    const int c = kt * KT + perm_k<BF>(llg, jj);
-                    vals[jj] = __expf(s_g[r * DK + c]) * io<T>::ld(&s_q[r * DK + c]);
-                }
-                qg[blk * 64 + l] = pack16<BF>(vals);
-            } else {
-                const int b2 = blk - NBQ;
-                const int rt = b2 / R_::NKT_C, kt = b2 - rt * R_::NKT_C;
-                const int ch = 16 * rt + lli;
-                const float gl = s_g[(C - 1) * DK + ch];
-#pragma unroll
-                for (int jj = 0; jj < EPL; ++jj) {
-                    const int tok = kt * KT + perm_k<BF>(llg, jj);
-                    vals[jj] = __expf(gl - s_g[tok * DK + ch]) * io<T>::ld(&s_k[tok * DK + ch]);
-                }
-                kg[b2 * 64 + l] = pack16<BF>(vals);
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 2: wave 0 inverts the four 16x16 diagonal blocks of (I + A); the other
-    //      waves write M in fragment order ----
-    if (wave == 0) {
-        const int R = lane >> 4, jc = lane & 15;      // column jc of T_RR
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
-#pragma unroll
-        for (int r = 1; r < 16; ++r) {
+        {
+            const int c = tid % DK, part = tid / DK;
+            float x[RPP];
             float acc = 0.f;
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc += s_A[(16 * R + r) * CP + 16 * R + m] * x[m];
-            if (r > jc) x[r] = -acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s_T[(R * 16 + r) * 16 + jc] = x[r];
-    } else {
-        constexpr int NBM = (C / 16) * R_::NKT_C;
-        u32x4 *mg = reinterpret_cast<u32x4 *>(rec + R_::M);
-        for (int idx = tid - 64; idx < NBM * 64; idx += NT - 64) {
-            const int blk = idx >> 6, l = idx & 63, lli = l & 15, llg = l >> 4;
-            const int rt = blk / R_::NKT_C, kt = blk - rt * R_::NKT_C;
-            const int r = 16 * rt + lli;
-            float vals[EPL];
-#pragma unroll
-            for (int jj = 0; jj < EPL; ++jj) vals[jj] = s_M[r * CP + kt * KT + perm_k<BF>(llg, jj)];
-            mg[blk * 64 + l] = pack16<BF>(vals);
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 3: blocked forward substitution, Y_R = T_RR (X_R - sum_{I<R} A_RI Y_I),
-    //      for X = gamma.b.k (Y = W~) and X = w.v (Y = U~); one 16-column tile per pass ----
-    {
-        constexpr int NCTW = DK / 16, NCT = DK / 16 + DV / 16;
-        OT *s_W = reinterpret_cast<OT *>(s_q);           // -W~ staging, [C][DK]
-        for (int ctile = wave; ctile < NCT; ctile += NW) {
-            const bool isW = ctile < NCTW;
-            const int ct = isW ? ctile : ctile - NCTW;
-            const int col = 16 * ct + li;
-            f32x4 Y[4];
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                f32x4 Z;
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int r = 16 * R + 4 * lg + ii;
-                    Z[ii] = isW ? __expf(s_g[r * DK + col]) * io<T>::ld(&s_b[r * DK + col]) *
-                                      io<T>::ld(&s_k[r * DK + col])
-                                : io<T>::ld(&s_w[r * DV + col]) * io<T>::ld(&s_v[r * DV + col]);
-                }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int I = 0; I < R; ++I) {
-                    const float *ap = &s_A[(16 * R + li) * CP + 16 * I + 4 * lg];
-                    const f32x4 a = {ap[0], ap[1], ap[2], ap[3]};
-                    if constexpr (BF) acc = mma_k16_bf16(f4_to_b16(a), f4_to_b16(Y[I]), acc);
-                    else acc = mma_k16_f32(a, Y[I], acc);
-                }
-                Z -= acc;
-                const f32x4 t = *reinterpret_cast<const f32x4 *>(&s_T[(R * 16 + li) * 16 + 4 * lg]);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (BF) Y[R] = mma_k16_bf16(f4_to_b16(t), f4_to_b16(Z), zero);
-                else Y[R] = mma_k16_f32(t, Z, zero);
+            for (int rr = 0; rr < RPP; ++rr) {
+                acc += io<T>::ld(&s_la[(part * RPP + rr) * SL + c]);
+                x[rr] = acc;
             }
-            if (!isW) {
-                char *ut = rec + R_::Ut;
+            s_part[part * DK + c] = acc;
+            __syncthreads();
+            float pre = 0.f;
+            for (int pp = 0; pp < part; ++pp) pre += s_part[pp * DK + c];
 #pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    const size_t off = (static_cast<size_t>(ct) * 4 + R) * R_::UT_TILE;
-                    if constexpr (BF) {
-                        reinterpret_cast<u32x2 *>(ut + off)[lane] = f4_to_b16(Y[R]);
-                    } else {
-                        reinterpret_cast<f32x4 *>(ut + off)[lane] = Y[R];
+            for (int rr = 0; rr < RPP; ++rr) s_g[(part * RPP + rr) * SG + c] = x[rr] + pre;
+            // w.v, rounded to the operand type (the rounding its matrix-core use applies),
+            // into the log alpha tile, which is no longer read
+#pragma unroll
+            for (int e = 0; e < RAWW; ++e) {
+                const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
+                float prod[16 / sizeof(T)];
+                if constexpr (BF) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        prod[2 * q4] = bf16_lo(rw[e][q4]) * bf16_lo(rv[e][q4]);
+                        prod[2 * q4 + 1] = bf16_hi(rw[e][q4]) * bf16_hi(rv[e][q4]);
+                    }
+                } else {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        prod[q4] = __uint_as_float(rw[e][q4]) * __uint_as_float(rv[e][q4]);
+                }
+                *reinterpret_cast<u32x4 *>(&s_la[r * SL + cv * VEC]) = pack16<BF>(prod);
+            }
+            __syncthreads();
+            if (has_next) load_raw(nxt);       // next record's raw tiles, in flight from here
+            if (tid < DK)
+                reinterpret_cast<float *>(rec + R_::gC)[tid] = __expf(s_g[(C - 1) * SG + tid]);
+        }
+
+        // ---- phase 1: A^T and M^T blocks (R >= I); zero upper blocks of M ----
+        char *mrec = rec + R_::M;
+        for (int pr = wave; pr < 10; pr += NW) {
+            const int R = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
+            const int I = pr - R * (R + 1) / 2;
+            const bool diag = (R == I);
+            const int refrow = diag ? 16 * R + 7 : 16 * R - 1;
+            const int ri = 16 * I + li;              // A operand: column-side token i
+            const int rr = 16 * R + li;              // B operand: row-side token r
+            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
+#pragma unroll
+            for (int kt = 0; kt < DK / KT; ++kt) {
+                const int c0 = kt * KT + KS * lg;
+                float kb[KS], ka[KS], qa[KS];
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int c = c0 + s;
+                    const float ref = s_g[refrow * SG + c];
+                    const float ec = __expf(ref - s_g[ri * SG + c]);
+                    const float ef = __expf(s_g[rr * SG + c] - ref);
+                    kb[s] = io<T>::ld(&s_k[ri * SK + c]) * ec;
+                    ka[s] = io<T>::ld(&s_b[rr * SK + c]) * io<T>::ld(&s_k[rr * SK + c]) * ef;
+                    qa[s] = io<T>::ld(&s_q[rr * SK + c]) * ef;
+                }
+                if constexpr (BF) {
+                    const u32x4 a = pack16<true>(kb);
+                    accA = mma_k32(a, pack16<true>(ka), accA);
+                    accM = mma_k32(a, pack16<true>(qa), accM);
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        accA = __builtin_amdgcn_mfma_f32_16x16x4f32(kb[s], ka[s], accA, 0, 0, 0);
+                        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(kb[s], qa[s], accM, 0, 0, 0);
                     }
                 }
+            }
+            // lane holds A[r = 16R + li][i = 16I + 4 lg + ii] (and M): fragment order already
+            f32x4 a4, m4;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int il = 4 * lg + ii;
+                a4[ii] = (diag && il >= li) ? 0.f : accA[ii];
+                m4[ii] = (diag && il > li) ? 0.f : accM[ii];
+            }
+            *reinterpret_cast<f32x4 *>(&s_A[lower_blk(R, I) * 256 + 4 * lane]) = a4;
+            if constexpr (BF) {
+                reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)] =
+                    f4_to_b16(m4);
             } else {
-#pragma unroll
-                for (int R = 0; R < 4; ++R)
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii)
-                        io<OT>::st(&s_W[(16 * R + 4 * lg + ii) * DK + col], -Y[R][ii]);
+                reinterpret_cast<f32x4 *>(mrec)[(R * NKC + I) * 64 + lane] = m4;
             }
         }
-    }
-    __syncthreads();
-
-    // ---- phase 4: -W~ in fragment order ----
-    {
-        constexpr int NBW = (C / 16) * R_::NKT_DK;
-        const OT *s_W = reinterpret_cast<const OT *>(s_q);
-        u32x4 *wg = reinterpret_cast<u32x4 *>(rec + R_::Wn);
-        for (int idx = tid; idx < NBW * 64; idx += NT) {
-            const int blk = idx >> 6, l = idx & 63, lli = l & 15, llg = l >> 4;
-            const int rt = blk / R_::NKT_DK, kt = blk - rt * R_::NKT_DK;
-            const int r = 16 * rt + lli;
-            float vals[EPL];
-#pragma unroll
-            for (int jj = 0; jj < EPL; ++jj)
-                vals[jj] = io<OT>::ld(&s_W[r * DK + kt * KT + perm_k<BF>(llg, jj)]);
-            wg[blk * 64 + l] = pack16<BF>(vals);
+        for (int u = wave; u < 6; u += NW) {
+            // (R, I) with I > R, in the order (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+            const int R2 = u < 3 ? 0 : (u < 5 ? 1 : 2);
+            const int I2 = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+            if constexpr (BF) {
+                const u32x2 z = {0u, 0u};
+                reinterpret_cast<u32x2 *>(mrec)[(((R2 * NKC + (I2 >> 1)) * 64 + lane) << 1) + (I2 & 1)] = z;
+            } else {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                reinterpret_cast<f32x4 *>(mrec)[(R2 * NKC + I2) * 64 + lane] = z;
+            }
         }
+        __syncthreads();
+
+        // ---- phase 2a: diagonal inverses (wave 0) || Qg and KgT (waves 1-7) ----
+        if (wave == 0) {
+            const int R = lane >> 4, jc = lane & 15;      // column jc of T_RR
+            const float *Ab = &s_A[lower_blk(R, R) * 256];
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+#pragma unroll
+            for (int r = 1; r < 16; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) acc += Ab[frag_idx(r, m)] * x[m];
+                if (r > jc) x[r] = -acc;
+            }
+            float *Tb = &s_T[lower_blk(R, R) * 256];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tb[frag_idx(r, jc)] = x[r];
+        } else {
+            constexpr int NBQ = (C / 16) * R_::NKT_DK;      // Qg blocks
+            constexpr int NBK = (DK / 16) * R_::NKT_C;      // KgT blocks
+            constexpr int EPL = Op<BF>::EPL;
+            u32x4 *qg = reinterpret_cast<u32x4 *>(rec + R_::Qg);
+            u32x4 *kg = reinterpret_cast<u32x4 *>(rec + R_::KgT);
+            for (int idx = tid - 64; idx < (NBQ + NBK) * 64; idx += NT - 64) {
+                const int blk = idx >> 6, l = idx & 63, lli = l & 15, llg = l >> 4;
+                float vals[EPL];
+                if (blk < NBQ) {
+                    const int rt = blk / R_::NKT_DK, kt = blk - rt * R_::NKT_DK;
+                    const int r = 16 * rt + lli;
+#pragma unroll
+                    for (int jj = 0; jj < EPL; ++jj) {
+                        const int c = kt * KT + perm_k<BF>(llg, jj);
+                        vals[jj] = __expf(s_g[r * SG + c]) * io<T>::ld(&s_q[r * SK + c]);
+                    }
+                    qg[blk * 64 + l] = pack16<BF>(vals);
+                } else {
+                    const int b2 = blk - NBQ;
+                    const int rt = b2 / R_::NKT_C, kt = b2 - rt * R_::NKT_C;
+                    const int ch = 16 * rt + lli;
+                    const float gl = s_g[(C - 1) * SG + ch];
+#pragma unroll
+                    for (int jj = 0; jj < EPL; ++jj) {
+                        const int tok = kt * KT + perm_k<BF>(llg, jj);
+                        vals[jj] = __expf(gl - s_g[tok * SG + ch]) * io<T>::ld(&s_k[tok * SK + ch]);
+                    }
+                    kg[b2 * 64 + l] = pack16<BF>(vals);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- phase 2b: off-diagonal blocks of T by levels d = R - I ----
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+            if (wave < 4 - d) {
+                const int R = d + wave, I = R - d;
+                f32x4 P = {0.f, 0.f, 0.f, 0.f};
+                for (int m = I; m < R; ++m) {
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(&s_A[lower_blk(R, m) * 256 + 4 * lane]);
+                    const float *Tm = &s_T[lower_blk(m, I) * 256];
+                    f32x4 bT;                      // B operand: T_mI[4 lg + s][li]
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) bT[s] = Tm[frag_idx(4 * lg + s, li)];
+                    P = mma_k16_f32(a, bT, P);
+                }
+                const f32x4 tRR = *reinterpret_cast<const f32x4 *>(&s_T[lower_blk(R, R) * 256 + 4 * lane]);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 Tn = mma_k16_f32(tRR, P, zero);   // lane: (T_RR P)[4 lg + ii][li]
+                float *Tb = &s_T[lower_blk(R, I) * 256];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) Tb[frag_idx(4 * lg + ii, li)] = -Tn[ii];
+            }
+            __syncthreads();
+        }
+
+        // ---- phase 3: W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) ----
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const bool isW = which == 0;
+            if (wave >= (isW ? DK : DV) / 16) continue;
+            const int ct = wave;
+            const int c = 16 * ct + li;
+            float xv[NKTC][KS];
+#pragma unroll
+            for (int kt = 0; kt < NKTC; ++kt)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int tok = kt * KT + KS * lg + s;
+                    if (isW) {
+                        xv[kt][s] = __expf(s_g[tok * SG + c]) * io<T>::ld(&s_b[tok * SK + c]) *
+                                    io<T>::ld(&s_k[tok * SK + c]);
+                    } else {
+                        xv[kt][s] = io<T>::ld(&s_la[tok * SL + c]);     // w.v
+                    }
+                }
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < NKTC; ++kt) {
+                    if (kt * KT > 16 * R + 15) break;
+                    float tv[KS];                  // T[16R + li][kt*KT + KS*lg + s]
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        const int tok = kt * KT + KS * lg + s;
+                        const int I = tok >> 4;
+                        tv[s] = (I <= R) ? s_T[lower_blk(R, I) * 256 + frag_idx(li, tok & 15)] : 0.f;
+                    }
+                    if constexpr (BF) {
+                        if (isW) acc = mma_k32(pack16<true>(xv[kt]), pack16<true>(tv), acc);
+                        else acc = mma_k32(pack16<true>(tv), pack16<true>(xv[kt]), acc);
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s)
+                            acc = isW ? __builtin_amdgcn_mfma_f32_16x16x4f32(xv[kt][s], tv[s], acc, 0, 0, 0)
+                                      : __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s], xv[kt][s], acc, 0, 0, 0);
+                    }
+                }
+                if (isW) {
+                    // lane: W~[16R + li][16 ct + 4 lg + ii] -> -W~ in K2's fragment order
+                    const f32x4 wn = -acc;
+                    char *wr = rec + R_::Wn;
+                    if constexpr (BF) {
+                        reinterpret_cast<u32x2 *>(wr)[(((R * R_::NKT_DK + (ct >> 1)) * 64 + lane) << 1) +
+                                                      (ct & 1)] = f4_to_b16(wn);
+                    } else {
+                        reinterpret_cast<f32x4 *>(wr)[(R * R_::NKT_DK + ct) * 64 + lane] = wn;
+                    }
+                } else {
+                    // lane: U~[16R + 4 lg + ii][16 ct + li], an output tile (D layout)
+                    char *ut = rec + R_::Ut + (static_cast<size_t>(ct) * 4 + R) * R_::UT_TILE;
+                    if constexpr (BF) reinterpret_cast<u32x2 *>(ut)[lane] = f4_to_b16(acc);
+                    else reinterpret_cast<f32x4 *>(ut)[lane] = acc;
+                }
+            }
+        }
+        __syncthreads();                       // LDS is reused by the next record
+        cur = nxt;
     }
 }
 
 // ---------------------------------------------------------------------------------------
 // K2: inter-chunk state pass. Each wave owns 16 columns of S (all d_k rows) as DK/16
-// output tiles in fp32 registers and walks the chunks of its sequence in order.
+// output tiles in fp32 registers and walks the chunks of its sequence in order. The waves
+// of a workgroup share one (sequence, head); each chunk's workspace record (the operands
+// common to all columns plus each wave's U~ slice) is copied into LDS by direct
+// global-to-LDS loads one chunk ahead, into a double buffer, so the matrix cores never wait
+// on memory latency except at the first chunk.
 // ---------------------------------------------------------------------------------------
-template <typename T, bool BF, int DK, int DV>
-__global__ __launch_bounds__(256) void chunk_state_kernel(ChunkParams p) {
+template <int DK, int DV, bool BF>
+struct StageLayout {
     using R_ = Rec<DK, DV, BF>;
+    static constexpr size_t SHARED = R_::Ut;                 // Wn, Qg, KgT, M
+    static constexpr size_t GCB = DK * 4;                    // gamma_C
+    static constexpr size_t UTS = 4 * R_::UT_TILE;           // one wave's U~ slice
+    __host__ __device__ static constexpr size_t buffer_bytes(int nw) { return SHARED + GCB + nw * UTS; }
+    static_assert(2 * (SHARED + GCB + UTS) <= 160 * 1024, "double buffer must fit in LDS");
+};
+
+__device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+}
+
+template <typename T, bool BF, int DK, int DV>
+__global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
+    using R_ = Rec<DK, DV, BF>;
+    using SL = StageLayout<DK, DV, BF>;
     constexpr int C = kChunk, RT = DK / 16;
+    constexpr int KT = Op<BF>::KT;
     constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
+    const size_t BUF = SL::buffer_bytes(nw);
 
     // XCD-aware decode: the column slices of one (sequence, head) pair share an XCD, so
     // its workspace records are fetched into one L2.
@@ -460,6 +578,19 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkParams p) {
     }
     const int nchunks = static_cast<int>((end - start + C - 1) / C);
 
+    // copy chunk c's record (shared part, gamma_C, this wave's U~ slice) into buffer `dst`
+    auto issue = [&](int c, char *dst) {
+        const char *rec = p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
+        for (int blk = wave; blk < static_cast<int>(SL::SHARED / 1024); blk += nw)
+            dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
+        if (wave == nw - 1 && lane < static_cast<int>(SL::GCB / 16))
+            dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
+        const char *us = rec + R_::Ut + static_cast<size_t>(ct) * SL::UTS;
+        char *ud = dst + SL::SHARED + SL::GCB + wave * SL::UTS;
+        for (int b = 0; b < static_cast<int>(SL::UTS / 1024); ++b)
+            dma16(us + b * 1024 + lane * 16, ud + b * 1024);
+    };
+
     f32x4 S[RT];
     const size_t sbase = static_cast<size_t>(pair) * DK * DV;
 #pragma unroll
@@ -470,16 +601,37 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkParams p) {
                              : 0.f;
 
     T *op = static_cast<T *>(p.o);
+    // o of chunk c is stored during chunk c + 1, after that chunk's copies are issued, so the
+    // wait at the top of each chunk only covers memory operations issued a chunk earlier.
+    f32x4 Oprev[4];
+    int64_t t0prev = 0;
+    int Lprev = 0;
+    auto store_o = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int row = 16 * rt + 4 * lg + ii;
+                if (row < Lprev)
+                    io<T>::st(op + (static_cast<size_t>(t0prev + row) * p.h_v + h) * DV + col,
+                              Oprev[rt][ii]);
+            }
+    };
+    if (nchunks > 0) issue(0, smem);
     for (int c = 0; c < nchunks; ++c) {
-        const char *rec = p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
-        const u32x4 *wn = reinterpret_cast<const u32x4 *>(rec + R_::Wn);
-        const u32x4 *qg = reinterpret_cast<const u32x4 *>(rec + R_::Qg);
-        const u32x4 *kg = reinterpret_cast<const u32x4 *>(rec + R_::KgT);
-        const u32x4 *mq = reinterpret_cast<const u32x4 *>(rec + R_::M);
-        const char *ut = rec + R_::Ut;
-        const float *gc = reinterpret_cast<const float *>(rec + R_::gC);
+        char *cur = smem + (c & 1) * BUF;
+        __builtin_amdgcn_s_waitcnt(0);      // this wave's copies for chunk c have landed
+        __syncthreads();                    // ... and every wave's; chunk c-1 fully consumed
+        if (c + 1 < nchunks) issue(c + 1, smem + ((c + 1) & 1) * BUF);
+        if (c > 0) store_o();
 
-        // B operands from the state (rows = d_k)
+        const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur + R_::Wn);
+        const u32x4 *qg = reinterpret_cast<const u32x4 *>(cur + R_::Qg);
+        const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + R_::KgT);
+        const u32x4 *mq = reinterpret_cast<const u32x4 *>(cur + R_::M);
+        const float *gc = reinterpret_cast<const float *>(cur + SL::SHARED);
+        const char *ut = cur + SL::SHARED + SL::GCB + wave * SL::UTS;
+
         u32x4 SB[BF ? NKD : 1];
         if constexpr (BF) {
 #pragma unroll
@@ -489,12 +641,11 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkParams p) {
         f32x4 U[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            const size_t toff = (static_cast<size_t>(ct) * 4 + rt) * R_::UT_TILE;
             if constexpr (BF) {
-                const u32x2 u = reinterpret_cast<const u32x2 *>(ut + toff)[lane];
+                const u32x2 u = reinterpret_cast<const u32x2 *>(ut + rt * R_::UT_TILE)[lane];
                 U[rt] = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
             } else {
-                U[rt] = reinterpret_cast<const f32x4 *>(ut + toff)[lane];
+                U[rt] = reinterpret_cast<const f32x4 *>(ut + rt * R_::UT_TILE)[lane];
             }
 #pragma unroll
             for (int kt = 0; kt < NKD; ++kt) {
@@ -508,7 +659,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkParams p) {
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) UB[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
         }
-        // O = Qg S + M U
+        // O = Qg S + M U   (M is lower triangular: skip k tiles above the diagonal)
         f32x4 O[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -521,6 +672,7 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkParams p) {
             }
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) {
+                if (kt * KT > 16 * rt + 15) break;
                 const u32x4 a = mq[(rt * NKC + kt) * 64 + lane];
                 if constexpr (BF) O[rt] = mma_k32(a, UB[kt], O[rt]);
                 else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a), U[kt], O[rt]);
@@ -538,19 +690,13 @@ __global__ __launch_bounds__(256) void chunk_state_kernel(ChunkParams p) {
                 else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a), U[kt], S[rt]);
             }
         }
-        // o rows of this chunk (identity padding rows are skipped)
-        const int64_t t0 = start + static_cast<int64_t>(c) * C;
-        const int L = static_cast<int>(min<int64_t>(C, end - t0));
+        // o rows of this chunk (identity padding rows are skipped), stored next iteration
+        t0prev = start + static_cast<int64_t>(c) * C;
+        Lprev = static_cast<int>(min<int64_t>(C, end - t0prev));
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int row = 16 * rt + 4 * lg + ii;
-                if (row < L)
-                    io<T>::st(op + (static_cast<size_t>(t0 + row) * p.h_v + h) * DV + col,
-                              O[rt][ii]);
-            }
+        for (int rt = 0; rt < 4; ++rt) Oprev[rt] = O[rt];
     }
+    if (nchunks > 0) store_o();
     if (p.S_T) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -590,6 +736,22 @@ bool chunk_dims_built(int d_k, int d_v, bool bf16) {
     return d_k == 64 && d_v == 64;
 }
 
+// Compute units of the current device (the persistent prep kernel runs one workgroup per
+// CU). Queried once per device and cached.
+static int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 template <typename T, bool BF, int DK, int DV>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     static_assert(Rec<DK, DV, BF>::bytes > 0, "");
@@ -611,21 +773,30 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     }
     const int64_t nchunks = chunk_upper_bound(a.batch, a.seqlen, N, packed);
     if (nchunks > 0) {
-        hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV>), dim3(nchunks, a.h_v), dim3(512),
-                           0, st, p);
+        const int64_t items = nchunks * a.h_v;
+        const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
+        hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV>), dim3(grid), dim3(512), 0, st, p);
     }
-    // K2: waves per workgroup chosen so that small batches still spread over the CUs.
+    // K2: waves per workgroup. More waves share one copy of each chunk's operands in LDS;
+    // fewer spread a small batch over more CUs.
     int nw = 1;
     const int ctiles = DV / 16;
-    while (nw < 4 && ctiles % (2 * nw) == 0 && static_cast<int64_t>(p.num_pairs) * ctiles /
-                                                   (2 * nw) >= 1024)
+    constexpr size_t kMaxLds = 160 * 1024;          // LDS per workgroup on gfx950
+    while (nw < 8 && ctiles % (2 * nw) == 0 &&
+           static_cast<int64_t>(p.num_pairs) * ctiles / (2 * nw) >= 256 &&
+           2 * StageLayout<DK, DV, BF>::buffer_bytes(2 * nw) <= kMaxLds)
         nw *= 2;
     p.nslices = ctiles / nw;
+    const size_t lds = 2 * StageLayout<DK, DV, BF>::buffer_bytes(nw);
+    auto kern = chunk_state_kernel<T, BF, DK, DV>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
     const int64_t pairs8 = (static_cast<int64_t>(p.num_pairs) + 7) / 8 * 8;
     const int64_t blocks = pairs8 * p.nslices;
     if (blocks > 0) {
-        hipLaunchKernelGGL((chunk_state_kernel<T, BF, DK, DV>), dim3(blocks), dim3(64 * nw), 0,
-                           st, p);
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * nw), lds, st, p);
     }
     return hipGetLastError();
 }

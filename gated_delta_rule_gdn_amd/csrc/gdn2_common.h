@@ -25,6 +25,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 template <typename T> struct io;
 
 template <> struct io<float> {
+    static __device__ __forceinline__ float val(float x) { return x; }
     static __device__ __forceinline__ float ld(const float *p) { return *p; }
     static __device__ __forceinline__ void st(float *p, float x) { *p = x; }
     static __device__ __forceinline__ f32x4 ld4(const float *p) {
@@ -36,6 +37,7 @@ template <> struct io<float> {
 };
 
 template <> struct io<bf16_t> {
+    static __device__ __forceinline__ float val(bf16_t x) { return bf16_to_f32(x.bits); }
     static __device__ __forceinline__ float ld(const bf16_t *p) { return bf16_to_f32(p->bits); }
     static __device__ __forceinline__ void st(bf16_t *p, float x) { p->bits = f32_to_bf16_bits(x); }
     static __device__ __forceinline__ f32x4 ld4(const bf16_t *p) {
