@@ -521,12 +521,17 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// K2: inter-chunk state pass. Each wave owns 16 columns of S (all d_k rows) as DK/16
+// K2: inter-chunk state pass. Each compute wave owns 16 columns of S (all d_k rows) as DK/16
 // output tiles in fp32 registers and walks the chunks of its sequence in order. The waves
-// of a workgroup share one (sequence, head); each chunk's workspace record (the operands
-// common to all columns plus each wave's U~ slice) is copied into LDS by direct
-// global-to-LDS loads one chunk ahead, into a double buffer, so the matrix cores never wait
-// on memory latency except at the first chunk.
+// of a workgroup share one (sequence, head). Per chunk:
+//   * the record (operands common to all columns, gamma_C, each wave's U~ slice) is copied
+//     into a double-buffered LDS stage one chunk ahead by kLoaders extra loader waves with
+//     direct global-to-LDS loads: one wave cannot keep enough copies in flight to move a
+//     record per chunk step, several can. Loaders wait for their own copies, then meet
+//     the compute waves at the per-chunk barrier (a plain s_barrier, no memory fence);
+//   * each matrix-core phase first reads all its A fragments from LDS, then issues the
+//     products with the independent accumulator chains interleaved;
+//   * o of a chunk is transposed through LDS and stored with 16-byte writes one chunk later.
 // ---------------------------------------------------------------------------------------
 template <int DK, int DV, bool BF>
 struct StageLayout {
@@ -534,13 +539,35 @@ struct StageLayout {
     static constexpr size_t SHARED = R_::Ut;                 // Wn, Qg, KgT, M
     static constexpr size_t GCB = DK * 4;                    // gamma_C
     static constexpr size_t UTS = 4 * R_::UT_TILE;           // one wave's U~ slice
-    __host__ __device__ static constexpr size_t buffer_bytes(int nw) { return SHARED + GCB + nw * UTS; }
-    static_assert(2 * (SHARED + GCB + UTS) <= 160 * 1024, "double buffer must fit in LDS");
+    static constexpr size_t OTILE = kChunk * 16 * 4;         // one wave's o transpose area
+    __host__ __device__ static constexpr size_t buffer_bytes(int nw) {
+        return SHARED + GCB + nw * UTS;
+    }
+    __host__ __device__ static constexpr size_t lds_bytes(int nw) {
+        return 2 * buffer_bytes(nw) + nw * OTILE;
+    }
+    static_assert(2 * (SHARED + GCB + UTS) + OTILE <= 160 * 1024,
+                  "double buffer must fit in LDS");
 };
 
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
+
+// s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt with lgkmcnt(0) only
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier without a memory fence (so it never waits for outstanding loads). The
+// empty asm statements keep the compiler from moving memory accesses across it; every wave
+// waits for its own copies with wait_vmem() before arriving when it needs them.
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kLoaders = 4;           // loader waves per state-pass workgroup
 
 template <typename T, bool BF, int DK, int DV>
 __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
@@ -550,10 +577,11 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
     constexpr int KT = Op<BF>::KT;
     constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int nw = blockDim.x >> 6;
+    const int nw = (blockDim.x >> 6) - kLoaders;   // compute waves; the rest load
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const size_t BUF = SL::buffer_bytes(nw);
+    char *otile_base = smem + 2 * BUF;
 
     // XCD-aware decode: the column slices of one (sequence, head) pair share an XCD, so
     // its workspace records are fetched into one L2.
@@ -562,8 +590,6 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
     const int pair = (rest / p.nslices) * 8 + xcd;
     if (pair >= p.num_pairs) return;
     const int n = pair / p.h_v, h = pair - n * p.h_v;
-    const int ct = slice * nw + wave;
-    const int col = 16 * ct + li;
 
     int64_t start, end;
     int cbase;
@@ -577,20 +603,37 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
         cbase = p.map[n];
     }
     const int nchunks = static_cast<int>((end - start + C - 1) / C);
-
-    // copy chunk c's record (shared part, gamma_C, this wave's U~ slice) into buffer `dst`
-    auto issue = [&](int c, char *dst) {
-        const char *rec = p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
-        for (int blk = wave; blk < static_cast<int>(SL::SHARED / 1024); blk += nw)
-            dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
-        if (wave == nw - 1 && lane < static_cast<int>(SL::GCB / 16))
-            dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
-        const char *us = rec + R_::Ut + static_cast<size_t>(ct) * SL::UTS;
-        char *ud = dst + SL::SHARED + SL::GCB + wave * SL::UTS;
-        for (int b = 0; b < static_cast<int>(SL::UTS / 1024); ++b)
-            dma16(us + b * 1024 + lane * 16, ud + b * 1024);
+    auto record = [&](int c) {
+        return p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
     };
 
+    if (wave >= nw) {
+        // ---- loader waves: copy chunk c + 1 into the other stage during chunk c
+        const int ldr = wave - nw;
+        auto issue = [&](int c, char *dst) {
+            const char *rec = record(c);
+            for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += kLoaders)
+                dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
+            if (ldr == kLoaders - 1 && lane < static_cast<int>(SL::GCB / 16))
+                dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
+            // the compute waves' U~ slices: column tiles slice*nw .. slice*nw + nw - 1 are
+            // contiguous in the record, and so are their stage slots
+            const char *us = rec + R_::Ut + static_cast<size_t>(slice) * nw * SL::UTS;
+            char *ud = dst + SL::SHARED + SL::GCB;
+            for (int b = ldr; b < static_cast<int>(nw * SL::UTS / 1024); b += kLoaders)
+                dma16(us + b * 1024 + lane * 16, ud + b * 1024);
+        };
+        if (nchunks > 0) issue(0, smem);
+        for (int c = 0; c < nchunks; ++c) {
+            wait_vmem();                    // this loader's copies for chunk c have landed
+            raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
+            if (c + 1 < nchunks) issue(c + 1, smem + ((c + 1) & 1) * BUF);
+        }
+        return;
+    }
+
+    const int ct = slice * nw + wave;
+    const int col = 16 * ct + li;
     f32x4 S[RT];
     const size_t sbase = static_cast<size_t>(pair) * DK * DV;
 #pragma unroll
@@ -600,29 +643,27 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
             S[rt][ii] = p.S0 ? p.S0[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col]
                              : 0.f;
 
+    // o of chunk c is written to this wave's LDS tile at the end of chunk c and stored to
+    // memory during chunk c + 1 as 16-byte rows.
     T *op = static_cast<T *>(p.o);
-    // o of chunk c is stored during chunk c + 1, after that chunk's copies are issued, so the
-    // wait at the top of each chunk only covers memory operations issued a chunk earlier.
-    f32x4 Oprev[4];
+    T *otile = reinterpret_cast<T *>(otile_base + wave * SL::OTILE);
+    constexpr int OPR = 16 * sizeof(T) / 16;        // 16-byte pieces per 16-column row
     int64_t t0prev = 0;
     int Lprev = 0;
     auto store_o = [&]() {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int row = 16 * rt + 4 * lg + ii;
-                if (row < Lprev)
-                    io<T>::st(op + (static_cast<size_t>(t0prev + row) * p.h_v + h) * DV + col,
-                              Oprev[rt][ii]);
-            }
+        for (int e = 0; e < C * OPR / 64; ++e) {
+            const int pidx = lane + 64 * e, row = pidx / OPR, piece = pidx - row * OPR;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(&otile[row * 16 + piece * (16 / sizeof(T))]);
+            if (row < Lprev)
+                *reinterpret_cast<u32x4 *>(op + (static_cast<size_t>(t0prev + row) * p.h_v + h) * DV +
+                                           16 * ct + piece * (16 / sizeof(T))) = v;
+        }
     };
-    if (nchunks > 0) issue(0, smem);
+
     for (int c = 0; c < nchunks; ++c) {
         char *cur = smem + (c & 1) * BUF;
-        __builtin_amdgcn_s_waitcnt(0);      // this wave's copies for chunk c have landed
-        __syncthreads();                    // ... and every wave's; chunk c-1 fully consumed
-        if (c + 1 < nchunks) issue(c + 1, smem + ((c + 1) & 1) * BUF);
+        raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
         if (c > 0) store_o();
 
         const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur + R_::Wn);
@@ -639,64 +680,98 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
         }
         // U = U~ + Wn S
         f32x4 U[4];
+        {
+            u32x4 a[4][NKD];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            if constexpr (BF) {
-                const u32x2 u = reinterpret_cast<const u32x2 *>(ut + rt * R_::UT_TILE)[lane];
-                U[rt] = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
-            } else {
-                U[rt] = reinterpret_cast<const f32x4 *>(ut + rt * R_::UT_TILE)[lane];
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int kt = 0; kt < NKD; ++kt) a[rt][kt] = wn[(rt * NKD + kt) * 64 + lane];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if constexpr (BF) {
+                    const u32x2 u = reinterpret_cast<const u32x2 *>(ut + rt * R_::UT_TILE)[lane];
+                    U[rt] = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+                } else {
+                    U[rt] = reinterpret_cast<const f32x4 *>(ut + rt * R_::UT_TILE)[lane];
+                }
             }
 #pragma unroll
-            for (int kt = 0; kt < NKD; ++kt) {
-                const u32x4 a = wn[(rt * NKD + kt) * 64 + lane];
-                if constexpr (BF) U[rt] = mma_k32(a, SB[kt], U[rt]);
-                else U[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a), S[kt], U[rt]);
-            }
+            for (int kt = 0; kt < NKD; ++kt)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    if constexpr (BF) U[rt] = mma_k32(a[rt][kt], SB[kt], U[rt]);
+                    else U[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a[rt][kt]), S[kt], U[rt]);
+                }
         }
         u32x4 UB[BF ? NKC : 1];
         if constexpr (BF) {
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) UB[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
         }
-        // O = Qg S + M U   (M is lower triangular: skip k tiles above the diagonal)
+        // O = Qg S + M U   (M is lower triangular: k tiles above the diagonal are skipped)
         f32x4 O[4];
+        {
+            u32x4 a[4][NKD], m[4][NKC];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
-            for (int kt = 0; kt < NKD; ++kt) {
-                const u32x4 a = qg[(rt * NKD + kt) * 64 + lane];
-                if constexpr (BF) O[rt] = mma_k32(a, SB[kt], O[rt]);
-                else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a), S[kt], O[rt]);
+                for (int kt = 0; kt < NKD; ++kt) a[rt][kt] = qg[(rt * NKD + kt) * 64 + lane];
+#pragma unroll
+                for (int kt = 0; kt < NKC; ++kt)
+                    if (kt * KT <= 16 * rt + 15) m[rt][kt] = mq[(rt * NKC + kt) * 64 + lane];
             }
 #pragma unroll
-            for (int kt = 0; kt < NKC; ++kt) {
-                if (kt * KT > 16 * rt + 15) break;
-                const u32x4 a = mq[(rt * NKC + kt) * 64 + lane];
-                if constexpr (BF) O[rt] = mma_k32(a, UB[kt], O[rt]);
-                else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a), U[kt], O[rt]);
-            }
+            for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < NKD; ++kt)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    if constexpr (BF) O[rt] = mma_k32(a[rt][kt], SB[kt], O[rt]);
+                    else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a[rt][kt]), S[kt], O[rt]);
+                }
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    if (kt * KT > 16 * rt + 15) continue;
+                    if constexpr (BF) O[rt] = mma_k32(m[rt][kt], UB[kt], O[rt]);
+                    else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, m[rt][kt]), U[kt], O[rt]);
+                }
         }
         // S = gamma_C S + KgT U
+        {
+            u32x4 a[RT][NKC];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
-            S[rt] *= g4;
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int kt = 0; kt < NKC; ++kt) {
-                const u32x4 a = kg[(rt * NKC + kt) * 64 + lane];
-                if constexpr (BF) S[rt] = mma_k32(a, UB[kt], S[rt]);
-                else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a), U[kt], S[rt]);
+                for (int kt = 0; kt < NKC; ++kt) a[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
+                S[rt] *= g4;
             }
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    if constexpr (BF) S[rt] = mma_k32(a[rt][kt], UB[kt], S[rt]);
+                    else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a[rt][kt]), U[kt], S[rt]);
+                }
         }
-        // o rows of this chunk (identity padding rows are skipped), stored next iteration
+        // o rows of this chunk into the wave's LDS tile (row-major [C][16]); stored next chunk
+        wait_lds();
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                io<T>::st(&otile[(16 * rt + 4 * lg + ii) * 16 + li], O[rt][ii]);
         t0prev = start + static_cast<int64_t>(c) * C;
         Lprev = static_cast<int>(min<int64_t>(C, end - t0prev));
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) Oprev[rt] = O[rt];
     }
-    if (nchunks > 0) store_o();
+    if (nchunks > 0) {
+        wait_lds();
+        store_o();
+    }
     if (p.S_T) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -777,17 +852,18 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
         hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV>), dim3(grid), dim3(512), 0, st, p);
     }
-    // K2: waves per workgroup. More waves share one copy of each chunk's operands in LDS;
-    // fewer spread a small batch over more CUs.
+    // K2: compute waves per workgroup (plus one prefetch wave). More waves share one copy of
+    // each chunk's operands in LDS; fewer spread a small batch over more CUs.
+    using SLy = StageLayout<DK, DV, BF>;
+    constexpr size_t kMaxLds = 160 * 1024;          // LDS per workgroup on gfx950
     int nw = 1;
     const int ctiles = DV / 16;
-    constexpr size_t kMaxLds = 160 * 1024;          // LDS per workgroup on gfx950
-    while (nw < 8 && ctiles % (2 * nw) == 0 &&
+    while (nw < 4 && ctiles % (2 * nw) == 0 &&
            static_cast<int64_t>(p.num_pairs) * ctiles / (2 * nw) >= 256 &&
-           2 * StageLayout<DK, DV, BF>::buffer_bytes(2 * nw) <= kMaxLds)
+           SLy::lds_bytes(2 * nw) <= kMaxLds)
         nw *= 2;
     p.nslices = ctiles / nw;
-    const size_t lds = 2 * StageLayout<DK, DV, BF>::buffer_bytes(nw);
+    const size_t lds = SLy::lds_bytes(nw);
     auto kern = chunk_state_kernel<T, BF, DK, DV>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -796,7 +872,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     const int64_t pairs8 = (static_cast<int64_t>(p.num_pairs) + 7) / 8 * 8;
     const int64_t blocks = pairs8 * p.nslices;
     if (blocks > 0) {
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * nw), lds, st, p);
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (nw + kLoaders)), lds, st, p);
     }
     return hipGetLastError();
 }
