@@ -141,6 +141,58 @@ def bench_decode(seed=3):
     return wl, t_step
 
 
+def bench_chunk_workload(wl, steps, warmup, seed):
+    """Warm back-to-back timing of one chunk-forward workload (inputs drawn on the GPU)."""
+    x = inputs.chunk_inputs_device(wl, seed)
+    B, T = x["q"].shape[:2]
+    N = x["num_seqs"]
+    ws = torch.empty(g.chunk_fwd_workspace_bytes(B, T, wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.dtype,
+                                                 num_seqs=N if x["cu_seqlens"] is not None else 0),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, T, wl.h_v, wl.d_v, dtype=wl.dtype, device="cuda")
+    S_T = torch.empty(N, wl.h_v, wl.d_k, wl.d_v, dtype=torch.float32, device="cuda")
+
+    def call():
+        g.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S0=x["S0"],
+                    cu_seqlens=x["cu_seqlens"], workspace=ws, out=o, final_state=S_T)
+
+    for _ in range(warmup):
+        call()
+    t = time_region(call, steps, torch.cuda.current_stream())
+    nbytes, flops = chunk_alg(wl, B * T, N)
+    res = {"workload": wl.name, "tokens": B * T, "us_per_call": t * 1e6,
+           "tokens_per_s": B * T / t, "alg_bytes": nbytes, "alg_flops": flops,
+           "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
+           "mfma_frac_bf16": flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+    del x, ws, o, S_T
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode_large_state(seed=4, steps=32):
+    """Decode with 128 sequences (403 MB of state, more than the 256 MB MALL)."""
+    wl = inputs.DecodeWorkload("decode_f32_n128_hv48_hk16_d128", torch.float32, 128, 16, 48,
+                               128, 128, steps=steps)
+    x = inputs.decode_inputs_device(wl, seed, steps)
+    S = x["S"]
+    o = torch.empty(steps, wl.num_seqs, wl.h_v, wl.d_v, device="cuda")
+
+    def run_all():
+        for t in range(steps):
+            g.recurrent_step(x["q"][t], x["k"][t], x["v"][t], x["log_alpha"][t], x["b"][t],
+                             x["w"][t], S, out=o[t])
+
+    run_all()
+    t_step = time_region(run_all, 1, torch.cuda.current_stream()) / steps
+    nbytes, st, _ = decode_alg(wl)
+    res = {"workload": wl.name, "steps": steps, "us_per_step": t_step * 1e6,
+           "state_GBps": st / t_step / 1e9, "total_GBps": nbytes / t_step / 1e9,
+           "hbm_frac": nbytes / t_step / 1e9 / HBM_PEAK_GBPS}
+    del x, S, o
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_chunk(wl, x, gpu_out):
     """fp64 oracle on the whole timed workload (16 independent head pairs)."""
     import oracle
@@ -193,13 +245,41 @@ def cpu_baseline_decode(wl, pairs=48):
                       f"{dt:.2f} s wall, scaled to all states"}
 
 
+def profile_driver():
+    wl = inputs.CHUNK_BF16_T4096
+    x = inputs.chunk_inputs(wl, seed=1002)
+    d = {n: x[n].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")}
+    for _ in range(5):
+        g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=d["S0"])
+    torch.cuda.synchronize()
+    dw = inputs.DECODE_F32
+    y = inputs.decode_inputs(dw, seed=3, steps=1)
+    S = y["S"].cuda()
+    yy = {n: y[n][0].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    for _ in range(20):
+        g.recurrent_step(yy["q"], yy["k"], yy["v"], yy["log_alpha"], yy["b"], yy["w"], S)
+    src = torch.empty(1 << 26, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile driver done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the timing of the other chunk workloads and the decode control")
     ap.add_argument("--only", choices=["chunk", "decode", "all"], default="all")
+    ap.add_argument("--profile-driver", action="store_true",
+                    help="short fixed sequence for hardware-counter runs: 5 chunk forwards, "
+                         "20 decode steps and 3 copies of 256 MiB (the copy calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -210,6 +290,9 @@ def main():
         sys.exit(2)
     g.lib()
     torch.cuda.set_device(0)
+    if args.profile_driver:
+        profile_driver()
+        return
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic"}
@@ -252,11 +335,18 @@ def main():
                             "kernel": "decode_step_kernel", "alg_bytes": dbytes}}
         if not args.no_cpu_baseline:
             dec["cpu_baseline"] = cpu_baseline_decode(dwl)
+        if not args.no_other_workloads:
+            dec["large_state_control"] = bench_decode_large_state()
         out["decode"] = dec
         if "value" not in out:
             out.update({"value": dwl.num_seqs / t_step, "unit": "tokens/s",
                         "ms_per_step": t_step * 1e3, "dtype": "f32",
                         "config": {"workload": dwl.name}, "roofline": dec["roofline"]})
+    if args.only in ("chunk", "all") and not args.no_other_workloads:
+        out["other_chunk_workloads"] = [
+            bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed)
+            for wl, seed in ((inputs.CHUNK_F32_SMALL, 2000), (inputs.CHUNK_BF16_B8, 2001),
+                             (inputs.VARLEN_BF16, 2004))]
     print(json.dumps(out))
 
 

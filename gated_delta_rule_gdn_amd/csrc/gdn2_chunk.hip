@@ -17,22 +17,22 @@
 //
 // Kernels:
 //   K0 chunk_map_kernel    packed batches: chunk offsets per sequence (no host sync).
-//   K1 chunk_prep_kernel   one workgroup per (chunk, value head), fully parallel: the
-//                          cumulative log decay, A and M on the matrix cores, T = (I + A)^{-1}
-//                          by 16x16 blocks (diagonal blocks by forward substitution, the rest
-//                          by fp32 matrix-core products), the WY factors as tile GEMMs, and
-//                          the per-chunk operands of K2, written to the workspace already in
-//                          matrix-core fragment order.
-//   K2 chunk_state_kernel  one wave per (sequence, value head, 16 columns of S), sequential
-//                          over the chunks of its sequence with its slice of S held in
-//                          registers in fp32 and the chunk operands prefetched into LDS one
-//                          chunk ahead; writes o and S_T.
+//   K1 chunk_prep_kernel   persistent over the (chunk, value head) records, fully parallel:
+//                          the cumulative log decay, A and M on the matrix cores,
+//                          T = (I + A)^{-1} by 16x16 blocks (diagonal blocks by forward
+//                          substitution, the rest by fp32 matrix-core products), the WY
+//                          factors as tile GEMMs, and the per-chunk operands of K2, written to
+//                          the workspace already in matrix-core fragment order.
+//   K2 chunk_state_kernel  per (sequence, value head, 16 columns of S): a chain wave that
+//                          runs the recurrence over the chunks with its slice of S in fp32
+//                          registers, an output wave that forms o from the operands the
+//                          chain wave publishes, and loader waves that stage each chunk's
+//                          operands in LDS one chunk ahead; writes o and S_T.
 //
-// Numerics: exp(g_r - g_i) is split as exp(g_r - ref) * exp(ref - g_i). For a block of
-// rows r in 16-token sub-chunk R against columns in an earlier sub-chunk, ref is the
-// cumulative decay at the end of sub-chunk R-1, so both factors are <= 1 and cannot
-// overflow (an underflowed factor means a negligible true product). Diagonal 16x16 blocks
-// use the middle token of the sub-chunk, so each factor spans at most 8 tokens of decay.
+// Numerics: exp(g_r - g_i) is split into factors relative to the middle token of each
+// 16-token sub-chunk (K1 below), so no factor spans more than 8 tokens of decay except the
+// sub-chunk-to-sub-chunk factors, which are <= 1 (an underflow there means a negligible
+// true product).
 // Padding rows of a partial chunk are identity tokens (k = q = b = 0, w.v = 0,
 // log alpha = 0), which leave the state unchanged.
 #include "gdn2_common.h"
@@ -144,33 +144,49 @@ __device__ __forceinline__ u32x4 pack16(const float *v) {
 //
 // One 512-thread workgroup per CU walks the (chunk, value head) records in chunk-major order
 // (record = chunk * h_v + h, stride = grid size). While a record is computed from LDS, the
-// raw k, q, b, log alpha tiles of the next one are already in flight into registers, and
-// its w.v operands are requested as soon as the current U~ tiles are done, so global memory
-// latency overlaps the math. LDS (about 125 KB at d = 128): raw k, q, b, log alpha with
-// padded rows, g = cumulative log decay (fp32), and the lower 16x16 blocks of A and of
-// T = (I + A)^{-1} (fp32, fragment order).
+// raw k, q, b, log alpha, w, v tiles of the next one are already in flight into registers.
+//
+// Factorisation: with g the cumulative log decay and Mid_R = g at the middle token of
+// 16-token sub-chunk R, every decay factor exp(g_r - g_i) (r in sub-chunk R, i in I <= R)
+// is built from bounded pieces computed once per record:
+//   Khat_r = b_r k_r exp(g_r - Mid_R),  Qhat_r = q_r exp(g_r - Mid_R)   (row side)
+//   Kbar_i = k_i exp(Mid_I - g_i)                                        (column side)
+//   f_RI   = exp(Mid_R - Mid_I) <= 1 per channel, for I < R
+// so A[r,i] = sum_c Khat_r Kbar_i f_RI and M[r,i] = sum_c Qhat_r Kbar_i f_RI. Each exponent
+// spans at most 8 tokens of decay except f_RI, which is <= 1 (an underflow there means a
+// negligible true product). The outputs reuse the same tiles: gamma.q = Qhat exp(Mid_R),
+// gamma.b.k = Khat exp(Mid_R), exp(g_C - g_i) k_i = Kbar_i exp(g_C - Mid_I).
 //
 // Phases per record:
-//   0  raw tiles -> LDS, cumulative sum of log alpha, gamma_C
-//   1  A^T and M^T blocks (the transposed products leave each lane's results in the
-//      row-per-lane fragment order the consumers read); M goes to the workspace
-//  2a wave 0: 16x16 diagonal inverses T_RR by forward substitution; waves 1-7: Qg, KgT
+//   0  log alpha -> LDS, cumulative sum in place, per-channel factors, gamma_C; Khat, Qhat,
+//      Kbar and w.v tiles from the registers; gamma.q written straight to the workspace
+//   1  A^T and M^T 16x16 blocks on the matrix cores (the transposed products leave each
+//      lane's results in row-per-lane order); M goes to the workspace, A to LDS
+//  2a wave 0: diagonal inverses T_RR by forward substitution; waves 1-7: KgT
 //  2b off-diagonal T blocks by levels, T_RI = -T_RR sum_{I<=m<R} A_Rm T_mI (fp32 MFMA)
 //   3  W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) as tile GEMMs, one column tile of
 //      each per wave, written to the workspace in the orders K2 reads
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ int lower_blk(int R, int I) { return R * (R + 1) / 2 + I; }
-
-// Element (r, c) of a 16x16 fp32 block stored in fragment order (lane 16 g + r holds
-// X[r][4 g .. 4 g + 3]).
-__device__ __forceinline__ int frag_idx(int r, int c) { return 4 * (16 * (c >> 2) + r) + (c & 3); }
-
 struct PrepLoc {
     int64_t t0;     // first token of the chunk
     int L;          // valid rows
     int h, hk;
     size_t rec;     // record index
 };
+
+template <bool BF>
+__device__ __forceinline__ void unpack16(u32x4 v, float *out) {
+    if constexpr (BF) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            out[2 * q] = bf16_lo(v[q]);
+            out[2 * q + 1] = bf16_hi(v[q]);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = __uint_as_float(v[q]);
+    }
+}
 
 template <typename T, bool BF, int DK, int DV>
 __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
@@ -179,26 +195,28 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
     constexpr int KT = Op<BF>::KT;            // k per matrix-core tile: 32 (bf16) / 16 (fp32)
     constexpr int KS = BF ? 8 : 4;            // consecutive k values a lane holds per tile
     constexpr int VEC = 16 / sizeof(T);
-    constexpr int SK = DK + VEC;              // padded row stride of the raw tiles (elements)
+    constexpr int SK = DK + VEC;              // padded row stride of the d_k tiles (elements)
+    constexpr int SV = DV + VEC;              // padded row stride of the w.v tile
     constexpr int SG = DK + 4;                // padded row stride of s_g (floats)
-    constexpr int VK = DK / VEC;              // 16-byte vectors per raw row
-    constexpr int RAWV = C * VK / NT;         // raw vectors per thread per tensor
+    constexpr int SA = C + 4;                 // padded row stride of A and T (floats)
+    constexpr int VK = DK / VEC, VV = DV / VEC;
+    constexpr int RAWV = C * VK / NT, RAWW = C * VV / NT;
     constexpr int PARTS = NT / DK;            // cumulative sum: token parts per channel
     constexpr int RPP = C / PARTS;
-    constexpr int NKC = R_::NKT_C, NKTC = C / KT;
-    constexpr int VV = DV / VEC;              // 16-byte vectors per raw value row
-    constexpr int RAWW = C * VV / NT;         // raw w / v vectors per thread
+    constexpr int NKC = R_::NKT_C, NKD = R_::NKT_DK, NKTC = C / KT;
     static_assert(RAWV >= 1 && RAWV * NT == C * VK, "raw tile split");
     static_assert(RAWW >= 1 && RAWW * NT == C * VV, "raw tile split");
-    constexpr int SL = (DK > DV ? DK : DV) + VEC;   // row stride of the log alpha / w.v tile
 
-    __shared__ __attribute__((aligned(16))) T s_k[C * SK];
-    __shared__ __attribute__((aligned(16))) T s_q[C * SK];
-    __shared__ __attribute__((aligned(16))) T s_b[C * SK];
-    __shared__ __attribute__((aligned(16))) T s_la[C * SL];  // log alpha, then w.v
+    __shared__ __attribute__((aligned(16))) T s_kh[C * SK];   // Khat
+    __shared__ __attribute__((aligned(16))) T s_qh[C * SK];   // Qhat
+    __shared__ __attribute__((aligned(16))) T s_kb[C * SK];   // Kbar
+    __shared__ __attribute__((aligned(16))) T s_wv[C * SV];   // w.v
     __shared__ __attribute__((aligned(16))) float s_g[C * SG];
-    __shared__ __attribute__((aligned(16))) float s_A[10 * 256];
-    __shared__ __attribute__((aligned(16))) float s_T[10 * 256];
+    __shared__ __attribute__((aligned(16))) float s_A[C * SA];
+    __shared__ __attribute__((aligned(16))) float s_T[C * SA];
+    __shared__ __attribute__((aligned(16))) float s_fmid[4 * DK];   // exp(Mid_R)
+    __shared__ __attribute__((aligned(16))) float s_fkg[4 * DK];    // exp(g_C - Mid_I)
+    __shared__ __attribute__((aligned(16))) float s_foff[6 * DK];   // exp(Mid_R - Mid_I), R > I
     __shared__ float s_part[PARTS * DK];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -221,20 +239,9 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         lc.L = static_cast<int>(min<int64_t>(C, end - lc.t0));
         lc.rec = static_cast<size_t>(item);
     };
-    // raw k, q, b, log alpha vectors of a record (rows >= L are zero: identity tokens)
+    // raw 16-byte vectors of a record (rows >= L are zero: identity tokens)
     u32x4 rk[RAWV], rq[RAWV], rb[RAWV], rl[RAWV], rw[RAWW], rv[RAWW];
     auto load_raw = [&](const PrepLoc &lc) {
-#pragma unroll
-        for (int e = 0; e < RAWW; ++e) {
-            const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            rw[e] = z; rv[e] = z;
-            if (r < lc.L) {
-                const size_t ov = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DV + cv * VEC;
-                rw[e] = *reinterpret_cast<const u32x4 *>(wp + ov);
-                rv[e] = *reinterpret_cast<const u32x4 *>(vp + ov);
-            }
-        }
 #pragma unroll
         for (int e = 0; e < RAWV; ++e) {
             const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
@@ -249,7 +256,19 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                 rl[e] = *reinterpret_cast<const u32x4 *>(lap + og);
             }
         }
+#pragma unroll
+        for (int e = 0; e < RAWW; ++e) {
+            const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            rw[e] = z; rv[e] = z;
+            if (r < lc.L) {
+                const size_t ov = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DV + cv * VEC;
+                rw[e] = *reinterpret_cast<const u32x4 *>(wp + ov);
+                rv[e] = *reinterpret_cast<const u32x4 *>(vp + ov);
+            }
+        }
     };
+
     int item = blockIdx.x;
     PrepLoc cur;
     if (item < nitems) {
@@ -263,14 +282,16 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         if (has_next) locate(next, nxt);
         char *rec = p.rec + cur.rec * R_::bytes;
 
-        // ---- phase 0 ----
+        // ---- phase 0: cumulative log decay (in place in s_g) ----
 #pragma unroll
         for (int e = 0; e < RAWV; ++e) {
             const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-            *reinterpret_cast<u32x4 *>(&s_k[r * SK + cv * VEC]) = rk[e];
-            *reinterpret_cast<u32x4 *>(&s_q[r * SK + cv * VEC]) = rq[e];
-            *reinterpret_cast<u32x4 *>(&s_b[r * SK + cv * VEC]) = rb[e];
-            *reinterpret_cast<u32x4 *>(&s_la[r * SL + cv * VEC]) = rl[e];
+            float x[VEC];
+            unpack16<BF>(rl[e], x);
+#pragma unroll
+            for (int s = 0; s < VEC; s += 4)
+                *reinterpret_cast<f32x4 *>(&s_g[r * SG + cv * VEC + s]) =
+                    f32x4{x[s], x[s + 1], x[s + 2], x[s + 3]};
         }
         __syncthreads();
         {
@@ -279,7 +300,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             float acc = 0.f;
 #pragma unroll
             for (int rr = 0; rr < RPP; ++rr) {
-                acc += io<T>::ld(&s_la[(part * RPP + rr) * SL + c]);
+                acc += s_g[(part * RPP + rr) * SG + c];
                 x[rr] = acc;
             }
             s_part[part * DK + c] = acc;
@@ -288,30 +309,76 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             for (int pp = 0; pp < part; ++pp) pre += s_part[pp * DK + c];
 #pragma unroll
             for (int rr = 0; rr < RPP; ++rr) s_g[(part * RPP + rr) * SG + c] = x[rr] + pre;
-            // w.v, rounded to the operand type (the rounding its matrix-core use applies),
-            // into the log alpha tile, which is no longer read
-#pragma unroll
-            for (int e = 0; e < RAWW; ++e) {
-                const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
-                float prod[16 / sizeof(T)];
-                if constexpr (BF) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        prod[2 * q4] = bf16_lo(rw[e][q4]) * bf16_lo(rv[e][q4]);
-                        prod[2 * q4 + 1] = bf16_hi(rw[e][q4]) * bf16_hi(rv[e][q4]);
-                    }
-                } else {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        prod[q4] = __uint_as_float(rw[e][q4]) * __uint_as_float(rv[e][q4]);
-                }
-                *reinterpret_cast<u32x4 *>(&s_la[r * SL + cv * VEC]) = pack16<BF>(prod);
-            }
-            __syncthreads();
-            if (has_next) load_raw(nxt);       // next record's raw tiles, in flight from here
-            if (tid < DK)
-                reinterpret_cast<float *>(rec + R_::gC)[tid] = __expf(s_g[(C - 1) * SG + tid]);
         }
+        __syncthreads();
+
+        // ---- phase 0b: per-channel factors, operand tiles, gamma.q ----
+        for (int idx = tid; idx < 14 * DK; idx += NT) {
+            const int c = idx % DK, kind = idx / DK;
+            if (kind < 4) {
+                s_fmid[kind * DK + c] = __expf(s_g[(16 * kind + 7) * SG + c]);
+            } else if (kind < 8) {
+                const int I = kind - 4;
+                s_fkg[I * DK + c] = __expf(s_g[(C - 1) * SG + c] - s_g[(16 * I + 7) * SG + c]);
+            } else {
+                const int pi = kind - 8;        // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+                const int R = pi < 1 ? 1 : (pi < 3 ? 2 : 3);
+                const int I = pi - R * (R - 1) / 2;
+                s_foff[pi * DK + c] = __expf(s_g[(16 * R + 7) * SG + c] - s_g[(16 * I + 7) * SG + c]);
+            }
+        }
+        if (tid < DK) reinterpret_cast<float *>(rec + R_::gC)[tid] = __expf(s_g[(C - 1) * SG + tid]);
+        char *qgrec = rec + R_::Qg;
+#pragma unroll
+        for (int e = 0; e < RAWV; ++e) {
+            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
+            const int c0 = cv * VEC, mid = ((r >> 4) * 16 + 7) * SG;
+            float kk[VEC], qq[VEC], bb[VEC], kh[VEC], qh[VEC], kb[VEC], qg[VEC];
+            unpack16<BF>(rk[e], kk);
+            unpack16<BF>(rq[e], qq);
+            unpack16<BF>(rb[e], bb);
+#pragma unroll
+            for (int s = 0; s < VEC; ++s) {
+                const float gr = s_g[r * SG + c0 + s], gm = s_g[mid + c0 + s];
+                const float ef = __expf(gr - gm), ei = __expf(gm - gr);
+                kh[s] = bb[s] * kk[s] * ef;
+                qh[s] = qq[s] * ef;
+                kb[s] = kk[s] * ei;
+                qg[s] = qq[s] * __expf(gr);
+            }
+            *reinterpret_cast<u32x4 *>(&s_kh[r * SK + c0]) = pack16<BF>(kh);
+            *reinterpret_cast<u32x4 *>(&s_qh[r * SK + c0]) = pack16<BF>(qh);
+            *reinterpret_cast<u32x4 *>(&s_kb[r * SK + c0]) = pack16<BF>(kb);
+            // gamma.q in K2's fragment order: row tile r/16, k tile c/KT, lane 16 lg + r%16
+            if constexpr (BF) {
+#pragma unroll
+                for (int j4 = 0; j4 < 2; ++j4) {
+                    const int c = c0 + 4 * j4, kt = c / 32, q4 = c % 32;
+                    const int half = q4 >= 16 ? 1 : 0, lgq = (q4 & 15) >> 2;
+                    const size_t slot = ((static_cast<size_t>(r >> 4) * NKD + kt) * 64 + 16 * lgq +
+                                         (r & 15)) * 2 + half;
+                    reinterpret_cast<u32x2 *>(qgrec)[slot] =
+                        u32x2{pack_bf16x2(qg[4 * j4], qg[4 * j4 + 1]),
+                              pack_bf16x2(qg[4 * j4 + 2], qg[4 * j4 + 3])};
+                }
+            } else {
+                const int kt = c0 / 16, lgq = (c0 & 15) >> 2;
+                reinterpret_cast<f32x4 *>(qgrec)[((r >> 4) * NKD + kt) * 64 + 16 * lgq + (r & 15)] =
+                    f32x4{qg[0], qg[1], qg[2], qg[3]};
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < RAWW; ++e) {
+            const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
+            float ww[VEC], vv[VEC], prod[VEC];
+            unpack16<BF>(rw[e], ww);
+            unpack16<BF>(rv[e], vv);
+#pragma unroll
+            for (int s = 0; s < VEC; ++s) prod[s] = ww[s] * vv[s];
+            *reinterpret_cast<u32x4 *>(&s_wv[r * SV + cv * VEC]) = pack16<BF>(prod);
+        }
+        __syncthreads();
+        if (has_next) load_raw(nxt);           // next record's raw tiles, in flight from here
 
         // ---- phase 1: A^T and M^T blocks (R >= I); zero upper blocks of M ----
         char *mrec = rec + R_::M;
@@ -319,37 +386,33 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             const int R = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
             const int I = pr - R * (R + 1) / 2;
             const bool diag = (R == I);
-            const int refrow = diag ? 16 * R + 7 : 16 * R - 1;
+            const int pi = diag ? 0 : R * (R - 1) / 2 + I;
             const int ri = 16 * I + li;              // A operand: column-side token i
             const int rr = 16 * R + li;              // B operand: row-side token r
             f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
 #pragma unroll
             for (int kt = 0; kt < DK / KT; ++kt) {
                 const int c0 = kt * KT + KS * lg;
-                float kb[KS], ka[KS], qa[KS];
+                u32x4 kb = *reinterpret_cast<const u32x4 *>(&s_kb[ri * SK + c0]);
+                if (!diag) {
+                    float x[KS];
+                    unpack16<BF>(kb, x);
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const int c = c0 + s;
-                    const float ref = s_g[refrow * SG + c];
-                    const float ec = __expf(ref - s_g[ri * SG + c]);
-                    const float ef = __expf(s_g[rr * SG + c] - ref);
-                    kb[s] = io<T>::ld(&s_k[ri * SK + c]) * ec;
-                    ka[s] = io<T>::ld(&s_b[rr * SK + c]) * io<T>::ld(&s_k[rr * SK + c]) * ef;
-                    qa[s] = io<T>::ld(&s_q[rr * SK + c]) * ef;
+                    for (int s = 0; s < KS; ++s) x[s] *= s_foff[pi * DK + c0 + s];
+                    kb = pack16<BF>(x);
                 }
+                const u32x4 kh = *reinterpret_cast<const u32x4 *>(&s_kh[rr * SK + c0]);
+                const u32x4 qh = *reinterpret_cast<const u32x4 *>(&s_qh[rr * SK + c0]);
                 if constexpr (BF) {
-                    const u32x4 a = pack16<true>(kb);
-                    accA = mma_k32(a, pack16<true>(ka), accA);
-                    accM = mma_k32(a, pack16<true>(qa), accM);
+                    accA = mma_k32(kb, kh, accA);
+                    accM = mma_k32(kb, qh, accM);
                 } else {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        accA = __builtin_amdgcn_mfma_f32_16x16x4f32(kb[s], ka[s], accA, 0, 0, 0);
-                        accM = __builtin_amdgcn_mfma_f32_16x16x4f32(kb[s], qa[s], accM, 0, 0, 0);
-                    }
+                    const f32x4 a = __builtin_bit_cast(f32x4, kb);
+                    accA = mma_k16_f32(a, __builtin_bit_cast(f32x4, kh), accA);
+                    accM = mma_k16_f32(a, __builtin_bit_cast(f32x4, qh), accM);
                 }
             }
-            // lane holds A[r = 16R + li][i = 16I + 4 lg + ii] (and M): fragment order already
+            // lane holds A[r = 16R + li][i = 16I + 4 lg + ii] (and M)
             f32x4 a4, m4;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
@@ -357,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                 a4[ii] = (diag && il >= li) ? 0.f : accA[ii];
                 m4[ii] = (diag && il > li) ? 0.f : accM[ii];
             }
-            *reinterpret_cast<f32x4 *>(&s_A[lower_blk(R, I) * 256 + 4 * lane]) = a4;
+            *reinterpret_cast<f32x4 *>(&s_A[rr * SA + 16 * I + 4 * lg]) = a4;
             if constexpr (BF) {
                 reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)] =
                     f4_to_b16(m4);
@@ -379,10 +442,10 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         }
         __syncthreads();
 
-        // ---- phase 2a: diagonal inverses (wave 0) || Qg and KgT (waves 1-7) ----
+        // ---- phase 2a: diagonal inverses (wave 0) || KgT (waves 1-7) ----
         if (wave == 0) {
             const int R = lane >> 4, jc = lane & 15;      // column jc of T_RR
-            const float *Ab = &s_A[lower_blk(R, R) * 256];
+            const float *Ab = &s_A[16 * R * SA + 16 * R];
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
@@ -390,42 +453,27 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             for (int r = 1; r < 16; ++r) {
                 float acc = 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc += Ab[frag_idx(r, m)] * x[m];
+                for (int m = 0; m < r; ++m) acc += Ab[r * SA + m] * x[m];
                 if (r > jc) x[r] = -acc;
             }
-            float *Tb = &s_T[lower_blk(R, R) * 256];
+            float *Tb = &s_T[16 * R * SA + 16 * R];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Tb[frag_idx(r, jc)] = x[r];
+            for (int r = 0; r < 16; ++r) Tb[r * SA + jc] = x[r];
         } else {
-            constexpr int NBQ = (C / 16) * R_::NKT_DK;      // Qg blocks
-            constexpr int NBK = (DK / 16) * R_::NKT_C;      // KgT blocks
+            constexpr int NBK = (DK / 16) * NKC;            // KgT blocks
             constexpr int EPL = Op<BF>::EPL;
-            u32x4 *qg = reinterpret_cast<u32x4 *>(rec + R_::Qg);
             u32x4 *kg = reinterpret_cast<u32x4 *>(rec + R_::KgT);
-            for (int idx = tid - 64; idx < (NBQ + NBK) * 64; idx += NT - 64) {
-                const int blk = idx >> 6, l = idx & 63, lli = l & 15, llg = l >> 4;
+            for (int idx = tid - 64; idx < NBK * 64; idx += NT - 64) {
+                const int b2 = idx >> 6, l = idx & 63, lli = l & 15, llg = l >> 4;
+                const int rt = b2 / NKC, kt = b2 - rt * NKC;
+                const int ch = 16 * rt + lli;
                 float vals[EPL];
-                if (blk < NBQ) {
-                    const int rt = blk / R_::NKT_DK, kt = blk - rt * R_::NKT_DK;
-                    const int r = 16 * rt + lli;
 #pragma unroll
-                    for (int jj = 0; jj < EPL; ++jj) {
-                        const int c = kt * KT + perm_k<BF>(llg, jj);
-                        vals[jj] = __expf(s_g[r * SG + c]) * io<T>::ld(&s_q[r * SK + c]);
-                    }
-                    qg[blk * 64 + l] = pack16<BF>(vals);
-                } else {
-                    const int b2 = blk - NBQ;
-                    const int rt = b2 / R_::NKT_C, kt = b2 - rt * R_::NKT_C;
-                    const int ch = 16 * rt + lli;
-                    const float gl = s_g[(C - 1) * SG + ch];
-#pragma unroll
-                    for (int jj = 0; jj < EPL; ++jj) {
-                        const int tok = kt * KT + perm_k<BF>(llg, jj);
-                        vals[jj] = __expf(gl - s_g[tok * SG + ch]) * io<T>::ld(&s_k[tok * SK + ch]);
-                    }
-                    kg[b2 * 64 + l] = pack16<BF>(vals);
+                for (int jj = 0; jj < EPL; ++jj) {
+                    const int tok = kt * KT + perm_k<BF>(llg, jj);
+                    vals[jj] = io<T>::ld(&s_kb[tok * SK + ch]) * s_fkg[(tok >> 4) * DK + ch];
                 }
+                kg[b2 * 64 + l] = pack16<BF>(vals);
             }
         }
         __syncthreads();
@@ -437,19 +485,17 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                 const int R = d + wave, I = R - d;
                 f32x4 P = {0.f, 0.f, 0.f, 0.f};
                 for (int m = I; m < R; ++m) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(&s_A[lower_blk(R, m) * 256 + 4 * lane]);
-                    const float *Tm = &s_T[lower_blk(m, I) * 256];
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(&s_A[(16 * R + li) * SA + 16 * m + 4 * lg]);
                     f32x4 bT;                      // B operand: T_mI[4 lg + s][li]
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) bT[s] = Tm[frag_idx(4 * lg + s, li)];
+                    for (int s = 0; s < 4; ++s) bT[s] = s_T[(16 * m + 4 * lg + s) * SA + 16 * I + li];
                     P = mma_k16_f32(a, bT, P);
                 }
-                const f32x4 tRR = *reinterpret_cast<const f32x4 *>(&s_T[lower_blk(R, R) * 256 + 4 * lane]);
+                const f32x4 tRR = *reinterpret_cast<const f32x4 *>(&s_T[(16 * R + li) * SA + 16 * R + 4 * lg]);
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 Tn = mma_k16_f32(tRR, P, zero);   // lane: (T_RR P)[4 lg + ii][li]
-                float *Tb = &s_T[lower_blk(R, I) * 256];
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Tb[frag_idx(4 * lg + ii, li)] = -Tn[ii];
+                for (int ii = 0; ii < 4; ++ii) s_T[(16 * R + 4 * lg + ii) * SA + 16 * I + li] = -Tn[ii];
             }
             __syncthreads();
         }
@@ -467,12 +513,8 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     const int tok = kt * KT + KS * lg + s;
-                    if (isW) {
-                        xv[kt][s] = __expf(s_g[tok * SG + c]) * io<T>::ld(&s_b[tok * SK + c]) *
-                                    io<T>::ld(&s_k[tok * SK + c]);
-                    } else {
-                        xv[kt][s] = io<T>::ld(&s_la[tok * SL + c]);     // w.v
-                    }
+                    xv[kt][s] = isW ? io<T>::ld(&s_kh[tok * SK + c]) * s_fmid[(tok >> 4) * DK + c]
+                                    : io<T>::ld(&s_wv[tok * SV + c]);
                 }
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
@@ -480,12 +522,15 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 #pragma unroll
                 for (int kt = 0; kt < NKTC; ++kt) {
                     if (kt * KT > 16 * R + 15) break;
-                    float tv[KS];                  // T[16R + li][kt*KT + KS*lg + s]
+                    // T[16R + li][kt*KT + KS*lg + s]; the KS tokens share one 16-block
+                    const int tok0 = kt * KT + KS * lg;
+                    float tv[KS];
+                    const bool live = (tok0 >> 4) <= R;
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) {
-                        const int tok = kt * KT + KS * lg + s;
-                        const int I = tok >> 4;
-                        tv[s] = (I <= R) ? s_T[lower_blk(R, I) * 256 + frag_idx(li, tok & 15)] : 0.f;
+                    for (int s = 0; s < KS; s += 4) {
+                        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s_T[(16 * R + li) * SA + tok0 + s]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) tv[s + e] = live ? t4[e] : 0.f;
                     }
                     if constexpr (BF) {
                         if (isW) acc = mma_k32(pack16<true>(xv[kt]), pack16<true>(tv), acc);
@@ -502,10 +547,10 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     const f32x4 wn = -acc;
                     char *wr = rec + R_::Wn;
                     if constexpr (BF) {
-                        reinterpret_cast<u32x2 *>(wr)[(((R * R_::NKT_DK + (ct >> 1)) * 64 + lane) << 1) +
+                        reinterpret_cast<u32x2 *>(wr)[(((R * NKD + (ct >> 1)) * 64 + lane) << 1) +
                                                       (ct & 1)] = f4_to_b16(wn);
                     } else {
-                        reinterpret_cast<f32x4 *>(wr)[(R * R_::NKT_DK + ct) * 64 + lane] = wn;
+                        reinterpret_cast<f32x4 *>(wr)[(R * NKD + ct) * 64 + lane] = wn;
                     }
                 } else {
                     // lane: U~[16R + 4 lg + ii][16 ct + li], an output tile (D layout)
@@ -521,33 +566,40 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// K2: inter-chunk state pass. Each compute wave owns 16 columns of S (all d_k rows) as DK/16
-// output tiles in fp32 registers and walks the chunks of its sequence in order. The waves
-// of a workgroup share one (sequence, head). Per chunk:
-//   * the record (operands common to all columns, gamma_C, each wave's U~ slice) is copied
-//     into a double-buffered LDS stage one chunk ahead by kLoaders extra loader waves with
-//     direct global-to-LDS loads: one wave cannot keep enough copies in flight to move a
-//     record per chunk step, several can. Loaders wait for their own copies, then meet
-//     the compute waves at the per-chunk barrier (a plain s_barrier, no memory fence);
-//   * each matrix-core phase first reads all its A fragments from LDS, then issues the
-//     products with the independent accumulator chains interleaved;
-//   * o of a chunk is transposed through LDS and stored with 16-byte writes one chunk later.
+// K2: inter-chunk state pass. Each 16-column slice of S (all d_k rows, fp32, in registers)
+// has two compute waves, and each workgroup has kLoaders loader waves:
+//   * the chain wave runs the recurrence: U = U~ + Wn S, then S = gamma_C S + KgT U. It
+//     publishes the matrix-core B operands of S (at chunk entry) and of U in LDS and sets a
+//     per-slice flag after each;
+//   * the output wave computes O = Qg S + M U from those published operands as they appear,
+//     off the recurrence's critical path, and leaves o in an LDS tile;
+//   * kCopyWaves copy waves load chunk c + 1's record (operands common to all columns,
+//     gamma_C, the slices' U~) into the other half of a double-buffered LDS stage with
+//     direct global-to-LDS loads (one wave cannot keep enough copies in flight);
+//   * one store wave writes the o tiles of chunk c - 1 to memory with 16-byte stores. It
+//     never waits for them: a wave that both copies and stores would have to wait for its
+//     stores too before each barrier, since both share one completion counter. Compute
+//     waves issue no global memory operation inside the chunk loop.
+// All waves meet once per chunk at a plain s_barrier (no memory fence: each wave waits for
+// exactly what it produced before arriving). The column-slice workgroups of one
+// (sequence, head) run on one XCD, so its records are fetched into one L2.
 // ---------------------------------------------------------------------------------------
 template <int DK, int DV, bool BF>
 struct StageLayout {
     using R_ = Rec<DK, DV, BF>;
+    static constexpr size_t E_O = BF ? 2 : 4;                // bytes per o element
     static constexpr size_t SHARED = R_::Ut;                 // Wn, Qg, KgT, M
     static constexpr size_t GCB = DK * 4;                    // gamma_C
-    static constexpr size_t UTS = 4 * R_::UT_TILE;           // one wave's U~ slice
-    static constexpr size_t OTILE = kChunk * 16 * 4;         // one wave's o transpose area
+    static constexpr size_t UTS = 4 * R_::UT_TILE;           // one slice's U~
+    static constexpr size_t OTILE = kChunk * 16 * E_O;       // one slice's o tile
+    static constexpr size_t XCH = (R_::NKT_DK + R_::NKT_C) * 1024;   // published S, U operands
     __host__ __device__ static constexpr size_t buffer_bytes(int nw) {
         return SHARED + GCB + nw * UTS;
     }
     __host__ __device__ static constexpr size_t lds_bytes(int nw) {
-        return 2 * buffer_bytes(nw) + nw * OTILE;
+        return 2 * buffer_bytes(nw) + 2 * nw * OTILE + nw * XCH + 64;
     }
-    static_assert(2 * (SHARED + GCB + UTS) + OTILE <= 160 * 1024,
-                  "double buffer must fit in LDS");
+    static_assert(lds_bytes(1) <= 160 * 1024, "stage must fit in LDS");
 };
 
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
@@ -559,32 +611,45 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // s_waitcnt with lgkmcnt(0) only
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier without a memory fence (so it never waits for outstanding loads). The
-// empty asm statements keep the compiler from moving memory accesses across it; every wave
-// waits for its own copies with wait_vmem() before arriving when it needs them.
+// empty asm statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void raw_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
-constexpr int kLoaders = 4;           // loader waves per state-pass workgroup
+// Spin (bounded) until an LDS flag written by another wave of the workgroup reaches `want`.
+// The writer is always able to progress, so the bound is never reached in a correct run; it
+// only guarantees that every wave exits.
+__device__ __forceinline__ void wait_flag(volatile int *flag, int want) {
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (*flag >= want) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kCopyWaves = 6;         // copy waves per state-pass workgroup
+constexpr int kLoaders = kCopyWaves + 1;   // plus one store wave
 
 template <typename T, bool BF, int DK, int DV>
-__global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
+__global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkParams p) {
     using R_ = Rec<DK, DV, BF>;
     using SL = StageLayout<DK, DV, BF>;
     constexpr int C = kChunk, RT = DK / 16;
     constexpr int KT = Op<BF>::KT;
     constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
+    static_assert(BF || NKD == RT, "fp32 operands are whole state tiles");
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int nw = (blockDim.x >> 6) - kLoaders;   // compute waves; the rest load
+    const int nw = ((blockDim.x >> 6) - kLoaders) / 2;   // column slices per workgroup
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
     const size_t BUF = SL::buffer_bytes(nw);
     char *otile_base = smem + 2 * BUF;
+    char *xch_base = otile_base + 2 * nw * SL::OTILE;
+    int *flags = reinterpret_cast<int *>(xch_base + nw * SL::XCH);   // [nw] S, [nw] U
 
-    // XCD-aware decode: the column slices of one (sequence, head) pair share an XCD, so
-    // its workspace records are fetched into one L2.
+    // XCD-aware decode: the column slices of one (sequence, head) pair share an XCD.
     const int bid = blockIdx.x, xcd = bid & 7, rest = bid >> 3;
     const int slice = rest % p.nslices;
     const int pair = (rest / p.nslices) * 8 + xcd;
@@ -607,87 +672,111 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
         return p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
     };
 
-    if (wave >= nw) {
-        // ---- loader waves: copy chunk c + 1 into the other stage during chunk c
-        const int ldr = wave - nw;
-        auto issue = [&](int c, char *dst) {
-            const char *rec = record(c);
-            for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += kLoaders)
-                dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
-            if (ldr == kLoaders - 1 && lane < static_cast<int>(SL::GCB / 16))
-                dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
-            // the compute waves' U~ slices: column tiles slice*nw .. slice*nw + nw - 1 are
-            // contiguous in the record, and so are their stage slots
-            const char *us = rec + R_::Ut + static_cast<size_t>(slice) * nw * SL::UTS;
-            char *ud = dst + SL::SHARED + SL::GCB;
-            for (int b = ldr; b < static_cast<int>(nw * SL::UTS / 1024); b += kLoaders)
-                dma16(us + b * 1024 + lane * 16, ud + b * 1024);
+    if (wave >= 2 * nw) {
+        const int ldr = wave - 2 * nw;
+        if (ldr < kCopyWaves) {
+            // ---- copy waves: stage chunk c + 1 in the other buffer during chunk c
+            auto issue = [&](int c, char *dst) {
+                const char *rec = record(c);
+                for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += kCopyWaves)
+                    dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
+                if (ldr == kCopyWaves - 1 && lane < static_cast<int>(SL::GCB / 16))
+                    dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
+                // the slices' U~: column tiles slice*nw .. slice*nw + nw - 1 are contiguous
+                // in the record, and so are their stage slots
+                const char *us = rec + R_::Ut + static_cast<size_t>(slice) * nw * SL::UTS;
+                char *ud = dst + SL::SHARED + SL::GCB;
+                for (int b = ldr; b < static_cast<int>(nw * SL::UTS / 1024); b += kCopyWaves)
+                    dma16(us + b * 1024 + lane * 16, ud + b * 1024);
+            };
+            if (nchunks > 0) issue(0, smem);
+            for (int c = 0; c < nchunks; ++c) {
+                wait_vmem();                // this wave's copies for chunk c have landed
+                raw_barrier();              // chunk c is staged; chunk c-1 fully consumed
+                if (c + 1 < nchunks) issue(c + 1, smem + ((c + 1) & 1) * BUF);
+            }
+            if (nchunks > 0) raw_barrier();
+            return;
+        }
+        // ---- store wave: o of chunk c - 1 (o tiles of buffer (c-1) & 1) during chunk c
+        T *op = static_cast<T *>(p.o);
+        constexpr int PPR = 16 * static_cast<int>(sizeof(T)) / 16;   // 16-byte pieces per row
+        auto store_o = [&](int c) {
+            const int64_t t0 = start + static_cast<int64_t>(c) * C;
+            const int L = static_cast<int>(min<int64_t>(C, end - t0));
+            const T *tiles = reinterpret_cast<const T *>(otile_base + (c & 1) * nw * SL::OTILE);
+            for (int idx = lane; idx < nw * C * PPR; idx += 64) {
+                const int w = idx / (C * PPR), rp = idx - w * C * PPR;
+                const int row = rp / PPR, piece = rp - row * PPR;
+                if (row < L) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                        &tiles[w * C * 16 + row * 16 + piece * (16 / sizeof(T))]);
+                    *reinterpret_cast<u32x4 *>(
+                        op + (static_cast<size_t>(t0 + row) * p.h_v + h) * DV +
+                        16 * (slice * nw + w) + piece * (16 / sizeof(T))) = v;
+                }
+            }
+            wait_lds();                     // tile reads done before the next barrier
         };
-        if (nchunks > 0) issue(0, smem);
         for (int c = 0; c < nchunks; ++c) {
-            wait_vmem();                    // this loader's copies for chunk c have landed
-            raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
-            if (c + 1 < nchunks) issue(c + 1, smem + ((c + 1) & 1) * BUF);
+            raw_barrier();
+            if (c > 0) store_o(c - 1);
+        }
+        if (nchunks > 0) {
+            raw_barrier();                  // the last chunk's o tiles are written
+            store_o(nchunks - 1);
         }
         return;
     }
 
-    const int ct = slice * nw + wave;
+    const bool chain = wave < nw;
+    const int sl = chain ? wave : wave - nw;             // slice within the workgroup
+    const int ct = slice * nw + sl;
     const int col = 16 * ct + li;
-    f32x4 S[RT];
-    const size_t sbase = static_cast<size_t>(pair) * DK * DV;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            S[rt][ii] = p.S0 ? p.S0[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col]
-                             : 0.f;
+    u32x4 *xS = reinterpret_cast<u32x4 *>(xch_base + sl * SL::XCH);   // published S operands
+    u32x4 *xU = xS + NKD * 64;                                         // published U operands
+    volatile int *flagS = flags + sl;
+    volatile int *flagU = flags + nw + sl;
+    if (chain && lane == 0) {
+        *flagS = 0;
+        *flagU = 0;
+    }
+    wait_lds();
 
-    // o of chunk c is written to this wave's LDS tile at the end of chunk c and stored to
-    // memory during chunk c + 1 as 16-byte rows.
-    T *op = static_cast<T *>(p.o);
-    T *otile = reinterpret_cast<T *>(otile_base + wave * SL::OTILE);
-    constexpr int OPR = 16 * sizeof(T) / 16;        // 16-byte pieces per 16-column row
-    int64_t t0prev = 0;
-    int Lprev = 0;
-    auto store_o = [&]() {
+    if (chain) {
+        // ---- chain wave ----
+        f32x4 S[RT];
+        const size_t sbase = static_cast<size_t>(pair) * DK * DV;
 #pragma unroll
-        for (int e = 0; e < C * OPR / 64; ++e) {
-            const int pidx = lane + 64 * e, row = pidx / OPR, piece = pidx - row * OPR;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(&otile[row * 16 + piece * (16 / sizeof(T))]);
-            if (row < Lprev)
-                *reinterpret_cast<u32x4 *>(op + (static_cast<size_t>(t0prev + row) * p.h_v + h) * DV +
-                                           16 * ct + piece * (16 / sizeof(T))) = v;
-        }
-    };
-
-    for (int c = 0; c < nchunks; ++c) {
-        char *cur = smem + (c & 1) * BUF;
-        raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
-        if (c > 0) store_o();
-
-        const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur + R_::Wn);
-        const u32x4 *qg = reinterpret_cast<const u32x4 *>(cur + R_::Qg);
-        const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + R_::KgT);
-        const u32x4 *mq = reinterpret_cast<const u32x4 *>(cur + R_::M);
-        const float *gc = reinterpret_cast<const float *>(cur + SL::SHARED);
-        const char *ut = cur + SL::SHARED + SL::GCB + wave * SL::UTS;
-
-        u32x4 SB[BF ? NKD : 1];
-        if constexpr (BF) {
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int kt = 0; kt < NKD; ++kt) SB[kt] = dpair_to_b32(S[2 * kt], S[2 * kt + 1]);
-        }
-        // U = U~ + Wn S
-        f32x4 U[4];
-        {
-            u32x4 a[4][NKD];
+            for (int ii = 0; ii < 4; ++ii)
+                S[rt][ii] = p.S0 ? p.S0[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col]
+                                 : 0.f;
+        for (int c = 0; c < nchunks; ++c) {
+            const char *cur = smem + (c & 1) * BUF;
+            raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
+            const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur + R_::Wn);
+            const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + R_::KgT);
+            const float *gc = reinterpret_cast<const float *>(cur + SL::SHARED);
+            const char *ut = cur + SL::SHARED + SL::GCB + sl * SL::UTS;
+            // publish S (chunk entry) as B operands
+            u32x4 SB[NKD];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int kt = 0; kt < NKD; ++kt) a[rt][kt] = wn[(rt * NKD + kt) * 64 + lane];
+            for (int kt = 0; kt < NKD; ++kt) {
+                if constexpr (BF) SB[kt] = dpair_to_b32(S[2 * kt], S[2 * kt + 1]);
+                else SB[kt] = __builtin_bit_cast(u32x4, S[kt]);
+                xS[kt * 64 + lane] = SB[kt];
+            }
+            wait_lds();
+            if (lane == 0) *flagS = c + 1;
+            // U = U~ + Wn S
+            u32x4 aw[4][NKD];
+            f32x4 U[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+                for (int kt = 0; kt < NKD; ++kt) aw[rt][kt] = wn[(rt * NKD + kt) * 64 + lane];
                 if constexpr (BF) {
                     const u32x2 u = reinterpret_cast<const u32x2 *>(ut + rt * R_::UT_TILE)[lane];
                     U[rt] = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
@@ -699,86 +788,104 @@ __global__ __launch_bounds__(512) void chunk_state_kernel(ChunkParams p) {
             for (int kt = 0; kt < NKD; ++kt)
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    if constexpr (BF) U[rt] = mma_k32(a[rt][kt], SB[kt], U[rt]);
-                    else U[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a[rt][kt]), S[kt], U[rt]);
+                    if constexpr (BF) U[rt] = mma_k32(aw[rt][kt], SB[kt], U[rt]);
+                    else U[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, aw[rt][kt]), S[kt], U[rt]);
                 }
-        }
-        u32x4 UB[BF ? NKC : 1];
-        if constexpr (BF) {
+            // publish U as B operands
+            u32x4 UB[NKC];
 #pragma unroll
-            for (int kt = 0; kt < NKC; ++kt) UB[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
-        }
-        // O = Qg S + M U   (M is lower triangular: k tiles above the diagonal are skipped)
-        f32x4 O[4];
-        {
-            u32x4 a[4][NKD], m[4][NKC];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-                for (int kt = 0; kt < NKD; ++kt) a[rt][kt] = qg[(rt * NKD + kt) * 64 + lane];
-#pragma unroll
-                for (int kt = 0; kt < NKC; ++kt)
-                    if (kt * KT <= 16 * rt + 15) m[rt][kt] = mq[(rt * NKC + kt) * 64 + lane];
+            for (int kt = 0; kt < NKC; ++kt) {
+                if constexpr (BF) UB[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
+                else UB[kt] = __builtin_bit_cast(u32x4, U[kt]);
+                xU[kt * 64 + lane] = UB[kt];
             }
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kt = 0; kt < NKD; ++kt)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    if constexpr (BF) O[rt] = mma_k32(a[rt][kt], SB[kt], O[rt]);
-                    else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a[rt][kt]), S[kt], O[rt]);
-                }
-#pragma unroll
-            for (int kt = 0; kt < NKC; ++kt)
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    if (kt * KT > 16 * rt + 15) continue;
-                    if constexpr (BF) O[rt] = mma_k32(m[rt][kt], UB[kt], O[rt]);
-                    else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, m[rt][kt]), U[kt], O[rt]);
-                }
-        }
-        // S = gamma_C S + KgT U
-        {
-            u32x4 a[RT][NKC];
+            wait_lds();
+            if (lane == 0) *flagU = c + 1;
+            // S = gamma_C S + KgT U
+            u32x4 ak[RT][NKC];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int kt = 0; kt < NKC; ++kt) a[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
+                for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
-                S[rt] *= g4;
-            }
+            for (int rt = 0; rt < RT; ++rt)
+                S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    if constexpr (BF) S[rt] = mma_k32(a[rt][kt], UB[kt], S[rt]);
-                    else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, a[rt][kt]), U[kt], S[rt]);
+                    if constexpr (BF) S[rt] = mma_k32(ak[rt][kt], UB[kt], S[rt]);
+                    else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, ak[rt][kt]), U[kt], S[rt]);
                 }
+            wait_lds();
         }
-        // o rows of this chunk into the wave's LDS tile (row-major [C][16]); stored next chunk
-        wait_lds();
+        if (nchunks > 0) raw_barrier();     // pairs with the loaders' final barrier
+        if (p.S_T) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    p.S_T[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = S[rt][ii];
+        }
+        return;
+    }
+
+    // ---- output wave ----
+    for (int c = 0; c < nchunks; ++c) {
+        const char *cur = smem + (c & 1) * BUF;
+        raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
+        const u32x4 *qg = reinterpret_cast<const u32x4 *>(cur + R_::Qg);
+        const u32x4 *mq = reinterpret_cast<const u32x4 *>(cur + R_::M);
+        u32x4 aq[4][NKD], am[4][NKC];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+            for (int kt = 0; kt < NKD; ++kt) aq[rt][kt] = qg[(rt * NKD + kt) * 64 + lane];
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt)
+                if (kt * KT <= 16 * rt + 15) am[rt][kt] = mq[(rt * NKC + kt) * 64 + lane];
+        }
+        f32x4 O[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // O = Qg S
+        wait_flag(flagS, c + 1);
+        u32x4 SB[NKD];
+#pragma unroll
+        for (int kt = 0; kt < NKD; ++kt) SB[kt] = xS[kt * 64 + lane];
+#pragma unroll
+        for (int kt = 0; kt < NKD; ++kt)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if constexpr (BF) O[rt] = mma_k32(aq[rt][kt], SB[kt], O[rt]);
+                else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, aq[rt][kt]),
+                                         __builtin_bit_cast(f32x4, SB[kt]), O[rt]);
+            }
+        // O += M U   (M is lower triangular: k tiles above the diagonal are skipped)
+        wait_flag(flagU, c + 1);
+        u32x4 UB[NKC];
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt) UB[kt] = xU[kt * 64 + lane];
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (kt * KT > 16 * rt + 15) continue;
+                if constexpr (BF) O[rt] = mma_k32(am[rt][kt], UB[kt], O[rt]);
+                else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, am[rt][kt]),
+                                         __builtin_bit_cast(f32x4, UB[kt]), O[rt]);
+            }
+        // o rows into this slice's tile of buffer c & 1 (row-major [C][16]); the loader
+        // waves store it during the next chunk
+        T *otile = reinterpret_cast<T *>(otile_base + ((c & 1) * nw + sl) * SL::OTILE);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 io<T>::st(&otile[(16 * rt + 4 * lg + ii) * 16 + li], O[rt][ii]);
-        t0prev = start + static_cast<int64_t>(c) * C;
-        Lprev = static_cast<int>(min<int64_t>(C, end - t0prev));
+        wait_lds();                         // tile writes done before the next barrier
     }
-    if (nchunks > 0) {
-        wait_lds();
-        store_o();
-    }
-    if (p.S_T) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                p.S_T[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = S[rt][ii];
-    }
+    if (nchunks > 0) raw_barrier();         // hand the last o tiles to the loaders
 }
 
 // ---------------------------------------------------------------------------------------
@@ -852,13 +959,14 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
         hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV>), dim3(grid), dim3(512), 0, st, p);
     }
-    // K2: compute waves per workgroup (plus one prefetch wave). More waves share one copy of
-    // each chunk's operands in LDS; fewer spread a small batch over more CUs.
+    // K2: column slices per workgroup (each with a chain and an output wave, plus the
+    // loader waves). More slices share one copy of each chunk's operands in LDS; fewer
+    // spread a small batch over more CUs.
     using SLy = StageLayout<DK, DV, BF>;
     constexpr size_t kMaxLds = 160 * 1024;          // LDS per workgroup on gfx950
     int nw = 1;
     const int ctiles = DV / 16;
-    while (nw < 4 && ctiles % (2 * nw) == 0 &&
+    while (nw < 2 && ctiles % (2 * nw) == 0 &&
            static_cast<int64_t>(p.num_pairs) * ctiles / (2 * nw) >= 256 &&
            SLy::lds_bytes(2 * nw) <= kMaxLds)
         nw *= 2;
@@ -872,7 +980,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     const int64_t pairs8 = (static_cast<int64_t>(p.num_pairs) + 7) / 8 * 8;
     const int64_t blocks = pairs8 * p.nslices;
     if (blocks > 0) {
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (nw + kLoaders)), lds, st, p);
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (2 * nw + kLoaders)), lds, st, p);
     }
     return hipGetLastError();
 }

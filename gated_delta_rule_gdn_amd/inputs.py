@@ -3,9 +3,11 @@
 This module is the only code shared by the GPU path's tests/benchmark and the CPU
 oracle. It holds none of the method's arithmetic: it only draws random tensors
 with the shapes and value distributions of the workloads and casts them to the
-working dtype. Everything is drawn on the host with numpy's PCG64 in a fixed
-order (lengths, q, k, v, log_alpha, b, w, S0) in fp32, then rounded to the
-working dtype by torch, so both sides read exactly the same values.
+working dtype. Everything that is compared with the oracle is drawn on the host
+with numpy's PCG64 in a fixed order (lengths, q, k, v, log_alpha, b, w, S0) in
+fp32, then rounded to the working dtype by torch, so both sides read exactly the
+same values. The *_device variants draw the same distributions on the GPU with a
+seeded torch generator, for timing runs whose outputs are not compared.
 
 Distributions (one reading per workload, recorded in the design doc):
   q, k       ~ N(0,1), L2-normalised per (token, head) before the cast
@@ -152,6 +154,63 @@ def decode_inputs(wl: DecodeWorkload, seed: int, steps: Optional[int] = None) ->
     out = draw_gates(rng, (st, wl.num_seqs), wl.h_k, wl.h_v, wl.d_k, wl.d_v, False, wl.dtype)
     out["S"] = torch.from_numpy(
         _normal(rng, (wl.num_seqs, wl.h_v, wl.d_k, wl.d_v)) * np.float32(wl.s0_std))
+    return out
+
+
+def chunk_inputs_device(wl: ChunkWorkload, seed: int, device="cuda") -> dict:
+    """Same shapes and distributions as ``chunk_inputs``, drawn directly on the GPU with a
+    seeded torch generator (for timing runs of large workloads, where host generation would
+    dominate). The values differ from ``chunk_inputs`` for the same seed; the packed lengths
+    are drawn on the host with the same numpy recipe."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    if wl.num_seqs > 0:
+        lens = _rng(seed).integers(wl.len_lo, wl.len_hi, size=wl.num_seqs, endpoint=True)
+        cu = np.zeros(wl.num_seqs + 1, dtype=np.int64)
+        cu[1:] = np.cumsum(lens)
+        B, T, N = 1, int(cu[-1]), wl.num_seqs
+        cu_t = torch.from_numpy(cu.astype(np.int32)).to(device)
+    else:
+        B, T, N = wl.batch, wl.seqlen, wl.batch
+        cu_t = None
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+
+    out = {"q": unit(normal(B, T, wl.h_k, wl.d_k)), "k": unit(normal(B, T, wl.h_k, wl.d_k)),
+           "v": normal(B, T, wl.h_v, wl.d_v),
+           "log_alpha": -torch.nn.functional.softplus(normal(B, T, wl.h_v, wl.d_k)),
+           "b": torch.sigmoid(normal(B, T, wl.h_v, wl.d_k)) * (2.0 if wl.neg_eig else 1.0),
+           "w": torch.sigmoid(normal(B, T, wl.h_v, wl.d_v))}
+    out = {n: x.to(wl.dtype).contiguous() for n, x in out.items()}
+    out["S0"] = None if wl.s0_std is None else normal(N, wl.h_v, wl.d_k, wl.d_v) * wl.s0_std
+    out["cu_seqlens"] = cu_t
+    out["num_seqs"] = N
+    return out
+
+
+def decode_inputs_device(wl: DecodeWorkload, seed: int, steps: int, device="cuda") -> dict:
+    """Decode inputs drawn on the GPU (same shapes and distributions as ``decode_inputs``)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+
+    N = wl.num_seqs
+    out = {"q": unit(normal(steps, N, wl.h_k, wl.d_k)), "k": unit(normal(steps, N, wl.h_k, wl.d_k)),
+           "v": normal(steps, N, wl.h_v, wl.d_v),
+           "log_alpha": -torch.nn.functional.softplus(normal(steps, N, wl.h_v, wl.d_k)),
+           "b": torch.sigmoid(normal(steps, N, wl.h_v, wl.d_k)),
+           "w": torch.sigmoid(normal(steps, N, wl.h_v, wl.d_v))}
+    out = {n: x.to(wl.dtype).contiguous() for n, x in out.items()}
+    out["S"] = normal(N, wl.h_v, wl.d_k, wl.d_v) * wl.s0_std
     return out
 
 
