@@ -81,7 +81,13 @@ struct ChunkParams {
     void *o;
     float *S_T;
     char *rec;           // first per-(chunk, head) record
+    // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of
+    // every pair are split into nseg segments of seg_len chunks that run concurrently.
+    float *seg_S;        // [pair][nseg][DK][DV]    state entering each segment (0: copy of S0)
+    float *seg_P;        // [pair][nseg-2][DK][DK]  transition of segments 1 .. nseg-2
+    float *seg_R;        // [pair][nseg-2][DK][DV]  end state of segments 1 .. nseg-2 from 0
     int seqlen, num_seqs, h_k, h_v, group, nc_dense, num_pairs, nslices;
+    int nseg, seg_len;
 };
 
 // Locates chunk `chunk` of the batch: sequence n, its chunk index j, and token range.
@@ -239,28 +245,39 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         lc.L = static_cast<int>(min<int64_t>(C, end - lc.t0));
         lc.rec = static_cast<size_t>(item);
     };
-    // raw 16-byte vectors of a record (rows >= L are zero: identity tokens)
+    // raw 16-byte vectors of a record (rows >= L are zero: identity tokens), loaded in four
+    // parts: a workgroup that issues all 96 KB at once stalls at the issue until most of it
+    // has arrived, so the next record's parts are issued one per phase instead.
     u32x4 rk[RAWV], rq[RAWV], rb[RAWV], rl[RAWV], rw[RAWW], rv[RAWW];
-    auto load_raw = [&](const PrepLoc &lc) {
+    auto load_gate = [&](const PrepLoc &lc, const T *src, u32x4 *dst) {   // [C][H_v][DK]
 #pragma unroll
         for (int e = 0; e < RAWV; ++e) {
             const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            rk[e] = z; rq[e] = z; rb[e] = z; rl[e] = z;
+            dst[e] = u32x4{0u, 0u, 0u, 0u};
+            if (r < lc.L)
+                dst[e] = *reinterpret_cast<const u32x4 *>(
+                    src + (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DK + cv * VEC);
+        }
+    };
+    auto load_qk = [&](const PrepLoc &lc) {                               // [C][H_k][DK]
+#pragma unroll
+        for (int e = 0; e < RAWV; ++e) {
+            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
+            rk[e] = u32x4{0u, 0u, 0u, 0u};
+            rq[e] = rk[e];
             if (r < lc.L) {
                 const size_t ok = (static_cast<size_t>(lc.t0 + r) * p.h_k + lc.hk) * DK + cv * VEC;
-                const size_t og = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DK + cv * VEC;
                 rk[e] = *reinterpret_cast<const u32x4 *>(kp + ok);
                 rq[e] = *reinterpret_cast<const u32x4 *>(qp + ok);
-                rb[e] = *reinterpret_cast<const u32x4 *>(bp + og);
-                rl[e] = *reinterpret_cast<const u32x4 *>(lap + og);
             }
         }
+    };
+    auto load_wv = [&](const PrepLoc &lc) {                               // [C][H_v][DV]
 #pragma unroll
         for (int e = 0; e < RAWW; ++e) {
             const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            rw[e] = z; rv[e] = z;
+            rw[e] = u32x4{0u, 0u, 0u, 0u};
+            rv[e] = rw[e];
             if (r < lc.L) {
                 const size_t ov = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DV + cv * VEC;
                 rw[e] = *reinterpret_cast<const u32x4 *>(wp + ov);
@@ -273,7 +290,10 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
     PrepLoc cur;
     if (item < nitems) {
         locate(item, cur);
-        load_raw(cur);
+        load_gate(cur, lap, rl);
+        load_qk(cur);
+        load_gate(cur, bp, rb);
+        load_wv(cur);
     }
     for (; item < nitems; item += gridDim.x) {
         const int next = item + gridDim.x;
@@ -328,6 +348,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             }
         }
         if (tid < DK) reinterpret_cast<float *>(rec + R_::gC)[tid] = __expf(s_g[(C - 1) * SG + tid]);
+        __syncthreads();                         // s_fmid is read by the tile loop below
         char *qgrec = rec + R_::Qg;
 #pragma unroll
         for (int e = 0; e < RAWV; ++e) {
@@ -344,7 +365,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                 kh[s] = bb[s] * kk[s] * ef;
                 qh[s] = qq[s] * ef;
                 kb[s] = kk[s] * ei;
-                qg[s] = qq[s] * __expf(gr);
+                qg[s] = qh[s] * s_fmid[(r >> 4) * DK + c0 + s];   // q exp(g_r)
             }
             *reinterpret_cast<u32x4 *>(&s_kh[r * SK + c0]) = pack16<BF>(kh);
             *reinterpret_cast<u32x4 *>(&s_qh[r * SK + c0]) = pack16<BF>(qh);
@@ -378,7 +399,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             *reinterpret_cast<u32x4 *>(&s_wv[r * SV + cv * VEC]) = pack16<BF>(prod);
         }
         __syncthreads();
-        if (has_next) load_raw(nxt);           // next record's raw tiles, in flight from here
+        if (has_next) load_gate(nxt, lap, rl);   // next record's raw tiles: first part
 
         // ---- phase 1: A^T and M^T blocks (R >= I); zero upper blocks of M ----
         char *mrec = rec + R_::M;
@@ -443,6 +464,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         __syncthreads();
 
         // ---- phase 2a: diagonal inverses (wave 0) || KgT (waves 1-7) ----
+        if (has_next) load_qk(nxt);
         if (wave == 0) {
             const int R = lane >> 4, jc = lane & 15;      // column jc of T_RR
             const float *Ab = &s_A[16 * R * SA + 16 * R];
@@ -479,6 +501,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         __syncthreads();
 
         // ---- phase 2b: off-diagonal blocks of T by levels d = R - I ----
+        if (has_next) load_gate(nxt, bp, rb);
 #pragma unroll
         for (int d = 1; d < 4; ++d) {
             if (wave < 4 - d) {
@@ -501,6 +524,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         }
 
         // ---- phase 3: W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) ----
+        if (has_next) load_wv(nxt);
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             const bool isW = which == 0;
@@ -597,7 +621,7 @@ struct StageLayout {
         return SHARED + GCB + nw * UTS;
     }
     __host__ __device__ static constexpr size_t lds_bytes(int nw) {
-        return 2 * buffer_bytes(nw) + 2 * nw * OTILE + nw * XCH + 64;
+        return 2 * buffer_bytes(nw) + 2 * nw * OTILE + nw * XCH;
     }
     static_assert(lds_bytes(1) <= 160 * 1024, "stage must fit in LDS");
 };
@@ -618,10 +642,13 @@ __device__ __forceinline__ void raw_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// An int in LDS, accessed with plain LDS instructions (no generic-pointer path).
+typedef __attribute__((address_space(3))) volatile int lds_flag;
+
 // Spin (bounded) until an LDS flag written by another wave of the workgroup reaches `want`.
 // The writer is always able to progress, so the bound is never reached in a correct run; it
 // only guarantees that every wave exits.
-__device__ __forceinline__ void wait_flag(volatile int *flag, int want) {
+__device__ __forceinline__ void wait_flag(lds_flag *flag, int want) {
     for (int spin = 0; spin < (1 << 22); ++spin) {
         if (*flag >= want) break;
         __builtin_amdgcn_s_sleep(1);
@@ -647,13 +674,18 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
     const size_t BUF = SL::buffer_bytes(nw);
     char *otile_base = smem + 2 * BUF;
     char *xch_base = otile_base + 2 * nw * SL::OTILE;
-    int *flags = reinterpret_cast<int *>(xch_base + nw * SL::XCH);   // [nw] S, [nw] U
+    // Per-slice publication counters ([slice] S, [2 + slice] U). A static LDS array, so
+    // every access is a plain LDS instruction: LDS operations of one wave complete in
+    // issue order, so a counter written after the data it announces is never seen
+    // ahead of that data.
+    __shared__ int flags[4];
 
-    // XCD-aware decode: the column slices of one (sequence, head) pair share an XCD.
+    // XCD-aware decode: the column slices of one (pair, segment) unit share an XCD.
     const int bid = blockIdx.x, xcd = bid & 7, rest = bid >> 3;
     const int slice = rest % p.nslices;
-    const int pair = (rest / p.nslices) * 8 + xcd;
-    if (pair >= p.num_pairs) return;
+    const int unit = (rest / p.nslices) * 8 + xcd;
+    if (unit >= p.num_pairs * p.nseg) return;
+    const int pair = unit / p.nseg, seg = unit - pair * p.nseg;
     const int n = pair / p.h_v, h = pair - n * p.h_v;
 
     int64_t start, end;
@@ -668,6 +700,9 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
         cbase = p.map[n];
     }
     const int nchunks = static_cast<int>((end - start + C - 1) / C);
+    // this workgroup's chunks [cb, ce) (the whole sequence when nseg == 1)
+    const int cb = p.nseg > 1 ? seg * p.seg_len : 0;
+    const int ce = p.nseg > 1 ? min(nchunks, cb + p.seg_len) : nchunks;
     auto record = [&](int c) {
         return p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
     };
@@ -689,13 +724,13 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                 for (int b = ldr; b < static_cast<int>(nw * SL::UTS / 1024); b += kCopyWaves)
                     dma16(us + b * 1024 + lane * 16, ud + b * 1024);
             };
-            if (nchunks > 0) issue(0, smem);
-            for (int c = 0; c < nchunks; ++c) {
+            if (ce > cb) issue(cb, smem + (cb & 1) * BUF);
+            for (int c = cb; c < ce; ++c) {
                 wait_vmem();                // this wave's copies for chunk c have landed
                 raw_barrier();              // chunk c is staged; chunk c-1 fully consumed
-                if (c + 1 < nchunks) issue(c + 1, smem + ((c + 1) & 1) * BUF);
+                if (c + 1 < ce) issue(c + 1, smem + ((c + 1) & 1) * BUF);
             }
-            if (nchunks > 0) raw_barrier();
+            if (ce > cb) raw_barrier();
             return;
         }
         // ---- store wave: o of chunk c - 1 (o tiles of buffer (c-1) & 1) during chunk c
@@ -718,13 +753,13 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
             }
             wait_lds();                     // tile reads done before the next barrier
         };
-        for (int c = 0; c < nchunks; ++c) {
+        for (int c = cb; c < ce; ++c) {
             raw_barrier();
-            if (c > 0) store_o(c - 1);
+            if (c > cb) store_o(c - 1);
         }
-        if (nchunks > 0) {
+        if (ce > cb) {
             raw_barrier();                  // the last chunk's o tiles are written
-            store_o(nchunks - 1);
+            store_o(ce - 1);
         }
         return;
     }
@@ -735,8 +770,8 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
     const int col = 16 * ct + li;
     u32x4 *xS = reinterpret_cast<u32x4 *>(xch_base + sl * SL::XCH);   // published S operands
     u32x4 *xU = xS + NKD * 64;                                         // published U operands
-    volatile int *flagS = flags + sl;
-    volatile int *flagU = flags + nw + sl;
+    lds_flag *flagS = (lds_flag *)(flags + sl);
+    lds_flag *flagU = (lds_flag *)(flags + 2 + sl);
     if (chain && lane == 0) {
         *flagS = 0;
         *flagU = 0;
@@ -747,36 +782,34 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
         // ---- chain wave ----
         f32x4 S[RT];
         const size_t sbase = static_cast<size_t>(pair) * DK * DV;
+        // state entering the first chunk: S0 (or zero), or the segment's start state
+        // (segmented: a copy made before this kernel, since S_T may be the S0 buffer and
+        // the last segment can finish before the first one starts)
+        const float *Sin = p.nseg == 1 ? p.S0
+                                       : p.seg_S + (static_cast<size_t>(pair) * p.nseg + seg) * DK * DV;
+        const size_t ibase = p.nseg == 1 ? sbase : 0;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
-                S[rt][ii] = p.S0 ? p.S0[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col]
-                                 : 0.f;
-        for (int c = 0; c < nchunks; ++c) {
+                S[rt][ii] = Sin ? Sin[ibase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col]
+                                : 0.f;
+        for (int c = cb; c < ce; ++c) {
             const char *cur = smem + (c & 1) * BUF;
             raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
             const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur + R_::Wn);
             const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + R_::KgT);
             const float *gc = reinterpret_cast<const float *>(cur + SL::SHARED);
             const char *ut = cur + SL::SHARED + SL::GCB + sl * SL::UTS;
-            // publish S (chunk entry) as B operands
-            u32x4 SB[NKD];
-#pragma unroll
-            for (int kt = 0; kt < NKD; ++kt) {
-                if constexpr (BF) SB[kt] = dpair_to_b32(S[2 * kt], S[2 * kt + 1]);
-                else SB[kt] = __builtin_bit_cast(u32x4, S[kt]);
-                xS[kt * 64 + lane] = SB[kt];
-            }
-            wait_lds();
-            if (lane == 0) *flagS = c + 1;
-            // U = U~ + Wn S
+            // all operands of U = U~ + Wn S go in flight first
             u32x4 aw[4][NKD];
             f32x4 U[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
+            for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int kt = 0; kt < NKD; ++kt) aw[rt][kt] = wn[(rt * NKD + kt) * 64 + lane];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
                 if constexpr (BF) {
                     const u32x2 u = reinterpret_cast<const u32x2 *>(ut + rt * R_::UT_TILE)[lane];
                     U[rt] = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
@@ -784,6 +817,16 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                     U[rt] = reinterpret_cast<const f32x4 *>(ut + rt * R_::UT_TILE)[lane];
                 }
             }
+            // publish S (chunk entry) as B operands, then its counter
+            u32x4 SB[NKD];
+#pragma unroll
+            for (int kt = 0; kt < NKD; ++kt) {
+                if constexpr (BF) SB[kt] = dpair_to_b32(S[2 * kt], S[2 * kt + 1]);
+                else SB[kt] = __builtin_bit_cast(u32x4, S[kt]);
+                xS[kt * 64 + lane] = SB[kt];
+            }
+            if (lane == 0) *flagS = c + 1;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kt = 0; kt < NKD; ++kt)
 #pragma unroll
@@ -791,7 +834,16 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                     if constexpr (BF) U[rt] = mma_k32(aw[rt][kt], SB[kt], U[rt]);
                     else U[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, aw[rt][kt]), S[kt], U[rt]);
                 }
-            // publish U as B operands
+            __builtin_amdgcn_sched_barrier(0);
+            // KgT operands and the decay of S, while the last U products drain
+            u32x4 ak[RT][NKC];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
+            // publish U as B operands, then its counter
             u32x4 UB[NKC];
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) {
@@ -799,17 +851,8 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                 else UB[kt] = __builtin_bit_cast(u32x4, U[kt]);
                 xU[kt * 64 + lane] = UB[kt];
             }
-            wait_lds();
             if (lane == 0) *flagU = c + 1;
             // S = gamma_C S + KgT U
-            u32x4 ak[RT][NKC];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt)
 #pragma unroll
@@ -817,10 +860,10 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                     if constexpr (BF) S[rt] = mma_k32(ak[rt][kt], UB[kt], S[rt]);
                     else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, ak[rt][kt]), U[kt], S[rt]);
                 }
-            wait_lds();
+            wait_lds();                     // this chunk's LDS reads and writes are done
         }
-        if (nchunks > 0) raw_barrier();     // pairs with the loaders' final barrier
-        if (p.S_T) {
+        if (ce > cb) raw_barrier();         // pairs with the loaders' final barrier
+        if (p.S_T && seg == p.nseg - 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -831,7 +874,7 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
     }
 
     // ---- output wave ----
-    for (int c = 0; c < nchunks; ++c) {
+    for (int c = cb; c < ce; ++c) {
         const char *cur = smem + (c & 1) * BUF;
         raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
         const u32x4 *qg = reinterpret_cast<const u32x4 *>(cur + R_::Qg);
@@ -875,8 +918,8 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                 else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, am[rt][kt]),
                                          __builtin_bit_cast(f32x4, UB[kt]), O[rt]);
             }
-        // o rows into this slice's tile of buffer c & 1 (row-major [C][16]); the loader
-        // waves store it during the next chunk
+        // o rows into this slice's tile of buffer c & 1 (row-major [C][16]); the store wave
+        // writes it to memory during the next chunk
         T *otile = reinterpret_cast<T *>(otile_base + ((c & 1) * nw + sl) * SL::OTILE);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -885,7 +928,256 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                 io<T>::st(&otile[(16 * rt + 4 * lg + ii) * 16 + li], O[rt][ii]);
         wait_lds();                         // tile writes done before the next barrier
     }
-    if (nchunks > 0) raw_barrier();         // hand the last o tiles to the loaders
+    if (ce > cb) raw_barrier();             // hand the last o tiles to the store wave
+}
+
+// ---------------------------------------------------------------------------------------
+// Segmented state pass. The state recursion over chunks is affine in S:
+//   S_{c+1} = (diag(gamma_C) + KgT Wn) S_c + KgT U~  =:  A_c S_c + B_c
+// so over a segment of chunks S_end = P S_start + R, with P the product of the A_c and R
+// the end state reached from S_start = 0. When a dense batch has too few (sequence, head)
+// pairs to fill the GPU, the chunks of each pair are cut into nseg segments:
+//   K2a chunk_seg_kernel   segment 0: a copy of S0 and the true end state from S0 (= state
+//                          entering segment 1); segments 1 .. nseg-2: P (the chain run on the
+//                          columns of the identity, without U~) and R (from zero). All
+//                          segments run concurrently; only the chain is computed.
+//   K2s chunk_scan_kernel  start states S_{g+1} = P_g S_g + R_g, g = 1 .. nseg-2, in fp32 on
+//                          the matrix cores.
+//   K2  chunk_state_kernel every segment from its start state, with outputs.
+// ---------------------------------------------------------------------------------------
+constexpr int kSegWaves = 4;   // chain waves per segment-pass workgroup
+constexpr int kSegCopy = 4;    // copy waves per segment-pass workgroup
+
+template <int DK, int DV, bool BF>
+struct SegLayout {
+    using R_ = Rec<DK, DV, BF>;
+    static constexpr size_t OPB = static_cast<size_t>(kChunk) * DK * Op<BF>::E;   // Wn / KgT
+    static constexpr size_t KG = OPB;                       // KgT offset in a stage
+    static constexpr size_t GC = 2 * OPB;                   // gamma_C
+    static constexpr size_t UT = GC + DK * 4;               // U~ tiles of the R slices
+    static constexpr size_t UTS = 4 * R_::UT_TILE;          // one column tile of U~
+    static constexpr size_t BUF = UT + kSegWaves * UTS;
+    static constexpr size_t LDS = 2 * BUF;
+    static constexpr int NP = DK / 16, NR = DV / 16;        // P and R column slices
+    static constexpr int NV = NP + NR;
+    static constexpr int GROUPS = (NV + kSegWaves - 1) / kSegWaves;   // workgroups per unit
+    static_assert(LDS <= 160 * 1024, "segment stage must fit in LDS");
+    static_assert(R_::KgT - R_::Qg == OPB, "record layout");
+};
+
+template <typename T, bool BF, int DK, int DV>
+__global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(ChunkParams p) {
+    using R_ = Rec<DK, DV, BF>;
+    using SG = SegLayout<DK, DV, BF>;
+    constexpr int C = kChunk, RT = DK / 16;
+    constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, lg = lane >> 4;
+
+    // unit = (pair, segment g < nseg - 1); its GROUPS workgroups share an XCD
+    const int bid = blockIdx.x, xcd = bid & 7, rest = bid >> 3;
+    const int grp = rest % SG::GROUPS;
+    const int unit = (rest / SG::GROUPS) * 8 + xcd;
+    const int nsa = p.nseg - 1;
+    if (unit >= p.num_pairs * nsa) return;
+    const int pair = unit / nsa, g = unit - pair * nsa;
+    const int h = pair % p.h_v, n = pair / p.h_v;
+    // virtual slices of this workgroup: v < NP are P columns (segments >= 1 only),
+    // v >= NP are R columns
+    const int v0 = grp * kSegWaves;
+    const int vlo = g == 0 ? (v0 > SG::NP ? v0 : SG::NP) : v0;
+    const int vhi = min(v0 + kSegWaves, SG::NV);
+    if (vlo >= vhi) return;                       // uniform over the workgroup
+    const int rlo = max(vlo, SG::NP) - SG::NP;     // R slices [rlo, rhi) are staged
+    const int rhi = max(vhi, SG::NP) - SG::NP;
+
+    const int cb = g * p.seg_len;
+    const int ce = min(p.nc_dense, cb + p.seg_len);
+    const int cbase = n * p.nc_dense;
+    auto record = [&](int c) {
+        return p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
+    };
+
+    if (wave >= kSegWaves) {
+        // ---- copy waves: Wn, KgT, gamma_C and the R slices' U~ of chunk c + 1
+        const int ldr = wave - kSegWaves;
+        auto issue = [&](int c, char *dst) {
+            const char *rec = record(c);
+            for (int blk = ldr; blk < static_cast<int>(SG::OPB / 1024); blk += kSegCopy) {
+                dma16(rec + R_::Wn + blk * 1024 + lane * 16, dst + blk * 1024);
+                dma16(rec + R_::KgT + blk * 1024 + lane * 16, dst + SG::KG + blk * 1024);
+            }
+            if (ldr == kSegCopy - 1 && lane < DK / 4) dma16(rec + R_::gC + lane * 16, dst + SG::GC);
+            const char *us = rec + R_::Ut + static_cast<size_t>(rlo) * SG::UTS;
+            for (int b = ldr; b < static_cast<int>((rhi - rlo) * SG::UTS / 1024); b += kSegCopy)
+                dma16(us + b * 1024 + lane * 16, dst + SG::UT + b * 1024);
+        };
+        if (ce > cb) issue(cb, smem + (cb & 1) * SG::BUF);
+        for (int c = cb; c < ce; ++c) {
+            wait_vmem();
+            raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
+            if (c + 1 < ce) issue(c + 1, smem + ((c + 1) & 1) * SG::BUF);
+        }
+        return;
+    }
+
+    // ---- chain waves ----
+    const int v = v0 + wave;
+    const bool active = v >= vlo && v < vhi;
+    const bool isP = v < SG::NP;
+    const int col = 16 * (isP ? v : v - SG::NP) + li;
+    f32x4 S[RT];
+    float *segS = p.seg_S + static_cast<size_t>(pair) * p.nseg * DK * DV;
+    const bool fromS0 = active && !isP && g == 0 && p.S0 != nullptr;
+    // all loads first, then the copies of segment 0's start state
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int row = 16 * rt + 4 * lg + ii;
+            S[rt][ii] = fromS0 ? p.S0[(static_cast<size_t>(pair) * DK + row) * DV + col]
+                               : ((isP && row == col) ? 1.f : 0.f);
+        }
+    if (active && g == 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                segS[static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = S[rt][ii];
+    }
+    for (int c = cb; c < ce; ++c) {
+        const char *cur = smem + (c & 1) * SG::BUF;
+        raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
+        if (!active) continue;
+        const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur);
+        const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + SG::KG);
+        const float *gc = reinterpret_cast<const float *>(cur + SG::GC);
+        const char *ut = cur + SG::UT + (isP ? 0 : (v - SG::NP - rlo)) * SG::UTS;
+        u32x4 aw[4][NKD];
+        f32x4 U[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int kt = 0; kt < NKD; ++kt) aw[rt][kt] = wn[(rt * NKD + kt) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (!isP) {
+                if constexpr (BF) {
+                    const u32x2 u = reinterpret_cast<const u32x2 *>(ut + rt * R_::UT_TILE)[lane];
+                    U[rt] = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
+                } else {
+                    U[rt] = reinterpret_cast<const f32x4 *>(ut + rt * R_::UT_TILE)[lane];
+                }
+            }
+        }
+        u32x4 SB[NKD];
+#pragma unroll
+        for (int kt = 0; kt < NKD; ++kt) {
+            if constexpr (BF) SB[kt] = dpair_to_b32(S[2 * kt], S[2 * kt + 1]);
+            else SB[kt] = __builtin_bit_cast(u32x4, S[kt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kt = 0; kt < NKD; ++kt)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if constexpr (BF) U[rt] = mma_k32(aw[rt][kt], SB[kt], U[rt]);
+                else U[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, aw[rt][kt]), S[kt], U[rt]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 ak[RT][NKC];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
+        u32x4 UB[NKC];
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt) {
+            if constexpr (BF) UB[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
+            else UB[kt] = __builtin_bit_cast(u32x4, U[kt]);
+        }
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                if constexpr (BF) S[rt] = mma_k32(ak[rt][kt], UB[kt], S[rt]);
+                else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, ak[rt][kt]), U[kt], S[rt]);
+            }
+        wait_lds();
+    }
+    if (!active) return;
+    float *dst;
+    int ld;
+    if (g == 0) {                            // state entering segment 1
+        dst = segS + static_cast<size_t>(DK) * DV;
+        ld = DV;
+    } else if (isP) {
+        dst = p.seg_P + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DK;
+        ld = DK;
+    } else {
+        dst = p.seg_R + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DV;
+        ld = DV;
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            dst[static_cast<size_t>(16 * rt + 4 * lg + ii) * ld + col] = S[rt][ii];
+}
+
+// K2s: start states of segments 2 .. nseg-1, S_{g+1} = P_g S_g + R_g in fp32. One
+// workgroup per (pair, 16 columns of S); wave w computes row tile w with fp32 matrix-core
+// products (A = rows of P_g straight from memory, B = S_g from LDS).
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (DK / 16)) void chunk_scan_kernel(ChunkParams p) {
+    constexpr int RT = DK / 16;
+    __shared__ __attribute__((aligned(16))) float sS[DK][16];
+    const int pair = blockIdx.x / (DV / 16), cbk = blockIdx.x % (DV / 16);
+    if (pair >= p.num_pairs) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int nsa = p.nseg - 1;
+    float *Sp = p.seg_S + static_cast<size_t>(pair) * p.nseg * DK * DV;   // [nseg][DK][DV]
+    const int col = 16 * cbk + li;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int row = 16 * wave + 4 * lg + ii;
+        sS[row][li] = Sp[static_cast<size_t>(DK + row) * DV + col];
+    }
+    __syncthreads();
+    for (int g = 1; g < nsa; ++g) {
+        const float *P = p.seg_P + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DK;
+        const float *R = p.seg_R + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DV;
+        f32x4 a[RT];
+#pragma unroll
+        for (int kt = 0; kt < RT; ++kt)
+            a[kt] = *reinterpret_cast<const f32x4 *>(P + static_cast<size_t>(16 * wave + li) * DK +
+                                                     16 * kt + 4 * lg);
+        f32x4 acc;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            acc[ii] = R[static_cast<size_t>(16 * wave + 4 * lg + ii) * DV + col];
+        __builtin_amdgcn_sched_barrier(0);   // every load of the step is in flight
+#pragma unroll
+        for (int kt = 0; kt < RT; ++kt) {
+            f32x4 b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = sS[16 * kt + 4 * lg + e][li];
+            acc = mma_k16_f32(a[kt], b, acc);
+        }
+        __syncthreads();                     // every wave has read S_g
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int row = 16 * wave + 4 * lg + ii;
+            sS[row][li] = acc[ii];
+            Sp[static_cast<size_t>((g + 1) * DK + row) * DV + col] = acc[ii];
+        }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -906,11 +1198,52 @@ size_t chunk_map_bytes(int num_seqs, bool packed) {
     return packed ? (static_cast<size_t>(num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
 }
 
+// Segmentation of the state pass: dense batches only, aiming at about kSegTargetWGs
+// workgroups of two column slices, with at least 4 chunks per segment.
+constexpr int64_t kSegTargetWGs = 256;
+
+struct SegPlan {
+    int nseg, seg_len;
+};
+
+static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v) {
+    SegPlan sp{1, nc};
+    const int64_t per_unit = d_v / 32;             // workgroups of two 16-column slices
+    if (packed || pairs <= 0 || nc < 8 || per_unit <= 0) return sp;
+    int64_t G = kSegTargetWGs / (pairs * per_unit);
+    if (G > nc / 4) G = nc / 4;
+    if (G < 2) return sp;
+    const int L = static_cast<int>((nc + G - 1) / G);
+    sp.nseg = (nc + L - 1) / L;
+    sp.seg_len = L;
+    return sp;
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// fp32 segment buffers: start states [pair][nseg][d_k][d_v], transitions
+// [pair][nseg-2][d_k][d_k] and zero-start end states [pair][nseg-2][d_k][d_v]
+static void seg_area(const SegPlan &sp, int64_t pairs, int d_k, int d_v, size_t off[3],
+                     size_t *total) {
+    const size_t nS = sp.nseg > 1 ? static_cast<size_t>(sp.nseg) : 0;
+    const size_t nPR = sp.nseg > 2 ? static_cast<size_t>(sp.nseg - 2) : 0;
+    off[0] = 0;
+    off[1] = off[0] + align256(pairs * nS * d_k * d_v * 4);
+    off[2] = off[1] + align256(pairs * nPR * d_k * d_k * 4);
+    *total = off[2] + align256(pairs * nPR * d_k * d_v * 4);
+}
+
 size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
                              bool bf16, bool packed) {
+    const int64_t nc = (static_cast<int64_t>(seqlen) + kChunk - 1) / kChunk;
+    const int64_t pairs = static_cast<int64_t>(packed ? num_seqs : batch) * h_v;
+    const SegPlan sp = chunk_seg_plan(packed, pairs, static_cast<int>(nc), d_v);
+    size_t off[3], segb;
+    seg_area(sp, pairs, d_k, d_v, off, &segb);
     return chunk_map_bytes(num_seqs, packed) +
            static_cast<size_t>(chunk_upper_bound(batch, seqlen, num_seqs, packed)) * h_v *
-               chunk_record_bytes(d_k, d_v, bf16);
+               chunk_record_bytes(d_k, d_v, bf16) +
+           segb;
 }
 
 bool chunk_dims_built(int d_k, int d_v, bool bf16) {
@@ -949,25 +1282,53 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.group = a.h_v / a.h_k;
     p.nc_dense = (a.seqlen + kChunk - 1) / kChunk;
     p.num_pairs = N * a.h_v;
+    const int64_t nrec = chunk_upper_bound(a.batch, a.seqlen, N, packed);
+    const SegPlan sp = chunk_seg_plan(packed, p.num_pairs, p.nc_dense, DV);
+    p.nseg = sp.nseg;
+    p.seg_len = sp.seg_len;
+    {
+        size_t off[3], segb;
+        seg_area(sp, p.num_pairs, DK, DV, off, &segb);
+        char *seg_base = p.rec + static_cast<size_t>(nrec) * a.h_v * Rec<DK, DV, BF>::bytes;
+        p.seg_S = reinterpret_cast<float *>(seg_base + off[0]);
+        p.seg_P = reinterpret_cast<float *>(seg_base + off[1]);
+        p.seg_R = reinterpret_cast<float *>(seg_base + off[2]);
+    }
     if (packed) {
         hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(64), 0, st, a.cu_seqlens,
                            reinterpret_cast<int32_t *>(a.workspace), N);
     }
-    const int64_t nchunks = chunk_upper_bound(a.batch, a.seqlen, N, packed);
+    const int64_t nchunks = nrec;
     if (nchunks > 0) {
         const int64_t items = nchunks * a.h_v;
         const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
         hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV>), dim3(grid), dim3(512), 0, st, p);
     }
+    constexpr size_t kMaxLds = 160 * 1024;          // LDS per workgroup on gfx950
+    const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
+    if (p.nseg > 1 && p.num_pairs > 0) {
+        // segment pass, then the scan over segments
+        using SGy = SegLayout<DK, DV, BF>;
+        auto skern = chunk_seg_kernel<T, BF, DK, DV>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           static_cast<int>(SGy::LDS));
+        if (e != hipSuccess) return e;
+        const int64_t ua = static_cast<int64_t>(p.num_pairs) * (p.nseg - 1);
+        const int64_t sblocks = (ua + 7) / 8 * 8 * SGy::GROUPS;
+        hipLaunchKernelGGL(skern, dim3(sblocks), dim3(64 * (kSegWaves + kSegCopy)), SGy::LDS, st, p);
+        if (p.nseg > 2)
+            hipLaunchKernelGGL((chunk_scan_kernel<DK, DV>), dim3(p.num_pairs * (DV / 16)),
+                               dim3(64 * (DK / 16)), 0, st, p);
+    }
     // K2: column slices per workgroup (each with a chain and an output wave, plus the
     // loader waves). More slices share one copy of each chunk's operands in LDS; fewer
     // spread a small batch over more CUs.
     using SLy = StageLayout<DK, DV, BF>;
-    constexpr size_t kMaxLds = 160 * 1024;          // LDS per workgroup on gfx950
     int nw = 1;
     const int ctiles = DV / 16;
     while (nw < 2 && ctiles % (2 * nw) == 0 &&
-           static_cast<int64_t>(p.num_pairs) * ctiles / (2 * nw) >= 256 &&
+           (p.nseg > 1 || units * ctiles / (2 * nw) >= 256) &&
            SLy::lds_bytes(2 * nw) <= kMaxLds)
         nw *= 2;
     p.nslices = ctiles / nw;
@@ -977,8 +1338,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    const int64_t pairs8 = (static_cast<int64_t>(p.num_pairs) + 7) / 8 * 8;
-    const int64_t blocks = pairs8 * p.nslices;
+    const int64_t units8 = (units + 7) / 8 * 8;
+    const int64_t blocks = units8 * p.nslices;
     if (blocks > 0) {
         hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (2 * nw + kLoaders)), lds, st, p);
     }

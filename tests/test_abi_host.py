@@ -114,6 +114,30 @@ def test_workspace_size_formula(L):
     d = Dims(1, 1000, 5, 1, 2, 64, 64, 0)
     rec = (4 * (3 * 64 * 64 + 64 * 64 + 64 * 64) + 4 * 64 + 255) // 256 * 256
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 256 + (16 + 5) * 2 * rec
+    # a dense batch with few (sequence, head) pairs: the state pass is split into segments
+    # (about 256 workgroups of two 16-column slices, at least 4 chunks per segment) and the
+    # workspace adds fp32 states entering each segment [pair][nseg][dk][dv], transitions
+    # [pair][nseg-2][dk][dk] and zero-start end states [pair][nseg-2][dk][dv]
+    def seg_bytes(pairs, nseg, dk, dv):
+        a = lambda x: (x + 255) // 256 * 256       # noqa: E731
+        return (a(pairs * nseg * dk * dv * 4) + a(pairs * (nseg - 2) * dk * dk * 4) +
+                a(pairs * (nseg - 2) * dk * dv * 4))
+    rec = (2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128 + 255) // 256 * 256
+    d = Dims(1, 4096, 0, 16, 16, 128, 128, 1)       # 16 pairs x 64 chunks -> 4 segments
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == \
+        64 * 16 * rec + seg_bytes(16, 4, 128, 128)
+    d = Dims(1, 1000, 0, 1, 2, 128, 128, 1)         # 2 pairs x 16 chunks -> 4 segments
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == \
+        16 * 2 * rec + seg_bytes(2, 4, 128, 128)
+    d = Dims(2, 640, 0, 1, 3, 128, 128, 1)          # 6 pairs x 10 chunks -> 2 segments
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == \
+        2 * 10 * 3 * rec + seg_bytes(6, 2, 128, 128)
+    rec64 = (2 * (3 * 64 * 128 + 64 * 64 + 64 * 64) + 4 * 128 + 255) // 256 * 256
+    d = Dims(1, 2000, 0, 2, 2, 128, 64, 1)          # 2 pairs x 32 chunks -> 8 segments
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == \
+        32 * 2 * rec64 + seg_bytes(2, 8, 128, 64)
+    d = Dims(8, 2048, 0, 8, 8, 128, 128, 1)         # 64 pairs: enough work, no segments
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 8 * 32 * 8 * rec
     assert L.gdn2_chunk_fwd_workspace_bytes(None, 64) == 0
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(Dims(1, 10, 0, 1, 1, 96, 64, 1)),
                                             64) == 0

@@ -12,8 +12,8 @@ import torch
 import oracle
 import gated_delta_rule_gdn_amd as g
 from gated_delta_rule_gdn_amd import inputs
-from gpu_common import (TOL, assert_chunk_parity, decode_oracle_pair, gpu_chunk, np64,
-                        oracle_chunk, flat_inputs)
+from gpu_common import (TOL, assert_chunk_parity, decode_oracle_pair, flat_inputs, gpu_chunk,
+                        np64, oracle_chunk, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +151,38 @@ def test_chunk_zero_initial_state_and_no_final_state():
     assert np.array_equal(o_full, o_only)
     o_r, _ = oracle_chunk(x)
     assert oracle.rel_l2(o_only, o_r) <= 2e-2
+
+
+# Dense batches with few (sequence, head) pairs take the segmented state pass: the chunks
+# of each pair are split into segments that run concurrently (segment transitions, a scan
+# over segments, then every segment from its start state). These shapes give 4, 2, 4 and 8
+# segments (the workspace size test on the CPU pins that plan).
+SEGMENTED = [
+    (torch.bfloat16, 128, 128, 1, 1000, 1, 2, 0.1),
+    (torch.bfloat16, 128, 128, 2, 640, 1, 3, 0.1),
+    (torch.float32, 64, 64, 1, 1024, 1, 1, 0.1),
+    (torch.bfloat16, 128, 64, 1, 2000, 2, 2, None),
+]
+
+
+@pytest.mark.parametrize("dtype,dk,dv,B,T,hk,hv,s0", SEGMENTED)
+def test_segmented_state_pass(dtype, dk, dv, B, T, hk, hv, s0):
+    wl = inputs.small_chunk(dtype=dtype, batch=B, seqlen=T, h_k=hk, h_v=hv, d_k=dk, d_v=dv,
+                            neg_eig=True, s0_std=s0)
+    x = inputs.chunk_inputs(wl, seed=T + hv)
+    assert_chunk_parity(x, dtype, label=f"segmented {dtype} {dk}x{dv} B={B} T={T} hv={hv}")
+
+
+def test_segmented_final_state_may_alias_initial_state():
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=1000, h_k=1, h_v=2, d_k=128,
+                            d_v=128, neg_eig=True, s0_std=0.1)
+    x = inputs.chunk_inputs(wl, seed=77)
+    o_ref, S_ref = gpu_chunk(x)
+    d = to_gpu(x)
+    S = d["S0"].clone()
+    o, S_T = g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=S,
+                         final_state=S)
+    torch.cuda.synchronize()
+    assert S_T.data_ptr() == S.data_ptr()
+    assert np.array_equal(np64(S), S_ref)
+    assert np.array_equal(np64(o).reshape(o_ref.shape), o_ref)
