@@ -173,6 +173,10 @@ __device__ __forceinline__ u32x4 pack16(const float *v) {
 //   3  W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) as tile GEMMs, one column tile of
 //      each per wave, written to the workspace in the orders K2 reads
 // ---------------------------------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x on the transcendental unit (the prep kernel keeps its cumulative decay in log2 units)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 struct PrepLoc {
     int64_t t0;     // first token of the chunk
     int L;          // valid rows
@@ -205,6 +209,8 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
     constexpr int SV = DV + VEC;              // padded row stride of the w.v tile
     constexpr int SG = DK + 4;                // padded row stride of s_g (floats)
     constexpr int SA = C + 4;                 // padded row stride of A and T (floats)
+    constexpr int STB = C + 8;                // row stride of the bf16 copy of T (elements)
+    static_assert(C * STB * 2 <= C * SA * 4, "bf16 T fits in the A space");
     constexpr int VK = DK / VEC, VV = DV / VEC;
     constexpr int RAWV = C * VK / NT, RAWW = C * VV / NT;
     constexpr int PARTS = NT / DK;            // cumulative sum: token parts per channel
@@ -309,9 +315,9 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             float x[VEC];
             unpack16<BF>(rl[e], x);
 #pragma unroll
-            for (int s = 0; s < VEC; s += 4)
+            for (int s = 0; s < VEC; s += 4)     // log2 units: every factor is one exp2
                 *reinterpret_cast<f32x4 *>(&s_g[r * SG + cv * VEC + s]) =
-                    f32x4{x[s], x[s + 1], x[s + 2], x[s + 3]};
+                    f32x4{x[s] * kLog2e, x[s + 1] * kLog2e, x[s + 2] * kLog2e, x[s + 3] * kLog2e};
         }
         __syncthreads();
         {
@@ -336,18 +342,18 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         for (int idx = tid; idx < 14 * DK; idx += NT) {
             const int c = idx % DK, kind = idx / DK;
             if (kind < 4) {
-                s_fmid[kind * DK + c] = __expf(s_g[(16 * kind + 7) * SG + c]);
+                s_fmid[kind * DK + c] = exp2_hw(s_g[(16 * kind + 7) * SG + c]);
             } else if (kind < 8) {
                 const int I = kind - 4;
-                s_fkg[I * DK + c] = __expf(s_g[(C - 1) * SG + c] - s_g[(16 * I + 7) * SG + c]);
+                s_fkg[I * DK + c] = exp2_hw(s_g[(C - 1) * SG + c] - s_g[(16 * I + 7) * SG + c]);
             } else {
                 const int pi = kind - 8;        // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
                 const int R = pi < 1 ? 1 : (pi < 3 ? 2 : 3);
                 const int I = pi - R * (R - 1) / 2;
-                s_foff[pi * DK + c] = __expf(s_g[(16 * R + 7) * SG + c] - s_g[(16 * I + 7) * SG + c]);
+                s_foff[pi * DK + c] = exp2_hw(s_g[(16 * R + 7) * SG + c] - s_g[(16 * I + 7) * SG + c]);
             }
         }
-        if (tid < DK) reinterpret_cast<float *>(rec + R_::gC)[tid] = __expf(s_g[(C - 1) * SG + tid]);
+        if (tid < DK) reinterpret_cast<float *>(rec + R_::gC)[tid] = exp2_hw(s_g[(C - 1) * SG + tid]);
         __syncthreads();                         // s_fmid is read by the tile loop below
         char *qgrec = rec + R_::Qg;
 #pragma unroll
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 #pragma unroll
             for (int s = 0; s < VEC; ++s) {
                 const float gr = s_g[r * SG + c0 + s], gm = s_g[mid + c0 + s];
-                const float ef = __expf(gr - gm), ei = __expf(gm - gr);
+                const float ef = exp2_hw(gr - gm), ei = exp2_hw(gm - gr);
                 kh[s] = bb[s] * kk[s] * ef;
                 qh[s] = qq[s] * ef;
                 kb[s] = kk[s] * ei;
@@ -403,9 +409,12 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 
         // ---- phase 1: A^T and M^T blocks (R >= I); zero upper blocks of M ----
         char *mrec = rec + R_::M;
+        // (R, I) block pairs: the six off-diagonal pairs (which also scale Kbar) go to six
+        // waves, the four cheaper diagonal pairs two each to the other two
+        static_assert(NW == 8, "pair schedule assumes eight waves");
         for (int pr = wave; pr < 10; pr += NW) {
-            const int R = pr >= 6 ? 3 : (pr >= 3 ? 2 : (pr >= 1 ? 1 : 0));
-            const int I = pr - R * (R + 1) / 2;
+            const int R = static_cast<int>((0x3233322110ull >> (4 * pr)) & 0xF);
+            const int I = static_cast<int>((0x3221010010ull >> (4 * pr)) & 0xF);
             const bool diag = (R == I);
             const int pi = diag ? 0 : R * (R - 1) / 2 + I;
             const int ri = 16 * I + li;              // A operand: column-side token i
@@ -501,7 +510,10 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         __syncthreads();
 
         // ---- phase 2b: off-diagonal blocks of T by levels d = R - I ----
-        if (has_next) load_gate(nxt, bp, rb);
+        if (has_next) {
+            load_gate(nxt, bp, rb);
+            load_wv(nxt);
+        }
 #pragma unroll
         for (int d = 1; d < 4; ++d) {
             if (wave < 4 - d) {
@@ -522,9 +534,25 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             }
             __syncthreads();
         }
+        if constexpr (BF) {
+            // bf16 copy of T (zero above the block diagonal) in the s_A space, read by phase 3
+            bf16_t *s_Tb = reinterpret_cast<bf16_t *>(s_A);
+            for (int idx = tid; idx < C * C / 8; idx += NT) {
+                const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
+                float t8[8];
+                const bool live = (c8 >> 4) <= (r >> 4);
+#pragma unroll
+                for (int e = 0; e < 8; e += 4) {
+                    const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s_T[r * SA + c8 + e]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) t8[e + q] = live ? t4[q] : 0.f;
+                }
+                *reinterpret_cast<u32x4 *>(&s_Tb[r * STB + c8]) = pack16<true>(t8);
+            }
+            __syncthreads();
+        }
 
         // ---- phase 3: W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) ----
-        if (has_next) load_wv(nxt);
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             const bool isW = which == 0;
@@ -548,18 +576,20 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     if (kt * KT > 16 * R + 15) break;
                     // T[16R + li][kt*KT + KS*lg + s]; the KS tokens share one 16-block
                     const int tok0 = kt * KT + KS * lg;
-                    float tv[KS];
-                    const bool live = (tok0 >> 4) <= R;
-#pragma unroll
-                    for (int s = 0; s < KS; s += 4) {
-                        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s_T[(16 * R + li) * SA + tok0 + s]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) tv[s + e] = live ? t4[e] : 0.f;
-                    }
                     if constexpr (BF) {
-                        if (isW) acc = mma_k32(pack16<true>(xv[kt]), pack16<true>(tv), acc);
-                        else acc = mma_k32(pack16<true>(tv), pack16<true>(xv[kt]), acc);
+                        const u32x4 tb = *reinterpret_cast<const u32x4 *>(
+                            &reinterpret_cast<const bf16_t *>(s_A)[(16 * R + li) * STB + tok0]);
+                        if (isW) acc = mma_k32(pack16<true>(xv[kt]), tb, acc);
+                        else acc = mma_k32(tb, pack16<true>(xv[kt]), acc);
                     } else {
+                        float tv[KS];
+                        const bool live = (tok0 >> 4) <= R;
+#pragma unroll
+                        for (int s = 0; s < KS; s += 4) {
+                            const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s_T[(16 * R + li) * SA + tok0 + s]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) tv[s + e] = live ? t4[e] : 0.f;
+                        }
 #pragma unroll
                         for (int s = 0; s < 4; ++s)
                             acc = isW ? __builtin_amdgcn_mfma_f32_16x16x4f32(xv[kt][s], tv[s], acc, 0, 0, 0)
