@@ -174,6 +174,18 @@ __device__ __forceinline__ u32x4 pack16(const float *v) {
 //      each per wave, written to the workspace in the orders K2 reads
 // ---------------------------------------------------------------------------------------
 constexpr float kLog2e = 1.4426950408889634f;
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group, lane j names an 8-byte
+// chunk; lane i receives element i % 4 of the chunks of lanes 4a + i / 4, a = 0..3. With
+// lane j pointing at row k0 + j / 4, columns c0 + 4 (j % 4) .. + 3 of a row-major 16-bit
+// tile, lane i therefore receives rows k0 .. k0 + 3 of column c0 + i: four consecutive k of
+// a matrix-core operand, read from a tile stored with k as its row index.
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr4(const void *p) {
+    const s16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4v *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
 // 2^x on the transcendental unit (the prep kernel keeps its cumulative decay in log2 units)
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -490,6 +502,27 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             float *Tb = &s_T[16 * R * SA + 16 * R];
 #pragma unroll
             for (int r = 0; r < 16; ++r) Tb[r * SA + jc] = x[r];
+        } else if constexpr (BF) {
+            // KgT fragment (channel rows 16 rt + li, tokens in perm order) by transpose reads
+            // of Kbar: half h holds tokens 32 kt + 16 h + 4 lg + a, a = 0..3
+            constexpr int NBK = (DK / 16) * NKC;
+            u32x4 *kg = reinterpret_cast<u32x4 *>(rec + R_::KgT);
+            for (int b2 = wave - 1; b2 < NBK; b2 += NW - 1) {
+                const int rt = b2 / NKC, kt = b2 - rt * NKC;
+                const int ch = 16 * rt + li;
+                float vals[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int k0 = kt * 32 + 16 * h + 4 * lg;
+                    const u32x2 t = lds_tr4(&s_kb[(k0 + (li >> 2)) * SK + 16 * rt + 4 * (li & 3)]);
+                    const float f = s_fkg[(2 * kt + h) * DK + ch];
+                    vals[4 * h + 0] = bf16_lo(t.x) * f;
+                    vals[4 * h + 1] = bf16_hi(t.x) * f;
+                    vals[4 * h + 2] = bf16_lo(t.y) * f;
+                    vals[4 * h + 3] = bf16_hi(t.y) * f;
+                }
+                kg[b2 * 64 + lane] = pack16<true>(vals);
+            }
         } else {
             constexpr int NBK = (DK / 16) * NKC;            // KgT blocks
             constexpr int EPL = Op<BF>::EPL;
@@ -560,14 +593,35 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             const int ct = wave;
             const int c = 16 * ct + li;
             float xv[NKTC][KS];
+            u32x4 xb[NKTC];                  // bf16: tokens 32 kt + 8 lg .. + 7 of column c
+            if constexpr (BF) {
+                const T *tile = isW ? s_kh : s_wv;
+                const int ld = isW ? SK : SV;
 #pragma unroll
-            for (int kt = 0; kt < NKTC; ++kt)
+                for (int kt = 0; kt < NKTC; ++kt) {
+                    const int k0 = kt * 32 + 8 * lg + (li >> 2);
+                    const u32x2 lo = lds_tr4(&tile[k0 * ld + 16 * ct + 4 * (li & 3)]);
+                    const u32x2 hi = lds_tr4(&tile[(k0 + 4) * ld + 16 * ct + 4 * (li & 3)]);
+                    xb[kt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+                    if (isW) {                   // X = Khat exp(Mid): one block per 8 tokens
+                        const float f = s_fmid[(2 * kt + (lg >> 1)) * DK + c];
+                        float x8[8];
+                        unpack16<true>(xb[kt], x8);
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const int tok = kt * KT + KS * lg + s;
-                    xv[kt][s] = isW ? io<T>::ld(&s_kh[tok * SK + c]) * s_fmid[(tok >> 4) * DK + c]
-                                    : io<T>::ld(&s_wv[tok * SV + c]);
+                        for (int s = 0; s < 8; ++s) x8[s] *= f;
+                        xb[kt] = pack16<true>(x8);
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < NKTC; ++kt)
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        const int tok = kt * KT + KS * lg + s;
+                        xv[kt][s] = isW ? io<T>::ld(&s_kh[tok * SK + c]) * s_fmid[(tok >> 4) * DK + c]
+                                        : io<T>::ld(&s_wv[tok * SV + c]);
+                    }
+            }
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -579,8 +633,8 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     if constexpr (BF) {
                         const u32x4 tb = *reinterpret_cast<const u32x4 *>(
                             &reinterpret_cast<const bf16_t *>(s_A)[(16 * R + li) * STB + tok0]);
-                        if (isW) acc = mma_k32(pack16<true>(xv[kt]), tb, acc);
-                        else acc = mma_k32(tb, pack16<true>(xv[kt]), acc);
+                        if (isW) acc = mma_k32(xb[kt], tb, acc);
+                        else acc = mma_k32(tb, xb[kt], acc);
                     } else {
                         float tv[KS];
                         const bool live = (tok0 >> 4) <= R;
