@@ -320,19 +320,52 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         if (has_next) locate(next, nxt);
         char *rec = p.rec + cur.rec * R_::bytes;
 
-        // ---- phase 0: cumulative log decay (in place in s_g) ----
+        // ---- phase 0: cumulative log decay, in log2 units, into s_g ----
+        if constexpr (BF) {
+            // g^T = la^T L^T on the matrix cores (L: lower-triangular ones): raw log alpha
+            // staged in the (still free) Khat tile, read back as A operands by transpose
+            // reads; the 0/1 operand is built in registers; each output tile is one
+            // 16-byte store of four channels of one token
 #pragma unroll
-        for (int e = 0; e < RAWV; ++e) {
-            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-            float x[VEC];
-            unpack16<BF>(rl[e], x);
+            for (int e = 0; e < RAWV; ++e) {
+                const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
+                *reinterpret_cast<u32x4 *>(&s_kh[r * SK + cv * VEC]) = rl[e];
+            }
+            __syncthreads();
+            for (int t = wave; t < (DK / 16) * 4; t += NW) {
+                const int ct = t >> 2, R = t & 3;         // channel tile, token tile
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < VEC; s += 4)     // log2 units: every factor is one exp2
-                *reinterpret_cast<f32x4 *>(&s_g[r * SG + cv * VEC + s]) =
-                    f32x4{x[s] * kLog2e, x[s + 1] * kLog2e, x[s + 2] * kLog2e, x[s + 3] * kLog2e};
-        }
-        __syncthreads();
-        {
+                for (int kt = 0; kt < 2; ++kt) {
+                    if (kt * 32 > 16 * R + 15) break;
+                    const int k0 = kt * 32 + 8 * lg + (li >> 2);
+                    const u32x2 lo = lds_tr4(&s_kh[k0 * SK + 16 * ct + 4 * (li & 3)]);
+                    const u32x2 hi = lds_tr4(&s_kh[(k0 + 4) * SK + 16 * ct + 4 * (li & 3)]);
+                    const int tok = 16 * R + li;          // output token (column of L^T)
+                    u32x4 ones;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int k = kt * 32 + 8 * lg + 2 * q;
+                        ones[q] = (k <= tok ? 0x3F80u : 0u) | (k + 1 <= tok ? 0x3F800000u : 0u);
+                    }
+                    acc = mma_k32(u32x4{lo.x, lo.y, hi.x, hi.y}, ones, acc);
+                }
+                // lane: g^T[16 ct + 4 lg + ii][16 R + li] = g[token][channel]
+                *reinterpret_cast<f32x4 *>(&s_g[(16 * R + li) * SG + 16 * ct + 4 * lg]) =
+                    f32x4{acc[0] * kLog2e, acc[1] * kLog2e, acc[2] * kLog2e, acc[3] * kLog2e};
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < RAWV; ++e) {
+                const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
+                float x[VEC];
+                unpack16<BF>(rl[e], x);
+#pragma unroll
+                for (int s = 0; s < VEC; s += 4)     // log2 units: every factor is one exp2
+                    *reinterpret_cast<f32x4 *>(&s_g[r * SG + cv * VEC + s]) =
+                        f32x4{x[s] * kLog2e, x[s + 1] * kLog2e, x[s + 2] * kLog2e, x[s + 3] * kLog2e};
+            }
+            __syncthreads();
             const int c = tid % DK, part = tid / DK;
             float x[RPP];
             float acc = 0.f;
@@ -489,15 +522,17 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
         if (wave == 0) {
             const int R = lane >> 4, jc = lane & 15;      // column jc of T_RR
             const float *Ab = &s_A[16 * R * SA + 16 * R];
-            float x[16];
+            // column jc of (I + A_RR)^{-1} by forward substitution, right-looking: once x[m]
+            // is known it is folded into every later row's sum, so the dependent chain is
+            // one FMA per row
+            float x[16], acc[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == jc) ? 1.f : 0.f;
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-            for (int r = 1; r < 16; ++r) {
-                float acc = 0.f;
+            for (int m = 0; m < 16; ++m) {
+                x[m] = m == jc ? 1.f : (m > jc ? -acc[m] : 0.f);
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc += Ab[r * SA + m] * x[m];
-                if (r > jc) x[r] = -acc;
+                for (int r = m + 1; r < 16; ++r) acc[r] += Ab[r * SA + m] * x[m];
             }
             float *Tb = &s_T[16 * R * SA + 16 * R];
 #pragma unroll

@@ -22,12 +22,14 @@
 
 namespace gdn2 {
 
+constexpr int kDecodeThreads = 256;   // threads per (sequence, head) state
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+__global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ b, const T *__restrict__ w,
     float *__restrict__ S, T *__restrict__ o, int h_k, int h_v, int group) {
-    constexpr int NT = 256;
+    constexpr int NT = kDecodeThreads, NW = NT / 64;
     constexpr int C4 = DV / 4;        // 16-byte column groups per row
     constexpr int RG = NT / C4;       // row groups
     constexpr int RPT = DK / RG;      // rows per thread
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     static_assert(C4 <= 64 && 64 % C4 == 0, "a wave must hold whole row groups");
 
     __shared__ float s_a[DK], s_bk[DK], s_k[DK], s_q[DK], s_wv[DV];
-    __shared__ float s_red[4][2 * DV + 4];
+    __shared__ float s_red[NW][2 * DV + 4];
 
     const int pair = blockIdx.x;
     const int n = pair / h_v;
@@ -52,17 +54,20 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         s[i] = io<float>::ld4(Sp + static_cast<size_t>(rg + RG * i) * DV + 4 * cg);
 
     // Token vectors of this (sequence, head), widened to fp32 and staged in LDS.
-    if (tid < DK) {
-        const size_t kq_off = (static_cast<size_t>(n) * h_k + hk) * DK + tid;
-        const size_t g_off = (static_cast<size_t>(n) * h_v + h) * DK + tid;
-        const float kk = io<T>::ld(k + kq_off);
-        s_k[tid] = kk;
-        s_q[tid] = io<T>::ld(q + kq_off);
-        s_bk[tid] = io<T>::ld(b + g_off) * kk;
-        s_a[tid] = __expf(io<T>::ld(log_alpha + g_off));
-    } else if (tid >= 128 && tid < 128 + DV) {
-        const size_t off = (static_cast<size_t>(n) * h_v + h) * DV + (tid - 128);
-        s_wv[tid - 128] = io<T>::ld(w + off) * io<T>::ld(v + off);
+    // (key-axis vectors on the first DK threads, w.v on the next DV, wrapping round)
+    for (int i = tid; i < DK + DV; i += NT) {
+        if (i < DK) {
+            const size_t kq_off = (static_cast<size_t>(n) * h_k + hk) * DK + i;
+            const size_t g_off = (static_cast<size_t>(n) * h_v + h) * DK + i;
+            const float kk = io<T>::ld(k + kq_off);
+            s_k[i] = kk;
+            s_q[i] = io<T>::ld(q + kq_off);
+            s_bk[i] = io<T>::ld(b + g_off) * kk;
+            s_a[i] = __expf(io<T>::ld(log_alpha + g_off));
+        } else {
+            const size_t off = (static_cast<size_t>(n) * h_v + h) * DV + (i - DK);
+            s_wv[i - DK] = io<T>::ld(w + off) * io<T>::ld(v + off);
+        }
     }
     __syncthreads();
 
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     f32x4 Y = {0.f, 0.f, 0.f, 0.f}, Z = {0.f, 0.f, 0.f, 0.f};
     float KQ = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < 4; ++wv) {
+    for (int wv = 0; wv < NW; ++wv) {
         Y += *reinterpret_cast<const f32x4 *>(&s_red[wv][4 * cg]);
         Z += *reinterpret_cast<const f32x4 *>(&s_red[wv][DV + 4 * cg]);
         KQ += s_red[wv][2 * DV];
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     const int pairs = a.num_seqs * a.h_v;
-    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(pairs), dim3(256), 0, st,
+    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(pairs), dim3(kDecodeThreads), 0, st,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<const T *>(a.log_alpha),
                        static_cast<const T *>(a.b), static_cast<const T *>(a.w), a.S,
