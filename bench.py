@@ -226,7 +226,7 @@ def cpu_baseline_chunk(wl, x, gpu_out):
     return base, parity
 
 
-def cpu_baseline_decode(wl, pairs=768):
+def cpu_baseline_decode(wl, pairs=1024):
     """fp64 oracle on `pairs` of the workload's states for all its steps, scaled to one step
     over every state."""
     import oracle
@@ -324,7 +324,7 @@ def main():
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": nbytes / t_warm / 1e9 / HBM_PEAK_GBPS,
                          "traffic": measured_traffic("chunk_fwd_t4096", src),
-                         "kernel": "chunk_prep_kernel + chunk_state_kernel (one gdn2_chunk_fwd)",
+                         "kernel": "one gdn2_chunk_fwd call: chunk_prep_kernel, chunk_seg_kernel, chunk_scan_kernel, chunk_state_kernel",
                          "alg_bytes": nbytes, "alg_flops": flops,
                          "mfma_frac_bf16": flops / t_warm / 1e12 / BF16_MFMA_PEAK_TFLOPS},
             "cold_cache": {"us_per_call": t_cold * 1e6, "tokens_per_s": B * T / t_cold,
