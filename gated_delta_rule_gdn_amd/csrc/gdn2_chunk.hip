@@ -709,23 +709,23 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
-// K2: inter-chunk state pass. Each 16-column slice of S (all d_k rows, fp32, in registers)
-// has two compute waves, and each workgroup has kLoaders loader waves:
-//   * the chain wave runs the recurrence: U = U~ + Wn S, then S = gamma_C S + KgT U. It
-//     publishes the matrix-core B operands of S (at chunk entry) and of U in LDS and sets a
-//     per-slice flag after each;
-//   * the output wave computes O = Qg S + M U from those published operands as they appear,
-//     off the recurrence's critical path, and leaves o in an LDS tile;
-//   * kCopyWaves copy waves load chunk c + 1's record (operands common to all columns,
-//     gamma_C, the slices' U~) into the other half of a double-buffered LDS stage with
-//     direct global-to-LDS loads (one wave cannot keep enough copies in flight);
-//   * one store wave writes the o tiles of chunk c - 1 to memory with 16-byte stores. It
-//     never waits for them: a wave that both copies and stores would have to wait for its
-//     stores too before each barrier, since both share one completion counter. Compute
-//     waves issue no global memory operation inside the chunk loop.
+// K2: inter-chunk state pass. A workgroup owns NW 16-column slices of S (all d_k rows,
+// fp32, in registers) of one (sequence, head, segment):
+//   * per slice, a chain wave runs the recurrence U = U~ + Wn S, then
+//     S = gamma_C S + KgT U. It publishes the matrix-core B operands of S (at chunk entry)
+//     and of U in LDS, and sets a per-slice counter after each;
+//   * per slice, an output wave computes O = Qg S + M U from those published operands as
+//     they appear, off the recurrence's critical path. It turns the o tile round through
+//     LDS (over the U operands it has consumed) into 16-byte rows and stores them. It
+//     issues no other global access, so it never waits on those stores;
+//   * copy waves load chunk c + 1's record (operands common to all columns, gamma_C, the
+//     slices' U~) into the other half of a double-buffered LDS stage with direct
+//     global-to-LDS loads (one wave cannot keep enough copies in flight).
 // All waves meet once per chunk at a plain s_barrier (no memory fence: each wave waits for
-// exactly what it produced before arriving). The column-slice workgroups of one
-// (sequence, head) run on one XCD, so its records are fetched into one L2.
+// exactly what it produced before arriving). The workgroups of one (sequence, head,
+// segment) run on one XCD, so its records are fetched into one L2. More slices per
+// workgroup share one staged copy of each record: the pass is bound by how fast a CU can
+// stream records into LDS.
 // ---------------------------------------------------------------------------------------
 template <int DK, int DV, bool BF>
 struct StageLayout {
@@ -734,13 +734,15 @@ struct StageLayout {
     static constexpr size_t SHARED = R_::Ut;                 // Wn, Qg, KgT, M
     static constexpr size_t GCB = DK * 4;                    // gamma_C
     static constexpr size_t UTS = 4 * R_::UT_TILE;           // one slice's U~
-    static constexpr size_t OTILE = kChunk * 16 * E_O;       // one slice's o tile
-    static constexpr size_t XCH = (R_::NKT_DK + R_::NKT_C) * 1024;   // published S, U operands
+    static constexpr size_t XS = R_::NKT_DK * 1024;          // published S operands
+    static constexpr size_t XU = R_::NKT_C * 1024;           // published U operands / o tile
+    static constexpr size_t XCH = XS + XU;
+    static_assert(XU >= static_cast<size_t>(kChunk) * 16 * E_O, "o tile fits over U");
     __host__ __device__ static constexpr size_t buffer_bytes(int nw) {
         return SHARED + GCB + nw * UTS;
     }
     __host__ __device__ static constexpr size_t lds_bytes(int nw) {
-        return 2 * buffer_bytes(nw) + 2 * nw * OTILE + nw * XCH;
+        return 2 * buffer_bytes(nw) + nw * XCH;
     }
     static_assert(lds_bytes(1) <= 160 * 1024, "stage must fit in LDS");
 };
@@ -775,31 +777,35 @@ __device__ __forceinline__ void wait_flag(lds_flag *flag, int want) {
     asm volatile("" ::: "memory");
 }
 
-constexpr int kCopyWaves = 6;         // copy waves per state-pass workgroup
-constexpr int kLoaders = kCopyWaves + 1;   // plus one store wave
+// copy waves per state-pass workgroup: six, four with four slices (the register budget of
+// twelve waves)
+template <int NW> struct StateWaves {
+    static constexpr int COPY = NW >= 4 ? 4 : 6;
+    static constexpr int ALL = 2 * NW + COPY;
+};
 
-template <typename T, bool BF, int DK, int DV>
-__global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkParams p) {
+template <typename T, bool BF, int DK, int DV, int NW>
+__global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(ChunkParams p) {
     using R_ = Rec<DK, DV, BF>;
     using SL = StageLayout<DK, DV, BF>;
     constexpr int C = kChunk, RT = DK / 16;
     constexpr int KT = Op<BF>::KT;
     constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
+    constexpr int NCOPY = StateWaves<NW>::COPY;
+    constexpr size_t BUF = SL::buffer_bytes(NW);
     static_assert(BF || NKD == RT, "fp32 operands are whole state tiles");
+    static_assert(SL::lds_bytes(NW) <= 160 * 1024, "stage must fit in LDS");
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int nw = ((blockDim.x >> 6) - kLoaders) / 2;   // column slices per workgroup
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, lg = lane >> 4;
-    const size_t BUF = SL::buffer_bytes(nw);
-    char *otile_base = smem + 2 * BUF;
-    char *xch_base = otile_base + 2 * nw * SL::OTILE;
-    // Per-slice publication counters ([slice] S, [2 + slice] U). A static LDS array, so
+    char *xch_base = smem + 2 * BUF;
+    // Per-slice publication counters ([slice] S, [NW + slice] U). A static LDS array, so
     // every access is a plain LDS instruction: LDS operations of one wave complete in
     // issue order, so a counter written after the data it announces is never seen
     // ahead of that data.
-    __shared__ int flags[4];
+    __shared__ int flags[2 * NW];
 
-    // XCD-aware decode: the column slices of one (pair, segment) unit share an XCD.
+    // XCD-aware decode: the workgroups of one (pair, segment) unit share an XCD.
     const int bid = blockIdx.x, xcd = bid & 7, rest = bid >> 3;
     const int slice = rest % p.nslices;
     const int unit = (rest / p.nslices) * 8 + xcd;
@@ -826,71 +832,39 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
         return p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
     };
 
-    if (wave >= 2 * nw) {
-        const int ldr = wave - 2 * nw;
-        if (ldr < kCopyWaves) {
-            // ---- copy waves: stage chunk c + 1 in the other buffer during chunk c
-            auto issue = [&](int c, char *dst) {
-                const char *rec = record(c);
-                for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += kCopyWaves)
-                    dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
-                if (ldr == kCopyWaves - 1 && lane < static_cast<int>(SL::GCB / 16))
-                    dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
-                // the slices' U~: column tiles slice*nw .. slice*nw + nw - 1 are contiguous
-                // in the record, and so are their stage slots
-                const char *us = rec + R_::Ut + static_cast<size_t>(slice) * nw * SL::UTS;
-                char *ud = dst + SL::SHARED + SL::GCB;
-                for (int b = ldr; b < static_cast<int>(nw * SL::UTS / 1024); b += kCopyWaves)
-                    dma16(us + b * 1024 + lane * 16, ud + b * 1024);
-            };
-            if (ce > cb) issue(cb, smem + (cb & 1) * BUF);
-            for (int c = cb; c < ce; ++c) {
-                wait_vmem();                // this wave's copies for chunk c have landed
-                raw_barrier();              // chunk c is staged; chunk c-1 fully consumed
-                if (c + 1 < ce) issue(c + 1, smem + ((c + 1) & 1) * BUF);
-            }
-            if (ce > cb) raw_barrier();
-            return;
-        }
-        // ---- store wave: o of chunk c - 1 (o tiles of buffer (c-1) & 1) during chunk c
-        T *op = static_cast<T *>(p.o);
-        constexpr int PPR = 16 * static_cast<int>(sizeof(T)) / 16;   // 16-byte pieces per row
-        auto store_o = [&](int c) {
-            const int64_t t0 = start + static_cast<int64_t>(c) * C;
-            const int L = static_cast<int>(min<int64_t>(C, end - t0));
-            const T *tiles = reinterpret_cast<const T *>(otile_base + (c & 1) * nw * SL::OTILE);
-            for (int idx = lane; idx < nw * C * PPR; idx += 64) {
-                const int w = idx / (C * PPR), rp = idx - w * C * PPR;
-                const int row = rp / PPR, piece = rp - row * PPR;
-                if (row < L) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(
-                        &tiles[w * C * 16 + row * 16 + piece * (16 / sizeof(T))]);
-                    *reinterpret_cast<u32x4 *>(
-                        op + (static_cast<size_t>(t0 + row) * p.h_v + h) * DV +
-                        16 * (slice * nw + w) + piece * (16 / sizeof(T))) = v;
-                }
-            }
-            wait_lds();                     // tile reads done before the next barrier
+    if (wave >= 2 * NW) {
+        // ---- copy waves: stage chunk c + 1 in the other buffer during chunk c
+        const int ldr = wave - 2 * NW;
+        auto issue = [&](int c, char *dst) {
+            const char *rec = record(c);
+            for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += NCOPY)
+                dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
+            if (ldr == NCOPY - 1 && lane < static_cast<int>(SL::GCB / 16))
+                dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
+            // the slices' U~: column tiles slice*NW .. slice*NW + NW - 1 are contiguous
+            // in the record, and so are their stage slots
+            const char *us = rec + R_::Ut + static_cast<size_t>(slice) * NW * SL::UTS;
+            char *ud = dst + SL::SHARED + SL::GCB;
+            for (int b = ldr; b < static_cast<int>(NW * SL::UTS / 1024); b += NCOPY)
+                dma16(us + b * 1024 + lane * 16, ud + b * 1024);
         };
+        if (ce > cb) issue(cb, smem + (cb & 1) * BUF);
         for (int c = cb; c < ce; ++c) {
-            raw_barrier();
-            if (c > cb) store_o(c - 1);
-        }
-        if (ce > cb) {
-            raw_barrier();                  // the last chunk's o tiles are written
-            store_o(ce - 1);
+            wait_vmem();                    // this wave's copies for chunk c have landed
+            raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
+            if (c + 1 < ce) issue(c + 1, smem + ((c + 1) & 1) * BUF);
         }
         return;
     }
 
-    const bool chain = wave < nw;
-    const int sl = chain ? wave : wave - nw;             // slice within the workgroup
-    const int ct = slice * nw + sl;
+    const bool chain = wave < NW;
+    const int sl = chain ? wave : wave - NW;             // slice within the workgroup
+    const int ct = slice * NW + sl;
     const int col = 16 * ct + li;
     u32x4 *xS = reinterpret_cast<u32x4 *>(xch_base + sl * SL::XCH);   // published S operands
     u32x4 *xU = xS + NKD * 64;                                         // published U operands
     lds_flag *flagS = (lds_flag *)(flags + sl);
-    lds_flag *flagU = (lds_flag *)(flags + 2 + sl);
+    lds_flag *flagU = (lds_flag *)(flags + NW + sl);
     if (chain && lane == 0) {
         *flagS = 0;
         *flagU = 0;
@@ -981,7 +955,6 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                 }
             wait_lds();                     // this chunk's LDS reads and writes are done
         }
-        if (ce > cb) raw_barrier();         // pairs with the loaders' final barrier
         if (p.S_T && seg == p.nseg - 1) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -1037,17 +1010,31 @@ __global__ __launch_bounds__(64 * (4 + kLoaders)) void chunk_state_kernel(ChunkP
                 else O[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, am[rt][kt]),
                                          __builtin_bit_cast(f32x4, UB[kt]), O[rt]);
             }
-        // o rows into this slice's tile of buffer c & 1 (row-major [C][16]); the store wave
-        // writes it to memory during the next chunk
-        T *otile = reinterpret_cast<T *>(otile_base + ((c & 1) * nw + sl) * SL::OTILE);
+        // o rows through LDS (over the consumed U operands, row-major [C][16]) into 16-byte
+        // row pieces, stored straight to memory
+        T *otile = reinterpret_cast<T *>(xU);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 io<T>::st(&otile[(16 * rt + 4 * lg + ii) * 16 + li], O[rt][ii]);
-        wait_lds();                         // tile writes done before the next barrier
+        wait_lds();
+        {
+            constexpr int PPR = 16 * static_cast<int>(sizeof(T)) / 16;   // pieces per row
+            const int64_t t0 = start + static_cast<int64_t>(c) * C;
+            const int L = static_cast<int>(min<int64_t>(C, end - t0));
+            T *op = static_cast<T *>(p.o);
+#pragma unroll
+            for (int idx = lane; idx < C * PPR; idx += 64) {
+                const int row = idx / PPR, piece = idx - row * PPR;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(&otile[row * 16 + piece * (16 / sizeof(T))]);
+                if (row < L)
+                    *reinterpret_cast<u32x4 *>(op + (static_cast<size_t>(t0 + row) * p.h_v + h) * DV +
+                                               16 * ct + piece * (16 / sizeof(T))) = v;
+            }
+        }
+        wait_lds();                         // tile reads done before U is published again
     }
-    if (ce > cb) raw_barrier();             // hand the last o tiles to the store wave
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1148,16 +1135,21 @@ __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(
     const int col = 16 * (isP ? v : v - SG::NP) + li;
     f32x4 S[RT];
     float *segS = p.seg_S + static_cast<size_t>(pair) * p.nseg * DK * DV;
-    const bool fromS0 = active && !isP && g == 0 && p.S0 != nullptr;
-    // all loads first, then the copies of segment 0's start state
+    const bool fromS0 = active && !isP && g == 0 && p.S0 != nullptr;   // uniform per wave
+    if (fromS0) {
+        const float *S0p = p.S0 + static_cast<size_t>(pair) * DK * DV + col;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int row = 16 * rt + 4 * lg + ii;
-            S[rt][ii] = fromS0 ? p.S0[(static_cast<size_t>(pair) * DK + row) * DV + col]
-                               : ((isP && row == col) ? 1.f : 0.f);
-        }
+            for (int ii = 0; ii < 4; ++ii)
+                S[rt][ii] = S0p[static_cast<size_t>(16 * rt + 4 * lg + ii) * DV];
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                S[rt][ii] = (isP && 16 * rt + 4 * lg + ii == col) ? 1.f : 0.f;
+    }
     if (active && g == 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -1268,19 +1260,25 @@ __global__ __launch_bounds__(64 * (DK / 16)) void chunk_scan_kernel(ChunkParams 
         sS[row][li] = Sp[static_cast<size_t>(DK + row) * DV + col];
     }
     __syncthreads();
-    for (int g = 1; g < nsa; ++g) {
+    // step g needs P_g (this wave's row tile), R_g and S_g; the loads of step g + 1 are
+    // issued before the products of step g
+    auto load_step = [&](int g, f32x4 *a, f32x4 &r4) {
         const float *P = p.seg_P + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DK;
         const float *R = p.seg_R + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DV;
-        f32x4 a[RT];
 #pragma unroll
         for (int kt = 0; kt < RT; ++kt)
             a[kt] = *reinterpret_cast<const f32x4 *>(P + static_cast<size_t>(16 * wave + li) * DK +
                                                      16 * kt + 4 * lg);
-        f32x4 acc;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            acc[ii] = R[static_cast<size_t>(16 * wave + 4 * lg + ii) * DV + col];
-        __builtin_amdgcn_sched_barrier(0);   // every load of the step is in flight
+            r4[ii] = R[static_cast<size_t>(16 * wave + 4 * lg + ii) * DV + col];
+    };
+    f32x4 a[RT], an[RT], r4, rn4;
+    if (nsa > 1) load_step(1, a, r4);
+    for (int g = 1; g < nsa; ++g) {
+        if (g + 1 < nsa) load_step(g + 1, an, rn4);
+        __builtin_amdgcn_sched_barrier(0);   // the next step's loads are in flight
+        f32x4 acc = r4;
 #pragma unroll
         for (int kt = 0; kt < RT; ++kt) {
             f32x4 b;
@@ -1296,6 +1294,9 @@ __global__ __launch_bounds__(64 * (DK / 16)) void chunk_scan_kernel(ChunkParams 
             Sp[static_cast<size_t>((g + 1) * DK + row) * DV + col] = acc[ii];
         }
         __syncthreads();
+#pragma unroll
+        for (int kt = 0; kt < RT; ++kt) a[kt] = an[kt];
+        r4 = rn4;
     }
 }
 
@@ -1318,16 +1319,26 @@ size_t chunk_map_bytes(int num_seqs, bool packed) {
 }
 
 // Segmentation of the state pass: dense batches only, aiming at about kSegTargetWGs
-// workgroups of two column slices, with at least 4 chunks per segment.
+// state-pass workgroups, with at least 4 chunks per segment.
 constexpr int64_t kSegTargetWGs = 256;
 
 struct SegPlan {
     int nseg, seg_len;
 };
 
-static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v) {
+// 16-column slices per state-pass workgroup. Two, unless the (sequence, head) pairs alone
+// give more two-slice workgroups than the target: then four, so that each staged record
+// serves more columns (fp32 records leave room for one only).
+static int state_slices(int d_v, bool bf16, int64_t pairs) {
+    if (!bf16) return 1;
+    const int ctiles = d_v / 16;
+    if (ctiles % 4 == 0 && pairs * (ctiles / 2) > kSegTargetWGs) return 4;
+    return ctiles % 2 == 0 ? 2 : 1;
+}
+
+static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v, bool bf16) {
     SegPlan sp{1, nc};
-    const int64_t per_unit = d_v / 32;             // workgroups of two 16-column slices
+    const int64_t per_unit = (d_v / 16) / state_slices(d_v, bf16, pairs);   // WGs per unit
     if (packed || pairs <= 0 || nc < 8 || per_unit <= 0) return sp;
     int64_t G = kSegTargetWGs / (pairs * per_unit);
     if (G > nc / 4) G = nc / 4;
@@ -1356,7 +1367,7 @@ size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d
                              bool bf16, bool packed) {
     const int64_t nc = (static_cast<int64_t>(seqlen) + kChunk - 1) / kChunk;
     const int64_t pairs = static_cast<int64_t>(packed ? num_seqs : batch) * h_v;
-    const SegPlan sp = chunk_seg_plan(packed, pairs, static_cast<int>(nc), d_v);
+    const SegPlan sp = chunk_seg_plan(packed, pairs, static_cast<int>(nc), d_v, bf16);
     size_t off[3], segb;
     seg_area(sp, pairs, d_k, d_v, off, &segb);
     return chunk_map_bytes(num_seqs, packed) +
@@ -1386,6 +1397,22 @@ static int device_cu_count() {
     return cached[dev];
 }
 
+template <typename T, bool BF, int DK, int DV, int NW>
+static hipError_t launch_state(ChunkParams p, int64_t units, hipStream_t st) {
+    using SLy = StageLayout<DK, DV, BF>;
+    p.nslices = DV / 16 / NW;
+    const size_t lds = SLy::lds_bytes(NW);
+    auto kern = chunk_state_kernel<T, BF, DK, DV, NW>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (units + 7) / 8 * 8 * p.nslices;
+    if (blocks > 0)
+        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * StateWaves<NW>::ALL), lds, st, p);
+    return hipGetLastError();
+}
+
 template <typename T, bool BF, int DK, int DV>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     static_assert(Rec<DK, DV, BF>::bytes > 0, "");
@@ -1402,7 +1429,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.nc_dense = (a.seqlen + kChunk - 1) / kChunk;
     p.num_pairs = N * a.h_v;
     const int64_t nrec = chunk_upper_bound(a.batch, a.seqlen, N, packed);
-    const SegPlan sp = chunk_seg_plan(packed, p.num_pairs, p.nc_dense, DV);
+    const SegPlan sp = chunk_seg_plan(packed, p.num_pairs, p.nc_dense, DV, BF);
     p.nseg = sp.nseg;
     p.seg_len = sp.seg_len;
     {
@@ -1423,7 +1450,6 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
         hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV>), dim3(grid), dim3(512), 0, st, p);
     }
-    constexpr size_t kMaxLds = 160 * 1024;          // LDS per workgroup on gfx950
     const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
     if (p.nseg > 1 && p.num_pairs > 0) {
         // segment pass, then the scan over segments
@@ -1440,29 +1466,16 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
             hipLaunchKernelGGL((chunk_scan_kernel<DK, DV>), dim3(p.num_pairs * (DV / 16)),
                                dim3(64 * (DK / 16)), 0, st, p);
     }
-    // K2: column slices per workgroup (each with a chain and an output wave, plus the
-    // loader waves). More slices share one copy of each chunk's operands in LDS; fewer
-    // spread a small batch over more CUs.
-    using SLy = StageLayout<DK, DV, BF>;
-    int nw = 1;
-    const int ctiles = DV / 16;
-    while (nw < 2 && ctiles % (2 * nw) == 0 &&
-           (p.nseg > 1 || units * ctiles / (2 * nw) >= 256) &&
-           SLy::lds_bytes(2 * nw) <= kMaxLds)
-        nw *= 2;
-    p.nslices = ctiles / nw;
-    const size_t lds = SLy::lds_bytes(nw);
-    auto kern = chunk_state_kernel<T, BF, DK, DV>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    const int64_t units8 = (units + 7) / 8 * 8;
-    const int64_t blocks = units8 * p.nslices;
-    if (blocks > 0) {
-        hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * (2 * nw + kLoaders)), lds, st, p);
+    // K2: NW column slices per workgroup (each with a chain and an output wave, plus the
+    // copy waves)
+    if constexpr (BF) {
+        const int nw = state_slices(DV, BF, p.num_pairs);
+        if (nw == 4) return launch_state<T, BF, DK, DV, 4>(p, units, st);
+        if (nw == 2) return launch_state<T, BF, DK, DV, 2>(p, units, st);
+        return launch_state<T, BF, DK, DV, 1>(p, units, st);
+    } else {
+        return launch_state<T, BF, DK, DV, 1>(p, units, st);
     }
-    return hipGetLastError();
 }
 
 template <typename T, bool BF>

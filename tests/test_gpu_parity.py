@@ -186,3 +186,12 @@ def test_segmented_final_state_may_alias_initial_state():
     assert S_T.data_ptr() == S.data_ptr()
     assert np.array_equal(np64(S), S_ref)
     assert np.array_equal(np64(o).reshape(o_ref.shape), o_ref)
+
+
+# Many (sequence, head) pairs: the state pass uses four-column-slice workgroups.
+@pytest.mark.parametrize("dk,dv,B,T,hk,hv", [(128, 128, 4, 200, 8, 32), (128, 64, 3, 150, 16, 48)])
+def test_many_pairs_wide_state_workgroups(dk, dv, B, T, hk, hv):
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=B, seqlen=T, h_k=hk, h_v=hv, d_k=dk,
+                            d_v=dv, neg_eig=True, s0_std=0.1)
+    x = inputs.chunk_inputs(wl, seed=B * T + hv)
+    assert_chunk_parity(x, torch.bfloat16, label=f"many pairs {dk}x{dv} B={B} T={T} hv={hv}")
