@@ -24,7 +24,13 @@ namespace gdn2 {
 
 constexpr int kDecodeThreads = 256;   // threads per (sequence, head) state
 
-template <typename T, int DK, int DV>
+// States larger than the last-level cache (MALL, 256 MB on MI355X) are written back with
+// non-temporal stores: no step can find them cached, and streaming them past the cache
+// measured 24 % faster for a 403 MB state. Smaller states keep ordinary stores, so that the
+// next step reads them from the cache.
+constexpr size_t kStreamStateBytes = static_cast<size_t>(256) << 20;
+
+template <typename T, int DK, int DV, bool NTS>
 __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ b, const T *__restrict__ w,
@@ -117,14 +123,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         s[i] += kr[i] * u;
-        io<float>::st4(Sp + static_cast<size_t>(rg + RG * i) * DV + 4 * cg, s[i]);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(Sp + static_cast<size_t>(rg + RG * i) * DV + 4 * cg);
+        if constexpr (NTS) __builtin_nontemporal_store(s[i], dst);
+        else *dst = s[i];
     }
 }
 
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     const int pairs = a.num_seqs * a.h_v;
-    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(pairs), dim3(kDecodeThreads), 0, st,
+    const size_t state_bytes = static_cast<size_t>(pairs) * DK * DV * 4;
+    auto kern = state_bytes > kStreamStateBytes ? decode_step_kernel<T, DK, DV, true>
+                                                : decode_step_kernel<T, DK, DV, false>;
+    hipLaunchKernelGGL(kern, dim3(pairs), dim3(kDecodeThreads), 0, st,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<const T *>(a.log_alpha),
                        static_cast<const T *>(a.b), static_cast<const T *>(a.w), a.S,

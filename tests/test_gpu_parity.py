@@ -5,6 +5,8 @@ o and on the final states. Small cases compare every element; the full-size work
 compare every element the oracle can afford and otherwise a seeded sample of whole
 (sequence, value head) pairs, each computed over all of its tokens.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -76,6 +78,34 @@ def test_decode_full_size_256_steps():
     eo = oracle.rel_l2(np.concatenate(go), np.concatenate(ro))
     es = oracle.rel_l2(np.concatenate(gs), np.concatenate(rs))
     print(f"[parity] decode full 256 steps, 24 sampled states: o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= 1e-4 and es <= 1e-4
+
+
+def test_decode_state_larger_than_last_level_cache():
+    """128 sequences x 48 heads (403 MB of state, above 256 MiB: streamed with non-temporal
+    stores), 4 steps in place, 24 sampled states against the oracle."""
+    wl = replace(inputs.DECODE_F32, num_seqs=128, steps=4)
+    x = inputs.decode_inputs(wl, seed=13)
+    dev = {n: x[n].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    S = x["S"].cuda()
+    o_all = torch.empty(wl.steps, wl.num_seqs, wl.h_v, wl.d_v, device="cuda")
+    for t in range(wl.steps):
+        g.recurrent_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["log_alpha"][t],
+                         dev["b"][t], dev["w"][t], S, out=o_all[t])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, wl.num_seqs, 24),
+                                              rng.integers(0, wl.h_v, 24))]
+    o_g, S_g = np64(o_all), np64(S)
+    go, gs, ro, rs = [], [], [], []
+    for n, h in pairs:
+        on, Sn = decode_oracle_pair(x, n, h, wl.steps, wl.h_v // wl.h_k)
+        go.append(o_g[:, n, h].ravel()); ro.append(on.ravel())
+        gs.append(S_g[n, h].ravel()); rs.append(Sn.ravel())
+    eo = oracle.rel_l2(np.concatenate(go), np.concatenate(ro))
+    es = oracle.rel_l2(np.concatenate(gs), np.concatenate(rs))
+    print(f"[parity] decode 128 seqs (streamed state), 24 sampled states: o={eo:.2e} S={es:.2e}",
+          flush=True)
     assert eo <= 1e-4 and es <= 1e-4
 
 
