@@ -189,6 +189,14 @@ __device__ __forceinline__ u32x2 lds_tr4(const void *p) {
 // 2^x on the transcendental unit (the prep kernel keeps its cumulative decay in log2 units)
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Record stores: non-temporal when the records cannot stay in the last-level cache until
+// the state pass reads them.
+template <bool NT, typename V>
+__device__ __forceinline__ void st_rec(V *p, V v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 struct PrepLoc {
     int64_t t0;     // first token of the chunk
     int L;          // valid rows
@@ -210,7 +218,7 @@ __device__ __forceinline__ void unpack16(u32x4 v, float *out) {
     }
 }
 
-template <typename T, bool BF, int DK, int DV>
+template <typename T, bool BF, int DK, int DV, bool NTR>
 __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
     using R_ = Rec<DK, DV, BF>;
     constexpr int C = kChunk, NT = 512, NW = NT / 64;
@@ -398,7 +406,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                 s_foff[pi * DK + c] = exp2_hw(s_g[(16 * R + 7) * SG + c] - s_g[(16 * I + 7) * SG + c]);
             }
         }
-        if (tid < DK) reinterpret_cast<float *>(rec + R_::gC)[tid] = exp2_hw(s_g[(C - 1) * SG + tid]);
+        if (tid < DK) st_rec<NTR>(&reinterpret_cast<float *>(rec + R_::gC)[tid], exp2_hw(s_g[(C - 1) * SG + tid]));
         __syncthreads();                         // s_fmid is read by the tile loop below
         char *qgrec = rec + R_::Qg;
 #pragma unroll
@@ -429,14 +437,14 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     const int half = q4 >= 16 ? 1 : 0, lgq = (q4 & 15) >> 2;
                     const size_t slot = ((static_cast<size_t>(r >> 4) * NKD + kt) * 64 + 16 * lgq +
                                          (r & 15)) * 2 + half;
-                    reinterpret_cast<u32x2 *>(qgrec)[slot] =
-                        u32x2{pack_bf16x2(qg[4 * j4], qg[4 * j4 + 1]),
-                              pack_bf16x2(qg[4 * j4 + 2], qg[4 * j4 + 3])};
+                    st_rec<NTR>(&reinterpret_cast<u32x2 *>(qgrec)[slot],
+                                u32x2{pack_bf16x2(qg[4 * j4], qg[4 * j4 + 1]),
+                                      pack_bf16x2(qg[4 * j4 + 2], qg[4 * j4 + 3])});
                 }
             } else {
                 const int kt = c0 / 16, lgq = (c0 & 15) >> 2;
-                reinterpret_cast<f32x4 *>(qgrec)[((r >> 4) * NKD + kt) * 64 + 16 * lgq + (r & 15)] =
-                    f32x4{qg[0], qg[1], qg[2], qg[3]};
+                st_rec<NTR>(&reinterpret_cast<f32x4 *>(qgrec)[((r >> 4) * NKD + kt) * 64 + 16 * lgq + (r & 15)],
+                            f32x4{qg[0], qg[1], qg[2], qg[3]});
             }
         }
 #pragma unroll
@@ -497,10 +505,10 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             }
             *reinterpret_cast<f32x4 *>(&s_A[rr * SA + 16 * I + 4 * lg]) = a4;
             if constexpr (BF) {
-                reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)] =
-                    f4_to_b16(m4);
+                st_rec<NTR>(&reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)],
+                            f4_to_b16(m4));
             } else {
-                reinterpret_cast<f32x4 *>(mrec)[(R * NKC + I) * 64 + lane] = m4;
+                st_rec<NTR>(&reinterpret_cast<f32x4 *>(mrec)[(R * NKC + I) * 64 + lane], m4);
             }
         }
         for (int u = wave; u < 6; u += NW) {
@@ -509,10 +517,10 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             const int I2 = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
             if constexpr (BF) {
                 const u32x2 z = {0u, 0u};
-                reinterpret_cast<u32x2 *>(mrec)[(((R2 * NKC + (I2 >> 1)) * 64 + lane) << 1) + (I2 & 1)] = z;
+                st_rec<NTR>(&reinterpret_cast<u32x2 *>(mrec)[(((R2 * NKC + (I2 >> 1)) * 64 + lane) << 1) + (I2 & 1)], z);
             } else {
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                reinterpret_cast<f32x4 *>(mrec)[(R2 * NKC + I2) * 64 + lane] = z;
+                st_rec<NTR>(&reinterpret_cast<f32x4 *>(mrec)[(R2 * NKC + I2) * 64 + lane], z);
             }
         }
         __syncthreads();
@@ -556,7 +564,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     vals[4 * h + 2] = bf16_lo(t.y) * f;
                     vals[4 * h + 3] = bf16_hi(t.y) * f;
                 }
-                kg[b2 * 64 + lane] = pack16<true>(vals);
+                st_rec<NTR>(&kg[b2 * 64 + lane], pack16<true>(vals));
             }
         } else {
             constexpr int NBK = (DK / 16) * NKC;            // KgT blocks
@@ -572,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     const int tok = kt * KT + perm_k<BF>(llg, jj);
                     vals[jj] = io<T>::ld(&s_kb[tok * SK + ch]) * s_fkg[(tok >> 4) * DK + ch];
                 }
-                kg[b2 * 64 + l] = pack16<BF>(vals);
+                st_rec<NTR>(&kg[b2 * 64 + l], pack16<BF>(vals));
             }
         }
         __syncthreads();
@@ -690,16 +698,16 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     const f32x4 wn = -acc;
                     char *wr = rec + R_::Wn;
                     if constexpr (BF) {
-                        reinterpret_cast<u32x2 *>(wr)[(((R * NKD + (ct >> 1)) * 64 + lane) << 1) +
-                                                      (ct & 1)] = f4_to_b16(wn);
+                        st_rec<NTR>(&reinterpret_cast<u32x2 *>(wr)[(((R * NKD + (ct >> 1)) * 64 + lane) << 1) +
+                                                                   (ct & 1)], f4_to_b16(wn));
                     } else {
-                        reinterpret_cast<f32x4 *>(wr)[(R * NKD + ct) * 64 + lane] = wn;
+                        st_rec<NTR>(&reinterpret_cast<f32x4 *>(wr)[(R * NKD + ct) * 64 + lane], wn);
                     }
                 } else {
                     // lane: U~[16R + 4 lg + ii][16 ct + li], an output tile (D layout)
                     char *ut = rec + R_::Ut + (static_cast<size_t>(ct) * 4 + R) * R_::UT_TILE;
-                    if constexpr (BF) reinterpret_cast<u32x2 *>(ut)[lane] = f4_to_b16(acc);
-                    else reinterpret_cast<f32x4 *>(ut)[lane] = acc;
+                    if constexpr (BF) st_rec<NTR>(&reinterpret_cast<u32x2 *>(ut)[lane], f4_to_b16(acc));
+                    else st_rec<NTR>(&reinterpret_cast<f32x4 *>(ut)[lane], acc);
                 }
             }
         }
@@ -1351,6 +1359,10 @@ static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v, bool 
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Records beyond the last-level cache size (MALL, 256 MB on MI355X) are written with
+// non-temporal stores.
+constexpr size_t kStreamRecordBytes = static_cast<size_t>(256) << 20;
+
 // fp32 segment buffers: start states [pair][nseg][d_k][d_v], transitions
 // [pair][nseg-2][d_k][d_k] and zero-start end states [pair][nseg-2][d_k][d_v]
 static void seg_area(const SegPlan &sp, int64_t pairs, int d_k, int d_v, size_t off[3],
@@ -1448,7 +1460,9 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     if (nchunks > 0) {
         const int64_t items = nchunks * a.h_v;
         const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
-        hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV>), dim3(grid), dim3(512), 0, st, p);
+        const bool ntr = static_cast<size_t>(items) * Rec<DK, DV, BF>::bytes > kStreamRecordBytes;
+        if (ntr) hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, true>), dim3(grid), dim3(512), 0, st, p);
+        else hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false>), dim3(grid), dim3(512), 0, st, p);
     }
     const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
     if (p.nseg > 1 && p.num_pairs > 0) {
