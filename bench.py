@@ -7,7 +7,8 @@ WY factors, inter-chunk state pass, outputs) over the bf16 workload B=1, T=4096,
 d_k = d_v = 128, chunk 64, negative-eigenvalue erase gates and a random fp32 initial state;
 `value` is its throughput in tokens/s. The decode step (gdn2_recurrent_step: 64 sequences,
 48 value heads over 16 key heads, d = 128, fp32 state updated in place) is timed over 256
-consecutive steps and reported in the `decode` object as state GB/s against HBM peak.
+consecutive steps and reported in the `decode` object as state GB/s against HBM peak, with
+the multi-token / bf16-state variants of gdn2_recurrent_fwd on the same shape beside it.
 
 Inputs are seeded synthetic tensors already resident in GPU memory when a timed region
 starts. Timing uses HIP events on the stream the library launches on (torch's current
@@ -193,6 +194,43 @@ def bench_decode_large_state(seed=4, steps=32):
     return res
 
 
+def bench_recurrent(T, state_dtype, calls, seed):
+    """gdn2_recurrent_fwd on the decode shape (64 sequences, 48 value heads over 16 key
+    heads, d = 128, fp32 inputs): `calls` back-to-back calls of T tokens each against one
+    state pool of `state_dtype`; inputs drawn on the GPU, laid out per call."""
+    sname = "bf16" if state_dtype == torch.bfloat16 else "f32"
+    wl = inputs.DecodeWorkload(f"recurrent_t{T}_{sname}state_n64_hv48_hk16_d128", torch.float32,
+                               64, 16, 48, 128, 128, steps=T * calls)
+    x = inputs.decode_inputs_device(wl, seed, T * calls)
+    N = wl.num_seqs
+    y = {n: x[n].reshape(calls, T, N, *x[n].shape[2:]).permute(0, 2, 1, 3, 4).contiguous()
+         for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    del x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"]
+    P = x["S"].to(state_dtype)
+    o = torch.empty(calls, N, T, wl.h_v, wl.d_v, device="cuda")
+
+    def run_all():
+        for c in range(calls):
+            g.recurrent_fwd(y["q"][c], y["k"][c], y["v"][c], y["log_alpha"][c], y["b"][c],
+                            y["w"][c], P, out=o[c])
+
+    run_all()
+    t_call = time_region(run_all, 1, torch.cuda.current_stream()) / calls
+    one = inputs.DecodeWorkload(wl.name, wl.dtype, N, wl.h_k, wl.h_v, wl.d_k, wl.d_v, steps=1)
+    nbytes1, st32, _ = decode_alg(one)
+    esz = 2 if state_dtype == torch.bfloat16 else 4
+    state_bytes = st32 * esz // 4
+    nbytes = state_bytes + T * (nbytes1 - st32)
+    assert torch.isfinite(P.float()).all()
+    res = {"workload": wl.name, "tokens_per_call": T, "calls": calls,
+           "us_per_call": t_call * 1e6, "tokens_per_s": N * T / t_call,
+           "state_GBps": state_bytes / t_call / 1e9, "total_GBps": nbytes / t_call / 1e9,
+           "hbm_frac": nbytes / t_call / 1e9 / HBM_PEAK_GBPS, "alg_bytes": nbytes}
+    del y, P, o
+    torch.cuda.empty_cache()
+    return res
+
+
 CPU_WORK_TARGET_S = 10.0     # CPU-seconds of oracle work per baseline sample
 
 
@@ -345,11 +383,14 @@ def main():
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": dbytes / t_step / 1e9 / HBM_PEAK_GBPS,
                             "traffic": measured_traffic("decode_step_n64_hv48", dsrc),
-                            "kernel": "decode_step_kernel", "alg_bytes": dbytes}}
+                            "kernel": "recurrent_fwd_kernel", "alg_bytes": dbytes}}
         if not args.no_cpu_baseline:
             dec["cpu_baseline"] = cpu_baseline_decode(dwl)
         if not args.no_other_workloads:
             dec["large_state_control"] = bench_decode_large_state()
+            dec["recurrent_variants"] = [bench_recurrent(1, torch.bfloat16, 256, 5),
+                                         bench_recurrent(4, torch.float32, 64, 6),
+                                         bench_recurrent(4, torch.bfloat16, 64, 7)]
         out["decode"] = dec
         if "value" not in out:
             out.update({"value": dwl.num_seqs / t_step, "unit": "tokens/s",

@@ -8,6 +8,8 @@ are not on a GPU.
 
     o, S_T = chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size=64)
     o      = recurrent_step(q, k, v, log_alpha, b, w, S)      # S updated in place
+    o      = recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx=None)
+                                      # T tokens per sequence against a state pool (fp32/bf16)
 
 Layouts: q, k [B,T,H_k,d_k]; v, w [B,T,H_v,d_v]; log_alpha, b [B,T,H_v,d_k];
 states [N,H_v,d_k,d_v] fp32. ``log_alpha`` is log of the decay (<= 0). Decode inputs drop
@@ -25,6 +27,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "_build", "libgdn2.so")
 
 GDN2_F32, GDN2_BF16 = 0, 1
+GDN2_STATE_F32, GDN2_STATE_BF16 = 0, 1
 STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL_ARG", 2: "GDN2_ERR_BAD_SHAPE",
           3: "GDN2_ERR_UNSUPPORTED", 4: "GDN2_ERR_WORKSPACE", 5: "GDN2_ERR_HIP"}
 CHUNK_SIZE = 64
@@ -68,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i32, vp, vp, dp, vp, sz, vp]
         L.gdn2_recurrent_step.restype = i32
         L.gdn2_recurrent_step.argtypes = [vp] * 8 + [dp, vp]
+        L.gdn2_recurrent_fwd.restype = i32
+        L.gdn2_recurrent_fwd.argtypes = [vp] * 7 + [i32, vp, i32, vp, dp, vp]
         L.gdn2_check_cu_seqlens.restype = i32
         L.gdn2_check_cu_seqlens.argtypes = [vp, i32, i32]
         _lib = L
@@ -179,6 +184,51 @@ def recurrent_step(q, k, v, log_alpha, b, w, S, out: Optional[torch.Tensor] = No
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib().gdn2_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                    _ptr(S), _ptr(o), ctypes.byref(dims), stream)
+    _raise_on(st)
+    return o
+
+
+def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """T tokens per sequence against a pool of recurrent states, updated in place.
+
+    q, k [N,T,H_k,d_k]; v, w [N,T,H_v,d_v]; log_alpha, b [N,T,H_v,d_k] (fp32 or bf16);
+    state [num_slots,H_v,d_k,d_v] fp32 or bf16; state_idx int32 [N] (slot of each sequence,
+    None: slot n; out-of-range entries are padding: zero o rows, no state change).
+    Returns o [N,T,H_v,d_v] in the input dtype.
+    """
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
+        _need_gpu(name, t, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    _need_gpu("state", state, dev)
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError("q and k must both be [N,T,H_k,d_k]")
+    N, T, Hk, dk = q.shape
+    if v.dim() != 4 or v.shape[:2] != (N, T) or w.shape != v.shape:
+        raise ValueError("v and w must both be [N,T,H_v,d_v]")
+    Hv, dv = v.shape[2], v.shape[3]
+    if log_alpha.shape != (N, T, Hv, dk) or b.shape != (N, T, Hv, dk):
+        raise ValueError("log_alpha and b must be [N,T,H_v,d_k]")
+    if state.dim() != 4 or state.shape[1:] != (Hv, dk, dv):
+        raise ValueError(f"state must be [num_slots,{Hv},{dk},{dv}]")
+    if state.dtype == torch.float32:
+        sdt = GDN2_STATE_F32
+    elif state.dtype == torch.bfloat16:
+        sdt = GDN2_STATE_BF16
+    else:
+        raise TypeError("state must be float32 or bfloat16")
+    if state_idx is not None:
+        _need_gpu("state_idx", state_idx, dev)
+        if state_idx.dtype != torch.int32 or state_idx.shape != (N,):
+            raise ValueError(f"state_idx must be int32 [{N}]")
+    dims = Dims(N, T, 0, Hk, Hv, dk, dv, _dtype_code(q.dtype))
+    o = out if out is not None else torch.empty(N, T, Hv, dv, dtype=q.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib().gdn2_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                  _ptr(state), sdt, _ptr(state_idx), state.shape[0], _ptr(o),
+                                  ctypes.byref(dims), stream)
     _raise_on(st)
     return o
 

@@ -136,37 +136,69 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
     return GDN2_OK;
 }
 
-gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
-                                const void *log_alpha, const void *b, const void *w, float *S,
-                                void *o, const gdn2_dims *dims, void *stream) {
+static gdn2_status recurrent_common(const void *q, const void *k, const void *v,
+                                    const void *log_alpha, const void *b, const void *w,
+                                    void *S, int32_t state_dtype, const int32_t *idx,
+                                    int32_t num_slots, void *o, const gdn2_dims *dims,
+                                    void *stream, const char *where) {
     if (!dims) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
     gdn2_status st = check_heads(dims);
     if (st != GDN2_OK) return st;
-    if (dims->seqlen != 1) return fail(GDN2_ERR_BAD_SHAPE, "recurrent step needs seqlen = 1");
+    if (state_dtype != GDN2_STATE_F32 && state_dtype != GDN2_STATE_BF16)
+        return fail(GDN2_ERR_UNSUPPORTED, "state_dtype must be GDN2_STATE_F32 or GDN2_STATE_BF16");
+    if (dims->seqlen < 1) return fail(GDN2_ERR_BAD_SHAPE, "seqlen (tokens per sequence) must be >= 1");
     if (dims->batch < 0) return fail(GDN2_ERR_BAD_SHAPE, "batch must be >= 0");
-    if (static_cast<int64_t>(dims->batch) * dims->h_v * dims->d_k * dims->d_v > kMaxElems)
+    if (num_slots < 0) return fail(GDN2_ERR_BAD_SHAPE, "num_slots must be >= 0");
+    if (!idx && num_slots < dims->batch)
+        return fail(GDN2_ERR_BAD_SHAPE, "without state_idx, num_slots must be >= batch");
+    const int64_t per_state = static_cast<int64_t>(dims->h_v) * dims->d_k * dims->d_v;
+    if (static_cast<int64_t>(num_slots) * per_state > kMaxElems)
         return fail(GDN2_ERR_BAD_SHAPE, "state tensor too large");
     if (static_cast<int64_t>(dims->batch) * dims->h_v > INT32_MAX)
         return fail(GDN2_ERR_BAD_SHAPE, "too many states");
+    const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
+    const int64_t hd = static_cast<int64_t>(dims->h_v) * (dims->d_k > dims->d_v ? dims->d_k : dims->d_v);
+    if (tokens > INT32_MAX || tokens * hd > kMaxElems)
+        return fail(GDN2_ERR_BAD_SHAPE, "tensors too large");
     if (dims->batch == 0) {
         g_last_error[0] = '\0';
         return GDN2_OK;
     }
-    if (!q || !k || !v || !log_alpha || !b || !w || !S || !o)
-        return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w, S and o are required");
+    if (!q || !k || !v || !log_alpha || !b || !w || !o || (num_slots > 0 && !S))
+        return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w, the state and o are required");
     if (o == q || o == k || o == v || o == log_alpha || o == b || o == w || o == S)
         return fail(GDN2_ERR_BAD_SHAPE, "o must not alias an input or the state");
 
     gdn2::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.b = b; a.w = w;
-    a.S = S; a.o = o;
-    a.num_seqs = dims->batch; a.h_k = dims->h_k; a.h_v = dims->h_v;
-    a.d_k = dims->d_k; a.d_v = dims->d_v;
+    a.S = S; a.idx = idx; a.o = o;
+    a.num_seqs = dims->batch; a.ntok = dims->seqlen; a.num_slots = num_slots;
+    a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
     a.bf16 = dims->dtype == GDN2_BF16;
+    a.state_bf16 = state_dtype == GDN2_STATE_BF16;
     const hipError_t e = gdn2::launch_decode(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return fail_hip(e, "gdn2_recurrent_step launch");
+    if (e != hipSuccess) return fail_hip(e, where);
     g_last_error[0] = '\0';
     return GDN2_OK;
+}
+
+gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
+                                const void *log_alpha, const void *b, const void *w, float *S,
+                                void *o, const gdn2_dims *dims, void *stream) {
+    if (!dims) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
+    if (dims->seqlen != 1) return fail(GDN2_ERR_BAD_SHAPE, "recurrent step needs seqlen = 1");
+    return recurrent_common(q, k, v, log_alpha, b, w, S, GDN2_STATE_F32, nullptr,
+                            dims->batch < 0 ? 0 : dims->batch, o, dims, stream,
+                            "gdn2_recurrent_step launch");
+}
+
+gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v,
+                               const void *log_alpha, const void *b, const void *w,
+                               void *state, int32_t state_dtype, const int32_t *state_idx,
+                               int32_t num_slots, void *o, const gdn2_dims *dims,
+                               void *stream) {
+    return recurrent_common(q, k, v, log_alpha, b, w, state, state_dtype, state_idx,
+                            num_slots, o, dims, stream, "gdn2_recurrent_fwd launch");
 }
 
 gdn2_status gdn2_check_cu_seqlens(const int32_t *cu, int32_t num_seqs, int32_t total_tokens) {

@@ -10,10 +10,12 @@ constexpr int kChunk = 64;   // chunk size of the chunked forward
 
 struct DecodeArgs {
     const void *q, *k, *v, *log_alpha, *b, *w;
-    float *S;
+    void *S;                 // state pool [num_slots][h_v][d_k][d_v], fp32 or bf16
+    const int32_t *idx;      // slot of each sequence, or NULL (slot n)
     void *o;
-    int num_seqs, h_k, h_v, d_k, d_v;
-    bool bf16;
+    int num_seqs, ntok, num_slots, h_k, h_v, d_k, d_v;
+    bool bf16;               // input dtype
+    bool state_bf16;         // state dtype
 };
 
 struct ChunkArgs {

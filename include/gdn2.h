@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 1
+#define GDN2_ABI_VERSION 2
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -73,6 +73,12 @@ typedef enum gdn2_dtype {
     GDN2_BF16 = 1               /* bf16 inputs and o; bf16 matrix-core operands, fp32
                                    accumulation, fp32 state */
 } gdn2_dtype;
+
+typedef enum gdn2_state_dtype {
+    GDN2_STATE_F32 = 0,         /* fp32 recurrent state */
+    GDN2_STATE_BF16 = 1         /* bf16 recurrent state: widened to fp32 for the update inside
+                                   a call, rounded to nearest even when written back */
+} gdn2_state_dtype;
 
 typedef struct gdn2_dims {
     int32_t batch;      /* dense: number of sequences B. packed: must be 1.
@@ -144,6 +150,40 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
 gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
                                 const void *log_alpha, const void *b, const void *w,
                                 float *S, void *o, const gdn2_dims *dims, void *stream);
+
+/*
+ * Multi-token recurrent forward against a state cache (burn-gdn2 "FusedRecurrent" mode run
+ * over T tokens). The llama.cpp decode notes (LocalAI mirror) describe, in section 2, the
+ * recurrent cache whose slots hold one state per sequence and are read and written back
+ * every step, and a fused kernel that keeps its share of a state in registers across the
+ * tokens of the call; section 4 names a bf16 state as the way to cut the state traffic.
+ * T > 1 serves short multi-token steps (draft tokens of speculative decoding, short
+ * prefills) at the state traffic of one step.
+ *
+ * Sequence n runs tokens 0..T-1 in order, starting from the state in its slot, and the
+ * slot holds the state after token T-1 on return. Every state is read from memory once and
+ * written once per call, whatever T is.
+ *
+ *   q, k          device [N, T, h_k, d_k]   (dims->batch = N >= 0, dims->seqlen = T >= 1)
+ *   v, w          device [N, T, h_v, d_v]
+ *   log_alpha, b  device [N, T, h_v, d_k]   (input dtype dims->dtype for all six)
+ *   state         device [num_slots, h_v, d_k, d_v] in state_dtype (gdn2_state_dtype),
+ *                 read and updated in place
+ *   state_idx     device int32 [N]: the slot of sequence n; or NULL, meaning slot n (then
+ *                 num_slots must be >= N). An entry outside [0, num_slots) marks a padding
+ *                 sequence: its slot is neither read nor written and its o rows are zeros.
+ *                 Precondition (not checked on the device): the valid entries are
+ *                 distinct; two sequences on one slot race.
+ *   o             device [N, T, h_v, d_v] in the input dtype; must not alias an input or
+ *                 the state
+ *   stream        hipStream_t
+ * With T = 1, state_idx = NULL and an fp32 state this is gdn2_recurrent_step.
+ */
+gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v,
+                               const void *log_alpha, const void *b, const void *w,
+                               void *state, int32_t state_dtype, const int32_t *state_idx,
+                               int32_t num_slots, void *o, const gdn2_dims *dims,
+                               void *stream);
 
 /*
  * Host helper: checks a HOST copy of cu_seqlens (N+1 entries) against total tokens T.

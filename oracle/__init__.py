@@ -9,7 +9,10 @@ Two independent evaluations of the method live here:
 
 * ``recurrent`` -- the per-token recurrence of the burn-gdn2 0.1.5 docs page
   (section "Architecture"), written out in plain C (``gdn2_oracle.c``), fp64, one
-  (sequence, value head) pair at a time. ``decode_step`` is one token of it.
+  (sequence, value head) pair at a time. ``decode_step`` is one token of it, and
+  ``recurrent_cache`` runs it over a pool of stored states (the recurrent cache of the
+  llama.cpp decode notes, LocalAI mirror, section 2), optionally stored in bfloat16
+  (section 4 of the same notes), with ``round_to_bf16`` the rounding of the stored state.
 * ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
   mode) and on the FG^2-GDN summary (section 2C, DPLR structure and the WY
   representation), in numpy fp64. It exists to pin the recurrence: the two are
@@ -150,6 +153,54 @@ def decode_step(q, k, v, log_alpha, b, w, S, pairs=None, threads=None):
     cu = np.arange(N + 1)
     return recurrent(q, k, v, log_alpha, b, w, S0=S, cu_seqlens=cu, pairs=pairs,
                      threads=threads)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 value of each element, ties to even, returned as fp64.
+
+    bfloat16 keeps 8 significant bits (1 implicit + 7 stored) and fp32's exponent range:
+    a finite x with 2^(e-1) <= |x| < 2^e (numpy's frexp exponent e) is rounded to a
+    multiple of 2^(e-8), and below the smallest normal 2^-126 to a multiple of 2^-133
+    (the subnormal spacing). np.rint rounds halves to even. Magnitudes that round past the
+    largest finite value (2 - 2^-7) * 2^127 become infinities; NaN stays NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    ulp = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(x / ulp) * ulp
+    big = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r = np.where(np.abs(r) > big, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def recurrent_cache(q, k, v, log_alpha, b, w, state, state_idx=None, bf16_state=False,
+                    threads=None):
+    """T tokens per sequence against a pool of recurrent states (the decode cache).
+
+    q, k [N,T,H_k,d_k]; v, w [N,T,H_v,d_v]; log_alpha, b [N,T,H_v,d_k]; ``state`` the pool
+    [num_slots,H_v,d_k,d_v] as stored; ``state_idx`` [N] the slot of each sequence (None:
+    slot n). An entry outside [0, num_slots) marks a padding sequence: its o rows are zero
+    and no slot changes. Each valid sequence runs the token-by-token recurrence over its T
+    tokens from the state in its slot; the slot then holds the final state, rounded to the
+    nearest bfloat16 when the pool is stored in bfloat16 (``bf16_state``).
+    Returns (o [N,T,H_v,d_v], new pool), fp64.
+    """
+    q, k, v, w, la, b = (np.asarray(x, dtype=np.float64) for x in (q, k, v, w, log_alpha, b))
+    N, T = k.shape[:2]
+    pool = np.array(state, dtype=np.float64, copy=True)
+    num_slots = pool.shape[0]
+    idx = np.arange(N) if state_idx is None else np.asarray(state_idx, dtype=np.int64)
+    o = np.zeros(v.shape)
+    live = [n for n in range(N) if 0 <= idx[n] < num_slots]
+    if not live:
+        return o, pool
+    flat = lambda x: x[live].reshape(len(live) * T, *x.shape[2:])
+    cu = np.arange(len(live) + 1) * T
+    o_l, S_l = recurrent(flat(q), flat(k), flat(v), flat(la), flat(b), flat(w),
+                         S0=pool[idx[live]], cu_seqlens=cu, threads=threads)
+    o[live] = o_l.reshape(len(live), T, *o_l.shape[1:])
+    pool[idx[live]] = round_to_bf16(S_l) if bf16_state else S_l
+    return o, pool
 
 
 def _unit_lower_inverse(L: np.ndarray) -> np.ndarray:

@@ -35,7 +35,8 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert {"gdn2_chunk_fwd", "gdn2_recurrent_step", "gdn2_chunk_fwd_workspace_bytes"} <= set(names)
+    assert {"gdn2_chunk_fwd", "gdn2_recurrent_step", "gdn2_recurrent_fwd",
+            "gdn2_chunk_fwd_workspace_bytes"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (gdn2_\w+)$", out, flags=re.M))
@@ -46,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn2_abi_version() == 1
+    assert L.gdn2_abi_version() == 2
     assert L.gdn2_status_string(0) == b"ok"
     assert b"workspace" in L.gdn2_status_string(4)
     assert L.gdn2_status_string(99) == b"unknown status"
@@ -102,6 +103,29 @@ def test_recurrent_step_rejects_bad_arguments(L):
     assert step(L, Dims(**ok), S=None) == 1
     assert step(L, Dims(**ok), o=FAKE) == 2               # o aliases q
     assert step(L, Dims(**{**ok, "batch": 0})) == 0       # empty batch: nothing to do
+
+
+def fwd(L, dims, state_dtype=0, idx=None, num_slots=8, S=FAKE, o=None):
+    # o defaults to the q pointer: a call that passed every other check is still rejected
+    return L.gdn2_recurrent_fwd(FAKE, ctypes.c_void_p(0x3000), FAKE, FAKE, FAKE, FAKE, S,
+                                state_dtype, idx, num_slots, FAKE if o is None else o,
+                                None if dims is None else ctypes.byref(dims), None)
+
+
+def test_recurrent_fwd_rejects_bad_arguments(L):
+    ok = dict(batch=4, seqlen=3, num_seqs=0, h_k=2, h_v=6, d_k=128, d_v=64, dtype=1)
+    assert fwd(L, None) == 1
+    assert fwd(L, Dims(**{**ok, "seqlen": 0})) == 2
+    assert fwd(L, Dims(**{**ok, "h_v": 5})) == 2
+    assert fwd(L, Dims(**{**ok, "d_k": 96})) == 3
+    assert fwd(L, Dims(**ok), state_dtype=2) == 3
+    assert fwd(L, Dims(**ok), num_slots=3) == 2            # no index: one slot per sequence
+    assert fwd(L, Dims(**ok), num_slots=-1, idx=FAKE) == 2
+    assert fwd(L, Dims(**ok), S=None) == 1
+    assert fwd(L, Dims(**ok), idx=FAKE, num_slots=2) == 2   # o aliases q
+    assert fwd(L, Dims(**ok), state_dtype=1, o=FAKE) == 2
+    assert fwd(L, Dims(**ok), o=ctypes.c_void_p(0x5000), S=ctypes.c_void_p(0x5000)) == 2
+    assert fwd(L, Dims(**{**ok, "batch": 0})) == 0          # empty batch: nothing to do
 
 
 def test_workspace_size_formula(L):

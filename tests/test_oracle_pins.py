@@ -300,3 +300,85 @@ def test_identity_token_leaves_state_unchanged():
     o, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
     assert close(ST, S0, 0.0)
     assert close(o[0, 0], S0[0, 0].T @ q[0, 0])
+
+
+# ---- the recurrent cache: slots, padding entries, bf16-stored states ---------------------
+# (llama.cpp decode notes, LocalAI mirror: section 2 for the slot cache read and written back
+# every step, section 4 for a bf16 state)
+
+def test_round_to_bf16_closed_forms_and_torch_cast():
+    """Round-to-nearest-even onto 8 significant bits, fp32's exponent range."""
+    import torch
+    r = oracle.round_to_bf16
+    # spacing 2^-7 on [1, 2): a half-way point goes to the even neighbour
+    assert r(1.0 + 2.0 ** -8) == 1.0
+    assert r(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert r(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert r(-(1.0 + 3 * 2.0 ** -8)) == -(1.0 + 2.0 ** -6)
+    assert r(3.0 * 2.0 ** 100) == 3.0 * 2.0 ** 100          # exactly representable
+    assert r(2.0 ** -133) == 2.0 ** -133                    # smallest subnormal
+    assert r(2.0 ** -135) == 0.0
+    assert r(0.0) == 0.0 and np.isinf(r(3.4e38)) and np.isnan(r(np.nan))
+    # an independent implementation: torch's fp32 -> bf16 cast, on fp32 inputs
+    x = np.random.default_rng(16).standard_normal(20000).astype(np.float32)
+    x *= np.float32(2.0) ** np.random.default_rng(17).integers(-60, 60, 20000).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(r(x.astype(np.float64)), t)
+
+
+def cache_case(rng, N, T, Hk=1, Hv=2, dk=4, dv=3, slots=7):
+    q, k, v, la, b, w = (x.reshape(N, T, *x.shape[1:]) for x in
+                         rand_case(rng, N * T, Hk=Hk, Hv=Hv, dk=dk, dv=dv))
+    pool = rng.standard_normal((slots, Hv, dk, dv))
+    return q, k, v, la, b, w, pool
+
+
+def test_cache_slots_follow_the_index_and_padding_is_inert():
+    rng = np.random.default_rng(18)
+    N, T = 5, 4
+    q, k, v, la, b, w, pool = cache_case(rng, N, T)
+    idx = np.array([6, 1, -1, 3, 7])          # -1 and 7 (>= 7 slots) are padding entries
+    o, new = oracle.recurrent_cache(q, k, v, la, b, w, pool, idx)
+    for n, s in enumerate(idx):
+        if 0 <= s < 7:
+            on, Sn = oracle.recurrent(q[n], k[n], v[n], la[n], b[n], w[n], S0=pool[s:s + 1])
+            assert close(o[n], on) and close(new[s], Sn[0])
+        else:
+            assert np.all(o[n] == 0.0)
+    for s in (0, 2, 4, 5):                     # slots no sequence names are unchanged
+        assert np.array_equal(new[s], pool[s])
+    # permuting the sequences together with their slots permutes nothing else
+    perm = np.array([3, 0, 4, 2, 1])
+    o2, new2 = oracle.recurrent_cache(q[perm], k[perm], v[perm], la[perm], b[perm], w[perm],
+                                      pool, idx[perm])
+    assert close(o2, o[perm]) and close(new2, new)
+
+
+def test_cache_multi_token_equals_single_token_calls():
+    """T tokens in one call equal T calls of one token with the pool carried (fp32 pool)."""
+    rng = np.random.default_rng(19)
+    N, T = 3, 6
+    q, k, v, la, b, w, pool = cache_case(rng, N, T, Hk=1, Hv=3, dk=5, dv=4)
+    idx = np.array([2, 0, 5])
+    o, new = oracle.recurrent_cache(q, k, v, la, b, w, pool, idx)
+    P = pool
+    for t in range(T):
+        sl = slice(t, t + 1)
+        ot, P = oracle.recurrent_cache(q[:, sl], k[:, sl], v[:, sl], la[:, sl], b[:, sl],
+                                       w[:, sl], P, idx)
+        assert close(ot[:, 0], o[:, t])
+    assert close(P, new)
+
+
+def test_cache_bf16_pool_rounds_only_the_stored_state():
+    rng = np.random.default_rng(20)
+    N, T = 2, 5
+    q, k, v, la, b, w, pool = cache_case(rng, N, T, dk=6, dv=4, slots=3)
+    pool = oracle.round_to_bf16(pool)          # a bf16 pool holds bf16 values
+    o32, new32 = oracle.recurrent_cache(q, k, v, la, b, w, pool, None)
+    o16, new16 = oracle.recurrent_cache(q, k, v, la, b, w, pool, None, bf16_state=True)
+    assert np.array_equal(o16, o32)            # outputs inside the call see the fp64 state
+    assert np.array_equal(new16[:N], oracle.round_to_bf16(new32[:N]))
+    assert np.array_equal(new16[N:], pool[N:])
+    rel = np.abs(new16[:N] - new32[:N]) / np.maximum(np.abs(new32[:N]), 1e-30)
+    assert np.max(rel) <= 2.0 ** -8            # half a unit in the last place of 8 bits
