@@ -194,7 +194,7 @@ def bench_decode_large_state(seed=4, steps=32):
     return res
 
 
-def bench_recurrent(T, state_dtype, calls, seed):
+def bench_recurrent(T, state_dtype, calls, seed, traffic_key=None):
     """gdn2_recurrent_fwd on the decode shape (64 sequences, 48 value heads over 16 key
     heads, d = 128, fp32 inputs): `calls` back-to-back calls of T tokens each against one
     state pool of `state_dtype`; inputs drawn on the GPU, laid out per call."""
@@ -225,7 +225,9 @@ def bench_recurrent(T, state_dtype, calls, seed):
     res = {"workload": wl.name, "tokens_per_call": T, "calls": calls,
            "us_per_call": t_call * 1e6, "tokens_per_s": N * T / t_call,
            "state_GBps": state_bytes / t_call / 1e9, "total_GBps": nbytes / t_call / 1e9,
-           "hbm_frac": nbytes / t_call / 1e9 / HBM_PEAK_GBPS, "alg_bytes": nbytes}
+           "hbm_frac": nbytes / t_call / 1e9 / HBM_PEAK_GBPS, "alg_bytes": nbytes,
+           "traffic": None if traffic_key is None else measured_traffic(
+               traffic_key, source_hash("gdn2_decode.hip", "gdn2_common.h"))}
     del y, P, o
     torch.cuda.empty_cache()
     return res
@@ -309,6 +311,10 @@ def profile_driver():
     yy = {n: y[n][0].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w")}
     for _ in range(20):
         g.recurrent_step(yy["q"], yy["k"], yy["v"], yy["log_alpha"], yy["b"], yy["w"], S)
+    Sb = S.to(torch.bfloat16)
+    y1 = {n: t[:, None] for n, t in yy.items()}
+    for _ in range(20):
+        g.recurrent_fwd(y1["q"], y1["k"], y1["v"], y1["log_alpha"], y1["b"], y1["w"], Sb)
     src = torch.empty(1 << 26, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -329,7 +335,8 @@ def main():
     ap.add_argument("--only", choices=["chunk", "decode", "all"], default="all")
     ap.add_argument("--profile-driver", action="store_true",
                     help="short fixed sequence for hardware-counter runs: 5 chunk forwards, "
-                         "20 decode steps and 3 copies of 256 MiB (the copy calibrates the "
+                         "20 decode steps with an fp32 state and 20 with a bf16 state, and 3 "
+                         "copies of 256 MiB (the copy calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -388,7 +395,8 @@ def main():
             dec["cpu_baseline"] = cpu_baseline_decode(dwl)
         if not args.no_other_workloads:
             dec["large_state_control"] = bench_decode_large_state()
-            dec["recurrent_variants"] = [bench_recurrent(1, torch.bfloat16, 256, 5),
+            dec["recurrent_variants"] = [bench_recurrent(1, torch.bfloat16, 256, 5,
+                                                         "decode_step_bf16state_n64_hv48"),
                                          bench_recurrent(4, torch.float32, 64, 6),
                                          bench_recurrent(4, torch.bfloat16, 64, 7)]
         out["decode"] = dec

@@ -20,12 +20,12 @@
 // no index is given). A slot outside [0, num_slots) marks a padding entry: the state is not
 // touched and the sequence's o rows are zero.
 //
-// Design for gfx950: one 256-thread workgroup per (sequence, value head) state. Thread t
-// owns one 16-byte vector of adjacent columns (4 fp32 or 8 bf16) of DK / RG rows, so each
-// wave instruction reads or writes whole contiguous rows. All state loads are issued
-// before any arithmetic. The state stays in fp32 registers across the T tokens; the token
-// vectors are staged in LDS eight tokens at a time. The column reductions run as a wave
-// shuffle across row groups and then a sum over the four waves through LDS.
+// Design for gfx950: one 256-thread workgroup per (sequence, value head) state, one 16-byte
+// vector (4 fp32 or 8 bf16 columns) per lane per row (lane geometry below). All state
+// loads are issued before any arithmetic, and the state stays in fp32 registers across the
+// T tokens. The token vectors are staged in LDS eight tokens at a time; the two reductions
+// over d_k run inside each wave on DPP row rotations and the gfx950 row-swap instructions
+// (VALU work, no LDS traffic).
 #include "gdn2_common.h"
 #include "gdn2_internal.h"
 #include "gdn2_mfma.h"
@@ -76,39 +76,81 @@ template <> struct svec<bf16_t> {
     }
 };
 
-template <typename T, typename ST, int DK, int DV, bool NTS>
+// Sum of x over the lanes of a wave that share lane % CGW (CGW a power of two < 64): row
+// rotations within 16-lane rows (DPP row_ror:1/2/4/8) for strides below 16, then the gfx950 row-swap
+// instructions for 16 and 32. Every lane ends with the full sum. All of it is VALU work.
+template <int CGW>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    if constexpr (CGW <= 1) x += __builtin_amdgcn_update_dpp(0.f, x, 0x121, 0xF, 0xF, false);
+    if constexpr (CGW <= 2) x += __builtin_amdgcn_update_dpp(0.f, x, 0x122, 0xF, 0xF, false);
+    if constexpr (CGW <= 4) x += __builtin_amdgcn_update_dpp(0.f, x, 0x124, 0xF, 0xF, false);
+    if constexpr (CGW <= 8) x += __builtin_amdgcn_update_dpp(0.f, x, 0x128, 0xF, 0xF, false);
+    if constexpr (CGW <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                        false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);                       // + lane ^ 16
+    }
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);                        // + lane ^ 32
+}
+
+// Lane geometry of one state. The workgroup's four waves split the state either by rows
+// (COLW = false: each wave holds whole rows, so every wave instruction reads whole rows,
+// the best pattern for streaming; the d_k reductions then finish across the waves through
+// LDS, one barrier per token) or by columns (COLW = true: each wave holds a quarter of the
+// columns of every row, 128-byte pieces of rows; the reductions stay inside the wave, so
+// tokens need no barrier). Single-token calls are bound by the state traffic and take the
+// row split; multi-token calls are bound by the per-token dependency chain and take the
+// column split.
+template <int DK, int DV, int VN, bool COLW>
+struct Geom {
+    static constexpr int NW = kDecodeThreads / 64;
+    static constexpr int WC = COLW ? DV / NW : DV;    // columns a wave spans
+    static constexpr int CG = WC / VN;                // column groups a wave spans
+    static constexpr int RGW = 64 / CG;               // row groups in one wave
+    static constexpr int RG = COLW ? RGW : RGW * NW;  // row groups of the workgroup
+    static constexpr int RPT = DK / RG;               // rows per lane
+    static_assert(CG >= 1 && CG <= 64 && (CG & (CG - 1)) == 0, "lane layout");
+    static_assert(RPT >= 1 && RG * RPT == DK, "tile shape");
+};
+
+template <typename T, typename ST, int DK, int DV, bool NTS, bool COLW>
 __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ b, const T *__restrict__ w,
     ST *__restrict__ S, const int32_t *__restrict__ idx, T *__restrict__ o, int ntok,
     int num_slots, int h_k, int h_v, int group) {
     constexpr int NT = kDecodeThreads, NW = NT / 64;
-    constexpr int VN = svec<ST>::N;   // columns per thread
-    constexpr int CG = DV / VN;       // column groups per row
-    constexpr int RG = NT / CG;       // row groups
-    constexpr int RPT = DK / RG;      // rows per thread
-    constexpr int TB = kTokBlock;
-    static_assert(RPT >= 1 && RG * RPT == DK, "tile shape");
-    static_assert(CG <= 64 && 64 % CG == 0, "a wave must hold whole row groups");
+    constexpr int VN = svec<ST>::N;   // columns per lane (one 16-byte vector)
+    using Gm = Geom<DK, DV, VN, COLW>;
+    constexpr int CG = Gm::CG, RG = Gm::RG, RPT = Gm::RPT;
+    // The row split serves single-token calls only (the launch picks it for T = 1), so its
+    // token loop is resolved at compile time.
+    constexpr int TB = COLW ? kTokBlock : 1;
+    const int nt = COLW ? ntok : 1;
 
-    // staged token vectors: decay, b.k, k, q (key axis) and w.v (value axis)
-    __shared__ float s_a[TB][DK], s_bk[TB][DK], s_k[TB][DK], s_q[TB][DK], s_wv[TB][DV];
-    __shared__ float s_red[2][NW][2 * DV + 4];
+    // staged token vectors: (decay, b.k, q, k) per key-axis row, and w.v per column
+    __shared__ f32x4 s_tok[TB][DK];
+    __shared__ float s_wv[TB][DV];
+    // per-wave partial sums (row split only)
+    __shared__ float s_red[COLW ? 1 : NW][COLW ? 1 : 2 * DV + 4];
 
     const int pair = blockIdx.x;
     const int n = pair / h_v;
     const int h = pair - n * h_v;
     const int hk = h / group;
     const int tid = threadIdx.x;
-    const int cg = tid % CG;
-    const int rg = tid / CG;
     const int wave = tid >> 6, lane = tid & 63;
+    const int cg = lane % CG;
+    const int rg = COLW ? lane / CG : tid / CG;       // row group: rows rg + RG i
+    const int c0 = (COLW ? wave * Gm::WC : 0) + cg * VN;   // first column of this lane
 
     const int slot = idx ? idx[n] : n;
     if (slot < 0 || slot >= num_slots) {     // padding entry: zero o rows, state untouched
-        for (int i = tid; i < ntok * DV; i += NT) {
+        for (int i = tid; i < nt * DV; i += NT) {
             const int t = i / DV, c = i - t * DV;
-            io<T>::st(o + ((static_cast<size_t>(n) * ntok + t) * h_v + h) * DV + c, 0.f);
+            io<T>::st(o + ((static_cast<size_t>(n) * nt + t) * h_v + h) * DV + c, 0.f);
         }
         return;
     }
@@ -117,100 +159,97 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     float s[RPT][VN];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        svec<ST>::ld(Sp + static_cast<size_t>(rg + RG * i) * DV + VN * cg, s[i]);
+        svec<ST>::ld(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
 
-    for (int t0 = 0; t0 < ntok; t0 += TB) {
-        const int nb = min(TB, ntok - t0);
+    for (int t0 = 0; t0 < nt; t0 += TB) {
+        const int nb = min(TB, nt - t0);
         if (t0 > 0) __syncthreads();         // the previous block's vectors are consumed
-        // Token vectors of this block, widened to fp32 and staged in LDS.
+        // one pass over the block's nb (DK + DV) entries, spread over all threads
         for (int i = tid; i < nb * (DK + DV); i += NT) {
-            const int tt = i / (DK + DV), c = i - tt * (DK + DV);
-            const size_t tok = static_cast<size_t>(n) * ntok + t0 + tt;
-            if (c < DK) {
-                const size_t kq_off = (tok * h_k + hk) * DK + c;
-                const size_t g_off = (tok * h_v + h) * DK + c;
+            if (i < nb * DK) {
+                const int tt = i / DK, r = i - tt * DK;
+                const size_t tok = static_cast<size_t>(n) * nt + t0 + tt;
+                const size_t kq_off = (tok * h_k + hk) * DK + r;
+                const size_t g_off = (tok * h_v + h) * DK + r;
                 const float kk = io<T>::ld(k + kq_off);
-                s_k[tt][c] = kk;
-                s_q[tt][c] = io<T>::ld(q + kq_off);
-                s_bk[tt][c] = io<T>::ld(b + g_off) * kk;
-                s_a[tt][c] = __expf(io<T>::ld(log_alpha + g_off));
+                s_tok[tt][r] = f32x4{__expf(io<T>::ld(log_alpha + g_off)),
+                                     io<T>::ld(b + g_off) * kk, io<T>::ld(q + kq_off), kk};
             } else {
-                const size_t off = (tok * h_v + h) * DV + (c - DK);
-                s_wv[tt][c - DK] = io<T>::ld(w + off) * io<T>::ld(v + off);
+                const int iv = i - nb * DK, tt = iv / DV, c = iv - tt * DV;
+                const size_t off = ((static_cast<size_t>(n) * nt + t0 + tt) * h_v + h) * DV + c;
+                s_wv[tt][c] = io<T>::ld(w + off) * io<T>::ld(v + off);
             }
         }
         __syncthreads();
 
         for (int tt = 0; tt < nb; ++tt) {
-            const int buf = tt & 1;
             float y[VN], z[VN];
 #pragma unroll
             for (int j = 0; j < VN; ++j) y[j] = z[j] = 0.f;
             float kq = 0.f;
+            float kr[COLW ? 1 : RPT];             // the row split keeps k in registers
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const int r = rg + RG * i;
-                const float a = s_a[tt][r], bk = s_bk[tt][r], qq = s_q[tt][r];
+                const f32x4 g = s_tok[tt][rg + RG * i];     // decay, b.k, q, k
+                if constexpr (!COLW) kr[i] = g.w;
 #pragma unroll
                 for (int j = 0; j < VN; ++j) {
-                    s[i][j] *= a;
-                    y[j] += bk * s[i][j];
-                    z[j] += qq * s[i][j];
+                    s[i][j] *= g.x;
+                    y[j] += g.y * s[i][j];
+                    z[j] += g.z * s[i][j];
                 }
-                kq += s_k[tt][r] * qq;
+                kq += g.w * g.z;
             }
-            // Sum over the row groups held by this wave (lanes that differ by multiples of CG).
+            // sum over the row groups of this wave (lanes that share lane % CG)
 #pragma unroll
-            for (int off = CG; off < 64; off <<= 1) {
-#pragma unroll
-                for (int j = 0; j < VN; ++j) {
-                    y[j] += __shfl_xor(y[j], off);
-                    z[j] += __shfl_xor(z[j], off);
-                }
-                kq += __shfl_xor(kq, off);
+            for (int j = 0; j < VN; ++j) {
+                y[j] = lane_group_sum<CG>(y[j]);
+                z[j] = lane_group_sum<CG>(z[j]);
             }
-            if (lane < CG) {
+            kq = lane_group_sum<CG>(kq);
+            if constexpr (!COLW) {
+                // and over the waves, through LDS (one token per call: one barrier)
+                if (lane < CG) {
 #pragma unroll
-                for (int j = 0; j < VN; j += 4) {
-                    *reinterpret_cast<f32x4 *>(&s_red[buf][wave][VN * cg + j]) =
-                        f32x4{y[j], y[j + 1], y[j + 2], y[j + 3]};
-                    *reinterpret_cast<f32x4 *>(&s_red[buf][wave][DV + VN * cg + j]) =
-                        f32x4{z[j], z[j + 1], z[j + 2], z[j + 3]};
+                    for (int j = 0; j < VN; j += 4) {
+                        *reinterpret_cast<f32x4 *>(&s_red[wave][c0 + j]) =
+                            f32x4{y[j], y[j + 1], y[j + 2], y[j + 3]};
+                        *reinterpret_cast<f32x4 *>(&s_red[wave][DV + c0 + j]) =
+                            f32x4{z[j], z[j + 1], z[j + 2], z[j + 3]};
+                    }
+                    if (lane == 0) s_red[wave][2 * DV] = kq;
                 }
-                if (lane == 0) s_red[buf][wave][2 * DV] = kq;
-            }
-            // One barrier per token: s_red is double-buffered, and a thread that writes
-            // buffer buf again (two tokens later) has passed the next token's barrier, which
-            // every thread reaches only after reading this token's sums.
-            __syncthreads();
-            float Y[VN], Z[VN];
+                __syncthreads();
 #pragma unroll
-            for (int j = 0; j < VN; ++j) Y[j] = Z[j] = 0.f;
-            float KQ = 0.f;
+                for (int j = 0; j < VN; ++j) y[j] = z[j] = 0.f;
+                kq = 0.f;
 #pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
+                for (int wv = 0; wv < NW; ++wv) {
 #pragma unroll
-                for (int j = 0; j < VN; j += 4) {
-                    const f32x4 yy = *reinterpret_cast<const f32x4 *>(&s_red[buf][wv][VN * cg + j]);
-                    const f32x4 zz = *reinterpret_cast<const f32x4 *>(&s_red[buf][wv][DV + VN * cg + j]);
-                    Y[j] += yy.x; Y[j + 1] += yy.y; Y[j + 2] += yy.z; Y[j + 3] += yy.w;
-                    Z[j] += zz.x; Z[j + 1] += zz.y; Z[j + 2] += zz.z; Z[j + 3] += zz.w;
+                    for (int j = 0; j < VN; j += 4) {
+                        const f32x4 yy = *reinterpret_cast<const f32x4 *>(&s_red[wv][c0 + j]);
+                        const f32x4 zz = *reinterpret_cast<const f32x4 *>(&s_red[wv][DV + c0 + j]);
+                        y[j] += yy.x; y[j + 1] += yy.y; y[j + 2] += yy.z; y[j + 3] += yy.w;
+                        z[j] += zz.x; z[j + 1] += zz.y; z[j + 2] += zz.z; z[j + 3] += zz.w;
+                    }
+                    kq += s_red[wv][2 * DV];
                 }
-                KQ += s_red[buf][wv][2 * DV];
             }
             float u[VN];
 #pragma unroll
-            for (int j = 0; j < VN; ++j) u[j] = s_wv[tt][VN * cg + j] - Y[j];
+            for (int j = 0; j < VN; ++j) u[j] = s_wv[tt][c0 + j] - y[j];
             if (rg == 0) {
-                T *op = o + ((static_cast<size_t>(n) * ntok + t0 + tt) * h_v + h) * DV + VN * cg;
+                T *op = o + ((static_cast<size_t>(n) * nt + t0 + tt) * h_v + h) * DV + c0;
 #pragma unroll
                 for (int j = 0; j < VN; j += 4)
-                    io<T>::st4(op + j, f32x4{Z[j] + KQ * u[j], Z[j + 1] + KQ * u[j + 1],
-                                             Z[j + 2] + KQ * u[j + 2], Z[j + 3] + KQ * u[j + 3]});
+                    io<T>::st4(op + j, f32x4{z[j] + kq * u[j], z[j + 1] + kq * u[j + 1],
+                                             z[j + 2] + kq * u[j + 2], z[j + 3] + kq * u[j + 3]});
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const float kk = s_k[tt][rg + RG * i];
+                float kk;
+                if constexpr (COLW) kk = s_tok[tt][rg + RG * i].w;
+                else kk = kr[i];
 #pragma unroll
                 for (int j = 0; j < VN; ++j) s[i][j] += kk * u[j];
             }
@@ -218,15 +257,18 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        svec<ST>::template st<NTS>(Sp + static_cast<size_t>(rg + RG * i) * DV + VN * cg, s[i]);
+        svec<ST>::template st<NTS>(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
 }
 
 template <typename T, typename ST, int DK, int DV>
 static hipError_t launch_recurrent_t(const DecodeArgs &a, hipStream_t st) {
     const int pairs = a.num_seqs * a.h_v;
     const size_t state_bytes = static_cast<size_t>(pairs) * DK * DV * sizeof(ST);
-    auto kern = state_bytes > kStreamStateBytes ? recurrent_fwd_kernel<T, ST, DK, DV, true>
-                                                : recurrent_fwd_kernel<T, ST, DK, DV, false>;
+    const bool nts = state_bytes > kStreamStateBytes, colw = a.ntok > 1;
+    auto kern = colw ? (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, true>
+                            : recurrent_fwd_kernel<T, ST, DK, DV, false, true>)
+                     : (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, false>
+                            : recurrent_fwd_kernel<T, ST, DK, DV, false, false>);
     hipLaunchKernelGGL(kern, dim3(pairs), dim3(kDecodeThreads), 0, st,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<const T *>(a.log_alpha),
