@@ -233,6 +233,74 @@ def bench_recurrent(T, state_dtype, calls, seed, traffic_key=None):
     return res
 
 
+def bench_fused(steps, warmup, seed=8):
+    """The timed chunk workload and the decode step with the fusions of the burn-gdn2
+    "Architecture" diagram turned on (q/k L2-norm before the recurrence, SiLU-gated RMS norm
+    after it), timed against the same calls without them. The gate tensor adds one read of
+    an o-sized tensor to the algorithmic bytes."""
+    res = {}
+    wl = inputs.CHUNK_BF16_T4096
+    x = inputs.chunk_inputs_device(wl, seed)
+    B, T = x["q"].shape[:2]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    gate = torch.randn(B, T, wl.h_v, wl.d_v, generator=gen, device="cuda").to(wl.dtype)
+    nw = torch.rand(wl.d_v, generator=gen, device="cuda") + 0.5
+    ws = torch.empty(g.chunk_fwd_workspace_bytes(B, T, wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.dtype),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, T, wl.h_v, wl.d_v, dtype=wl.dtype, device="cuda")
+    S_T = torch.empty_like(x["S0"])
+
+    def call(fused):
+        def fn():
+            g.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S0=x["S0"],
+                        workspace=ws, out=o, final_state=S_T, qk_l2norm=fused,
+                        gate=gate if fused else None, norm_weight=nw if fused else None)
+        return fn
+
+    stream = torch.cuda.current_stream()
+    for fused in (False, True):
+        for _ in range(warmup):
+            call(fused)()
+    t_plain = time_region(call(False), steps, stream)
+    t_fused = time_region(call(True), steps, stream)
+    nbytes, _ = chunk_alg(wl, B * T, B)
+    nbytes += gate.numel() * gate.element_size()
+    res["chunk"] = {"workload": wl.name + "_qkl2norm_gatednorm", "us_per_call": t_fused * 1e6,
+                    "us_per_call_unfused": t_plain * 1e6, "tokens_per_s": B * T / t_fused,
+                    "alg_bytes": nbytes, "hbm_frac": nbytes / t_fused / 1e9 / HBM_PEAK_GBPS}
+    del x, ws, o, S_T, gate
+    dw = inputs.DECODE_F32
+    steps_d = 64
+    y = inputs.decode_inputs_device(dw, seed, steps_d)
+    yy = {n: y[n][:, :, None].contiguous() for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    dgate = torch.randn(steps_d, dw.num_seqs, 1, dw.h_v, dw.d_v, generator=gen, device="cuda")
+    dnw = torch.rand(dw.d_v, generator=gen, device="cuda") + 0.5
+    od = torch.empty(dw.num_seqs, 1, dw.h_v, dw.d_v, device="cuda")
+
+    def dcall(fused):
+        def fn():
+            for t in range(steps_d):
+                g.recurrent_fwd(yy["q"][t], yy["k"][t], yy["v"][t], yy["log_alpha"][t],
+                                yy["b"][t], yy["w"][t], y["S"], out=od, qk_l2norm=fused,
+                                gate=dgate[t] if fused else None,
+                                norm_weight=dnw if fused else None)
+        return fn
+
+    for fused in (False, True):
+        dcall(fused)()
+    t_plain = time_region(dcall(False), 1, stream) / steps_d
+    t_fused = time_region(dcall(True), 1, stream) / steps_d
+    dbytes, _, _ = decode_alg(dw)
+    dbytes += dw.num_seqs * dw.h_v * dw.d_v * 4
+    res["decode"] = {"workload": dw.name + "_qkl2norm_gatednorm", "us_per_step": t_fused * 1e6,
+                     "us_per_step_unfused": t_plain * 1e6, "alg_bytes": dbytes,
+                     "hbm_frac": dbytes / t_fused / 1e9 / HBM_PEAK_GBPS}
+    del y, yy, dgate, od
+    torch.cuda.empty_cache()
+    return res
+
+
 CPU_WORK_TARGET_S = 10.0     # CPU-seconds of oracle work per baseline sample
 
 
@@ -404,6 +472,8 @@ def main():
             out.update({"value": dwl.num_seqs / t_step, "unit": "tokens/s",
                         "ms_per_step": t_step * 1e3, "dtype": "f32",
                         "config": {"workload": dwl.name}, "roofline": dec["roofline"]})
+    if args.only == "all" and not args.no_other_workloads:
+        out["fused_qkl2norm_gatednorm"] = bench_fused(max(10, args.steps // 2), 3)
     if args.only in ("chunk", "all") and not args.no_other_workloads:
         out["other_chunk_workloads"] = [
             bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed)

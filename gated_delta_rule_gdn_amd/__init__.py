@@ -40,6 +40,12 @@ class Dims(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class Fusion(ctypes.Structure):
+    _fields_ = [("qk_l2norm", ctypes.c_int32), ("l2norm_eps", ctypes.c_float),
+                ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
+
+
 class GDN2Error(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS.get(status, status)}: {message}")
@@ -68,11 +74,12 @@ def lib() -> ctypes.CDLL:
         L.gdn2_chunk_fwd_workspace_bytes.restype = sz
         L.gdn2_chunk_fwd_workspace_bytes.argtypes = [dp, i32]
         L.gdn2_chunk_fwd.restype = i32
-        L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i32, vp, vp, dp, vp, sz, vp]
+        fp = ctypes.POINTER(Fusion)
+        L.gdn2_chunk_fwd.argtypes = [vp] * 8 + [i32, vp, vp, dp, vp, sz, fp, vp]
         L.gdn2_recurrent_step.restype = i32
         L.gdn2_recurrent_step.argtypes = [vp] * 8 + [dp, vp]
         L.gdn2_recurrent_fwd.restype = i32
-        L.gdn2_recurrent_fwd.argtypes = [vp] * 7 + [i32, vp, i32, vp, dp, vp]
+        L.gdn2_recurrent_fwd.argtypes = [vp] * 7 + [i32, vp, i32, vp, dp, fp, vp]
         L.gdn2_check_cu_seqlens.restype = i32
         L.gdn2_check_cu_seqlens.argtypes = [vp, i32, i32]
         _lib = L
@@ -106,6 +113,22 @@ def _need_gpu(name: str, t: torch.Tensor, device) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight, norm_eps):
+    """The gdn2_fusion argument (None when nothing is fused)."""
+    if not qk_l2norm and gate is None:
+        return None
+    if gate is not None:
+        _need_gpu("gate", gate, dev)
+        if gate.dtype != out_dtype or tuple(gate.shape) != tuple(out_shape):
+            raise ValueError(f"gate must be {out_dtype} {tuple(out_shape)}")
+        if norm_weight is None:
+            raise ValueError("a gate needs norm_weight")
+        _need_gpu("norm_weight", norm_weight, dev)
+        if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (out_shape[-1],):
+            raise ValueError(f"norm_weight must be fp32 [{out_shape[-1]}]")
+    return Fusion(1 if qk_l2norm else 0, l2norm_eps, _ptr(gate), _ptr(norm_weight), norm_eps)
+
+
 def chunk_fwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: int, d_v: int,
                               dtype: torch.dtype, num_seqs: int = 0,
                               chunk_size: int = CHUNK_SIZE) -> int:
@@ -115,9 +138,15 @@ def chunk_fwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: 
 
 def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: int = CHUNK_SIZE,
               output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
-              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked WY forward. Returns (o [B,T,H_v,d_v], S_T [N,H_v,d_k,d_v] fp32 or None)."""
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              qk_l2norm: bool = False, l2norm_eps: float = 1e-6,
+              gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+              norm_eps: float = 1e-5) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked WY forward. Returns (o [B,T,H_v,d_v], S_T [N,H_v,d_k,d_v] fp32 or None).
+
+    qk_l2norm: L2-normalise q and k inside the kernels. gate [B,T,H_v,d_v] with norm_weight
+    fp32 [d_v]: o is returned through the gated RMS norm o/rms(o) * weight * silu(gate).
+    """
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
         _need_gpu(name, t, dev)
@@ -152,10 +181,13 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
     if output_final_state:
         S_T = final_state if final_state is not None else torch.empty(
             N, Hv, dk, dv, dtype=torch.float32, device=dev)
+    fu = _fusion(dev, (B, T, Hv, dv), q.dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
+                 norm_eps)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                               _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(o), _ptr(S_T),
-                              ctypes.byref(dims), _ptr(workspace), workspace.numel(), stream)
+                              ctypes.byref(dims), _ptr(workspace), workspace.numel(),
+                              None if fu is None else ctypes.byref(fu), stream)
     _raise_on(st)
     return o, S_T
 
@@ -189,13 +221,16 @@ def recurrent_step(q, k, v, log_alpha, b, w, S, out: Optional[torch.Tensor] = No
 
 
 def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Tensor] = None,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                  l2norm_eps: float = 1e-6, gate: Optional[torch.Tensor] = None,
+                  norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5
+                  ) -> torch.Tensor:
     """T tokens per sequence against a pool of recurrent states, updated in place.
 
     q, k [N,T,H_k,d_k]; v, w [N,T,H_v,d_v]; log_alpha, b [N,T,H_v,d_k] (fp32 or bf16);
     state [num_slots,H_v,d_k,d_v] fp32 or bf16; state_idx int32 [N] (slot of each sequence,
     None: slot n; out-of-range entries are padding: zero o rows, no state change).
-    Returns o [N,T,H_v,d_v] in the input dtype.
+    Returns o [N,T,H_v,d_v] in the input dtype. qk_l2norm, gate, norm_weight: as in chunk_fwd.
     """
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
@@ -225,10 +260,13 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
             raise ValueError(f"state_idx must be int32 [{N}]")
     dims = Dims(N, T, 0, Hk, Hv, dk, dv, _dtype_code(q.dtype))
     o = out if out is not None else torch.empty(N, T, Hv, dv, dtype=q.dtype, device=dev)
+    fu = _fusion(dev, (N, T, Hv, dv), q.dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
+                 norm_eps)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib().gdn2_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                   _ptr(state), sdt, _ptr(state_idx), state.shape[0], _ptr(o),
-                                  ctypes.byref(dims), stream)
+                                  ctypes.byref(dims), None if fu is None else ctypes.byref(fu),
+                                  stream)
     _raise_on(st)
     return o
 

@@ -39,6 +39,27 @@ gdn2_status check_heads(const gdn2_dims *d) {
 
 constexpr int64_t kMaxElems = (int64_t{1} << 40);   // bound on any tensor's element count
 
+bool eps_ok(float e) { return e >= 0.f && e <= 1e30f; }   // also rejects NaN
+
+// Checks the optional fusion options and copies them into the launch arguments.
+gdn2_status take_fusion(const gdn2_fusion *f, const void *o, gdn2::Fusion *out) {
+    *out = gdn2::Fusion{};
+    if (!f) return GDN2_OK;
+    if (f->qk_l2norm && !eps_ok(f->l2norm_eps))
+        return fail(GDN2_ERR_BAD_SHAPE, "l2norm_eps must be finite and >= 0");
+    if (f->gate) {
+        if (!f->norm_weight) return fail(GDN2_ERR_NULL_ARG, "a gate needs norm_weight");
+        if (!eps_ok(f->norm_eps)) return fail(GDN2_ERR_BAD_SHAPE, "norm_eps must be finite and >= 0");
+        if (f->gate == o) return fail(GDN2_ERR_BAD_SHAPE, "the gate must not alias o");
+    }
+    out->qk_norm = f->qk_l2norm != 0;
+    out->l2eps = f->l2norm_eps;
+    out->gate = f->gate;
+    out->nw = f->norm_weight;
+    out->neps = f->norm_eps;
+    return GDN2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,9 +127,12 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
                            const void *b, const void *w, const float *S0,
                            const int32_t *cu_seqlens, int32_t chunk_size, void *o, float *S_T,
                            const gdn2_dims *dims, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           const gdn2_fusion *fusion, void *stream) {
     const bool packed = cu_seqlens != nullptr;
     gdn2_status st = check_chunk_dims(dims, chunk_size, packed);
+    if (st != GDN2_OK) return st;
+    gdn2::Fusion fu;
+    st = take_fusion(fusion, o, &fu);
     if (st != GDN2_OK) return st;
     const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
     if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
@@ -130,6 +154,7 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
     a.batch = dims->batch; a.seqlen = dims->seqlen; a.num_seqs = packed ? dims->num_seqs : 0;
     a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
     a.bf16 = bf;
+    a.fu = fu;
     const hipError_t e = gdn2::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, "gdn2_chunk_fwd launch");
     g_last_error[0] = '\0';
@@ -140,9 +165,13 @@ static gdn2_status recurrent_common(const void *q, const void *k, const void *v,
                                     const void *log_alpha, const void *b, const void *w,
                                     void *S, int32_t state_dtype, const int32_t *idx,
                                     int32_t num_slots, void *o, const gdn2_dims *dims,
-                                    void *stream, const char *where) {
+                                    const gdn2_fusion *fusion, void *stream,
+                                    const char *where) {
     if (!dims) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
     gdn2_status st = check_heads(dims);
+    if (st != GDN2_OK) return st;
+    gdn2::Fusion fu;
+    st = take_fusion(fusion, o, &fu);
     if (st != GDN2_OK) return st;
     if (state_dtype != GDN2_STATE_F32 && state_dtype != GDN2_STATE_BF16)
         return fail(GDN2_ERR_UNSUPPORTED, "state_dtype must be GDN2_STATE_F32 or GDN2_STATE_BF16");
@@ -176,6 +205,7 @@ static gdn2_status recurrent_common(const void *q, const void *k, const void *v,
     a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
     a.bf16 = dims->dtype == GDN2_BF16;
     a.state_bf16 = state_dtype == GDN2_STATE_BF16;
+    a.fu = fu;
     const hipError_t e = gdn2::launch_decode(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, where);
     g_last_error[0] = '\0';
@@ -188,7 +218,7 @@ gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
     if (!dims) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
     if (dims->seqlen != 1) return fail(GDN2_ERR_BAD_SHAPE, "recurrent step needs seqlen = 1");
     return recurrent_common(q, k, v, log_alpha, b, w, S, GDN2_STATE_F32, nullptr,
-                            dims->batch < 0 ? 0 : dims->batch, o, dims, stream,
+                            dims->batch < 0 ? 0 : dims->batch, o, dims, nullptr, stream,
                             "gdn2_recurrent_step launch");
 }
 
@@ -196,9 +226,9 @@ gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v,
                                const void *log_alpha, const void *b, const void *w,
                                void *state, int32_t state_dtype, const int32_t *state_idx,
                                int32_t num_slots, void *o, const gdn2_dims *dims,
-                               void *stream) {
+                               const gdn2_fusion *fusion, void *stream) {
     return recurrent_common(q, k, v, log_alpha, b, w, state, state_dtype, state_idx,
-                            num_slots, o, dims, stream, "gdn2_recurrent_fwd launch");
+                            num_slots, o, dims, fusion, stream, "gdn2_recurrent_fwd launch");
 }
 
 gdn2_status gdn2_check_cu_seqlens(const int32_t *cu, int32_t num_seqs, int32_t total_tokens) {

@@ -88,6 +88,8 @@ struct ChunkParams {
     float *seg_R;        // [pair][nseg-2][DK][DV]  end state of segments 1 .. nseg-2 from 0
     int seqlen, num_seqs, h_k, h_v, group, nc_dense, num_pairs, nslices;
     int nseg, seg_len;
+    int qkn;             // nonzero: q and k rows are L2-normalised in K1
+    float l2eps;
 };
 
 // Locates chunk `chunk` of the batch: sequence n, its chunk index j, and token range.
@@ -417,6 +419,27 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             unpack16<BF>(rk[e], kk);
             unpack16<BF>(rq[e], qq);
             unpack16<BF>(rb[e], bb);
+            if (p.qkn) {
+                // L2-norm of the q and k rows: the VK lanes holding row r are consecutive
+                // and aligned, so the row sums are butterflies over them
+                float sk = 0.f, sq = 0.f;
+#pragma unroll
+                for (int s = 0; s < VEC; ++s) {
+                    sk += kk[s] * kk[s];
+                    sq += qq[s] * qq[s];
+                }
+#pragma unroll
+                for (int off = 1; off < VK; off <<= 1) {
+                    sk += __shfl_xor(sk, off);
+                    sq += __shfl_xor(sq, off);
+                }
+                const float fk = rsqrtf(sk + p.l2eps), fq = rsqrtf(sq + p.l2eps);
+#pragma unroll
+                for (int s = 0; s < VEC; ++s) {
+                    kk[s] *= fk;
+                    qq[s] *= fq;
+                }
+            }
 #pragma unroll
             for (int s = 0; s < VEC; ++s) {
                 const float gr = s_g[r * SG + c0 + s], gm = s_g[mid + c0 + s];
@@ -1317,6 +1340,41 @@ size_t chunk_record_bytes(int d_k, int d_v, bool bf16) {
     return (gc + static_cast<size_t>(d_k) * 4 + 255) / 256 * 256;
 }
 
+// ---------------------------------------------------------------------------------------
+// Gated RMS norm of the outputs (burn-gdn2 "Architecture": Gated RMS Norm with a SiLU gate
+// after the recurrence), in place on o after the state pass:
+//     o <- o / sqrt(mean_c o_c^2 + eps) * weight * gate / (1 + exp(-gate))
+// per (token, value head) row of d_v values. The state pass splits d_v over workgroups, so
+// the row norm runs as its own pass: one group of DV/VEC lanes per row, 16-byte accesses.
+// ---------------------------------------------------------------------------------------
+template <typename T, int DV>
+__global__ __launch_bounds__(256) void gated_norm_kernel(T *__restrict__ o,
+                                                         const T *__restrict__ gate,
+                                                         const float *__restrict__ nw, float eps,
+                                                         int64_t rows) {
+    constexpr int VEC = 16 / sizeof(T);    // elements per 16-byte vector
+    constexpr int LPR = DV / VEC;          // lanes per row
+    constexpr int RPB = 256 / LPR;         // rows per block
+    static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row split");
+    const int cl = threadIdx.x % LPR;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR;
+    if (row >= rows) return;               // whole lane groups leave together
+    const size_t off = static_cast<size_t>(row) * DV + cl * VEC;
+    float x[VEC], g[VEC];
+    unpack16<sizeof(T) == 2>(*reinterpret_cast<const u32x4 *>(o + off), x);
+    unpack16<sizeof(T) == 2>(*reinterpret_cast<const u32x4 *>(gate + off), g);
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) ss += x[j] * x[j];
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m);
+    const float scale = rsqrtf(ss * (1.f / DV) + eps);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+        x[j] = x[j] * scale * nw[cl * VEC + j] * (g[j] / (1.f + __expf(-g[j])));
+    *reinterpret_cast<u32x4 *>(o + off) = pack16<sizeof(T) == 2>(x);
+}
+
 int64_t chunk_upper_bound(int batch, int seqlen, int num_seqs, bool packed) {
     const int64_t per = (static_cast<int64_t>(seqlen) + kChunk - 1) / kChunk;
     return packed ? per + num_seqs : per * batch;
@@ -1440,6 +1498,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.group = a.h_v / a.h_k;
     p.nc_dense = (a.seqlen + kChunk - 1) / kChunk;
     p.num_pairs = N * a.h_v;
+    p.qkn = a.fu.qk_norm ? 1 : 0;
+    p.l2eps = a.fu.l2eps;
     const int64_t nrec = chunk_upper_bound(a.batch, a.seqlen, N, packed);
     const SegPlan sp = chunk_seg_plan(packed, p.num_pairs, p.nc_dense, DV, BF);
     p.nseg = sp.nseg;
@@ -1482,14 +1542,23 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     }
     // K2: NW column slices per workgroup (each with a chain and an output wave, plus the
     // copy waves)
+    hipError_t e;
     if constexpr (BF) {
         const int nw = state_slices(DV, BF, p.num_pairs);
-        if (nw == 4) return launch_state<T, BF, DK, DV, 4>(p, units, st);
-        if (nw == 2) return launch_state<T, BF, DK, DV, 2>(p, units, st);
-        return launch_state<T, BF, DK, DV, 1>(p, units, st);
+        if (nw == 4) e = launch_state<T, BF, DK, DV, 4>(p, units, st);
+        else if (nw == 2) e = launch_state<T, BF, DK, DV, 2>(p, units, st);
+        else e = launch_state<T, BF, DK, DV, 1>(p, units, st);
     } else {
-        return launch_state<T, BF, DK, DV, 1>(p, units, st);
+        e = launch_state<T, BF, DK, DV, 1>(p, units, st);
     }
+    if (e != hipSuccess || !a.fu.gate) return e;
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.seqlen * a.h_v;
+    constexpr int RPB = 256 / (DV / (16 / sizeof(T)));
+    if (rows > 0)
+        hipLaunchKernelGGL((gated_norm_kernel<T, DV>), dim3((rows + RPB - 1) / RPB), dim3(256), 0,
+                           st, static_cast<T *>(a.o), static_cast<const T *>(a.fu.gate), a.fu.nw,
+                           a.fu.neps, rows);
+    return hipGetLastError();
 }
 
 template <typename T, bool BF>

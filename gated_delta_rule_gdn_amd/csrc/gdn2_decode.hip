@@ -16,6 +16,10 @@
 // through HBM exactly once per call, whatever T is, and can keep the state in bf16 (half
 // the bytes).
 //
+// Optional fusions (burn-gdn2 "Architecture": L2-Norm before the recurrence, Gated RMS
+// Norm with a SiLU gate after it): q and k divided by their L2 norms, and each output row
+// replaced by o / sqrt(mean o^2 + eps) * weight * silu(gate).
+//
 // State cache: the states live in a pool of slots; sequence n uses slot idx[n] (or n when
 // no index is given). A slot outside [0, num_slots) marks a padding entry: the state is not
 // touched and the sequence's o rows are zero.
@@ -115,12 +119,13 @@ struct Geom {
     static_assert(RPT >= 1 && RG * RPT == DK, "tile shape");
 };
 
-template <typename T, typename ST, int DK, int DV, bool NTS, bool COLW>
+template <typename T, typename ST, int DK, int DV, bool NTS, bool COLW, bool FU>
 __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ b, const T *__restrict__ w,
     ST *__restrict__ S, const int32_t *__restrict__ idx, T *__restrict__ o, int ntok,
-    int num_slots, int h_k, int h_v, int group) {
+    int num_slots, int h_k, int h_v, int group, int qkn, float l2eps,
+    const T *__restrict__ gate, const float *__restrict__ nw, float neps) {
     constexpr int NT = kDecodeThreads, NW = NT / 64;
     constexpr int VN = svec<ST>::N;   // columns per lane (one 16-byte vector)
     using Gm = Geom<DK, DV, VN, COLW>;
@@ -129,12 +134,17 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     // token loop is resolved at compile time.
     constexpr int TB = COLW ? kTokBlock : 1;
     const int nt = COLW ? ntok : 1;
+    // the fusions are compiled only into the FU instantiations
+    const bool do_qkn = FU && qkn != 0;
+    const bool do_gate = FU && gate != nullptr;
 
     // staged token vectors: (decay, b.k, q, k) per key-axis row, and w.v per column
     __shared__ f32x4 s_tok[TB][DK];
     __shared__ float s_wv[TB][DV];
-    // per-wave partial sums (row split only)
+    // per-wave partial sums (row split only): y, z, then k.q, |q|^2, |k|^2
     __shared__ float s_red[COLW ? 1 : NW][COLW ? 1 : 2 * DV + 4];
+    // outputs of the block's tokens, for the gated norm over d_v
+    __shared__ float s_o[TB][DV];
 
     const int pair = blockIdx.x;
     const int n = pair / h_v;
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
             float y[VN], z[VN];
 #pragma unroll
             for (int j = 0; j < VN; ++j) y[j] = z[j] = 0.f;
-            float kq = 0.f;
+            float kq = 0.f, qsq = 0.f, ksq = 0.f;
             float kr[COLW ? 1 : RPT];             // the row split keeps k in registers
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
@@ -199,6 +209,8 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                     z[j] += g.z * s[i][j];
                 }
                 kq += g.w * g.z;
+                qsq += g.z * g.z;
+                ksq += g.w * g.w;
             }
             // sum over the row groups of this wave (lanes that share lane % CG)
 #pragma unroll
@@ -207,6 +219,10 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                 z[j] = lane_group_sum<CG>(z[j]);
             }
             kq = lane_group_sum<CG>(kq);
+            if (do_qkn) {
+                qsq = lane_group_sum<CG>(qsq);
+                ksq = lane_group_sum<CG>(ksq);
+            }
             if constexpr (!COLW) {
                 // and over the waves, through LDS (one token per call: one barrier)
                 if (lane < CG) {
@@ -217,12 +233,16 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                         *reinterpret_cast<f32x4 *>(&s_red[wave][DV + c0 + j]) =
                             f32x4{z[j], z[j + 1], z[j + 2], z[j + 3]};
                     }
-                    if (lane == 0) s_red[wave][2 * DV] = kq;
+                    if (lane == 0) {
+                        s_red[wave][2 * DV] = kq;
+                        s_red[wave][2 * DV + 1] = qsq;
+                        s_red[wave][2 * DV + 2] = ksq;
+                    }
                 }
                 __syncthreads();
 #pragma unroll
                 for (int j = 0; j < VN; ++j) y[j] = z[j] = 0.f;
-                kq = 0.f;
+                kq = qsq = ksq = 0.f;
 #pragma unroll
                 for (int wv = 0; wv < NW; ++wv) {
 #pragma unroll
@@ -233,25 +253,68 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                         z[j] += zz.x; z[j + 1] += zz.y; z[j + 2] += zz.z; z[j + 3] += zz.w;
                     }
                     kq += s_red[wv][2 * DV];
+                    qsq += s_red[wv][2 * DV + 1];
+                    ksq += s_red[wv][2 * DV + 2];
                 }
+            }
+            // q/k L2-norm: the products are linear in q and in k, so the raw vectors are
+            // used and the sums scaled: y by 1/|k|, z by 1/|q|, k.q by both, k u^T by 1/|k|
+            float nk = 1.f;
+            if (do_qkn) {
+                const float nq = rsqrtf(qsq + l2eps);
+                nk = rsqrtf(ksq + l2eps);
+#pragma unroll
+                for (int j = 0; j < VN; ++j) {
+                    y[j] *= nk;
+                    z[j] *= nq;
+                }
+                kq *= nq * nk;
             }
             float u[VN];
 #pragma unroll
             for (int j = 0; j < VN; ++j) u[j] = s_wv[tt][c0 + j] - y[j];
             if (rg == 0) {
-                T *op = o + ((static_cast<size_t>(n) * nt + t0 + tt) * h_v + h) * DV + c0;
+                if (do_gate) {
 #pragma unroll
-                for (int j = 0; j < VN; j += 4)
-                    io<T>::st4(op + j, f32x4{z[j] + kq * u[j], z[j + 1] + kq * u[j + 1],
-                                             z[j + 2] + kq * u[j + 2], z[j + 3] + kq * u[j + 3]});
+                    for (int j = 0; j < VN; ++j) s_o[tt][c0 + j] = z[j] + kq * u[j];
+                } else {
+                    T *op = o + ((static_cast<size_t>(n) * nt + t0 + tt) * h_v + h) * DV + c0;
+#pragma unroll
+                    for (int j = 0; j < VN; j += 4)
+                        io<T>::st4(op + j, f32x4{z[j] + kq * u[j], z[j + 1] + kq * u[j + 1],
+                                                 z[j + 2] + kq * u[j + 2],
+                                                 z[j + 3] + kq * u[j + 3]});
+                }
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 float kk;
-                if constexpr (COLW) kk = s_tok[tt][rg + RG * i].w;
-                else kk = kr[i];
+                if constexpr (COLW) kk = s_tok[tt][rg + RG * i].w * nk;
+                else kk = kr[i] * nk;
 #pragma unroll
                 for (int j = 0; j < VN; ++j) s[i][j] += kk * u[j];
+            }
+        }
+        if (do_gate) {
+            // gated RMS norm of each output row over d_v, one wave per token
+            __syncthreads();
+            constexpr int PL = DV / 64;           // values per lane
+            for (int tt = wave; tt < nb; tt += NW) {
+                float ov[PL], ss = 0.f;
+#pragma unroll
+                for (int j = 0; j < PL; ++j) {
+                    ov[j] = s_o[tt][lane * PL + j];
+                    ss += ov[j] * ov[j];
+                }
+                ss = lane_group_sum<1>(ss);
+                const float scale = rsqrtf(ss * (1.f / DV) + neps);
+                const size_t row = ((static_cast<size_t>(n) * nt + t0 + tt) * h_v + h) * DV;
+#pragma unroll
+                for (int j = 0; j < PL; ++j) {
+                    const int c = lane * PL + j;
+                    const float gv = io<T>::ld(gate + row + c);
+                    io<T>::st(o + row + c, ov[j] * scale * nw[c] * (gv / (1.f + __expf(-gv))));
+                }
             }
         }
     }
@@ -260,22 +323,29 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
         svec<ST>::template st<NTS>(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
 }
 
-template <typename T, typename ST, int DK, int DV>
-static hipError_t launch_recurrent_t(const DecodeArgs &a, hipStream_t st) {
+template <typename T, typename ST, int DK, int DV, bool FU>
+static hipError_t launch_recurrent_f(const DecodeArgs &a, hipStream_t st) {
     const int pairs = a.num_seqs * a.h_v;
     const size_t state_bytes = static_cast<size_t>(pairs) * DK * DV * sizeof(ST);
     const bool nts = state_bytes > kStreamStateBytes, colw = a.ntok > 1;
-    auto kern = colw ? (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, true>
-                            : recurrent_fwd_kernel<T, ST, DK, DV, false, true>)
-                     : (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, false>
-                            : recurrent_fwd_kernel<T, ST, DK, DV, false, false>);
+    auto kern = colw ? (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, true, FU>
+                            : recurrent_fwd_kernel<T, ST, DK, DV, false, true, FU>)
+                     : (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, false, FU>
+                            : recurrent_fwd_kernel<T, ST, DK, DV, false, false, FU>);
     hipLaunchKernelGGL(kern, dim3(pairs), dim3(kDecodeThreads), 0, st,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<const T *>(a.log_alpha),
                        static_cast<const T *>(a.b), static_cast<const T *>(a.w),
                        static_cast<ST *>(a.S), a.idx, static_cast<T *>(a.o), a.ntok,
-                       a.num_slots, a.h_k, a.h_v, a.h_v / a.h_k);
+                       a.num_slots, a.h_k, a.h_v, a.h_v / a.h_k, a.fu.qk_norm ? 1 : 0,
+                       a.fu.l2eps, static_cast<const T *>(a.fu.gate), a.fu.nw, a.fu.neps);
     return hipGetLastError();
+}
+
+template <typename T, typename ST, int DK, int DV>
+static hipError_t launch_recurrent_t(const DecodeArgs &a, hipStream_t st) {
+    if (a.fu.qk_norm || a.fu.gate) return launch_recurrent_f<T, ST, DK, DV, true>(a, st);
+    return launch_recurrent_f<T, ST, DK, DV, false>(a, st);
 }
 
 template <typename T, typename ST>

@@ -8,6 +8,15 @@ namespace gdn2 {
 
 constexpr int kChunk = 64;   // chunk size of the chunked forward
 
+// Optional fusions (gdn2_fusion): q/k L2-norm before the recurrence, gated RMS norm after.
+struct Fusion {
+    bool qk_norm = false;
+    float l2eps = 0.f;
+    const void *gate = nullptr;      // [.., h_v, d_v] input dtype, or NULL
+    const float *nw = nullptr;       // [d_v] fp32
+    float neps = 0.f;
+};
+
 struct DecodeArgs {
     const void *q, *k, *v, *log_alpha, *b, *w;
     void *S;                 // state pool [num_slots][h_v][d_k][d_v], fp32 or bf16
@@ -16,6 +25,7 @@ struct DecodeArgs {
     int num_seqs, ntok, num_slots, h_k, h_v, d_k, d_v;
     bool bf16;               // input dtype
     bool state_bf16;         // state dtype
+    Fusion fu;
 };
 
 struct ChunkArgs {
@@ -27,6 +37,7 @@ struct ChunkArgs {
     char *workspace;
     int batch, seqlen, num_seqs, h_k, h_v, d_k, d_v;
     bool bf16;
+    Fusion fu;
 };
 
 // Workspace layout of the chunked forward (all offsets 256-byte aligned):

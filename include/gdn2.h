@@ -80,6 +80,28 @@ typedef enum gdn2_state_dtype {
                                    a call, rounded to nearest even when written back */
 } gdn2_state_dtype;
 
+/*
+ * Optional fusions of the stages the burn-gdn2 page (section "Architecture") draws around
+ * the recurrence: the L2-Norm of q and k before it, and the Gated RMS Norm with a SiLU
+ * gate after it (its Configuration table gives norm_eps = 1e-5). Pass NULL for none.
+ *
+ *   qk_l2norm    nonzero: every q and k vector (one token of one key head, d_k values) is
+ *                replaced by x / sqrt(sum_c x_c^2 + l2norm_eps) before it is used
+ *   l2norm_eps   >= 0 (1e-6 is a usual choice; with 0 an all-zero vector gives NaN)
+ *   gate         NULL, or a device tensor shaped like o ([.., h_v, d_v], input dtype): the
+ *                output becomes  o / sqrt(mean_c o_c^2 + norm_eps) * norm_weight * silu(gate)
+ *                per (token, value head), silu(g) = g / (1 + exp(-g)); must not alias o
+ *   norm_weight  device fp32 [d_v], required with a gate (shared by all value heads)
+ *   norm_eps     >= 0
+ */
+typedef struct gdn2_fusion {
+    int32_t qk_l2norm;
+    float l2norm_eps;
+    const void *gate;
+    const float *norm_weight;
+    float norm_eps;
+} gdn2_fusion;
+
 typedef struct gdn2_dims {
     int32_t batch;      /* dense: number of sequences B. packed: must be 1.
                            recurrent step: number of sequences N. */
@@ -126,6 +148,8 @@ size_t gdn2_chunk_fwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
  *               be the same buffer as S0 (in-place continuation); no other aliasing.
  *   workspace   device buffer of at least gdn2_chunk_fwd_workspace_bytes() bytes, 256-byte
  *               aligned; its contents on entry are ignored and are clobbered.
+ *   fusion      NULL, or the optional q/k L2-norm and gated output norm (gdn2_fusion);
+ *               the gate is [B, T, h_v, d_v]
  *   stream      hipStream_t the work is enqueued on
  * Returns GDN2_OK or an error status (nothing is enqueued on a validation error).
  */
@@ -133,7 +157,8 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                            const void *log_alpha, const void *b, const void *w,
                            const float *S0, const int32_t *cu_seqlens, int32_t chunk_size,
                            void *o, float *S_T, const gdn2_dims *dims,
-                           void *workspace, size_t workspace_bytes, void *stream);
+                           void *workspace, size_t workspace_bytes,
+                           const gdn2_fusion *fusion, void *stream);
 
 /*
  * One decode step for N sequences, one token each (burn-gdn2 "FusedRecurrent" mode; the
@@ -176,6 +201,8 @@ gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
  *                 distinct; two sequences on one slot race.
  *   o             device [N, T, h_v, d_v] in the input dtype; must not alias an input or
  *                 the state
+ *   fusion        NULL, or the optional q/k L2-norm and gated output norm (gdn2_fusion);
+ *                 the gate is [N, T, h_v, d_v]. Padding sequences still get zero o rows.
  *   stream        hipStream_t
  * With T = 1, state_idx = NULL and an fp32 state this is gdn2_recurrent_step.
  */
@@ -183,7 +210,7 @@ gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v,
                                const void *log_alpha, const void *b, const void *w,
                                void *state, int32_t state_dtype, const int32_t *state_idx,
                                int32_t num_slots, void *o, const gdn2_dims *dims,
-                               void *stream);
+                               const gdn2_fusion *fusion, void *stream);
 
 /*
  * Host helper: checks a HOST copy of cu_seqlens (N+1 entries) against total tokens T.

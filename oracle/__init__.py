@@ -13,6 +13,9 @@ Two independent evaluations of the method live here:
   ``recurrent_cache`` runs it over a pool of stored states (the recurrent cache of the
   llama.cpp decode notes, LocalAI mirror, section 2), optionally stored in bfloat16
   (section 4 of the same notes), with ``round_to_bf16`` the rounding of the stored state.
+* ``l2_normalize`` and ``gated_rms_norm`` -- the stages the burn-gdn2 "Architecture"
+  diagram draws around the recurrence (L2-Norm of q and k before it, Gated RMS Norm
+  with a SiLU gate after it), in numpy fp64.
 * ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
   mode) and on the FG^2-GDN summary (section 2C, DPLR structure and the WY
   representation), in numpy fp64. It exists to pin the recurrence: the two are
@@ -201,6 +204,27 @@ def recurrent_cache(q, k, v, log_alpha, b, w, state, state_idx=None, bf16_state=
     o[live] = o_l.reshape(len(live), T, *o_l.shape[1:])
     pool[idx[live]] = round_to_bf16(S_l) if bf16_state else S_l
     return o, pool
+
+
+def l2_normalize(x, eps):
+    """Each vector along the last axis divided by sqrt(sum of its squares + eps).
+
+    The L2-Norm stage that the burn-gdn2 page (section "Architecture") places on q and k
+    before the recurrence; the epsilon is this build's reading (the page names none).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gated_rms_norm(o, gate, weight, eps):
+    """The Gated RMS Norm with a SiLU gate after the recurrence (burn-gdn2 "Architecture";
+    norm_eps in its Configuration table), per vector along the last axis:
+        o / sqrt(mean(o^2) + eps) * weight * silu(gate),   silu(g) = g / (1 + exp(-g)).
+    """
+    o = np.asarray(o, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o / rms * np.asarray(weight, dtype=np.float64) * (g / (1.0 + np.exp(-g)))
 
 
 def _unit_lower_inverse(L: np.ndarray) -> np.ndarray:

@@ -53,10 +53,12 @@ def test_version_and_status_strings(L):
     assert L.gdn2_status_string(99) == b"unknown status"
 
 
-def chunk(L, dims, chunk_size=64, ws=FAKE, ws_bytes=1 << 40, cu=None, o=FAKE, q=FAKE):
+def chunk(L, dims, chunk_size=64, ws=FAKE, ws_bytes=1 << 40, cu=None, o=FAKE, q=FAKE,
+          fusion=None):
     # o defaults to the q pointer: a call that passed every other check is still rejected
     return L.gdn2_chunk_fwd(q, FAKE, FAKE, FAKE, FAKE, FAKE, None, cu, chunk_size, o, None,
-                            None if dims is None else ctypes.byref(dims), ws, ws_bytes, None)
+                            None if dims is None else ctypes.byref(dims), ws, ws_bytes, fusion,
+                            None)
 
 
 def test_chunk_fwd_rejects_bad_arguments(L):
@@ -105,11 +107,36 @@ def test_recurrent_step_rejects_bad_arguments(L):
     assert step(L, Dims(**{**ok, "batch": 0})) == 0       # empty batch: nothing to do
 
 
-def fwd(L, dims, state_dtype=0, idx=None, num_slots=8, S=FAKE, o=None):
+def fwd(L, dims, state_dtype=0, idx=None, num_slots=8, S=FAKE, o=None, fusion=None):
     # o defaults to the q pointer: a call that passed every other check is still rejected
     return L.gdn2_recurrent_fwd(FAKE, ctypes.c_void_p(0x3000), FAKE, FAKE, FAKE, FAKE, S,
                                 state_dtype, idx, num_slots, FAKE if o is None else o,
-                                None if dims is None else ctypes.byref(dims), None)
+                                None if dims is None else ctypes.byref(dims),
+                                None if fusion is None else ctypes.byref(fusion), None)
+
+
+def test_fusion_options_are_validated(L):
+    from gated_delta_rule_gdn_amd import Fusion
+    okc = Dims(2, 100, 0, 2, 4, 128, 128, 1)
+    okr = Dims(4, 3, 0, 2, 6, 128, 64, 1)
+    W = ctypes.c_void_p(0x7000)
+    bad = [(Fusion(1, -1.0, None, None, 0.0), 2),            # negative L2-norm epsilon
+           (Fusion(1, float("nan"), None, None, 0.0), 2),
+           (Fusion(0, 0.0, ctypes.c_void_p(0x6000), None, 1e-5), 1),   # gate without weight
+           (Fusion(0, 0.0, ctypes.c_void_p(0x6000), W, -1.0), 2),      # negative norm epsilon
+           (Fusion(0, 0.0, ctypes.c_void_p(0x6000), W, float("inf")), 2)]
+    for f, want in bad:
+        assert chunk(L, okc, fusion=f) == want
+        assert fwd(L, okr, fusion=f) == want
+    # a gate aliasing o
+    assert chunk(L, okc, o=ctypes.c_void_p(0x6000), q=ctypes.c_void_p(0x4000),
+                 fusion=Fusion(0, 0.0, ctypes.c_void_p(0x6000), W, 1e-5)) == 2
+    assert fwd(L, okr, o=ctypes.c_void_p(0x6000),
+               fusion=Fusion(0, 0.0, ctypes.c_void_p(0x6000), W, 1e-5)) == 2
+    # valid options pass the fusion checks and are rejected later (o aliases q)
+    good = Fusion(1, 1e-6, ctypes.c_void_p(0x6000), W, 1e-5)
+    assert chunk(L, okc, fusion=good) == 2
+    assert fwd(L, okr, fusion=good) == 2
 
 
 def test_recurrent_fwd_rejects_bad_arguments(L):

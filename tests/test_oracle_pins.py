@@ -382,3 +382,36 @@ def test_cache_bf16_pool_rounds_only_the_stored_state():
     assert np.array_equal(new16[N:], pool[N:])
     rel = np.abs(new16[:N] - new32[:N]) / np.maximum(np.abs(new32[:N]), 1e-30)
     assert np.max(rel) <= 2.0 ** -8            # half a unit in the last place of 8 bits
+
+
+# ---- the stages around the recurrence (burn-gdn2 "Architecture": L2-Norm before it, Gated
+# RMS Norm with a SiLU gate after it) --------------------------------------------------------
+
+def test_l2_normalize_closed_forms():
+    assert np.allclose(oracle.l2_normalize([3.0, 4.0], 0.0), [0.6, 0.8], rtol=0, atol=1e-15)
+    assert np.allclose(oracle.l2_normalize([3.0, 4.0], 11.0), [0.5, 4.0 / 6.0], rtol=0,
+                       atol=1e-15)                       # sqrt(25 + 11) = 6
+    x = np.random.default_rng(21).standard_normal((50, 7))
+    n = oracle.l2_normalize(x, 0.0)
+    assert np.allclose(np.linalg.norm(n, axis=-1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(oracle.l2_normalize(5.5 * x, 0.0), n, rtol=0, atol=1e-14)
+    assert np.all(oracle.l2_normalize(np.zeros(4), 1e-6) == 0.0)
+
+
+def test_gated_rms_norm_closed_forms():
+    ln3 = np.log(3.0)                                    # sigmoid(ln 3) = 3/4
+    out = oracle.gated_rms_norm([2.0, -2.0], [0.0, ln3], [5.0, 7.0], 0.0)
+    assert np.allclose(out, [0.0, -7.0 * 0.75 * ln3], rtol=0, atol=1e-14)
+    # mean square 4 + eps 5 -> rms 3
+    out = oracle.gated_rms_norm([2.0, 2.0, 2.0, 2.0], [ln3] * 4, [1.0, 2.0, 3.0, 4.0], 5.0)
+    assert np.allclose(out, np.array([1.0, 2.0, 3.0, 4.0]) * (2.0 / 3.0) * 0.75 * ln3,
+                       rtol=0, atol=1e-14)
+    # with eps = 0 the output divided by weight * silu(gate) has unit root-mean-square
+    rng = np.random.default_rng(22)
+    o, g = rng.standard_normal((40, 9)), rng.standard_normal((40, 9))
+    w = rng.uniform(0.5, 2.0, 9)
+    r = oracle.gated_rms_norm(o, g, w, 0.0) / (w * g / (1.0 + np.exp(-g)))
+    assert np.allclose(np.sqrt(np.mean(r * r, axis=-1)), 1.0, rtol=0, atol=1e-12)
+    # and it is invariant to a positive scale of o
+    assert np.allclose(oracle.gated_rms_norm(3.0 * o, g, w, 0.0),
+                       oracle.gated_rms_norm(o, g, w, 0.0), rtol=0, atol=1e-13)
