@@ -287,16 +287,32 @@ def bench_fused(steps, warmup, seed=8):
                                 norm_weight=dnw if fused else None)
         return fn
 
+    C = 2 * dw.h_k * dw.d_k + dw.h_v * dw.d_v
+    cw = torch.randn(C, 4, generator=gen, device="cuda") * 0.5
+    cst = torch.randn(dw.num_seqs, 3, C, generator=gen, device="cuda")
+
+    def ccall():
+        for t in range(steps_d):
+            g.recurrent_fwd(yy["q"][t], yy["k"][t], yy["v"][t], yy["log_alpha"][t], yy["b"][t],
+                            yy["w"][t], y["S"], out=od, qk_l2norm=True, gate=dgate[t],
+                            norm_weight=dnw, conv_weight=cw, conv_state=cst, conv_silu=True)
+
     for fused in (False, True):
         dcall(fused)()
+    ccall()
     t_plain = time_region(dcall(False), 1, stream) / steps_d
     t_fused = time_region(dcall(True), 1, stream) / steps_d
+    t_conv = time_region(ccall, 1, stream) / steps_d
     dbytes, _, _ = decode_alg(dw)
     dbytes += dw.num_seqs * dw.h_v * dw.d_v * 4
+    cbytes = dbytes + 2 * dw.num_seqs * 3 * C * 4 + C * 4 * 4   # conv state in and out, taps
     res["decode"] = {"workload": dw.name + "_qkl2norm_gatednorm", "us_per_step": t_fused * 1e6,
                      "us_per_step_unfused": t_plain * 1e6, "alg_bytes": dbytes,
                      "hbm_frac": dbytes / t_fused / 1e9 / HBM_PEAK_GBPS}
-    del y, yy, dgate, od
+    res["decode_conv"] = {"workload": dw.name + "_shortconv_qkl2norm_gatednorm",
+                          "us_per_step": t_conv * 1e6, "alg_bytes": cbytes,
+                          "hbm_frac": cbytes / t_conv / 1e9 / HBM_PEAK_GBPS}
+    del y, yy, dgate, od, cst
     torch.cuda.empty_cache()
     return res
 

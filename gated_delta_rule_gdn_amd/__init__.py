@@ -43,7 +43,8 @@ class Dims(ctypes.Structure):
 class Fusion(ctypes.Structure):
     _fields_ = [("qk_l2norm", ctypes.c_int32), ("l2norm_eps", ctypes.c_float),
                 ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("conv_weight", ctypes.c_void_p),
+                ("conv_state", ctypes.c_void_p), ("conv_silu", ctypes.c_int32)]
 
 
 class GDN2Error(RuntimeError):
@@ -113,10 +114,22 @@ def _need_gpu(name: str, t: torch.Tensor, device) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight, norm_eps):
-    """The gdn2_fusion argument (None when nothing is fused)."""
-    if not qk_l2norm and gate is None:
+def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight, norm_eps,
+            conv=None):
+    """The gdn2_fusion argument (None when nothing is fused). ``conv`` is
+    (conv_weight, conv_state, conv_silu, channels, num_slots) or None."""
+    if not qk_l2norm and gate is None and conv is None:
         return None
+    cw = cs = None
+    silu = 0
+    if conv is not None:
+        cw, cs, silu, C, slots = conv
+        _need_gpu("conv_weight", cw, dev)
+        _need_gpu("conv_state", cs, dev)
+        if cw.dtype != torch.float32 or tuple(cw.shape) != (C, 4):
+            raise ValueError(f"conv_weight must be fp32 [{C},4]")
+        if cs.dtype != torch.float32 or tuple(cs.shape) != (slots, 3, C):
+            raise ValueError(f"conv_state must be fp32 [{slots},3,{C}]")
     if gate is not None:
         _need_gpu("gate", gate, dev)
         if gate.dtype != out_dtype or tuple(gate.shape) != tuple(out_shape):
@@ -126,7 +139,8 @@ def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
         _need_gpu("norm_weight", norm_weight, dev)
         if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (out_shape[-1],):
             raise ValueError(f"norm_weight must be fp32 [{out_shape[-1]}]")
-    return Fusion(1 if qk_l2norm else 0, l2norm_eps, _ptr(gate), _ptr(norm_weight), norm_eps)
+    return Fusion(1 if qk_l2norm else 0, l2norm_eps, _ptr(gate), _ptr(norm_weight), norm_eps,
+                  _ptr(cw), _ptr(cs), 1 if silu else 0)
 
 
 def chunk_fwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: int, d_v: int,
@@ -223,7 +237,9 @@ def recurrent_step(q, k, v, log_alpha, b, w, S, out: Optional[torch.Tensor] = No
 def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Tensor] = None,
                   out: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
                   l2norm_eps: float = 1e-6, gate: Optional[torch.Tensor] = None,
-                  norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5
+                  norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5,
+                  conv_weight: Optional[torch.Tensor] = None,
+                  conv_state: Optional[torch.Tensor] = None, conv_silu: bool = False
                   ) -> torch.Tensor:
     """T tokens per sequence against a pool of recurrent states, updated in place.
 
@@ -231,6 +247,9 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
     state [num_slots,H_v,d_k,d_v] fp32 or bf16; state_idx int32 [N] (slot of each sequence,
     None: slot n; out-of-range entries are padding: zero o rows, no state change).
     Returns o [N,T,H_v,d_v] in the input dtype. qk_l2norm, gate, norm_weight: as in chunk_fwd.
+    conv_weight fp32 [C,4] with conv_state fp32 [num_slots,3,C], C = 2 H_k d_k + H_v d_v:
+    the short causal convolution of q, k, v (channel order q, k, v), its state updated in
+    place; conv_silu applies SiLU after it.
     """
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
@@ -260,8 +279,13 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
             raise ValueError(f"state_idx must be int32 [{N}]")
     dims = Dims(N, T, 0, Hk, Hv, dk, dv, _dtype_code(q.dtype))
     o = out if out is not None else torch.empty(N, T, Hv, dv, dtype=q.dtype, device=dev)
+    conv = None
+    if conv_weight is not None or conv_state is not None:
+        if conv_weight is None or conv_state is None:
+            raise ValueError("conv_weight and conv_state go together")
+        conv = (conv_weight, conv_state, conv_silu, 2 * Hk * dk + Hv * dv, state.shape[0])
     fu = _fusion(dev, (N, T, Hv, dv), q.dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
-                 norm_eps)
+                 norm_eps, conv)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib().gdn2_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                   _ptr(state), sdt, _ptr(state_idx), state.shape[0], _ptr(o),

@@ -52,7 +52,14 @@ gdn2_status take_fusion(const gdn2_fusion *f, const void *o, gdn2::Fusion *out) 
         if (!eps_ok(f->norm_eps)) return fail(GDN2_ERR_BAD_SHAPE, "norm_eps must be finite and >= 0");
         if (f->gate == o) return fail(GDN2_ERR_BAD_SHAPE, "the gate must not alias o");
     }
+    if (f->conv_weight && !f->conv_state)
+        return fail(GDN2_ERR_NULL_ARG, "a short convolution needs conv_state");
+    if (f->conv_weight && (f->conv_state == o || static_cast<const void *>(f->conv_weight) == o))
+        return fail(GDN2_ERR_BAD_SHAPE, "the convolution buffers must not alias o");
     out->qk_norm = f->qk_l2norm != 0;
+    out->cw = f->conv_weight;
+    out->cst = f->conv_state;
+    out->csilu = f->conv_silu != 0;
     out->l2eps = f->l2norm_eps;
     out->gate = f->gate;
     out->nw = f->norm_weight;
@@ -134,6 +141,8 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
     gdn2::Fusion fu;
     st = take_fusion(fusion, o, &fu);
     if (st != GDN2_OK) return st;
+    if (fu.cw)
+        return fail(GDN2_ERR_UNSUPPORTED, "the short convolution is built for gdn2_recurrent_fwd only");
     const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
     if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
         return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w and o are required");

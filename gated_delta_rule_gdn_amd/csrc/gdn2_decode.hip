@@ -16,9 +16,11 @@
 // through HBM exactly once per call, whatever T is, and can keep the state in bf16 (half
 // the bytes).
 //
-// Optional fusions (burn-gdn2 "Architecture": L2-Norm before the recurrence, Gated RMS
-// Norm with a SiLU gate after it): q and k divided by their L2 norms, and each output row
-// replaced by o / sqrt(mean o^2 + eps) * weight * silu(gate).
+// Optional fusions (burn-gdn2 "Architecture": ShortConv and L2-Norm before the recurrence,
+// Gated RMS Norm with a SiLU gate after it): a causal depthwise convolution of width 4 over
+// q, k and v with its three-input state in the cache (llama.cpp decode notes, sections 1
+// and 2), q and k divided by their L2 norms, and each output row replaced by
+// o / sqrt(mean o^2 + eps) * weight * silu(gate).
 //
 // State cache: the states live in a pool of slots; sequence n uses slot idx[n] (or n when
 // no index is given). A slot outside [0, num_slots) marks a padding entry: the state is not
@@ -119,13 +121,19 @@ struct Geom {
     static_assert(RPT >= 1 && RG * RPT == DK, "tile shape");
 };
 
-template <typename T, typename ST, int DK, int DV, bool NTS, bool COLW, bool FU>
+// CV: with the short causal convolution of q, k and v. Every workgroup convolves its q and
+// k (those of its key head) from the conv state, which it only reads there: the G value
+// heads of a key head all need the old q/k state, so conv_qk_state_kernel rewrites it
+// after this kernel. The v channels belong to one value head, so the workgroup rewrites
+// their state itself.
+template <typename T, typename ST, int DK, int DV, bool NTS, bool COLW, bool FU, bool CV>
 __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const T *__restrict__ log_alpha, const T *__restrict__ b, const T *__restrict__ w,
     ST *__restrict__ S, const int32_t *__restrict__ idx, T *__restrict__ o, int ntok,
     int num_slots, int h_k, int h_v, int group, int qkn, float l2eps,
-    const T *__restrict__ gate, const float *__restrict__ nw, float neps) {
+    const T *__restrict__ gate, const float *__restrict__ nw, float neps,
+    const float *__restrict__ cw, float *__restrict__ cst, int csilu) {
     constexpr int NT = kDecodeThreads, NW = NT / 64;
     constexpr int VN = svec<ST>::N;   // columns per lane (one 16-byte vector)
     using Gm = Geom<DK, DV, VN, COLW>;
@@ -165,6 +173,42 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
         return;
     }
 
+    // short convolution: channel ch at token tg of this call; raw(t') reads the call's own
+    // inputs, earlier tokens come from the conv state (the last three inputs, oldest first)
+    const int C = 2 * h_k * DK + h_v * DV;
+    float *cs = CV ? cst + static_cast<size_t>(slot) * 3 * C : nullptr;
+    // (Both candidate inputs of a tap are loaded and one is selected, so that all loads of a
+    // channel issue together instead of one round trip per tap.)
+    auto conv_at = [&](int ch, int tg, auto raw) -> float {
+        const f32x4 wt = *reinterpret_cast<const f32x4 *>(cw + static_cast<size_t>(ch) * 4);
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tp = tg - 3 + j;
+            const float a = raw(tp < 0 ? 0 : tp);
+            const float b = cs[(tp < 0 ? 3 + tp : 0) * C + ch];
+            x[j] = tp >= 0 ? a : b;
+        }
+        const float acc = wt.x * x[0] + wt.y * x[1] + wt.z * x[2] + wt.w * x[3];
+        return csilu ? acc / (1.f + __expf(-acc)) : acc;
+    };
+
+    // new conv state of this head's v channels (their last three inputs), loaded now and
+    // stored once the first block's staging has read the old state
+    float cv_new[CV ? 3 : 1];
+    if constexpr (CV) {
+        if (tid < DV) {
+            const int ch = 2 * h_k * DK + h * DV + tid;
+#pragma unroll
+            for (int e = 0; e < 3; ++e) {
+                const int tp = nt - 3 + e;
+                const float a = io<T>::ld(v + ((static_cast<size_t>(n) * nt + (tp < 0 ? 0 : tp)) * h_v + h) * DV + tid);
+                const float b = cs[(tp < 0 ? 3 + tp : 0) * C + ch];
+                cv_new[e] = tp >= 0 ? a : b;
+            }
+        }
+    }
+
     ST *Sp = S + (static_cast<size_t>(slot) * h_v + h) * DK * DV;
     float s[RPT][VN];
 #pragma unroll
@@ -181,16 +225,41 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                 const size_t tok = static_cast<size_t>(n) * nt + t0 + tt;
                 const size_t kq_off = (tok * h_k + hk) * DK + r;
                 const size_t g_off = (tok * h_v + h) * DK + r;
-                const float kk = io<T>::ld(k + kq_off);
+                float kk, qq;
+                if constexpr (CV) {
+                    const size_t base = static_cast<size_t>(n) * nt;
+                    kk = conv_at(h_k * DK + hk * DK + r, t0 + tt, [&](int tp) {
+                        return io<T>::ld(k + ((base + tp) * h_k + hk) * DK + r); });
+                    qq = conv_at(hk * DK + r, t0 + tt, [&](int tp) {
+                        return io<T>::ld(q + ((base + tp) * h_k + hk) * DK + r); });
+                } else {
+                    kk = io<T>::ld(k + kq_off);
+                    qq = io<T>::ld(q + kq_off);
+                }
                 s_tok[tt][r] = f32x4{__expf(io<T>::ld(log_alpha + g_off)),
-                                     io<T>::ld(b + g_off) * kk, io<T>::ld(q + kq_off), kk};
+                                     io<T>::ld(b + g_off) * kk, qq, kk};
             } else {
                 const int iv = i - nb * DK, tt = iv / DV, c = iv - tt * DV;
                 const size_t off = ((static_cast<size_t>(n) * nt + t0 + tt) * h_v + h) * DV + c;
-                s_wv[tt][c] = io<T>::ld(w + off) * io<T>::ld(v + off);
+                float vv;
+                if constexpr (CV) {
+                    const size_t base = static_cast<size_t>(n) * nt;
+                    vv = conv_at(2 * h_k * DK + h * DV + c, t0 + tt, [&](int tp) {
+                        return io<T>::ld(v + ((base + tp) * h_v + h) * DV + c); });
+                } else {
+                    vv = io<T>::ld(v + off);
+                }
+                s_wv[tt][c] = io<T>::ld(w + off) * vv;
             }
         }
         __syncthreads();
+        if constexpr (CV) {
+            // the old state is read only by the first three tokens, all in the first block
+            if (t0 == 0 && tid < DV) {
+#pragma unroll
+                for (int e = 0; e < 3; ++e) cs[e * C + 2 * h_k * DK + h * DV + tid] = cv_new[e];
+            }
+        }
 
         for (int tt = 0; tt < nb; ++tt) {
             float y[VN], z[VN];
@@ -321,31 +390,69 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         svec<ST>::template st<NTS>(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
+
 }
 
-template <typename T, typename ST, int DK, int DV, bool FU>
+// The new conv state of the q and k channels, after recurrent_fwd_kernel has convolved them
+// from the old one: the last three inputs of each channel (older state entries shift down
+// when the call had fewer than three tokens). One thread per channel of one sequence.
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void conv_qk_state_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const int32_t *__restrict__ idx,
+    float *__restrict__ cst, int num_seqs, int ntok, int num_slots, int h_k, int C) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int per = 2 * h_k * DK;                 // q and k channels of one sequence
+    if (i >= static_cast<int64_t>(num_seqs) * per) return;
+    const int n = static_cast<int>(i / per), ch = static_cast<int>(i % per);
+    const int slot = idx ? idx[n] : n;
+    if (slot < 0 || slot >= num_slots) return;
+    const T *src = ch < h_k * DK ? q : k;
+    const int r = ch % (h_k * DK);                // key head * DK + row
+    float *cs = cst + static_cast<size_t>(slot) * 3 * C;
+    float nv[3];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {            // both candidates loaded: one round trip
+        const int tp = ntok - 3 + e;
+        const float a = io<T>::ld(src + (static_cast<size_t>(n) * ntok + (tp < 0 ? 0 : tp)) * h_k * DK + r);
+        const float b = cs[(tp < 0 ? 3 + tp : 0) * C + ch];
+        nv[e] = tp >= 0 ? a : b;
+    }
+#pragma unroll
+    for (int e = 0; e < 3; ++e) cs[e * C + ch] = nv[e];
+}
+
+template <typename T, typename ST, int DK, int DV, bool FU, bool CV>
 static hipError_t launch_recurrent_f(const DecodeArgs &a, hipStream_t st) {
     const int pairs = a.num_seqs * a.h_v;
     const size_t state_bytes = static_cast<size_t>(pairs) * DK * DV * sizeof(ST);
     const bool nts = state_bytes > kStreamStateBytes, colw = a.ntok > 1;
-    auto kern = colw ? (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, true, FU>
-                            : recurrent_fwd_kernel<T, ST, DK, DV, false, true, FU>)
-                     : (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, false, FU>
-                            : recurrent_fwd_kernel<T, ST, DK, DV, false, false, FU>);
+    auto kern = colw ? (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, true, FU, CV>
+                            : recurrent_fwd_kernel<T, ST, DK, DV, false, true, FU, CV>)
+                     : (nts ? recurrent_fwd_kernel<T, ST, DK, DV, true, false, FU, CV>
+                            : recurrent_fwd_kernel<T, ST, DK, DV, false, false, FU, CV>);
     hipLaunchKernelGGL(kern, dim3(pairs), dim3(kDecodeThreads), 0, st,
                        static_cast<const T *>(a.q), static_cast<const T *>(a.k),
                        static_cast<const T *>(a.v), static_cast<const T *>(a.log_alpha),
                        static_cast<const T *>(a.b), static_cast<const T *>(a.w),
                        static_cast<ST *>(a.S), a.idx, static_cast<T *>(a.o), a.ntok,
                        a.num_slots, a.h_k, a.h_v, a.h_v / a.h_k, a.fu.qk_norm ? 1 : 0,
-                       a.fu.l2eps, static_cast<const T *>(a.fu.gate), a.fu.nw, a.fu.neps);
+                       a.fu.l2eps, static_cast<const T *>(a.fu.gate), a.fu.nw, a.fu.neps,
+                       a.fu.cw, a.fu.cst, a.fu.csilu ? 1 : 0);
+    if constexpr (CV) {
+        const int64_t threads = static_cast<int64_t>(a.num_seqs) * 2 * a.h_k * DK;
+        const int C = 2 * a.h_k * DK + a.h_v * DV;
+        hipLaunchKernelGGL((conv_qk_state_kernel<T, DK>), dim3((threads + 255) / 256), dim3(256),
+                           0, st, static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+                           a.idx, a.fu.cst, a.num_seqs, a.ntok, a.num_slots, a.h_k, C);
+    }
     return hipGetLastError();
 }
 
 template <typename T, typename ST, int DK, int DV>
 static hipError_t launch_recurrent_t(const DecodeArgs &a, hipStream_t st) {
-    if (a.fu.qk_norm || a.fu.gate) return launch_recurrent_f<T, ST, DK, DV, true>(a, st);
-    return launch_recurrent_f<T, ST, DK, DV, false>(a, st);
+    if (a.fu.cw) return launch_recurrent_f<T, ST, DK, DV, true, true>(a, st);
+    if (a.fu.qk_norm || a.fu.gate) return launch_recurrent_f<T, ST, DK, DV, true, false>(a, st);
+    return launch_recurrent_f<T, ST, DK, DV, false, false>(a, st);
 }
 
 template <typename T, typename ST>

@@ -15,6 +15,9 @@ struct Fusion {
     const void *gate = nullptr;      // [.., h_v, d_v] input dtype, or NULL
     const float *nw = nullptr;       // [d_v] fp32
     float neps = 0.f;
+    const float *cw = nullptr;       // short convolution taps [C][4] fp32, or NULL
+    float *cst = nullptr;            // conv state [num_slots][3][C] fp32
+    bool csilu = false;
 };
 
 struct DecodeArgs {

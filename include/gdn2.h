@@ -93,6 +93,20 @@ typedef enum gdn2_state_dtype {
  *                per (token, value head), silu(g) = g / (1 + exp(-g)); must not alias o
  *   norm_weight  device fp32 [d_v], required with a gate (shared by all value heads)
  *   norm_eps     >= 0
+ *
+ * gdn2_recurrent_fwd only: the short causal depthwise convolution that the same diagram
+ * puts before the L2-Norm (burn-gdn2 use_short_conv; the llama.cpp decode notes, section 1,
+ * give its kernel width 4, and section 2 its state of the last 3 inputs per channel, kept
+ * in the recurrent cache and read and written back every step). The convolved channels are
+ * q, k and v, C = 2 h_k d_k + h_v d_v of them in that order (q of key head 0..h_k-1, then
+ * k likewise, then v of value head 0..h_v-1, each head's d values contiguous):
+ *   conv_weight  NULL: no convolution. Else device fp32 [C][4]; tap 3 multiplies the
+ *                current token, tap 0 the input three tokens back
+ *   conv_state   device fp32 [num_slots][3][C], the last three inputs of each channel
+ *                (oldest first), on the same slots as the recurrent state; read and updated
+ *                in place
+ *   conv_silu    nonzero: y = silu(conv(x)); zero: y = conv(x)
+ * The convolved q and k are what the L2-norm (if on) and the recurrence see.
  */
 typedef struct gdn2_fusion {
     int32_t qk_l2norm;
@@ -100,6 +114,9 @@ typedef struct gdn2_fusion {
     const void *gate;
     const float *norm_weight;
     float norm_eps;
+    const float *conv_weight;
+    float *conv_state;
+    int32_t conv_silu;
 } gdn2_fusion;
 
 typedef struct gdn2_dims {
@@ -149,7 +166,8 @@ size_t gdn2_chunk_fwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
  *   workspace   device buffer of at least gdn2_chunk_fwd_workspace_bytes() bytes, 256-byte
  *               aligned; its contents on entry are ignored and are clobbered.
  *   fusion      NULL, or the optional q/k L2-norm and gated output norm (gdn2_fusion);
- *               the gate is [B, T, h_v, d_v]
+ *               the gate is [B, T, h_v, d_v]. A short convolution is not built for this
+ *               call (GDN2_ERR_UNSUPPORTED)
  *   stream      hipStream_t the work is enqueued on
  * Returns GDN2_OK or an error status (nothing is enqueued on a validation error).
  */
@@ -201,8 +219,9 @@ gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
  *                 distinct; two sequences on one slot race.
  *   o             device [N, T, h_v, d_v] in the input dtype; must not alias an input or
  *                 the state
- *   fusion        NULL, or the optional q/k L2-norm and gated output norm (gdn2_fusion);
- *                 the gate is [N, T, h_v, d_v]. Padding sequences still get zero o rows.
+ *   fusion        NULL, or the optional short convolution, q/k L2-norm and gated output
+ *                 norm (gdn2_fusion); the gate is [N, T, h_v, d_v]. Padding sequences still
+ *                 get zero o rows, and their conv state is untouched.
  *   stream        hipStream_t
  * With T = 1, state_idx = NULL and an fp32 state this is gdn2_recurrent_step.
  */

@@ -13,9 +13,10 @@ Two independent evaluations of the method live here:
   ``recurrent_cache`` runs it over a pool of stored states (the recurrent cache of the
   llama.cpp decode notes, LocalAI mirror, section 2), optionally stored in bfloat16
   (section 4 of the same notes), with ``round_to_bf16`` the rounding of the stored state.
-* ``l2_normalize`` and ``gated_rms_norm`` -- the stages the burn-gdn2 "Architecture"
-  diagram draws around the recurrence (L2-Norm of q and k before it, Gated RMS Norm
-  with a SiLU gate after it), in numpy fp64.
+* ``short_conv`` / ``conv_qkv``, ``l2_normalize`` and ``gated_rms_norm`` -- the stages
+  the burn-gdn2 "Architecture" diagram draws around the recurrence (ShortConv and the
+  L2-Norm of q and k before it, the Gated RMS Norm with a SiLU gate after it), in numpy
+  fp64.
 * ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
   mode) and on the FG^2-GDN summary (section 2C, DPLR structure and the WY
   representation), in numpy fp64. It exists to pin the recurrence: the two are
@@ -225,6 +226,53 @@ def gated_rms_norm(o, gate, weight, eps):
     g = np.asarray(gate, dtype=np.float64)
     rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
     return o / rms * np.asarray(weight, dtype=np.float64) * (g / (1.0 + np.exp(-g)))
+
+
+def short_conv(x, weight, state, silu=False):
+    """Causal depthwise convolution of width 4 along the token axis, one sequence.
+
+    The ShortConv stage of the burn-gdn2 "Architecture" diagram; the llama.cpp decode notes
+    give its width 4 (section 1) and its state, the last three inputs of every channel
+    (section 2). x [T, C] the inputs; weight [C, 4], tap 3 on the current token and tap 0
+    on the input three tokens back; state [3, C] the three inputs before x, oldest first.
+    With ``silu`` the output passes through y / (1 + exp(-y)) (the pages name no
+    activation; it is an option). Returns (y [T, C], the new state [3, C]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    xx = np.concatenate([np.asarray(state, dtype=np.float64), x], axis=0)
+    y = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        for j in range(4):
+            y[t] += w[:, j] * xx[t + j]
+    if silu:
+        y = y / (1.0 + np.exp(-y))
+    return y, xx[-3:].copy()
+
+
+def conv_qkv(q, k, v, weight, conv_pool, state_idx=None, silu=False):
+    """short_conv over the q, k and v channels of each sequence against a pool of conv
+    states. q, k [N,T,H_k,d_k]; v [N,T,H_v,d_v]; channels in the order q (key heads), k
+    (key heads), v (value heads), each head's values contiguous; weight [C, 4]; conv_pool
+    [num_slots, 3, C]; ``state_idx`` as in ``recurrent_cache`` (padding entries leave
+    their slot alone and return their inputs unchanged). Returns (q', k', v', new pool)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    N, T, H_k, d_k = q.shape
+    H_v, d_v = v.shape[2:]
+    pool = np.array(conv_pool, dtype=np.float64, copy=True)
+    idx = np.arange(N) if state_idx is None else np.asarray(state_idx, dtype=np.int64)
+    qo, ko, vo = q.copy(), k.copy(), v.copy()
+    for n in range(N):
+        s = idx[n]
+        if not 0 <= s < pool.shape[0]:
+            continue
+        x = np.concatenate([q[n].reshape(T, -1), k[n].reshape(T, -1), v[n].reshape(T, -1)], 1)
+        y, pool[s] = short_conv(x, weight, pool[s], silu)
+        a, bnd = H_k * d_k, 2 * H_k * d_k
+        qo[n] = y[:, :a].reshape(T, H_k, d_k)
+        ko[n] = y[:, a:bnd].reshape(T, H_k, d_k)
+        vo[n] = y[:, bnd:].reshape(T, H_v, d_v)
+    return qo, ko, vo, pool
 
 
 def _unit_lower_inverse(L: np.ndarray) -> np.ndarray:

@@ -133,6 +133,12 @@ def test_fusion_options_are_validated(L):
                  fusion=Fusion(0, 0.0, ctypes.c_void_p(0x6000), W, 1e-5)) == 2
     assert fwd(L, okr, o=ctypes.c_void_p(0x6000),
                fusion=Fusion(0, 0.0, ctypes.c_void_p(0x6000), W, 1e-5)) == 2
+    # the short convolution: recurrent forward only, and it needs its state
+    CW, CS = ctypes.c_void_p(0x8000), ctypes.c_void_p(0x9000)
+    assert chunk(L, okc, fusion=Fusion(0, 0.0, None, None, 0.0, CW, CS, 1)) == 3
+    assert fwd(L, okr, fusion=Fusion(0, 0.0, None, None, 0.0, CW, None, 1)) == 1
+    assert fwd(L, okr, o=CS, fusion=Fusion(0, 0.0, None, None, 0.0, CW, CS, 1)) == 2
+    assert fwd(L, okr, fusion=Fusion(0, 0.0, None, None, 0.0, CW, CS, 1)) == 2   # o aliases q
     # valid options pass the fusion checks and are rejected later (o aliases q)
     good = Fusion(1, 1e-6, ctypes.c_void_p(0x6000), W, 1e-5)
     assert chunk(L, okc, fusion=good) == 2

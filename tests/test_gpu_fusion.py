@@ -165,3 +165,81 @@ def test_fusions_on_unit_rows_change_only_the_output_stage():
     assert oracle.rel_l2(np64(o1), np64(o0)) <= 2e-2
     assert oracle.rel_l2(np64(S1_T), np64(S0_T)) <= 2e-2
     assert torch.equal(S2_T, S0_T)
+
+
+# ---- short causal convolution of q, k, v fused into the recurrent forward ---------------
+
+def conv_case(dtype, N, T, hk, hv, d, slots, seed):
+    wl = inputs.DecodeWorkload("recurrent_conv", dtype, N, hk, hv, d, d, steps=T)
+    x = inputs.decode_inputs(wl, seed=seed)
+    y = {n: x[n].transpose(0, 1).contiguous() for n in NAMES}
+    C = 2 * hk * d + hv * d
+    rng = np.random.default_rng(seed + 1)
+    cw = torch.from_numpy((0.5 * rng.standard_normal((C, 4))).astype(np.float32))
+    cpool = torch.from_numpy(rng.standard_normal((slots, 3, C)).astype(np.float32))
+    pool = torch.from_numpy((0.1 * rng.standard_normal((slots, hv, d, d))).astype(np.float32))
+    return y, cw, cpool, pool
+
+
+def oracle_conv_call(y, cw, cpool, pool, idx, silu, qk_norm, gate=None, w=None,
+                     bf16_state=False):
+    q, k, v, cnew = oracle.conv_qkv(np64(y["q"]), np64(y["k"]), np64(y["v"]), np64(cw),
+                                    cpool, idx, silu)
+    if qk_norm:
+        q, k = oracle.l2_normalize(q, L2EPS), oracle.l2_normalize(k, L2EPS)
+    o, pnew = oracle.recurrent_cache(q, k, v, np64(y["log_alpha"]), np64(y["b"]), np64(y["w"]),
+                                     pool, idx, bf16_state=bf16_state, threads=16)
+    if gate is not None:
+        o = oracle.gated_rms_norm(o, np64(gate), np64(w), NEPS)
+        o[[i for i, s in enumerate(idx) if not 0 <= s < pool.shape[0]]] = 0.0
+    return o, pnew, cnew
+
+
+@pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("dtype,T,extra", [(torch.float32, 1, False), (torch.float32, 2, True),
+                                           (torch.float32, 5, False), (torch.bfloat16, 1, True),
+                                           (torch.bfloat16, 11, False), (torch.bfloat16, 3, True)])
+def test_recurrent_short_conv(dtype, T, extra, silu):
+    """GVA (3 value heads per key head), 7 slots with a padding entry; `extra` also turns on
+    the L2-norm and the gated output norm."""
+    y, cw, cpool, pool = conv_case(dtype, 5, T, 2, 6, 128, 7, seed=120 + T)
+    idx = [6, 0, -1, 3, 2]
+    gate, w = gate_and_weight((5, T, 6, 128), dtype, 128, seed=121) if extra else (None, None)
+    P, CP = pool.cuda(), cpool.cuda()
+    o = g.recurrent_fwd(*(y[n].cuda() for n in NAMES), P,
+                        state_idx=torch.tensor(idx, dtype=torch.int32, device="cuda"),
+                        qk_l2norm=extra, l2norm_eps=L2EPS,
+                        gate=None if gate is None else gate.cuda(),
+                        norm_weight=None if w is None else w.cuda(), norm_eps=NEPS,
+                        conv_weight=cw.cuda(), conv_state=CP, conv_silu=silu)
+    torch.cuda.synchronize()
+    o_r, P_r, C_r = oracle_conv_call(y, cw, np64(cpool), np64(pool), idx, silu, extra, gate, w)
+    assert np.array_equal(np64(CP), C_r)          # the new conv state is the raw inputs
+    assert np.all(np64(o)[2] == 0.0)
+    tol = TOL[dtype]
+    eo, es = oracle.rel_l2(np64(o), o_r), oracle.rel_l2(np64(P), P_r)
+    print(f"[parity] short conv silu={silu} {dtype} T={T} extra={extra}: o={eo:.2e} S={es:.2e}",
+          flush=True)
+    assert eo <= tol and es <= tol
+
+
+def test_short_conv_state_carried_over_calls():
+    """Eight calls of two tokens each (fewer than the conv width) on one pair of pools, with
+    a bf16 recurrent state: every call against the oracle carrying both pools."""
+    dtype, calls, T = torch.bfloat16, 8, 2
+    y, cw, cpool, pool = conv_case(dtype, 4, calls * T, 1, 2, 64, 4, seed=130)
+    P, CP = pool.to(torch.bfloat16).cuda(), cpool.cuda()
+    Pr, Cr = oracle.round_to_bf16(np64(pool)), np64(cpool)
+    eo_max = 0.0
+    for c in range(calls):
+        part = {n: y[n][:, c * T:(c + 1) * T].contiguous() for n in NAMES}
+        o = g.recurrent_fwd(*(part[n].cuda() for n in NAMES), P, conv_weight=cw.cuda(),
+                            conv_state=CP, conv_silu=True)
+        o_r, Pr, Cr = oracle_conv_call(part, cw, Cr, Pr, None, True, False, bf16_state=True)
+        torch.cuda.synchronize()
+        eo_max = max(eo_max, oracle.rel_l2(np64(o), o_r))
+        assert np.array_equal(np64(CP), Cr)
+    es = oracle.rel_l2(np64(P), Pr)
+    print(f"[parity] short conv over {calls} calls of {T} tokens: o max={eo_max:.2e} S={es:.2e}",
+          flush=True)
+    assert eo_max <= 2e-2 and es <= 2e-2

@@ -415,3 +415,55 @@ def test_gated_rms_norm_closed_forms():
     # and it is invariant to a positive scale of o
     assert np.allclose(oracle.gated_rms_norm(3.0 * o, g, w, 0.0),
                        oracle.gated_rms_norm(o, g, w, 0.0), rtol=0, atol=1e-13)
+
+
+def test_short_conv_closed_forms_and_library_convolution():
+    rng = np.random.default_rng(23)
+    T, C = 9, 5
+    x, st = rng.standard_normal((T, C)), rng.standard_normal((3, C))
+    eye = np.zeros((C, 4))
+    eye[:, 3] = 1.0                                       # tap 3: the current token
+    y, ns = oracle.short_conv(x, eye, st)
+    assert np.array_equal(y, x) and np.array_equal(ns, x[-3:])
+    back = np.zeros((C, 4))
+    back[:, 0] = 1.0                                      # tap 0: three tokens back
+    y, _ = oracle.short_conv(x, back, st)
+    assert np.array_equal(y[:3], st) and np.array_equal(y[3:], x[:-3])
+    # against numpy's convolution (a library routine) channel by channel
+    w = rng.standard_normal((C, 4))
+    y, _ = oracle.short_conv(x, w, st)
+    xx = np.concatenate([st, x])
+    for c in range(C):
+        assert np.allclose(y[:, c], np.convolve(xx[:, c], w[c, ::-1], mode="valid"),
+                           rtol=0, atol=1e-13)
+    # a short call keeps older state entries: T = 2 shifts the state by two
+    y2, ns2 = oracle.short_conv(x[:2], w, st)
+    assert np.array_equal(ns2, np.concatenate([st[2:], x[:2]]))
+    # split and resume with the state carried equals one call; SiLU closed form
+    ya, sa = oracle.short_conv(x[:4], w, st)
+    yb, sb = oracle.short_conv(x[4:], w, sa)
+    yf, sf = oracle.short_conv(x, w, st)
+    assert np.allclose(np.concatenate([ya, yb]), yf, rtol=0, atol=1e-14) and np.array_equal(sb, sf)
+    one = np.zeros((1, 4))
+    one[0, 3] = np.log(3.0)
+    ys, _ = oracle.short_conv([[1.0]], one, np.zeros((3, 1)), silu=True)
+    assert abs(ys[0, 0] - 0.75 * np.log(3.0)) < 1e-15
+
+
+def test_conv_qkv_channel_order_and_padding():
+    rng = np.random.default_rng(24)
+    N, T, Hk, Hv, dk, dv = 3, 4, 1, 2, 2, 3
+    q, k = rng.standard_normal((N, T, Hk, dk)), rng.standard_normal((N, T, Hk, dk))
+    v = rng.standard_normal((N, T, Hv, dv))
+    C = 2 * Hk * dk + Hv * dv
+    w = np.zeros((C, 4))
+    w[:, 3] = np.arange(1, C + 1)                         # channel c scaled by c + 1
+    pool = rng.standard_normal((4, 3, C))
+    qo, ko, vo, npool = oracle.conv_qkv(q, k, v, w, pool, [2, -1, 0])
+    assert np.array_equal(qo[0], q[0] * np.array([1.0, 2.0]))
+    assert np.array_equal(ko[0], k[0] * np.array([3.0, 4.0]))
+    assert np.array_equal(vo[0], v[0] * np.arange(5, 11).reshape(2, 3))
+    assert np.array_equal(qo[1], q[1]) and np.array_equal(npool[1], pool[1])   # padding
+    assert np.array_equal(npool[3], pool[3])
+    x2 = np.concatenate([q[2].reshape(T, -1), k[2].reshape(T, -1), v[2].reshape(T, -1)], 1)
+    assert np.array_equal(npool[0], x2[-3:])
