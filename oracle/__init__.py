@@ -17,6 +17,9 @@ Two independent evaluations of the method live here:
   the burn-gdn2 "Architecture" diagram draws around the recurrence (ShortConv and the
   L2-Norm of q and k before it, the Gated RMS Norm with a SiLU gate after it), in numpy
   fp64.
+* ``recurrent_bwd`` -- the gradient of ``recurrent`` with respect to every input and the
+  initial state, by the token-by-token adjoint of the recurrence (chain rule through the
+  decay, erase, write and read-out steps, in reverse), fp64, in the same C file.
 * ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
   mode) and on the FG^2-GDN summary (section 2C, DPLR structure and the WY
   representation), in numpy fp64. It exists to pin the recurrence: the two are
@@ -72,6 +75,9 @@ def _load():
         lib.gdn2_oracle_sequence.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                              dp, dp, dp, dp, dp, dp, dp, dp]
         lib.gdn2_oracle_sequence.restype = ctypes.c_int
+        lib.gdn2_oracle_sequence_bwd.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + \
+            [dp] * 16
+        lib.gdn2_oracle_sequence_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -148,6 +154,73 @@ def recurrent(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, pairs=None, th
         with ThreadPoolExecutor(max_workers=nthr) as ex:
             list(ex.map(run, pairs))
     return o, S_T
+
+
+def sequence_bwd(q, k, v, w, log_alpha, b, S0, do, dS_T=None):
+    """Gradient of ``sequence`` for one (sequence, value head) pair, by the token-by-token
+    adjoint of the recurrence (gdn2_oracle.c). do [T,d_v] and dS_T [d_k,d_v] (None: zero)
+    are the gradients of the loss with respect to o and S_T. Returns a dict of fp64 arrays
+    dq, dk, dlog_alpha, db [T,d_k]; dv, dw [T,d_v]; dS0 [d_k,d_v]."""
+    lib = _load()
+    q, k, v, w, la, b, dO = (_f64(x) for x in (q, k, v, w, log_alpha, b, do))
+    T, d_k = k.shape
+    d_v = v.shape[1]
+    S0 = _f64(S0)
+    dST = None if dS_T is None else _f64(dS_T)
+    out = {n: np.zeros((T, d_k)) for n in ("dq", "dk", "dlog_alpha", "db")}
+    out.update({n: np.zeros((T, d_v)) for n in ("dv", "dw")})
+    out["dS0"] = np.zeros((d_k, d_v))
+    rc = lib.gdn2_oracle_sequence_bwd(
+        T, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(la), _ptr(b), _ptr(S0), _ptr(dO),
+        None if dST is None else _ptr(dST), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dw"]), _ptr(out["dlog_alpha"]), _ptr(out["db"]), _ptr(out["dS0"]))
+    if rc != 0:
+        raise MemoryError("gdn2_oracle_sequence_bwd failed")
+    return out
+
+
+def recurrent_bwd(q, k, v, log_alpha, b, w, do, S0=None, dS_T=None, cu_seqlens=None,
+                  threads=None):
+    """Gradient of ``recurrent`` (same packed layouts; do like o, dS_T like S_T or None).
+    Under grouped value heads the q and k gradients sum over the value heads that read the
+    key head. Returns a dict: dq, dk [T_total,H_k,d_k]; dv, dw [T_total,H_v,d_v];
+    dlog_alpha, db [T_total,H_v,d_k]; dS0 [N,H_v,d_k,d_v]."""
+    q, k, v, w, la, b, dO = (np.asarray(x) for x in (q, k, v, w, log_alpha, b, do))
+    T_total, H_k, d_k = k.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    G = H_v // H_k
+    cu = np.array([0, T_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    res = {"dq": np.zeros((T_total, H_k, d_k)), "dk": np.zeros((T_total, H_k, d_k)),
+           "dv": np.zeros((T_total, H_v, d_v)), "dw": np.zeros((T_total, H_v, d_v)),
+           "dlog_alpha": np.zeros((T_total, H_v, d_k)), "db": np.zeros((T_total, H_v, d_k)),
+           "dS0": np.zeros((N, H_v, d_k, d_v))}
+    pairs = [(n, h) for n in range(N) for h in range(H_v)]
+
+    def run(pair):
+        n, h = pair
+        s, e = int(cu[n]), int(cu[n + 1])
+        hk = h // G
+        S_init = np.zeros((d_k, d_v)) if S0 is None else np.asarray(S0)[n, h]
+        dst = None if dS_T is None else np.asarray(dS_T)[n, h]
+        return pair, sequence_bwd(q[s:e, hk], k[s:e, hk], v[s:e, h], w[s:e, h], la[s:e, h],
+                                  b[s:e, h], S_init, dO[s:e, h], dst)
+
+    nthr = threads or default_threads()
+    if nthr <= 1 or len(pairs) <= 1:
+        results = [run(p) for p in pairs]
+    else:
+        with ThreadPoolExecutor(max_workers=nthr) as ex:
+            results = list(ex.map(run, pairs))
+    for (n, h), gr in results:           # accumulated in a fixed order
+        s, e = int(cu[n]), int(cu[n + 1])
+        hk = h // G
+        res["dq"][s:e, hk] += gr["dq"]
+        res["dk"][s:e, hk] += gr["dk"]
+        for nm in ("dv", "dw", "dlog_alpha", "db"):
+            res[nm][s:e, h] = gr[nm]
+        res["dS0"][n, h] = gr["dS0"]
+    return res
 
 
 def decode_step(q, k, v, log_alpha, b, w, S, pairs=None, threads=None):

@@ -467,3 +467,71 @@ def test_conv_qkv_channel_order_and_padding():
     assert np.array_equal(npool[3], pool[3])
     x2 = np.concatenate([q[2].reshape(T, -1), k[2].reshape(T, -1), v[2].reshape(T, -1)], 1)
     assert np.array_equal(npool[0], x2[-3:])
+
+
+# ---- the gradient of the recurrence (oracle.recurrent_bwd) --------------------------------
+
+def _loss_parts(rng, T, Hv, dv, N, dk):
+    return rng.standard_normal((T, Hv, dv)), rng.standard_normal((N, Hv, dk, dv))
+
+
+def test_recurrent_bwd_matches_central_differences():
+    """Every gradient against central differences of L = sum(o . R) + sum(S_T . R2), on two
+    packed sequences with grouped value heads (2 value heads over 1 key head)."""
+    rng = np.random.default_rng(30)
+    T, Hk, Hv, dk, dv = 7, 1, 2, 3, 2
+    q, k, v, la, b, w = rand_case(rng, T, Hk=Hk, Hv=Hv, dk=dk, dv=dv)
+    cu = [0, 3, 7]
+    S0 = rng.standard_normal((2, Hv, dk, dv))
+    R, R2 = _loss_parts(rng, T, Hv, dv, 2, dk)
+    ins = {"q": q, "k": k, "v": v, "log_alpha": la, "b": b, "w": w, "S0": S0}
+
+    def loss(x):
+        o, ST = oracle.recurrent(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"],
+                                 S0=x["S0"], cu_seqlens=cu, threads=1)
+        return float(np.sum(o * R) + np.sum(ST * R2))
+
+    gr = oracle.recurrent_bwd(q, k, v, la, b, w, R, S0=S0, dS_T=R2, cu_seqlens=cu, threads=1)
+    names = {"q": "dq", "k": "dk", "v": "dv", "log_alpha": "dlog_alpha", "b": "db", "w": "dw",
+             "S0": "dS0"}
+    eps = 1e-6
+    for nm, gname in names.items():
+        num = np.zeros_like(ins[nm])
+        for idx in np.ndindex(ins[nm].shape):
+            xp = {a: c.copy() for a, c in ins.items()}
+            xm = {a: c.copy() for a, c in ins.items()}
+            xp[nm][idx] += eps
+            xm[nm][idx] -= eps
+            num[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+        assert np.allclose(gr[gname], num, rtol=1e-6, atol=1e-7), nm
+
+
+def test_recurrent_bwd_matches_torch_autograd_across_checkpoints():
+    """An independent evaluation: torch autograd in fp64 through a plain loop of the
+    recurrence, at T = 150 (the oracle recomputes states from checkpoints every 64 tokens)."""
+    import torch
+    rng = np.random.default_rng(31)
+    T, dk, dv = 150, 5, 4
+    q, k, v, la, b, w = rand_case(rng, T, dk=dk, dv=dv)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    R, R2 = _loss_parts(rng, T, 1, dv, 1, dk)
+    gr = oracle.recurrent_bwd(q, k, v, la, b, w, R, S0=S0, dS_T=R2, threads=1)
+    t = {n: torch.tensor(x[:, 0], dtype=torch.float64, requires_grad=True)
+         for n, x in (("q", q), ("k", k), ("v", v), ("la", la), ("b", b), ("w", w))}
+    S = torch.tensor(S0[0, 0], dtype=torch.float64, requires_grad=True)
+    S_in = S
+    loss = torch.zeros((), dtype=torch.float64)
+    Rt, R2t = torch.tensor(R[:, 0]), torch.tensor(R2[0, 0])
+    for i in range(T):
+        kk, qq = t["k"][i], t["q"][i]
+        P = (torch.eye(dk, dtype=torch.float64) - torch.outer(kk, t["b"][i] * kk)) @ \
+            torch.diag(torch.exp(t["la"][i]))
+        S = P @ S + torch.outer(kk, t["w"][i] * t["v"][i])
+        loss = loss + (S.T @ qq) @ Rt[i]
+    loss = loss + torch.sum(S * R2t)
+    loss.backward()
+    pairs = (("q", "dq"), ("k", "dk"), ("v", "dv"), ("la", "dlog_alpha"), ("b", "db"),
+             ("w", "dw"))
+    for n, gname in pairs:
+        assert np.allclose(gr[gname][:, 0], t[n].grad.numpy(), rtol=1e-9, atol=1e-10), n
+    assert np.allclose(gr["dS0"][0, 0], S_in.grad.numpy(), rtol=1e-9, atol=1e-10)
