@@ -83,8 +83,8 @@ struct ChunkParams {
     char *rec;           // first per-(chunk, head) record
     // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of
     // every pair are split into nseg segments of seg_len chunks that run concurrently.
-    float *seg_S;        // [pair][nseg][DK][DV]    state entering each segment (0: copy of S0)
-    float *seg_P;        // [pair][nseg-2][DK][DK]  transition of segments 1 .. nseg-2
+    float *seg_S;        // [pair][2][DK][DV]       states entering segments 0 (copy of S0) and 1
+    float *seg_P;        // [pair][nseg-2] SegPFrag transition of segments 1 .. nseg-2
     float *seg_R;        // [pair][nseg-2][DK][DV]  end state of segments 1 .. nseg-2 from 0
     int seqlen, num_seqs, h_k, h_v, group, nc_dense, num_pairs, nslices;
     int nseg, seg_len;
@@ -778,12 +778,145 @@ struct StageLayout {
     static_assert(lds_bytes(1) <= 160 * 1024, "stage must fit in LDS");
 };
 
+// Segment transitions P (d_k x d_k, see the segmented state pass below) as the segment pass
+// writes them and the state pass reads them: matrix-core A operands, so that the product
+// P S needs no transposition. Fragment (rt, kt) covers rows 16 rt .. 16 rt + 15 and one k
+// tile of columns; lane li + 16 lg holds row 16 rt + li at the k slots of group lg (the perm
+// order of mma_k32 for bf16 records, k = 4 lg + s for fp32 ones).
+//   bf16 records: two planes hi = bf16(P) and lo = bf16(P - hi), each [RT][DK/32][64][8]
+//                 bf16; P S is formed as hi S_hi + hi S_lo + lo S_hi, which keeps about 16
+//                 significant bits of the fp32 operands;
+//   fp32 records: one plane [RT][RT][64][4] fp32.
+template <int DK, bool BF>
+struct SegPFrag {
+    static constexpr int RT = DK / 16, NK = BF ? DK / 32 : DK / 16;
+    static constexpr size_t PLANE = static_cast<size_t>(RT) * NK * 64 * 16;   // bytes
+    static constexpr size_t BYTES = BF ? 2 * PLANE : PLANE;
+    static_assert(BYTES == static_cast<size_t>(DK) * DK * 4, "the size of an fp32 P");
+    // stores element P[r][c]
+    __device__ static void put(char *base, int r, int c, float x) {
+        const int rt = r >> 4, lane = (r & 15) + 16 * ((c & 15) >> 2);
+        if constexpr (BF) {
+            const int kt = c >> 5, slot = 4 * ((c >> 4) & 1) + (c & 3);
+            const size_t off = ((static_cast<size_t>(rt) * NK + kt) * 64 + lane) * 16 + slot * 2;
+            const __bf16 hi = static_cast<__bf16>(x);
+            const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+            *reinterpret_cast<__bf16 *>(base + off) = hi;
+            *reinterpret_cast<__bf16 *>(base + PLANE + off) = lo;
+        } else {
+            const int kt = c >> 4, slot = c & 3;
+            const size_t off = ((static_cast<size_t>(rt) * NK + kt) * 64 + lane) * 16 + slot * 4;
+            *reinterpret_cast<float *>(base + off) = x;
+        }
+    }
+    // Row tiles R0 .. R0 + RT/2 - 1 of P S + R, for the 16 columns of S a wave holds in D
+    // layout (lane: rows 16 rt + 4 lg + ii of its column), written over those tiles of S and
+    // into the exchange `xch` ([rt][lane]); P staged in LDS at `pl`, R (these tiles) in D
+    // layout. The fragments of the next row tile are read while the products of one run.
+    template <int R0>
+    __device__ static void carry_half(const char *pl, const f32x4 (&R)[RT / 2], f32x4 (&S)[RT],
+                                      f32x4 *xch) {
+        constexpr int H = RT / 2;
+        const int lane = threadIdx.x & 63;
+        // this lane's LDS address in the staged P, kept opaque so that the compiler folds only
+        // the fragment offsets (< 64 KB) into the LDS instructions instead of keeping one
+        // address register per fragment
+        uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                            (__attribute__((address_space(3))) const char *)pl)) + lane * 16;
+        asm volatile("" : "+v"(base));
+        auto frag = [&](uint32_t off) {
+            return *(__attribute__((address_space(3))) const u32x4 *)(static_cast<uintptr_t>(base + off));
+        };
+        f32x4 acc[H];
+#pragma unroll
+        for (int j = 0; j < H; ++j) acc[j] = R[j];
+        if constexpr (BF) {
+            u32x4 sh[NK], sl[NK];
+#pragma unroll
+            for (int kt = 0; kt < NK; ++kt) {
+                const f32x4 a = S[2 * kt], b = S[2 * kt + 1];
+                sh[kt] = dpair_to_b32(a, b);
+                const f32x4 ar = {bf16_lo(sh[kt].x), bf16_hi(sh[kt].x), bf16_lo(sh[kt].y), bf16_hi(sh[kt].y)};
+                const f32x4 br = {bf16_lo(sh[kt].z), bf16_hi(sh[kt].z), bf16_lo(sh[kt].w), bf16_hi(sh[kt].w)};
+                sl[kt] = dpair_to_b32(a - ar, b - br);
+            }
+            u32x4 fh[2][NK], fl[2][NK];
+#pragma unroll
+            for (int kt = 0; kt < NK; ++kt) {
+                fh[0][kt] = frag((R0 * NK + kt) * 1024);
+                fl[0][kt] = frag(PLANE + (R0 * NK + kt) * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const int cb = j & 1, nb = cb ^ 1;
+                if (j + 1 < H) {
+#pragma unroll
+                    for (int kt = 0; kt < NK; ++kt) {
+                        fh[nb][kt] = frag(((R0 + j + 1) * NK + kt) * 1024);
+                        fl[nb][kt] = frag(PLANE + ((R0 + j + 1) * NK + kt) * 1024);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kt = 0; kt < NK; ++kt) {
+                    acc[j] = mma_k32(fh[cb][kt], sh[kt], acc[j]);
+                    acc[j] = mma_k32(fh[cb][kt], sl[kt], acc[j]);
+                    acc[j] = mma_k32(fl[cb][kt], sh[kt], acc[j]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            f32x4 f[2][NK];
+#pragma unroll
+            for (int kt = 0; kt < NK; ++kt) f[0][kt] = __builtin_bit_cast(f32x4, frag((R0 * NK + kt) * 1024));
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const int cb = j & 1, nb = cb ^ 1;
+                if (j + 1 < H) {
+#pragma unroll
+                    for (int kt = 0; kt < NK; ++kt)
+                        f[nb][kt] = __builtin_bit_cast(f32x4, frag(((R0 + j + 1) * NK + kt) * 1024));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kt = 0; kt < NK; ++kt) acc[j] = mma_k16_f32(f[cb][kt], S[kt], acc[j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            S[R0 + j] = acc[j];
+            xch[(R0 + j) * 64 + lane] = acc[j];
+        }
+    }
+};
+
+// LDS of the segment carry in the state pass: P_g, then the exchange of the carried state
+// ([slice][rt][lane] f32x4), placed after stage buffer 0 when the workgroup's LDS can grow to
+// hold them there, so that the first chunk is staged into buffer 0 during the carry.
+template <int DK, int DV, bool BF, int NW>
+struct CarryLayout {
+    using SL = StageLayout<DK, DV, BF>;
+    static constexpr size_t P = SegPFrag<DK, BF>::BYTES;
+    static constexpr size_t X = static_cast<size_t>(NW) * (DK / 16) * 1024;
+    static constexpr bool EARLY = SL::buffer_bytes(NW) + P + X <= 159 * 1024;
+    static constexpr size_t PSLOT = EARLY ? SL::buffer_bytes(NW) : 0;
+    static constexpr size_t LDS = PSLOT + P + X > SL::lds_bytes(NW) ? PSLOT + P + X : SL::lds_bytes(NW);
+    static_assert(LDS <= 159 * 1024, "carry fits in LDS");
+};
+
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
 }
 
 // s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt with vmcnt(N) only: at most N vector memory loads of this wave outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
 // s_waitcnt with lgkmcnt(0) only
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier without a memory fence (so it never waits for outstanding loads). The
@@ -863,35 +996,109 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
         return p.rec + (static_cast<size_t>(cbase + c) * p.h_v + h) * R_::bytes;
     };
 
-    if (wave >= 2 * NW) {
-        // ---- copy waves: stage chunk c + 1 in the other buffer during chunk c
-        const int ldr = wave - 2 * NW;
-        auto issue = [&](int c, char *dst) {
-            const char *rec = record(c);
-            for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += NCOPY)
-                dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
-            if (ldr == NCOPY - 1 && lane < static_cast<int>(SL::GCB / 16))
-                dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
-            // the slices' U~: column tiles slice*NW .. slice*NW + NW - 1 are contiguous
-            // in the record, and so are their stage slots
-            const char *us = rec + R_::Ut + static_cast<size_t>(slice) * NW * SL::UTS;
-            char *ud = dst + SL::SHARED + SL::GCB;
-            for (int b = ldr; b < static_cast<int>(NW * SL::UTS / 1024); b += NCOPY)
-                dma16(us + b * 1024 + lane * 16, ud + b * 1024);
-        };
-        if (ce > cb) issue(cb, smem + (cb & 1) * BUF);
-        for (int c = cb; c < ce; ++c) {
-            wait_vmem();                    // this wave's copies for chunk c have landed
-            raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
-            if (c + 1 < ce) issue(c + 1, smem + ((c + 1) & 1) * BUF);
-        }
-        return;
-    }
-
     const bool chain = wave < NW;
     const int sl = chain ? wave : wave - NW;             // slice within the workgroup
     const int ct = slice * NW + sl;
     const int col = 16 * ct + li;
+    // copy waves (wave >= 2 NW): stage chunk c's record part into a stage buffer; chunk c
+    // of the workgroup's segment uses buffer (c - cb) & 1
+    const int ldr = wave - 2 * NW;
+    auto issue = [&](int c, char *dst) {
+        const char *rec = record(c);
+        for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += NCOPY)
+            dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
+        if (ldr == NCOPY - 1 && lane < static_cast<int>(SL::GCB / 16))
+            dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
+        // the slices' U~: column tiles slice*NW .. slice*NW + NW - 1 are contiguous in the
+        // record, and so are their stage slots
+        const char *us = rec + R_::Ut + static_cast<size_t>(slice) * NW * SL::UTS;
+        char *ud = dst + SL::SHARED + SL::GCB;
+        for (int b = ldr; b < static_cast<int>(NW * SL::UTS / 1024); b += NCOPY)
+            dma16(us + b * 1024 + lane * 16, ud + b * 1024);
+    };
+    // State entering the first chunk (the chain waves hold it through the chunk loop): S0
+    // (or zero) without segments; with segments, the copy of S0 (segment 0) or the state
+    // entering segment 1 (copies made before this kernel, since S_T may be the S0 buffer and
+    // the last segment can finish before the first one starts). Segment seg >= 2 carries
+    // that state over segments 1 .. seg-1 first, S <- P_g S + R_g: the chain wave and the
+    // output wave of each slice (idle until the chunk loop) form half the row tiles each and
+    // swap halves through LDS, while the copy waves stage P_g and, where the LDS allows it,
+    // the first chunk into buffer 0. `carry` and the step count are uniform over the
+    // workgroup.
+    using PF = SegPFrag<DK, BF>;
+    using CL = CarryLayout<DK, DV, BF, NW>;
+    constexpr int NBLK = static_cast<int>(PF::BYTES / 1024);
+    constexpr int H = RT / 2;
+    constexpr int CB_MIN = static_cast<int>(SL::SHARED / 1024) / NCOPY +
+                           static_cast<int>(NW * SL::UTS / 1024) / NCOPY;   // see issue()
+    char *pslot = smem + CL::PSLOT;
+    f32x4 *xch = reinterpret_cast<f32x4 *>(pslot + PF::BYTES) + sl * RT * 64;
+    const bool carry = seg >= 2;
+    const bool holds = wave < 2 * NW;                     // chain and output waves
+    f32x4 S[RT];
+    const size_t sbase = static_cast<size_t>(pair) * DK * DV;
+    if (carry ? holds : chain) {
+        const float *Sin = p.nseg == 1 ? p.S0 : p.seg_S + (sbase << 1) + (seg > 0 ? DK * DV : 0);
+        const size_t ibase = p.nseg == 1 ? sbase : 0;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                S[rt][ii] = Sin ? Sin[ibase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col]
+                                : 0.f;
+    }
+    auto stage_P = [&](int g) {            // copy waves
+        const char *Pg = reinterpret_cast<const char *>(p.seg_P) +
+                         (static_cast<size_t>(pair) * (p.nseg - 2) + g - 1) * PF::BYTES;
+        for (int blk = ldr; blk < NBLK; blk += NCOPY) dma16(Pg + blk * 1024 + lane * 16, pslot + blk * 1024);
+    };
+    if (carry && !holds) stage_P(1);      // ahead of the first chunk, which is needed later
+    if (CL::EARLY && !holds && ce > cb) issue(cb, smem);
+    for (int g = 1; g < seg; ++g) {
+        f32x4 R[H];                         // this wave's half of R_g
+        if (holds) {
+            const float *Rg = p.seg_R + (static_cast<size_t>(pair) * (p.nseg - 2) + g - 1) * DK * DV;
+            const int r0 = chain ? 0 : H;
+#pragma unroll
+            for (int j = 0; j < H; ++j)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    R[j][ii] = Rg[static_cast<size_t>(16 * (r0 + j) + 4 * lg + ii) * DV + col];
+        } else if (CL::EARLY && g == 1 && ce > cb) {
+            // P_1 has landed once no more than the first chunk's loads (issued after it; at
+            // least CB_MIN per copy wave) are outstanding
+            wait_vmem_n<CB_MIN>();
+        } else {
+            wait_vmem();
+        }
+        raw_barrier();                      // P_g is staged; the last exchange has been read
+        if (chain) PF::template carry_half<0>(pslot, R, S, xch);
+        else if (holds) PF::template carry_half<H>(pslot, R, S, xch);
+        wait_lds();
+        raw_barrier();                      // every read of P_g is done; both halves written
+        if (holds) {
+#pragma unroll
+            for (int j = 0; j < H; ++j) {   // the other wave's half
+                if (chain) S[H + j] = xch[(H + j) * 64 + lane];
+                else S[j] = xch[j * 64 + lane];
+            }
+            wait_lds();                     // read before the next step or buffer 1 refills
+        } else if (g + 1 < seg) {
+            stage_P(g + 1);
+        }
+    }
+
+    if (wave >= 2 * NW) {
+        // ---- copy waves: stage chunk c + 1 in the other buffer during chunk c
+        if (!CL::EARLY && ce > cb) issue(cb, smem);
+        for (int c = cb; c < ce; ++c) {
+            wait_vmem();                    // this wave's copies for chunk c have landed
+            raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
+            if (c + 1 < ce) issue(c + 1, smem + ((c + 1 - cb) & 1) * BUF);
+        }
+        return;
+    }
+
     u32x4 *xS = reinterpret_cast<u32x4 *>(xch_base + sl * SL::XCH);   // published S operands
     u32x4 *xU = xS + NKD * 64;                                         // published U operands
     lds_flag *flagS = (lds_flag *)(flags + sl);
@@ -904,22 +1111,8 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
 
     if (chain) {
         // ---- chain wave ----
-        f32x4 S[RT];
-        const size_t sbase = static_cast<size_t>(pair) * DK * DV;
-        // state entering the first chunk: S0 (or zero), or the segment's start state
-        // (segmented: a copy made before this kernel, since S_T may be the S0 buffer and
-        // the last segment can finish before the first one starts)
-        const float *Sin = p.nseg == 1 ? p.S0
-                                       : p.seg_S + (static_cast<size_t>(pair) * p.nseg + seg) * DK * DV;
-        const size_t ibase = p.nseg == 1 ? sbase : 0;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                S[rt][ii] = Sin ? Sin[ibase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col]
-                                : 0.f;
         for (int c = cb; c < ce; ++c) {
-            const char *cur = smem + (c & 1) * BUF;
+            const char *cur = smem + ((c - cb) & 1) * BUF;
             raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
             const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur + R_::Wn);
             const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + R_::KgT);
@@ -998,7 +1191,7 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
 
     // ---- output wave ----
     for (int c = cb; c < ce; ++c) {
-        const char *cur = smem + (c & 1) * BUF;
+        const char *cur = smem + ((c - cb) & 1) * BUF;
         raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
         const u32x4 *qg = reinterpret_cast<const u32x4 *>(cur + R_::Qg);
         const u32x4 *mq = reinterpret_cast<const u32x4 *>(cur + R_::M);
@@ -1078,9 +1271,9 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
 //                          entering segment 1); segments 1 .. nseg-2: P (the chain run on the
 //                          columns of the identity, without U~) and R (from zero). All
 //                          segments run concurrently; only the chain is computed.
-//   K2s chunk_scan_kernel  start states S_{g+1} = P_g S_g + R_g, g = 1 .. nseg-2, in fp32 on
-//                          the matrix cores.
-//   K2  chunk_state_kernel every segment from its start state, with outputs.
+//   K2  chunk_state_kernel every segment from its start state, with outputs. The workgroups
+//                          of segment g >= 2 first form S_g from the state entering segment
+//                          1, S_{h+1} = P_h S_h + R_h for h = 1 .. g-1, on the matrix cores.
 // ---------------------------------------------------------------------------------------
 constexpr int kSegWaves = 4;   // chain waves per segment-pass workgroup
 constexpr int kSegCopy = 4;    // copy waves per segment-pass workgroup
@@ -1165,7 +1358,7 @@ __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(
     const bool isP = v < SG::NP;
     const int col = 16 * (isP ? v : v - SG::NP) + li;
     f32x4 S[RT];
-    float *segS = p.seg_S + static_cast<size_t>(pair) * p.nseg * DK * DV;
+    float *segS = p.seg_S + static_cast<size_t>(pair) * 2 * DK * DV;
     const bool fromS0 = active && !isP && g == 0 && p.S0 != nullptr;   // uniform per wave
     if (fromS0) {
         const float *S0p = p.S0 + static_cast<size_t>(pair) * DK * DV + col;
@@ -1252,83 +1445,24 @@ __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(
         wait_lds();
     }
     if (!active) return;
-    float *dst;
-    int ld;
-    if (g == 0) {                            // state entering segment 1
-        dst = segS + static_cast<size_t>(DK) * DV;
-        ld = DV;
-    } else if (isP) {
-        dst = p.seg_P + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DK;
-        ld = DK;
-    } else {
-        dst = p.seg_R + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DV;
-        ld = DV;
+    if (isP) {
+        // P as matrix-core A operands (SegPFrag): this wave holds P[16 rt + 4 lg + ii][col]
+        char *dst = reinterpret_cast<char *>(p.seg_P) +
+                    (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * SegPFrag<DK, BF>::BYTES;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                SegPFrag<DK, BF>::put(dst, 16 * rt + 4 * lg + ii, col, S[rt][ii]);
+        return;
     }
+    float *dst = g == 0 ? segS + static_cast<size_t>(DK) * DV   // state entering segment 1
+                        : p.seg_R + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            dst[static_cast<size_t>(16 * rt + 4 * lg + ii) * ld + col] = S[rt][ii];
-}
-
-// K2s: start states of segments 2 .. nseg-1, S_{g+1} = P_g S_g + R_g in fp32. One
-// workgroup per (pair, 16 columns of S); wave w computes row tile w with fp32 matrix-core
-// products (A = rows of P_g straight from memory, B = S_g from LDS).
-template <int DK, int DV>
-__global__ __launch_bounds__(64 * (DK / 16)) void chunk_scan_kernel(ChunkParams p) {
-    constexpr int RT = DK / 16;
-    __shared__ __attribute__((aligned(16))) float sS[DK][16];
-    const int pair = blockIdx.x / (DV / 16), cbk = blockIdx.x % (DV / 16);
-    if (pair >= p.num_pairs) return;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int li = lane & 15, lg = lane >> 4;
-    const int nsa = p.nseg - 1;
-    float *Sp = p.seg_S + static_cast<size_t>(pair) * p.nseg * DK * DV;   // [nseg][DK][DV]
-    const int col = 16 * cbk + li;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        const int row = 16 * wave + 4 * lg + ii;
-        sS[row][li] = Sp[static_cast<size_t>(DK + row) * DV + col];
-    }
-    __syncthreads();
-    // step g needs P_g (this wave's row tile), R_g and S_g; the loads of step g + 1 are
-    // issued before the products of step g
-    auto load_step = [&](int g, f32x4 *a, f32x4 &r4) {
-        const float *P = p.seg_P + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DK;
-        const float *R = p.seg_R + (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * DK * DV;
-#pragma unroll
-        for (int kt = 0; kt < RT; ++kt)
-            a[kt] = *reinterpret_cast<const f32x4 *>(P + static_cast<size_t>(16 * wave + li) * DK +
-                                                     16 * kt + 4 * lg);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            r4[ii] = R[static_cast<size_t>(16 * wave + 4 * lg + ii) * DV + col];
-    };
-    f32x4 a[RT], an[RT], r4, rn4;
-    if (nsa > 1) load_step(1, a, r4);
-    for (int g = 1; g < nsa; ++g) {
-        if (g + 1 < nsa) load_step(g + 1, an, rn4);
-        __builtin_amdgcn_sched_barrier(0);   // the next step's loads are in flight
-        f32x4 acc = r4;
-#pragma unroll
-        for (int kt = 0; kt < RT; ++kt) {
-            f32x4 b;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) b[e] = sS[16 * kt + 4 * lg + e][li];
-            acc = mma_k16_f32(a[kt], b, acc);
-        }
-        __syncthreads();                     // every wave has read S_g
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int row = 16 * wave + 4 * lg + ii;
-            sS[row][li] = acc[ii];
-            Sp[static_cast<size_t>((g + 1) * DK + row) * DV + col] = acc[ii];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kt = 0; kt < RT; ++kt) a[kt] = an[kt];
-        r4 = rn4;
-    }
+            dst[static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = S[rt][ii];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1421,11 +1555,12 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // non-temporal stores.
 constexpr size_t kStreamRecordBytes = static_cast<size_t>(256) << 20;
 
-// fp32 segment buffers: start states [pair][nseg][d_k][d_v], transitions
-// [pair][nseg-2][d_k][d_k] and zero-start end states [pair][nseg-2][d_k][d_v]
+// Segment buffers: fp32 start states of segments 0 and 1 [pair][2][d_k][d_v], transitions
+// [pair][nseg-2] (d_k x d_k as matrix-core fragments, 4 bytes per element) and fp32
+// zero-start end states [pair][nseg-2][d_k][d_v]
 static void seg_area(const SegPlan &sp, int64_t pairs, int d_k, int d_v, size_t off[3],
                      size_t *total) {
-    const size_t nS = sp.nseg > 1 ? static_cast<size_t>(sp.nseg) : 0;
+    const size_t nS = sp.nseg > 1 ? 2 : 0;
     const size_t nPR = sp.nseg > 2 ? static_cast<size_t>(sp.nseg - 2) : 0;
     off[0] = 0;
     off[1] = off[0] + align256(pairs * nS * d_k * d_v * 4);
@@ -1469,9 +1604,8 @@ static int device_cu_count() {
 
 template <typename T, bool BF, int DK, int DV, int NW>
 static hipError_t launch_state(ChunkParams p, int64_t units, hipStream_t st) {
-    using SLy = StageLayout<DK, DV, BF>;
     p.nslices = DV / 16 / NW;
-    const size_t lds = SLy::lds_bytes(NW);
+    const size_t lds = CarryLayout<DK, DV, BF, NW>::LDS;
     auto kern = chunk_state_kernel<T, BF, DK, DV, NW>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1526,7 +1660,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     }
     const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
     if (p.nseg > 1 && p.num_pairs > 0) {
-        // segment pass, then the scan over segments
+        // segment pass
         using SGy = SegLayout<DK, DV, BF>;
         auto skern = chunk_seg_kernel<T, BF, DK, DV>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skern),
@@ -1536,9 +1670,6 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         const int64_t ua = static_cast<int64_t>(p.num_pairs) * (p.nseg - 1);
         const int64_t sblocks = (ua + 7) / 8 * 8 * SGy::GROUPS;
         hipLaunchKernelGGL(skern, dim3(sblocks), dim3(64 * (kSegWaves + kSegCopy)), SGy::LDS, st, p);
-        if (p.nseg > 2)
-            hipLaunchKernelGGL((chunk_scan_kernel<DK, DV>), dim3(p.num_pairs * (DV / 16)),
-                               dim3(64 * (DK / 16)), 0, st, p);
     }
     // K2: NW column slices per workgroup (each with a chain and an output wave, plus the
     // copy waves)

@@ -173,11 +173,12 @@ def test_workspace_size_formula(L):
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 256 + (16 + 5) * 2 * rec
     # a dense batch with few (sequence, head) pairs: the state pass is split into segments
     # (about 256 workgroups of two 16-column slices, at least 4 chunks per segment) and the
-    # workspace adds fp32 states entering each segment [pair][nseg][dk][dv], transitions
-    # [pair][nseg-2][dk][dk] and zero-start end states [pair][nseg-2][dk][dv]
+    # workspace adds fp32 states entering segments 0 and 1 [pair][2][dk][dv], transitions
+    # [pair][nseg-2] (dk x dk, 4 bytes per element) and zero-start end states
+    # [pair][nseg-2][dk][dv]
     def seg_bytes(pairs, nseg, dk, dv):
         a = lambda x: (x + 255) // 256 * 256       # noqa: E731
-        return (a(pairs * nseg * dk * dv * 4) + a(pairs * (nseg - 2) * dk * dk * 4) +
+        return (a(pairs * 2 * dk * dv * 4) + a(pairs * (nseg - 2) * dk * dk * 4) +
                 a(pairs * (nseg - 2) * dk * dv * 4))
     rec = (2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128 + 255) // 256 * 256
     d = Dims(1, 4096, 0, 16, 16, 128, 128, 1)       # 16 pairs x 64 chunks -> 4 segments

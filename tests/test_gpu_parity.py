@@ -184,9 +184,10 @@ def test_chunk_zero_initial_state_and_no_final_state():
 
 
 # Dense batches with few (sequence, head) pairs take the segmented state pass: the chunks
-# of each pair are split into segments that run concurrently (segment transitions, a scan
-# over segments, then every segment from its start state). These shapes give 4, 2, 4 and 8
-# segments (the workspace size test on the CPU pins that plan).
+# of each pair are split into segments that run concurrently (segment transitions, then
+# every segment from its start state, which segments after the second carry over the
+# transitions before them). These shapes give 4, 2, 4 and 8 segments (the workspace size
+# test on the CPU pins that plan).
 SEGMENTED = [
     (torch.bfloat16, 128, 128, 1, 1000, 1, 2, 0.1),
     (torch.bfloat16, 128, 128, 2, 640, 1, 3, 0.1),
