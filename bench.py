@@ -408,6 +408,61 @@ def profile_driver():
     print("profile driver done")
 
 
+def pmc_summary(fetch_dir, write_dir):
+    """Writes profiles/pmc_traffic.json from two `rocprofv3 --pmc` runs of --profile-driver
+    (FETCH_SIZE, then WRITE_SIZE; their counter_collection CSVs under the two directories).
+    Each counter is scaled by what it reads for the 256 MiB copy of the driver; the rows it
+    prints are the per-launch table of profiles/hbm_traffic_counters.md."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def load(d, ctr):
+        agg = defaultdict(list)
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == ctr:
+                        agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in agg.items()}
+
+    F, W = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copyk = [k for k in F if "copyBuffer" in k][0]
+    copy_kib = 256 * 1024
+    ff, wf = copy_kib / F[copyk][0], copy_kib / W[copyk][0]
+    print(f"calibration: FETCH_SIZE {F[copyk][0]:,.0f} KiB per 256 MiB copy -> x{ff:.2f}; "
+          f"WRITE_SIZE {W[copyk][0]:,.0f} KiB -> x{wf:.2f}")
+    ff, wf = round(ff, 1), round(wf, 1)
+    chunk, dec = {}, {}
+    for k, (fk, n) in F.items():
+        if "gdn2" not in k:
+            continue
+        wk = W.get(k, (0.0, 0))[0]
+        rb, wb = fk * ff * 1024, wk * wf * 1024
+        short = k.split("(")[0].replace("void gdn2::", "")
+        print(f"| {short} | {n} | {fk:,.0f} | {rb / 1e6:.1f} MB | {wk:,.0f} | {wb / 1e6:.1f} MB | "
+              f"{(rb + wb) / 1e6:.1f} MB |")
+        name = short.split("<")[0]
+        if name.startswith("chunk_"):
+            chunk[name] = int(rb + wb)
+        elif name == "recurrent_fwd_kernel":
+            key = ("decode_step_bf16state_n64_hv48" if "float, gdn2::bf16_t" in short
+                   else "decode_step_n64_hv48")
+            dec.setdefault(key, {"bytes_per_launch": int(rb + wb), "kernel": short})
+    out = {"_note": f"HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x{ff}) and "
+                    f"WRITE_SIZE (x{wf}); commands and calibration in hbm_traffic_counters.md",
+           "chunk_fwd_t4096": {"source_hash": source_hash("gdn2_chunk.hip", "gdn2_mfma.h",
+                                                          "gdn2_common.h"),
+                               "bytes_per_launch": sum(chunk.values()), "kernels": chunk}}
+    dsrc = source_hash("gdn2_decode.hip", "gdn2_common.h")
+    for key, rec in dec.items():
+        out[key] = {"source_hash": dsrc, **rec}
+    with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -422,7 +477,12 @@ def main():
                          "20 decode steps with an fp32 state and 20 with a bf16 state, and 3 "
                          "copies of 256 MiB (the copy calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/pmc_traffic.json from the two counter runs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(pass --gpus 1).", file=sys.stderr)
