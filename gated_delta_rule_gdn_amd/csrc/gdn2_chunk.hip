@@ -44,10 +44,12 @@ namespace gdn2 {
 template <bool BF> struct Op;
 template <> struct Op<true> {     // bf16 operands, K = 32 per fragment block
     using type = bf16_t;
+    using UTile = u32x2;              // one lane's part of a D-layout tile of U~ (4 x bf16)
     static constexpr int KT = 32, EPL = 8, E = 2;
 };
 template <> struct Op<false> {    // fp32 operands, K = 16 per fragment block
     using type = float;
+    using UTile = f32x4;
     static constexpr int KT = 16, EPL = 4, E = 4;
 };
 
@@ -1389,31 +1391,39 @@ __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(
         const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + SG::KG);
         const float *gc = reinterpret_cast<const float *>(cur + SG::GC);
         const char *ut = cur + SG::UT + (isP ? 0 : (v - SG::NP - rlo)) * SG::UTS;
-        u32x4 aw[4][NKD];
-        f32x4 U[4];
+        // every LDS operand of the chunk goes in flight first, in the order of use
+        u32x4 aw[4][NKD], ak[RT][NKC];
+        f32x4 U[4], g4[RT];
+        typename Op<BF>::UTile ub[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int kt = 0; kt < NKD; ++kt) aw[rt][kt] = wn[(rt * NKD + kt) * 64 + lane];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (!isP) {
-                if constexpr (BF) {
-                    const u32x2 u = reinterpret_cast<const u32x2 *>(ut + rt * R_::UT_TILE)[lane];
-                    U[rt] = f32x4{bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y)};
-                } else {
-                    U[rt] = reinterpret_cast<const f32x4 *>(ut + rt * R_::UT_TILE)[lane];
-                }
-            }
-        }
+        for (int rt = 0; rt < 4; ++rt)       // read for P slices too (discarded): no branch
+            ub[rt] = reinterpret_cast<const typename Op<BF>::UTile *>(ut + rt * R_::UT_TILE)[lane];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) g4[rt] = *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
+        __builtin_amdgcn_sched_barrier(0);
         u32x4 SB[NKD];
 #pragma unroll
         for (int kt = 0; kt < NKD; ++kt) {
             if constexpr (BF) SB[kt] = dpair_to_b32(S[2 * kt], S[2 * kt + 1]);
             else SB[kt] = __builtin_bit_cast(u32x4, S[kt]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            if constexpr (BF) {
+                U[rt] = f32x4{bf16_lo(ub[rt].x), bf16_hi(ub[rt].x), bf16_lo(ub[rt].y), bf16_hi(ub[rt].y)};
+            } else {
+                U[rt] = ub[rt];
+            }
+            if (isP) U[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
         for (int kt = 0; kt < NKD; ++kt)
 #pragma unroll
@@ -1422,13 +1432,8 @@ __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(
                 else U[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, aw[rt][kt]), S[kt], U[rt]);
             }
         __builtin_amdgcn_sched_barrier(0);
-        u32x4 ak[RT][NKC];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
+        for (int rt = 0; rt < RT; ++rt) S[rt] *= g4[rt];
         u32x4 UB[NKC];
 #pragma unroll
         for (int kt = 0; kt < NKC; ++kt) {
