@@ -233,6 +233,45 @@ def bench_recurrent(T, state_dtype, calls, seed, traffic_key=None):
     return res
 
 
+def bench_gate_variants(steps, warmup, seed=9):
+    """The timed chunk shape (bf16, B=1 T=4096 H=16 d=128) run as KDA and as FG2-GDN+ through
+    the gate mappings (gdn2_map_gates, then the GDN-2 chunked forward), with the mapping pass
+    timed on its own. The mapping is an elementwise HBM pass: its algorithmic bytes are the
+    gate tensors it reads and the GDN-2 tensors it writes."""
+    wl = inputs.CHUNK_BF16_T4096
+    res = {}
+    stream = torch.cuda.current_stream()
+    for mode in ("kda", "fg2+"):
+        x = inputs.variant_inputs(mode, wl.dtype, 1, wl.seqlen, wl.h_k, wl.h_v, wl.d_k, wl.d_v,
+                                  seed)
+        d = {n: t.cuda() for n, t in x.items()}
+        ws = torch.empty(g.chunk_fwd_workspace_bytes(1, wl.seqlen, wl.h_k, wl.h_v, wl.d_k,
+                                                     wl.d_v, wl.dtype),
+                         dtype=torch.uint8, device="cuda")
+
+        def mapping():
+            return g.map_gates(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                               d.get("beta_v"))
+
+        def whole():
+            g.chunk_fwd(*mapping(), S0=d["S"], workspace=ws)
+
+        for _ in range(warmup):
+            whole()
+        t_map = time_region(mapping, steps, stream)
+        t_all = time_region(whole, steps, stream)
+        T, H, dk, dv, e = wl.seqlen, wl.h_v, wl.d_k, wl.d_v, 2
+        if mode == "kda":
+            nbytes = T * H * e + T * H * (dk + dv) * e          # beta in; b, w out
+        else:                                                   # beta, beta_v, k in; k', b, w out
+            nbytes = T * H * (dk + dv) * e + T * wl.h_k * dk * e + T * H * (2 * dk + dv) * e
+        res[mode] = {"workload": f"{wl.name}_{mode}", "us_per_call": t_all * 1e6,
+                     "tokens_per_s": T / t_all, "map_us": t_map * 1e6,
+                     "map_alg_bytes": nbytes, "map_hbm_frac": nbytes / t_map / 1e9 / HBM_PEAK_GBPS}
+        del d, ws
+    return res
+
+
 def bench_fused(steps, warmup, seed=8):
     """The timed chunk workload and the decode step with the fusions of the burn-gdn2
     "Architecture" diagram turned on (q/k L2-norm before the recurrence, SiLU-gated RMS norm
@@ -550,6 +589,7 @@ def main():
                         "config": {"workload": dwl.name}, "roofline": dec["roofline"]})
     if args.only == "all" and not args.no_other_workloads:
         out["fused_qkl2norm_gatednorm"] = bench_fused(max(10, args.steps // 2), 3)
+        out["gate_variants"] = bench_gate_variants(max(10, args.steps // 4), 3)
     if args.only in ("chunk", "all") and not args.no_other_workloads:
         out["other_chunk_workloads"] = [
             bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed)

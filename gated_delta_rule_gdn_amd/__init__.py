@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.gdn2_recurrent_fwd.argtypes = [vp] * 7 + [i32, vp, i32, vp, dp, fp, vp]
         L.gdn2_check_cu_seqlens.restype = i32
         L.gdn2_check_cu_seqlens.argtypes = [vp, i32, i32]
+        L.gdn2_map_gates.restype = i32
+        L.gdn2_map_gates.argtypes = [i32, dp] + [vp] * 13
         _lib = L
     return _lib
 
@@ -293,6 +295,97 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
                                   stream)
     _raise_on(st)
     return o
+
+
+# gdn2_gate_mode: other delta-rule variants as GDN-2 inputs (include/gdn2.h)
+GATE_MODES = {"kda": 1, "fg2": 2, "fg2+": 3, "gdn": 4}
+
+
+def map_gates(mode: str, q, k, v, log_alpha, beta, beta_v=None):
+    """Maps the inputs of a delta-rule variant onto GDN-2 inputs, on the GPU (gdn2_map_gates).
+
+    Leading dims L are those of q ([*L, H_k, d_k]: [B,T], [1,T] packed or [N,T] recurrent).
+      "kda"   beta [*L, H_v]; log_alpha [*L, H_v, d_k]:  b = w = beta
+      "gdn"   beta [*L, H_v]; log_alpha [*L, H_v] (scalar decay): broadcast over d_k
+      "fg2"   beta [*L, H_v, d_k], d_v = d_k: k' = sqrt(beta) k, v' = sqrt(beta) v, b = w = 1
+      "fg2+"  beta [*L, H_v, d_k], beta_v [*L, H_v, d_v]: k' = sqrt(beta) k, b = 1,
+              w = sqrt(beta_v)
+    Returns (q', k', v', log_alpha', b, w) for chunk_fwd / recurrent_fwd. In the FG2 modes k'
+    (and q', when H_v > H_k) is per value head.
+    """
+    if mode not in GATE_MODES:
+        raise ValueError(f"mode must be one of {sorted(GATE_MODES)}")
+    code = GATE_MODES[mode]
+    dev = q.device
+    if q.dim() < 3 or k.shape != q.shape:
+        raise ValueError("q and k must both be [*L, H_k, d_k]")
+    lead, Hk, dk = tuple(q.shape[:-2]), q.shape[-2], q.shape[-1]
+    if v.dim() != q.dim() or tuple(v.shape[:-2]) != lead:
+        raise ValueError("v must be [*L, H_v, d_v]")
+    Hv, dv = v.shape[-2], v.shape[-1]
+    scalar = mode in ("kda", "gdn")
+    want_beta = lead + ((Hv,) if scalar else (Hv, dk))
+    want_la = lead + ((Hv,) if mode == "gdn" else (Hv, dk))
+    if tuple(beta.shape) != want_beta:
+        raise ValueError(f"beta must be {list(want_beta)} for mode {mode!r}")
+    if tuple(log_alpha.shape) != want_la:
+        raise ValueError(f"log_alpha must be {list(want_la)} for mode {mode!r}")
+    if mode == "fg2+":
+        if beta_v is None or tuple(beta_v.shape) != lead + (Hv, dv):
+            raise ValueError(f"beta_v must be {list(lead + (Hv, dv))} for mode 'fg2+'")
+    elif beta_v is not None:
+        raise ValueError("beta_v is for mode 'fg2+' only")
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta),
+                    ("beta_v", beta_v)):
+        if t is None:
+            continue
+        _need_gpu(name, t, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    rows = 1
+    for x in lead:
+        rows *= x
+    dims = Dims(rows, 1, 0, Hk, Hv, dk, dv, _dtype_code(q.dtype))
+    new = lambda *shape: torch.empty(*shape, dtype=q.dtype, device=dev)  # noqa: E731
+    b, w = new(*lead, Hv, dk), new(*lead, Hv, dv)
+    q2, k2, v2, la2 = q, k, v, log_alpha
+    if mode == "gdn":
+        la2 = new(*lead, Hv, dk)
+    if mode in ("fg2", "fg2+"):
+        k2 = new(*lead, Hv, dk)
+        if Hv > Hk:
+            q2 = new(*lead, Hv, dk)
+    if mode == "fg2":
+        v2 = new(*lead, Hv, dv)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib().gdn2_map_gates(code, ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(log_alpha), _ptr(beta), _ptr(beta_v),
+                              _ptr(q2) if q2 is not q else None, _ptr(k2) if k2 is not k else None,
+                              _ptr(v2) if v2 is not v else None,
+                              _ptr(la2) if la2 is not log_alpha else None, _ptr(b), _ptr(w),
+                              stream)
+    _raise_on(st)
+    return q2, k2, v2, la2, b, w
+
+
+def _fg2_fusion_check(mode, kw):
+    if mode in ("fg2", "fg2+") and (kw.get("qk_l2norm") or kw.get("conv_weight") is not None):
+        raise ValueError("the fused q/k L2-norm and short convolution would act on the scaled "
+                         "keys of the FG2 modes; normalise or convolve q and k before mapping")
+
+
+def gated_chunk_fwd(mode: str, q, k, v, log_alpha, beta, beta_v=None, **kw):
+    """chunk_fwd of a delta-rule variant (see map_gates): maps the inputs, then runs the
+    GDN-2 chunked forward. Keyword arguments go to chunk_fwd."""
+    _fg2_fusion_check(mode, kw)
+    return chunk_fwd(*map_gates(mode, q, k, v, log_alpha, beta, beta_v), **kw)
+
+
+def gated_recurrent_fwd(mode: str, q, k, v, log_alpha, beta, state, beta_v=None, **kw):
+    """recurrent_fwd of a delta-rule variant (see map_gates) against a state pool. Keyword
+    arguments go to recurrent_fwd."""
+    _fg2_fusion_check(mode, kw)
+    return recurrent_fwd(*map_gates(mode, q, k, v, log_alpha, beta, beta_v), state, **kw)
 
 
 def abi_version() -> int:

@@ -240,6 +240,62 @@ gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v,
                             num_slots, o, dims, fusion, stream, "gdn2_recurrent_fwd launch");
 }
 
+gdn2_status gdn2_map_gates(int32_t mode, const gdn2_dims *dims, const void *q, const void *k,
+                           const void *v, const void *log_alpha, const void *beta,
+                           const void *beta_v, void *q_out, void *k_out, void *v_out,
+                           void *log_alpha_out, void *b_out, void *w_out, void *stream) {
+    if (!dims) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
+    gdn2_status st = check_heads(dims);
+    if (st != GDN2_OK) return st;
+    if (mode != GDN2_GATES_KDA && mode != GDN2_GATES_FG2 && mode != GDN2_GATES_FG2_PLUS &&
+        mode != GDN2_GATES_GDN)
+        return fail(GDN2_ERR_UNSUPPORTED, "mode must be a gdn2_gate_mode");
+    const bool fg2 = mode == GDN2_GATES_FG2 || mode == GDN2_GATES_FG2_PLUS;
+    if (mode == GDN2_GATES_FG2 && dims->d_v != dims->d_k)
+        return fail(GDN2_ERR_BAD_SHAPE, "GDN2_GATES_FG2 scales v by sqrt(beta): d_v must equal d_k");
+    if (dims->batch < 0 || dims->seqlen < 0) return fail(GDN2_ERR_BAD_SHAPE, "batch and seqlen must be >= 0");
+    const int64_t rows = static_cast<int64_t>(dims->batch) * dims->seqlen;
+    const int64_t hd = static_cast<int64_t>(dims->h_v) * (dims->d_k > dims->d_v ? dims->d_k : dims->d_v);
+    if (rows > INT32_MAX || rows * hd > kMaxElems) return fail(GDN2_ERR_BAD_SHAPE, "tensors too large");
+    if (rows == 0) {
+        g_last_error[0] = '\0';
+        return GDN2_OK;
+    }
+    const bool share = dims->h_v > dims->h_k;       // value heads share key heads
+    if (!beta || !b_out || !w_out) return fail(GDN2_ERR_NULL_ARG, "beta, b_out and w_out are required");
+    if (mode == GDN2_GATES_GDN && (!log_alpha || !log_alpha_out))
+        return fail(GDN2_ERR_NULL_ARG, "GDN2_GATES_GDN needs log_alpha and log_alpha_out");
+    if (fg2 && (!k || !k_out)) return fail(GDN2_ERR_NULL_ARG, "the FG2 modes need k and k_out");
+    if (mode == GDN2_GATES_FG2 && (!v || !v_out)) return fail(GDN2_ERR_NULL_ARG, "GDN2_GATES_FG2 needs v and v_out");
+    if (mode == GDN2_GATES_FG2_PLUS && !beta_v) return fail(GDN2_ERR_NULL_ARG, "GDN2_GATES_FG2_PLUS needs beta_v");
+    if (fg2 && share && !q_out)
+        return fail(GDN2_ERR_NULL_ARG, "the FG2 modes need q_out when value heads share key heads");
+    if (fg2 && q_out && !q) return fail(GDN2_ERR_NULL_ARG, "q_out needs q");
+    // the outputs this mode writes must not overlap each other or any input
+    const void *ins[6] = {q, k, v, log_alpha, beta, beta_v};
+    void *outs[6] = {fg2 ? q_out : nullptr, fg2 ? k_out : nullptr,
+                     mode == GDN2_GATES_FG2 ? v_out : nullptr,
+                     mode == GDN2_GATES_GDN ? log_alpha_out : nullptr, b_out, w_out};
+    for (int i = 0; i < 6; ++i) {
+        if (!outs[i]) continue;
+        for (int j = 0; j < 6; ++j)
+            if (ins[j] && outs[i] == ins[j]) return fail(GDN2_ERR_BAD_SHAPE, "an output aliases an input");
+        for (int j = i + 1; j < 6; ++j)
+            if (outs[i] == outs[j]) return fail(GDN2_ERR_BAD_SHAPE, "two outputs are the same buffer");
+    }
+    gdn2::GateArgs a;
+    a.mode = mode;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.beta_v = beta_v;
+    a.q_out = fg2 ? q_out : nullptr; a.k_out = k_out; a.v_out = v_out;
+    a.log_alpha_out = log_alpha_out; a.b_out = b_out; a.w_out = w_out;
+    a.rows = rows; a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
+    a.bf16 = dims->dtype == GDN2_BF16;
+    const hipError_t e = gdn2::launch_map_gates(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "gdn2_map_gates launch");
+    g_last_error[0] = '\0';
+    return GDN2_OK;
+}
+
 gdn2_status gdn2_check_cu_seqlens(const int32_t *cu, int32_t num_seqs, int32_t total_tokens) {
     if (!cu) return fail(GDN2_ERR_NULL_ARG, "cu_seqlens is NULL");
     if (num_seqs < 1) return fail(GDN2_ERR_BAD_SHAPE, "num_seqs must be >= 1");

@@ -53,7 +53,20 @@ size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d
                              bool bf16, bool packed);
 bool chunk_dims_built(int d_k, int d_v, bool bf16);
 
+// Gate mappings of other delta-rule variants onto the GDN-2 inputs (gdn2_map_gates).
+enum GateMode { GATES_KDA = 1, GATES_FG2 = 2, GATES_FG2_PLUS = 3, GATES_GDN = 4 };
+
+struct GateArgs {
+    int mode;
+    const void *q, *k, *v, *log_alpha, *beta, *beta_v;
+    void *q_out, *k_out, *v_out, *log_alpha_out, *b_out, *w_out;
+    int64_t rows;            // tokens: batch x seqlen
+    int h_k, h_v, d_k, d_v;
+    bool bf16;
+};
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_map_gates(const GateArgs &a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st);
 
 }  // namespace gdn2

@@ -224,3 +224,26 @@ def small_chunk(dtype=torch.float32, batch=1, seqlen=100, h_k=2, h_v=2, d_k=64, 
 
 def with_dtype(wl, dtype):
     return replace(wl, dtype=dtype)
+
+
+def variant_inputs(mode: str, dtype, N: int, T: int, h_k: int, h_v: int, d_k: int, d_v: int,
+                   seed: int, s0_std: float = 0.1) -> dict:
+    """Inputs of a delta-rule variant (host tensors, leading dims [N, T]): q, k unit rows;
+    v normal; log_alpha = -softplus(normal) per channel ([N,T,H_v,d_k]) or, for "gdn", per
+    head ([N,T,H_v]); beta = sigmoid(normal) per head ("kda", "gdn": [N,T,H_v]) or per key
+    channel ("fg2", "fg2+": [N,T,H_v,d_k]); beta_v = sigmoid(normal) [N,T,H_v,d_v] for "fg2+";
+    S fp32 [N,H_v,d_k,d_v] normal * s0_std."""
+    rng = _rng(seed)
+    lead = (N, T)
+    q = _unit_rows(_normal(rng, lead + (h_k, d_k)))
+    k = _unit_rows(_normal(rng, lead + (h_k, d_k)))
+    v = _normal(rng, lead + (h_v, d_v))
+    la_shape = lead + ((h_v,) if mode == "gdn" else (h_v, d_k))
+    la = -_softplus(_normal(rng, la_shape))
+    beta = _sigmoid(_normal(rng, lead + ((h_v,) if mode in ("kda", "gdn") else (h_v, d_k))))
+    out = {"q": q, "k": k, "v": v, "log_alpha": la, "beta": beta}
+    if mode == "fg2+":
+        out["beta_v"] = _sigmoid(_normal(rng, lead + (h_v, d_v)))
+    out = {n: _cast(x, dtype) for n, x in out.items()}
+    out["S"] = torch.from_numpy(_normal(rng, (N, h_v, d_k, d_v)) * np.float32(s0_std))
+    return out

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 2
+#define GDN2_ABI_VERSION 3
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -230,6 +230,49 @@ gdn2_status gdn2_recurrent_fwd(const void *q, const void *k, const void *v,
                                void *state, int32_t state_dtype, const int32_t *state_idx,
                                int32_t num_slots, void *o, const gdn2_dims *dims,
                                const gdn2_fusion *fusion, void *stream);
+
+/*
+ * Gate mappings: other members of the gated delta-rule family as GDN-2 inputs. The
+ * burn-gdn2 page ("Architecture") introduces the channel-wise b_t and w_t as the
+ * replacement of the scalar gate of Kimi Delta Attention; the FG2-GDN page (section 2)
+ * writes its update with keys and values scaled by sqrt(beta). Each mode below is exactly
+ * GDN-2 with mapped inputs (per value head h, key head h / (h_v / h_k)):
+ *
+ *   GDN2_GATES_KDA       S = (I - beta k k^T) diag(alpha) S + beta k v^T
+ *                        beta  [rows, h_v] (one value per token and value head)
+ *                        -> b_out [rows, h_v, d_k] = beta, w_out [rows, h_v, d_v] = beta;
+ *                        q, k, v and log_alpha are used as they are
+ *   GDN2_GATES_GDN       as KDA with a scalar decay: log_alpha [rows, h_v]
+ *                        -> also log_alpha_out [rows, h_v, d_k] = log_alpha
+ *   GDN2_GATES_FG2       S = (I - k~ k~^T) diag(alpha) S + k~ v~^T, k~ = sqrt(beta) . k,
+ *                        v~ = sqrt(beta) . v; beta [rows, h_v, d_k]; needs d_v = d_k
+ *                        -> k_out [rows, h_v, d_k] = k~, v_out [rows, h_v, d_v] = v~,
+ *                           b_out = w_out = 1
+ *   GDN2_GATES_FG2_PLUS  as FG2 with the erase scale beta [rows, h_v, d_k] on the keys and
+ *                        the write scale beta_v [rows, h_v, d_v] on the values:
+ *                        S = (I - k~ k~^T) diag(alpha) S + k~ (sqrt(beta_v) . v)^T
+ *                        -> k_out = sqrt(beta) . k, b_out = 1, w_out = sqrt(beta_v);
+ *                           v is used as it is
+ *
+ * rows = dims->batch x dims->seqlen tokens in the layout of the call that follows (dense,
+ * packed or recurrent); dims is that call's dims. In the FG2 modes k_out is per value head,
+ * so the follow-up call takes h_k = h_v, with q_out [rows, h_v, d_k] (q replicated per
+ * value head) in place of q; q_out is required when h_v > h_k and may be NULL (q used as it
+ * is) when h_v = h_k. All tensors are in dims->dtype. Pointers a mode does not use are
+ * ignored. The outputs a mode writes must not alias its inputs or each other. An
+ * elementwise pass on `stream` (HBM-bound); nothing else is computed.
+ */
+typedef enum gdn2_gate_mode {
+    GDN2_GATES_KDA = 1,
+    GDN2_GATES_FG2 = 2,
+    GDN2_GATES_FG2_PLUS = 3,
+    GDN2_GATES_GDN = 4
+} gdn2_gate_mode;
+
+gdn2_status gdn2_map_gates(int32_t mode, const gdn2_dims *dims, const void *q, const void *k,
+                           const void *v, const void *log_alpha, const void *beta,
+                           const void *beta_v, void *q_out, void *k_out, void *v_out,
+                           void *log_alpha_out, void *b_out, void *w_out, void *stream);
 
 /*
  * Host helper: checks a HOST copy of cu_seqlens (N+1 entries) against total tokens T.

@@ -20,6 +20,10 @@ Two independent evaluations of the method live here:
 * ``recurrent_bwd`` -- the gradient of ``recurrent`` with respect to every input and the
   initial state, by the token-by-token adjoint of the recurrence (chain rule through the
   decay, erase, write and read-out steps, in reverse), fp64, in the same C file.
+* ``variant_sequence`` / ``variant`` -- the update rules of the neighbouring delta-rule
+  models the pages name (the scalar-gate KDA that the "Architecture" section says b and w
+  replace, a scalar-decay GDN, and FG2-GDN and FG2-GDN+ of the FG2-GDN summary, section 2),
+  each written from its own formula in numpy fp64.
 * ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
   mode) and on the FG^2-GDN summary (section 2C, DPLR structure and the WY
   representation), in numpy fp64. It exists to pin the recurrence: the two are
@@ -420,6 +424,61 @@ def chunked(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size=64):
                                       la[s:e, h], b[s:e, h], S_init, chunk_size)
             o[s:e, h] = on
             S_T[n, h] = Sn
+    return o, S_T
+
+
+def variant_sequence(mode, q, k, v, log_alpha, beta, S0, beta_v=None):
+    """One (sequence, value head) pair of another gated delta-rule variant, fp64, token by
+    token from that variant's own update rule (not through the GDN-2 form):
+
+    * ``"kda"`` (the scalar-gate model the burn-gdn2 "Architecture" section says b and w
+      replace): ``S <- (I - beta k k^T) diag(alpha) S + beta k v^T``, beta [T] scalar;
+    * ``"gdn"``: the same with a scalar decay, ``log_alpha`` [T];
+    * ``"fg2"`` (FG2-GDN page, section 2A): ``k~ = sqrt(beta) k``, ``v~ = sqrt(beta) v`` with
+      beta [T, d_k] (d_v = d_k), ``S <- (I - k~ k~^T) diag(alpha) S + k~ v~^T``;
+    * ``"fg2+"`` (section 2B): as fg2 with ``v~ = sqrt(beta_v) v``, beta_v [T, d_v].
+
+    q, k [T, d_k]; v [T, d_v]; log_alpha [T, d_k] (or [T]); S0 [d_k, d_v]. The output reads
+    the updated state, ``o_t = S_t^T q_t``. Returns (o [T, d_v], S_T) fp64.
+    """
+    q, k, v, la, beta = (_f64(x) for x in (q, k, v, log_alpha, beta))
+    bv = None if beta_v is None else _f64(beta_v)
+    S = _f64(S0).copy()
+    T, d_v = v.shape
+    o = np.zeros((T, d_v))
+    for t in range(T):
+        a = np.exp(la[t])
+        Sp = (a[:, None] * S) if np.ndim(a) else a * S
+        if mode in ("kda", "gdn"):
+            kk, vv, bt = k[t], v[t], beta[t]
+            S = Sp - bt * np.outer(kk, kk @ Sp) + bt * np.outer(kk, vv)
+        elif mode in ("fg2", "fg2+"):
+            kk = np.sqrt(beta[t]) * k[t]
+            vv = (np.sqrt(beta[t]) if mode == "fg2" else np.sqrt(bv[t])) * v[t]
+            S = Sp - np.outer(kk, kk @ Sp) + np.outer(kk, vv)
+        else:
+            raise ValueError(f"unknown mode {mode!r}")
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def variant(mode, q, k, v, log_alpha, beta, S0=None, beta_v=None, pairs=None):
+    """``variant_sequence`` over every (sequence, value head) pair of [N, T, ...] inputs
+    (value head h reads key head h // (H_v // H_k)). q, k [N,T,H_k,d_k]; v [N,T,H_v,d_v];
+    log_alpha and beta per value head as in ``variant_sequence``; S0 [N,H_v,d_k,d_v] or None.
+    Returns (o [N,T,H_v,d_v], S_T [N,H_v,d_k,d_v]) fp64 (NaN outside ``pairs``)."""
+    q, k, v = (np.asarray(x) for x in (q, k, v))
+    N, T, H_k, d_k = k.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    G = H_v // H_k
+    o = np.full((N, T, H_v, d_v), np.nan)
+    S_T = np.full((N, H_v, d_k, d_v), np.nan)
+    for n, h in (pairs or [(n, h) for n in range(N) for h in range(H_v)]):
+        S_init = np.zeros((d_k, d_v)) if S0 is None else np.asarray(S0)[n, h]
+        o[n, :, h], S_T[n, h] = variant_sequence(
+            mode, q[n, :, h // G], k[n, :, h // G], v[n, :, h], np.asarray(log_alpha)[n, :, h],
+            np.asarray(beta)[n, :, h], S_init,
+            None if beta_v is None else np.asarray(beta_v)[n, :, h])
     return o, S_T
 
 

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn2_abi_version() == 2
+    assert L.gdn2_abi_version() == 3
     assert L.gdn2_status_string(0) == b"ok"
     assert b"workspace" in L.gdn2_status_string(4)
     assert L.gdn2_status_string(99) == b"unknown status"
@@ -217,3 +217,30 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 1, 64)
     with pytest.raises(ValueError, match="GPU"):
         g.chunk_fwd(x, x, x, x, x, x)
+
+
+def gates(L, mode, dims, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, beta_v=FAKE, q_out=None,
+          k_out=None, v_out=None, la_out=None, b_out=None, w_out=None):
+    return L.gdn2_map_gates(mode, None if dims is None else ctypes.byref(dims), q, k, v, la,
+                            beta, beta_v, q_out, k_out, v_out, la_out, b_out, w_out, None)
+
+
+def test_map_gates_validation(L):
+    """Every call here stops at host validation (each lacks exactly one requirement)."""
+    P = [ctypes.c_void_p(0x2000 + 0x100 * i) for i in range(6)]    # distinct output pointers
+    d = Dims(2, 10, 0, 2, 4, 64, 64, 1)
+    assert gates(L, 1, None) == 1                                     # NULL dims
+    assert gates(L, 0, d) == 3 and gates(L, 5, d) == 3                # not a gate mode
+    assert gates(L, 1, Dims(2, 10, 0, 2, 4, 96, 64, 1)) == 3          # head dim not built
+    assert gates(L, 1, Dims(2, 10, 0, 3, 4, 64, 64, 1)) == 2          # h_v % h_k != 0
+    assert gates(L, 1, Dims(-1, 10, 0, 2, 4, 64, 64, 1)) == 2         # negative batch
+    assert gates(L, 1, d, b_out=P[0]) == 1                            # KDA: w_out missing
+    assert gates(L, 1, d, beta=None, b_out=P[0], w_out=P[1]) == 1     # KDA: beta missing
+    assert gates(L, 4, d, b_out=P[0], w_out=P[1]) == 1                # GDN: log_alpha_out
+    assert gates(L, 2, Dims(2, 10, 0, 2, 4, 128, 64, 1)) == 2         # FG2 needs d_v = d_k
+    assert gates(L, 2, d, q_out=P[0], v_out=P[2], b_out=P[3], w_out=P[4]) == 1   # k_out
+    assert gates(L, 2, d, k_out=P[1], v_out=P[2], b_out=P[3], w_out=P[4]) == 1   # q_out: h_v > h_k
+    assert gates(L, 3, d, beta_v=None, q_out=P[0], k_out=P[1], b_out=P[3], w_out=P[4]) == 1
+    assert gates(L, 1, d, b_out=FAKE, w_out=P[1]) == 2                # b_out aliases an input
+    assert gates(L, 1, d, b_out=P[0], w_out=P[0]) == 2                # two outputs alike
+    assert gates(L, 1, Dims(0, 10, 0, 2, 4, 64, 64, 1)) == 0          # no tokens: nothing to do

@@ -1,0 +1,104 @@
+"""GPU parity of the delta-rule variants run through the gate mappings (gdn2_map_gates, then
+the GDN-2 chunked forward or recurrent forward) against the oracle's direct update rules of
+those variants (oracle.variant: KDA, scalar-decay GDN, FG2-GDN, FG2-GDN+).
+
+Gate (relative L2 per output tensor): 1e-4 for fp32 inputs, 2e-2 for bf16 inputs, on o and
+on the final states. In bf16 the mapped keys and values of the FG2 modes are rounded to
+bf16 once more; the error this adds is far inside the gate.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gated_delta_rule_gdn_amd as g
+from gated_delta_rule_gdn_amd import inputs
+from gpu_common import TOL, np64
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["kda", "gdn", "fg2", "fg2+"]
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g.lib()
+
+
+def oracle_run(mode, x):
+    f = {n: np64(t) for n, t in x.items()}
+    return oracle.variant(mode, f["q"], f["k"], f["v"], f["log_alpha"], f["beta"], S0=f["S"],
+                          beta_v=f.get("beta_v"))
+
+
+def shapes(dtype, mode):
+    if dtype == torch.float32:
+        return 64, 64                     # the fp32 chunked forward is built for 64 x 64
+    return (128, 128) if mode == "fg2" else (128, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("mode", MODES)
+def test_chunk_forward_of_variants(mode, dtype):
+    dk, dv = shapes(dtype, mode)
+    x = inputs.variant_inputs(mode, dtype, 2, 150, 2, 4, dk, dv, seed=80 + MODES.index(mode))
+    d = {n: t.cuda() for n, t in x.items()}
+    o, S_T = g.gated_chunk_fwd(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                               beta_v=d.get("beta_v"), S0=d["S"])
+    torch.cuda.synchronize()
+    o_r, S_r = oracle_run(mode, x)
+    eo, es = oracle.rel_l2(np64(o), o_r), oracle.rel_l2(np64(S_T), S_r)
+    print(f"[parity] chunk {mode} {dtype} {dk}x{dv}: o={eo:.2e} S_T={es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("mode", MODES)
+def test_recurrent_forward_of_variants(mode, dtype):
+    dk, dv = (128, 128) if mode == "fg2" else (128, 64)
+    x = inputs.variant_inputs(mode, dtype, 3, 5, 2, 6, dk, dv, seed=90 + MODES.index(mode))
+    d = {n: t.cuda() for n, t in x.items()}
+    state = d["S"].clone()
+    o = g.gated_recurrent_fwd(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], state,
+                              beta_v=d.get("beta_v"))
+    torch.cuda.synchronize()
+    o_r, S_r = oracle_run(mode, x)
+    eo, es = oracle.rel_l2(np64(o), o_r), oracle.rel_l2(np64(state), S_r)
+    print(f"[parity] recurrent {mode} {dtype} {dk}x{dv}: o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_mapped_inputs_are_the_gdn2_form():
+    """The mapping itself, element by element: KDA broadcasts beta into b and w; FG2+ scales
+    the keys by sqrt(beta) per value head and puts sqrt(beta_v) in w (fp32: exact up to the
+    rounding of the square root and one product)."""
+    x = inputs.variant_inputs("fg2+", torch.float32, 2, 7, 2, 4, 64, 128, seed=7)
+    d = {n: t.cuda() for n, t in x.items()}
+    q2, k2, v2, la2, b, w = g.map_gates("fg2+", d["q"], d["k"], d["v"], d["log_alpha"],
+                                        d["beta"], d["beta_v"])
+    torch.cuda.synchronize()
+    G = 2
+    kq = np64(x["k"]).repeat(G, axis=2)
+    assert np.allclose(np64(k2), np.sqrt(np64(x["beta"])) * kq, rtol=1e-6, atol=0)
+    assert np.array_equal(np64(q2), np64(x["q"]).repeat(G, axis=2))
+    assert np.all(np64(b) == 1.0)
+    assert np.allclose(np64(w), np.sqrt(np64(x["beta_v"])), rtol=1e-6, atol=0)
+    assert v2.data_ptr() == d["v"].data_ptr() and la2.data_ptr() == d["log_alpha"].data_ptr()
+    y = inputs.variant_inputs("kda", torch.bfloat16, 1, 9, 1, 3, 128, 64, seed=8)
+    e = {n: t.cuda() for n, t in y.items()}
+    _, _, _, _, b, w = g.map_gates("kda", e["q"], e["k"], e["v"], e["log_alpha"], e["beta"])
+    torch.cuda.synchronize()
+    beta = np64(y["beta"])
+    assert np.array_equal(np64(b), np.broadcast_to(beta[..., None], b.shape))
+    assert np.array_equal(np64(w), np.broadcast_to(beta[..., None], w.shape))
+
+
+def test_fg2_rejects_unequal_head_dims_and_fused_key_stages():
+    x = inputs.variant_inputs("fg2", torch.bfloat16, 1, 4, 1, 1, 128, 64, seed=9)
+    d = {n: t.cuda() for n, t in x.items()}
+    with pytest.raises(g.GDN2Error):
+        g.map_gates("fg2", d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
+    with pytest.raises(ValueError):
+        g.gated_chunk_fwd("fg2+", d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                          beta_v=torch.ones_like(d["v"]), qk_l2norm=True)

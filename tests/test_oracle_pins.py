@@ -535,3 +535,91 @@ def test_recurrent_bwd_matches_torch_autograd_across_checkpoints():
     for n, gname in pairs:
         assert np.allclose(gr[gname][:, 0], t[n].grad.numpy(), rtol=1e-9, atol=1e-10), n
     assert np.allclose(gr["dS0"][0, 0], S_in.grad.numpy(), rtol=1e-9, atol=1e-10)
+
+
+# ---- variant rules (oracle.variant_sequence): KDA, scalar-decay GDN, FG2-GDN, FG2-GDN+ ---
+
+def variant_case(rng, T, dk, dv, mode):
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    la = -np.logaddexp(0.0, rng.standard_normal((T,) if mode == "gdn" else (T, dk)))
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x))  # noqa: E731
+    beta = sig(rng.standard_normal((T,) if mode in ("kda", "gdn") else (T, dk)))
+    beta_v = sig(rng.standard_normal((T, dv))) if mode == "fg2+" else None
+    return q, k, v, la, beta, beta_v
+
+
+@pytest.mark.parametrize("mode", ["kda", "gdn", "fg2", "fg2+"])
+def test_variant_rules_match_explicit_matrices(mode):
+    """Each variant's update as explicit d_k x d_k matrices: (I - k~ e~^T) D S + k~ u~^T with
+    (KDA, GDN) e~ = beta k, k~ = k, u~ = beta v; (FG2) k~ = e~ = sqrt(beta) k, u~ = sqrt(beta) v;
+    (FG2+) k~ = e~ = sqrt(beta) k, u~ = sqrt(beta_v) v."""
+    rng = np.random.default_rng(31)
+    T, dk = 9, 5
+    dv = dk if mode == "fg2" else 3
+    q, k, v, la, beta, beta_v = variant_case(rng, T, dk, dv, mode)
+    S0 = rng.standard_normal((dk, dv))
+    o, ST = oracle.variant_sequence(mode, q, k, v, la, beta, S0, beta_v)
+    S = S0.copy()
+    for t in range(T):
+        D = np.diag(np.exp(la[t]) * np.ones(dk))
+        if mode in ("kda", "gdn"):
+            kt, et, ut = k[t], beta[t] * k[t], beta[t] * v[t]
+        else:
+            kt = et = np.sqrt(beta[t]) * k[t]
+            ut = (np.sqrt(beta[t]) if mode == "fg2" else np.sqrt(beta_v[t])) * v[t]
+        S = (np.eye(dk) - np.outer(kt, et)) @ D @ S + np.outer(kt, ut)
+        assert close(o[t], S.T @ q[t])
+    assert close(ST, S)
+
+
+def test_variant_kda_exact_retrieval():
+    """alpha = 1, beta = 1, unit keys: each token's key retrieves its value, k_t^T S_t = v_t."""
+    rng = np.random.default_rng(32)
+    T, dk, dv = 12, 6, 4
+    q, k, v, _, _, _ = variant_case(rng, T, dk, dv, "kda")
+    for t in range(1, T + 1):
+        _, S = oracle.variant_sequence("kda", q[:t], k[:t], v[:t], np.zeros((t, dk)),
+                                       np.ones(t), rng.standard_normal((dk, dv)))
+        assert close(k[t - 1] @ S, v[t - 1])
+
+
+def test_variant_gdn_beta_zero_closed_form():
+    """beta = 0: nothing is erased or written, S_t = (prod_{i<=t} alpha_i) S_0."""
+    rng = np.random.default_rng(33)
+    T, dk, dv = 7, 5, 3
+    q, k, v, la, _, _ = variant_case(rng, T, dk, dv, "gdn")
+    S0 = rng.standard_normal((dk, dv))
+    o, ST = oracle.variant_sequence("gdn", q, k, v, la, np.zeros(T), S0)
+    for t in range(T):
+        assert close(o[t], np.exp(np.sum(la[:t + 1])) * (S0.T @ q[t]))
+    assert close(ST, np.exp(np.sum(la)) * S0)
+
+
+@pytest.mark.parametrize("mode", ["kda", "gdn"])
+def test_variant_kda_gdn_are_gdn2_with_scalar_gates(mode):
+    """The burn-gdn2 page's channel-wise b and w replace KDA's scalar gate: with b = w = beta
+    in every channel (and, for GDN, log alpha in every channel) the C oracle of GDN-2 gives
+    the variant's outputs."""
+    rng = np.random.default_rng(34)
+    T, dk, dv = 10, 6, 4
+    q, k, v, la, beta, _ = variant_case(rng, T, dk, dv, mode)
+    S0 = rng.standard_normal((dk, dv))
+    o, ST = oracle.variant_sequence(mode, q, k, v, la, beta, S0)
+    la2 = np.broadcast_to(la[:, None], (T, dk)) if mode == "gdn" else la
+    b = np.broadcast_to(beta[:, None], (T, dk))
+    w = np.broadcast_to(beta[:, None], (T, dv))
+    o2, S2 = oracle.sequence(q, k, v, w, la2, b, S0)
+    assert close(o, o2) and close(ST, S2)
+
+
+def test_variant_fg2_plus_with_equal_scales_is_fg2():
+    rng = np.random.default_rng(35)
+    T, d = 8, 5
+    q, k, v, la, beta, _ = variant_case(rng, T, d, d, "fg2")
+    S0 = rng.standard_normal((d, d))
+    o1, S1 = oracle.variant_sequence("fg2", q, k, v, la, beta, S0)
+    o2, S2 = oracle.variant_sequence("fg2+", q, k, v, la, beta, S0, beta_v=beta)
+    assert close(o1, o2) and close(S1, S2)
