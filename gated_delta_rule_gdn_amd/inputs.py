@@ -9,7 +9,7 @@ fp32, then rounded to the working dtype by torch, so both sides read exactly the
 same values. The *_device variants draw the same distributions on the GPU with a
 seeded torch generator, for timing runs whose outputs are not compared.
 
-Distributions (one reading per workload, recorded in the design doc):
+Distributions (one reading per workload):
   q, k       ~ N(0,1), L2-normalised per (token, head) before the cast
   v          ~ N(0,1)
   log_alpha  = -softplus(N(0,1))  per key channel   (decay alpha in (0,1))

@@ -29,7 +29,7 @@ Two independent evaluations of the method live here:
   representation), in numpy fp64. It exists to pin the recurrence: the two are
   different algorithms and agree only if both are right.
 
-Conventions (taken where the pages are silent; each listed in the design doc):
+Conventions (taken where the pages are silent):
 
 * packed token layout: ``q, k`` are ``[T_total, H_k, d_k]``, ``v, w`` are
   ``[T_total, H_v, d_v]``, ``log_alpha, b`` are ``[T_total, H_v, d_k]``;
