@@ -234,8 +234,9 @@ def bench_recurrent(T, state_dtype, calls, seed, traffic_key=None):
 
 
 def bench_gate_variants(steps, warmup, seed=9):
-    """The timed chunk shape (bf16, B=1 T=4096 H=16 d=128) run as KDA and as FG2-GDN+ through
-    the gate mappings (gdn2_map_gates, then the GDN-2 chunked forward), with the mapping pass
+    """The timed chunk shape (bf16, B=1 T=4096 H=16 d=128) run as KDA and as FG2-GDN+, two
+    ways: natively (gdn2_fusion.gate_mode: the prep kernel reads beta itself) and through the
+    gate mappings (gdn2_map_gates, then the GDN-2 chunked forward), with the mapping pass
     timed on its own. The mapping is an elementwise HBM pass: its algorithmic bytes are the
     gate tensors it reads and the GDN-2 tensors it writes."""
     wl = inputs.CHUNK_BF16_T4096
@@ -253,21 +254,28 @@ def bench_gate_variants(steps, warmup, seed=9):
             return g.map_gates(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
                                d.get("beta_v"))
 
-        def whole():
+        def mapped():
             g.chunk_fwd(*mapping(), S0=d["S"], workspace=ws)
 
+        def native():
+            g.gated_chunk_fwd(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
+                              beta_v=d.get("beta_v"), S0=d["S"], workspace=ws)
+
         for _ in range(warmup):
-            whole()
+            mapped()
+            native()
         t_map = time_region(mapping, steps, stream)
-        t_all = time_region(whole, steps, stream)
+        t_mapped = time_region(mapped, steps, stream)
+        t_native = time_region(native, steps, stream)
         T, H, dk, dv, e = wl.seqlen, wl.h_v, wl.d_k, wl.d_v, 2
         if mode == "kda":
             nbytes = T * H * e + T * H * (dk + dv) * e          # beta in; b, w out
         else:                                                   # beta, beta_v, k in; k', b, w out
             nbytes = T * H * (dk + dv) * e + T * wl.h_k * dk * e + T * H * (2 * dk + dv) * e
-        res[mode] = {"workload": f"{wl.name}_{mode}", "us_per_call": t_all * 1e6,
-                     "tokens_per_s": T / t_all, "map_us": t_map * 1e6,
-                     "map_alg_bytes": nbytes, "map_hbm_frac": nbytes / t_map / 1e9 / HBM_PEAK_GBPS}
+        res[mode] = {"workload": f"{wl.name}_{mode}", "us_per_call": t_native * 1e6,
+                     "tokens_per_s": T / t_native, "mapped_us_per_call": t_mapped * 1e6,
+                     "map_us": t_map * 1e6, "map_alg_bytes": nbytes,
+                     "map_hbm_frac": nbytes / t_map / 1e9 / HBM_PEAK_GBPS}
         del d, ws
     return res
 

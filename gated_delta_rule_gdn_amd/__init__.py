@@ -44,7 +44,8 @@ class Fusion(ctypes.Structure):
     _fields_ = [("qk_l2norm", ctypes.c_int32), ("l2norm_eps", ctypes.c_float),
                 ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
                 ("norm_eps", ctypes.c_float), ("conv_weight", ctypes.c_void_p),
-                ("conv_state", ctypes.c_void_p), ("conv_silu", ctypes.c_int32)]
+                ("conv_state", ctypes.c_void_p), ("conv_silu", ctypes.c_int32),
+                ("gate_mode", ctypes.c_int32)]
 
 
 class GDN2Error(RuntimeError):
@@ -117,10 +118,10 @@ def _need_gpu(name: str, t: torch.Tensor, device) -> None:
 
 
 def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight, norm_eps,
-            conv=None):
+            conv=None, gate_mode=0):
     """The gdn2_fusion argument (None when nothing is fused). ``conv`` is
     (conv_weight, conv_state, conv_silu, channels, num_slots) or None."""
-    if not qk_l2norm and gate is None and conv is None:
+    if not qk_l2norm and gate is None and conv is None and not gate_mode:
         return None
     cw = cs = None
     silu = 0
@@ -142,7 +143,29 @@ def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
         if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (out_shape[-1],):
             raise ValueError(f"norm_weight must be fp32 [{out_shape[-1]}]")
     return Fusion(1 if qk_l2norm else 0, l2norm_eps, _ptr(gate), _ptr(norm_weight), norm_eps,
-                  _ptr(cw), _ptr(cs), 1 if silu else 0)
+                  _ptr(cw), _ptr(cs), 1 if silu else 0, gate_mode)
+
+
+def _gate_shapes(mode, lead, Hv, dk, dv, log_alpha, b, w):
+    """Checks log_alpha, b and w for a gate mode (None: the GDN-2 gates). Returns the mode
+    code. See gdn2_fusion.gate_mode."""
+    code = 0 if mode is None else GATE_MODES.get(mode)
+    if code is None:
+        raise ValueError(f"gate_mode must be None or one of {sorted(GATE_MODES)}")
+    la_shape = lead + ((Hv,) if mode == "gdn" else (Hv, dk))
+    b_shape = lead + ((Hv,) if mode in ("kda", "gdn") else (Hv, dk))
+    if tuple(log_alpha.shape) != la_shape:
+        raise ValueError(f"log_alpha must be {list(la_shape)}")
+    if tuple(b.shape) != b_shape:
+        raise ValueError(f"b must be {list(b_shape)}" + (f" (beta of mode {mode!r})" if mode else ""))
+    if mode in (None, "fg2+"):
+        if w is None or tuple(w.shape) != lead + (Hv, dv):
+            raise ValueError(f"w must be {list(lead + (Hv, dv))}")
+    elif w is not None:
+        raise ValueError(f"gate mode {mode!r} takes no w (pass None)")
+    if mode == "fg2" and dv != dk:
+        raise ValueError("gate mode 'fg2' needs d_v = d_k")
+    return code
 
 
 def chunk_fwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: int, d_v: int,
@@ -157,25 +180,29 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
               out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
               qk_l2norm: bool = False, l2norm_eps: float = 1e-6,
               gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
-              norm_eps: float = 1e-5) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              norm_eps: float = 1e-5, gate_mode: Optional[str] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked WY forward. Returns (o [B,T,H_v,d_v], S_T [N,H_v,d_k,d_v] fp32 or None).
 
     qk_l2norm: L2-normalise q and k inside the kernels. gate [B,T,H_v,d_v] with norm_weight
     fp32 [d_v]: o is returned through the gated RMS norm o/rms(o) * weight * silu(gate).
+    gate_mode ("kda", "gdn", "fg2", "fg2+"): run that variant natively; b carries its beta
+    and w is None (or beta_v for "fg2+"), see map_gates for the shapes.
     """
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
+        if t is None and name == "w" and gate_mode not in (None, "fg2+"):
+            continue
         _need_gpu(name, t, dev)
         if t.dtype != q.dtype:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
     if q.dim() != 4 or k.shape != q.shape:
         raise ValueError("q and k must both be [B,T,H_k,d_k]")
     B, T, Hk, dk = q.shape
-    if v.dim() != 4 or v.shape[:2] != (B, T) or w.shape != v.shape:
-        raise ValueError("v and w must both be [B,T,H_v,d_v]")
+    if v.dim() != 4 or v.shape[:2] != (B, T):
+        raise ValueError("v must be [B,T,H_v,d_v]")
     Hv, dv = v.shape[2], v.shape[3]
-    if log_alpha.shape != (B, T, Hv, dk) or b.shape != (B, T, Hv, dk):
-        raise ValueError("log_alpha and b must be [B,T,H_v,d_k]")
+    gcode = _gate_shapes(gate_mode, (B, T), Hv, dk, dv, log_alpha, b, w)
     if cu_seqlens is not None:
         _need_gpu("cu_seqlens", cu_seqlens, dev)
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
@@ -198,7 +225,7 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
         S_T = final_state if final_state is not None else torch.empty(
             N, Hv, dk, dv, dtype=torch.float32, device=dev)
     fu = _fusion(dev, (B, T, Hv, dv), q.dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
-                 norm_eps)
+                 norm_eps, gate_mode=gcode)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                               _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(o), _ptr(S_T),
@@ -241,8 +268,8 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
                   l2norm_eps: float = 1e-6, gate: Optional[torch.Tensor] = None,
                   norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5,
                   conv_weight: Optional[torch.Tensor] = None,
-                  conv_state: Optional[torch.Tensor] = None, conv_silu: bool = False
-                  ) -> torch.Tensor:
+                  conv_state: Optional[torch.Tensor] = None, conv_silu: bool = False,
+                  gate_mode: Optional[str] = None) -> torch.Tensor:
     """T tokens per sequence against a pool of recurrent states, updated in place.
 
     q, k [N,T,H_k,d_k]; v, w [N,T,H_v,d_v]; log_alpha, b [N,T,H_v,d_k] (fp32 or bf16);
@@ -251,10 +278,12 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
     Returns o [N,T,H_v,d_v] in the input dtype. qk_l2norm, gate, norm_weight: as in chunk_fwd.
     conv_weight fp32 [C,4] with conv_state fp32 [num_slots,3,C], C = 2 H_k d_k + H_v d_v:
     the short causal convolution of q, k, v (channel order q, k, v), its state updated in
-    place; conv_silu applies SiLU after it.
+    place; conv_silu applies SiLU after it. gate_mode: as in chunk_fwd.
     """
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
+        if t is None and name == "w" and gate_mode not in (None, "fg2+"):
+            continue
         _need_gpu(name, t, dev)
         if t.dtype != q.dtype:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
@@ -262,11 +291,10 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
     if q.dim() != 4 or k.shape != q.shape:
         raise ValueError("q and k must both be [N,T,H_k,d_k]")
     N, T, Hk, dk = q.shape
-    if v.dim() != 4 or v.shape[:2] != (N, T) or w.shape != v.shape:
-        raise ValueError("v and w must both be [N,T,H_v,d_v]")
+    if v.dim() != 4 or v.shape[:2] != (N, T):
+        raise ValueError("v must be [N,T,H_v,d_v]")
     Hv, dv = v.shape[2], v.shape[3]
-    if log_alpha.shape != (N, T, Hv, dk) or b.shape != (N, T, Hv, dk):
-        raise ValueError("log_alpha and b must be [N,T,H_v,d_k]")
+    gcode = _gate_shapes(gate_mode, (N, T), Hv, dk, dv, log_alpha, b, w)
     if state.dim() != 4 or state.shape[1:] != (Hv, dk, dv):
         raise ValueError(f"state must be [num_slots,{Hv},{dk},{dv}]")
     if state.dtype == torch.float32:
@@ -287,7 +315,7 @@ def recurrent_fwd(q, k, v, log_alpha, b, w, state, state_idx: Optional[torch.Ten
             raise ValueError("conv_weight and conv_state go together")
         conv = (conv_weight, conv_state, conv_silu, 2 * Hk * dk + Hv * dv, state.shape[0])
     fu = _fusion(dev, (N, T, Hv, dv), q.dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
-                 norm_eps, conv)
+                 norm_eps, conv, gate_mode=gcode)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib().gdn2_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                                   _ptr(state), sdt, _ptr(state_idx), state.shape[0], _ptr(o),
@@ -374,18 +402,29 @@ def _fg2_fusion_check(mode, kw):
                          "keys of the FG2 modes; normalise or convolve q and k before mapping")
 
 
-def gated_chunk_fwd(mode: str, q, k, v, log_alpha, beta, beta_v=None, **kw):
-    """chunk_fwd of a delta-rule variant (see map_gates): maps the inputs, then runs the
-    GDN-2 chunked forward. Keyword arguments go to chunk_fwd."""
+def gated_chunk_fwd(mode: str, q, k, v, log_alpha, beta, beta_v=None, mapped: bool = False,
+                    **kw):
+    """chunk_fwd of a delta-rule variant (shapes as in map_gates). By default the variant
+    runs natively (gdn2_fusion.gate_mode: the kernels read beta); mapped=True runs
+    map_gates first and then the plain GDN-2 call. Keyword arguments go to chunk_fwd."""
     _fg2_fusion_check(mode, kw)
-    return chunk_fwd(*map_gates(mode, q, k, v, log_alpha, beta, beta_v), **kw)
+    if mapped:
+        return chunk_fwd(*map_gates(mode, q, k, v, log_alpha, beta, beta_v), **kw)
+    if mode not in GATE_MODES:
+        raise ValueError(f"mode must be one of {sorted(GATE_MODES)}")
+    return chunk_fwd(q, k, v, log_alpha, beta, beta_v, gate_mode=mode, **kw)
 
 
-def gated_recurrent_fwd(mode: str, q, k, v, log_alpha, beta, state, beta_v=None, **kw):
-    """recurrent_fwd of a delta-rule variant (see map_gates) against a state pool. Keyword
-    arguments go to recurrent_fwd."""
+def gated_recurrent_fwd(mode: str, q, k, v, log_alpha, beta, state, beta_v=None,
+                        mapped: bool = False, **kw):
+    """recurrent_fwd of a delta-rule variant against a state pool (native by default, as in
+    gated_chunk_fwd). Keyword arguments go to recurrent_fwd."""
     _fg2_fusion_check(mode, kw)
-    return recurrent_fwd(*map_gates(mode, q, k, v, log_alpha, beta, beta_v), state, **kw)
+    if mapped:
+        return recurrent_fwd(*map_gates(mode, q, k, v, log_alpha, beta, beta_v), state, **kw)
+    if mode not in GATE_MODES:
+        raise ValueError(f"mode must be one of {sorted(GATE_MODES)}")
+    return recurrent_fwd(q, k, v, log_alpha, beta, beta_v, state, gate_mode=mode, **kw)
 
 
 def abi_version() -> int:

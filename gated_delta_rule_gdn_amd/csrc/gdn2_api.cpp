@@ -42,9 +42,18 @@ constexpr int64_t kMaxElems = (int64_t{1} << 40);   // bound on any tensor's ele
 bool eps_ok(float e) { return e >= 0.f && e <= 1e30f; }   // also rejects NaN
 
 // Checks the optional fusion options and copies them into the launch arguments.
-gdn2_status take_fusion(const gdn2_fusion *f, const void *o, gdn2::Fusion *out) {
+gdn2_status take_fusion(const gdn2_fusion *f, const void *o, const gdn2_dims *d,
+                        gdn2::Fusion *out) {
     *out = gdn2::Fusion{};
     if (!f) return GDN2_OK;
+    if (f->gate_mode < 0 || f->gate_mode > GDN2_GATES_GDN)
+        return fail(GDN2_ERR_UNSUPPORTED, "gate_mode must be 0 or a gdn2_gate_mode");
+    const bool fg2 = f->gate_mode == GDN2_GATES_FG2 || f->gate_mode == GDN2_GATES_FG2_PLUS;
+    if (fg2 && (f->qk_l2norm || f->conv_weight))
+        return fail(GDN2_ERR_UNSUPPORTED,
+                    "the FG2 gate modes take neither the q/k L2-norm nor the convolution");
+    if (f->gate_mode == GDN2_GATES_FG2 && d->d_v != d->d_k)
+        return fail(GDN2_ERR_BAD_SHAPE, "GDN2_GATES_FG2 needs d_v = d_k");
     if (f->qk_l2norm && !eps_ok(f->l2norm_eps))
         return fail(GDN2_ERR_BAD_SHAPE, "l2norm_eps must be finite and >= 0");
     if (f->gate) {
@@ -64,7 +73,13 @@ gdn2_status take_fusion(const gdn2_fusion *f, const void *o, gdn2::Fusion *out) 
     out->gate = f->gate;
     out->nw = f->norm_weight;
     out->neps = f->norm_eps;
+    out->gmode = f->gate_mode;
     return GDN2_OK;
+}
+
+// The w argument is unused by the gate modes that derive w from b.
+bool needs_w(const gdn2::Fusion &fu) {
+    return fu.gmode == 0 || fu.gmode == GDN2_GATES_FG2_PLUS;
 }
 
 }  // namespace
@@ -139,12 +154,12 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
     gdn2_status st = check_chunk_dims(dims, chunk_size, packed);
     if (st != GDN2_OK) return st;
     gdn2::Fusion fu;
-    st = take_fusion(fusion, o, &fu);
+    st = take_fusion(fusion, o, dims, &fu);
     if (st != GDN2_OK) return st;
     if (fu.cw)
         return fail(GDN2_ERR_UNSUPPORTED, "the short convolution is built for gdn2_recurrent_fwd only");
     const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
-    if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !o))
+    if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || (!w && needs_w(fu)) || !o))
         return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w and o are required");
     const bool bf = dims->dtype == GDN2_BF16;
     const size_t need = gdn2::chunk_workspace_bytes(dims->batch, dims->seqlen, dims->num_seqs,
@@ -180,7 +195,7 @@ static gdn2_status recurrent_common(const void *q, const void *k, const void *v,
     gdn2_status st = check_heads(dims);
     if (st != GDN2_OK) return st;
     gdn2::Fusion fu;
-    st = take_fusion(fusion, o, &fu);
+    st = take_fusion(fusion, o, dims, &fu);
     if (st != GDN2_OK) return st;
     if (state_dtype != GDN2_STATE_F32 && state_dtype != GDN2_STATE_BF16)
         return fail(GDN2_ERR_UNSUPPORTED, "state_dtype must be GDN2_STATE_F32 or GDN2_STATE_BF16");
@@ -202,7 +217,7 @@ static gdn2_status recurrent_common(const void *q, const void *k, const void *v,
         g_last_error[0] = '\0';
         return GDN2_OK;
     }
-    if (!q || !k || !v || !log_alpha || !b || !w || !o || (num_slots > 0 && !S))
+    if (!q || !k || !v || !log_alpha || !b || (!w && needs_w(fu)) || !o || (num_slots > 0 && !S))
         return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w, the state and o are required");
     if (o == q || o == k || o == v || o == log_alpha || o == b || o == w || o == S)
         return fail(GDN2_ERR_BAD_SHAPE, "o must not alias an input or the state");

@@ -92,6 +92,7 @@ struct ChunkParams {
     int nseg, seg_len;
     int qkn;             // nonzero: q and k rows are L2-normalised in K1
     float l2eps;
+    int gmode;           // GateMode: how b (and w, log_alpha) carry the gates
 };
 
 // Locates chunk `chunk` of the batch: sequence n, its chunk index j, and token range.
@@ -222,7 +223,9 @@ __device__ __forceinline__ void unpack16(u32x4 v, float *out) {
     }
 }
 
-template <typename T, bool BF, int DK, int DV, bool NTR>
+// GM: the gate mode (GateMode), one instance per mode, so that no instance carries another
+// mode's selects (run-time selects around the prefetched loads measured 7 us slower).
+template <typename T, bool BF, int DK, int DV, bool NTR, int GM>
 __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
     using R_ = Rec<DK, DV, BF>;
     constexpr int C = kChunk, NT = 512, NW = NT / 64;
@@ -279,7 +282,31 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
     // parts: a workgroup that issues all 96 KB at once stalls at the issue until most of it
     // has arrived, so the next record's parts are issued one per phase instead.
     u32x4 rk[RAWV], rq[RAWV], rb[RAWV], rl[RAWV], rw[RAWW], rv[RAWW];
-    auto load_gate = [&](const PrepLoc &lc, const T *src, u32x4 *dst) {   // [C][H_v][DK]
+    // Gate modes (GateMode): KDA and GDN carry one b per (token, value head) in b, which also
+    // serves as w, and GDN one decay per (token, value head); FG2 carries beta [..][DK] in b
+    // (k <- sqrt(beta) k, b <- 1 and w <- sqrt(beta), applied in phase 0b), FG2+ also
+    // beta_v in w (w <- sqrt(beta_v)).
+    constexpr bool b_scalar = GM == GATES_KDA || GM == GATES_GDN;
+    constexpr bool la_scalar = GM == GATES_GDN;
+    constexpr bool fg2 = GM == GATES_FG2 || GM == GATES_FG2_PLUS;
+    // a 16-byte vector of VEC copies of one element
+    auto bcast = [](const T *x) {
+        uint32_t u;
+        if constexpr (sizeof(T) == 4) u = __float_as_uint(io<T>::ld(x));
+        else u = static_cast<uint32_t>(x->bits) * 0x10001u;
+        return u32x4{u, u, u, u};
+    };
+    // (`scalar` is uniform over the workgroup: one branch around the whole loop)
+    auto load_gate = [&](const PrepLoc &lc, const T *src, u32x4 *dst, bool scalar) {   // [C][H_v][DK]
+        if (scalar) {
+#pragma unroll
+            for (int e = 0; e < RAWV; ++e) {
+                const int r = (tid + NT * e) / VK;
+                dst[e] = u32x4{0u, 0u, 0u, 0u};
+                if (r < lc.L) dst[e] = bcast(src + static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h);
+            }
+            return;
+        }
 #pragma unroll
         for (int e = 0; e < RAWV; ++e) {
             const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
@@ -302,6 +329,9 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             }
         }
     };
+    // w's source: w itself (GDN-2, FG2+), or b (KDA and GDN: the scalar; FG2: beta, whose
+    // [..][DK] rows index like w's [..][DV] rows since d_v = d_k there)
+    const T *wsrc = (b_scalar || GM == GATES_FG2) ? bp : wp;
     auto load_wv = [&](const PrepLoc &lc) {                               // [C][H_v][DV]
 #pragma unroll
         for (int e = 0; e < RAWW; ++e) {
@@ -310,8 +340,16 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             rv[e] = rw[e];
             if (r < lc.L) {
                 const size_t ov = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DV + cv * VEC;
-                rw[e] = *reinterpret_cast<const u32x4 *>(wp + ov);
+                // a scalar b is [rows][H_v]: only the broadcast below may index it
+                if (!b_scalar) rw[e] = *reinterpret_cast<const u32x4 *>(wsrc + ov);
                 rv[e] = *reinterpret_cast<const u32x4 *>(vp + ov);
+            }
+        }
+        if (b_scalar) {                  // w = the scalar b (uniform branch)
+#pragma unroll
+            for (int e = 0; e < RAWW; ++e) {
+                const int r = (tid + NT * e) / VV;
+                if (r < lc.L) rw[e] = bcast(wsrc + static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h);
             }
         }
     };
@@ -320,9 +358,9 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
     PrepLoc cur;
     if (item < nitems) {
         locate(item, cur);
-        load_gate(cur, lap, rl);
+        load_gate(cur, lap, rl, la_scalar);
         load_qk(cur);
-        load_gate(cur, bp, rb);
+        load_gate(cur, bp, rb, b_scalar);
         load_wv(cur);
     }
     for (; item < nitems; item += gridDim.x) {
@@ -442,6 +480,13 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
                     qq[s] *= fq;
                 }
             }
+            if (fg2) {                              // k <- sqrt(beta) k, b <- 1
+#pragma unroll
+                for (int s = 0; s < VEC; ++s) {
+                    kk[s] *= sqrt_hw(bb[s]);
+                    bb[s] = 1.f;
+                }
+            }
 #pragma unroll
             for (int s = 0; s < VEC; ++s) {
                 const float gr = s_g[r * SG + c0 + s], gm = s_g[mid + c0 + s];
@@ -479,11 +524,11 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
             unpack16<BF>(rw[e], ww);
             unpack16<BF>(rv[e], vv);
 #pragma unroll
-            for (int s = 0; s < VEC; ++s) prod[s] = ww[s] * vv[s];
+            for (int s = 0; s < VEC; ++s) prod[s] = (fg2 ? sqrt_hw(ww[s]) : ww[s]) * vv[s];
             *reinterpret_cast<u32x4 *>(&s_wv[r * SV + cv * VEC]) = pack16<BF>(prod);
         }
         __syncthreads();
-        if (has_next) load_gate(nxt, lap, rl);   // next record's raw tiles: first part
+        if (has_next) load_gate(nxt, lap, rl, la_scalar);   // next record's raw tiles: first part
 
         // ---- phase 1: A^T and M^T blocks (R >= I); zero upper blocks of M ----
         char *mrec = rec + R_::M;
@@ -612,7 +657,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 
         // ---- phase 2b: off-diagonal blocks of T by levels d = R - I ----
         if (has_next) {
-            load_gate(nxt, bp, rb);
+            load_gate(nxt, bp, rb, b_scalar);
             load_wv(nxt);
         }
 #pragma unroll
@@ -1301,7 +1346,7 @@ template <typename T, bool BF, int DK, int DV>
 __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(ChunkParams p) {
     using R_ = Rec<DK, DV, BF>;
     using SG = SegLayout<DK, DV, BF>;
-    constexpr int C = kChunk, RT = DK / 16;
+    constexpr int RT = DK / 16;
     constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -1639,6 +1684,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.num_pairs = N * a.h_v;
     p.qkn = a.fu.qk_norm ? 1 : 0;
     p.l2eps = a.fu.l2eps;
+    p.gmode = a.fu.gmode;
     const int64_t nrec = chunk_upper_bound(a.batch, a.seqlen, N, packed);
     const SegPlan sp = chunk_seg_plan(packed, p.num_pairs, p.nc_dense, DV, BF);
     p.nseg = sp.nseg;
@@ -1660,8 +1706,20 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         const int64_t items = nchunks * a.h_v;
         const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
         const bool ntr = static_cast<size_t>(items) * Rec<DK, DV, BF>::bytes > kStreamRecordBytes;
-        if (ntr) hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, true>), dim3(grid), dim3(512), 0, st, p);
-        else hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false>), dim3(grid), dim3(512), 0, st, p);
+        // (the gate-mode instances keep the default stores at every size: fewer instances)
+        const dim3 g3(grid), b3(512);
+        switch (p.gmode) {
+        case GATES_KDA: hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_KDA>), g3, b3, 0, st, p); break;
+        case GATES_GDN: hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_GDN>), g3, b3, 0, st, p); break;
+        case GATES_FG2_PLUS: hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_FG2_PLUS>), g3, b3, 0, st, p); break;
+        case GATES_FG2:                       // d_v = d_k (refused otherwise before the launch)
+            if constexpr (DK == DV) hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_FG2>), g3, b3, 0, st, p);
+            else return hipErrorInvalidValue;
+            break;
+        default:
+            if (ntr) hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, true, GATES_GDN2>), g3, b3, 0, st, p);
+            else hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_GDN2>), g3, b3, 0, st, p);
+        }
     }
     const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
     if (p.nseg > 1 && p.num_pairs > 0) {

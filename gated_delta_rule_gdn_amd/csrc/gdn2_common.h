@@ -21,6 +21,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Square root on the transcendental unit (within 1 ulp): the gate scales of the FG2 modes.
+// sqrtf's correctly rounded sequence adds a compare-and-select rescaling per value.
+__device__ __forceinline__ float sqrt_hw(float x) { return __builtin_amdgcn_sqrtf(x); }
+
 // Element loads/stores of the input dtype, widened to fp32.
 template <typename T> struct io;
 

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     ST *__restrict__ S, const int32_t *__restrict__ idx, T *__restrict__ o, int ntok,
     int num_slots, int h_k, int h_v, int group, int qkn, float l2eps,
     const T *__restrict__ gate, const float *__restrict__ nw, float neps,
-    const float *__restrict__ cw, float *__restrict__ cst, int csilu) {
+    const float *__restrict__ cw, float *__restrict__ cst, int csilu, int gmode) {
     constexpr int NT = kDecodeThreads, NW = NT / 64;
     constexpr int VN = svec<ST>::N;   // columns per lane (one 16-byte vector)
     using Gm = Geom<DK, DV, VN, COLW>;
@@ -216,6 +216,33 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     float s[RPT][VN];
     // Single-token calls with the convolution stage their one token before the state loads
     // (EARLY); every other instance loads the state first.
+    // Gate modes (GateMode): KDA and GDN read one b per (token, value head) from b, which
+    // also serves as w, GDN one decay per (token, value head); FG2 reads beta [..][DK] from b
+    // (k <- sqrt(beta) k, b <- 1, w <- sqrt(beta), d_v = d_k), FG2+ beta_v from w
+    // (w <- sqrt(beta_v)). `tok` is the token row of the call's [N][T] layout.
+    const bool b_scalar = gmode == GATES_KDA || gmode == GATES_GDN;
+    const bool la_scalar = gmode == GATES_GDN;
+    const bool fg2 = gmode == GATES_FG2 || gmode == GATES_FG2_PLUS;
+    auto gate_la = [&](size_t tok, int r) {
+        const size_t rh = tok * h_v + h;
+        return io<T>::ld(log_alpha + (la_scalar ? rh : rh * DK + r));
+    };
+    auto gate_b = [&](size_t tok, int r) {
+        const size_t rh = tok * h_v + h;
+        return io<T>::ld(b + (b_scalar ? rh : rh * DK + r));
+    };
+    auto gate_w = [&](size_t tok, int c) {
+        const size_t rh = tok * h_v + h;
+        if (b_scalar) return io<T>::ld(b + rh);
+        if (gmode == GATES_FG2) return sqrt_hw(io<T>::ld(b + rh * DK + c));
+        const float x = io<T>::ld(w + rh * DV + c);
+        return gmode == GATES_FG2_PLUS ? sqrt_hw(x) : x;
+    };
+    // staged key row: (decay, b . k, q, k), with FG2's key scaling
+    auto stage_key = [&](float la, float bv, float qq, float kk) {
+        const float kx = fg2 ? sqrt_hw(bv) * kk : kk;
+        return f32x4{__expf(la), (fg2 ? 1.f : bv) * kx, qq, kx};
+    };
     constexpr bool EARLY = CV && !COLW;
     if constexpr (EARLY) {
         // One token, one staging entry per thread (key row tid, or v column tid - DK). Its
@@ -226,7 +253,6 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
         const bool krow = tid < DK, vcol = tid >= DK && tid < DK + DV;
         const int r = krow ? tid : 0, c = vcol ? tid - DK : 0;
         const size_t kq_off = (static_cast<size_t>(n) * h_k + hk) * DK + r;
-        const size_t g_off = (static_cast<size_t>(n) * h_v + h) * DK + r;
         const size_t v_off = (static_cast<size_t>(n) * h_v + h) * DV + c;
         float xk = 0.f, xq = 0.f, xla = 0.f, xb = 0.f, xw = 0.f, xv = 0.f;
         f32x4 wk4 = {}, wq4 = {}, wv4 = {};
@@ -235,8 +261,8 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
         if (krow) {
             xk = io<T>::ld(k + kq_off);
             xq = io<T>::ld(q + kq_off);
-            xla = io<T>::ld(log_alpha + g_off);
-            xb = io<T>::ld(b + g_off);
+            xla = gate_la(n, r);
+            xb = gate_b(n, r);
             if constexpr (CV) {
                 wk4 = *reinterpret_cast<const f32x4 *>(cw + static_cast<size_t>(chk) * 4);
                 wq4 = *reinterpret_cast<const f32x4 *>(cw + static_cast<size_t>(chq) * 4);
@@ -248,7 +274,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
             }
         }
         if (vcol) {
-            xw = io<T>::ld(w + v_off);
+            xw = gate_w(n, c);
             xv = io<T>::ld(v + v_off);
             if constexpr (CV) {
                 wv4 = *reinterpret_cast<const f32x4 *>(cw + static_cast<size_t>(chv) * 4);
@@ -269,7 +295,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
         if (krow) {
             const float kk = CV ? conv1(wk4, ck, xk) : xk;
             const float qq = CV ? conv1(wq4, cq, xq) : xq;
-            s_tok[0][r] = f32x4{__expf(xla), xb * kk, qq, kk};
+            s_tok[0][r] = stage_key(xla, xb, qq, kk);
         }
         if (vcol) {
             s_wv[0][c] = xw * (CV ? conv1(wv4, cvv, xv) : xv);
@@ -295,7 +321,6 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                 const int tt = i / DK, r = i - tt * DK;
                 const size_t tok = static_cast<size_t>(n) * nt + t0 + tt;
                 const size_t kq_off = (tok * h_k + hk) * DK + r;
-                const size_t g_off = (tok * h_v + h) * DK + r;
                 float kk, qq;
                 if constexpr (CV) {
                     const size_t base = static_cast<size_t>(n) * nt;
@@ -307,8 +332,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                     kk = io<T>::ld(k + kq_off);
                     qq = io<T>::ld(q + kq_off);
                 }
-                s_tok[tt][r] = f32x4{__expf(io<T>::ld(log_alpha + g_off)),
-                                     io<T>::ld(b + g_off) * kk, qq, kk};
+                s_tok[tt][r] = stage_key(gate_la(tok, r), gate_b(tok, r), qq, kk);
             } else {
                 const int iv = i - nb * DK, tt = iv / DV, c = iv - tt * DV;
                 const size_t off = ((static_cast<size_t>(n) * nt + t0 + tt) * h_v + h) * DV + c;
@@ -320,7 +344,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
                 } else {
                     vv = io<T>::ld(v + off);
                 }
-                s_wv[tt][c] = io<T>::ld(w + off) * vv;
+                s_wv[tt][c] = gate_w(static_cast<size_t>(n) * nt + t0 + tt, c) * vv;
             }
         }
         __syncthreads();
@@ -508,7 +532,7 @@ static hipError_t launch_recurrent_f(const DecodeArgs &a, hipStream_t st) {
                        static_cast<ST *>(a.S), a.idx, static_cast<T *>(a.o), a.ntok,
                        a.num_slots, a.h_k, a.h_v, a.h_v / a.h_k, a.fu.qk_norm ? 1 : 0,
                        a.fu.l2eps, static_cast<const T *>(a.fu.gate), a.fu.nw, a.fu.neps,
-                       a.fu.cw, a.fu.cst, a.fu.csilu ? 1 : 0);
+                       a.fu.cw, a.fu.cst, a.fu.csilu ? 1 : 0, a.fu.gmode);
     if constexpr (CV) {
         const int64_t threads = static_cast<int64_t>(a.num_seqs) * 2 * a.h_k * DK;
         const int C = 2 * a.h_k * DK + a.h_v * DV;

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void map_gates_kernel(GateArgs a) {
                 Vec16<T>::load(beta + o, bk);
                 Vec16<T>::load(k + ok, kk);
 #pragma unroll
-                for (int e = 0; e < N; ++e) x[e] = sqrtf(bk[e]) * kk[e];
+                for (int e = 0; e < N; ++e) x[e] = sqrt_hw(bk[e]) * kk[e];
                 Vec16<T>::store(static_cast<T *>(a.k_out) + o, x);
 #pragma unroll
                 for (int e = 0; e < N; ++e) x[e] = 1.f;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void map_gates_kernel(GateArgs a) {
                 Vec16<T>::load(beta + o, bk);
                 Vec16<T>::load(v + o, vv);
 #pragma unroll
-                for (int e = 0; e < N; ++e) x[e] = sqrtf(bk[e]) * vv[e];
+                for (int e = 0; e < N; ++e) x[e] = sqrt_hw(bk[e]) * vv[e];
                 Vec16<T>::store(static_cast<T *>(a.v_out) + o, x);
 #pragma unroll
                 for (int e = 0; e < N; ++e) x[e] = 1.f;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void map_gates_kernel(GateArgs a) {
                 float bv[N];
                 Vec16<T>::load(beta_v + o, bv);
 #pragma unroll
-                for (int e = 0; e < N; ++e) x[e] = sqrtf(bv[e]);
+                for (int e = 0; e < N; ++e) x[e] = sqrt_hw(bv[e]);
                 Vec16<T>::store(static_cast<T *>(a.w_out) + o, x);
             }
         }

@@ -18,6 +18,7 @@ struct Fusion {
     const float *cw = nullptr;       // short convolution taps [C][4] fp32, or NULL
     float *cst = nullptr;            // conv state [num_slots][3][C] fp32
     bool csilu = false;
+    int gmode = 0;                   // GateMode of the b / w arguments (0: GDN-2 gates)
 };
 
 struct DecodeArgs {
@@ -54,7 +55,7 @@ size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d
 bool chunk_dims_built(int d_k, int d_v, bool bf16);
 
 // Gate mappings of other delta-rule variants onto the GDN-2 inputs (gdn2_map_gates).
-enum GateMode { GATES_KDA = 1, GATES_FG2 = 2, GATES_FG2_PLUS = 3, GATES_GDN = 4 };
+enum GateMode { GATES_GDN2 = 0, GATES_KDA = 1, GATES_FG2 = 2, GATES_FG2_PLUS = 3, GATES_GDN = 4 };
 
 struct GateArgs {
     int mode;

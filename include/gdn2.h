@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 3
+#define GDN2_ABI_VERSION 4
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -107,6 +107,16 @@ typedef enum gdn2_state_dtype {
  *                in place
  *   conv_silu    nonzero: y = silu(conv(x)); zero: y = conv(x)
  * The convolved q and k are what the L2-norm (if on) and the recurrence see.
+ *
+ *   gate_mode    0: b and w are the GDN-2 gates. A gdn2_gate_mode (see gdn2_map_gates):
+ *                the call runs that variant with its gate mapping fused into the kernels,
+ *                reading the variant's own gates (no mapping pass, no mapped tensors):
+ *                  GDN2_GATES_KDA       b = beta [.., h_v]; w unused (may be NULL)
+ *                  GDN2_GATES_GDN       as KDA, and log_alpha [.., h_v] (one per head)
+ *                  GDN2_GATES_FG2       b = beta [.., h_v, d_k], d_v = d_k; w unused
+ *                  GDN2_GATES_FG2_PLUS  b = beta [.., h_v, d_k], w = beta_v [.., h_v, d_v]
+ *                The FG2 modes scale the keys by sqrt(beta) inside the kernels, so they
+ *                take neither qk_l2norm nor the short convolution (GDN2_ERR_UNSUPPORTED).
  */
 typedef struct gdn2_fusion {
     int32_t qk_l2norm;
@@ -117,6 +127,7 @@ typedef struct gdn2_fusion {
     const float *conv_weight;
     float *conv_state;
     int32_t conv_silu;
+    int32_t gate_mode;
 } gdn2_fusion;
 
 typedef struct gdn2_dims {

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn2_abi_version() == 3
+    assert L.gdn2_abi_version() == 4
     assert L.gdn2_status_string(0) == b"ok"
     assert b"workspace" in L.gdn2_status_string(4)
     assert L.gdn2_status_string(99) == b"unknown status"
@@ -244,3 +244,19 @@ def test_map_gates_validation(L):
     assert gates(L, 1, d, b_out=FAKE, w_out=P[1]) == 2                # b_out aliases an input
     assert gates(L, 1, d, b_out=P[0], w_out=P[0]) == 2                # two outputs alike
     assert gates(L, 1, Dims(0, 10, 0, 2, 4, 64, 64, 1)) == 0          # no tokens: nothing to do
+
+
+def test_gate_mode_validation(L):
+    """gdn2_fusion.gate_mode: bad modes and combinations stop at host validation; the modes
+    that derive w from b accept w = NULL (the call then stops at a later check)."""
+    from gated_delta_rule_gdn_amd import Fusion
+    d = Dims(1, 64, 0, 1, 1, 128, 128, 1)
+    def call(mode, w=FAKE, qkn=0, dims=d, o=ctypes.c_void_p(0x9000)):
+        fu = Fusion(qkn, 1e-6, None, None, 1e-5, None, None, 0, mode)
+        return L.gdn2_chunk_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, w, None, None, 64, o, None,
+                                ctypes.byref(dims), FAKE, 1 << 40, ctypes.byref(fu), None)
+    assert call(5) == 3 and call(-1) == 3                       # not a gate mode
+    assert call(2, qkn=1) == 3 and call(3, qkn=1) == 3          # FG2 modes with the L2-norm
+    assert call(2, dims=Dims(1, 64, 0, 1, 1, 128, 64, 1)) == 2  # FG2 needs d_v = d_k
+    assert call(0, w=None) == 1 and call(3, w=None) == 1        # these modes need w
+    assert call(1, w=None, o=FAKE) == 2                         # KDA: no w; then o aliases q

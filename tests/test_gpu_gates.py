@@ -1,6 +1,7 @@
-"""GPU parity of the delta-rule variants run through the gate mappings (gdn2_map_gates, then
-the GDN-2 chunked forward or recurrent forward) against the oracle's direct update rules of
-those variants (oracle.variant: KDA, scalar-decay GDN, FG2-GDN, FG2-GDN+).
+"""GPU parity of the delta-rule variants (KDA, scalar-decay GDN, FG2-GDN, FG2-GDN+) against
+the oracle's direct update rules of those variants (oracle.variant), run two ways: natively
+(gdn2_fusion.gate_mode: the chunked and recurrent kernels read beta themselves) and mapped
+(gdn2_map_gates writes GDN-2 inputs, then the plain GDN-2 call).
 
 Gate (relative L2 per output tensor): 1e-4 for fp32 inputs, 2e-2 for bf16 inputs, on o and
 on the final states. In bf16 the mapped keys and values of the FG2 modes are rounded to
@@ -38,34 +39,38 @@ def shapes(dtype, mode):
     return (128, 128) if mode == "fg2" else (128, 64)
 
 
+@pytest.mark.parametrize("mapped", [False, True])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("mode", MODES)
-def test_chunk_forward_of_variants(mode, dtype):
+def test_chunk_forward_of_variants(mode, dtype, mapped):
     dk, dv = shapes(dtype, mode)
     x = inputs.variant_inputs(mode, dtype, 2, 150, 2, 4, dk, dv, seed=80 + MODES.index(mode))
     d = {n: t.cuda() for n, t in x.items()}
     o, S_T = g.gated_chunk_fwd(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
-                               beta_v=d.get("beta_v"), S0=d["S"])
+                               beta_v=d.get("beta_v"), mapped=mapped, S0=d["S"])
     torch.cuda.synchronize()
     o_r, S_r = oracle_run(mode, x)
     eo, es = oracle.rel_l2(np64(o), o_r), oracle.rel_l2(np64(S_T), S_r)
-    print(f"[parity] chunk {mode} {dtype} {dk}x{dv}: o={eo:.2e} S_T={es:.2e}", flush=True)
+    how = "mapped" if mapped else "native"
+    print(f"[parity] chunk {mode} {how} {dtype} {dk}x{dv}: o={eo:.2e} S_T={es:.2e}", flush=True)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("mapped", [False, True])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("mode", MODES)
-def test_recurrent_forward_of_variants(mode, dtype):
+def test_recurrent_forward_of_variants(mode, dtype, mapped):
     dk, dv = (128, 128) if mode == "fg2" else (128, 64)
     x = inputs.variant_inputs(mode, dtype, 3, 5, 2, 6, dk, dv, seed=90 + MODES.index(mode))
     d = {n: t.cuda() for n, t in x.items()}
     state = d["S"].clone()
     o = g.gated_recurrent_fwd(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], state,
-                              beta_v=d.get("beta_v"))
+                              beta_v=d.get("beta_v"), mapped=mapped)
     torch.cuda.synchronize()
     o_r, S_r = oracle_run(mode, x)
     eo, es = oracle.rel_l2(np64(o), o_r), oracle.rel_l2(np64(state), S_r)
-    print(f"[parity] recurrent {mode} {dtype} {dk}x{dv}: o={eo:.2e} S={es:.2e}", flush=True)
+    how = "mapped" if mapped else "native"
+    print(f"[parity] recurrent {mode} {how} {dtype} {dk}x{dv}: o={eo:.2e} S={es:.2e}", flush=True)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
@@ -100,5 +105,68 @@ def test_fg2_rejects_unequal_head_dims_and_fused_key_stages():
     with pytest.raises(g.GDN2Error):
         g.map_gates("fg2", d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
     with pytest.raises(ValueError):
+        g.gated_chunk_fwd("fg2", d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
+    with pytest.raises(ValueError):
         g.gated_chunk_fwd("fg2+", d["q"], d["k"], d["v"], d["log_alpha"], d["beta"],
                           beta_v=torch.ones_like(d["v"]), qk_l2norm=True)
+
+
+def test_native_kda_with_fused_norms_and_multi_token_slots():
+    """KDA natively with the q/k L2-norm and the gated output norm on, through the slot
+    cache (padding entry included): equals the same run on GDN-2 inputs (b = w = beta)."""
+    x = inputs.variant_inputs("kda", torch.bfloat16, 3, 4, 2, 6, 128, 128, seed=10)
+    d = {n: t.cuda() for n, t in x.items()}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    gate = torch.randn(3, 4, 6, 128, generator=gen, device="cuda").to(torch.bfloat16)
+    nw = torch.rand(128, generator=gen, device="cuda") + 0.5
+    idx = torch.tensor([2, -1, 0], dtype=torch.int32, device="cuda")
+    kw = dict(state_idx=idx, qk_l2norm=True, gate=gate, norm_weight=nw)
+    s1, s2 = d["S"].clone(), d["S"].clone()
+    o1 = g.gated_recurrent_fwd("kda", d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], s1, **kw)
+    b = d["beta"][..., None].expand(3, 4, 6, 128).contiguous()
+    o2 = g.recurrent_fwd(d["q"], d["k"], d["v"], d["log_alpha"], b, b.clone(), s2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_native_variants_at_the_timed_chunk_shape(mode):
+    """Each variant natively at the timed chunk shape (bf16, T = 4096, 16 heads, d = 128),
+    where the gate tensors are large enough that a read past them leaves their allocation.
+    KDA and GDN read the same gate values natively as mapped (rel. L2 <= 1e-5); the FG2
+    modes differ from the mapped run by the bf16 rounding of the mapped keys and values."""
+    wl = inputs.CHUNK_BF16_T4096
+    x = inputs.variant_inputs(mode, wl.dtype, 1, wl.seqlen, wl.h_k, wl.h_v, wl.d_k, wl.d_v,
+                              seed=120 + MODES.index(mode))
+    d = {n: t.cuda() for n, t in x.items()}
+    print(f"[case] native {mode} at B=1 T={wl.seqlen} H={wl.h_v} d={wl.d_k}", flush=True)
+    args = (mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
+    o_n, s_n = g.gated_chunk_fwd(*args, beta_v=d.get("beta_v"), S0=d["S"])
+    o_m, s_m = g.gated_chunk_fwd(*args, beta_v=d.get("beta_v"), S0=d["S"], mapped=True)
+    torch.cuda.synchronize()
+    tol = 1e-5 if mode in ("kda", "gdn") else TOL[torch.bfloat16]
+    eo, es = oracle.rel_l2(np64(o_n), np64(o_m)), oracle.rel_l2(np64(s_n), np64(s_m))
+    print(f"[parity] native vs mapped {mode} full size: o={eo:.2e} S_T={es:.2e}", flush=True)
+    assert eo <= tol and es <= tol
+    assert torch.isfinite(o_n.float()).all()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_native_variants_at_the_decode_shape(mode):
+    """One decode step of each variant natively at the timed decode shape (64 sequences,
+    16 key heads, 48 value heads, d = 128) against the mapped run (tolerances as above)."""
+    dw = inputs.DECODE_F32
+    x = inputs.variant_inputs(mode, dw.dtype, dw.num_seqs, 1, dw.h_k, dw.h_v, dw.d_k, dw.d_v,
+                              seed=130 + MODES.index(mode))
+    d = {n: t.cuda() for n, t in x.items()}
+    print(f"[case] native {mode} decode N={dw.num_seqs} H_v={dw.h_v} d={dw.d_k}", flush=True)
+    s_n, s_m = d["S"].clone(), d["S"].clone()
+    args = (mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"])
+    o_n = g.gated_recurrent_fwd(*args, s_n, beta_v=d.get("beta_v"))
+    o_m = g.gated_recurrent_fwd(*args, s_m, beta_v=d.get("beta_v"), mapped=True)
+    torch.cuda.synchronize()
+    tol = 1e-5 if mode in ("kda", "gdn") else TOL[torch.float32]
+    eo, es = oracle.rel_l2(np64(o_n), np64(o_m)), oracle.rel_l2(np64(s_n), np64(s_m))
+    print(f"[parity] native vs mapped {mode} decode: o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= tol and es <= tol
