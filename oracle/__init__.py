@@ -17,6 +17,9 @@ Two independent evaluations of the method live here:
   the burn-gdn2 "Architecture" diagram draws around the recurrence (ShortConv and the
   L2-Norm of q and k before it, the Gated RMS Norm with a SiLU gate after it), in numpy
   fp64.
+* ``chunk_states`` -- the state of ``recurrent`` after every whole multiple of the chunk
+  size (the state entering each chunk of the chunked form), by running the same C
+  recurrence span by span.
 * ``recurrent_bwd`` -- the gradient of ``recurrent`` with respect to every input and the
   initial state, by the token-by-token adjoint of the recurrence (chain rule through the
   decay, erase, write and read-out steps, in reverse), fp64, in the same C file.
@@ -158,6 +161,44 @@ def recurrent(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, pairs=None, th
         with ThreadPoolExecutor(max_workers=nthr) as ex:
             list(ex.map(run, pairs))
     return o, S_T
+
+
+def chunk_states(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size=64,
+                 threads=None):
+    """The state entering every chunk: for sequence n and chunk j, the state of the
+    token-by-token recurrence after the first j * chunk_size tokens of the sequence (j = 0:
+    S0, or zeros). Layout as ``recurrent``; returns fp64 [num_chunks, H_v, d_k, d_v] with
+    sequence n's chunks at rows sum_{m<n} ceil(len_m / chunk_size) + j."""
+    q, k, v, w, la, b = (np.asarray(x) for x in (q, k, v, w, log_alpha, b))
+    T_total, H_k, d_k = k.shape
+    H_v, d_v = v.shape[1], v.shape[2]
+    G = H_v // H_k
+    cu = np.array([0, T_total] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    nch = [-(-int(cu[n + 1] - cu[n]) // chunk_size) for n in range(N)]
+    first = np.concatenate([[0], np.cumsum(nch)]).astype(np.int64)
+    out = np.full((int(first[-1]), H_v, d_k, d_v), np.nan)
+
+    def run(pair):
+        n, h = pair
+        hk = h // G
+        S = np.zeros((d_k, d_v)) if S0 is None else _f64(np.asarray(S0)[n, h])
+        for j in range(nch[n]):
+            out[first[n] + j, h] = S
+            s = int(cu[n]) + j * chunk_size
+            e = min(int(cu[n + 1]), s + chunk_size)
+            _, S = sequence(q[s:e, hk], k[s:e, hk], v[s:e, h], w[s:e, h], la[s:e, h],
+                            b[s:e, h], S)
+
+    pairs = [(n, h) for n in range(N) for h in range(H_v)]
+    nthr = threads or default_threads()
+    if nthr <= 1 or len(pairs) <= 1:
+        for pr in pairs:
+            run(pr)
+    else:
+        with ThreadPoolExecutor(max_workers=nthr) as ex:
+            list(ex.map(run, pairs))
+    return out
 
 
 def sequence_bwd(q, k, v, w, log_alpha, b, S0, do, dS_T=None):

@@ -105,6 +105,47 @@ def test_linear_attention_closed_form():
     assert close(ST[0, 0], S_ref)
 
 
+def test_chunk_states_are_linear_attention_prefix_sums():
+    """With alpha = 1 and b = 0 the state after n tokens is S0 + sum_{i<n} k_i (w_i v_i)^T,
+    so the state entering chunk j is that sum up to j * chunk_size; packed sequences
+    (one of them empty) and two value heads on one key head."""
+    rng = np.random.default_rng(31)
+    lens, C, dk, dv = [13, 0, 7], 4, 5, 3
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, la, b, w = rand_case(rng, int(cu[-1]), Hk=1, Hv=2, dk=dk, dv=dv, unit_k=False)
+    la[:] = 0.0
+    b[:] = 0.0
+    S0 = rng.standard_normal((3, 2, dk, dv))
+    ck = oracle.chunk_states(q, k, v, la, b, w, S0=S0, cu_seqlens=cu, chunk_size=C)
+    assert ck.shape == (4 + 0 + 2, 2, dk, dv)
+    row = 0
+    for n, L in enumerate(lens):
+        for j in range(-(-L // C)):
+            for h in range(2):
+                ref = S0[n, h].copy()
+                for i in range(cu[n], cu[n] + j * C):
+                    ref += np.outer(k[i, 0], w[i, h] * v[i, h])
+                assert close(ck[row, h], ref)
+            row += 1
+    assert row == ck.shape[0]
+
+
+def test_chunk_states_resume_to_the_final_state():
+    """General gates: entry 0 is S0, and the recurrence resumed from the last entry over
+    the sequence's last (ragged) chunk ends at the final state of the whole sequence."""
+    rng = np.random.default_rng(32)
+    T, C = 11, 4
+    q, k, v, la, b, w = rand_case(rng, T, Hk=1, Hv=1, dk=5, dv=3)
+    S0 = rng.standard_normal((1, 1, 5, 3))
+    ck = oracle.chunk_states(q, k, v, la, b, w, S0=S0, chunk_size=C)
+    assert ck.shape[0] == 3 and np.array_equal(ck[0], S0[0])
+    _, ST = oracle.recurrent(q, k, v, la, b, w, S0=S0)
+    _, S_end = oracle.recurrent(q[8:], k[8:], v[8:], la[8:], b[8:], w[8:], S0=ck[2][None])
+    assert close(S_end, ST)
+    _, S8 = oracle.recurrent(q[:8], k[:8], v[:8], la[:8], b[:8], w[:8], S0=S0)
+    assert close(ck[2][None], S8)
+
+
 # ---- P4: exact delta-rule retrieval ----------------------------------------------------
 
 def test_exact_retrieval():
