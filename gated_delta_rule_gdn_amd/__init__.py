@@ -45,7 +45,7 @@ class Fusion(ctypes.Structure):
                 ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p),
                 ("norm_eps", ctypes.c_float), ("conv_weight", ctypes.c_void_p),
                 ("conv_state", ctypes.c_void_p), ("conv_silu", ctypes.c_int32),
-                ("gate_mode", ctypes.c_int32)]
+                ("gate_mode", ctypes.c_int32), ("chunk_states", ctypes.c_void_p)]
 
 
 class GDN2Error(RuntimeError):
@@ -118,10 +118,10 @@ def _need_gpu(name: str, t: torch.Tensor, device) -> None:
 
 
 def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight, norm_eps,
-            conv=None, gate_mode=0):
+            conv=None, gate_mode=0, chunk_states=None):
     """The gdn2_fusion argument (None when nothing is fused). ``conv`` is
     (conv_weight, conv_state, conv_silu, channels, num_slots) or None."""
-    if not qk_l2norm and gate is None and conv is None and not gate_mode:
+    if not qk_l2norm and gate is None and conv is None and not gate_mode and chunk_states is None:
         return None
     cw = cs = None
     silu = 0
@@ -143,7 +143,7 @@ def _fusion(dev, out_shape, out_dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
         if norm_weight.dtype != torch.float32 or tuple(norm_weight.shape) != (out_shape[-1],):
             raise ValueError(f"norm_weight must be fp32 [{out_shape[-1]}]")
     return Fusion(1 if qk_l2norm else 0, l2norm_eps, _ptr(gate), _ptr(norm_weight), norm_eps,
-                  _ptr(cw), _ptr(cs), 1 if silu else 0, gate_mode)
+                  _ptr(cw), _ptr(cs), 1 if silu else 0, gate_mode, _ptr(chunk_states))
 
 
 def _gate_shapes(mode, lead, Hv, dk, dv, log_alpha, b, w):
@@ -180,9 +180,13 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
               out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
               qk_l2norm: bool = False, l2norm_eps: float = 1e-6,
               gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
-              norm_eps: float = 1e-5, gate_mode: Optional[str] = None
+              norm_eps: float = 1e-5, gate_mode: Optional[str] = None,
+              chunk_states: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked WY forward. Returns (o [B,T,H_v,d_v], S_T [N,H_v,d_k,d_v] fp32 or None).
+
+    chunk_states: an fp32 [num_chunks(...), H_v, d_k, d_v] buffer that receives the state
+    entering every chunk (see num_chunks for the row of each sequence's chunks).
 
     qk_l2norm: L2-normalise q and k inside the kernels. gate [B,T,H_v,d_v] with norm_weight
     fp32 [d_v]: o is returned through the gated RMS norm o/rms(o) * weight * silu(gate).
@@ -224,8 +228,13 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
     if output_final_state:
         S_T = final_state if final_state is not None else torch.empty(
             N, Hv, dk, dv, dtype=torch.float32, device=dev)
+    if chunk_states is not None:
+        _need_gpu("chunk_states", chunk_states, dev)
+        nc = num_chunks(T if cu_seqlens is None else cu_seqlens, B, chunk_size)
+        if chunk_states.dtype != torch.float32 or chunk_states.shape != (nc, Hv, dk, dv):
+            raise ValueError(f"chunk_states must be fp32 [{nc},{Hv},{dk},{dv}]")
     fu = _fusion(dev, (B, T, Hv, dv), q.dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
-                 norm_eps, gate_mode=gcode)
+                 norm_eps, gate_mode=gcode, chunk_states=chunk_states)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
                               _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(o), _ptr(S_T),
@@ -233,6 +242,18 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
                               None if fu is None else ctypes.byref(fu), stream)
     _raise_on(st)
     return o, S_T
+
+
+def num_chunks(seqlen_or_cu_seqlens, batch: int = 1, chunk_size: int = CHUNK_SIZE) -> int:
+    """Rows of chunk_states: batch * ceil(T / chunk_size) for a dense batch (pass T), or
+    sum_n ceil(len_n / chunk_size) for a packed one (pass cu_seqlens; a device tensor is
+    copied to the host, which synchronises). Sequence n's chunks start at row
+    n * ceil(T / chunk_size), respectively at the sum over the sequences before it."""
+    if isinstance(seqlen_or_cu_seqlens, int):
+        return batch * (-(-seqlen_or_cu_seqlens // chunk_size))
+    cu = torch.as_tensor(seqlen_or_cu_seqlens).cpu().to(torch.int64)
+    lens = cu[1:] - cu[:-1]
+    return int(((lens + chunk_size - 1) // chunk_size).sum())
 
 
 def recurrent_step(q, k, v, log_alpha, b, w, S, out: Optional[torch.Tensor] = None

@@ -73,7 +73,10 @@ gdn2_status take_fusion(const gdn2_fusion *f, const void *o, const gdn2_dims *d,
     out->gate = f->gate;
     out->nw = f->norm_weight;
     out->neps = f->norm_eps;
+    if (f->chunk_states && static_cast<const void *>(f->chunk_states) == o)
+        return fail(GDN2_ERR_BAD_SHAPE, "chunk_states must not alias o");
     out->gmode = f->gate_mode;
+    out->cks = f->chunk_states;
     return GDN2_OK;
 }
 
@@ -170,6 +173,12 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
         return fail(GDN2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     if (o && (o == q || o == k || o == v || o == log_alpha || o == b || o == w))
         return fail(GDN2_ERR_BAD_SHAPE, "o must not alias an input");
+    if (fu.cks) {
+        const void *c = fu.cks;
+        if (c == q || c == k || c == v || c == log_alpha || c == b || c == w || c == S0 ||
+            c == S_T || c == workspace || c == cu_seqlens)
+            return fail(GDN2_ERR_BAD_SHAPE, "chunk_states must not alias an input or output");
+    }
 
     gdn2::ChunkArgs a;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.b = b; a.w = w;
@@ -197,6 +206,7 @@ static gdn2_status recurrent_common(const void *q, const void *k, const void *v,
     gdn2::Fusion fu;
     st = take_fusion(fusion, o, dims, &fu);
     if (st != GDN2_OK) return st;
+    if (fu.cks) return fail(GDN2_ERR_UNSUPPORTED, "chunk_states is an output of gdn2_chunk_fwd only");
     if (state_dtype != GDN2_STATE_F32 && state_dtype != GDN2_STATE_BF16)
         return fail(GDN2_ERR_UNSUPPORTED, "state_dtype must be GDN2_STATE_F32 or GDN2_STATE_BF16");
     if (dims->seqlen < 1) return fail(GDN2_ERR_BAD_SHAPE, "seqlen (tokens per sequence) must be >= 1");

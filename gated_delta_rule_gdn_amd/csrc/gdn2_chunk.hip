@@ -82,6 +82,7 @@ struct ChunkParams {
     const int32_t *map;
     void *o;
     float *S_T;
+    float *S_ck;         // state entering every chunk [chunk][h_v][DK][DV], or NULL
     char *rec;           // first per-(chunk, head) record
     // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of
     // every pair are split into nseg segments of seg_len chunks that run concurrently.
@@ -1160,6 +1161,14 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
         // ---- chain wave ----
         for (int c = cb; c < ce; ++c) {
             const char *cur = smem + ((c - cb) & 1) * BUF;
+            if (p.S_ck) {                   // the state entering chunk c, this wave's columns
+                float *ck = p.S_ck + (static_cast<size_t>(cbase + c) * p.h_v + h) * (DK * DV);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii)
+                        ck[static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = S[rt][ii];
+            }
             raw_barrier();                  // chunk c is staged; chunk c-1 fully consumed
             const u32x4 *wn = reinterpret_cast<const u32x4 *>(cur + R_::Wn);
             const u32x4 *kg = reinterpret_cast<const u32x4 *>(cur + R_::KgT);
@@ -1674,7 +1683,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     const int N = packed ? a.num_seqs : a.batch;
     ChunkParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.b = a.b; p.w = a.w;
-    p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T;
+    p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks;
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
     p.rec = a.workspace + mapb;

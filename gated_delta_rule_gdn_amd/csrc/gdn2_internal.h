@@ -19,6 +19,7 @@ struct Fusion {
     float *cst = nullptr;            // conv state [num_slots][3][C] fp32
     bool csilu = false;
     int gmode = 0;                   // GateMode of the b / w arguments (0: GDN-2 gates)
+    float *cks = nullptr;            // chunked forward: state entering every chunk, or NULL
 };
 
 struct DecodeArgs {

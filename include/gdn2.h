@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 4
+#define GDN2_ABI_VERSION 5
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -117,6 +117,18 @@ typedef enum gdn2_state_dtype {
  *                  GDN2_GATES_FG2_PLUS  b = beta [.., h_v, d_k], w = beta_v [.., h_v, d_v]
  *                The FG2 modes scale the keys by sqrt(beta) inside the kernels, so they
  *                take neither qk_l2norm nor the short convolution (GDN2_ERR_UNSUPPORTED).
+ *
+ * gdn2_chunk_fwd only (the recurrent calls return GDN2_ERR_UNSUPPORTED when it is set):
+ *   chunk_states NULL, or device fp32 [num_chunks][h_v][d_k][d_v]: the state entering
+ *                every chunk of every sequence, the quantity the chunked form hands from one
+ *                chunk to the next (burn-gdn2 docs page, "Architecture", Chunk WY mode): a
+ *                training backward recomputes each chunk from it, and a serving cache can
+ *                resume any sequence at a chunk boundary from it. Chunk j of sequence n is
+ *                entry n * ceil(T / chunk_size) + j of a dense batch, and entry
+ *                sum_{m < n} ceil(len_m / chunk_size) + j of a packed one (len_m =
+ *                cu_seqlens[m+1] - cu_seqlens[m]); entry j holds the state after the first
+ *                j * chunk_size tokens of the sequence (entry 0: S0, or zeros). The caller
+ *                owns it; it must not overlap any input, output or the workspace.
  */
 typedef struct gdn2_fusion {
     int32_t qk_l2norm;
@@ -128,6 +140,7 @@ typedef struct gdn2_fusion {
     float *conv_state;
     int32_t conv_silu;
     int32_t gate_mode;
+    float *chunk_states;
 } gdn2_fusion;
 
 typedef struct gdn2_dims {

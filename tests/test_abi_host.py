@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn2_abi_version() == 4
+    assert L.gdn2_abi_version() == 5
     assert L.gdn2_status_string(0) == b"ok"
     assert b"workspace" in L.gdn2_status_string(4)
     assert L.gdn2_status_string(99) == b"unknown status"
@@ -260,3 +260,21 @@ def test_gate_mode_validation(L):
     assert call(2, dims=Dims(1, 64, 0, 1, 1, 128, 64, 1)) == 2  # FG2 needs d_v = d_k
     assert call(0, w=None) == 1 and call(3, w=None) == 1        # these modes need w
     assert call(1, w=None, o=FAKE) == 2                         # KDA: no w; then o aliases q
+
+
+def test_chunk_states_validation(L):
+    """gdn2_fusion.chunk_states: an output of the chunked forward only, and it may not alias
+    an input, an output or the workspace (each call stops before any launch)."""
+    from gated_delta_rule_gdn_amd import Fusion
+    d = Dims(1, 64, 0, 1, 1, 128, 128, 1)
+    O, WS = ctypes.c_void_p(0x9000), ctypes.c_void_p(0xA000)
+
+    def chunk_call(cks, q=FAKE):
+        fu = Fusion(0, 0.0, None, None, 0.0, None, None, 0, 0, cks)
+        return L.gdn2_chunk_fwd(q, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 64, O, None,
+                                ctypes.byref(d), WS, 1 << 40, ctypes.byref(fu), None)
+    assert chunk_call(O) == 2                         # aliases o
+    assert chunk_call(WS) == 2                        # aliases the workspace
+    assert chunk_call(FAKE, q=ctypes.c_void_p(0xB000)) == 2   # aliases k (and v, b, ...)
+    fu = Fusion(0, 0.0, None, None, 0.0, None, None, 0, 0, ctypes.c_void_p(0xC000))
+    assert fwd(L, Dims(4, 3, 0, 2, 6, 128, 64, 1), o=ctypes.c_void_p(0xD000), fusion=fu) == 3
