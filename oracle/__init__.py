@@ -27,6 +27,8 @@ Two independent evaluations of the method live here:
   models the pages name (the scalar-gate KDA that the "Architecture" section says b and w
   replace, a scalar-decay GDN, and FG2-GDN and FG2-GDN+ of the FG2-GDN summary, section 2),
   each written from its own formula in numpy fp64.
+* ``chunked_sequence_bwd`` -- the gradient taken through that chunked form, step by step
+  (the backward pass chunked kernels follow), checked against ``recurrent_bwd``.
 * ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
   mode) and on the FG^2-GDN summary (section 2C, DPLR structure and the WY
   representation), in numpy fp64. It exists to pin the recurrence: the two are
@@ -466,6 +468,84 @@ def chunked(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size=64):
             o[s:e, h] = on
             S_T[n, h] = Sn
     return o, S_T
+
+
+def chunked_sequence_bwd(q, k, v, w, log_alpha, b, S0, do, dS_T, chunk_size):
+    """Gradient of ``chunked_sequence`` for one pair, taken through the chunked WY form
+    itself (fp64): the backward pass the chunked kernels follow, written out so that it can
+    be checked against the token-by-token adjoint (``sequence_bwd``). With the forward's
+    chunk quantities (g, A, T, W~, U~, U, Mqk, Qg = exp(g).q, Kg = exp(g_L - g).k, the entry
+    state S) and dS' = dL/dS_next, per chunk from the last:
+      dU   = Mqk^T dO + Kg dS'
+      dS   = diag(exp(g_L)) dS' + Qg^T dO - W~^T dU                 (handed to the chunk before)
+      dMqk = lower(dO U^T),  dQg = dO S^T,  dKg = U dS'^T,  dW~ = -dU S^T,  dU~ = dU
+      dX   = T^T dU~ (X = w.v),  dY = T^T dW~ (Y = exp(g).b.k)
+      dT   = dU~ X^T + dW~ Y^T,  dA = strictly-lower(-T^T dT T^T)
+    then the chain rule through A, Mqk, Y, Qg, Kg and exp(g_L) to q, k, b, g, and
+    dlog_alpha_i = sum_{r >= i} dg_r within the chunk. Same outputs as ``sequence_bwd``."""
+    q, k, v, w, la, b, dO = (_f64(x) for x in (q, k, v, w, log_alpha, b, do))
+    T, d_k = k.shape
+    d_v = v.shape[1]
+    S = _f64(S0).copy()
+    starts = list(range(0, T, chunk_size))
+    entry = []
+    for c0 in starts:                      # forward: the state entering each chunk
+        entry.append(S.copy())
+        sl = slice(c0, min(T, c0 + chunk_size))
+        _, S = chunked_sequence(q[sl], k[sl], v[sl], w[sl], la[sl], b[sl], S, chunk_size)
+    out = {n: np.zeros((T, d_k)) for n in ("dq", "dk", "dlog_alpha", "db")}
+    out.update({n: np.zeros((T, d_v)) for n in ("dv", "dw")})
+    dS = np.zeros((d_k, d_v)) if dS_T is None else _f64(dS_T).copy()
+    for c0, S in zip(reversed(starts), reversed(entry)):
+        sl = slice(c0, min(T, c0 + chunk_size))
+        qc, kc, vc, wc, lac, bc, dOc = q[sl], k[sl], v[sl], w[sl], la[sl], b[sl], dO[sl]
+        L = kc.shape[0]
+        g = np.cumsum(lac, axis=0)
+        E = np.exp(g[:, None, :] - g[None, :, :])          # E[r, i] = exp(g_r - g_i)
+        low = np.tril(np.ones((L, L)))
+        slow = np.tril(np.ones((L, L)), -1)
+        bk = bc * kc
+        A = np.einsum("rc,ic,ric->ri", bk, kc, E) * slow
+        Mqk = np.einsum("rc,ic,ric->ri", qc, kc, E) * low
+        Tm = _unit_lower_inverse(np.eye(L) + A)
+        gam = np.exp(g)
+        Y, X = gam * bk, wc * vc
+        W_t, U_t = Tm @ Y, Tm @ X
+        U = U_t - W_t @ S
+        Qg = gam * qc
+        fK = np.exp(g[-1][None, :] - g)
+        Kg = fK * kc
+        # the chunk's own adjoints
+        dU = Mqk.T @ dOc + Kg @ dS
+        dS_prev = gam[-1][:, None] * dS + Qg.T @ dOc - W_t.T @ dU
+        dM = (dOc @ U.T) * low
+        dQg = dOc @ S.T
+        dKg = U @ dS.T
+        dW = -dU @ S.T
+        dgam_L = np.sum(dS * S, axis=1)
+        dX = Tm.T @ dU
+        dY = Tm.T @ dW
+        dT = dU @ X.T + dW @ Y.T
+        dA = -(Tm.T @ dT @ Tm.T) * slow
+        # to the token vectors and g
+        dq = np.einsum("ri,ic,ric->rc", dM, kc, E) + gam * dQg
+        dk = (np.einsum("ri,rc,ric->ic", dM, qc, E) + np.einsum("ri,rc,ric->ic", dA, bk, E)
+              + fK * dKg)
+        dbk = np.einsum("ri,ic,ric->rc", dA, kc, E) + gam * dY
+        tA = np.einsum("ri,rc,ic,ric->ric", dA, bk, kc, E)
+        tM = np.einsum("ri,rc,ic,ric->ric", dM, qc, kc, E)
+        dg = (tA.sum(1) - tA.sum(0) + tM.sum(1) - tM.sum(0)
+              + gam * bk * dY + gam * qc * dQg - fK * kc * dKg)
+        dg[-1] += np.sum(fK * kc * dKg, axis=0) + gam[-1] * dgam_L
+        out["dq"][sl] = dq
+        out["dk"][sl] = dk + bc * dbk
+        out["db"][sl] = kc * dbk
+        out["dv"][sl] = wc * dX
+        out["dw"][sl] = vc * dX
+        out["dlog_alpha"][sl] = np.cumsum(dg[::-1], axis=0)[::-1]
+        dS = dS_prev
+    out["dS0"] = dS
+    return out
 
 
 def variant_sequence(mode, q, k, v, log_alpha, beta, S0, beta_v=None):

@@ -547,6 +547,25 @@ def test_recurrent_bwd_matches_central_differences():
         assert np.allclose(gr[gname], num, rtol=1e-6, atol=1e-7), nm
 
 
+@pytest.mark.parametrize("C", [1, 4, 7, 23, 64])
+def test_chunked_bwd_equals_token_adjoint(C):
+    """The gradient through the chunked WY form (oracle.chunked_sequence_bwd: dU, dS, dMqk,
+    dT, dA and the chain rule through the decay factors) equals the token-by-token adjoint
+    of the recurrence, which the finite-difference and autograd pins fix. Chunk sizes: one
+    token, exact multiples, a ragged tail, one chunk, and a chunk longer than the sequence;
+    erase gates up to 2 (negative eigenvalues) and d_k != d_v."""
+    rng = np.random.default_rng(40 + C)
+    T, dk, dv = 23, 5, 3
+    q, k, v, la, b, w = (x[:, 0] for x in rand_case(rng, T, dk=dk, dv=dv))
+    S0 = rng.standard_normal((dk, dv))
+    do = rng.standard_normal((T, dv))
+    for dST in (None, rng.standard_normal((dk, dv))):
+        ref = oracle.sequence_bwd(q, k, v, w, la, b, S0, do, dST)
+        got = oracle.chunked_sequence_bwd(q, k, v, w, la, b, S0, do, dST, C)
+        for name in ref:
+            assert close(got[name], ref[name], 1e-10), (C, name)
+
+
 def test_recurrent_bwd_matches_torch_autograd_across_checkpoints():
     """An independent evaluation: torch autograd in fp64 through a plain loop of the
     recurrence, at T = 150 (the oracle recomputes states from checkpoints every 64 tokens)."""
