@@ -280,6 +280,42 @@ def bench_gate_variants(steps, warmup, seed=9):
     return res
 
 
+def bench_chunk_states(steps, warmup, seed=10):
+    """The timed chunk workload with the state entering every chunk written out (the
+    checkpoints a training backward starts from), beside the same call without them. The
+    64 MB of fp32 states are added to the algorithmic bytes."""
+    wl = inputs.CHUNK_BF16_T4096
+    x = inputs.chunk_inputs_device(wl, seed)
+    B, T = x["q"].shape[:2]
+    ws = torch.empty(g.chunk_fwd_workspace_bytes(B, T, wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.dtype),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, T, wl.h_v, wl.d_v, dtype=wl.dtype, device="cuda")
+    S_T = torch.empty_like(x["S0"])
+    nc = g.num_chunks(T, B)
+    ck = torch.empty(nc, wl.h_v, wl.d_k, wl.d_v, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call(states):
+        def fn():
+            g.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S0=x["S0"],
+                        workspace=ws, out=o, final_state=S_T,
+                        chunk_states=ck if states else None)
+        return fn
+
+    for _ in range(warmup):
+        call(True)()
+        call(False)()
+    t_on = time_region(call(True), steps, stream)
+    t_off = time_region(call(False), steps, stream)
+    nbytes = chunk_alg(wl, B * T, B)[0] + ck.numel() * 4
+    del x, ws, o, S_T
+    res = {"workload": f"{wl.name}_chunk_states", "us_per_call": t_on * 1e6,
+           "us_per_call_without": t_off * 1e6, "tokens_per_s": T * B / t_on,
+           "alg_bytes": nbytes, "hbm_frac": nbytes / t_on / 1e9 / HBM_PEAK_GBPS}
+    del ck
+    return res
+
+
 def bench_fused(steps, warmup, seed=8):
     """The timed chunk workload and the decode step with the fusions of the burn-gdn2
     "Architecture" diagram turned on (q/k L2-norm before the recurrence, SiLU-gated RMS norm
@@ -598,6 +634,7 @@ def main():
     if args.only == "all" and not args.no_other_workloads:
         out["fused_qkl2norm_gatednorm"] = bench_fused(max(10, args.steps // 2), 3)
         out["gate_variants"] = bench_gate_variants(max(10, args.steps // 4), 3)
+        out["chunk_states"] = bench_chunk_states(max(10, args.steps // 4), 3)
     if args.only in ("chunk", "all") and not args.no_other_workloads:
         out["other_chunk_workloads"] = [
             bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed)
