@@ -40,6 +40,9 @@
  *
  * Streams: every call only enqueues work on `stream` (a hipStream_t; NULL is the default
  * stream) and returns without synchronising. No call reads device memory on the host.
+ * The work enqueued is kernel launches only (no allocation, copy, fill or host
+ * synchronisation), so a caller may capture the calls into a HIP graph and replay it; a
+ * replay reads and writes the buffers given at capture time.
  *
  * Errors: arguments are validated on the host before anything is enqueued; a failed check
  * returns a status code and launches nothing. A failed launch returns GDN2_ERR_HIP. A short

@@ -1,0 +1,93 @@
+"""The library's calls under HIP graph capture: they enqueue only kernels on the caller's
+stream (no allocation, copy, fill or synchronisation), so a caller may capture them. Each
+graph is replayed several times with eager work and synchronisations between the replays,
+and every replay must equal the eager calls bit for bit."""
+import pytest
+import torch
+
+import gated_delta_rule_gdn_amd as g
+from gated_delta_rule_gdn_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("q", "k", "v", "log_alpha", "b", "w")
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g.lib()
+
+
+def capture(fn):
+    """Runs fn once on a side stream (lazy initialisation), then captures it."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def test_chunk_forward_replays_in_a_graph():
+    """A segmented chunked forward (4 pairs, 32 chunks) with the chunk-state output."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=2048, h_k=2, h_v=4, d_k=128,
+                            d_v=128, neg_eig=True)
+    x = {n: t.cuda() if isinstance(t, torch.Tensor) else t
+         for n, t in inputs.chunk_inputs(wl, seed=51).items()}
+    args = [x[n] for n in NAMES]
+    B, T = 1, 2048
+    nbytes = g.chunk_fwd_workspace_bytes(B, T, 2, 4, 128, 128, torch.bfloat16)
+
+    def buffers():
+        return (torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+                torch.empty(B, T, 4, 128, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(1, 4, 128, 128, dtype=torch.float32, device="cuda"),
+                torch.empty(g.num_chunks(T, B), 4, 128, 128, dtype=torch.float32, device="cuda"))
+
+    ws_e, o_e, S_e, ck_e = buffers()
+    g.chunk_fwd(*args, S0=x["S0"], workspace=ws_e, out=o_e, final_state=S_e, chunk_states=ck_e)
+    ws, o, S_T, ck = buffers()
+    graph = capture(lambda: g.chunk_fwd(*args, S0=x["S0"], workspace=ws, out=o, final_state=S_T,
+                                        chunk_states=ck))
+    for rep in range(3):
+        o.zero_()
+        S_T.fill_(float("nan"))
+        ck.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] chunk forward replay {rep}", flush=True)
+        assert torch.equal(o, o_e) and torch.equal(S_T, S_e) and torch.equal(ck, ck_e)
+
+
+def test_decode_steps_replay_in_a_graph():
+    """Four in-place decode steps on one state pool, captured once: every replay advances
+    the state by the same four steps as the eager calls."""
+    wl = inputs.DecodeWorkload("graph_decode", torch.float32, 8, 2, 6, 128, 128, steps=4)
+    x = inputs.decode_inputs(wl, seed=52)
+    d = {n: x[n].cuda() for n in NAMES}
+    S_eager, S_graph = x["S"].cuda(), x["S"].cuda()
+    o_eager = torch.empty(4, 8, 6, 128, device="cuda")
+    o_graph = torch.empty_like(o_eager)
+
+    def steps(S, out):
+        for t in range(4):
+            g.recurrent_step(*(d[n][t] for n in NAMES), S, out=out[t])
+
+    graph = capture(lambda: steps(S_graph, o_graph))
+    S_graph.copy_(x["S"].cuda())           # undo the warm-up and capture-time steps
+    torch.cuda.synchronize()
+    for rep in range(3):
+        steps(S_eager, o_eager)
+        o_graph.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] decode replay {rep}", flush=True)
+        assert torch.equal(o_graph, o_eager) and torch.equal(S_graph, S_eager)
