@@ -316,6 +316,38 @@ def bench_chunk_states(steps, warmup, seed=10):
     return res
 
 
+def bench_chunk_bwd(steps, warmup, seed=11):
+    """The chunked backward (gdn2_chunk_bwd) on the timed chunk workload: the forward re-run
+    that stores the chunk states, the reverse state pass and the per-chunk gradients.
+    Algorithmic bytes: the forward inputs, dO, S0 and dS_T read once, the fp32 gradients
+    written once."""
+    wl = inputs.CHUNK_BF16_T4096
+    x = inputs.chunk_inputs_device(wl, seed)
+    B, T = x["q"].shape[:2]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    dO = torch.randn(B, T, wl.h_v, wl.d_v, generator=gen, device="cuda").to(wl.dtype)
+    dST = torch.randn_like(x["S0"])
+    ws = torch.empty(g.chunk_bwd_workspace_bytes(B, T, wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.dtype),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        g.chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], dO, S0=x["S0"],
+                    dS_T=dST, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    t = time_region(call, steps, torch.cuda.current_stream())
+    e = 2
+    tok_in = T * (2 * wl.h_k * wl.d_k + wl.h_v * (2 * wl.d_k + 3 * wl.d_v)) * e   # q k, la b, v w dO
+    grads = T * (2 * wl.h_k * wl.d_k + wl.h_v * (2 * wl.d_k + 2 * wl.d_v)) * 4
+    states = 3 * x["S0"].numel() * 4                                          # S0, dS_T, dS0
+    nbytes = tok_in + grads + states
+    del x, ws, dO, dST
+    return {"workload": f"{wl.name}_bwd", "us_per_call": t * 1e6, "tokens_per_s": T * B / t,
+            "alg_bytes": nbytes, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+
+
 def bench_fused(steps, warmup, seed=8):
     """The timed chunk workload and the decode step with the fusions of the burn-gdn2
     "Architecture" diagram turned on (q/k L2-norm before the recurrence, SiLU-gated RMS norm
@@ -635,6 +667,7 @@ def main():
         out["fused_qkl2norm_gatednorm"] = bench_fused(max(10, args.steps // 2), 3)
         out["gate_variants"] = bench_gate_variants(max(10, args.steps // 4), 3)
         out["chunk_states"] = bench_chunk_states(max(10, args.steps // 4), 3)
+        out["chunk_bwd"] = bench_chunk_bwd(max(5, args.steps // 10), 2)
     if args.only in ("chunk", "all") and not args.no_other_workloads:
         out["other_chunk_workloads"] = [
             bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed)

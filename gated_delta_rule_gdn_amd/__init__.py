@@ -86,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.gdn2_check_cu_seqlens.argtypes = [vp, i32, i32]
         L.gdn2_map_gates.restype = i32
         L.gdn2_map_gates.argtypes = [i32, dp] + [vp] * 13
+        L.gdn2_chunk_bwd_workspace_bytes.restype = sz
+        L.gdn2_chunk_bwd_workspace_bytes.argtypes = [dp, i32]
+        L.gdn2_chunk_bwd.restype = i32
+        L.gdn2_chunk_bwd.argtypes = [vp] * 8 + [i32] + [vp] * 9 + [dp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -242,6 +246,63 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
                               None if fu is None else ctypes.byref(fu), stream)
     _raise_on(st)
     return o, S_T
+
+
+def chunk_bwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: int, d_v: int,
+                              dtype: torch.dtype, num_seqs: int = 0,
+                              chunk_size: int = CHUNK_SIZE) -> int:
+    d = Dims(batch, seqlen, num_seqs, h_k, h_v, d_k, d_v, _dtype_code(dtype))
+    return int(lib().gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), chunk_size))
+
+
+def chunk_bwd(q, k, v, log_alpha, b, w, dO, S0=None, cu_seqlens=None, dS_T=None,
+              chunk_size: int = CHUNK_SIZE, workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of chunk_fwd (GDN-2 gates, no fusion options) given dO = dL/do and
+    dS_T = dL/dS_T (None: zero). Returns fp32 tensors: dq, dk [B,T,H_k,d_k]; dv, dw
+    [B,T,H_v,d_v]; dlog_alpha, db [B,T,H_v,d_k]; dS0 [N,H_v,d_k,d_v]."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w),
+                    ("dO", dO)):
+        _need_gpu(name, t, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {q.dtype}")
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError("q and k must both be [B,T,H_k,d_k]")
+    B, T, Hk, dk_ = q.shape
+    if v.dim() != 4 or v.shape[:2] != (B, T) or w.shape != v.shape or dO.shape != v.shape:
+        raise ValueError("v, w and dO must be [B,T,H_v,d_v]")
+    Hv, dv_ = v.shape[2], v.shape[3]
+    if log_alpha.shape != (B, T, Hv, dk_) or b.shape != (B, T, Hv, dk_):
+        raise ValueError("log_alpha and b must be [B,T,H_v,d_k]")
+    if cu_seqlens is not None:
+        _need_gpu("cu_seqlens", cu_seqlens, dev)
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-D int32 tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None:
+            _need_gpu(name, t, dev)
+            if t.dtype != torch.float32 or t.shape != (N, Hv, dk_, dv_):
+                raise ValueError(f"{name} must be fp32 [{N},{Hv},{dk_},{dv_}]")
+    dims = Dims(B, T, N if cu_seqlens is not None else 0, Hk, Hv, dk_, dv_, _dtype_code(q.dtype))
+    need = int(lib().gdn2_chunk_bwd_workspace_bytes(ctypes.byref(dims), chunk_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty(B, T, Hk, dk_, **f32), "dk": torch.empty(B, T, Hk, dk_, **f32),
+           "dv": torch.empty(B, T, Hv, dv_, **f32), "dw": torch.empty(B, T, Hv, dv_, **f32),
+           "dlog_alpha": torch.empty(B, T, Hv, dk_, **f32), "db": torch.empty(B, T, Hv, dk_, **f32),
+           "dS0": torch.empty(N, Hv, dk_, dv_, **f32)}
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib().gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                              _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(dO), _ptr(dS_T),
+                              *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dw", "dlog_alpha", "db",
+                                                       "dS0")),
+                              ctypes.byref(dims), _ptr(workspace), workspace.numel(), stream)
+    _raise_on(st)
+    return out
 
 
 def num_chunks(seqlen_or_cu_seqlens, batch: int = 1, chunk_size: int = CHUNK_SIZE) -> int:

@@ -194,6 +194,69 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
     return GDN2_OK;
 }
 
+size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size) {
+    if (!dims) return 0;
+    const bool packed = dims->num_seqs > 0 && dims->batch == 1;
+    if (check_chunk_dims(dims, chunk_size, false) != GDN2_OK &&
+        check_chunk_dims(dims, chunk_size, packed) != GDN2_OK)
+        return 0;
+    const bool bf = dims->dtype == GDN2_BF16;
+    const size_t dense = gdn2::chunk_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->num_seqs,
+                                                          dims->h_v, dims->d_k, dims->d_v, bf, false);
+    const size_t pk = packed ? gdn2::chunk_bwd_workspace_bytes(dims->batch, dims->seqlen,
+                                                               dims->num_seqs, dims->h_v, dims->d_k,
+                                                               dims->d_v, bf, true)
+                             : 0;
+    return dense > pk ? dense : pk;
+}
+
+gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *b, const void *w, const float *S0,
+                           const int32_t *cu_seqlens, int32_t chunk_size, const void *dO,
+                           const float *dS_T, float *dq, float *dk, float *dv, float *dw,
+                           float *dlog_alpha, float *db, float *dS0, const gdn2_dims *dims,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    const bool packed = cu_seqlens != nullptr;
+    gdn2_status st = check_chunk_dims(dims, chunk_size, packed);
+    if (st != GDN2_OK) return st;
+    const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
+    const int N = packed ? dims->num_seqs : dims->batch;
+    if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv ||
+                       !dw || !dlog_alpha || !db))
+        return fail(GDN2_ERR_NULL_ARG, "the inputs, dO and every token gradient are required");
+    if (N > 0 && !dS0) return fail(GDN2_ERR_NULL_ARG, "dS0 is required");
+    const void *outs[] = {dq, dk, dv, dw, dlog_alpha, db, dS0};
+    const void *ins[] = {q, k, v, log_alpha, b, w, S0, cu_seqlens, dO, dS_T, workspace};
+    for (const void *x : outs) {
+        if (!x) continue;
+        for (const void *y : ins)
+            if (x == y) return fail(GDN2_ERR_BAD_SHAPE, "an output aliases an input or the workspace");
+        int same = 0;
+        for (const void *y : outs) same += x == y;
+        if (same > 1) return fail(GDN2_ERR_BAD_SHAPE, "two outputs alias");
+    }
+    const bool bf = dims->dtype == GDN2_BF16;
+    const size_t need = gdn2::chunk_bwd_workspace_bytes(dims->batch, dims->seqlen, dims->num_seqs,
+                                                        dims->h_v, dims->d_k, dims->d_v, bf, packed);
+    if (need > 0 && !workspace) return fail(GDN2_ERR_WORKSPACE, "workspace is NULL");
+    if (workspace_bytes < need) return fail(GDN2_ERR_WORKSPACE, "workspace is too small");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(GDN2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    gdn2::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.b = b; a.w = w;
+    a.S0 = S0; a.cu_seqlens = cu_seqlens; a.dO = dO; a.dS_T = dS_T;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw; a.dla = dlog_alpha; a.db = db; a.dS0 = dS0;
+    a.workspace = static_cast<char *>(workspace);
+    a.batch = dims->batch; a.seqlen = dims->seqlen; a.num_seqs = packed ? dims->num_seqs : 0;
+    a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
+    a.bf16 = bf;
+    const hipError_t e = gdn2::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "gdn2_chunk_bwd launch");
+    g_last_error[0] = '\0';
+    return GDN2_OK;
+}
+
 static gdn2_status recurrent_common(const void *q, const void *k, const void *v,
                                     const void *log_alpha, const void *b, const void *w,
                                     void *S, int32_t state_dtype, const int32_t *idx,

@@ -1,0 +1,509 @@
+// gdn2_bwd.hip -- chunked backward of Gated DeltaNet-2 (gradients of the chunked forward).
+//
+// Method: the chunked WY form of the burn-gdn2 docs page, section "Architecture" (Chunk
+// mode), differentiated chunk by chunk. Within a chunk of C = 64 tokens entering with state
+// S and leaving with S', with g the cumulative log decay over the chunk, gamma = exp(g),
+// gamma_L its last row, E[r,i,c] = exp(g_r[c] - g_i[c]) for i <= r:
+//   A[r,i]  = sum_c b_r k_r k_i E (i < r),   M[r,i] = sum_c q_r k_i E (i <= r),   Tm = (I + A)^-1
+//   Y = gamma.b.k,  X = w.v,  W~ = Tm Y,  U~ = Tm X,  U = U~ - W~ S
+//   Qg = gamma.q,  Kg = exp(gL - g).k,  O = Qg S + M U,  S' = gamma_L S + Kg^T U
+// Given dO and dS' = dL/dS', per chunk from the last:
+//   dU = M^T dO + Kg dS',   dS = gamma_L dS' + Qg^T dO - W~^T dU            (to the chunk before)
+//   dM = lower(dO U^T), dQg = dO S^T, dKg = U dS'^T, dW~ = -dU S^T, dX = Tm^T dU,
+//   dY = Tm^T dW~, dT = dU X^T + dW~ Y^T, dA = strictly-lower(-Tm^T dT Tm^T),
+// then the chain rule through E, Y, Qg, Kg and gamma_L to q, k, b and g, and
+// dlog_alpha_i = sum_{r >= i} dg_r within the chunk.
+//
+// Kernels (one call of gdn2_chunk_bwd, after a chunked forward that writes the state
+// entering every chunk):
+//   bwd_factors_kernel  per (chunk, value head) record, in parallel: g, A, M, Tm, W~, U~,
+//                       Qg, Kg and the dO terms of the chain, M^T dO and Qg^T dO
+//   bwd_chain_kernel    per (sequence, value head, 16 columns), sequential over the chunks
+//                       from the last: dU of every chunk and the dS' it leaves, then dS0
+//   bwd_grads_kernel    per record, in parallel: every input gradient of the chunk
+// The products are fp32 matrix-core tiles (16x16x4) with operands read from the per-record
+// fp32 scratch of the workspace; q and k gradients of value heads that share a key head are
+// summed with fp32 atomics.
+#include "gdn2_common.h"
+#include "gdn2_internal.h"
+#include "gdn2_mfma.h"
+
+namespace gdn2 {
+
+namespace {
+
+constexpr int C = kChunk;
+constexpr int kBwdThreads = 256;
+
+// Per-record fp32 scratch (offsets in floats).
+template <int DK, int DV>
+struct BLay {
+    static constexpr size_t CK = static_cast<size_t>(C) * DK, CV = static_cast<size_t>(C) * DV;
+    static constexpr size_t KV = static_cast<size_t>(DK) * DV, CC = static_cast<size_t>(C) * C;
+    // [C][DK] tiles
+    static constexpr size_t G = 0, K = CK, Q = 2 * CK, BK = 3 * CK, Y = 4 * CK, WT = 5 * CK,
+                            KG = 6 * CK, QG = 7 * CK, DQG = 8 * CK, DKG = 9 * CK, DW = 10 * CK,
+                            DY = 11 * CK;
+    // [C][DV] tiles
+    static constexpr size_t X = 12 * CK, UT = X + CV, E1 = X + 2 * CV, DU = X + 3 * CV,
+                            U = X + 4 * CV, DX = X + 5 * CV;
+    // [DK][DV]
+    static constexpr size_t E2 = X + 6 * CV, DSN = E2 + KV;
+    // [C][C]
+    static constexpr size_t A = DSN + KV, TM = A + CC, M = A + 2 * CC, DM = A + 3 * CC,
+                            DT = A + 4 * CC, TMP = A + 5 * CC, DA = A + 6 * CC;
+    // [DK]
+    static constexpr size_t GL = A + 7 * CC, DGL = GL + DK;
+    static constexpr size_t FLOATS = DGL + DK;
+};
+
+struct BwdParams {
+    const void *q, *k, *v, *la, *b, *w, *dO;
+    const float *dS_T;                 // [N][h_v][DK][DV], or NULL
+    const int32_t *cu, *map;           // packed batches: offsets and chunk map, else NULL
+    const float *ck;                   // state entering every chunk, [record][DK][DV]
+    float *scr;                        // per-record scratch
+    float *dq, *dk, *dv, *dw, *dla, *db, *dS0;
+    int num_seqs, seqlen, nc_dense, h_k, h_v, group;
+};
+
+// chunk -> (sequence n, chunk j of it, token range); false past the last chunk
+__device__ __forceinline__ bool locate(const BwdParams &p, int chunk, int &n, int &j,
+                                       int64_t &start, int64_t &end) {
+    if (p.cu == nullptr) {
+        n = chunk / p.nc_dense;
+        j = chunk - n * p.nc_dense;
+        start = static_cast<int64_t>(n) * p.seqlen;
+        end = start + p.seqlen;
+        return n < p.num_seqs;
+    }
+    if (chunk >= p.map[p.num_seqs]) return false;
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.map[mid] <= chunk) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    j = chunk - p.map[n];
+    start = p.cu[n];
+    end = p.cu[n + 1];
+    return true;
+}
+
+// out[M x N] from sum_k a(m, k) b(k, n) over K (all multiples of 16), 16x16 tiles spread
+// over the workgroup's waves. Lane (li, lg) gives a(m0 + li, k0 + 4 lg + s) and
+// b(k0 + 4 lg + s, n0 + li); it receives out[m0 + 4 lg + ii][n0 + li].
+template <class FA, class FB, class FS>
+__device__ void block_mm(int M, int N, int K, FA a, FB b, FS store) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int nw = blockDim.x >> 6, tn = N / 16, tiles = (M / 16) * tn;
+    for (int t = wave; t < tiles; t += nw) {
+        const int m0 = (t / tn) * 16, n0 = (t - (t / tn) * tn) * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            f32x4 av, bv;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                av[s] = a(m0 + li, k0 + 4 * lg + s);
+                bv[s] = b(k0 + 4 * lg + s, n0 + li);
+            }
+            acc = mma_k16_f32(av, bv, acc);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) store(m0 + 4 * lg + ii, n0 + li, acc[ii]);
+    }
+}
+
+template <typename T>
+__global__ void zero_kernel(float *a, float *b, int64_t n) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        a[i] = 0.f;
+        b[i] = 0.f;
+    }
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
+    using L_ = BLay<DK, DV>;
+    const int rec = blockIdx.x, chunk = rec / p.h_v, h = rec - chunk * p.h_v;
+    int n, j;
+    int64_t start, end;
+    if (!locate(p, chunk, n, j, start, end)) return;
+    const int64_t t0 = start + static_cast<int64_t>(j) * C;
+    const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
+    const int hk = h / p.group, tid = threadIdx.x;
+    const T *q = static_cast<const T *>(p.q), *k = static_cast<const T *>(p.k);
+    const T *v = static_cast<const T *>(p.v), *la = static_cast<const T *>(p.la);
+    const T *b = static_cast<const T *>(p.b), *w = static_cast<const T *>(p.w);
+    const T *dO = static_cast<const T *>(p.dO);
+    float *s = p.scr + static_cast<size_t>(rec) * L_::FLOATS;
+
+    // token vectors, the cumulative decay and the elementwise factors (rows >= Lr are
+    // identity tokens: k = q = b = w.v = 0, log alpha = 0)
+    if (tid < DK) {
+        const int c = tid;
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            float kk = 0.f, qq = 0.f, bb = 0.f;
+            if (r < Lr) {
+                const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c;
+                const size_t og = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c;
+                kk = io<T>::ld(k + ok);
+                qq = io<T>::ld(q + ok);
+                bb = io<T>::ld(b + og);
+                acc += io<T>::ld(la + og);
+            }
+            s[L_::G + r * DK + c] = acc;
+            s[L_::K + r * DK + c] = kk;
+            s[L_::Q + r * DK + c] = qq;
+            s[L_::BK + r * DK + c] = bb * kk;
+        }
+        s[L_::GL + c] = acc;
+        for (int r = 0; r < C; ++r) {
+            const float g = s[L_::G + r * DK + c];
+            const float ga = __expf(g);
+            s[L_::Y + r * DK + c] = ga * s[L_::BK + r * DK + c];
+            s[L_::QG + r * DK + c] = ga * s[L_::Q + r * DK + c];
+            s[L_::KG + r * DK + c] = __expf(acc - g) * s[L_::K + r * DK + c];
+        }
+    } else if (tid < DK + DV) {
+        const int c = tid - DK;
+        for (int r = 0; r < C; ++r) {
+            float x = 0.f;
+            if (r < Lr) {
+                const size_t ov = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c;
+                x = io<T>::ld(w + ov) * io<T>::ld(v + ov);
+            }
+            s[L_::X + r * DV + c] = x;
+        }
+    }
+    __syncthreads();
+    // A and M, one (r, i) entry per thread at a time
+    for (int e = tid; e < C * C; e += kBwdThreads) {
+        const int r = e / C, i = e - r * C;
+        float a = 0.f, m = 0.f;
+        if (i <= r) {
+            for (int c = 0; c < DK; ++c) {
+                const float ex = __expf(s[L_::G + r * DK + c] - s[L_::G + i * DK + c]);
+                const float ki = s[L_::K + i * DK + c];
+                m += s[L_::Q + r * DK + c] * ki * ex;
+                a += s[L_::BK + r * DK + c] * ki * ex;
+            }
+        }
+        s[L_::A + e] = i < r ? a : 0.f;
+        s[L_::M + e] = m;
+    }
+    __syncthreads();
+    // Tm = (I + A)^-1 by forward substitution, one column per thread
+    if (tid < C) {
+        const int jc = tid;
+        for (int r = 0; r < C; ++r) {
+            float t = r == jc ? 1.f : 0.f;
+            for (int i = jc; i < r; ++i) t -= s[L_::A + r * C + i] * s[L_::TM + i * C + jc];
+            s[L_::TM + r * C + jc] = r < jc ? 0.f : t;
+        }
+    }
+    __syncthreads();
+    const float *sc = s;
+    block_mm(C, DK, C, [&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
+             [&](int kk, int nn) { return sc[L_::Y + kk * DK + nn]; },
+             [&](int m, int nn, float x) { s[L_::WT + m * DK + nn] = x; });
+    block_mm(C, DV, C, [&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
+             [&](int kk, int nn) { return sc[L_::X + kk * DV + nn]; },
+             [&](int m, int nn, float x) { s[L_::UT + m * DV + nn] = x; });
+    auto dO_at = [&](int r, int c) {
+        return r < Lr ? io<T>::ld(dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c) : 0.f;
+    };
+    block_mm(C, DV, C, [&](int m, int kk) { return sc[L_::M + kk * C + m]; }, dO_at,
+             [&](int m, int nn, float x) { s[L_::E1 + m * DV + nn] = x; });
+    block_mm(DK, DV, C, [&](int m, int kk) { return sc[L_::QG + kk * DK + m]; }, dO_at,
+             [&](int m, int nn, float x) { s[L_::E2 + m * DV + nn] = x; });
+}
+
+// One wave per (sequence, value head, 16 columns of the state).
+template <int DK, int DV>
+__global__ __launch_bounds__(64) void bwd_chain_kernel(BwdParams p) {
+    using L_ = BLay<DK, DV>;
+    constexpr int RT = DK / 16, NS = DV / 16;
+    const int unit = blockIdx.x, pair = unit / NS, sl = unit - pair * NS;
+    const int n = pair / p.h_v, h = pair - n * p.h_v;
+    const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4, col = 16 * sl + li;
+    int64_t start, end;
+    int cbase;
+    if (p.cu == nullptr) {
+        start = static_cast<int64_t>(n) * p.seqlen;
+        end = start + p.seqlen;
+        cbase = n * p.nc_dense;
+    } else {
+        start = p.cu[n];
+        end = p.cu[n + 1];
+        cbase = p.map[n];
+    }
+    const int nchunks = static_cast<int>((end - start + C - 1) / C);
+    f32x4 D[RT];                                   // dS' rows 16 rt + 4 lg + ii, column col
+    const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            D[rt][ii] = p.dS_T ? p.dS_T[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] : 0.f;
+    for (int c = nchunks - 1; c >= 0; --c) {
+        float *s = p.scr + (static_cast<size_t>(cbase + c) * p.h_v + h) * L_::FLOATS;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                s[L_::DSN + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = D[rt][ii];
+        // dU = M^T dO + Kg dS'
+        f32x4 U4[C / 16];
+#pragma unroll
+        for (int ut = 0; ut < C / 16; ++ut) {
+            f32x4 acc;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[ii] = s[L_::E1 + (16 * ut + 4 * lg + ii) * DV + col];
+#pragma unroll
+            for (int kt = 0; kt < RT; ++kt) {
+                f32x4 av;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) av[e] = s[L_::KG + (16 * ut + li) * DK + 16 * kt + 4 * lg + e];
+                acc = mma_k16_f32(av, D[kt], acc);
+            }
+            U4[ut] = acc;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) s[L_::DU + (16 * ut + 4 * lg + ii) * DV + col] = acc[ii];
+        }
+        // dS = gamma_L dS' + Qg^T dO - W~^T dU
+        f32x4 Dn[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            f32x4 acc;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int row = 16 * rt + 4 * lg + ii;
+                acc[ii] = __expf(s[L_::GL + row]) * D[rt][ii] + s[L_::E2 + static_cast<size_t>(row) * DV + col];
+            }
+#pragma unroll
+            for (int kt = 0; kt < C / 16; ++kt) {
+                f32x4 av;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) av[e] = -s[L_::WT + (16 * kt + 4 * lg + e) * DK + 16 * rt + li];
+                acc = mma_k16_f32(av, U4[kt], acc);
+            }
+            Dn[rt] = acc;
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) D[rt] = Dn[rt];
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            p.dS0[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = D[rt][ii];
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
+    using L_ = BLay<DK, DV>;
+    const int rec = blockIdx.x, chunk = rec / p.h_v, h = rec - chunk * p.h_v;
+    int n, j;
+    int64_t start, end;
+    if (!locate(p, chunk, n, j, start, end)) return;
+    const int64_t t0 = start + static_cast<int64_t>(j) * C;
+    const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
+    const int hk = h / p.group, tid = threadIdx.x;
+    const T *b = static_cast<const T *>(p.b), *w = static_cast<const T *>(p.w);
+    const T *v = static_cast<const T *>(p.v), *dO = static_cast<const T *>(p.dO);
+    float *s = p.scr + static_cast<size_t>(rec) * L_::FLOATS;
+    const float *sc = s;
+    const float *S = p.ck + static_cast<size_t>(rec) * DK * DV;     // state entering the chunk
+    auto dO_at = [&](int r, int c) {
+        return r < Lr ? io<T>::ld(dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c) : 0.f;
+    };
+
+    // U = U~ - W~ S
+    block_mm(C, DV, DK, [&](int m, int kk) { return sc[L_::WT + m * DK + kk]; },
+             [&](int kk, int nn) { return S[kk * DV + nn]; },
+             [&](int m, int nn, float x) { s[L_::U + m * DV + nn] = sc[L_::UT + m * DV + nn] - x; });
+    __syncthreads();
+    // dM = lower(dO U^T), dQg = dO S^T, dKg = U dS'^T, dW~ = -dU S^T, dX = Tm^T dU
+    block_mm(C, C, DV, dO_at, [&](int kk, int nn) { return sc[L_::U + nn * DV + kk]; },
+             [&](int m, int nn, float x) { s[L_::DM + m * C + nn] = nn <= m ? x : 0.f; });
+    block_mm(C, DK, DV, dO_at, [&](int kk, int nn) { return S[nn * DV + kk]; },
+             [&](int m, int nn, float x) { s[L_::DQG + m * DK + nn] = x; });
+    block_mm(C, DK, DV, [&](int m, int kk) { return sc[L_::U + m * DV + kk]; },
+             [&](int kk, int nn) { return sc[L_::DSN + nn * DV + kk]; },
+             [&](int m, int nn, float x) { s[L_::DKG + m * DK + nn] = x; });
+    block_mm(C, DK, DV, [&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
+             [&](int kk, int nn) { return S[nn * DV + kk]; },
+             [&](int m, int nn, float x) { s[L_::DW + m * DK + nn] = -x; });
+    block_mm(C, DV, C, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+             [&](int kk, int nn) { return sc[L_::DU + kk * DV + nn]; },
+             [&](int m, int nn, float x) { s[L_::DX + m * DV + nn] = x; });
+    for (int c = tid; c < DK; c += kBwdThreads) {      // dL/d gamma_L (before the exp)
+        float acc = 0.f;
+        for (int vv = 0; vv < DV; ++vv)
+            acc += sc[L_::DSN + static_cast<size_t>(c) * DV + vv] * S[static_cast<size_t>(c) * DV + vv];
+        s[L_::DGL + c] = acc;
+    }
+    __syncthreads();
+    // dY = Tm^T dW~, dT = dU X^T + dW~ Y^T
+    block_mm(C, DK, C, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+             [&](int kk, int nn) { return sc[L_::DW + kk * DK + nn]; },
+             [&](int m, int nn, float x) { s[L_::DY + m * DK + nn] = x; });
+    block_mm(C, C, DV, [&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
+             [&](int kk, int nn) { return sc[L_::X + nn * DV + kk]; },
+             [&](int m, int nn, float x) { s[L_::DT + m * C + nn] = x; });
+    __syncthreads();
+    block_mm(C, C, DK, [&](int m, int kk) { return sc[L_::DW + m * DK + kk]; },
+             [&](int kk, int nn) { return sc[L_::Y + nn * DK + kk]; },
+             [&](int m, int nn, float x) { s[L_::DT + m * C + nn] += x; });
+    __syncthreads();
+    // dA = strictly-lower(-Tm^T dT Tm^T)
+    block_mm(C, C, C, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+             [&](int kk, int nn) { return sc[L_::DT + kk * C + nn]; },
+             [&](int m, int nn, float x) { s[L_::TMP + m * C + nn] = x; });
+    __syncthreads();
+    block_mm(C, C, C, [&](int m, int kk) { return sc[L_::TMP + m * C + kk]; },
+             [&](int kk, int nn) { return sc[L_::TM + nn * C + kk]; },
+             [&](int m, int nn, float x) { s[L_::DA + m * C + nn] = nn < m ? -x : 0.f; });
+    __syncthreads();
+    // through E, Y, Qg, Kg to q, k, b and g; one (row x, key channel c) per thread
+    float *dq = p.dq, *dk = p.dk;
+    for (int e = tid; e < C * DK; e += kBwdThreads) {
+        const int x = e / DK, c = e - x * DK;
+        const float gx = sc[L_::G + x * DK + c];
+        float p1 = 0.f, p2 = 0.f, p3 = 0.f, p4 = 0.f;
+        for (int i = 0; i <= x; ++i) {             // i <= x: E[x, i]
+            const float ex = __expf(gx - sc[L_::G + i * DK + c]);
+            const float ki = sc[L_::K + i * DK + c];
+            p1 += sc[L_::DA + x * C + i] * ki * ex;
+            p3 += sc[L_::DM + x * C + i] * ki * ex;
+        }
+        for (int r = x; r < C; ++r) {              // r >= x: E[r, x]
+            const float ex = __expf(sc[L_::G + r * DK + c] - gx);
+            p2 += sc[L_::DA + r * C + x] * sc[L_::BK + r * DK + c] * ex;
+            p4 += sc[L_::DM + r * C + x] * sc[L_::Q + r * DK + c] * ex;
+        }
+        const float ga = __expf(gx), fk = __expf(sc[L_::GL + c] - gx);
+        const float kk = sc[L_::K + x * DK + c], qq = sc[L_::Q + x * DK + c];
+        const float bk = sc[L_::BK + x * DK + c];
+        const float dy = sc[L_::DY + x * DK + c], dqg = sc[L_::DQG + x * DK + c];
+        const float dkg = sc[L_::DKG + x * DK + c];
+        const float bb = x < Lr ? io<T>::ld(b + (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c) : 0.f;
+        const float dbk = p1 + ga * dy;
+        const float dgv = bk * p1 - kk * p2 + qq * p3 - kk * p4 + ga * bk * dy + ga * qq * dqg -
+                          fk * kk * dkg;
+        s[L_::DY + x * DK + c] = dgv;              // this thread's own entries, read above
+        s[L_::DKG + x * DK + c] = fk * kk * dkg;
+        if (x < Lr) {
+            const size_t ok = (static_cast<size_t>(t0 + x) * p.h_k + hk) * DK + c;
+            const size_t og = (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c;
+            atomicAdd(dq + ok, p3 + ga * dqg);
+            atomicAdd(dk + ok, p4 + p2 + fk * dkg + bb * dbk);
+            p.db[og] = kk * dbk;
+        }
+    }
+    for (int e = tid; e < C * DV; e += kBwdThreads) {
+        const int x = e / DV, c = e - x * DV;
+        if (x < Lr) {
+            const size_t ov = (static_cast<size_t>(t0 + x) * p.h_v + h) * DV + c;
+            const float dx = sc[L_::DX + x * DV + c];
+            p.dv[ov] = io<T>::ld(w + ov) * dx;
+            p.dw[ov] = io<T>::ld(v + ov) * dx;
+        }
+    }
+    __syncthreads();
+    // d log alpha: reverse cumulative sum of dg, with the gamma_L terms on the last row
+    for (int c = tid; c < DK; c += kBwdThreads) {
+        float acc = __expf(sc[L_::GL + c]) * sc[L_::DGL + c];
+        for (int x = 0; x < C; ++x) acc += sc[L_::DKG + x * DK + c];
+        for (int x = C - 1; x >= 0; --x) {
+            acc += sc[L_::DY + x * DK + c];
+            if (x < Lr) p.dla[(static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c] = acc;
+        }
+    }
+}
+
+template <typename T, int DK, int DV>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
+    static_assert(BLay<DK, DV>::FLOATS == 12 * static_cast<size_t>(C) * DK + 6 * static_cast<size_t>(C) * DV +
+                      2 * static_cast<size_t>(DK) * DV + 7 * static_cast<size_t>(C) * C + 2 * DK,
+                  "the per-record scratch matches chunk_bwd_workspace_bytes");
+    const bool packed = a.cu_seqlens != nullptr;
+    const int N = packed ? a.num_seqs : a.batch;
+    const int64_t nrec = chunk_upper_bound(a.batch, a.seqlen, a.num_seqs, packed) * a.h_v;
+    char *base = a.workspace;
+    const size_t fwd_ws = chunk_workspace_bytes(a.batch, a.seqlen, a.num_seqs, a.h_v, DK, DV,
+                                                a.bf16, packed);
+    float *ck = reinterpret_cast<float *>(base + fwd_ws);
+    char *o_scratch = base + (fwd_ws + static_cast<size_t>(nrec) * DK * DV * 4 + 255) / 256 * 256;
+    const size_t o_bytes = (static_cast<size_t>(a.batch) * a.seqlen * a.h_v * DV * sizeof(T) + 255) / 256 * 256;
+    float *scr = reinterpret_cast<float *>(o_scratch + o_bytes);
+
+    ChunkArgs f;
+    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.b = a.b; f.w = a.w;
+    f.S0 = a.S0; f.cu_seqlens = a.cu_seqlens; f.o = o_scratch; f.S_T = nullptr;
+    f.workspace = base;
+    f.batch = a.batch; f.seqlen = a.seqlen; f.num_seqs = a.num_seqs;
+    f.h_k = a.h_k; f.h_v = a.h_v; f.d_k = DK; f.d_v = DV; f.bf16 = a.bf16;
+    f.fu = Fusion{};
+    f.fu.cks = ck;
+    hipError_t e = launch_chunk_fwd(f, st);
+    if (e != hipSuccess) return e;
+
+    BwdParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.la = a.log_alpha; p.b = a.b; p.w = a.w; p.dO = a.dO;
+    p.dS_T = a.dS_T;
+    p.cu = a.cu_seqlens;
+    p.map = packed ? reinterpret_cast<const int32_t *>(base) : nullptr;
+    p.ck = ck;
+    p.scr = scr;
+    p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dw = a.dw; p.dla = a.dla; p.db = a.db; p.dS0 = a.dS0;
+    p.num_seqs = N; p.seqlen = a.seqlen;
+    p.nc_dense = (a.seqlen + C - 1) / C;
+    p.h_k = a.h_k; p.h_v = a.h_v; p.group = a.h_v / a.h_k;
+    const int64_t qk = static_cast<int64_t>(a.batch) * a.seqlen * a.h_k * DK;
+    if (qk > 0) {
+        const int64_t blocks = (qk + 255) / 256;
+        hipLaunchKernelGGL((zero_kernel<T>), dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
+                           a.dq, a.dk, qk);
+    }
+    if (nrec > 0) {
+        hipLaunchKernelGGL((bwd_factors_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), 0, st, p);
+    }
+    const int64_t units = static_cast<int64_t>(N) * a.h_v * (DV / 16);
+    if (units > 0) hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units), dim3(64), 0, st, p);
+    if (nrec > 0) {
+        hipLaunchKernelGGL((bwd_grads_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_dt(const BwdArgs &a, hipStream_t st) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_bwd_t<T, 128, 128>(a, st);
+    if (a.d_k == 64 && a.d_v == 64) return launch_bwd_t<T, 64, 64>(a, st);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bwd_t<T, 128, 64>(a, st);
+    return launch_bwd_t<T, 64, 128>(a, st);
+}
+
+}  // namespace
+
+size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
+                                 bool bf16, bool packed) {
+    const int64_t nrec = chunk_upper_bound(batch, seqlen, num_seqs, packed) * h_v;
+    // (the floats of BLay<d_k, d_v>)
+    const size_t per = 4 * (12 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * d_v +
+                            2 * static_cast<size_t>(d_k) * d_v + 7 * static_cast<size_t>(C) * C + 2 * d_k);
+    const size_t o_bytes = (static_cast<size_t>(batch) * seqlen * h_v * d_v * (bf16 ? 2 : 4) + 255) / 256 * 256;
+    const size_t head = (chunk_workspace_bytes(batch, seqlen, num_seqs, h_v, d_k, d_v, bf16, packed) +
+                         static_cast<size_t>(nrec) * d_k * d_v * 4 + 255) / 256 * 256;
+    return head + o_bytes + static_cast<size_t>(nrec) * per;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t st) {
+    return a.bf16 ? launch_bwd_dt<bf16_t>(a, st) : launch_bwd_dt<float>(a, st);
+}
+
+}  // namespace gdn2

@@ -55,6 +55,23 @@ size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d
                              bool bf16, bool packed);
 bool chunk_dims_built(int d_k, int d_v, bool bf16);
 
+// Chunked backward (gdn2_chunk_bwd). Workspace: the forward's, then the state entering every
+// chunk (fp32), a scratch o, then a per-record fp32 scratch.
+struct BwdArgs {
+    const void *q, *k, *v, *log_alpha, *b, *w;
+    const float *S0;
+    const int32_t *cu_seqlens;
+    const void *dO;
+    const float *dS_T;
+    float *dq, *dk, *dv, *dw, *dla, *db, *dS0;
+    char *workspace;
+    int batch, seqlen, num_seqs, h_k, h_v, d_k, d_v;
+    bool bf16;
+};
+size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
+                                 bool bf16, bool packed);
+hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t st);
+
 // Gate mappings of other delta-rule variants onto the GDN-2 inputs (gdn2_map_gates).
 enum GateMode { GATES_GDN2 = 0, GATES_KDA = 1, GATES_FG2 = 2, GATES_FG2_PLUS = 3, GATES_GDN = 4 };
 

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 5
+#define GDN2_ABI_VERSION 6
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -204,6 +204,38 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                            void *o, float *S_T, const gdn2_dims *dims,
                            void *workspace, size_t workspace_bytes,
                            const gdn2_fusion *fusion, void *stream);
+
+/*
+ * Bytes of device workspace gdn2_chunk_bwd needs for these dims and chunk size, or 0 if
+ * the dims are invalid (same upper bound on the chunks of a packed batch as the forward).
+ */
+size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size);
+
+/*
+ * Gradients of gdn2_chunk_fwd (without fusion options, GDN-2 gates) with respect to every
+ * input and the initial state, taken through the chunked form of the burn-gdn2 docs page
+ * ("Architecture", Chunk mode; its Chunk WY training path): the forward is re-run to store
+ * the state entering every chunk, then one pass runs the state gradient backward over the
+ * chunks, and one pass per chunk forms the input gradients.
+ *
+ *   q .. w, S0, cu_seqlens, chunk_size, dims   as for gdn2_chunk_fwd
+ *   dO          device [B, T, h_v, d_v] in the input dtype: dL/do
+ *   dS_T        device fp32 [N, h_v, d_k, d_v]: dL/dS_T, or NULL for zero
+ *   dq, dk      device fp32 [B, T, h_k, d_k]   (value heads that share a key head add up)
+ *   dv, dw      device fp32 [B, T, h_v, d_v]
+ *   dlog_alpha, db   device fp32 [B, T, h_v, d_k]
+ *   dS0         device fp32 [N, h_v, d_k, d_v]: dL/dS0 (written also when S0 is NULL)
+ *   workspace   at least gdn2_chunk_bwd_workspace_bytes() bytes, 256-byte aligned
+ * Outputs must not alias inputs or each other. Every output is overwritten.
+ * Returns GDN2_OK or an error status (nothing is enqueued on a validation error).
+ */
+gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v,
+                           const void *log_alpha, const void *b, const void *w,
+                           const float *S0, const int32_t *cu_seqlens, int32_t chunk_size,
+                           const void *dO, const float *dS_T, float *dq, float *dk, float *dv,
+                           float *dw, float *dlog_alpha, float *db, float *dS0,
+                           const gdn2_dims *dims, void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /*
  * One decode step for N sequences, one token each (burn-gdn2 "FusedRecurrent" mode; the

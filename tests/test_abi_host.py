@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn2_abi_version() == 5
+    assert L.gdn2_abi_version() == 6
     assert L.gdn2_status_string(0) == b"ok"
     assert b"workspace" in L.gdn2_status_string(4)
     assert L.gdn2_status_string(99) == b"unknown status"
@@ -278,3 +278,27 @@ def test_chunk_states_validation(L):
     assert chunk_call(FAKE, q=ctypes.c_void_p(0xB000)) == 2   # aliases k (and v, b, ...)
     fu = Fusion(0, 0.0, None, None, 0.0, None, None, 0, 0, ctypes.c_void_p(0xC000))
     assert fwd(L, Dims(4, 3, 0, 2, 6, 128, 64, 1), o=ctypes.c_void_p(0xD000), fusion=fu) == 3
+
+
+def test_chunk_bwd_validation(L):
+    """gdn2_chunk_bwd: bad dims, missing pointers, outputs aliasing inputs or each other and
+    a short workspace stop at host validation (nothing is launched)."""
+    d = Dims(2, 100, 0, 2, 4, 128, 128, 1)
+    P = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(20)]
+    need = L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 64)
+    assert need > L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64)
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(Dims(2, 100, 0, 2, 4, 32, 128, 1)), 64) == 0
+
+    def call(dims=d, outs=None, ws=P[19], ws_bytes=None, dO=P[8]):
+        o = P[10:17] if outs is None else outs
+        return L.gdn2_chunk_bwd(P[0], P[1], P[2], P[3], P[4], P[5], None, None, 64, dO, None,
+                                *o, ctypes.byref(dims), ws, need if ws_bytes is None else ws_bytes,
+                                None)
+    assert call(dims=Dims(2, 100, 0, 2, 4, 128, 128, 7)) == 3          # dtype
+    assert call(dims=Dims(2, 100, 0, 2, 5, 128, 128, 1)) == 2          # h_v not a multiple of h_k
+    assert call(dO=None) == 1
+    assert call(outs=[None] + P[11:17]) == 1
+    assert call(outs=[P[0]] + P[11:17]) == 2                           # dq aliases q
+    assert call(outs=[P[10], P[10]] + P[12:17]) == 2                   # dq and dk alias
+    assert call(ws_bytes=need - 1) == 4
+    assert call(ws=ctypes.c_void_p(0x10001)) == 4                      # misaligned workspace
