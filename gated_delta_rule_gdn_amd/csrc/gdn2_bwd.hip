@@ -33,7 +33,7 @@ namespace gdn2 {
 namespace {
 
 constexpr int C = kChunk;
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 512;
 
 // Per-record fp32 scratch (offsets in floats).
 template <int DK, int DV>
@@ -55,6 +55,22 @@ struct BLay {
     // [DK]
     static constexpr size_t GL = A + 7 * CC, DGL = GL + DK;
     static constexpr size_t FLOATS = DGL + DK;
+};
+
+// LDS copies of g, k, q and b.k of one record, rows padded to DK + 1 floats so that the
+// lanes of a wave reading one channel of consecutive rows hit different banks.
+template <int DK>
+struct KeyTiles {
+    static constexpr int SP = DK + 1;
+    static constexpr int BYTES = 4 * C * SP * 4;
+    float *g, *k, *q, *bk;
+    __device__ explicit KeyTiles(char *base) {
+        float *f = reinterpret_cast<float *>(base);
+        g = f;
+        k = f + C * SP;
+        q = f + 2 * C * SP;
+        bk = f + 3 * C * SP;
+    }
 };
 
 struct BwdParams {
@@ -90,25 +106,28 @@ __device__ __forceinline__ bool locate(const BwdParams &p, int chunk, int &n, in
     return true;
 }
 
-// out[M x N] from sum_k a(m, k) b(k, n) over K (all multiples of 16), 16x16 tiles spread
-// over the workgroup's waves. Lane (li, lg) gives a(m0 + li, k0 + 4 lg + s) and
-// b(k0 + 4 lg + s, n0 + li); it receives out[m0 + 4 lg + ii][n0 + li].
-template <class FA, class FB, class FS>
-__device__ void block_mm(int M, int N, int K, FA a, FB b, FS store) {
+// out[M x N] from sum_k a(m, k) b(k, n) (all sizes multiples of 16), 16x16 tiles spread
+// over the workgroup's waves; each tile's operands are all loaded before its products.
+// Lane (li, lg) gives a(m0 + li, k0 + 4 lg + s) and b(k0 + 4 lg + s, n0 + li); it
+// receives out[m0 + 4 lg + ii][n0 + li].
+template <int M, int N, int K, class FA, class FB, class FS>
+__device__ void block_mm(FA a, FB b, FS store) {
+    constexpr int TN = N / 16, TILES = (M / 16) * TN, KS = K / 16;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
-    const int nw = blockDim.x >> 6, tn = N / 16, tiles = (M / 16) * tn;
-    for (int t = wave; t < tiles; t += nw) {
-        const int m0 = (t / tn) * 16, n0 = (t - (t / tn) * tn) * 16;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < K; k0 += 16) {
-            f32x4 av, bv;
+    const int nw = blockDim.x >> 6;
+    for (int t = wave; t < TILES; t += nw) {
+        const int m0 = (t / TN) * 16, n0 = (t - (t / TN) * TN) * 16;
+        f32x4 av[KS], bv[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                av[s] = a(m0 + li, k0 + 4 * lg + s);
-                bv[s] = b(k0 + 4 * lg + s, n0 + li);
+                av[ks][s] = a(m0 + li, 16 * ks + 4 * lg + s);
+                bv[ks][s] = b(16 * ks + 4 * lg + s, n0 + li);
             }
-            acc = mma_k16_f32(av, bv, acc);
-        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mma_k16_f32(av[ks], bv[ks], acc);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) store(m0 + 4 * lg + ii, n0 + li, acc[ii]);
     }
@@ -138,57 +157,71 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
     const T *b = static_cast<const T *>(p.b), *w = static_cast<const T *>(p.w);
     const T *dO = static_cast<const T *>(p.dO);
     float *s = p.scr + static_cast<size_t>(rec) * L_::FLOATS;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    KeyTiles<DK> lt(smem);
+    constexpr int SP = KeyTiles<DK>::SP;
 
-    // token vectors, the cumulative decay and the elementwise factors (rows >= Lr are
-    // identity tokens: k = q = b = w.v = 0, log alpha = 0)
-    if (tid < DK) {
-        const int c = tid;
-        float acc = 0.f;
-        for (int r = 0; r < C; ++r) {
-            float kk = 0.f, qq = 0.f, bb = 0.f;
-            if (r < Lr) {
-                const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c;
-                const size_t og = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c;
-                kk = io<T>::ld(k + ok);
-                qq = io<T>::ld(q + ok);
-                bb = io<T>::ld(b + og);
-                acc += io<T>::ld(la + og);
-            }
-            s[L_::G + r * DK + c] = acc;
-            s[L_::K + r * DK + c] = kk;
-            s[L_::Q + r * DK + c] = qq;
-            s[L_::BK + r * DK + c] = bb * kk;
+    // token vectors (rows >= Lr are identity tokens: k = q = b = w.v = 0, log alpha = 0),
+    // one (row, channel) per thread at a time
+    for (int e = tid; e < C * DK; e += kBwdThreads) {
+        const int r = e / DK, c = e - r * DK;
+        float kk = 0.f, qq = 0.f, bb = 0.f, ll = 0.f;
+        if (r < Lr) {
+            const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c;
+            const size_t og = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c;
+            kk = io<T>::ld(k + ok);
+            qq = io<T>::ld(q + ok);
+            bb = io<T>::ld(b + og);
+            ll = io<T>::ld(la + og);
         }
-        s[L_::GL + c] = acc;
-        for (int r = 0; r < C; ++r) {
-            const float g = s[L_::G + r * DK + c];
-            const float ga = __expf(g);
-            s[L_::Y + r * DK + c] = ga * s[L_::BK + r * DK + c];
-            s[L_::QG + r * DK + c] = ga * s[L_::Q + r * DK + c];
-            s[L_::KG + r * DK + c] = __expf(acc - g) * s[L_::K + r * DK + c];
+        s[L_::K + e] = kk;
+        s[L_::Q + e] = qq;
+        s[L_::BK + e] = bb * kk;
+        lt.k[r * SP + c] = kk;
+        lt.q[r * SP + c] = qq;
+        lt.bk[r * SP + c] = bb * kk;
+        lt.g[r * SP + c] = ll;
+    }
+    for (int e = tid; e < C * DV; e += kBwdThreads) {
+        const int r = e / DV, c = e - r * DV;
+        float x = 0.f;
+        if (r < Lr) {
+            const size_t ov = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c;
+            x = io<T>::ld(w + ov) * io<T>::ld(v + ov);
         }
-    } else if (tid < DK + DV) {
-        const int c = tid - DK;
-        for (int r = 0; r < C; ++r) {
-            float x = 0.f;
-            if (r < Lr) {
-                const size_t ov = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c;
-                x = io<T>::ld(w + ov) * io<T>::ld(v + ov);
-            }
-            s[L_::X + r * DV + c] = x;
-        }
+        s[L_::X + e] = x;
     }
     __syncthreads();
+    // the cumulative decay, one channel per thread
+    for (int c = tid; c < DK; c += kBwdThreads) {
+        float acc = 0.f;
+        for (int r = 0; r < C; ++r) {
+            acc += lt.g[r * SP + c];
+            lt.g[r * SP + c] = acc;
+            s[L_::G + r * DK + c] = acc;
+        }
+        s[L_::GL + c] = acc;
+    }
+    __syncthreads();
+    // gamma.b.k, gamma.q and exp(g_L - g).k
+    for (int e = tid; e < C * DK; e += kBwdThreads) {
+        const int r = e / DK, c = e - r * DK;
+        const float g = lt.g[r * SP + c], gL = lt.g[(C - 1) * SP + c];
+        const float ga = __expf(g);
+        s[L_::Y + e] = ga * lt.bk[r * SP + c];
+        s[L_::QG + e] = ga * lt.q[r * SP + c];
+        s[L_::KG + e] = __expf(gL - g) * lt.k[r * SP + c];
+    }
     // A and M, one (r, i) entry per thread at a time
     for (int e = tid; e < C * C; e += kBwdThreads) {
         const int r = e / C, i = e - r * C;
         float a = 0.f, m = 0.f;
         if (i <= r) {
             for (int c = 0; c < DK; ++c) {
-                const float ex = __expf(s[L_::G + r * DK + c] - s[L_::G + i * DK + c]);
-                const float ki = s[L_::K + i * DK + c];
-                m += s[L_::Q + r * DK + c] * ki * ex;
-                a += s[L_::BK + r * DK + c] * ki * ex;
+                const float ex = __expf(lt.g[r * SP + c] - lt.g[i * SP + c]);
+                const float ki = lt.k[i * SP + c];
+                m += lt.q[r * SP + c] * ki * ex;
+                a += lt.bk[r * SP + c] * ki * ex;
             }
         }
         s[L_::A + e] = i < r ? a : 0.f;
@@ -206,29 +239,50 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
     }
     __syncthreads();
     const float *sc = s;
-    block_mm(C, DK, C, [&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
+    block_mm<C, DK, C>([&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
              [&](int kk, int nn) { return sc[L_::Y + kk * DK + nn]; },
              [&](int m, int nn, float x) { s[L_::WT + m * DK + nn] = x; });
-    block_mm(C, DV, C, [&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
+    block_mm<C, DV, C>([&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
              [&](int kk, int nn) { return sc[L_::X + kk * DV + nn]; },
              [&](int m, int nn, float x) { s[L_::UT + m * DV + nn] = x; });
     auto dO_at = [&](int r, int c) {
         return r < Lr ? io<T>::ld(dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c) : 0.f;
     };
-    block_mm(C, DV, C, [&](int m, int kk) { return sc[L_::M + kk * C + m]; }, dO_at,
+    block_mm<C, DV, C>([&](int m, int kk) { return sc[L_::M + kk * C + m]; }, dO_at,
              [&](int m, int nn, float x) { s[L_::E1 + m * DV + nn] = x; });
-    block_mm(DK, DV, C, [&](int m, int kk) { return sc[L_::QG + kk * DK + m]; }, dO_at,
+    block_mm<DK, DV, C>([&](int m, int kk) { return sc[L_::QG + kk * DK + m]; }, dO_at,
              [&](int m, int nn, float x) { s[L_::E2 + m * DV + nn] = x; });
 }
 
-// One wave per (sequence, value head, 16 columns of the state).
+__device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+}
+// s_waitcnt with vmcnt(0) only
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS stage of one chunk for the reverse pass: W~ and Kg ([C][DK] each, adjacent in the
+// record scratch), then g_L.
+template <int DK>
+struct ChainStage {
+    static constexpr int TILES = 2 * C * DK * 4;              // bytes of W~ and Kg
+    static constexpr int BYTES = TILES + DK * 4;
+};
+
+// Four waves per workgroup, each owning 16 state columns of one (sequence, value head);
+// the workgroup stages each chunk's W~, Kg and g_L in LDS (double-buffered, direct
+// global-to-LDS loads issued one chunk ahead), and each wave prefetches its columns of
+// M^T dO and Qg^T dO into registers one chunk ahead.
 template <int DK, int DV>
-__global__ __launch_bounds__(64) void bwd_chain_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
     using L_ = BLay<DK, DV>;
-    constexpr int RT = DK / 16, NS = DV / 16;
-    const int unit = blockIdx.x, pair = unit / NS, sl = unit - pair * NS;
+    using CS = ChainStage<DK>;
+    constexpr int RT = DK / 16, NS = DV / 16, WPP = NS / 4, UT = C / 16;
+    static_assert(NS % 4 == 0, "four 16-column slices per workgroup");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int unit = blockIdx.x, pair = unit / WPP, part = unit - pair * WPP;
     const int n = pair / p.h_v, h = pair - n * p.h_v;
-    const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4, col = 16 * sl + li;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const int col = 16 * (4 * part + wave) + li;
     int64_t start, end;
     int cbase;
     if (p.cu == nullptr) {
@@ -241,32 +295,75 @@ __global__ __launch_bounds__(64) void bwd_chain_kernel(BwdParams p) {
         cbase = p.map[n];
     }
     const int nchunks = static_cast<int>((end - start + C - 1) / C);
-    f32x4 D[RT];                                   // dS' rows 16 rt + 4 lg + ii, column col
+    auto scratch = [&](int c) {
+        return p.scr + (static_cast<size_t>(cbase + c) * p.h_v + h) * L_::FLOATS;
+    };
+    auto stage = [&](int c, char *dst) {            // this wave's share of chunk c's copies
+        const char *src = reinterpret_cast<const char *>(scratch(c) + L_::WT);
+        for (int blk = wave; blk < CS::TILES / 1024; blk += 4)
+            dma16(src + blk * 1024 + lane * 16, dst + blk * 1024);
+        if (wave == 3 && lane < DK / 4)
+            dma16(reinterpret_cast<const char *>(scratch(c) + L_::GL) + lane * 16, dst + CS::TILES);
+    };
+    float e1n[UT][4], e2n[RT][4];                   // this lane's M^T dO and Qg^T dO, next chunk
+    auto prefetch = [&](int c) {
+        const float *s = scratch(c);
+#pragma unroll
+        for (int ut = 0; ut < UT; ++ut)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) e1n[ut][ii] = s[L_::E1 + (16 * ut + 4 * lg + ii) * DV + col];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                e2n[rt][ii] = s[L_::E2 + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col];
+    };
+
+    f32x4 D[RT];                                    // dS' rows 16 rt + 4 lg + ii, column col
     const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * DK * DV;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
             D[rt][ii] = p.dS_T ? p.dS_T[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] : 0.f;
+    if (nchunks > 0) {
+        prefetch(nchunks - 1);
+        stage(nchunks - 1, smem);
+    }
     for (int c = nchunks - 1; c >= 0; --c) {
-        float *s = p.scr + (static_cast<size_t>(cbase + c) * p.h_v + h) * L_::FLOATS;
+        const char *buf = smem + ((nchunks - 1 - c) & 1) * CS::BYTES;
+        wait_vmem();                                // this wave's copies and prefetches landed
+        __syncthreads();                            // everyone's; the other buffer is free
+        float e1[UT][4], e2[RT][4];
+#pragma unroll
+        for (int ut = 0; ut < UT; ++ut)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) e1[ut][ii] = e1n[ut][ii];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) e2[rt][ii] = e2n[rt][ii];
+        if (c > 0) {
+            prefetch(c - 1);
+            stage(c - 1, smem + ((nchunks - c) & 1) * CS::BYTES);
+        }
+        const float *wt = reinterpret_cast<const float *>(buf);
+        const float *kg = wt + C * DK;
+        const float *gl = wt + 2 * C * DK;
+        float *s = scratch(c);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 s[L_::DSN + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = D[rt][ii];
         // dU = M^T dO + Kg dS'
-        f32x4 U4[C / 16];
+        f32x4 U4[UT];
 #pragma unroll
-        for (int ut = 0; ut < C / 16; ++ut) {
-            f32x4 acc;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[ii] = s[L_::E1 + (16 * ut + 4 * lg + ii) * DV + col];
+        for (int ut = 0; ut < UT; ++ut) {
+            f32x4 acc = {e1[ut][0], e1[ut][1], e1[ut][2], e1[ut][3]};
 #pragma unroll
             for (int kt = 0; kt < RT; ++kt) {
-                f32x4 av;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) av[e] = s[L_::KG + (16 * ut + li) * DK + 16 * kt + 4 * lg + e];
+                const f32x4 av = *reinterpret_cast<const f32x4 *>(&kg[(16 * ut + li) * DK + 16 * kt + 4 * lg]);
                 acc = mma_k16_f32(av, D[kt], acc);
             }
             U4[ut] = acc;
@@ -274,26 +371,21 @@ __global__ __launch_bounds__(64) void bwd_chain_kernel(BwdParams p) {
             for (int ii = 0; ii < 4; ++ii) s[L_::DU + (16 * ut + 4 * lg + ii) * DV + col] = acc[ii];
         }
         // dS = gamma_L dS' + Qg^T dO - W~^T dU
-        f32x4 Dn[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 acc;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int row = 16 * rt + 4 * lg + ii;
-                acc[ii] = __expf(s[L_::GL + row]) * D[rt][ii] + s[L_::E2 + static_cast<size_t>(row) * DV + col];
-            }
+            for (int ii = 0; ii < 4; ++ii)
+                acc[ii] = __expf(gl[16 * rt + 4 * lg + ii]) * D[rt][ii] + e2[rt][ii];
 #pragma unroll
-            for (int kt = 0; kt < C / 16; ++kt) {
+            for (int kt = 0; kt < UT; ++kt) {
                 f32x4 av;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) av[e] = -s[L_::WT + (16 * kt + 4 * lg + e) * DK + 16 * rt + li];
+                for (int e = 0; e < 4; ++e) av[e] = -wt[(16 * kt + 4 * lg + e) * DK + 16 * rt + li];
                 acc = mma_k16_f32(av, U4[kt], acc);
             }
-            Dn[rt] = acc;
+            D[rt] = acc;
         }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) D[rt] = Dn[rt];
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -317,27 +409,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     float *s = p.scr + static_cast<size_t>(rec) * L_::FLOATS;
     const float *sc = s;
     const float *S = p.ck + static_cast<size_t>(rec) * DK * DV;     // state entering the chunk
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    KeyTiles<DK> lt(smem);
+    constexpr int SP = KeyTiles<DK>::SP;
+    for (int e = tid; e < C * DK; e += kBwdThreads) {
+        const int r = e / DK, c = e - r * DK;
+        lt.g[r * SP + c] = sc[L_::G + e];
+        lt.k[r * SP + c] = sc[L_::K + e];
+        lt.q[r * SP + c] = sc[L_::Q + e];
+        lt.bk[r * SP + c] = sc[L_::BK + e];
+    }
     auto dO_at = [&](int r, int c) {
         return r < Lr ? io<T>::ld(dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c) : 0.f;
     };
 
     // U = U~ - W~ S
-    block_mm(C, DV, DK, [&](int m, int kk) { return sc[L_::WT + m * DK + kk]; },
+    block_mm<C, DV, DK>([&](int m, int kk) { return sc[L_::WT + m * DK + kk]; },
              [&](int kk, int nn) { return S[kk * DV + nn]; },
              [&](int m, int nn, float x) { s[L_::U + m * DV + nn] = sc[L_::UT + m * DV + nn] - x; });
     __syncthreads();
     // dM = lower(dO U^T), dQg = dO S^T, dKg = U dS'^T, dW~ = -dU S^T, dX = Tm^T dU
-    block_mm(C, C, DV, dO_at, [&](int kk, int nn) { return sc[L_::U + nn * DV + kk]; },
+    block_mm<C, C, DV>(dO_at, [&](int kk, int nn) { return sc[L_::U + nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DM + m * C + nn] = nn <= m ? x : 0.f; });
-    block_mm(C, DK, DV, dO_at, [&](int kk, int nn) { return S[nn * DV + kk]; },
+    block_mm<C, DK, DV>(dO_at, [&](int kk, int nn) { return S[nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DQG + m * DK + nn] = x; });
-    block_mm(C, DK, DV, [&](int m, int kk) { return sc[L_::U + m * DV + kk]; },
+    block_mm<C, DK, DV>([&](int m, int kk) { return sc[L_::U + m * DV + kk]; },
              [&](int kk, int nn) { return sc[L_::DSN + nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DKG + m * DK + nn] = x; });
-    block_mm(C, DK, DV, [&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
+    block_mm<C, DK, DV>([&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
              [&](int kk, int nn) { return S[nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DW + m * DK + nn] = -x; });
-    block_mm(C, DV, C, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+    block_mm<C, DV, C>([&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
              [&](int kk, int nn) { return sc[L_::DU + kk * DV + nn]; },
              [&](int m, int nn, float x) { s[L_::DX + m * DV + nn] = x; });
     for (int c = tid; c < DK; c += kBwdThreads) {      // dL/d gamma_L (before the exp)
@@ -348,23 +450,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     }
     __syncthreads();
     // dY = Tm^T dW~, dT = dU X^T + dW~ Y^T
-    block_mm(C, DK, C, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+    block_mm<C, DK, C>([&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
              [&](int kk, int nn) { return sc[L_::DW + kk * DK + nn]; },
              [&](int m, int nn, float x) { s[L_::DY + m * DK + nn] = x; });
-    block_mm(C, C, DV, [&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
+    block_mm<C, C, DV>([&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
              [&](int kk, int nn) { return sc[L_::X + nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DT + m * C + nn] = x; });
     __syncthreads();
-    block_mm(C, C, DK, [&](int m, int kk) { return sc[L_::DW + m * DK + kk]; },
+    block_mm<C, C, DK>([&](int m, int kk) { return sc[L_::DW + m * DK + kk]; },
              [&](int kk, int nn) { return sc[L_::Y + nn * DK + kk]; },
              [&](int m, int nn, float x) { s[L_::DT + m * C + nn] += x; });
     __syncthreads();
     // dA = strictly-lower(-Tm^T dT Tm^T)
-    block_mm(C, C, C, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+    block_mm<C, C, C>([&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
              [&](int kk, int nn) { return sc[L_::DT + kk * C + nn]; },
              [&](int m, int nn, float x) { s[L_::TMP + m * C + nn] = x; });
     __syncthreads();
-    block_mm(C, C, C, [&](int m, int kk) { return sc[L_::TMP + m * C + kk]; },
+    block_mm<C, C, C>([&](int m, int kk) { return sc[L_::TMP + m * C + kk]; },
              [&](int kk, int nn) { return sc[L_::TM + nn * C + kk]; },
              [&](int m, int nn, float x) { s[L_::DA + m * C + nn] = nn < m ? -x : 0.f; });
     __syncthreads();
@@ -372,18 +474,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     float *dq = p.dq, *dk = p.dk;
     for (int e = tid; e < C * DK; e += kBwdThreads) {
         const int x = e / DK, c = e - x * DK;
-        const float gx = sc[L_::G + x * DK + c];
+        const float gx = lt.g[x * SP + c];
         float p1 = 0.f, p2 = 0.f, p3 = 0.f, p4 = 0.f;
         for (int i = 0; i <= x; ++i) {             // i <= x: E[x, i]
-            const float ex = __expf(gx - sc[L_::G + i * DK + c]);
-            const float ki = sc[L_::K + i * DK + c];
+            const float ex = __expf(gx - lt.g[i * SP + c]);
+            const float ki = lt.k[i * SP + c];
             p1 += sc[L_::DA + x * C + i] * ki * ex;
             p3 += sc[L_::DM + x * C + i] * ki * ex;
         }
         for (int r = x; r < C; ++r) {              // r >= x: E[r, x]
-            const float ex = __expf(sc[L_::G + r * DK + c] - gx);
-            p2 += sc[L_::DA + r * C + x] * sc[L_::BK + r * DK + c] * ex;
-            p4 += sc[L_::DM + r * C + x] * sc[L_::Q + r * DK + c] * ex;
+            const float ex = __expf(lt.g[r * SP + c] - gx);
+            p2 += sc[L_::DA + r * C + x] * lt.bk[r * SP + c] * ex;
+            p4 += sc[L_::DM + r * C + x] * lt.q[r * SP + c] * ex;
         }
         const float ga = __expf(gx), fk = __expf(sc[L_::GL + c] - gx);
         const float kk = sc[L_::K + x * DK + c], qq = sc[L_::Q + x * DK + c];
@@ -417,7 +519,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     // d log alpha: reverse cumulative sum of dg, with the gamma_L terms on the last row
     for (int c = tid; c < DK; c += kBwdThreads) {
         float acc = __expf(sc[L_::GL + c]) * sc[L_::DGL + c];
+#pragma unroll 16
         for (int x = 0; x < C; ++x) acc += sc[L_::DKG + x * DK + c];
+#pragma unroll 16
         for (int x = C - 1; x >= 0; --x) {
             acc += sc[L_::DY + x * DK + c];
             if (x < Lr) p.dla[(static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c] = acc;
@@ -469,13 +573,26 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((zero_kernel<T>), dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
                            a.dq, a.dk, qk);
     }
+    constexpr int klds = KeyTiles<DK>::BYTES;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_factors_kernel<T, DK, DV>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, klds);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel<T, DK, DV>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, klds);
+    if (e != hipSuccess) return e;
     if (nrec > 0) {
-        hipLaunchKernelGGL((bwd_factors_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), 0, st, p);
+        hipLaunchKernelGGL((bwd_factors_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), klds, st, p);
     }
-    const int64_t units = static_cast<int64_t>(N) * a.h_v * (DV / 16);
-    if (units > 0) hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units), dim3(64), 0, st, p);
+    const int64_t units = static_cast<int64_t>(N) * a.h_v * (DV / 64);
+    if (units > 0) {
+        const int lds = 2 * ChainStage<DK>::BYTES;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_chain_kernel<DK, DV>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units), dim3(256), lds, st, p);
+    }
     if (nrec > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), 0, st, p);
+        hipLaunchKernelGGL((bwd_grads_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), klds, st, p);
     }
     return hipGetLastError();
 }
