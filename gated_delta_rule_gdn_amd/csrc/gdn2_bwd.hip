@@ -57,11 +57,11 @@ struct BLay {
     static constexpr size_t FLOATS = DGL + DK;
 };
 
-// LDS copies of g, k, q and b.k of one record, rows padded to DK + 1 floats so that the
-// lanes of a wave reading one channel of consecutive rows hit different banks.
-template <int DK>
+// LDS copies of g, k, q and b.k of one record with row stride SP floats (DK + 1 where the
+// lanes of a wave read one channel of consecutive rows, so that they hit different banks).
+template <int DK, int SP_ = DK + 1>
 struct KeyTiles {
-    static constexpr int SP = DK + 1;
+    static constexpr int SP = SP_;
     static constexpr int BYTES = 4 * C * SP * 4;
     float *g, *k, *q, *bk;
     __device__ explicit KeyTiles(char *base) {
@@ -228,15 +228,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
         s[L_::M + e] = m;
     }
     __syncthreads();
-    // Tm = (I + A)^-1 by forward substitution, one column per thread
+    // Tm = (I + A)^-1 by forward substitution in LDS (the key tiles are no longer needed),
+    // one column per thread
+    float *lA = reinterpret_cast<float *>(smem), *lT = lA + C * C;
+    for (int e = tid; e < C * C; e += kBwdThreads) lA[e] = s[L_::A + e];
+    __syncthreads();
     if (tid < C) {
         const int jc = tid;
         for (int r = 0; r < C; ++r) {
             float t = r == jc ? 1.f : 0.f;
-            for (int i = jc; i < r; ++i) t -= s[L_::A + r * C + i] * s[L_::TM + i * C + jc];
-            s[L_::TM + r * C + jc] = r < jc ? 0.f : t;
+            for (int i = jc; i < r; ++i) t -= lA[r * C + i] * lT[i * C + jc];
+            lT[r * C + jc] = r < jc ? 0.f : t;
         }
     }
+    __syncthreads();
+    for (int e = tid; e < C * C; e += kBwdThreads) s[L_::TM + e] = lT[e];
     __syncthreads();
     const float *sc = s;
     block_mm<C, DK, C>([&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
@@ -410,8 +416,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     const float *sc = s;
     const float *S = p.ck + static_cast<size_t>(rec) * DK * DV;     // state entering the chunk
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    KeyTiles<DK> lt(smem);
-    constexpr int SP = KeyTiles<DK>::SP;
+    KeyTiles<DK, DK> lt(smem);                      // lanes run along channels: no padding
+    constexpr int SP = DK;
+    float *lDA = reinterpret_cast<float *>(smem + KeyTiles<DK, DK>::BYTES), *lDM = lDA + C * C;
     for (int e = tid; e < C * DK; e += kBwdThreads) {
         const int r = e / DK, c = e - r * DK;
         lt.g[r * SP + c] = sc[L_::G + e];
@@ -470,6 +477,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
              [&](int kk, int nn) { return sc[L_::TM + nn * C + kk]; },
              [&](int m, int nn, float x) { s[L_::DA + m * C + nn] = nn < m ? -x : 0.f; });
     __syncthreads();
+    for (int e = tid; e < C * C; e += kBwdThreads) {
+        lDA[e] = sc[L_::DA + e];
+        lDM[e] = sc[L_::DM + e];
+    }
+    __syncthreads();
     // through E, Y, Qg, Kg to q, k, b and g; one (row x, key channel c) per thread
     float *dq = p.dq, *dk = p.dk;
     for (int e = tid; e < C * DK; e += kBwdThreads) {
@@ -479,13 +491,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
         for (int i = 0; i <= x; ++i) {             // i <= x: E[x, i]
             const float ex = __expf(gx - lt.g[i * SP + c]);
             const float ki = lt.k[i * SP + c];
-            p1 += sc[L_::DA + x * C + i] * ki * ex;
-            p3 += sc[L_::DM + x * C + i] * ki * ex;
+            p1 += lDA[x * C + i] * ki * ex;
+            p3 += lDM[x * C + i] * ki * ex;
         }
         for (int r = x; r < C; ++r) {              // r >= x: E[r, x]
             const float ex = __expf(lt.g[r * SP + c] - gx);
-            p2 += sc[L_::DA + r * C + x] * lt.bk[r * SP + c] * ex;
-            p4 += sc[L_::DM + r * C + x] * lt.q[r * SP + c] * ex;
+            p2 += lDA[r * C + x] * lt.bk[r * SP + c] * ex;
+            p4 += lDM[r * C + x] * lt.q[r * SP + c] * ex;
         }
         const float ga = __expf(gx), fk = __expf(sc[L_::GL + c] - gx);
         const float kk = sc[L_::K + x * DK + c], qq = sc[L_::Q + x * DK + c];
@@ -577,8 +589,10 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_factors_kernel<T, DK, DV>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, klds);
     if (e != hipSuccess) return e;
+    constexpr int glds = KeyTiles<DK, DK>::BYTES + 2 * C * C * 4;
+    static_assert(glds <= 160 * 1024 && klds <= 160 * 1024, "LDS");
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel<T, DK, DV>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, klds);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, glds);
     if (e != hipSuccess) return e;
     if (nrec > 0) {
         hipLaunchKernelGGL((bwd_factors_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), klds, st, p);
@@ -592,7 +606,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units), dim3(256), lds, st, p);
     }
     if (nrec > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), klds, st, p);
+        hipLaunchKernelGGL((bwd_grads_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), glds, st, p);
     }
     return hipGetLastError();
 }
