@@ -586,7 +586,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the timing of the other chunk workloads and the decode control")
-    ap.add_argument("--only", choices=["chunk", "decode", "all"], default="all")
+    ap.add_argument("--only", choices=["chunk", "decode", "bwd", "all"], default="all",
+                    help="bwd: time the chunked backward alone (its own JSON line)")
     ap.add_argument("--profile-driver", action="store_true",
                     help="short fixed sequence for hardware-counter runs: 5 chunk forwards, "
                          "20 decode steps with an fp32 state and 20 with a bf16 state, and 3 "
@@ -609,6 +610,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_driver:
         profile_driver()
+        return
+    if args.only == "bwd":
+        print(json.dumps(bench_chunk_bwd(max(5, args.steps // 10), 2)))
         return
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
