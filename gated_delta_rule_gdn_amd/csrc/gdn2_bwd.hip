@@ -133,6 +133,29 @@ __device__ void block_mm(FA a, FB b, FS store) {
     }
 }
 
+// The same product with both operands first copied to LDS, each element read once. The copy
+// walks each source along its contiguous axis: TA when a is contiguous along m (else along
+// k), TB when b is contiguous along k (else along n). lds holds at least (M (K + 4) + K (N + 4)) floats. Ends with a barrier,
+// after which lds may be reused.
+template <int M, int N, int K, bool TA, bool TB, class FA, class FB, class FS>
+__device__ void block_mm_lds(float *lds, FA a, FB b, FS store) {
+    constexpr int SA = K + 4, SB = N + 4;
+    float *As = lds, *Bs = lds + M * SA;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int e = tid; e < M * K; e += nt) {
+        const int m = TA ? e % M : e / K, k = TA ? e / M : e % K;
+        As[m * SA + k] = a(m, k);
+    }
+    for (int e = tid; e < K * N; e += nt) {
+        const int k = TB ? e % K : e / N, n = TB ? e / K : e % N;
+        Bs[k * SB + n] = b(k, n);
+    }
+    __syncthreads();
+    block_mm<M, N, K>([&](int m, int k) { return As[m * SA + k]; },
+                      [&](int k, int n) { return Bs[k * SB + n]; }, store);
+    __syncthreads();
+}
+
 template <typename T>
 __global__ void zero_kernel(float *a, float *b, int64_t n) {
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
@@ -245,18 +268,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
     for (int e = tid; e < C * C; e += kBwdThreads) s[L_::TM + e] = lT[e];
     __syncthreads();
     const float *sc = s;
-    block_mm<C, DK, C>([&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
+    float *lf = reinterpret_cast<float *>(smem);       // product staging from here on
+    block_mm_lds<C, DK, C, false, false>(lf, [&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
              [&](int kk, int nn) { return sc[L_::Y + kk * DK + nn]; },
              [&](int m, int nn, float x) { s[L_::WT + m * DK + nn] = x; });
-    block_mm<C, DV, C>([&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
+    block_mm_lds<C, DV, C, false, false>(lf, [&](int m, int kk) { return sc[L_::TM + m * C + kk]; },
              [&](int kk, int nn) { return sc[L_::X + kk * DV + nn]; },
              [&](int m, int nn, float x) { s[L_::UT + m * DV + nn] = x; });
     auto dO_at = [&](int r, int c) {
         return r < Lr ? io<T>::ld(dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c) : 0.f;
     };
-    block_mm<C, DV, C>([&](int m, int kk) { return sc[L_::M + kk * C + m]; }, dO_at,
+    block_mm_lds<C, DV, C, true, false>(lf, [&](int m, int kk) { return sc[L_::M + kk * C + m]; }, dO_at,
              [&](int m, int nn, float x) { s[L_::E1 + m * DV + nn] = x; });
-    block_mm<DK, DV, C>([&](int m, int kk) { return sc[L_::QG + kk * DK + m]; }, dO_at,
+    block_mm_lds<DK, DV, C, true, false>(lf, [&](int m, int kk) { return sc[L_::QG + kk * DK + m]; }, dO_at,
              [&](int m, int nn, float x) { s[L_::E2 + m * DV + nn] = x; });
 }
 
@@ -419,34 +443,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     KeyTiles<DK, DK> lt(smem);                      // lanes run along channels: no padding
     constexpr int SP = DK;
     float *lDA = reinterpret_cast<float *>(smem + KeyTiles<DK, DK>::BYTES), *lDM = lDA + C * C;
-    for (int e = tid; e < C * DK; e += kBwdThreads) {
-        const int r = e / DK, c = e - r * DK;
-        lt.g[r * SP + c] = sc[L_::G + e];
-        lt.k[r * SP + c] = sc[L_::K + e];
-        lt.q[r * SP + c] = sc[L_::Q + e];
-        lt.bk[r * SP + c] = sc[L_::BK + e];
-    }
+    float *lf = reinterpret_cast<float *>(smem);       // product staging, then the tiles
     auto dO_at = [&](int r, int c) {
         return r < Lr ? io<T>::ld(dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c) : 0.f;
     };
 
     // U = U~ - W~ S
-    block_mm<C, DV, DK>([&](int m, int kk) { return sc[L_::WT + m * DK + kk]; },
+    block_mm_lds<C, DV, DK, false, false>(lf, [&](int m, int kk) { return sc[L_::WT + m * DK + kk]; },
              [&](int kk, int nn) { return S[kk * DV + nn]; },
              [&](int m, int nn, float x) { s[L_::U + m * DV + nn] = sc[L_::UT + m * DV + nn] - x; });
     __syncthreads();
     // dM = lower(dO U^T), dQg = dO S^T, dKg = U dS'^T, dW~ = -dU S^T, dX = Tm^T dU
-    block_mm<C, C, DV>(dO_at, [&](int kk, int nn) { return sc[L_::U + nn * DV + kk]; },
+    block_mm_lds<C, C, DV, false, true>(lf, dO_at, [&](int kk, int nn) { return sc[L_::U + nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DM + m * C + nn] = nn <= m ? x : 0.f; });
-    block_mm<C, DK, DV>(dO_at, [&](int kk, int nn) { return S[nn * DV + kk]; },
+    block_mm_lds<C, DK, DV, false, true>(lf, dO_at, [&](int kk, int nn) { return S[nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DQG + m * DK + nn] = x; });
-    block_mm<C, DK, DV>([&](int m, int kk) { return sc[L_::U + m * DV + kk]; },
+    block_mm_lds<C, DK, DV, false, true>(lf, [&](int m, int kk) { return sc[L_::U + m * DV + kk]; },
              [&](int kk, int nn) { return sc[L_::DSN + nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DKG + m * DK + nn] = x; });
-    block_mm<C, DK, DV>([&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
+    block_mm_lds<C, DK, DV, false, true>(lf, [&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
              [&](int kk, int nn) { return S[nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DW + m * DK + nn] = -x; });
-    block_mm<C, DV, C>([&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+    block_mm_lds<C, DV, C, true, false>(lf, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
              [&](int kk, int nn) { return sc[L_::DU + kk * DV + nn]; },
              [&](int m, int nn, float x) { s[L_::DX + m * DV + nn] = x; });
     for (int c = tid; c < DK; c += kBwdThreads) {      // dL/d gamma_L (before the exp)
@@ -457,26 +475,33 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     }
     __syncthreads();
     // dY = Tm^T dW~, dT = dU X^T + dW~ Y^T
-    block_mm<C, DK, C>([&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+    block_mm_lds<C, DK, C, true, false>(lf, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
              [&](int kk, int nn) { return sc[L_::DW + kk * DK + nn]; },
              [&](int m, int nn, float x) { s[L_::DY + m * DK + nn] = x; });
-    block_mm<C, C, DV>([&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
+    block_mm_lds<C, C, DV, false, true>(lf, [&](int m, int kk) { return sc[L_::DU + m * DV + kk]; },
              [&](int kk, int nn) { return sc[L_::X + nn * DV + kk]; },
              [&](int m, int nn, float x) { s[L_::DT + m * C + nn] = x; });
     __syncthreads();
-    block_mm<C, C, DK>([&](int m, int kk) { return sc[L_::DW + m * DK + kk]; },
+    block_mm_lds<C, C, DK, false, true>(lf, [&](int m, int kk) { return sc[L_::DW + m * DK + kk]; },
              [&](int kk, int nn) { return sc[L_::Y + nn * DK + kk]; },
              [&](int m, int nn, float x) { s[L_::DT + m * C + nn] += x; });
     __syncthreads();
     // dA = strictly-lower(-Tm^T dT Tm^T)
-    block_mm<C, C, C>([&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
+    block_mm_lds<C, C, C, true, false>(lf, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
              [&](int kk, int nn) { return sc[L_::DT + kk * C + nn]; },
              [&](int m, int nn, float x) { s[L_::TMP + m * C + nn] = x; });
     __syncthreads();
-    block_mm<C, C, C>([&](int m, int kk) { return sc[L_::TMP + m * C + kk]; },
+    block_mm_lds<C, C, C, false, true>(lf, [&](int m, int kk) { return sc[L_::TMP + m * C + kk]; },
              [&](int kk, int nn) { return sc[L_::TM + nn * C + kk]; },
              [&](int m, int nn, float x) { s[L_::DA + m * C + nn] = nn < m ? -x : 0.f; });
     __syncthreads();
+    for (int e = tid; e < C * DK; e += kBwdThreads) {
+        const int r = e / DK, c = e - r * DK;
+        lt.g[r * SP + c] = sc[L_::G + e];
+        lt.k[r * SP + c] = sc[L_::K + e];
+        lt.q[r * SP + c] = sc[L_::Q + e];
+        lt.bk[r * SP + c] = sc[L_::BK + e];
+    }
     for (int e = tid; e < C * C; e += kBwdThreads) {
         lDA[e] = sc[L_::DA + e];
         lDM[e] = sc[L_::DM + e];
@@ -590,6 +615,12 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, klds);
     if (e != hipSuccess) return e;
     constexpr int glds = KeyTiles<DK, DK>::BYTES + 2 * C * C * 4;
+    constexpr auto mm = [](int M, int N, int K) { return 4 * (M * (K + 4) + K * (N + 4)); };
+    static_assert(mm(C, DK, C) <= klds && mm(C, DV, C) <= klds && mm(DK, DV, C) <= klds,
+                  "the staged products of the factors kernel fit in its LDS");
+    static_assert(mm(C, DV, DK) <= glds && mm(C, C, DV) <= glds && mm(C, DK, DV) <= glds &&
+                      mm(C, DK, C) <= glds && mm(C, C, DK) <= glds && mm(C, C, C) <= glds,
+                  "the staged products of the gradients kernel fit in its LDS");
     static_assert(glds <= 160 * 1024 && klds <= 160 * 1024, "LDS");
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel<T, DK, DV>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, glds);
