@@ -18,12 +18,14 @@
 // entering every chunk):
 //   bwd_factors_kernel  per (chunk, value head) record, in parallel: g, A, M, Tm, W~, U~,
 //                       Qg, Kg and the dO terms of the chain, M^T dO and Qg^T dO
-//   bwd_chain_kernel    per (sequence, value head, 16 columns), sequential over the chunks
-//                       from the last: dU of every chunk and the dS' it leaves, then dS0
+//   bwd_chain_kernel    per (sequence, value head, 64 columns), four waves of 16 columns,
+//                       sequential over the chunks from the last: dU of every chunk and the
+//                       dS' it leaves, then dS0
 //   bwd_grads_kernel    per record, in parallel: every input gradient of the chunk
-// The products are fp32 matrix-core tiles (16x16x4) with operands read from the per-record
-// fp32 scratch of the workspace; q and k gradients of value heads that share a key head are
-// summed with fp32 atomics.
+// The record kernels keep their intermediates in a per-record fp32 scratch of the workspace
+// and stage each product's operands in LDS; the products are fp32 matrix-core tiles
+// (16x16x4). q and k gradients of value heads that share a key head are summed with fp32
+// atomics.
 #include "gdn2_common.h"
 #include "gdn2_internal.h"
 #include "gdn2_mfma.h"
@@ -156,7 +158,7 @@ __device__ void block_mm_lds(float *lds, FA a, FB b, FS store) {
     __syncthreads();
 }
 
-template <typename T>
+// Clears the atomically accumulated dq and dk.
 __global__ void zero_kernel(float *a, float *b, int64_t n) {
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -607,7 +609,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const int64_t qk = static_cast<int64_t>(a.batch) * a.seqlen * a.h_k * DK;
     if (qk > 0) {
         const int64_t blocks = (qk + 255) / 256;
-        hipLaunchKernelGGL((zero_kernel<T>), dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
+        hipLaunchKernelGGL(zero_kernel, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
                            a.dq, a.dk, qk);
     }
     constexpr int klds = KeyTiles<DK>::BYTES;

@@ -97,3 +97,16 @@ def test_bwd_timed_chunk_shape():
     """B=1 T=4096 H=16 d=128 (64 chunks per pair; the forward that stores the chunk states
     takes the segmented state pass)."""
     run_case(inputs.chunk_inputs(inputs.CHUNK_BF16_T4096, seed=66), "bf16 B=1 T=4096 H=16", 6)
+
+
+def test_bwd_empty_batch_passes_the_final_gradient_through():
+    """T = 0: no chunks, so dS0 = dS_T (and zero without it)."""
+    q = torch.zeros(2, 0, 1, 64, device="cuda")
+    v = torch.zeros(2, 0, 2, 64, device="cuda")
+    la = torch.zeros(2, 0, 2, 64, device="cuda")
+    dST = torch.randn(2, 2, 64, 64, device="cuda")
+    got = g.chunk_bwd(q, q, v, la, la, v, v, dS_T=dST)
+    none = g.chunk_bwd(q, q, v, la, la, v, v)
+    torch.cuda.synchronize()
+    assert torch.equal(got["dS0"], dST)
+    assert torch.count_nonzero(none["dS0"]) == 0
