@@ -509,23 +509,73 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
         lDM[e] = sc[L_::DM + e];
     }
     __syncthreads();
+    // The decay sums on the matrix cores, per 16-row block B with reference row rho = 16 B + 7
+    // (exp(g_r - g_i) = exp(g_r - g_rho) exp(g_rho - g_i), every factor within 8 tokens of
+    // decay or <= 1):
+    //   P1[x] = sum_{i<x}  dA[x,i] k_i E[x,i],   P3[x] = sum_{i<=x} dM[x,i] k_i E[x,i]   (x in B)
+    //   P2[x] = sum_{r>x}  dA[r,x] bk_r E[r,x],  P4[x] = sum_{r>=x} dM[r,x] q_r E[r,x]  (x in B)
+    // dA and dM carry their triangular masks, so each block runs over whole 16-row k blocks.
+    // Written to free scratch tiles: P1 -> W~, P2 -> Y, P3 -> Kg, P4 -> Qg.
+    {
+        const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+        constexpr int NW = kBwdThreads / 64, CT = DK / 16;
+        for (int u = wave; u < 4 * CT * 2; u += NW) {
+            const int side = u / (4 * CT), rest = u - side * 4 * CT;
+            const int B = rest / CT, n0 = (rest - B * CT) * 16, rho = 16 * B + 7, c = n0 + li;
+            const float grho = lt.g[rho * SP + c];
+            f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc1;
+            if (side == 0) {                        // P1, P3: k over rows 0 .. 16 B + 15
+                for (int kb = 0; kb <= B; ++kb) {
+                    f32x4 a1, a3, bv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * kb + 4 * lg + e;
+                        a1[e] = lDA[(16 * B + li) * C + i];
+                        a3[e] = lDM[(16 * B + li) * C + i];
+                        bv[e] = lt.k[i * SP + c] * __expf(grho - lt.g[i * SP + c]);
+                    }
+                    acc1 = mma_k16_f32(a1, bv, acc1);
+                    acc2 = mma_k16_f32(a3, bv, acc2);
+                }
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int x = 16 * B + 4 * lg + ii;
+                    const float f = __expf(lt.g[x * SP + c] - grho);
+                    s[L_::WT + x * DK + c] = acc1[ii] * f;
+                    s[L_::KG + x * DK + c] = acc2[ii] * f;
+                }
+            } else {                                // P2, P4: k over rows 16 B .. C - 1
+                for (int kb = B; kb < C / 16; ++kb) {
+                    f32x4 a2, a4, b2, b4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * kb + 4 * lg + e;
+                        a2[e] = lDA[r * C + 16 * B + li];
+                        a4[e] = lDM[r * C + 16 * B + li];
+                        const float f = __expf(lt.g[r * SP + c] - grho);
+                        b2[e] = lt.bk[r * SP + c] * f;
+                        b4[e] = lt.q[r * SP + c] * f;
+                    }
+                    acc1 = mma_k16_f32(a2, b2, acc1);
+                    acc2 = mma_k16_f32(a4, b4, acc2);
+                }
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int x = 16 * B + 4 * lg + ii;
+                    const float f = __expf(grho - lt.g[x * SP + c]);
+                    s[L_::Y + x * DK + c] = acc1[ii] * f;
+                    s[L_::QG + x * DK + c] = acc2[ii] * f;
+                }
+            }
+        }
+    }
+    __syncthreads();
     // through E, Y, Qg, Kg to q, k, b and g; one (row x, key channel c) per thread
     float *dq = p.dq, *dk = p.dk;
     for (int e = tid; e < C * DK; e += kBwdThreads) {
         const int x = e / DK, c = e - x * DK;
         const float gx = lt.g[x * SP + c];
-        float p1 = 0.f, p2 = 0.f, p3 = 0.f, p4 = 0.f;
-        for (int i = 0; i <= x; ++i) {             // i <= x: E[x, i]
-            const float ex = __expf(gx - lt.g[i * SP + c]);
-            const float ki = lt.k[i * SP + c];
-            p1 += lDA[x * C + i] * ki * ex;
-            p3 += lDM[x * C + i] * ki * ex;
-        }
-        for (int r = x; r < C; ++r) {              // r >= x: E[r, x]
-            const float ex = __expf(lt.g[r * SP + c] - gx);
-            p2 += lDA[r * C + x] * lt.bk[r * SP + c] * ex;
-            p4 += lDM[r * C + x] * lt.q[r * SP + c] * ex;
-        }
+        const float p1 = sc[L_::WT + e], p2 = sc[L_::Y + e], p3 = sc[L_::KG + e], p4 = sc[L_::QG + e];
         const float ga = __expf(gx), fk = __expf(sc[L_::GL + c] - gx);
         const float kk = sc[L_::K + x * DK + c], qq = sc[L_::Q + x * DK + c];
         const float bk = sc[L_::BK + x * DK + c];
