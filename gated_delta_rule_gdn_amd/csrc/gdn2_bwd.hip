@@ -237,20 +237,39 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
         s[L_::QG + e] = ga * lt.q[r * SP + c];
         s[L_::KG + e] = __expf(gL - g) * lt.k[r * SP + c];
     }
-    // A and M, one (r, i) entry per thread at a time
-    for (int e = tid; e < C * C; e += kBwdThreads) {
-        const int r = e / C, i = e - r * C;
-        float a = 0.f, m = 0.f;
-        if (i <= r) {
-            for (int c = 0; c < DK; ++c) {
-                const float ex = __expf(lt.g[r * SP + c] - lt.g[i * SP + c]);
-                const float ki = lt.k[i * SP + c];
-                m += lt.q[r * SP + c] * ki * ex;
-                a += lt.bk[r * SP + c] * ki * ex;
+    // A and M on the matrix cores, per 16x16 block (row block R, column block I <= R) with
+    // the reference row rho = 16 R + 7: sum_c (x_r exp(g_r - g_rho)) (k_i exp(g_rho - g_i)),
+    // x = b.k for A (i < r) and q for M (i <= r); blocks above the diagonal are zero.
+    {
+        const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+        constexpr int NW = kBwdThreads / 64;
+        for (int u = wave; u < 16; u += NW) {
+            const int R = u >> 2, I = u & 3, rho = 16 * R + 7;
+            f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_m = acc_a;
+            if (I <= R) {
+                const int r = 16 * R + li, i = 16 * I + li;
+                for (int ks = 0; ks < DK / 16; ++ks) {
+                    f32x4 aa, am, bv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 16 * ks + 4 * lg + e;
+                        const float grho = lt.g[rho * SP + c];
+                        const float fr = __expf(lt.g[r * SP + c] - grho);
+                        aa[e] = lt.bk[r * SP + c] * fr;
+                        am[e] = lt.q[r * SP + c] * fr;
+                        bv[e] = lt.k[i * SP + c] * __expf(grho - lt.g[i * SP + c]);
+                    }
+                    acc_a = mma_k16_f32(aa, bv, acc_a);
+                    acc_m = mma_k16_f32(am, bv, acc_m);
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * R + 4 * lg + ii, i = 16 * I + li;
+                s[L_::A + r * C + i] = i < r ? acc_a[ii] : 0.f;
+                s[L_::M + r * C + i] = i <= r ? acc_m[ii] : 0.f;
             }
         }
-        s[L_::A + e] = i < r ? a : 0.f;
-        s[L_::M + e] = m;
     }
     __syncthreads();
     // Tm = (I + A)^-1 by forward substitution in LDS (the key tiles are no longer needed),
