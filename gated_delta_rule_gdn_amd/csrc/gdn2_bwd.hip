@@ -311,6 +311,28 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
 // s_waitcnt with vmcnt(0) only
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Eight fp32 values -> a bf16 matrix-core operand in the order of mma_k32 (slots 0-3 and
+// 4-7 as given) as hi = bf16(x) and lo = bf16(x - hi): hi*hi + hi*lo + lo*hi keeps about 16
+// significant bits of a product.
+__device__ __forceinline__ void split_op(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t h = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        hi[j] = h;
+        lo[j] = pack_bf16x2(x[2 * j] - bf16_lo(h), x[2 * j + 1] - bf16_hi(h));
+    }
+}
+__device__ __forceinline__ f32x4 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+    c = mma_k32(ah, bh, c);
+    c = mma_k32(ah, bl, c);
+    return mma_k32(al, bh, c);
+}
+// two D tiles (k rows 0-15 and 16-31) as a split B operand
+__device__ __forceinline__ void split_dpair(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &lo) {
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    split_op(x, hi, lo);
+}
+
 // LDS stage of one chunk for the reverse pass: W~ and Kg ([C][DK] each, adjacent in the
 // record scratch), then g_L.
 template <int DK>
@@ -322,8 +344,10 @@ struct ChainStage {
 // Four waves per workgroup, each owning 16 state columns of one (sequence, value head);
 // the workgroup stages each chunk's W~, Kg and g_L in LDS (double-buffered, direct
 // global-to-LDS loads issued one chunk ahead), and each wave prefetches its columns of
-// M^T dO and Qg^T dO into registers one chunk ahead.
-template <int DK, int DV>
+// M^T dO and Qg^T dO into registers one chunk ahead. BF (bf16 inputs): the products are
+// three bf16 products of split operands (about 16 significant bits); fp32 inputs keep
+// fp32 products.
+template <int DK, int DV, bool BF>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
     using L_ = BLay<DK, DV>;
     using CS = ChainStage<DK>;
@@ -409,31 +433,69 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
                 s[L_::DSN + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = D[rt][ii];
         // dU = M^T dO + Kg dS'
         f32x4 U4[UT];
+        u32x4 dbh[BF ? RT / 2 : 1], dbl[BF ? RT / 2 : 1];      // dS' as split B operands
+        if constexpr (BF) {
+#pragma unroll
+            for (int k2 = 0; k2 < RT / 2; ++k2) split_dpair(D[2 * k2], D[2 * k2 + 1], dbh[k2], dbl[k2]);
+        }
 #pragma unroll
         for (int ut = 0; ut < UT; ++ut) {
             f32x4 acc = {e1[ut][0], e1[ut][1], e1[ut][2], e1[ut][3]};
+            if constexpr (BF) {
 #pragma unroll
-            for (int kt = 0; kt < RT; ++kt) {
-                const f32x4 av = *reinterpret_cast<const f32x4 *>(&kg[(16 * ut + li) * DK + 16 * kt + 4 * lg]);
-                acc = mma_k16_f32(av, D[kt], acc);
+                for (int k2 = 0; k2 < RT / 2; ++k2) {
+                    const float *row = &kg[(16 * ut + li) * DK + 32 * k2 + 4 * lg];
+                    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(row + 16);
+                    const float xa[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                    u32x4 ah, al;
+                    split_op(xa, ah, al);
+                    acc = mma3(ah, al, dbh[k2], dbl[k2], acc);
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < RT; ++kt) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&kg[(16 * ut + li) * DK + 16 * kt + 4 * lg]);
+                    acc = mma_k16_f32(av, D[kt], acc);
+                }
             }
             U4[ut] = acc;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) s[L_::DU + (16 * ut + 4 * lg + ii) * DV + col] = acc[ii];
         }
         // dS = gamma_L dS' + Qg^T dO - W~^T dU
+        u32x4 ubh[BF ? UT / 2 : 1], ubl[BF ? UT / 2 : 1];      // dU as split B operands
+        if constexpr (BF) {
+#pragma unroll
+            for (int k2 = 0; k2 < UT / 2; ++k2) split_dpair(U4[2 * k2], U4[2 * k2 + 1], ubh[k2], ubl[k2]);
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 acc;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 acc[ii] = __expf(gl[16 * rt + 4 * lg + ii]) * D[rt][ii] + e2[rt][ii];
+            if constexpr (BF) {
 #pragma unroll
-            for (int kt = 0; kt < UT; ++kt) {
-                f32x4 av;
+                for (int k2 = 0; k2 < UT / 2; ++k2) {
+                    float xa[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) av[e] = -wt[(16 * kt + 4 * lg + e) * DK + 16 * rt + li];
-                acc = mma_k16_f32(av, U4[kt], acc);
+                    for (int e = 0; e < 4; ++e) {
+                        xa[e] = -wt[(32 * k2 + 4 * lg + e) * DK + 16 * rt + li];
+                        xa[4 + e] = -wt[(32 * k2 + 16 + 4 * lg + e) * DK + 16 * rt + li];
+                    }
+                    u32x4 ah, al;
+                    split_op(xa, ah, al);
+                    acc = mma3(ah, al, ubh[k2], ubl[k2], acc);
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < UT; ++kt) {
+                    f32x4 av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) av[e] = -wt[(16 * kt + 4 * lg + e) * DK + 16 * rt + li];
+                    acc = mma_k16_f32(av, U4[kt], acc);
+                }
             }
             D[rt] = acc;
         }
@@ -702,10 +764,11 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const int64_t units = static_cast<int64_t>(N) * a.h_v * (DV / 64);
     if (units > 0) {
         const int lds = 2 * ChainStage<DK>::BYTES;
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_chain_kernel<DK, DV>),
+        constexpr bool BF = sizeof(T) == 2;
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_chain_kernel<DK, DV, BF>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units), dim3(256), lds, st, p);
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, BF>), dim3(units), dim3(256), lds, st, p);
     }
     if (nrec > 0) {
         hipLaunchKernelGGL((bwd_grads_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), glds, st, p);
