@@ -137,20 +137,37 @@ __device__ void block_mm(FA a, FB b, FS store) {
 
 // The same product with both operands first copied to LDS, each element read once. The copy
 // walks each source along its contiguous axis: TA when a is contiguous along m (else along
-// k), TB when b is contiguous along k (else along n). lds holds at least (M (K + 4) + K (N + 4)) floats. Ends with a barrier,
-// after which lds may be reused.
+// k), TB when b is contiguous along k (else along n), and each thread issues all of its
+// loads before its first LDS store, so that the copy costs one memory round trip rather
+// than one per element. lds holds at least (M (K + 4) + K (N + 4)) floats. Runs on
+// kBwdThreads threads; ends with a barrier, after which lds may be reused.
 template <int M, int N, int K, bool TA, bool TB, class FA, class FB, class FS>
 __device__ void block_mm_lds(float *lds, FA a, FB b, FS store) {
-    constexpr int SA = K + 4, SB = N + 4;
+    constexpr int SA = K + 4, SB = N + 4, NT = kBwdThreads;
+    constexpr int NA = M * K / NT, NB = K * N / NT;
+    static_assert(NA * NT == M * K && NB * NT == K * N, "operands split evenly over the threads");
     float *As = lds, *Bs = lds + M * SA;
-    const int tid = threadIdx.x, nt = blockDim.x;
-    for (int e = tid; e < M * K; e += nt) {
-        const int m = TA ? e % M : e / K, k = TA ? e / M : e % K;
-        As[m * SA + k] = a(m, k);
+    const int tid = threadIdx.x;
+    float ra[NA], rb[NB];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int e = tid + i * NT, m = TA ? e % M : e / K, k = TA ? e / M : e % K;
+        ra[i] = a(m, k);
     }
-    for (int e = tid; e < K * N; e += nt) {
-        const int k = TB ? e % K : e / N, n = TB ? e / K : e % N;
-        Bs[k * SB + n] = b(k, n);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int e = tid + i * NT, k = TB ? e % K : e / N, n = TB ? e / K : e % N;
+        rb[i] = b(k, n);
+    }
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+        const int e = tid + i * NT, m = TA ? e % M : e / K, k = TA ? e / M : e % K;
+        As[m * SA + k] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int e = tid + i * NT, k = TB ? e % K : e / N, n = TB ? e / K : e % N;
+        Bs[k * SB + n] = rb[i];
     }
     __syncthreads();
     block_mm<M, N, K>([&](int m, int k) { return As[m * SA + k]; },
