@@ -204,34 +204,47 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
     constexpr int SP = KeyTiles<DK>::SP;
 
     // token vectors (rows >= Lr are identity tokens: k = q = b = w.v = 0, log alpha = 0),
-    // one (row, channel) per thread at a time
-    for (int e = tid; e < C * DK; e += kBwdThreads) {
-        const int r = e / DK, c = e - r * DK;
-        float kk = 0.f, qq = 0.f, bb = 0.f, ll = 0.f;
-        if (r < Lr) {
-            const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c;
-            const size_t og = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c;
-            kk = io<T>::ld(k + ok);
-            qq = io<T>::ld(q + ok);
-            bb = io<T>::ld(b + og);
-            ll = io<T>::ld(la + og);
+    // (row, channel) entries tid + i * kBwdThreads; every load is issued before the stores
+    {
+        constexpr int NE = C * DK / kBwdThreads, NX = C * DV / kBwdThreads;
+        static_assert(NE * kBwdThreads == C * DK && NX * kBwdThreads == C * DV, "even split");
+        float kk[NE], qq[NE], bb[NE], ll[NE], xw[NX], xv[NX];
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = tid + i * kBwdThreads, r = e / DK, c = e - r * DK;
+            kk[i] = qq[i] = bb[i] = ll[i] = 0.f;
+            if (r < Lr) {
+                const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c;
+                const size_t og = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c;
+                kk[i] = io<T>::ld(k + ok);
+                qq[i] = io<T>::ld(q + ok);
+                bb[i] = io<T>::ld(b + og);
+                ll[i] = io<T>::ld(la + og);
+            }
         }
-        s[L_::K + e] = kk;
-        s[L_::Q + e] = qq;
-        s[L_::BK + e] = bb * kk;
-        lt.k[r * SP + c] = kk;
-        lt.q[r * SP + c] = qq;
-        lt.bk[r * SP + c] = bb * kk;
-        lt.g[r * SP + c] = ll;
-    }
-    for (int e = tid; e < C * DV; e += kBwdThreads) {
-        const int r = e / DV, c = e - r * DV;
-        float x = 0.f;
-        if (r < Lr) {
-            const size_t ov = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c;
-            x = io<T>::ld(w + ov) * io<T>::ld(v + ov);
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int e = tid + i * kBwdThreads, r = e / DV, c = e - r * DV;
+            xw[i] = xv[i] = 0.f;
+            if (r < Lr) {
+                const size_t ov = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c;
+                xw[i] = io<T>::ld(w + ov);
+                xv[i] = io<T>::ld(v + ov);
+            }
         }
-        s[L_::X + e] = x;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e = tid + i * kBwdThreads, r = e / DK, c = e - r * DK;
+            s[L_::K + e] = kk[i];
+            s[L_::Q + e] = qq[i];
+            s[L_::BK + e] = bb[i] * kk[i];
+            lt.k[r * SP + c] = kk[i];
+            lt.q[r * SP + c] = qq[i];
+            lt.bk[r * SP + c] = bb[i] * kk[i];
+            lt.g[r * SP + c] = ll[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NX; ++i) s[L_::X + tid + i * kBwdThreads] = xw[i] * xv[i];
     }
     __syncthreads();
     // the cumulative decay, one channel per thread
@@ -289,17 +302,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
         }
     }
     __syncthreads();
-    // Tm = (I + A)^-1 by forward substitution in LDS (the key tiles are no longer needed),
-    // one column per thread
+    // Tm = (I + A)^-1 by forward substitution (A strictly lower: row r of column col is
+    // [r == col] - sum_{i<r} A[r][i] Tm[i][col], zero above the diagonal by itself), with A in
+    // LDS (the key tiles are no longer needed). Eight lanes per column: lane l keeps
+    // Tm[i][col] for i = l mod 8 in registers and sums those terms of each row; the eight
+    // partial sums meet by lane exchanges.
     float *lA = reinterpret_cast<float *>(smem), *lT = lA + C * C;
     for (int e = tid; e < C * C; e += kBwdThreads) lA[e] = s[L_::A + e];
     __syncthreads();
-    if (tid < C) {
-        const int jc = tid;
+    {
+        static_assert(C * 8 == kBwdThreads, "eight lanes per column of Tm");
+        const int col = tid >> 3, l = tid & 7;
+        float tr[C / 8];
+#pragma unroll
+        for (int ib = 0; ib < C / 8; ++ib) tr[ib] = 0.f;
+#pragma unroll
         for (int r = 0; r < C; ++r) {
-            float t = r == jc ? 1.f : 0.f;
-            for (int i = jc; i < r; ++i) t -= lA[r * C + i] * lT[i * C + jc];
-            lT[r * C + jc] = r < jc ? 0.f : t;
+            float part = 0.f;
+#pragma unroll
+            for (int ib = 0; 8 * ib < r; ++ib)
+                if (8 * ib + l < r) part += lA[r * C + 8 * ib + l] * tr[ib];
+            part += __shfl_xor(part, 1);
+            part += __shfl_xor(part, 2);
+            part += __shfl_xor(part, 4);
+            const float t = (r == col ? 1.f : 0.f) - part;
+            if ((r & 7) == l) {
+                tr[r >> 3] = t;
+                lT[r * C + col] = t;
+            }
         }
     }
     __syncthreads();
@@ -567,11 +597,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     block_mm_lds<C, DV, C, true, false>(lf, [&](int m, int kk) { return sc[L_::TM + kk * C + m]; },
              [&](int kk, int nn) { return sc[L_::DU + kk * DV + nn]; },
              [&](int m, int nn, float x) { s[L_::DX + m * DV + nn] = x; });
-    for (int c = tid; c < DK; c += kBwdThreads) {      // dL/d gamma_L (before the exp)
+    {                                                   // dL/d gamma_L (before the exp)
+        constexpr int PARTS = kBwdThreads / DK, PV = DV / PARTS;
+        static_assert(PARTS == 4 || PARTS == 8, "four or eight threads per key channel");
+        const int c = tid / PARTS, part = tid - c * PARTS;
+        const size_t o = static_cast<size_t>(c) * DV + part * PV;
         float acc = 0.f;
-        for (int vv = 0; vv < DV; ++vv)
-            acc += sc[L_::DSN + static_cast<size_t>(c) * DV + vv] * S[static_cast<size_t>(c) * DV + vv];
-        s[L_::DGL + c] = acc;
+#pragma unroll
+        for (int vv = 0; vv < PV; ++vv) acc += sc[L_::DSN + o + vv] * S[o + vv];
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        if (PARTS == 8) acc += __shfl_xor(acc, 4);
+        if (part == 0) s[L_::DGL + c] = acc;
     }
     __syncthreads();
     // dY = Tm^T dW~, dT = dU X^T + dW~ Y^T
@@ -704,14 +741,20 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     }
     __syncthreads();
     // d log alpha: reverse cumulative sum of dg, with the gamma_L terms on the last row
+    // (16 rows per batch, whose loads all precede their stores)
     for (int c = tid; c < DK; c += kBwdThreads) {
         float acc = __expf(sc[L_::GL + c]) * sc[L_::DGL + c];
 #pragma unroll 16
         for (int x = 0; x < C; ++x) acc += sc[L_::DKG + x * DK + c];
-#pragma unroll 16
-        for (int x = C - 1; x >= 0; --x) {
-            acc += sc[L_::DY + x * DK + c];
-            if (x < Lr) p.dla[(static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c] = acc;
+        for (int x0 = C - 16; x0 >= 0; x0 -= 16) {
+            float dgv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) dgv[i] = sc[L_::DY + (x0 + i) * DK + c];
+#pragma unroll
+            for (int i = 15; i >= 0; --i) {
+                acc += dgv[i];
+                if (x0 + i < Lr) p.dla[(static_cast<size_t>(t0 + x0 + i) * p.h_v + h) * DK + c] = acc;
+            }
         }
     }
 }
