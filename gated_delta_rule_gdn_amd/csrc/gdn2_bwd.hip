@@ -56,7 +56,10 @@ struct BLay {
                             DT = A + 4 * CC, TMP = A + 5 * CC, DA = A + 6 * CC;
     // [DK]
     static constexpr size_t GL = A + 7 * CC, DGL = GL + DK;
-    static constexpr size_t FLOATS = DGL + DK;
+    // bf16 inputs: the reverse pass's W~ and Kg operands, split into bf16 hi and lo parts
+    // (2 CK floats of u32x4 fragments: W~ hi, W~ lo, Kg hi, Kg lo)
+    static constexpr size_t OPS = DGL + DK;
+    static constexpr size_t FLOATS = OPS + 2 * CK;
 };
 
 // LDS copies of g, k, q and b.k of one record with row stride SP floats (DK + 1 where the
@@ -173,6 +176,28 @@ __device__ void block_mm_lds(float *lds, FA a, FB b, FS store) {
     block_mm<M, N, K>([&](int m, int k) { return As[m * SA + k]; },
                       [&](int k, int n) { return Bs[k * SB + n]; }, store);
     __syncthreads();
+}
+
+// Eight fp32 values -> a bf16 matrix-core operand in the order of mma_k32 (slots 0-3 and
+// 4-7 as given) as hi = bf16(x) and lo = bf16(x - hi): hi*hi + hi*lo + lo*hi keeps about 16
+// significant bits of a product.
+__device__ __forceinline__ void split_op(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t h = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+        hi[j] = h;
+        lo[j] = pack_bf16x2(x[2 * j] - bf16_lo(h), x[2 * j + 1] - bf16_hi(h));
+    }
+}
+__device__ __forceinline__ f32x4 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+    c = mma_k32(ah, bh, c);
+    c = mma_k32(ah, bl, c);
+    return mma_k32(al, bh, c);
+}
+// two D tiles (k rows 0-15 and 16-31) as a split B operand
+__device__ __forceinline__ void split_dpair(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &lo) {
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    split_op(x, hi, lo);
 }
 
 // Clears the atomically accumulated dq and dk.
@@ -350,6 +375,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
              [&](int m, int nn, float x) { s[L_::E1 + m * DV + nn] = x; });
     block_mm_lds<DK, DV, C, true, false>(lf, [&](int m, int kk) { return sc[L_::QG + kk * DK + m]; }, dO_at,
              [&](int m, int nn, float x) { s[L_::E2 + m * DV + nn] = x; });
+    if constexpr (sizeof(T) == 2) {
+        // The reverse pass's bf16 operands, split here once rather than by every wave at
+        // every step: -W~^T tiles (A operands of dS) and Kg tiles (A operands of dU), each
+        // as the u32x4 fragment lane (li, lg) passes to mma_k32, hi parts then lo parts.
+        constexpr int UT = C / 16, RT = DK / 16, NOP = UT * (RT / 2) * 64;
+        u32x4 *ops = reinterpret_cast<u32x4 *>(s + L_::OPS);
+        for (int e = tid; e < NOP; e += kBwdThreads) {
+            const int lane = e & 63, li = lane & 15, lg = lane >> 4, t = e >> 6;
+            float xa[8];
+            u32x4 hi, lo;
+            const int rt = t / (UT / 2), kw = t - rt * (UT / 2);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                xa[q] = -sc[L_::WT + (32 * kw + 4 * lg + q) * DK + 16 * rt + li];
+                xa[4 + q] = -sc[L_::WT + (32 * kw + 16 + 4 * lg + q) * DK + 16 * rt + li];
+            }
+            split_op(xa, hi, lo);
+            ops[e] = hi;
+            ops[NOP + e] = lo;
+            const int ut = t / (RT / 2), kk = t - ut * (RT / 2);
+            const float *row = sc + L_::KG + (16 * ut + li) * DK + 32 * kk + 4 * lg;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                xa[q] = row[q];
+                xa[4 + q] = row[16 + q];
+            }
+            split_op(xa, hi, lo);
+            ops[2 * NOP + e] = hi;
+            ops[3 * NOP + e] = lo;
+        }
+    }
 }
 
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
@@ -358,29 +414,8 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
 // s_waitcnt with vmcnt(0) only
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Eight fp32 values -> a bf16 matrix-core operand in the order of mma_k32 (slots 0-3 and
-// 4-7 as given) as hi = bf16(x) and lo = bf16(x - hi): hi*hi + hi*lo + lo*hi keeps about 16
-// significant bits of a product.
-__device__ __forceinline__ void split_op(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t h = pack_bf16x2(x[2 * j], x[2 * j + 1]);
-        hi[j] = h;
-        lo[j] = pack_bf16x2(x[2 * j] - bf16_lo(h), x[2 * j + 1] - bf16_hi(h));
-    }
-}
-__device__ __forceinline__ f32x4 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
-    c = mma_k32(ah, bh, c);
-    c = mma_k32(ah, bl, c);
-    return mma_k32(al, bh, c);
-}
-// two D tiles (k rows 0-15 and 16-31) as a split B operand
-__device__ __forceinline__ void split_dpair(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &lo) {
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    split_op(x, hi, lo);
-}
-
-// LDS stage of one chunk for the reverse pass: W~ and Kg ([C][DK] each, adjacent in the
+// LDS stage of one chunk for the reverse pass (W~ and Kg as fp32 tiles, or with bf16
+// inputs as split operand fragments of the same size, then g_L): W~ and Kg ([C][DK] each, adjacent in the
 // record scratch), then g_L.
 template <int DK>
 struct ChainStage {
@@ -421,7 +456,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
         return p.scr + (static_cast<size_t>(cbase + c) * p.h_v + h) * L_::FLOATS;
     };
     auto stage = [&](int c, char *dst) {            // this wave's share of chunk c's copies
-        const char *src = reinterpret_cast<const char *>(scratch(c) + L_::WT);
+        const char *src = reinterpret_cast<const char *>(scratch(c) + (BF ? L_::OPS : L_::WT));
         for (int blk = wave; blk < CS::TILES / 1024; blk += 4)
             dma16(src + blk * 1024 + lane * 16, dst + blk * 1024);
         if (wave == 3 && lane < DK / 4)
@@ -471,6 +506,8 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
         }
         const float *wt = reinterpret_cast<const float *>(buf);
         const float *kg = wt + C * DK;
+        constexpr int NOP = UT * (RT / 2) * 64;
+        const u32x4 *ops = reinterpret_cast<const u32x4 *>(buf);      // bf16 inputs
         const float *gl = wt + 2 * C * DK;
         float *s = scratch(c);
 #pragma unroll
@@ -491,13 +528,8 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
             if constexpr (BF) {
 #pragma unroll
                 for (int k2 = 0; k2 < RT / 2; ++k2) {
-                    const float *row = &kg[(16 * ut + li) * DK + 32 * k2 + 4 * lg];
-                    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row);
-                    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(row + 16);
-                    const float xa[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                    u32x4 ah, al;
-                    split_op(xa, ah, al);
-                    acc = mma3(ah, al, dbh[k2], dbl[k2], acc);
+                    const int o = (ut * (RT / 2) + k2) * 64 + lane;
+                    acc = mma3(ops[2 * NOP + o], ops[3 * NOP + o], dbh[k2], dbl[k2], acc);
                 }
             } else {
 #pragma unroll
@@ -525,15 +557,8 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
             if constexpr (BF) {
 #pragma unroll
                 for (int k2 = 0; k2 < UT / 2; ++k2) {
-                    float xa[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        xa[e] = -wt[(32 * k2 + 4 * lg + e) * DK + 16 * rt + li];
-                        xa[4 + e] = -wt[(32 * k2 + 16 + 4 * lg + e) * DK + 16 * rt + li];
-                    }
-                    u32x4 ah, al;
-                    split_op(xa, ah, al);
-                    acc = mma3(ah, al, ubh[k2], ubl[k2], acc);
+                    const int o = (rt * (UT / 2) + k2) * 64 + lane;
+                    acc = mma3(ops[o], ops[NOP + o], ubh[k2], ubl[k2], acc);
                 }
             } else {
 #pragma unroll
@@ -761,7 +786,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
 
 template <typename T, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
-    static_assert(BLay<DK, DV>::FLOATS == 12 * static_cast<size_t>(C) * DK + 6 * static_cast<size_t>(C) * DV +
+    static_assert(BLay<DK, DV>::FLOATS == 14 * static_cast<size_t>(C) * DK + 6 * static_cast<size_t>(C) * DV +
                       2 * static_cast<size_t>(DK) * DV + 7 * static_cast<size_t>(C) * C + 2 * DK,
                   "the per-record scratch matches chunk_bwd_workspace_bytes");
     const bool packed = a.cu_seqlens != nullptr;
@@ -850,7 +875,7 @@ size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, i
                                  bool bf16, bool packed) {
     const int64_t nrec = chunk_upper_bound(batch, seqlen, num_seqs, packed) * h_v;
     // (the floats of BLay<d_k, d_v>)
-    const size_t per = 4 * (12 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * d_v +
+    const size_t per = 4 * (14 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * d_v +
                             2 * static_cast<size_t>(d_k) * d_v + 7 * static_cast<size_t>(C) * C + 2 * d_k);
     const size_t o_bytes = (static_cast<size_t>(batch) * seqlen * h_v * d_v * (bf16 ? 2 : 4) + 255) / 256 * 256;
     const size_t head = (chunk_workspace_bytes(batch, seqlen, num_seqs, h_v, d_k, d_v, bf16, packed) +
