@@ -25,7 +25,7 @@
 // The record kernels keep their intermediates in a per-record fp32 scratch of the workspace
 // and stage each product's operands in LDS; the products are fp32 matrix-core tiles
 // (16x16x4). q and k gradients of value heads that share a key head are summed with fp32
-// atomics.
+// atomics; with one value head per key head they are stored.
 #include "gdn2_common.h"
 #include "gdn2_internal.h"
 #include "gdn2_mfma.h"
@@ -737,8 +737,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
         const float gx = lt.g[x * SP + c];
         const float p1 = sc[L_::WT + e], p2 = sc[L_::Y + e], p3 = sc[L_::KG + e], p4 = sc[L_::QG + e];
         const float ga = __expf(gx), fk = __expf(sc[L_::GL + c] - gx);
-        const float kk = sc[L_::K + x * DK + c], qq = sc[L_::Q + x * DK + c];
-        const float bk = sc[L_::BK + x * DK + c];
+        const float kk = lt.k[x * SP + c], qq = lt.q[x * SP + c], bk = lt.bk[x * SP + c];
         const float dy = sc[L_::DY + x * DK + c], dqg = sc[L_::DQG + x * DK + c];
         const float dkg = sc[L_::DKG + x * DK + c];
         const float bb = x < Lr ? io<T>::ld(b + (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c) : 0.f;
@@ -750,8 +749,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
         if (x < Lr) {
             const size_t ok = (static_cast<size_t>(t0 + x) * p.h_k + hk) * DK + c;
             const size_t og = (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c;
-            atomicAdd(dq + ok, p3 + ga * dqg);
-            atomicAdd(dk + ok, p4 + p2 + fk * dkg + bb * dbk);
+            if (p.group == 1) {
+                dq[ok] = p3 + ga * dqg;
+                dk[ok] = p4 + p2 + fk * dkg + bb * dbk;
+            } else {
+                atomicAdd(dq + ok, p3 + ga * dqg);
+                atomicAdd(dk + ok, p4 + p2 + fk * dkg + bb * dbk);
+            }
             p.db[og] = kk * dbk;
         }
     }
@@ -766,20 +770,39 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     }
     __syncthreads();
     // d log alpha: reverse cumulative sum of dg, with the gamma_L terms on the last row
-    // (16 rows per batch, whose loads all precede their stores)
-    for (int c = tid; c < DK; c += kBwdThreads) {
-        float acc = __expf(sc[L_::GL + c]) * sc[L_::DGL + c];
-#pragma unroll 16
-        for (int x = 0; x < C; ++x) acc += sc[L_::DKG + x * DK + c];
-        for (int x0 = C - 16; x0 >= 0; x0 -= 16) {
-            float dgv[16];
+    // PARTS threads per key channel, RP rows each: every load first, then the partial sums
+    // meet by lane exchanges (the DKG terms over all rows, the dg sums of later parts)
+    {
+        constexpr int PARTS = kBwdThreads / DK, RP = C / PARTS;
+        static_assert(PARTS * DK == kBwdThreads && (PARTS == 4 || PARTS == 8), "parts per channel");
+        const int c = tid / PARTS, part = tid - c * PARTS, x0 = part * RP;
+        float dgv[RP], dkt[RP];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) dgv[i] = sc[L_::DY + (x0 + i) * DK + c];
+        for (int i = 0; i < RP; ++i) {
+            dgv[i] = sc[L_::DY + (x0 + i) * DK + c];
+            dkt[i] = sc[L_::DKG + (x0 + i) * DK + c];
+        }
+        const float base = __expf(sc[L_::GL + c]) * sc[L_::DGL + c];
+        float all = 0.f, own = 0.f;
 #pragma unroll
-            for (int i = 15; i >= 0; --i) {
-                acc += dgv[i];
-                if (x0 + i < Lr) p.dla[(static_cast<size_t>(t0 + x0 + i) * p.h_v + h) * DK + c] = acc;
-            }
+        for (int i = 0; i < RP; ++i) {
+            all += dkt[i];
+            own += dgv[i];
+        }
+        all += __shfl_xor(all, 1);
+        all += __shfl_xor(all, 2);
+        if (PARTS == 8) all += __shfl_xor(all, 4);
+        float later = 0.f;
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q) {
+            const float o = __shfl(own, q, PARTS);
+            if (q > part) later += o;
+        }
+        float acc = base + all + later;
+#pragma unroll
+        for (int i = RP - 1; i >= 0; --i) {
+            acc += dgv[i];
+            if (x0 + i < Lr) p.dla[(static_cast<size_t>(t0 + x0 + i) * p.h_v + h) * DK + c] = acc;
         }
     }
 }
@@ -823,7 +846,7 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     p.nc_dense = (a.seqlen + C - 1) / C;
     p.h_k = a.h_k; p.h_v = a.h_v; p.group = a.h_v / a.h_k;
     const int64_t qk = static_cast<int64_t>(a.batch) * a.seqlen * a.h_k * DK;
-    if (qk > 0) {
+    if (qk > 0 && p.group > 1) {
         const int64_t blocks = (qk + 255) / 256;
         hipLaunchKernelGGL(zero_kernel, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
                            a.dq, a.dk, qk);

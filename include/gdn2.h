@@ -223,7 +223,8 @@ size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
  *   dS_T        device fp32 [N, h_v, d_k, d_v]: dL/dS_T, or NULL for zero
  *   dq, dk      device fp32 [B, T, h_k, d_k]   (value heads that share a key head add up,
  *               with fp32 atomics: when h_v > h_k the summation order, and so the last bits,
- *               may differ between runs)
+ *               may differ between runs; with h_v == h_k they are stored, and every call
+ *               gives the same bits)
  *   dv, dw      device fp32 [B, T, h_v, d_v]
  *   dlog_alpha, db   device fp32 [B, T, h_v, d_k]
  *   dS0         device fp32 [N, h_v, d_k, d_v]: dL/dS0 (written also when S0 is NULL)
