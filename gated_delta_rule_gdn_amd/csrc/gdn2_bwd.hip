@@ -675,88 +675,80 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
     //   P1[x] = sum_{i<x}  dA[x,i] k_i E[x,i],   P3[x] = sum_{i<=x} dM[x,i] k_i E[x,i]   (x in B)
     //   P2[x] = sum_{r>x}  dA[r,x] bk_r E[r,x],  P4[x] = sum_{r>=x} dM[r,x] q_r E[r,x]  (x in B)
     // dA and dM carry their triangular masks, so each block runs over whole 16-row k blocks.
-    // Written to free scratch tiles: P1 -> W~, P2 -> Y, P3 -> Kg, P4 -> Qg.
+    // One wave per (row block, 16 key channels) forms all four (B + 1 plus 4 - B k blocks,
+    // the same work for every unit), then takes them through E, Y, Qg and Kg to q, k, b and
+    // g for its 16 x 16 entries: lane (li, lg) holds rows 16 B + 4 lg + ii of channel
+    // n0 + li. Its scratch loads are issued before the products.
+    float *dq = p.dq, *dk = p.dk;
     {
         const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
         constexpr int NW = kBwdThreads / 64, CT = DK / 16;
-        for (int u = wave; u < 4 * CT * 2; u += NW) {
-            const int side = u / (4 * CT), rest = u - side * 4 * CT;
-            const int B = rest / CT, n0 = (rest - B * CT) * 16, rho = 16 * B + 7, c = n0 + li;
+        for (int u = wave; u < 4 * CT; u += NW) {
+            const int B = u / CT, n0 = (u - B * CT) * 16, rho = 16 * B + 7, c = n0 + li;
+            float dy[4], dqg[4], dkg[4], bb[4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int x = 16 * B + 4 * lg + ii;
+                dy[ii] = sc[L_::DY + x * DK + c];
+                dqg[ii] = sc[L_::DQG + x * DK + c];
+                dkg[ii] = sc[L_::DKG + x * DK + c];
+                bb[ii] = x < Lr ? io<T>::ld(b + (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c) : 0.f;
+            }
+            const float glc = sc[L_::GL + c];
             const float grho = lt.g[rho * SP + c];
-            f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc1;
-            if (side == 0) {                        // P1, P3: k over rows 0 .. 16 B + 15
-                for (int kb = 0; kb <= B; ++kb) {
-                    f32x4 a1, a3, bv;
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a3 = a1, a2 = a1, a4 = a1;
+            for (int kb = 0; kb <= B; ++kb) {           // P1, P3: k over rows 0 .. 16 B + 15
+                f32x4 d1, d3, bv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * kb + 4 * lg + e;
-                        a1[e] = lDA[(16 * B + li) * C + i];
-                        a3[e] = lDM[(16 * B + li) * C + i];
-                        bv[e] = lt.k[i * SP + c] * __expf(grho - lt.g[i * SP + c]);
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * kb + 4 * lg + e;
+                    d1[e] = lDA[(16 * B + li) * C + i];
+                    d3[e] = lDM[(16 * B + li) * C + i];
+                    bv[e] = lt.k[i * SP + c] * __expf(grho - lt.g[i * SP + c]);
+                }
+                a1 = mma_k16_f32(d1, bv, a1);
+                a3 = mma_k16_f32(d3, bv, a3);
+            }
+            for (int kb = B; kb < C / 16; ++kb) {       // P2, P4: k over rows 16 B .. C - 1
+                f32x4 d2, d4, b2, b4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * kb + 4 * lg + e;
+                    d2[e] = lDA[r * C + 16 * B + li];
+                    d4[e] = lDM[r * C + 16 * B + li];
+                    const float f = __expf(lt.g[r * SP + c] - grho);
+                    b2[e] = lt.bk[r * SP + c] * f;
+                    b4[e] = lt.q[r * SP + c] * f;
+                }
+                a2 = mma_k16_f32(d2, b2, a2);
+                a4 = mma_k16_f32(d4, b4, a4);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int x = 16 * B + 4 * lg + ii;
+                const float gx = lt.g[x * SP + c];
+                const float f0 = __expf(gx - grho), f1 = __expf(grho - gx);
+                const float p1 = a1[ii] * f0, p3 = a3[ii] * f0, p2 = a2[ii] * f1, p4 = a4[ii] * f1;
+                const float ga = __expf(gx), fk = __expf(glc - gx);
+                const float kk = lt.k[x * SP + c], qq = lt.q[x * SP + c], bk = lt.bk[x * SP + c];
+                const float dbk = p1 + ga * dy[ii];
+                const float dgv = bk * p1 - kk * p2 + qq * p3 - kk * p4 + ga * bk * dy[ii] +
+                                  ga * qq * dqg[ii] - fk * kk * dkg[ii];
+                s[L_::DY + x * DK + c] = dgv;          // this lane's own entries, read above
+                s[L_::DKG + x * DK + c] = fk * kk * dkg[ii];
+                if (x < Lr) {
+                    const size_t ok = (static_cast<size_t>(t0 + x) * p.h_k + hk) * DK + c;
+                    const size_t og = (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c;
+                    if (p.group == 1) {
+                        dq[ok] = p3 + ga * dqg[ii];
+                        dk[ok] = p4 + p2 + fk * dkg[ii] + bb[ii] * dbk;
+                    } else {
+                        atomicAdd(dq + ok, p3 + ga * dqg[ii]);
+                        atomicAdd(dk + ok, p4 + p2 + fk * dkg[ii] + bb[ii] * dbk);
                     }
-                    acc1 = mma_k16_f32(a1, bv, acc1);
-                    acc2 = mma_k16_f32(a3, bv, acc2);
-                }
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int x = 16 * B + 4 * lg + ii;
-                    const float f = __expf(lt.g[x * SP + c] - grho);
-                    s[L_::WT + x * DK + c] = acc1[ii] * f;
-                    s[L_::KG + x * DK + c] = acc2[ii] * f;
-                }
-            } else {                                // P2, P4: k over rows 16 B .. C - 1
-                for (int kb = B; kb < C / 16; ++kb) {
-                    f32x4 a2, a4, b2, b4;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * kb + 4 * lg + e;
-                        a2[e] = lDA[r * C + 16 * B + li];
-                        a4[e] = lDM[r * C + 16 * B + li];
-                        const float f = __expf(lt.g[r * SP + c] - grho);
-                        b2[e] = lt.bk[r * SP + c] * f;
-                        b4[e] = lt.q[r * SP + c] * f;
-                    }
-                    acc1 = mma_k16_f32(a2, b2, acc1);
-                    acc2 = mma_k16_f32(a4, b4, acc2);
-                }
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int x = 16 * B + 4 * lg + ii;
-                    const float f = __expf(grho - lt.g[x * SP + c]);
-                    s[L_::Y + x * DK + c] = acc1[ii] * f;
-                    s[L_::QG + x * DK + c] = acc2[ii] * f;
+                    p.db[og] = kk * dbk;
                 }
             }
-        }
-    }
-    __syncthreads();
-    // through E, Y, Qg, Kg to q, k, b and g; one (row x, key channel c) per thread
-    float *dq = p.dq, *dk = p.dk;
-    for (int e = tid; e < C * DK; e += kBwdThreads) {
-        const int x = e / DK, c = e - x * DK;
-        const float gx = lt.g[x * SP + c];
-        const float p1 = sc[L_::WT + e], p2 = sc[L_::Y + e], p3 = sc[L_::KG + e], p4 = sc[L_::QG + e];
-        const float ga = __expf(gx), fk = __expf(sc[L_::GL + c] - gx);
-        const float kk = lt.k[x * SP + c], qq = lt.q[x * SP + c], bk = lt.bk[x * SP + c];
-        const float dy = sc[L_::DY + x * DK + c], dqg = sc[L_::DQG + x * DK + c];
-        const float dkg = sc[L_::DKG + x * DK + c];
-        const float bb = x < Lr ? io<T>::ld(b + (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c) : 0.f;
-        const float dbk = p1 + ga * dy;
-        const float dgv = bk * p1 - kk * p2 + qq * p3 - kk * p4 + ga * bk * dy + ga * qq * dqg -
-                          fk * kk * dkg;
-        s[L_::DY + x * DK + c] = dgv;              // this thread's own entries, read above
-        s[L_::DKG + x * DK + c] = fk * kk * dkg;
-        if (x < Lr) {
-            const size_t ok = (static_cast<size_t>(t0 + x) * p.h_k + hk) * DK + c;
-            const size_t og = (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c;
-            if (p.group == 1) {
-                dq[ok] = p3 + ga * dqg;
-                dk[ok] = p4 + p2 + fk * dkg + bb * dbk;
-            } else {
-                atomicAdd(dq + ok, p3 + ga * dqg);
-                atomicAdd(dk + ok, p4 + p2 + fk * dkg + bb * dbk);
-            }
-            p.db[og] = kk * dbk;
         }
     }
     for (int e = tid; e < C * DV; e += kBwdThreads) {
