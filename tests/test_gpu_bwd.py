@@ -1,9 +1,9 @@
 """GPU parity of the chunked backward (gdn2_chunk_bwd) against the oracle's token-by-token
 adjoint of the recurrence (oracle.recurrent_bwd), every gradient by relative L2: 1e-4 for
 fp32 inputs, 2e-2 for bf16 inputs. Cases: ragged tails, grouped value heads (2 and 3 per
-key head), every built head shape, packed batches with an empty sequence, zero initial
-state and zero dS_T, and the timed chunk shape (whose forward takes the segmented state
-pass)."""
+key head, and 4 over 32 pairs), every built head shape, packed batches with an empty
+sequence, zero initial state and zero dS_T, and the timed chunk shape (whose forward takes
+the segmented state pass); bit-equal repeated calls when no value heads share a key head."""
 import numpy as np
 import pytest
 import torch
@@ -97,6 +97,30 @@ def test_bwd_timed_chunk_shape():
     """B=1 T=4096 H=16 d=128 (64 chunks per pair; the forward that stores the chunk states
     takes the segmented state pass)."""
     run_case(inputs.chunk_inputs(inputs.CHUNK_BF16_T4096, seed=66), "bf16 B=1 T=4096 H=16", 6)
+
+
+def test_bwd_grouped_heads_at_scale():
+    """Four value heads per key head over 32 (sequence, value head) pairs of 16 chunks: the
+    q and k gradients of each key head are summed with atomics from four records at once,
+    and the forward takes the segmented state pass."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=2, seqlen=1000, h_k=4, h_v=16,
+                            d_k=128, d_v=128, neg_eig=True)
+    run_case(inputs.chunk_inputs(wl, seed=67), "bf16 B=2 T=1000 H_k=4 H_v=16", 7)
+
+
+def test_bwd_is_deterministic_without_grouped_heads():
+    """With one value head per key head no gradient is summed with atomics: two calls give
+    the same bits."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=2, seqlen=300, h_k=3, h_v=3,
+                            d_k=128, d_v=128, neg_eig=True)
+    d = to_gpu(inputs.chunk_inputs(wl, seed=68))
+    dO = torch.randn(2, 300, 3, 128, device="cuda").to(torch.bfloat16)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO)
+    first = g.chunk_bwd(*args, S0=d["S0"])
+    second = g.chunk_bwd(*args, S0=d["S0"])
+    torch.cuda.synchronize()
+    for n in first:
+        assert torch.equal(first[n], second[n]), n
 
 
 def test_bwd_empty_batch_passes_the_final_gradient_through():
