@@ -600,7 +600,7 @@ def main():
         pmc_summary(*args.pmc_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(pass --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
