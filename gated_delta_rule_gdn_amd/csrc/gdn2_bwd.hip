@@ -23,9 +23,11 @@
 //                       dS' it leaves, then dS0
 //   bwd_grads_kernel    per record, in parallel: every input gradient of the chunk
 // The record kernels keep their intermediates in a per-record fp32 scratch of the workspace
-// and stage each product's operands in LDS; the products are fp32 matrix-core tiles
-// (16x16x4). q and k gradients of value heads that share a key head are summed with fp32
-// atomics; with one value head per key head they are stored.
+// and stage each product's operands in LDS; their products are fp32 matrix-core tiles
+// (16x16x4). With bf16 inputs the reverse pass takes three bf16 products of hi/lo-split
+// operands, which the factors kernel splits once per record. q and k gradients of value
+// heads that share a key head are summed with fp32 atomics; with one value head per key
+// head they are stored.
 #include "gdn2_common.h"
 #include "gdn2_internal.h"
 #include "gdn2_mfma.h"
