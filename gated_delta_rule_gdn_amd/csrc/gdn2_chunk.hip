@@ -980,13 +980,20 @@ typedef __attribute__((address_space(3))) volatile int lds_flag;
 
 // Spin (bounded) until an LDS flag written by another wave of the workgroup reaches `want`.
 // The writer is always able to progress, so the bound is never reached in a correct run; it
-// only guarantees that every wave exits.
-__device__ __forceinline__ void wait_flag(lds_flag *flag, int want) {
+// guarantees that every wave exits. Returns false if the bound was reached: the caller then
+// writes NaN in place of the outputs that depended on the flag, so a missed publication
+// shows up in the results instead of passing stale operands on silently.
+__device__ __forceinline__ bool wait_flag(lds_flag *flag, int want) {
+    bool ok = false;
     for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (*flag >= want) break;
+        if (*flag >= want) {
+            ok = true;
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
+    return ok;
 }
 
 // copy waves per state-pass workgroup: six, four with four slices (the register budget of
@@ -1264,7 +1271,7 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
         // O = Qg S
-        wait_flag(flagS, c + 1);
+        bool published = wait_flag(flagS, c + 1);
         u32x4 SB[NKD];
 #pragma unroll
         for (int kt = 0; kt < NKD; ++kt) SB[kt] = xS[kt * 64 + lane];
@@ -1277,7 +1284,7 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
                                          __builtin_bit_cast(f32x4, SB[kt]), O[rt]);
             }
         // O += M U   (M is lower triangular: k tiles above the diagonal are skipped)
-        wait_flag(flagU, c + 1);
+        published = wait_flag(flagU, c + 1) && published;
         u32x4 UB[NKC];
 #pragma unroll
         for (int kt = 0; kt < NKC; ++kt) UB[kt] = xU[kt * 64 + lane];
@@ -1293,6 +1300,10 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
         // o rows through LDS (over the consumed U operands, row-major [C][16]) into 16-byte
         // row pieces, stored straight to memory
         T *otile = reinterpret_cast<T *>(xU);
+        if (!published) {                   // a wait ran out: NaN rows, not stale results
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) O[rt] = f32x4{NAN, NAN, NAN, NAN};
+        }
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll

@@ -53,9 +53,11 @@ def select(o, S, cu, pairs):
     return np.concatenate(parts_o), np.concatenate(parts_s)
 
 
-def assert_chunk_parity(x, dtype, pairs=None, label=""):
-    """Runs both paths; compares all pairs (or the sampled ones) within the dtype's tolerance."""
-    o_g, S_g = gpu_chunk(x)
+def assert_chunk_parity(x, dtype, pairs=None, label="", worst=False, **kw):
+    """Runs both paths; compares all pairs (or the given ones) within the dtype's tolerance.
+    worst=True also prints the largest per-(sequence, head) error as a diagnostic. Extra
+    keywords go to the GPU call (chunk_size, ...)."""
+    o_g, S_g = gpu_chunk(x, **kw)
     o_r, S_r = oracle_chunk(x, pairs=pairs)
     _, cu, _ = flat_inputs(x)
     if pairs is None:
@@ -66,7 +68,14 @@ def assert_chunk_parity(x, dtype, pairs=None, label=""):
         eo, es = oracle.rel_l2(go, ro), oracle.rel_l2(gs, rs)
         assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(S_g))
     tol = TOL[dtype]
-    print(f"[parity] {label} rel_l2 o={eo:.3e} S_T={es:.3e} tol={tol:g}", flush=True)
+    extra = ""
+    if worst:
+        N, H = S_g.shape[:2]
+        wo = max(oracle.rel_l2(o_g[cu[n]:cu[n + 1], h], o_r[cu[n]:cu[n + 1], h])
+                 for n in range(N) for h in range(H) if cu[n + 1] > cu[n])
+        ws = max(oracle.rel_l2(S_g[n, h], S_r[n, h]) for n in range(N) for h in range(H))
+        extra = f" worst pair o={wo:.3e} S_T={ws:.3e}"
+    print(f"[parity] {label} rel_l2 o={eo:.3e} S_T={es:.3e} tol={tol:g}{extra}", flush=True)
     assert eo <= tol and es <= tol, (label, eo, es)
     return eo, es
 

@@ -1,9 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle on seeded inputs.
 
 Gate (relative L2 error per output tensor): 1e-4 for fp32 inputs, 2e-2 for bf16 inputs, on
-o and on the final states. Small cases compare every element; the full-size workloads
-compare every element the oracle can afford and otherwise a seeded sample of whole
-(sequence, value head) pairs, each computed over all of its tokens.
+o and on the final states. Every case compares every element of o and of the final states,
+the full-size decode and varlen workloads included (the threaded fp64 oracle on the host's
+cores); those two also report their worst single (sequence, head) pair.
 """
 from dataclasses import replace
 
@@ -14,8 +14,8 @@ import torch
 import oracle
 import gated_delta_rule_gdn_amd as g
 from gated_delta_rule_gdn_amd import inputs
-from gpu_common import (TOL, assert_chunk_parity, decode_oracle_pair, flat_inputs, gpu_chunk,
-                        np64, oracle_chunk, to_gpu)
+from gpu_common import (ORACLE_THREADS, TOL, assert_chunk_parity, decode_oracle_pair,
+                        flat_inputs, gpu_chunk, np64, oracle_chunk, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,8 +53,30 @@ def test_decode_small(dtype, dk, dv):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+def decode_oracle_all(x, steps, h_v):
+    """Every (sequence, value head) state of a decode workload over `steps` steps with the
+    threaded fp64 oracle: the steps of sequence n are its tokens. Returns (o [steps, N, H_v,
+    d_v], S [N, H_v, d_k, d_v])."""
+    N = x["S"].shape[0]
+    flat = {n: np64(x[n][:steps].transpose(0, 1)).reshape(N * steps, *x[n].shape[2:])
+            for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    o, S = oracle.recurrent(flat["q"], flat["k"], flat["v"], flat["log_alpha"], flat["b"],
+                            flat["w"], S0=np64(x["S"]), cu_seqlens=np.arange(N + 1) * steps,
+                            threads=ORACLE_THREADS)
+    return o.reshape(N, steps, h_v, -1).transpose(1, 0, 2, 3), S
+
+
+def worst_pair(o_g, o_r, S_g, S_r):
+    """Largest per-(sequence, head) relative L2 error of o (over all steps) and of S."""
+    N, H = S_g.shape[:2]
+    wo = max(oracle.rel_l2(o_g[:, n, h], o_r[:, n, h]) for n in range(N) for h in range(H))
+    ws = max(oracle.rel_l2(S_g[n, h], S_r[n, h]) for n in range(N) for h in range(H))
+    return wo, ws
+
+
 def test_decode_full_size_256_steps():
-    """64 sequences, 48 value heads over 16 key heads, d=128, fp32 state, 256 steps in place."""
+    """64 sequences, 48 value heads over 16 key heads, d=128, fp32 state, 256 steps in place;
+    every output of every step and every state after the last step against the oracle."""
     wl = inputs.DECODE_F32
     x = inputs.decode_inputs(wl, seed=3)
     dev = {n: x[n].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w")}
@@ -64,26 +86,20 @@ def test_decode_full_size_256_steps():
         g.recurrent_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["log_alpha"][t],
                          dev["b"][t], dev["w"][t], S, out=o_all[t])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, wl.num_seqs, 24),
-                                              rng.integers(0, wl.h_v, 24))]
     o_g = np64(o_all)
     S_g = np64(S)
     assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(S_g))
-    go, gs, ro, rs = [], [], [], []
-    for n, h in pairs:
-        on, Sn = decode_oracle_pair(x, n, h, wl.steps, wl.h_v // wl.h_k)
-        go.append(o_g[:, n, h].ravel()); ro.append(on.ravel())
-        gs.append(S_g[n, h].ravel()); rs.append(Sn.ravel())
-    eo = oracle.rel_l2(np.concatenate(go), np.concatenate(ro))
-    es = oracle.rel_l2(np.concatenate(gs), np.concatenate(rs))
-    print(f"[parity] decode full 256 steps, 24 sampled states: o={eo:.2e} S={es:.2e}", flush=True)
+    o_r, S_r = decode_oracle_all(x, wl.steps, wl.h_v)
+    eo, es = oracle.rel_l2(o_g, o_r), oracle.rel_l2(S_g, S_r)
+    wo, ws = worst_pair(o_g, o_r, S_g, S_r)
+    print(f"[parity] decode full 256 steps, all {wl.num_seqs * wl.h_v} states: o={eo:.2e} "
+          f"S={es:.2e}; worst state o={wo:.2e} S={ws:.2e}", flush=True)
     assert eo <= 1e-4 and es <= 1e-4
 
 
 def test_decode_state_larger_than_last_level_cache():
     """128 sequences x 48 heads (403 MB of state, above 256 MiB: streamed with non-temporal
-    stores), 4 steps in place, 24 sampled states against the oracle."""
+    stores), 4 steps in place, every state against the oracle."""
     wl = replace(inputs.DECODE_F32, num_seqs=128, steps=4)
     x = inputs.decode_inputs(wl, seed=13)
     dev = {n: x[n].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w")}
@@ -93,19 +109,12 @@ def test_decode_state_larger_than_last_level_cache():
         g.recurrent_step(dev["q"][t], dev["k"][t], dev["v"][t], dev["log_alpha"][t],
                          dev["b"][t], dev["w"][t], S, out=o_all[t])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    pairs = [(int(n), int(h)) for n, h in zip(rng.integers(0, wl.num_seqs, 24),
-                                              rng.integers(0, wl.h_v, 24))]
     o_g, S_g = np64(o_all), np64(S)
-    go, gs, ro, rs = [], [], [], []
-    for n, h in pairs:
-        on, Sn = decode_oracle_pair(x, n, h, wl.steps, wl.h_v // wl.h_k)
-        go.append(o_g[:, n, h].ravel()); ro.append(on.ravel())
-        gs.append(S_g[n, h].ravel()); rs.append(Sn.ravel())
-    eo = oracle.rel_l2(np.concatenate(go), np.concatenate(ro))
-    es = oracle.rel_l2(np.concatenate(gs), np.concatenate(rs))
-    print(f"[parity] decode 128 seqs (streamed state), 24 sampled states: o={eo:.2e} S={es:.2e}",
-          flush=True)
+    o_r, S_r = decode_oracle_all(x, wl.steps, wl.h_v)
+    eo, es = oracle.rel_l2(o_g, o_r), oracle.rel_l2(S_g, S_r)
+    wo, ws = worst_pair(o_g, o_r, S_g, S_r)
+    print(f"[parity] decode 128 seqs (streamed state), all states: o={eo:.2e} S={es:.2e}; "
+          f"worst state o={wo:.2e} S={ws:.2e}", flush=True)
     assert eo <= 1e-4 and es <= 1e-4
 
 
@@ -127,11 +136,12 @@ def test_chunk_bf16_b1_t4096_h16_d128_negeig():
 
 
 def test_varlen_bf16_n16_hv32_hk16_d128():
+    """16 packed sequences, 32 value heads over 16 key heads: all 512 (sequence, head) pairs
+    against the oracle, with the worst pair reported."""
     x = inputs.chunk_inputs(inputs.VARLEN_BF16, seed=1004)
-    rng = np.random.default_rng(4)
-    pairs = [(n, int(h)) for n in range(16) for h in rng.choice(32, 2, replace=False)]
     print("[parity] varlen tokens:", int(x["cu_seqlens"][-1]), flush=True)
-    assert_chunk_parity(x, torch.bfloat16, pairs=pairs, label="varlen bf16 16 seqs (32 pairs)")
+    eo, es = assert_chunk_parity(x, torch.bfloat16, label="varlen bf16 16 seqs (all 512 pairs)",
+                                 worst=True)
 
 
 @pytest.mark.parametrize("dtype,dk,dv", [(torch.float32, 64, 64), (torch.bfloat16, 128, 128),

@@ -683,3 +683,62 @@ def test_variant_fg2_plus_with_equal_scales_is_fg2():
     o1, S1 = oracle.variant_sequence("fg2", q, k, v, la, beta, S0)
     o2, S2 = oracle.variant_sequence("fg2+", q, k, v, la, beta, S0, beta_v=beta)
     assert close(o1, o2) and close(S1, S2)
+
+
+# ---- the parity metric and the key-head map of the variant rules ---------------------------
+
+def test_rel_l2_closed_forms():
+    """rel_l2 is ||x - ref||_2 / ||ref||_2 over every element at once (the parity gate of the
+    spec tolerance): closed forms on small vectors, and the absolute norm when the
+    reference is zero."""
+    assert abs(oracle.rel_l2([1.0, 0.0], [0.0, 1.0]) - np.sqrt(2.0)) < 1e-15
+    assert abs(oracle.rel_l2([3.0, 4.0], [0.0, 0.0]) - 5.0) < 1e-15
+    assert oracle.rel_l2([0.0, 0.0], [0.0, 0.0]) == 0.0
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((7, 5))
+    assert abs(oracle.rel_l2(2.0 * x, x) - 1.0) < 1e-14
+    assert oracle.rel_l2(x, x) == 0.0
+    # one norm over all elements, not a mean or maximum of per-row errors
+    ref = np.array([[1.0, 0.0], [0.0, 1.0]])
+    assert abs(oracle.rel_l2([[1.0, 0.0], [0.0, 2.0]], ref) - 1.0 / np.sqrt(2.0)) < 1e-15
+    assert abs(oracle.rel_l2([[1.0, 0.0], [0.0, 0.0]], ref) - 1.0 / np.sqrt(2.0)) < 1e-15
+    # a perturbation of norm eps * ||ref|| reads eps, at both gates
+    u = rng.standard_normal(x.shape)
+    u *= np.linalg.norm(x) / np.linalg.norm(u)
+    for eps in (1e-4, 2e-2):
+        assert abs(oracle.rel_l2(x + eps * u, x) - eps) < 1e-12
+    # scale invariance
+    y = x + 1e-3 * u
+    assert abs(oracle.rel_l2(1e6 * y, 1e6 * x) - oracle.rel_l2(y, x)) < 1e-12
+
+
+def test_variant_value_head_reads_key_head_group():
+    """variant(): value head h reads key head h // (H_v / H_k) (contiguous groups). Value heads
+    0, 1 and 3 get identical value-side inputs; with 6 value heads over 2 key heads, heads 0
+    and 1 must then agree exactly (both read key head 0) while head 3 must not (it reads key
+    head 1). The
+    multi-head call also equals the C oracle of GDN-2 (its own head map, pinned above against
+    single-head calls) with KDA's b = w = beta in every channel."""
+    rng = np.random.default_rng(42)
+    N, T, Hk, Hv, dk, dv = 2, 9, 2, 6, 5, 3
+    q = rng.standard_normal((N, T, Hk, dk))
+    k = rng.standard_normal((N, T, Hk, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((N, T, Hv, dv))
+    la = -np.logaddexp(0.0, rng.standard_normal((N, T, Hv, dk)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((N, T, Hv))))
+    S0 = rng.standard_normal((N, Hv, dk, dv))
+    for arr in (v, la, beta):
+        arr[:, :, 1] = arr[:, :, 0]
+        arr[:, :, 3] = arr[:, :, 0]
+    S0[:, 1] = S0[:, 0]
+    S0[:, 3] = S0[:, 0]
+    o, ST = oracle.variant("kda", q, k, v, la, beta, S0=S0)
+    assert np.array_equal(o[:, :, 1], o[:, :, 0]) and np.array_equal(ST[:, 1], ST[:, 0])
+    assert np.max(np.abs(o[:, :, 3] - o[:, :, 0])) > 1e-3
+    b = np.broadcast_to(beta[..., None], (N, T, Hv, dk))
+    w = np.broadcast_to(beta[..., None], (N, T, Hv, dv))
+    flat = lambda a: np.ascontiguousarray(a).reshape(N * T, *a.shape[2:])  # noqa: E731
+    o2, S2 = oracle.recurrent(flat(q), flat(k), flat(v), flat(la), flat(b), flat(w), S0=S0,
+                              cu_seqlens=np.arange(N + 1) * T)
+    assert close(o.reshape(N * T, Hv, dv), o2) and close(ST, S2)
