@@ -31,6 +31,7 @@ GDN2_STATE_F32, GDN2_STATE_BF16 = 0, 1
 STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL_ARG", 2: "GDN2_ERR_BAD_SHAPE",
           3: "GDN2_ERR_UNSUPPORTED", 4: "GDN2_ERR_WORKSPACE", 5: "GDN2_ERR_HIP"}
 CHUNK_SIZE = 64
+STATIC_WORKSPACE_BYTES = 128 << 20    # GDN2_STATIC_WORKSPACE_BYTES of gdn2.h
 
 
 class Dims(ctypes.Structure):
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.gdn2_check_cu_seqlens.argtypes = [vp, i32, i32]
         L.gdn2_map_gates.restype = i32
         L.gdn2_map_gates.argtypes = [i32, dp] + [vp] * 13
+        L.gdn2_chunk_fwd_noalloc.restype = i32
+        L.gdn2_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i32, vp, vp, dp, fp, vp]
         L.gdn2_chunk_bwd_workspace_bytes.restype = sz
         L.gdn2_chunk_bwd_workspace_bytes.argtypes = [dp, i32]
         L.gdn2_chunk_bwd.restype = i32
@@ -179,24 +182,10 @@ def chunk_fwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: 
     return int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), chunk_size))
 
 
-def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: int = CHUNK_SIZE,
-              output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
-              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              qk_l2norm: bool = False, l2norm_eps: float = 1e-6,
-              gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
-              norm_eps: float = 1e-5, gate_mode: Optional[str] = None,
-              chunk_states: Optional[torch.Tensor] = None
-              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked WY forward. Returns (o [B,T,H_v,d_v], S_T [N,H_v,d_k,d_v] fp32 or None).
-
-    chunk_states: an fp32 [num_chunks(...), H_v, d_k, d_v] buffer that receives the state
-    entering every chunk (see num_chunks for the row of each sequence's chunks).
-
-    qk_l2norm: L2-normalise q and k inside the kernels. gate [B,T,H_v,d_v] with norm_weight
-    fp32 [d_v]: o is returned through the gated RMS norm o/rms(o) * weight * silu(gate).
-    gate_mode ("kda", "gdn", "fg2", "fg2+"): run that variant natively; b carries its beta
-    and w is None (or beta_v for "fg2+"), see map_gates for the shapes.
-    """
+def _chunk_call(noalloc, q, k, v, log_alpha, b, w, S0, cu_seqlens, chunk_size,
+                output_final_state, workspace, out, final_state, qk_l2norm, l2norm_eps, gate,
+                norm_weight, norm_eps, gate_mode, chunk_states):
+    """Shape checks, output allocation and the C call of chunk_fwd / chunk_fwd_noalloc."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w)):
         if t is None and name == "w" and gate_mode not in (None, "fg2+"):
@@ -224,8 +213,8 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
             raise ValueError(f"S0 must be fp32 [{N},{Hv},{dk},{dv}]")
     code = _dtype_code(q.dtype)
     dims = Dims(B, T, N if cu_seqlens is not None else 0, Hk, Hv, dk, dv, code)
-    need = int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), chunk_size))
-    if workspace is None:
+    if not noalloc and workspace is None:
+        need = int(lib().gdn2_chunk_fwd_workspace_bytes(ctypes.byref(dims), chunk_size))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     o = out if out is not None else torch.empty(B, T, Hv, dv, dtype=q.dtype, device=dev)
     S_T = None
@@ -240,12 +229,56 @@ def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: in
     fu = _fusion(dev, (B, T, Hv, dv), q.dtype, qk_l2norm, l2norm_eps, gate, norm_weight,
                  norm_eps, gate_mode=gcode, chunk_states=chunk_states)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib().gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                              _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(o), _ptr(S_T),
-                              ctypes.byref(dims), _ptr(workspace), workspace.numel(),
-                              None if fu is None else ctypes.byref(fu), stream)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w), _ptr(S0),
+            _ptr(cu_seqlens), chunk_size, _ptr(o), _ptr(S_T), ctypes.byref(dims))
+    fptr = None if fu is None else ctypes.byref(fu)
+    if noalloc:
+        st = lib().gdn2_chunk_fwd_noalloc(*args, fptr, stream)
+    else:
+        st = lib().gdn2_chunk_fwd(*args, _ptr(workspace), workspace.numel(), fptr, stream)
     _raise_on(st)
     return o, S_T
+
+
+def chunk_fwd(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None, chunk_size: int = CHUNK_SIZE,
+              output_final_state: bool = True, workspace: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              qk_l2norm: bool = False, l2norm_eps: float = 1e-6,
+              gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+              norm_eps: float = 1e-5, gate_mode: Optional[str] = None,
+              chunk_states: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked WY forward. Returns (o [B,T,H_v,d_v], S_T [N,H_v,d_k,d_v] fp32 or None).
+
+    chunk_states: an fp32 [num_chunks(...), H_v, d_k, d_v] buffer that receives the state
+    entering every chunk (see num_chunks for the row of each sequence's chunks).
+
+    qk_l2norm: L2-normalise q and k inside the kernels. gate [B,T,H_v,d_v] with norm_weight
+    fp32 [d_v]: o is returned through the gated RMS norm o/rms(o) * weight * silu(gate).
+    gate_mode ("kda", "gdn", "fg2", "fg2+"): run that variant natively; b carries its beta
+    and w is None (or beta_v for "fg2+"), see map_gates for the shapes.
+    """
+    return _chunk_call(False, q, k, v, log_alpha, b, w, S0, cu_seqlens, chunk_size,
+                       output_final_state, workspace, out, final_state, qk_l2norm, l2norm_eps,
+                       gate, norm_weight, norm_eps, gate_mode, chunk_states)
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, b, w, S0=None, cu_seqlens=None,
+                      chunk_size: int = CHUNK_SIZE, output_final_state: bool = True,
+                      out: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None, qk_l2norm: bool = False,
+                      l2norm_eps: float = 1e-6, gate: Optional[torch.Tensor] = None,
+                      norm_weight: Optional[torch.Tensor] = None, norm_eps: float = 1e-5,
+                      gate_mode: Optional[str] = None,
+                      chunk_states: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """chunk_fwd through gdn2_chunk_fwd_noalloc: the workspace is the library's static device
+    array (STATIC_WORKSPACE_BYTES per GPU), so the library allocates nothing. Pass `out` (and
+    `final_state`) to allocate nothing on this side either. Calls that may overlap in time
+    on one GPU must be ordered (they share the array)."""
+    return _chunk_call(True, q, k, v, log_alpha, b, w, S0, cu_seqlens, chunk_size,
+                       output_final_state, None, out, final_state, qk_l2norm, l2norm_eps,
+                       gate, norm_weight, norm_eps, gate_mode, chunk_states)
 
 
 def chunk_bwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: int, d_v: int,

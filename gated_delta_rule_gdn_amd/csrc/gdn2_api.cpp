@@ -87,6 +87,11 @@ bool needs_w(const gdn2::Fusion &fu) {
 
 }  // namespace
 
+namespace gdn2 {
+gdn2_status report(gdn2_status st, const char *msg) { return fail(st, msg); }
+gdn2_status report_hip(hipError_t e, const char *where) { return fail_hip(e, where); }
+}  // namespace gdn2
+
 extern "C" {
 
 int32_t gdn2_abi_version(void) { return GDN2_ABI_VERSION; }

@@ -4,7 +4,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gdn2.h"
+
 namespace gdn2 {
+
+// Records a failure message for gdn2_last_error() on this thread and returns `st`.
+gdn2_status report(gdn2_status st, const char *msg);
+gdn2_status report_hip(hipError_t e, const char *where);
 
 constexpr int kChunk = 64;   // chunk size of the chunked forward
 

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 6
+#define GDN2_ABI_VERSION 7
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -204,6 +204,33 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v,
                            void *o, float *S_T, const gdn2_dims *dims,
                            void *workspace, size_t workspace_bytes,
                            const gdn2_fusion *fusion, void *stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. gdn2_chunk_fwd with the same arguments
+ * minus the workspace, which comes instead from a static device array of
+ * GDN2_STATIC_WORKSPACE_BYTES (128 MiB) that the library holds on every GPU it runs on
+ * until the process ends. The call allocates nothing (no hipMalloc, no allocating library
+ * routine); the caller still allocates the inputs and outputs.
+ *   - Calls whose gdn2_chunk_fwd_workspace_bytes() exceeds GDN2_STATIC_WORKSPACE_BYTES
+ *     return GDN2_ERR_WORKSPACE and enqueue nothing (128 MiB holds, for instance, a bf16
+ *     batch of 4,096 tokens x 16 heads at d = 128 with chunk_size 64).
+ *   - Every call on one GPU uses that GPU's one array, and the array keeps the last call's
+ *     contents (none of which a later call reads). Calls that can overlap in time on one
+ *     GPU -- issued to different streams with no ordering between them -- race on the
+ *     array and give undefined results; order them on one stream (or with events).
+ *   - The device is the stream's (the current device for a NULL stream). The first call on
+ *     a device looks the array's address up once (hipGetSymbolAddress); later calls reuse it.
+ * Results are those of gdn2_chunk_fwd (the same kernels run).
+ */
+#define GDN2_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+
+gdn2_status gdn2_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                   const void *log_alpha, const void *b, const void *w,
+                                   const float *S0, const int32_t *cu_seqlens,
+                                   int32_t chunk_size, void *o, float *S_T,
+                                   const gdn2_dims *dims, const gdn2_fusion *fusion,
+                                   void *stream);
 
 /*
  * Bytes of device workspace gdn2_chunk_bwd needs for these dims and chunk size, or 0 if

@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn2_abi_version() == 6
+    assert L.gdn2_abi_version() == 7
     assert L.gdn2_status_string(0) == b"ok"
     assert b"workspace" in L.gdn2_status_string(4)
     assert L.gdn2_status_string(99) == b"unknown status"
@@ -302,3 +302,20 @@ def test_chunk_bwd_validation(L):
     assert call(outs=[P[10], P[10]] + P[12:17]) == 2                   # dq and dk alias
     assert call(ws_bytes=need - 1) == 4
     assert call(ws=ctypes.c_void_p(0x10001)) == 4                      # misaligned workspace
+
+
+def test_chunk_fwd_noalloc_rejects_without_touching_a_device(L):
+    """The static-workspace call checks its sizes on the host first: a NULL dims, and dims
+    whose workspace exceeds GDN2_STATIC_WORKSPACE_BYTES (128 MiB), are refused before any
+    HIP call (no device is needed to see it)."""
+    def call(dims, chunk_size=64):
+        return L.gdn2_chunk_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                        chunk_size, FAKE, None,
+                                        None if dims is None else ctypes.byref(dims), None, None)
+    assert call(None) == 1
+    big = Dims(1, 8192, 0, 16, 16, 128, 128, 1)            # 2x the 4,096-token batch
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(big), 64) > g.STATIC_WORKSPACE_BYTES
+    assert call(big) == 4
+    assert b"static" in L.gdn2_last_error()
+    fits = Dims(1, 4096, 0, 16, 16, 128, 128, 1)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(fits), 64) <= g.STATIC_WORKSPACE_BYTES
