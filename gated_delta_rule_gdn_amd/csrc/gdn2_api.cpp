@@ -110,15 +110,24 @@ const char *gdn2_status_string(int32_t s) {
 
 const char *gdn2_last_error(void) { return g_last_error; }
 
+// The chunked backward is built for 64-token chunks, bf16 records at any supported head dims
+// and fp32 records at d_k = d_v = 64.
+static gdn2_status check_bwd_built(const gdn2_dims *d, int32_t chunk_size) {
+    if (!d) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
+    if (chunk_size != gdn2::kChunk)
+        return fail(GDN2_ERR_UNSUPPORTED, "the chunked backward is built for chunk_size 64");
+    if (d->dtype == GDN2_F32 && (d->d_k != 64 || d->d_v != 64))
+        return fail(GDN2_ERR_UNSUPPORTED, "the fp32 chunked backward is built for d_k = d_v = 64");
+    return GDN2_OK;
+}
+
 static gdn2_status check_chunk_dims(const gdn2_dims *d, int32_t chunk_size, bool packed) {
     if (!d) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
     gdn2_status st = check_heads(d);
     if (st != GDN2_OK) return st;
     if (chunk_size < 1) return fail(GDN2_ERR_BAD_SHAPE, "chunk_size must be >= 1");
-    if (chunk_size != gdn2::kChunk) return fail(GDN2_ERR_UNSUPPORTED, "chunk_size must be 64");
-    if (!gdn2::chunk_dims_built(d->d_k, d->d_v, d->dtype == GDN2_BF16))
-        return fail(GDN2_ERR_UNSUPPORTED,
-                    "fp32 chunk forward is built for d_k = d_v = 64 only");
+    if (!gdn2::chunk_size_built(chunk_size))
+        return fail(GDN2_ERR_UNSUPPORTED, "chunk_size must be 32, 64 or 128");
     if (d->seqlen < 0) return fail(GDN2_ERR_BAD_SHAPE, "seqlen must be >= 0");
     if (packed) {
         if (d->batch != 1) return fail(GDN2_ERR_BAD_SHAPE, "packed batches need batch = 1");
@@ -144,9 +153,10 @@ size_t gdn2_chunk_fwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
         check_chunk_dims(dims, chunk_size, packed) != GDN2_OK)
         return 0;
     const bool bf = dims->dtype == GDN2_BF16;
-    const size_t dense = gdn2::chunk_workspace_bytes(dims->batch, dims->seqlen, dims->num_seqs,
-                                                      dims->h_v, dims->d_k, dims->d_v, bf, false);
-    const size_t pk = packed ? gdn2::chunk_workspace_bytes(dims->batch, dims->seqlen,
+    const size_t dense = gdn2::chunk_workspace_bytes(chunk_size, dims->batch, dims->seqlen,
+                                                      dims->num_seqs, dims->h_v, dims->d_k,
+                                                      dims->d_v, bf, false);
+    const size_t pk = packed ? gdn2::chunk_workspace_bytes(chunk_size, dims->batch, dims->seqlen,
                                                            dims->num_seqs, dims->h_v, dims->d_k,
                                                            dims->d_v, bf, true)
                              : 0;
@@ -170,8 +180,9 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
     if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || (!w && needs_w(fu)) || !o))
         return fail(GDN2_ERR_NULL_ARG, "q, k, v, log_alpha, b, w and o are required");
     const bool bf = dims->dtype == GDN2_BF16;
-    const size_t need = gdn2::chunk_workspace_bytes(dims->batch, dims->seqlen, dims->num_seqs,
-                                                    dims->h_v, dims->d_k, dims->d_v, bf, packed);
+    const size_t need = gdn2::chunk_workspace_bytes(chunk_size, dims->batch, dims->seqlen,
+                                                    dims->num_seqs, dims->h_v, dims->d_k,
+                                                    dims->d_v, bf, packed);
     if (need > 0 && !workspace) return fail(GDN2_ERR_WORKSPACE, "workspace is NULL");
     if (workspace_bytes < need) return fail(GDN2_ERR_WORKSPACE, "workspace is too small");
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
@@ -191,6 +202,7 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
     a.workspace = static_cast<char *>(workspace);
     a.batch = dims->batch; a.seqlen = dims->seqlen; a.num_seqs = packed ? dims->num_seqs : 0;
     a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
+    a.chunk = chunk_size;
     a.bf16 = bf;
     a.fu = fu;
     const hipError_t e = gdn2::launch_chunk_fwd(a, static_cast<hipStream_t>(stream));
@@ -201,6 +213,7 @@ gdn2_status gdn2_chunk_fwd(const void *q, const void *k, const void *v, const vo
 
 size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size) {
     if (!dims) return 0;
+    if (check_bwd_built(dims, chunk_size) != GDN2_OK) return 0;
     const bool packed = dims->num_seqs > 0 && dims->batch == 1;
     if (check_chunk_dims(dims, chunk_size, false) != GDN2_OK &&
         check_chunk_dims(dims, chunk_size, packed) != GDN2_OK)
@@ -223,6 +236,8 @@ gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            void *workspace, size_t workspace_bytes, void *stream) {
     const bool packed = cu_seqlens != nullptr;
     gdn2_status st = check_chunk_dims(dims, chunk_size, packed);
+    if (st != GDN2_OK) return st;
+    st = check_bwd_built(dims, chunk_size);
     if (st != GDN2_OK) return st;
     const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
     const int N = packed ? dims->num_seqs : dims->batch;

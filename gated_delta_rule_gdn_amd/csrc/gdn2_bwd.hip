@@ -808,9 +808,9 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
                   "the per-record scratch matches chunk_bwd_workspace_bytes");
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
-    const int64_t nrec = chunk_upper_bound(a.batch, a.seqlen, a.num_seqs, packed) * a.h_v;
+    const int64_t nrec = chunk_upper_bound(kChunk, a.batch, a.seqlen, a.num_seqs, packed) * a.h_v;
     char *base = a.workspace;
-    const size_t fwd_ws = chunk_workspace_bytes(a.batch, a.seqlen, a.num_seqs, a.h_v, DK, DV,
+    const size_t fwd_ws = chunk_workspace_bytes(kChunk, a.batch, a.seqlen, a.num_seqs, a.h_v, DK, DV,
                                                 a.bf16, packed);
     float *ck = reinterpret_cast<float *>(base + fwd_ws);
     char *o_scratch = base + (fwd_ws + static_cast<size_t>(nrec) * DK * DV * 4 + 255) / 256 * 256;
@@ -890,12 +890,12 @@ hipError_t launch_bwd_dt(const BwdArgs &a, hipStream_t st) {
 
 size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
                                  bool bf16, bool packed) {
-    const int64_t nrec = chunk_upper_bound(batch, seqlen, num_seqs, packed) * h_v;
+    const int64_t nrec = chunk_upper_bound(kChunk, batch, seqlen, num_seqs, packed) * h_v;
     // (the floats of BLay<d_k, d_v>)
     const size_t per = 4 * (14 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * d_v +
                             2 * static_cast<size_t>(d_k) * d_v + 7 * static_cast<size_t>(C) * C + 2 * d_k);
     const size_t o_bytes = (static_cast<size_t>(batch) * seqlen * h_v * d_v * (bf16 ? 2 : 4) + 255) / 256 * 256;
-    const size_t head = (chunk_workspace_bytes(batch, seqlen, num_seqs, h_v, d_k, d_v, bf16, packed) +
+    const size_t head = (chunk_workspace_bytes(kChunk, batch, seqlen, num_seqs, h_v, d_k, d_v, bf16, packed) +
                          static_cast<size_t>(nrec) * d_k * d_v * 4 + 255) / 256 * 256;
     return head + o_bytes + static_cast<size_t>(nrec) * per;
 }

@@ -1,0 +1,211 @@
+// gdn2_chunk.h -- definitions shared by the kernels of the chunked forward: the per-chunk
+// record that the prep kernel writes and the state passes read, the launch parameters, and
+// small device helpers.
+#pragma once
+#include "gdn2_common.h"
+#include "gdn2_internal.h"
+#include "gdn2_mfma.h"
+
+namespace gdn2 {
+
+template <bool BF> struct Op;
+template <> struct Op<true> {     // bf16 operands, K = 32 per fragment block
+    using type = bf16_t;
+    using UTile = u32x2;              // one lane's part of a D-layout tile of U~ (4 x bf16)
+    static constexpr int KT = 32, EPL = 8, E = 2;
+};
+template <> struct Op<false> {    // fp32 operands, K = 16 per fragment block
+    using type = float;
+    using UTile = f32x4;
+    static constexpr int KT = 16, EPL = 4, E = 4;
+};
+
+// Per (chunk, value head) workspace record of a chunk of C tokens. A-operand matrices are
+// stored as 1 KB fragment blocks (64 lanes x 16 B) in (row tile, k tile) order, in perm
+// order (gdn2_mfma.h):
+//   Wn  = -W~          [C][DK]   (state pass: U = U~ + Wn S)
+//   Qg  = gamma . q     [C][DK]   (state pass: O = Qg S + M U)
+//   KgT = ((gamma_C / gamma) . k)^T  [DK][C]  (state pass: S = gamma_C S + KgT U)
+//   M                   [C][C]    (blocks above the diagonal are never read, except the
+//                                  upper half of a k tile that straddles the diagonal,
+//                                  which holds zeros)
+// U~ is stored as 16x16 output tiles (D layout), column tile major (tile ct * C/16 + rt);
+// gamma_C as fp32 [DK].
+template <int C, int DK, int DV, bool BF>
+struct Rec {
+    static constexpr size_t E = Op<BF>::E;
+    static constexpr size_t Wn = 0;
+    static constexpr size_t Qg = Wn + static_cast<size_t>(C) * DK * E;
+    static constexpr size_t KgT = Qg + static_cast<size_t>(C) * DK * E;
+    static constexpr size_t M = KgT + static_cast<size_t>(DK) * C * E;
+    static constexpr size_t Ut = M + static_cast<size_t>(C) * C * E;
+    static constexpr size_t gC = Ut + static_cast<size_t>(C) * DV * E;
+    static constexpr size_t bytes = (gC + DK * 4 + 255) / 256 * 256;
+    static constexpr int NKT_DK = DK / Op<BF>::KT;     // k tiles over d_k
+    static constexpr int NKT_C = C / Op<BF>::KT;       // k tiles over the chunk
+    static constexpr size_t UT_TILE = 64 * 4 * E;      // one D-layout tile
+};
+
+struct ChunkParams {
+    const void *q, *k, *v, *log_alpha, *b, *w;
+    const float *S0;
+    const int32_t *cu;
+    const int32_t *map;
+    void *o;
+    float *S_T;
+    float *S_ck;         // state entering every chunk [chunk][h_v][DK][DV], or NULL
+    char *rec;           // first per-(chunk, head) record
+    // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of
+    // every pair are split into nseg segments of seg_len chunks that run concurrently.
+    float *seg_S;        // [pair][2][DK][DV]       states entering segments 0 (copy of S0) and 1
+    float *seg_P;        // [pair][nseg-2] SegPFrag transition of segments 1 .. nseg-2
+    float *seg_R;        // [pair][nseg-2][DK][DV]  end state of segments 1 .. nseg-2 from 0
+    int seqlen, num_seqs, h_k, h_v, group, nc_dense, num_pairs, nslices;
+    int nseg, seg_len;
+    int qkn;             // nonzero: q and k rows are L2-normalised in K1
+    float l2eps;
+    int gmode;           // GateMode: how b (and w, log_alpha) carry the gates
+};
+
+// Locates chunk `chunk` of the batch: sequence n, its chunk index j, and token range.
+__device__ __forceinline__ bool locate_chunk(const ChunkParams &p, int chunk, int &n, int &j,
+                                             int64_t &start, int64_t &end) {
+    if (p.cu == nullptr) {
+        n = chunk / p.nc_dense;
+        j = chunk - n * p.nc_dense;
+        start = static_cast<int64_t>(n) * p.seqlen;
+        end = start + p.seqlen;
+        return true;
+    }
+    if (chunk >= p.map[p.num_seqs]) return false;
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {                       // largest n with map[n] <= chunk
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.map[mid] <= chunk) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    j = chunk - p.map[n];
+    start = p.cu[n];
+    end = p.cu[n + 1];
+    return true;
+}
+
+template <bool BF>
+__device__ __forceinline__ u32x4 pack16(const float *v) {
+    u32x4 r;
+    if constexpr (BF) {
+        r.x = pack_bf16x2(v[0], v[1]);
+        r.y = pack_bf16x2(v[2], v[3]);
+        r.z = pack_bf16x2(v[4], v[5]);
+        r.w = pack_bf16x2(v[6], v[7]);
+    } else {
+        r.x = __float_as_uint(v[0]);
+        r.y = __float_as_uint(v[1]);
+        r.z = __float_as_uint(v[2]);
+        r.w = __float_as_uint(v[3]);
+    }
+    return r;
+}
+
+template <bool BF>
+__device__ __forceinline__ void unpack16(u32x4 v, float *out) {
+    if constexpr (BF) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            out[2 * q] = bf16_lo(v[q]);
+            out[2 * q + 1] = bf16_hi(v[q]);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = __uint_as_float(v[q]);
+    }
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group, lane j names an 8-byte
+// chunk; lane i receives element i % 4 of the chunks of lanes 4a + i / 4, a = 0..3. With
+// lane j pointing at row k0 + j / 4, columns c0 + 4 (j % 4) .. + 3 of a row-major 16-bit
+// tile, lane i therefore receives rows k0 .. k0 + 3 of column c0 + i: four consecutive k of
+// a matrix-core operand, read from a tile stored with k as its row index.
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr4(const void *p) {
+    const s16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4v *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+// 2^x on the transcendental unit (the prep kernel keeps its cumulative decay in log2 units)
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Record stores: non-temporal when the records cannot stay in the last-level cache until
+// the state pass reads them.
+template <bool NT, typename V>
+__device__ __forceinline__ void st_rec(V *p, V v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// s_waitcnt with lgkmcnt(0) only
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier without a memory fence (so it never waits for outstanding loads). The
+// empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// Barrier for data exchanged through LDS only: this wave's LDS accesses complete, then the
+// workgroup meets. Unlike __syncthreads() it does not wait for outstanding global loads and
+// stores (on gfx9 a workgroup fence waits for every vector memory operation in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS (lds_dst: the wave's base address,
+// lane l writes lds_dst + 16 l)
+__device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt with vmcnt(N) only: at most N vector memory loads of this wave outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// An int in LDS, accessed with plain LDS instructions (no generic-pointer path).
+typedef __attribute__((address_space(3))) volatile int lds_flag;
+
+// Spin (bounded) until an LDS flag written by another wave of the workgroup reaches `want`.
+// The writer is always able to progress, so the bound is never reached in a correct run; it
+// guarantees that every wave exits. Returns false if the bound was reached: the caller then
+// writes NaN in place of the outputs that depended on the flag, so a missed publication
+// shows up in the results instead of passing stale operands on silently.
+__device__ __forceinline__ bool wait_flag(lds_flag *flag, int want) {
+    bool ok = false;
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (*flag >= want) {
+            ok = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+    return ok;
+}
+
+// The intra-chunk pass (gdn2_prep.hip): one record per (chunk, value head) item, for the
+// chunk sizes and dims it is built for.
+hipError_t launch_prep(const ChunkParams &p, int chunk, int dk, int dv, bool bf16, int64_t items,
+                       hipStream_t st);
+// The panel state pass (gdn2_state.hip) over the records of launch_prep.
+hipError_t launch_panel_state(const ChunkParams &p, int chunk, int dk, int dv, bool bf16,
+                              hipStream_t st);
+
+}  // namespace gdn2

@@ -35,120 +35,23 @@
 // true product).
 // Padding rows of a partial chunk are identity tokens (k = q = b = 0, w.v = 0,
 // log alpha = 0), which leave the state unchanged.
-#include "gdn2_common.h"
-#include "gdn2_internal.h"
-#include "gdn2_mfma.h"
+#include "gdn2_chunk.h"
 
 namespace gdn2 {
 
-template <bool BF> struct Op;
-template <> struct Op<true> {     // bf16 operands, K = 32 per fragment block
-    using type = bf16_t;
-    using UTile = u32x2;              // one lane's part of a D-layout tile of U~ (4 x bf16)
-    static constexpr int KT = 32, EPL = 8, E = 2;
-};
-template <> struct Op<false> {    // fp32 operands, K = 16 per fragment block
-    using type = float;
-    using UTile = f32x4;
-    static constexpr int KT = 16, EPL = 4, E = 4;
-};
-
-// Per (chunk, value head) workspace record. A-operand matrices are stored as 1 KB fragment
-// blocks (64 lanes x 16 B) in (row tile, k tile) order, in perm order (gdn2_mfma.h):
-//   Wn  = -W~          [C][DK]   (K2: U = U~ + Wn S)
-//   Qg  = gamma . q     [C][DK]   (K2: O = Qg S + M U)
-//   KgT = ((gamma_C / gamma) . k)^T  [DK][C]  (K2: S = gamma_C S + KgT U)
-//   M                   [C][C]
-// U~ is stored as output tiles (D layout), column tile major; gamma_C as fp32 [DK].
-template <int DK, int DV, bool BF>
-struct Rec {
-    static constexpr size_t E = Op<BF>::E;
-    static constexpr size_t Wn = 0;
-    static constexpr size_t Qg = Wn + kChunk * DK * E;
-    static constexpr size_t KgT = Qg + kChunk * DK * E;
-    static constexpr size_t M = KgT + DK * kChunk * E;
-    static constexpr size_t Ut = M + kChunk * kChunk * E;
-    static constexpr size_t gC = Ut + kChunk * DV * E;
-    static constexpr size_t bytes = (gC + DK * 4 + 255) / 256 * 256;
-    static constexpr int NKT_DK = DK / Op<BF>::KT;     // k tiles over d_k
-    static constexpr int NKT_C = kChunk / Op<BF>::KT;  // k tiles over the chunk
-    static constexpr size_t UT_TILE = 64 * 4 * E;       // one D-layout tile
-};
-
-struct ChunkParams {
-    const void *q, *k, *v, *log_alpha, *b, *w;
-    const float *S0;
-    const int32_t *cu;
-    const int32_t *map;
-    void *o;
-    float *S_T;
-    float *S_ck;         // state entering every chunk [chunk][h_v][DK][DV], or NULL
-    char *rec;           // first per-(chunk, head) record
-    // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of
-    // every pair are split into nseg segments of seg_len chunks that run concurrently.
-    float *seg_S;        // [pair][2][DK][DV]       states entering segments 0 (copy of S0) and 1
-    float *seg_P;        // [pair][nseg-2] SegPFrag transition of segments 1 .. nseg-2
-    float *seg_R;        // [pair][nseg-2][DK][DV]  end state of segments 1 .. nseg-2 from 0
-    int seqlen, num_seqs, h_k, h_v, group, nc_dense, num_pairs, nslices;
-    int nseg, seg_len;
-    int qkn;             // nonzero: q and k rows are L2-normalised in K1
-    float l2eps;
-    int gmode;           // GateMode: how b (and w, log_alpha) carry the gates
-};
-
-// Locates chunk `chunk` of the batch: sequence n, its chunk index j, and token range.
-__device__ __forceinline__ bool locate_chunk(const ChunkParams &p, int chunk, int &n, int &j,
-                                             int64_t &start, int64_t &end) {
-    if (p.cu == nullptr) {
-        n = chunk / p.nc_dense;
-        j = chunk - n * p.nc_dense;
-        start = static_cast<int64_t>(n) * p.seqlen;
-        end = start + p.seqlen;
-        return true;
-    }
-    if (chunk >= p.map[p.num_seqs]) return false;
-    int lo = 0, hi = p.num_seqs - 1;
-    while (lo < hi) {                       // largest n with map[n] <= chunk
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.map[mid] <= chunk) lo = mid; else hi = mid - 1;
-    }
-    n = lo;
-    j = chunk - p.map[n];
-    start = p.cu[n];
-    end = p.cu[n + 1];
-    return true;
-}
-
-// K0: chunk offsets of a packed batch, map[n] = sum_{m<n} ceil(len_m / C).
+// K0: chunk offsets of a packed batch, map[n] = sum_{m<n} ceil(len_m / chunk).
 __global__ void chunk_map_kernel(const int32_t *__restrict__ cu, int32_t *__restrict__ map,
-                                 int num_seqs) {
+                                 int num_seqs, int chunk) {
     if (threadIdx.x == 0 && blockIdx.x == 0) {
         int acc = 0;
         map[0] = 0;
         for (int n = 0; n < num_seqs; ++n) {
             int len = cu[n + 1] - cu[n];
             len = len < 0 ? 0 : len;
-            acc += (len + kChunk - 1) / kChunk;
+            acc += (len + chunk - 1) / chunk;
             map[n + 1] = acc;
         }
     }
-}
-
-template <bool BF>
-__device__ __forceinline__ u32x4 pack16(const float *v) {
-    u32x4 r;
-    if constexpr (BF) {
-        r.x = pack_bf16x2(v[0], v[1]);
-        r.y = pack_bf16x2(v[2], v[3]);
-        r.z = pack_bf16x2(v[4], v[5]);
-        r.w = pack_bf16x2(v[6], v[7]);
-    } else {
-        r.x = __float_as_uint(v[0]);
-        r.y = __float_as_uint(v[1]);
-        r.z = __float_as_uint(v[2]);
-        r.w = __float_as_uint(v[3]);
-    }
-    return r;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -179,29 +82,7 @@ __device__ __forceinline__ u32x4 pack16(const float *v) {
 //   3  W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) as tile GEMMs, one column tile of
 //      each per wave, written to the workspace in the orders K2 reads
 // ---------------------------------------------------------------------------------------
-constexpr float kLog2e = 1.4426950408889634f;
 
-// LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group, lane j names an 8-byte
-// chunk; lane i receives element i % 4 of the chunks of lanes 4a + i / 4, a = 0..3. With
-// lane j pointing at row k0 + j / 4, columns c0 + 4 (j % 4) .. + 3 of a row-major 16-bit
-// tile, lane i therefore receives rows k0 .. k0 + 3 of column c0 + i: four consecutive k of
-// a matrix-core operand, read from a tile stored with k as its row index.
-typedef short s16x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_tr4(const void *p) {
-    const s16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4v *)(p));
-    return __builtin_bit_cast(u32x2, r);
-}
-// 2^x on the transcendental unit (the prep kernel keeps its cumulative decay in log2 units)
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Record stores: non-temporal when the records cannot stay in the last-level cache until
-// the state pass reads them.
-template <bool NT, typename V>
-__device__ __forceinline__ void st_rec(V *p, V v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
 
 struct PrepLoc {
     int64_t t0;     // first token of the chunk
@@ -210,25 +91,12 @@ struct PrepLoc {
     size_t rec;     // record index
 };
 
-template <bool BF>
-__device__ __forceinline__ void unpack16(u32x4 v, float *out) {
-    if constexpr (BF) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            out[2 * q] = bf16_lo(v[q]);
-            out[2 * q + 1] = bf16_hi(v[q]);
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = __uint_as_float(v[q]);
-    }
-}
 
 // GM: the gate mode (GateMode), one instance per mode, so that no instance carries another
 // mode's selects (run-time selects around the prefetched loads measured 7 us slower).
 template <typename T, bool BF, int DK, int DV, bool NTR, int GM>
 __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
-    using R_ = Rec<DK, DV, BF>;
+    using R_ = Rec<kChunk, DK, DV, BF>;
     constexpr int C = kChunk, NT = 512, NW = NT / 64;
     constexpr int KT = Op<BF>::KT;            // k per matrix-core tile: 32 (bf16) / 16 (fp32)
     constexpr int KS = BF ? 8 : 4;            // consecutive k values a lane holds per tile
@@ -808,7 +676,7 @@ __global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
 // ---------------------------------------------------------------------------------------
 template <int DK, int DV, bool BF>
 struct StageLayout {
-    using R_ = Rec<DK, DV, BF>;
+    using R_ = Rec<kChunk, DK, DV, BF>;
     static constexpr size_t E_O = BF ? 2 : 4;                // bytes per o element
     static constexpr size_t SHARED = R_::Ut;                 // Wn, Qg, KgT, M
     static constexpr size_t GCB = DK * 4;                    // gamma_C
@@ -953,49 +821,6 @@ struct CarryLayout {
     static_assert(LDS <= 159 * 1024, "carry fits in LDS");
 };
 
-__device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, 0, 0);
-}
-
-// s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima)
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// s_waitcnt with vmcnt(N) only: at most N vector memory loads of this wave outstanding
-template <int N>
-__device__ __forceinline__ void wait_vmem_n() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
-}
-// s_waitcnt with lgkmcnt(0) only
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-// Workgroup barrier without a memory fence (so it never waits for outstanding loads). The
-// empty asm statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void raw_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// An int in LDS, accessed with plain LDS instructions (no generic-pointer path).
-typedef __attribute__((address_space(3))) volatile int lds_flag;
-
-// Spin (bounded) until an LDS flag written by another wave of the workgroup reaches `want`.
-// The writer is always able to progress, so the bound is never reached in a correct run; it
-// guarantees that every wave exits. Returns false if the bound was reached: the caller then
-// writes NaN in place of the outputs that depended on the flag, so a missed publication
-// shows up in the results instead of passing stale operands on silently.
-__device__ __forceinline__ bool wait_flag(lds_flag *flag, int want) {
-    bool ok = false;
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (*flag >= want) {
-            ok = true;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");
-    return ok;
-}
-
 // copy waves per state-pass workgroup: six, four with four slices (the register budget of
 // twelve waves)
 template <int NW> struct StateWaves {
@@ -1005,7 +830,7 @@ template <int NW> struct StateWaves {
 
 template <typename T, bool BF, int DK, int DV, int NW>
 __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(ChunkParams p) {
-    using R_ = Rec<DK, DV, BF>;
+    using R_ = Rec<kChunk, DK, DV, BF>;
     using SL = StageLayout<DK, DV, BF>;
     constexpr int C = kChunk, RT = DK / 16;
     constexpr int KT = Op<BF>::KT;
@@ -1347,7 +1172,7 @@ constexpr int kSegCopy = 4;    // copy waves per segment-pass workgroup
 
 template <int DK, int DV, bool BF>
 struct SegLayout {
-    using R_ = Rec<DK, DV, BF>;
+    using R_ = Rec<kChunk, DK, DV, BF>;
     static constexpr size_t OPB = static_cast<size_t>(kChunk) * DK * Op<BF>::E;   // Wn / KgT
     static constexpr size_t KG = OPB;                       // KgT offset in a stage
     static constexpr size_t GC = 2 * OPB;                   // gamma_C
@@ -1364,7 +1189,7 @@ struct SegLayout {
 
 template <typename T, bool BF, int DK, int DV>
 __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(ChunkParams p) {
-    using R_ = Rec<DK, DV, BF>;
+    using R_ = Rec<kChunk, DK, DV, BF>;
     using SG = SegLayout<DK, DV, BF>;
     constexpr int RT = DK / 16;
     constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
@@ -1538,9 +1363,10 @@ __global__ __launch_bounds__(64 * (kSegWaves + kSegCopy)) void chunk_seg_kernel(
 // ---------------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------------
-size_t chunk_record_bytes(int d_k, int d_v, bool bf16) {
+size_t chunk_record_bytes(int chunk, int d_k, int d_v, bool bf16) {
     const size_t E = bf16 ? 2 : 4;
-    const size_t gc = E * (3 * kChunk * d_k + kChunk * kChunk + kChunk * d_v);
+    const size_t C = static_cast<size_t>(chunk);
+    const size_t gc = E * (3 * C * d_k + C * C + C * d_v);
     return (gc + static_cast<size_t>(d_k) * 4 + 255) / 256 * 256;
 }
 
@@ -1579,8 +1405,8 @@ __global__ __launch_bounds__(256) void gated_norm_kernel(T *__restrict__ o,
     *reinterpret_cast<u32x4 *>(o + off) = pack16<sizeof(T) == 2>(x);
 }
 
-int64_t chunk_upper_bound(int batch, int seqlen, int num_seqs, bool packed) {
-    const int64_t per = (static_cast<int64_t>(seqlen) + kChunk - 1) / kChunk;
+int64_t chunk_upper_bound(int chunk, int batch, int seqlen, int num_seqs, bool packed) {
+    const int64_t per = (static_cast<int64_t>(seqlen) + chunk - 1) / chunk;
     return packed ? per + num_seqs : per * batch;
 }
 
@@ -1638,23 +1464,30 @@ static void seg_area(const SegPlan &sp, int64_t pairs, int d_k, int d_v, size_t 
     *total = off[2] + align256(pairs * nPR * d_k * d_v * 4);
 }
 
-size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
-                             bool bf16, bool packed) {
-    const int64_t nc = (static_cast<int64_t>(seqlen) + kChunk - 1) / kChunk;
+// The 64-token path with the segmented state pass: bf16 records at any supported head dims,
+// fp32 records at d_k = d_v = 64. Other chunk sizes and fp32 records at d = 128 take the
+// generic path (prep kernel of gdn2_prep.hip, panel state pass of gdn2_state.hip).
+static bool tuned_path(int chunk, int d_k, int d_v, bool bf16) {
+    return chunk == kChunk && (bf16 || (d_k == 64 && d_v == 64));
+}
+
+size_t chunk_workspace_bytes(int chunk, int batch, int seqlen, int num_seqs, int h_v, int d_k,
+                             int d_v, bool bf16, bool packed) {
+    const int64_t nc = (static_cast<int64_t>(seqlen) + chunk - 1) / chunk;
     const int64_t pairs = static_cast<int64_t>(packed ? num_seqs : batch) * h_v;
-    const SegPlan sp = chunk_seg_plan(packed, pairs, static_cast<int>(nc), d_v, bf16);
-    size_t off[3], segb;
-    seg_area(sp, pairs, d_k, d_v, off, &segb);
+    size_t segb = 0;
+    if (tuned_path(chunk, d_k, d_v, bf16)) {
+        const SegPlan sp = chunk_seg_plan(packed, pairs, static_cast<int>(nc), d_v, bf16);
+        size_t off[3];
+        seg_area(sp, pairs, d_k, d_v, off, &segb);
+    }
     return chunk_map_bytes(num_seqs, packed) +
-           static_cast<size_t>(chunk_upper_bound(batch, seqlen, num_seqs, packed)) * h_v *
-               chunk_record_bytes(d_k, d_v, bf16) +
+           static_cast<size_t>(chunk_upper_bound(chunk, batch, seqlen, num_seqs, packed)) * h_v *
+               chunk_record_bytes(chunk, d_k, d_v, bf16) +
            segb;
 }
 
-bool chunk_dims_built(int d_k, int d_v, bool bf16) {
-    if (bf16) return (d_k == 64 || d_k == 128) && (d_v == 64 || d_v == 128);
-    return d_k == 64 && d_v == 64;
-}
+bool chunk_size_built(int chunk) { return chunk == 32 || chunk == 64 || chunk == 128; }
 
 // Compute units of the current device (the persistent prep kernel runs one workgroup per
 // CU). Queried once per device and cached.
@@ -1689,7 +1522,7 @@ static hipError_t launch_state(ChunkParams p, int64_t units, hipStream_t st) {
 
 template <typename T, bool BF, int DK, int DV>
 static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
-    static_assert(Rec<DK, DV, BF>::bytes > 0, "");
+    static_assert(Rec<kChunk, DK, DV, BF>::bytes > 0, "");
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
     ChunkParams p;
@@ -1705,27 +1538,27 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.qkn = a.fu.qk_norm ? 1 : 0;
     p.l2eps = a.fu.l2eps;
     p.gmode = a.fu.gmode;
-    const int64_t nrec = chunk_upper_bound(a.batch, a.seqlen, N, packed);
+    const int64_t nrec = chunk_upper_bound(kChunk, a.batch, a.seqlen, N, packed);
     const SegPlan sp = chunk_seg_plan(packed, p.num_pairs, p.nc_dense, DV, BF);
     p.nseg = sp.nseg;
     p.seg_len = sp.seg_len;
     {
         size_t off[3], segb;
         seg_area(sp, p.num_pairs, DK, DV, off, &segb);
-        char *seg_base = p.rec + static_cast<size_t>(nrec) * a.h_v * Rec<DK, DV, BF>::bytes;
+        char *seg_base = p.rec + static_cast<size_t>(nrec) * a.h_v * Rec<kChunk, DK, DV, BF>::bytes;
         p.seg_S = reinterpret_cast<float *>(seg_base + off[0]);
         p.seg_P = reinterpret_cast<float *>(seg_base + off[1]);
         p.seg_R = reinterpret_cast<float *>(seg_base + off[2]);
     }
     if (packed) {
         hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(64), 0, st, a.cu_seqlens,
-                           reinterpret_cast<int32_t *>(a.workspace), N);
+                           reinterpret_cast<int32_t *>(a.workspace), N, kChunk);
     }
     const int64_t nchunks = nrec;
     if (nchunks > 0) {
         const int64_t items = nchunks * a.h_v;
         const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
-        const bool ntr = static_cast<size_t>(items) * Rec<DK, DV, BF>::bytes > kStreamRecordBytes;
+        const bool ntr = static_cast<size_t>(items) * Rec<kChunk, DK, DV, BF>::bytes > kStreamRecordBytes;
         // (the gate-mode instances keep the default stores at every size: fewer instances)
         const dim3 g3(grid), b3(512);
         switch (p.gmode) {
@@ -1787,7 +1620,63 @@ static hipError_t launch_chunk_dt(const ChunkArgs &a, hipStream_t st) {
     }
 }
 
+// Generic path: any built chunk size, both dtypes, all head dims; the state pass walks each
+// chunk in row panels and runs every (sequence, head) from its start (no segments).
+static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
+    const bool packed = a.cu_seqlens != nullptr;
+    const int N = packed ? a.num_seqs : a.batch;
+    const int C = a.chunk;
+    ChunkParams p{};
+    p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.b = a.b; p.w = a.w;
+    p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks;
+    const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
+    p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
+    p.rec = a.workspace + mapb;
+    p.seqlen = a.seqlen; p.num_seqs = N; p.h_k = a.h_k; p.h_v = a.h_v;
+    p.group = a.h_v / a.h_k;
+    p.nc_dense = (a.seqlen + C - 1) / C;
+    p.num_pairs = N * a.h_v;
+    p.nseg = 1;
+    p.seg_len = p.nc_dense;
+    p.qkn = a.fu.qk_norm ? 1 : 0;
+    p.l2eps = a.fu.l2eps;
+    p.gmode = a.fu.gmode;
+    if (packed)
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(64), 0, st, a.cu_seqlens,
+                           reinterpret_cast<int32_t *>(a.workspace), N, C);
+    const int64_t nrec = chunk_upper_bound(C, a.batch, a.seqlen, N, packed);
+    hipError_t e = launch_prep(p, C, a.d_k, a.d_v, a.bf16, nrec * a.h_v, st);
+    if (e != hipSuccess) return e;
+    e = launch_panel_state(p, C, a.d_k, a.d_v, a.bf16, st);
+    if (e != hipSuccess || !a.fu.gate) return e;
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.seqlen * a.h_v;
+    if (rows <= 0) return hipSuccess;
+    if (a.bf16) {
+        if (a.d_v == 128) {
+            constexpr int RPB = 256 / (128 / 8);
+            hipLaunchKernelGGL((gated_norm_kernel<bf16_t, 128>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                               static_cast<bf16_t *>(a.o), static_cast<const bf16_t *>(a.fu.gate), a.fu.nw, a.fu.neps, rows);
+        } else {
+            constexpr int RPB = 256 / (64 / 8);
+            hipLaunchKernelGGL((gated_norm_kernel<bf16_t, 64>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                               static_cast<bf16_t *>(a.o), static_cast<const bf16_t *>(a.fu.gate), a.fu.nw, a.fu.neps, rows);
+        }
+    } else {
+        if (a.d_v == 128) {
+            constexpr int RPB = 256 / (128 / 4);
+            hipLaunchKernelGGL((gated_norm_kernel<float, 128>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                               static_cast<float *>(a.o), static_cast<const float *>(a.fu.gate), a.fu.nw, a.fu.neps, rows);
+        } else {
+            constexpr int RPB = 256 / (64 / 4);
+            hipLaunchKernelGGL((gated_norm_kernel<float, 64>), dim3((rows + RPB - 1) / RPB), dim3(256), 0, st,
+                               static_cast<float *>(a.o), static_cast<const float *>(a.fu.gate), a.fu.nw, a.fu.neps, rows);
+        }
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st) {
+    if (!tuned_path(a.chunk, a.d_k, a.d_v, a.bf16)) return launch_chunk_generic(a, st);
     return a.bf16 ? launch_chunk_dt<bf16_t, true>(a, st) : launch_chunk_dt<float, false>(a, st);
 }
 

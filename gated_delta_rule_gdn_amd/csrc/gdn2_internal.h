@@ -47,6 +47,7 @@ struct ChunkArgs {
     float *S_T;
     char *workspace;
     int batch, seqlen, num_seqs, h_k, h_v, d_k, d_v;
+    int chunk = kChunk;          // chunk size: 32, 64 or 128
     bool bf16;
     Fusion fu;
 };
@@ -54,12 +55,12 @@ struct ChunkArgs {
 // Workspace layout of the chunked forward (all offsets 256-byte aligned):
 //   [chunk map: int32[num_seqs + 1], packed batches only]
 //   [per (chunk, value head) record of chunk_record_bytes()]
-size_t chunk_record_bytes(int d_k, int d_v, bool bf16);
-int64_t chunk_upper_bound(int batch, int seqlen, int num_seqs, bool packed);
+size_t chunk_record_bytes(int chunk, int d_k, int d_v, bool bf16);
+int64_t chunk_upper_bound(int chunk, int batch, int seqlen, int num_seqs, bool packed);
 size_t chunk_map_bytes(int num_seqs, bool packed);
-size_t chunk_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
-                             bool bf16, bool packed);
-bool chunk_dims_built(int d_k, int d_v, bool bf16);
+size_t chunk_workspace_bytes(int chunk, int batch, int seqlen, int num_seqs, int h_v, int d_k,
+                             int d_v, bool bf16, bool packed);
+bool chunk_size_built(int chunk);
 
 // Chunked backward (gdn2_chunk_bwd). Workspace: the forward's, then the state entering every
 // chunk (fp32), a scratch o, then a per-record fp32 scratch.

@@ -1,0 +1,615 @@
+// gdn2_prep.hip -- the intra-chunk pass of the chunked WY forward (the prep kernel) on gfx950.
+//
+// Method: burn-gdn2 0.1.5 docs page, section "Architecture" (the recurrence and its "Chunk
+// WY" training path). For a chunk of C tokens (rows r, i; g_r = sum_{i<=r} log alpha_i per
+// key channel, gamma = exp(g)) the state pass needs, per (chunk, value head):
+//   A  = strict_lower(K^ K-bar^T)  with A[r,i] = sum_c b_r k_r k_i exp(g_r - g_i)
+//   M  = lower_incl(Q^ K-bar^T)    with M[r,i] = sum_c q_r k_i exp(g_r - g_i)
+//   T  = (I + A)^{-1}
+//   Wn = -T (gamma . b . k),  U~ = T (w . v),  Qg = gamma . q,
+//   KgT = ((gamma_C / gamma) . k)^T,  gamma_C
+// (the record layout of gdn2_chunk.h).
+//
+// One 256-thread workgroup per record, small enough in LDS that two records run on a CU
+// at once for C <= 64 (the rounds of one hide the latency of the other's). The key
+// channels are processed in rounds of one matrix-core k tile (32 bf16 / 16 fp32 channels):
+//   scan    every lane holds one token of a 16-token sub-chunk and 8 (bf16) or 4 (fp32)
+//           channels; the cumulative log decay inside each sub-chunk is an in-row scan of the
+//           16 lanes (DPP row shifts), in log2 units; sub-chunk sums go through LDS
+//   round   K^ = b k 2^(c_r - c_mid), Q^ = q 2^(c_r - c_mid), K-bar = k 2^(c_mid - c_r) with
+//           c the in-sub-chunk cumsum and c_mid its value at the sub-chunk's middle token (no
+//           factor spans more than 8 tokens of decay), written to LDS tiles; A and M
+//           accumulate on the matrix cores in registers over the rounds, block pair by block
+//           pair, the off-diagonal pairs with the per-channel factor 2^(g_mid_R - g_mid_I) <= 1
+//   solve   T = (I + A)^{-1} on 16x16 blocks stored as a packed lower triangle: diagonal
+//           blocks by forward substitution, the rest level by level on fp32 matrix cores
+//   WY      W~^T = X^T T^T (X = gamma . b . k, kept in registers from the rounds) and
+//           U~ = T (w . v), one channel block per round, written in the record's order.
+// Padding rows of a partial chunk are identity tokens (k = q = b = 0, w.v = 0,
+// log alpha = 0).
+#include "gdn2_chunk.h"
+
+namespace gdn2 {
+
+// The (R, I) block pairs of the lower triangle (R >= I) of NS 16-token sub-chunks, numbered
+// off-diagonal pairs first ((1,0), (2,0), (2,1), (3,0), ...), then the diagonal; wave w
+// takes pairs w, w + 4, ...
+__device__ __forceinline__ void pair_of(int idx, int ns, int &R, int &I) {
+    const int noff = ns * (ns - 1) / 2;
+    if (idx >= noff) {
+        R = I = idx - noff;
+        return;
+    }
+    int r = 1;
+    while (r * (r + 1) / 2 <= idx) ++r;
+    R = r;
+    I = idx - r * (r - 1) / 2;
+}
+
+// Index of block (R, I), R >= I, in the packed lower triangle.
+__host__ __device__ constexpr int tri_blk(int R, int I) { return R * (R + 1) / 2 + I; }
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes outside the row read 0).
+__device__ __forceinline__ float row_scan16(float x) {
+    int v = __builtin_bit_cast(int, x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true));
+    v = __builtin_bit_cast(int, x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true));
+    v = __builtin_bit_cast(int, x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true));
+    v = __builtin_bit_cast(int, x);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true));
+    return x;
+}
+
+template <typename T, bool BF, int C, int DK, int DV, int GM>
+__global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParams p) {
+    using R_ = Rec<C, DK, DV, BF>;
+    constexpr int NS = C / 16;                 // 16-token sub-chunks
+    constexpr int VEC = 16 / sizeof(T);        // elements per 16-byte vector
+    constexpr int CB = 4 * VEC;                // channels per round: one k tile
+    constexpr int KT = Op<BF>::KT;
+    static_assert(KT == CB, "a round is one matrix-core k tile");
+    constexpr int NJ = DK / CB, NJV = DV / CB;
+    constexpr int NSW = (NS + 3) / 4;          // sub-chunks per wave
+    constexpr int NPAIR = NS * (NS + 1) / 2, NOFF = NS * (NS - 1) / 2;
+    constexpr int PPW = (NPAIR + 3) / 4;       // block pairs per wave (at most)
+    constexpr int SB = CB + VEC;               // tile row stride (elements), 16 B of padding
+    constexpr int TILE = C * SB;
+    constexpr bool DBUF = C <= 64;             // double-buffered round tiles
+    constexpr int NBUF = DBUF ? 2 : 1;
+    constexpr int BSTR = 20, BS = 16 * BSTR;   // fp32 16x16 block: row stride, size (floats)
+    constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
+    constexpr int CT = CB / 16;                // 16-channel tiles per round
+    constexpr int STB = C + 8;                 // row stride of the bf16 copy of T
+    constexpr bool b_scalar = GM == GATES_KDA || GM == GATES_GDN;
+    constexpr bool la_scalar = GM == GATES_GDN;
+    constexpr bool fg2 = GM == GATES_FG2 || GM == GATES_FG2_PLUS;
+    static_assert(NBUF * 3 * TILE >= 2 * TILE, "two X / w.v tiles fit in the round tiles");
+    static_assert(!BF || C * STB * 2 <= NPAIR * BS * 4, "bf16 T fits over A");
+
+    __shared__ float s_tot[NS * DK];           // sum of the log2 decay over each sub-chunk
+    __shared__ float s_cmid[NS * DK];          // in-sub-chunk cumsum at its middle token
+    __shared__ float s_fkg[NS * DK];           // 2^(g_C - g_mid_R)
+    __shared__ float s_foff[(NOFF > 0 ? NOFF : 1) * DK];   // 2^(g_mid_R - g_mid_I), R > I
+    __shared__ __attribute__((aligned(16))) T s_tile[NBUF * 3 * TILE];
+    __shared__ __attribute__((aligned(16))) float s_A[NPAIR * BS];
+    __shared__ __attribute__((aligned(16))) float s_T[NPAIR * BS];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 15, lg = lane >> 4;   // matrix-core lane roles (= t, gi below)
+    const int t = li, gi = lg;                  // elementwise roles: token in sub-chunk, group
+
+    const int item = blockIdx.x;
+    const int chunk = item / p.h_v, h = item - chunk * p.h_v, hk = h / p.group;
+    int n, jc;
+    int64_t start, end;
+    if (!locate_chunk(p, chunk, n, jc, start, end)) return;      // uniform: past the last chunk
+    const int64_t t0 = start + static_cast<int64_t>(jc) * C;
+    const int L = static_cast<int>(min<int64_t>(C, end - t0));
+    char *rec = p.rec + static_cast<size_t>(item) * R_::bytes;
+
+    const T *kp = static_cast<const T *>(p.k), *qp = static_cast<const T *>(p.q);
+    const T *bp = static_cast<const T *>(p.b), *lap = static_cast<const T *>(p.log_alpha);
+    const T *vp = static_cast<const T *>(p.v), *wp = static_cast<const T *>(p.w);
+
+    // rows of this lane: token 16 R_s + t of sub-chunk R_s = wave + 4 s
+    auto subR = [&](int s) { return wave + 4 * s; };
+    auto row_ok = [&](int s) { return subR(s) < NS && 16 * subR(s) + t < L; };
+    auto tok = [&](int s) { return t0 + 16 * subR(s) + t; };
+    auto bcast = [](const T *x) {      // a 16-byte vector of VEC copies of one element
+        uint32_t u;
+        if constexpr (sizeof(T) == 4) u = __float_as_uint(io<T>::ld(x));
+        else u = static_cast<uint32_t>(x->bits) * 0x10001u;
+        return u32x4{u, u, u, u};
+    };
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    // ---- k, q, b of a round (channels CB j + VEC gi ..), prefetched one round ahead ----
+    u32x4 rk[2][NSW], rq[2][NSW], rb[2][NSW];
+    auto load_round = [&](int j, int slot) {
+#pragma unroll
+        for (int s = 0; s < NSW; ++s) {
+            rk[slot][s] = zero4;
+            rq[slot][s] = zero4;
+            rb[slot][s] = zero4;
+            if (row_ok(s)) {
+                const size_t okq = (static_cast<size_t>(tok(s)) * p.h_k + hk) * DK + CB * j + VEC * gi;
+                rk[slot][s] = *reinterpret_cast<const u32x4 *>(kp + okq);
+                rq[slot][s] = *reinterpret_cast<const u32x4 *>(qp + okq);
+                if constexpr (b_scalar)
+                    rb[slot][s] = bcast(bp + static_cast<size_t>(tok(s)) * p.h_v + h);
+                else
+                    rb[slot][s] = *reinterpret_cast<const u32x4 *>(
+                        bp + (static_cast<size_t>(tok(s)) * p.h_v + h) * DK + CB * j + VEC * gi);
+            }
+        }
+    };
+    load_round(0, 0);
+
+    // ---- scan: in-sub-chunk cumulative log2 decay of every round's channels ----
+    float cs[NSW][NJ][VEC];
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) {
+        if (subR(s) >= NS) continue;               // uniform over the wave
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            u32x4 raw = zero4;
+            if (row_ok(s)) {
+                if constexpr (la_scalar) raw = bcast(lap + static_cast<size_t>(tok(s)) * p.h_v + h);
+                else raw = *reinterpret_cast<const u32x4 *>(
+                         lap + (static_cast<size_t>(tok(s)) * p.h_v + h) * DK + CB * j + VEC * gi);
+            }
+            unpack16<BF>(raw, cs[s][j]);
+        }
+    }
+    // q/k L2-norm factors (a uniform branch): sums of squares over all d_k channels of the
+    // token, the VEC channels of each round in-lane, the four lane groups by butterflies
+    float fk[NSW], fq[NSW];
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) fk[s] = fq[s] = 1.f;
+    if (p.qkn) {
+#pragma unroll
+        for (int s = 0; s < NSW; ++s) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                u32x4 k4 = zero4, q4 = zero4;
+                if (row_ok(s)) {
+                    const size_t okq = (static_cast<size_t>(tok(s)) * p.h_k + hk) * DK + CB * j + VEC * gi;
+                    k4 = *reinterpret_cast<const u32x4 *>(kp + okq);
+                    q4 = *reinterpret_cast<const u32x4 *>(qp + okq);
+                }
+                float kk[VEC], qq[VEC];
+                unpack16<BF>(k4, kk);
+                unpack16<BF>(q4, qq);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    sk += kk[e] * kk[e];
+                    sq += qq[e] * qq[e];
+                }
+            }
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            fk[s] = rsqrtf(sk + p.l2eps);
+            fq[s] = rsqrtf(sq + p.l2eps);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) {
+        if (subR(s) >= NS) continue;
+        const int R = subR(s);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) cs[s][j][e] = row_scan16(cs[s][j][e] * kLog2e);
+            const int c0 = CB * j + VEC * gi;
+            if (t == 15) {
+#pragma unroll
+                for (int e = 0; e < VEC; e += 4)
+                    *reinterpret_cast<f32x4 *>(&s_tot[R * DK + c0 + e]) =
+                        f32x4{cs[s][j][e], cs[s][j][e + 1], cs[s][j][e + 2], cs[s][j][e + 3]};
+            }
+            if (t == 7) {
+#pragma unroll
+                for (int e = 0; e < VEC; e += 4)
+                    *reinterpret_cast<f32x4 *>(&s_cmid[R * DK + c0 + e]) =
+                        f32x4{cs[s][j][e], cs[s][j][e + 1], cs[s][j][e + 2], cs[s][j][e + 3]};
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- per-channel factors (one thread per channel) and gamma_C ----
+    for (int c = tid; c < DK; c += 256) {
+        float gmid[NS];
+        float run = 0.f;
+#pragma unroll
+        for (int R = 0; R < NS; ++R) {
+            gmid[R] = run + s_cmid[R * DK + c];
+            run += s_tot[R * DK + c];
+        }
+        reinterpret_cast<float *>(rec + R_::gC)[c] = exp2_hw(run);
+#pragma unroll
+        for (int R = 0; R < NS; ++R) s_fkg[R * DK + c] = exp2_hw(run - gmid[R]);
+#pragma unroll
+        for (int R = 1; R < NS; ++R)
+#pragma unroll
+            for (int I = 0; I < R; ++I)
+                s_foff[(R * (R - 1) / 2 + I) * DK + c] = exp2_hw(gmid[R] - gmid[I]);
+    }
+    // this lane's values relative to its sub-chunk's middle token: cs <- c_r - c_mid
+#pragma unroll
+    for (int s = 0; s < NSW; ++s) {
+        if (subR(s) >= NS) continue;
+        const int R = subR(s);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const f32x4 cm = *reinterpret_cast<const f32x4 *>(&s_cmid[R * DK + CB * j + VEC * gi + e]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cs[s][j][e + q] -= cm[q];
+            }
+    }
+    // 2^(g at the middle token of sub-chunk R) for this lane's channels of round j (the same
+    // sums in the same order as the per-channel factors above)
+    auto fmid_of = [&](int R, int j, float *out) {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            const int c = CB * j + VEC * gi + e;
+            f32x4 run = {0.f, 0.f, 0.f, 0.f};
+            for (int R2 = 0; R2 < R; ++R2) run += *reinterpret_cast<const f32x4 *>(&s_tot[R2 * DK + c]);
+            const f32x4 cm = *reinterpret_cast<const f32x4 *>(&s_cmid[R * DK + c]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) out[e + q] = exp2_hw(run[q] + cm[q]);
+        }
+    };
+
+    // ---- rounds over the key channels: operand tiles, A and M on the matrix cores ----
+    f32x4 accA[PPW], accM[PPW];
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi) accA[pi] = accM[pi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 X[NSW][NJ];                          // gamma . b . k of this lane, for the WY pass
+    char *qgrec = rec + R_::Qg;
+    u32x4 *kgrec = reinterpret_cast<u32x4 *>(rec + R_::KgT);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int slot = j & 1, buf = DBUF ? (j & 1) : 0;
+        if (j + 1 < NJ) load_round(j + 1, slot ^ 1);
+        T *tkh = s_tile + buf * 3 * TILE, *tqh = tkh + TILE, *tkb = tkh + 2 * TILE;
+        if constexpr (!DBUF) {
+            if (j > 0) lds_barrier();        // the previous round's products are done
+        }
+#pragma unroll
+        for (int s = 0; s < NSW; ++s) {
+            if (subR(s) >= NS) continue;
+            const int r = 16 * subR(s) + t;
+            float kk[VEC], qq[VEC], bb[VEC], kh[VEC], qh[VEC], kb[VEC], xx[VEC], qg[VEC], fm[VEC];
+            fmid_of(subR(s), j, fm);
+            unpack16<BF>(rk[slot][s], kk);
+            unpack16<BF>(rq[slot][s], qq);
+            unpack16<BF>(rb[slot][s], bb);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                kk[e] *= fk[s];
+                qq[e] *= fq[s];
+                if constexpr (fg2) {           // k <- sqrt(beta) k, b <- 1
+                    kk[e] *= sqrt_hw(bb[e]);
+                    bb[e] = 1.f;
+                }
+                const float d = cs[s][j][e];
+                const float ef = exp2_hw(d), ei = exp2_hw(-d);
+                kh[e] = bb[e] * kk[e] * ef;
+                qh[e] = qq[e] * ef;
+                kb[e] = kk[e] * ei;
+                xx[e] = kh[e] * fm[e];
+                qg[e] = qh[e] * fm[e];
+            }
+            const int col = VEC * gi;
+            *reinterpret_cast<u32x4 *>(&tkh[r * SB + col]) = pack16<BF>(kh);
+            *reinterpret_cast<u32x4 *>(&tqh[r * SB + col]) = pack16<BF>(qh);
+            *reinterpret_cast<u32x4 *>(&tkb[r * SB + col]) = pack16<BF>(kb);
+            X[s][j] = pack16<BF>(xx);
+            // gamma . q in the record's fragment order: row tile r / 16, k tile j
+            if constexpr (BF) {
+#pragma unroll
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    const int q4 = 8 * gi + 4 * h4, half = q4 >= 16 ? 1 : 0, lgq = (q4 & 15) >> 2;
+                    const size_t sl = ((static_cast<size_t>(r >> 4) * NKD + j) * 64 + 16 * lgq + (r & 15)) * 2 + half;
+                    reinterpret_cast<u32x2 *>(qgrec)[sl] =
+                        u32x2{pack_bf16x2(qg[4 * h4], qg[4 * h4 + 1]), pack_bf16x2(qg[4 * h4 + 2], qg[4 * h4 + 3])};
+                }
+            } else {
+                reinterpret_cast<f32x4 *>(qgrec)[((r >> 4) * NKD + j) * 64 + 16 * gi + (r & 15)] =
+                    f32x4{qg[0], qg[1], qg[2], qg[3]};
+            }
+        }
+        lds_barrier();                       // round j's tiles are written
+        // A^T and M^T of the block pairs (lane: A[16R + li][16I + 4 lg + ii])
+#pragma unroll
+        for (int pi = 0; pi < PPW; ++pi) {
+            const int idx = wave + 4 * pi;
+            if (idx >= NPAIR) break;
+            int R, I;
+            pair_of(idx, NS, R, I);
+            u32x4 kbv = *reinterpret_cast<const u32x4 *>(&tkb[(16 * I + li) * SB + VEC * lg]);
+            if (R != I) {
+                const float *f = &s_foff[(R * (R - 1) / 2 + I) * DK + CB * j + VEC * lg];
+                float x[VEC];
+                unpack16<BF>(kbv, x);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) x[e] *= f[e];
+                kbv = pack16<BF>(x);
+            }
+            const u32x4 khv = *reinterpret_cast<const u32x4 *>(&tkh[(16 * R + li) * SB + VEC * lg]);
+            const u32x4 qhv = *reinterpret_cast<const u32x4 *>(&tqh[(16 * R + li) * SB + VEC * lg]);
+            if constexpr (BF) {
+                accA[pi] = mma_k32(kbv, khv, accA[pi]);
+                accM[pi] = mma_k32(kbv, qhv, accM[pi]);
+            } else {
+                const f32x4 a = __builtin_bit_cast(f32x4, kbv);
+                accA[pi] = mma_k16_f32(a, __builtin_bit_cast(f32x4, khv), accA[pi]);
+                accM[pi] = mma_k16_f32(a, __builtin_bit_cast(f32x4, qhv), accM[pi]);
+            }
+        }
+        // KgT fragments of this round's channel tiles: (channel tile, token k tile) blocks
+        for (int f = wave; f < CT * NKC; f += 4) {
+            const int ctl = f / NKC, kt = f - ctl * NKC;
+            const int rt = CT * j + ctl;                 // channel tile of the record
+            const int ch = CB * j + 16 * ctl + li;       // this lane's channel
+            float vals[Op<BF>::EPL];
+            if constexpr (BF) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int k0 = kt * 32 + 16 * hh + 4 * lg;
+                    const u32x2 tv = lds_tr4(&tkb[(k0 + (li >> 2)) * SB + 16 * ctl + 4 * (li & 3)]);
+                    const float fkv = s_fkg[(2 * kt + hh) * DK + ch];
+                    vals[4 * hh + 0] = bf16_lo(tv.x) * fkv;
+                    vals[4 * hh + 1] = bf16_hi(tv.x) * fkv;
+                    vals[4 * hh + 2] = bf16_lo(tv.y) * fkv;
+                    vals[4 * hh + 3] = bf16_hi(tv.y) * fkv;
+                }
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int tk = kt * 16 + 4 * lg + jj;
+                    vals[jj] = io<T>::ld(&tkb[tk * SB + 16 * ctl + li]) * s_fkg[(tk >> 4) * DK + ch];
+                }
+            }
+            kgrec[(rt * NKC + kt) * 64 + lane] = pack16<BF>(vals);
+        }
+    }
+
+    // ---- w and v (issued now, consumed after the solve) ----
+    u32x4 rw[NSW][NJV], rv[NSW][NJV];
+#pragma unroll
+    for (int s = 0; s < NSW; ++s)
+#pragma unroll
+        for (int jv = 0; jv < NJV; ++jv) {
+            rw[s][jv] = zero4;
+            rv[s][jv] = zero4;
+            if (row_ok(s)) {
+                const size_t ov = (static_cast<size_t>(tok(s)) * p.h_v + h) * DV + CB * jv + VEC * gi;
+                rv[s][jv] = *reinterpret_cast<const u32x4 *>(vp + ov);
+                if constexpr (b_scalar) {
+                    rw[s][jv] = bcast(bp + static_cast<size_t>(tok(s)) * p.h_v + h);
+                } else if constexpr (GM == GATES_FG2) {
+                    // beta [.., d_k] indexes like w [.., d_v] (d_v = d_k)
+                    rw[s][jv] = *reinterpret_cast<const u32x4 *>(bp + ov);
+                } else {
+                    rw[s][jv] = *reinterpret_cast<const u32x4 *>(wp + ov);
+                }
+            }
+        }
+
+    // ---- A to LDS (blocks of the lower triangle), M to the record ----
+    char *mrec = rec + R_::M;
+#pragma unroll
+    for (int pi = 0; pi < PPW; ++pi) {
+        const int idx = wave + 4 * pi;
+        if (idx >= NPAIR) break;
+        int R, I;
+        pair_of(idx, NS, R, I);
+        const bool dg = R == I;
+        f32x4 a4, m4;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int il = 4 * lg + ii;
+            a4[ii] = (dg && il >= li) ? 0.f : accA[pi][ii];
+            m4[ii] = (dg && il > li) ? 0.f : accM[pi][ii];
+        }
+        *reinterpret_cast<f32x4 *>(&s_A[tri_blk(R, I) * BS + li * BSTR + 4 * lg]) = a4;
+        if constexpr (BF) {
+            reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)] = f4_to_b16(m4);
+            if (dg && !(R & 1) && R + 1 < NS)    // the upper half of a k tile on the diagonal
+                reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (R >> 1)) * 64 + lane) << 1) + 1] = u32x2{0u, 0u};
+        } else {
+            reinterpret_cast<f32x4 *>(mrec)[(R * NKC + I) * 64 + lane] = m4;
+        }
+    }
+    lds_barrier();
+
+    // ---- T = (I + A)^{-1}: diagonal blocks by forward substitution (one lane per column) ----
+    if (tid < 16 * NS) {
+        const int R = tid >> 4, jcol = tid & 15;
+        const float *Ab = &s_A[tri_blk(R, R) * BS];
+        float x[16], acc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            x[m] = m == jcol ? 1.f : (m > jcol ? -acc[m] : 0.f);
+#pragma unroll
+            for (int r = m + 1; r < 16; ++r) acc[r] += Ab[r * BSTR + m] * x[m];
+        }
+        float *Tb = &s_T[tri_blk(R, R) * BS];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Tb[r * BSTR + jcol] = x[r];
+    }
+    lds_barrier();
+    // off-diagonal blocks by levels d = R - I: T_RI = -T_RR sum_{I <= m < R} A_Rm T_mI
+#pragma unroll
+    for (int d = 1; d < NS; ++d) {
+        for (int b = wave; b < NS - d; b += 4) {
+            const int R = b + d, I = b;
+            f32x4 P = {0.f, 0.f, 0.f, 0.f};
+            for (int m = I; m < R; ++m) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&s_A[tri_blk(R, m) * BS + li * BSTR + 4 * lg]);
+                f32x4 bT;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) bT[s2] = s_T[tri_blk(m, I) * BS + (4 * lg + s2) * BSTR + li];
+                P = mma_k16_f32(a, bT, P);
+            }
+            const f32x4 tRR = *reinterpret_cast<const f32x4 *>(&s_T[tri_blk(R, R) * BS + li * BSTR + 4 * lg]);
+            const f32x4 Tn = mma_k16_f32(tRR, P, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) s_T[tri_blk(R, I) * BS + (4 * lg + ii) * BSTR + li] = -Tn[ii];
+        }
+        lds_barrier();
+    }
+    if constexpr (BF) {
+        // bf16 copy of T, row-major [C][STB], zero above the diagonal blocks, over A
+        bf16_t *s_Tb = reinterpret_cast<bf16_t *>(s_A);
+        for (int idx = tid; idx < C * C / 8; idx += 256) {
+            const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
+            const int R = r >> 4, I = c8 >> 4;
+            float t8[8];
+            if (I <= R) {
+                const float *src = &s_T[tri_blk(R, I) * BS + (r & 15) * BSTR + (c8 & 15)];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t8[e] = src[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t8[e] = 0.f;
+            }
+            *reinterpret_cast<u32x4 *>(&s_Tb[r * STB + c8]) = pack16<true>(t8);
+        }
+    }
+
+    // ---- W~^T = X^T T^T per channel round, U~ = T (w.v) per value round ----
+    // wave roles: channel tile ctl = wave % CT within the round, row tiles R = wave / CT + k
+    // (4 / CT); with CT = 2 the even and the odd row tiles carry equal k ranges
+    const int ctl = wave % CT, rg = wave / CT;
+    constexpr int RSTEP = 4 / CT;
+    const bf16_t *s_Tb = reinterpret_cast<const bf16_t *>(s_A);
+    char *wrec = rec + R_::Wn;
+#pragma unroll
+    for (int rnd = 0; rnd < NJ + NJV; ++rnd) {
+        const bool isW = rnd < NJ;
+        const int j = isW ? rnd : rnd - NJ;
+        T *xt = s_tile + (rnd & 1) * TILE;
+        // this lane's rows of X (W rounds) or of w.v (U rounds)
+#pragma unroll
+        for (int s = 0; s < NSW; ++s) {
+            if (subR(s) >= NS) continue;
+            const int r = 16 * subR(s) + t;
+            u32x4 v4;
+            if (isW) {
+                v4 = X[s][j < NJ ? j : 0];
+            } else {
+                float ww[VEC], vv[VEC], pr[VEC];
+                unpack16<BF>(rw[s][j < NJV ? j : 0], ww);
+                unpack16<BF>(rv[s][j < NJV ? j : 0], vv);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) pr[e] = (fg2 ? sqrt_hw(ww[e]) : ww[e]) * vv[e];
+                v4 = pack16<BF>(pr);
+            }
+            *reinterpret_cast<u32x4 *>(&xt[r * SB + VEC * gi]) = v4;
+        }
+        lds_barrier();                       // this round's tile (and, first time, T) is ready
+        const int ct = CT * j + ctl;           // channel (or value column) tile of the record
+        if constexpr (BF) {
+            u32x4 xb[NKC];                     // k = tokens 32 kt + 8 lg + 0..7 of column 16 ctl + li
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) {
+                const int k0 = kt * 32 + 8 * lg + (li >> 2);
+                const u32x2 lo = lds_tr4(&xt[k0 * SB + 16 * ctl + 4 * (li & 3)]);
+                const u32x2 hi = lds_tr4(&xt[(k0 + 4) * SB + 16 * ctl + 4 * (li & 3)]);
+                xb[kt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+            }
+            for (int R = rg; R < NS; R += RSTEP) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < NKC; ++kt) {
+                    if (kt * 32 > 16 * R + 15) break;
+                    const u32x4 tb = *reinterpret_cast<const u32x4 *>(&s_Tb[(16 * R + li) * STB + kt * 32 + 8 * lg]);
+                    acc = isW ? mma_k32(xb[kt], tb, acc) : mma_k32(tb, xb[kt], acc);
+                }
+                if (isW) {   // lane: W~[16R + li][16 ct + 4 lg + ii] -> -W~ fragments
+                    reinterpret_cast<u32x2 *>(wrec)[(((R * NKD + (ct >> 1)) * 64 + lane) << 1) + (ct & 1)] =
+                        f4_to_b16(-acc);
+                } else {     // lane: U~[16R + 4 lg + ii][16 ct + li], a D-layout tile
+                    reinterpret_cast<u32x2 *>(rec + R_::Ut + (static_cast<size_t>(ct) * NS + R) * R_::UT_TILE)[lane] =
+                        f4_to_b16(acc);
+                }
+            }
+        } else {
+            float xv[NKC][4];
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) xv[kt][s2] = io<T>::ld(&xt[(kt * 16 + 4 * lg + s2) * SB + 16 * ctl + li]);
+            for (int R = rg; R < NS; R += RSTEP) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int kt = 0; kt <= R; ++kt) {
+                    const f32x4 tv = *reinterpret_cast<const f32x4 *>(&s_T[tri_blk(R, kt) * BS + li * BSTR + 4 * lg]);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2)
+                        acc = isW ? __builtin_amdgcn_mfma_f32_16x16x4f32(xv[kt][s2], tv[s2], acc, 0, 0, 0)
+                                  : __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s2], xv[kt][s2], acc, 0, 0, 0);
+                }
+                if (isW) reinterpret_cast<f32x4 *>(wrec)[(R * NKD + ct) * 64 + lane] = -acc;
+                else reinterpret_cast<f32x4 *>(rec + R_::Ut + (static_cast<size_t>(ct) * NS + R) * R_::UT_TILE)[lane] = acc;
+            }
+        }
+    }
+}
+
+template <typename T, bool BF, int C, int DK, int DV>
+hipError_t launch_prep_t(const ChunkParams &p, int64_t items, hipStream_t st) {
+    if (items <= 0) return hipSuccess;
+    const dim3 g(static_cast<unsigned>(items)), b(256);
+    switch (p.gmode) {
+    case GATES_KDA: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_KDA>), g, b, 0, st, p); break;
+    case GATES_GDN: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN>), g, b, 0, st, p); break;
+    case GATES_FG2_PLUS: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2_PLUS>), g, b, 0, st, p); break;
+    case GATES_FG2:
+        if constexpr (DK == DV) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2>), g, b, 0, st, p);
+        else return hipErrorInvalidValue;
+        break;
+    default: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2>), g, b, 0, st, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn2
+
+namespace gdn2 {
+
+template <typename T, bool BF, int C>
+static hipError_t launch_prep_c(const ChunkParams &p, int dk, int dv, int64_t items, hipStream_t st) {
+    if (dk == 128 && dv == 128) return launch_prep_t<T, BF, C, 128, 128>(p, items, st);
+    if (dk == 64 && dv == 64) return launch_prep_t<T, BF, C, 64, 64>(p, items, st);
+    if (dk == 128 && dv == 64) return launch_prep_t<T, BF, C, 128, 64>(p, items, st);
+    if (dk == 64 && dv == 128) return launch_prep_t<T, BF, C, 64, 128>(p, items, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prep(const ChunkParams &p, int chunk, int dk, int dv, bool bf16, int64_t items,
+                       hipStream_t st) {
+    if (bf16) {
+        if (chunk == 32) return launch_prep_c<bf16_t, true, 32>(p, dk, dv, items, st);
+        if (chunk == 64) return launch_prep_c<bf16_t, true, 64>(p, dk, dv, items, st);
+        if (chunk == 128) return launch_prep_c<bf16_t, true, 128>(p, dk, dv, items, st);
+    } else {
+        if (chunk == 32) return launch_prep_c<float, false, 32>(p, dk, dv, items, st);
+        if (chunk == 64) return launch_prep_c<float, false, 64>(p, dk, dv, items, st);
+        if (chunk == 128) return launch_prep_c<float, false, 128>(p, dk, dv, items, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn2

@@ -171,7 +171,7 @@ const char *gdn2_last_error(void);
 
 /*
  * Bytes of device workspace gdn2_chunk_fwd needs for these dims and chunk size, or 0 if
- * the dims are invalid. For a packed batch the size uses the upper bound
+ * the dims or the chunk size are invalid. For a packed batch the size uses the upper bound
  * ceil(T / chunk_size) + N on the number of chunks, so it depends only on the dims.
  */
 size_t gdn2_chunk_fwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size);
@@ -186,7 +186,8 @@ size_t gdn2_chunk_fwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
  *               Precondition (not checked on the device): cu_seqlens[0] = 0,
  *               non-decreasing, cu_seqlens[N] = T. Zero-length sequences are allowed and
  *               return S_T = S0 (or zeros).
- *   chunk_size  64 (the only size built)
+ *   chunk_size  32, 64 or 128 tokens per chunk of the WY form (results do not depend on
+ *               it beyond rounding). Every dtype and head-dim pair is built at every size.
  *   o           device output [B, T, h_v, d_v] in the input dtype; must not alias inputs
  *   S_T         device fp32 [N, h_v, d_k, d_v] final states, or NULL to skip them. S_T may
  *               be the same buffer as S0 (in-place continuation); no other aliasing.
@@ -240,7 +241,8 @@ size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
 
 /*
  * Gradients of gdn2_chunk_fwd (without fusion options, GDN-2 gates) with respect to every
- * input and the initial state, taken through the chunked form of the burn-gdn2 docs page
+ * input and the initial state (built for chunk_size 64, bf16 at any head dims and fp32 at
+ * d_k = d_v = 64; other configurations return GDN2_ERR_UNSUPPORTED), taken through the chunked form of the burn-gdn2 docs page
  * ("Architecture", Chunk mode; its Chunk WY training path): the forward is re-run to store
  * the state entering every chunk, then one pass runs the state gradient backward over the
  * chunks, and one pass per chunk forms the input gradients.

@@ -70,11 +70,14 @@ def test_chunk_fwd_rejects_bad_arguments(L):
     assert chunk(L, Dims(**{**ok, "h_k": 0})) == 2
     assert chunk(L, Dims(**{**ok, "d_k": 96})) == 3
     assert chunk(L, Dims(**{**ok, "d_v": 0})) == 2
-    assert chunk(L, Dims(**ok), chunk_size=32) == 3
+    assert chunk(L, Dims(**ok), chunk_size=16) == 3           # built: 32, 64 and 128
+    assert chunk(L, Dims(**ok), chunk_size=96) == 3
     assert chunk(L, Dims(**ok), chunk_size=0) == 2
     assert chunk(L, Dims(**{**ok, "seqlen": -1})) == 2
     assert chunk(L, Dims(**{**ok, "batch": 0})) == 2
-    assert chunk(L, Dims(**{**ok, "dtype": 0})) == 3          # fp32 is built for d = 64 only
+    for cs in (32, 64, 128):                                  # valid: stopped at o aliasing q
+        assert chunk(L, Dims(**{**ok, "dtype": 0}), chunk_size=cs) == 2
+        assert chunk(L, Dims(**ok), chunk_size=cs) == 2
     assert chunk(L, Dims(**ok), q=None) == 1
     assert chunk(L, Dims(**ok), ws=None) == 4
     assert chunk(L, Dims(**ok), ws_bytes=1024) == 4
@@ -196,6 +199,17 @@ def test_workspace_size_formula(L):
         32 * 2 * rec64 + seg_bytes(2, 8, 128, 64)
     d = Dims(8, 2048, 0, 8, 8, 128, 128, 1)         # 64 pairs: enough work, no segments
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 8 * 32 * 8 * rec
+    # chunk sizes 32 and 128, and fp32 records at d = 128: records of
+    # E*(3*C*dk + C*C + C*dv) + 4*dk bytes, no segment area
+    def rec_c(C, E, dk, dv):
+        return (E * (3 * C * dk + C * C + C * dv) + 4 * dk + 255) // 256 * 256
+    d = Dims(1, 4096, 0, 16, 16, 128, 128, 1)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 32 * 16 * rec_c(128, 2, 128, 128)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 32) == 128 * 16 * rec_c(32, 2, 128, 128)
+    d = Dims(1, 4096, 0, 16, 16, 128, 128, 0)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 64 * 16 * rec_c(64, 4, 128, 128)
+    d = Dims(1, 1000, 5, 1, 2, 128, 64, 0)          # packed, fp32, 128-token chunks
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 256 + (8 + 5) * 2 * rec_c(128, 4, 128, 64)
     assert L.gdn2_chunk_fwd_workspace_bytes(None, 64) == 0
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(Dims(1, 10, 0, 1, 1, 96, 64, 1)),
                                             64) == 0
@@ -288,6 +302,9 @@ def test_chunk_bwd_validation(L):
     need = L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 64)
     assert need > L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64)
     assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(Dims(2, 100, 0, 2, 4, 32, 128, 1)), 64) == 0
+    # the backward is built for 64-token chunks, and in fp32 for d_k = d_v = 64
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 128) == 0
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(Dims(2, 100, 0, 2, 4, 128, 128, 0)), 64) == 0
 
     def call(dims=d, outs=None, ws=P[19], ws_bytes=None, dO=P[8]):
         o = P[10:17] if outs is None else outs
@@ -295,6 +312,7 @@ def test_chunk_bwd_validation(L):
                                 *o, ctypes.byref(dims), ws, need if ws_bytes is None else ws_bytes,
                                 None)
     assert call(dims=Dims(2, 100, 0, 2, 4, 128, 128, 7)) == 3          # dtype
+    assert call(dims=Dims(2, 100, 0, 2, 4, 128, 128, 0)) == 3          # fp32 at d = 128
     assert call(dims=Dims(2, 100, 0, 2, 5, 128, 128, 1)) == 2          # h_v not a multiple of h_k
     assert call(dO=None) == 1
     assert call(outs=[None] + P[11:17]) == 1
