@@ -17,6 +17,7 @@ cores over a bounded sample as a reported baseline (`cpu_baseline`), and its out
 as a parity check of the timed run.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -38,7 +39,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0    # dense
 CHUNK = 64
 
 
-def chunk_alg(wl, tokens, nseq):
+def chunk_alg(wl, tokens, nseq, chunk=CHUNK):
     """Algorithmic bytes and flops of one chunked forward (per-tensor element counts)."""
     e = 2 if wl.dtype == torch.bfloat16 else 4
     qk = 2 * tokens * wl.h_k * wl.d_k * e
@@ -48,7 +49,7 @@ def chunk_alg(wl, tokens, nseq):
     states = (2 if wl.s0_std is not None else 1) * nseq * wl.h_v * wl.d_k * wl.d_v * 4
     bytes_ = qk + vw + ab + o + states
     # triangle-aware flops per (token, value head): C(3 d_k + 2 d_v) + 6 d_k d_v
-    flops = tokens * wl.h_v * (CHUNK * (3 * wl.d_k + 2 * wl.d_v) + 6 * wl.d_k * wl.d_v)
+    flops = tokens * wl.h_v * (chunk * (3 * wl.d_k + 2 * wl.d_v) + 6 * wl.d_k * wl.d_v)
     return bytes_, flops
 
 
@@ -122,7 +123,9 @@ def bench_chunk(steps, warmup, seed=1002):
     return wl, x, (o, S_T), t_warm, float(np.median(cold))
 
 
-def bench_decode(seed=3):
+def bench_decode(seed=3, repeats=5):
+    """The decode workload's 256 consecutive steps, timed `repeats` times back to back
+    (median per step), eagerly and as one captured HIP graph replayed."""
     wl = inputs.DECODE_F32
     x = inputs.decode_inputs(wl, seed=seed)
     d = {n: x[n].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w")}
@@ -136,32 +139,47 @@ def bench_decode(seed=3):
 
     run_all()                                   # warm-up pass (state keeps evolving)
     stream = torch.cuda.current_stream()
-    t_step = time_region(run_all, 1, stream) / wl.steps
-    # parity sample of the first pass is covered by the tests; here check finiteness
+    eager = [time_region(run_all, 1, stream) / wl.steps for _ in range(repeats)]
+    # the same 256 launches captured once and replayed (no host launch cost per step)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        run_all()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            run_all()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    graphed = [time_region(graph.replay, 1, stream) / wl.steps for _ in range(repeats)]
     assert torch.isfinite(S).all()
-    return wl, t_step
+    del graph
+    return wl, float(np.median(eager)), float(np.median(graphed)), eager, graphed
 
 
-def bench_chunk_workload(wl, steps, warmup, seed):
+def bench_chunk_workload(wl, steps, warmup, seed, chunk=CHUNK):
     """Warm back-to-back timing of one chunk-forward workload (inputs drawn on the GPU)."""
     x = inputs.chunk_inputs_device(wl, seed)
     B, T = x["q"].shape[:2]
     N = x["num_seqs"]
     ws = torch.empty(g.chunk_fwd_workspace_bytes(B, T, wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.dtype,
-                                                 num_seqs=N if x["cu_seqlens"] is not None else 0),
+                                                 num_seqs=N if x["cu_seqlens"] is not None else 0,
+                                                 chunk_size=chunk),
                      dtype=torch.uint8, device="cuda")
     o = torch.empty(B, T, wl.h_v, wl.d_v, dtype=wl.dtype, device="cuda")
     S_T = torch.empty(N, wl.h_v, wl.d_k, wl.d_v, dtype=torch.float32, device="cuda")
 
     def call():
         g.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S0=x["S0"],
-                    cu_seqlens=x["cu_seqlens"], workspace=ws, out=o, final_state=S_T)
+                    cu_seqlens=x["cu_seqlens"], workspace=ws, out=o, final_state=S_T,
+                    chunk_size=chunk)
 
     for _ in range(warmup):
         call()
     t = time_region(call, steps, torch.cuda.current_stream())
-    nbytes, flops = chunk_alg(wl, B * T, N)
-    res = {"workload": wl.name, "tokens": B * T, "us_per_call": t * 1e6,
+    nbytes, flops = chunk_alg(wl, B * T, N, chunk)
+    res = {"workload": wl.name, "chunk_size": chunk, "tokens": B * T, "us_per_call": t * 1e6,
            "tokens_per_s": B * T / t, "alg_bytes": nbytes, "alg_flops": flops,
            "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
            "mfma_frac_bf16": flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS}
@@ -435,6 +453,24 @@ def bench_fused(steps, warmup, seed=8):
 CPU_WORK_TARGET_S = 10.0     # CPU-seconds of oracle work per baseline sample
 
 
+def host_cpu():
+    """(CPU model name from /proc/cpuinfo, cores this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return model, cores
+
+
 def cpu_baseline_chunk(wl, x, gpu_out):
     """fp64 oracle over the whole timed workload, repeated until the sample holds about
     CPU_WORK_TARGET_S CPU-seconds (threads x wall); the first pass also gives parity."""
@@ -458,7 +494,9 @@ def cpu_baseline_chunk(wl, x, gpu_out):
                       "tol": 2e-2}
         if wall * threads >= CPU_WORK_TARGET_S or reps >= 20:
             break
+    model, host_cores = host_cpu()
     base = {"value": reps * B * T / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cores": host_cores,
             "sample": f"whole workload ({B * T} tokens x {wl.h_v} heads, fp64, "
                       f"{wl.h_v * B} (sequence, head) pairs over {threads} threads) x {reps} "
                       f"passes, {wall:.2f} s wall"}
@@ -491,8 +529,9 @@ def cpu_baseline_decode(wl, pairs=1024):
     state_updates = pairs * wl.steps
     per_step_equiv = dt / state_updates * (wl.num_seqs * wl.h_v)   # all states, one step
     st_bytes = 2 * wl.num_seqs * wl.h_v * wl.d_k * wl.d_v * 4
+    model, host_cores = host_cpu()
     return {"value": st_bytes / per_step_equiv / 1e9, "unit": "state GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cores": host_cores,
             "sample": f"{pairs} of {wl.num_seqs * wl.h_v} states x {wl.steps} steps, fp64, "
                       f"{dt:.2f} s wall, scaled to all states"}
 
@@ -566,8 +605,8 @@ def pmc_summary(fetch_dir, write_dir):
             dec.setdefault(key, {"bytes_per_launch": int(rb + wb), "kernel": short})
     out = {"_note": f"HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x{ff}) and "
                     f"WRITE_SIZE (x{wf}); commands and calibration in hbm_traffic_counters.md",
-           "chunk_fwd_t4096": {"source_hash": source_hash("gdn2_chunk.hip", "gdn2_mfma.h",
-                                                          "gdn2_common.h"),
+           "chunk_fwd_t4096": {"source_hash": source_hash("gdn2_chunk.hip", "gdn2_chunk.h",
+                                                          "gdn2_mfma.h", "gdn2_common.h"),
                                "bytes_per_launch": sum(chunk.values()), "kernels": chunk}}
     dsrc = source_hash("gdn2_decode.hip", "gdn2_common.h")
     for key, rec in dec.items():
@@ -622,7 +661,7 @@ def main():
         wl, x, gout, t_warm, t_cold = bench_chunk(args.steps, args.warmup)
         B, T = x["q"].shape[:2]
         nbytes, flops = chunk_alg(wl, B * T, B)
-        src = source_hash("gdn2_chunk.hip", "gdn2_mfma.h", "gdn2_common.h")
+        src = source_hash("gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h", "gdn2_common.h")
         out.update({
             "value": B * T / t_warm, "unit": "tokens/s", "ms_per_step": t_warm * 1e3,
             "config": {"workload": wl.name, "batch": B, "seq_len": T, "h_k": wl.h_k,
@@ -643,10 +682,16 @@ def main():
             out["cpu_baseline"] = base
             out["parity"] = parity
     if args.only in ("decode", "all"):
-        dwl, t_step = bench_decode()
+        dwl, t_step, t_graph, eager, graphed = bench_decode()
         dbytes, dstate, dflops = decode_alg(dwl)
         dsrc = source_hash("gdn2_decode.hip", "gdn2_common.h")
         dec = {"workload": dwl.name, "steps": dwl.steps, "us_per_step": t_step * 1e6,
+               "timing": f"median over 5 timed passes of {dwl.steps} steps each, eager "
+                         "launches; graph: the same steps captured once and replayed",
+               "us_per_step_passes": [round(t * 1e6, 3) for t in eager],
+               "us_per_step_graph": t_graph * 1e6,
+               "us_per_step_graph_passes": [round(t * 1e6, 3) for t in graphed],
+               "graph_hbm_frac": dbytes / t_graph / 1e9 / HBM_PEAK_GBPS,
                "tokens_per_s": dwl.num_seqs / t_step,
                "state_GBps": dstate / t_step / 1e9, "total_GBps": dbytes / t_step / 1e9,
                "roofline": {"bound": "hbm", "achieved": dbytes / t_step / 1e9,
@@ -673,10 +718,16 @@ def main():
         out["chunk_states"] = bench_chunk_states(max(10, args.steps // 4), 3)
         out["chunk_bwd"] = bench_chunk_bwd(max(5, args.steps // 10), 2)
     if args.only in ("chunk", "all") and not args.no_other_workloads:
+        t4096_f32 = dataclasses.replace(inputs.CHUNK_BF16_T4096, dtype=torch.float32,
+                                        name="chunk_f32_b1_t4096_h16_d128_negeig")
         out["other_chunk_workloads"] = [
-            bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed)
-            for wl, seed in ((inputs.CHUNK_F32_SMALL, 2000), (inputs.CHUNK_BF16_B8, 2001),
-                             (inputs.VARLEN_BF16, 2004))]
+            bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed, chunk)
+            for wl, seed, chunk in ((inputs.CHUNK_F32_SMALL, 2000, 64),
+                                    (inputs.CHUNK_BF16_B8, 2001, 64),
+                                    (inputs.VARLEN_BF16, 2004, 64),
+                                    (inputs.CHUNK_BF16_T4096, 2002, 128),
+                                    (inputs.CHUNK_BF16_T4096, 2002, 32),
+                                    (t4096_f32, 2012, 64))]
     print(json.dumps(out))
 
 
