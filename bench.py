@@ -362,8 +362,11 @@ def bench_chunk_bwd(steps, warmup, seed=11):
     states = 3 * x["S0"].numel() * 4                                          # S0, dS_T, dS0
     nbytes = tok_in + grads + states
     del x, ws, dO, dST
+    bsrc = source_hash("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h",
+                       "gdn2_common.h")
     return {"workload": f"{wl.name}_bwd", "us_per_call": t * 1e6, "tokens_per_s": T * B / t,
-            "alg_bytes": nbytes, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS}
+            "alg_bytes": nbytes, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
+            "traffic": measured_traffic("chunk_bwd_t4096", bsrc)}
 
 
 def bench_fused(steps, warmup, seed=8):
@@ -537,12 +540,32 @@ def cpu_baseline_decode(wl, pairs=1024):
 
 
 def profile_driver():
+    """Short fixed sequence for hardware-counter runs: 5 chunk forwards (bf16, B=1 T=4096
+    H=16 d=128, chunk 64), 2 at chunk 128, 2 fp32 forwards of that shape, 3 chunked
+    backwards, 20 decode steps with an fp32 state and 20 with a bf16 state, and 3 copies of
+    256 MiB (the copy calibrates the FETCH_SIZE / WRITE_SIZE counters)."""
     wl = inputs.CHUNK_BF16_T4096
     x = inputs.chunk_inputs(wl, seed=1002)
     d = {n: x[n].cuda() for n in ("q", "k", "v", "log_alpha", "b", "w", "S0")}
     for _ in range(5):
         g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=d["S0"])
+    for _ in range(2):
+        g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=d["S0"],
+                    chunk_size=128)
     torch.cuda.synchronize()
+    f = {n: t.float() for n, t in d.items()}
+    for _ in range(2):
+        g.chunk_fwd(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"], S0=f["S0"])
+    del f
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    dO = torch.randn(1, wl.seqlen, wl.h_v, wl.d_v, generator=gen, device="cuda").to(wl.dtype)
+    for _ in range(3):
+        g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO, S0=d["S0"],
+                    dS_T=torch.ones_like(d["S0"]))
+    torch.cuda.synchronize()
+    del dO
+    torch.cuda.empty_cache()
     dw = inputs.DECODE_F32
     y = inputs.decode_inputs(dw, seed=3, steps=1)
     S = y["S"].cuda()
@@ -562,52 +585,122 @@ def profile_driver():
     print("profile driver done")
 
 
+def kernel_short(k):
+    """A kernel's name without its parameter list and namespaces."""
+    for pre in ("void ", "gdn2::", "(anonymous namespace)::"):
+        k = k.replace(pre, "")
+    return k.split("(")[0]
+
+
+def pmc_table(dirs):
+    """Per-kernel averages of every counter found in the counter_collection CSVs under the
+    given directories (one rocprofv3 --pmc run of --profile-driver each), with the derived
+    ratios: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs),
+    and LDS bank-conflict cycles per LDS-active cycle."""
+    import csv
+    import glob
+    from collections import defaultdict
+    agg = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if "gdn2" not in r["Kernel_Name"]:
+                        continue
+                    agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    rows = []
+    for k, ctrs in sorted(agg.items()):
+        avg = {c: sum(v) / len(v) for c, v in ctrs.items()}
+        short = kernel_short(k)
+        row = {"kernel": short, "launches": max(len(v) for v in ctrs.values()), **avg}
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("GRBM_GUI_ACTIVE"):
+            # GRBM_GUI_ACTIVE comes summed over the 8 XCDs: busy cycles per SIMD over the
+            # kernel's active cycles on one XCD (the max-over-XCDs of the tool's MfmaUtil)
+            row["gui_active_cycles_per_xcd"] = avg["GRBM_GUI_ACTIVE"] / 8
+            row["mfma_busy_frac"] = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (avg["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            row["lds_conflict_per_active"] = avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"]
+        rows.append(row)
+    for r in rows:
+        print(json.dumps(r))
+    return rows
+
+
 def pmc_summary(fetch_dir, write_dir):
     """Writes profiles/pmc_traffic.json from two `rocprofv3 --pmc` runs of --profile-driver
     (FETCH_SIZE, then WRITE_SIZE; their counter_collection CSVs under the two directories).
-    Each counter is scaled by what it reads for the 256 MiB copy of the driver; the rows it
-    prints are the per-launch table of profiles/hbm_traffic_counters.md."""
+    Each counter is scaled by what it reads for the 256 MiB copy of the driver. Launches of
+    one kernel are kept in dispatch order, so the chunk-forward kernels of the 5 plain
+    forwards (the first 5 launches) are told apart from the forward re-run inside the 3
+    backwards (the next 3). Prints the per-launch rows of the traffic table."""
     import csv
     import glob
     from collections import defaultdict
 
     def load(d, ctr):
-        agg = defaultdict(list)
+        per = defaultdict(list)
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for r in csv.DictReader(f):
                     if r["Counter_Name"] == ctr:
-                        agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        return {k: (sum(v) / len(v), len(v)) for k, v in agg.items()}
+                        per[r["Kernel_Name"]].append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        return {k: [v for _, v in sorted(x)] for k, x in per.items()}
 
     F, W = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
     copyk = [k for k in F if "copyBuffer" in k][0]
     copy_kib = 256 * 1024
-    ff, wf = copy_kib / F[copyk][0], copy_kib / W[copyk][0]
-    print(f"calibration: FETCH_SIZE {F[copyk][0]:,.0f} KiB per 256 MiB copy -> x{ff:.2f}; "
-          f"WRITE_SIZE {W[copyk][0]:,.0f} KiB -> x{wf:.2f}")
+    ff, wf = copy_kib / np.mean(F[copyk]), copy_kib / np.mean(W[copyk])
+    print(f"calibration: FETCH_SIZE {np.mean(F[copyk]):,.0f} KiB per 256 MiB copy -> x{ff:.2f}; "
+          f"WRITE_SIZE {np.mean(W[copyk]):,.0f} KiB -> x{wf:.2f}")
     ff, wf = round(ff, 1), round(wf, 1)
-    chunk, dec = {}, {}
-    for k, (fk, n) in F.items():
+
+    def group(key, lo, hi):
+        """(read, written) bytes per launch of launches lo..hi-1 of a kernel."""
+        fv, wv = F.get(key, [])[lo:hi], W.get(key, [])[lo:hi]
+        if not fv:
+            return None
+        return float(np.mean(fv)) * ff * 1024, float(np.mean(wv)) * wf * 1024 if wv else 0.0
+
+    groups = {"chunk_fwd_t4096": [], "chunk_fwd_t4096_c128": [], "chunk_fwd_f32_t4096": [],
+              "chunk_bwd_t4096": []}
+    dec = {}
+    for k in F:
         if "gdn2" not in k:
             continue
-        wk = W.get(k, (0.0, 0))[0]
-        rb, wb = fk * ff * 1024, wk * wf * 1024
-        short = k.split("(")[0].replace("void gdn2::", "")
-        print(f"| {short} | {n} | {fk:,.0f} | {rb / 1e6:.1f} MB | {wk:,.0f} | {wb / 1e6:.1f} MB | "
-              f"{(rb + wb) / 1e6:.1f} MB |")
-        name = short.split("<")[0]
-        if name.startswith("chunk_"):
-            chunk[name] = int(rb + wb)
-        elif name == "recurrent_fwd_kernel":
-            key = ("decode_step_bf16state_n64_hv48" if "float, gdn2::bf16_t" in short
+        name = kernel_short(k)
+        base = name.split("<")[0]
+        if base in ("chunk_prep_kernel", "chunk_seg_kernel", "chunk_state_kernel"):
+            parts = [("chunk_fwd_t4096", 0, 5), ("chunk_bwd_t4096", 5, 8)]
+        elif base in ("prep_kernel", "panel_state_kernel"):
+            parts = [("chunk_fwd_f32_t4096" if "<float" in name else "chunk_fwd_t4096_c128", 0, 2)]
+        elif base.startswith("bwd_"):
+            parts = [("chunk_bwd_t4096", 0, 3)]
+        elif base == "recurrent_fwd_kernel":
+            key = ("decode_step_bf16state_n64_hv48" if "float, bf16_t" in name
                    else "decode_step_n64_hv48")
-            dec.setdefault(key, {"bytes_per_launch": int(rb + wb), "kernel": short})
+            rw = group(k, 0, 20)
+            dec[key] = {"bytes_per_launch": int(sum(rw)), "kernel": name}
+            print(f"| {name} | {key} | {rw[0] / 1e6:.1f} MB | {rw[1] / 1e6:.1f} MB | {sum(rw) / 1e6:.1f} MB |")
+            continue
+        else:
+            continue
+        for gname, lo, hi in parts:
+            rw = group(k, lo, hi)
+            if rw is None:
+                continue
+            groups[gname].append((name, rw))
+            print(f"| {name} | {gname} | {rw[0] / 1e6:.1f} MB | {rw[1] / 1e6:.1f} MB | {sum(rw) / 1e6:.1f} MB |")
     out = {"_note": f"HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x{ff}) and "
-                    f"WRITE_SIZE (x{wf}); commands and calibration in hbm_traffic_counters.md",
-           "chunk_fwd_t4096": {"source_hash": source_hash("gdn2_chunk.hip", "gdn2_chunk.h",
-                                                          "gdn2_mfma.h", "gdn2_common.h"),
-                               "bytes_per_launch": sum(chunk.values()), "kernels": chunk}}
+                    f"WRITE_SIZE (x{wf}); commands and calibration in hbm_traffic_counters.md"}
+    csrc = source_hash("gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h", "gdn2_common.h")
+    gsrc = source_hash("gdn2_prep.hip", "gdn2_state.hip", "gdn2_chunk.h", "gdn2_mfma.h",
+                       "gdn2_common.h")
+    bsrc = source_hash("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h",
+                       "gdn2_common.h")
+    for gname, items in groups.items():
+        src = {"chunk_fwd_t4096": csrc, "chunk_bwd_t4096": bsrc}.get(gname, gsrc)
+        out[gname] = {"source_hash": src, "bytes_per_launch": int(sum(sum(rw) for _, rw in items)),
+                      "kernels": {n: int(sum(rw)) for n, rw in items}}
     dsrc = source_hash("gdn2_decode.hip", "gdn2_common.h")
     for key, rec in dec.items():
         out[key] = {"source_hash": dsrc, **rec}
@@ -628,15 +721,18 @@ def main():
     ap.add_argument("--only", choices=["chunk", "decode", "bwd", "all"], default="all",
                     help="bwd: time the chunked backward alone (its own JSON line)")
     ap.add_argument("--profile-driver", action="store_true",
-                    help="short fixed sequence for hardware-counter runs: 5 chunk forwards, "
-                         "20 decode steps with an fp32 state and 20 with a bf16 state, and 3 "
-                         "copies of 256 MiB (the copy calibrates the "
-                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+                    help="short fixed sequence for hardware-counter runs (see profile_driver)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/pmc_traffic.json from the two counter runs and exit")
+    ap.add_argument("--pmc-table", nargs="+", metavar="DIR",
+                    help="print per-kernel averages of the counters under the given rocprofv3 "
+                         "--pmc output directories (with the MFMA-busy and LDS ratios) and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.pmc_table:
+        pmc_table(args.pmc_table)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
