@@ -17,12 +17,11 @@
 //
 // Kernels:
 //   K0 chunk_map_kernel    packed batches: chunk offsets per sequence (no host sync).
-//   K1 chunk_prep_kernel   persistent over the (chunk, value head) records, fully parallel:
-//                          the cumulative log decay, A and M on the matrix cores,
-//                          T = (I + A)^{-1} by 16x16 blocks (diagonal blocks by forward
-//                          substitution, the rest by fp32 matrix-core products), the WY
-//                          factors as tile GEMMs, and the per-chunk operands of K2, written to
-//                          the workspace already in matrix-core fragment order.
+//   K1 prep_kernel        (gdn2_prep.hip) one workgroup per (chunk, value head) record, fully
+//                          parallel: the cumulative log decay, A and M on the matrix cores,
+//                          T = (I + A)^{-1} by 16x16 blocks, the WY factors as tile GEMMs, and
+//                          the per-chunk operands of K2, written already in matrix-core
+//                          fragment order.
 //   K2 chunk_state_kernel  per (sequence, value head, 16 columns of S): a chain wave that
 //                          runs the recurrence over the chunks with its slice of S in fp32
 //                          registers, an output wave that forms o from the operands the
@@ -30,7 +29,7 @@
 //                          operands in LDS one chunk ahead; writes o and S_T.
 //
 // Numerics: exp(g_r - g_i) is split into factors relative to the middle token of each
-// 16-token sub-chunk (K1 below), so no factor spans more than 8 tokens of decay except the
+// 16-token sub-chunk (K1), so no factor spans more than 8 tokens of decay except the
 // sub-chunk-to-sub-chunk factors, which are <= 1 (an underflow there means a negligible
 // true product).
 // Padding rows of a partial chunk are identity tokens (k = q = b = 0, w.v = 0,
@@ -51,607 +50,6 @@ __global__ void chunk_map_kernel(const int32_t *__restrict__ cu, int32_t *__rest
             acc += (len + chunk - 1) / chunk;
             map[n + 1] = acc;
         }
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// K1: per (chunk, value head) WY factors and K2 operands, as a persistent kernel.
-//
-// One 512-thread workgroup per CU walks the (chunk, value head) records in chunk-major order
-// (record = chunk * h_v + h, stride = grid size). While a record is computed from LDS, the
-// raw k, q, b, log alpha, w, v tiles of the next one are already in flight into registers.
-//
-// Factorisation: with g the cumulative log decay and Mid_R = g at the middle token of
-// 16-token sub-chunk R, every decay factor exp(g_r - g_i) (r in sub-chunk R, i in I <= R)
-// is built from bounded pieces computed once per record:
-//   Khat_r = b_r k_r exp(g_r - Mid_R),  Qhat_r = q_r exp(g_r - Mid_R)   (row side)
-//   Kbar_i = k_i exp(Mid_I - g_i)                                        (column side)
-//   f_RI   = exp(Mid_R - Mid_I) <= 1 per channel, for I < R
-// so A[r,i] = sum_c Khat_r Kbar_i f_RI and M[r,i] = sum_c Qhat_r Kbar_i f_RI. Each exponent
-// spans at most 8 tokens of decay except f_RI, which is <= 1 (an underflow there means a
-// negligible true product). The outputs reuse the same tiles: gamma.q = Qhat exp(Mid_R),
-// gamma.b.k = Khat exp(Mid_R), exp(g_C - g_i) k_i = Kbar_i exp(g_C - Mid_I).
-//
-// Phases per record:
-//   0  log alpha -> LDS, cumulative sum in place, per-channel factors, gamma_C; Khat, Qhat,
-//      Kbar and w.v tiles from the registers; gamma.q written straight to the workspace
-//   1  A^T and M^T 16x16 blocks on the matrix cores (the transposed products leave each
-//      lane's results in row-per-lane order); M goes to the workspace, A to LDS
-//  2a wave 0: diagonal inverses T_RR by forward substitution; waves 1-7: KgT
-//  2b off-diagonal T blocks by levels, T_RI = -T_RR sum_{I<=m<R} A_Rm T_mI (fp32 MFMA)
-//   3  W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) as tile GEMMs, one column tile of
-//      each per wave, written to the workspace in the orders K2 reads
-// ---------------------------------------------------------------------------------------
-
-
-struct PrepLoc {
-    int64_t t0;     // first token of the chunk
-    int L;          // valid rows
-    int h, hk;
-    size_t rec;     // record index
-};
-
-
-// GM: the gate mode (GateMode), one instance per mode, so that no instance carries another
-// mode's selects (run-time selects around the prefetched loads measured 7 us slower).
-template <typename T, bool BF, int DK, int DV, bool NTR, int GM>
-__global__ __launch_bounds__(512, 1) void chunk_prep_kernel(ChunkParams p) {
-    using R_ = Rec<kChunk, DK, DV, BF>;
-    constexpr int C = kChunk, NT = 512, NW = NT / 64;
-    constexpr int KT = Op<BF>::KT;            // k per matrix-core tile: 32 (bf16) / 16 (fp32)
-    constexpr int KS = BF ? 8 : 4;            // consecutive k values a lane holds per tile
-    constexpr int VEC = 16 / sizeof(T);
-    constexpr int SK = DK + VEC;              // padded row stride of the d_k tiles (elements)
-    constexpr int SV = DV + VEC;              // padded row stride of the w.v tile
-    constexpr int SG = DK + 4;                // padded row stride of s_g (floats)
-    constexpr int SA = C + 4;                 // padded row stride of A and T (floats)
-    constexpr int STB = C + 8;                // row stride of the bf16 copy of T (elements)
-    static_assert(C * STB * 2 <= C * SA * 4, "bf16 T fits in the A space");
-    constexpr int VK = DK / VEC, VV = DV / VEC;
-    constexpr int RAWV = C * VK / NT, RAWW = C * VV / NT;
-    constexpr int PARTS = NT / DK;            // cumulative sum: token parts per channel
-    constexpr int RPP = C / PARTS;
-    constexpr int NKC = R_::NKT_C, NKD = R_::NKT_DK, NKTC = C / KT;
-    static_assert(RAWV >= 1 && RAWV * NT == C * VK, "raw tile split");
-    static_assert(RAWW >= 1 && RAWW * NT == C * VV, "raw tile split");
-
-    __shared__ __attribute__((aligned(16))) T s_kh[C * SK];   // Khat
-    __shared__ __attribute__((aligned(16))) T s_qh[C * SK];   // Qhat
-    __shared__ __attribute__((aligned(16))) T s_kb[C * SK];   // Kbar
-    __shared__ __attribute__((aligned(16))) T s_wv[C * SV];   // w.v
-    __shared__ __attribute__((aligned(16))) float s_g[C * SG];
-    __shared__ __attribute__((aligned(16))) float s_A[C * SA];
-    __shared__ __attribute__((aligned(16))) float s_T[C * SA];
-    __shared__ __attribute__((aligned(16))) float s_fmid[4 * DK];   // exp(Mid_R)
-    __shared__ __attribute__((aligned(16))) float s_fkg[4 * DK];    // exp(g_C - Mid_I)
-    __shared__ __attribute__((aligned(16))) float s_foff[6 * DK];   // exp(Mid_R - Mid_I), R > I
-    __shared__ float s_part[PARTS * DK];
-
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 15, lg = lane >> 4;
-    const T *kp = static_cast<const T *>(p.k), *qp = static_cast<const T *>(p.q);
-    const T *bp = static_cast<const T *>(p.b), *lap = static_cast<const T *>(p.log_alpha);
-    const T *vp = static_cast<const T *>(p.v), *wp = static_cast<const T *>(p.w);
-
-    const int total_chunks = p.cu ? p.map[p.num_seqs] : p.num_seqs * p.nc_dense;
-    const int nitems = total_chunks * p.h_v;
-
-    auto locate = [&](int item, PrepLoc &lc) {
-        const int chunk = item / p.h_v;
-        lc.h = item - chunk * p.h_v;
-        lc.hk = lc.h / p.group;
-        int n, j;
-        int64_t start, end;
-        locate_chunk(p, chunk, n, j, start, end);
-        lc.t0 = start + static_cast<int64_t>(j) * C;
-        lc.L = static_cast<int>(min<int64_t>(C, end - lc.t0));
-        lc.rec = static_cast<size_t>(item);
-    };
-    // raw 16-byte vectors of a record (rows >= L are zero: identity tokens), loaded in four
-    // parts: a workgroup that issues all 96 KB at once stalls at the issue until most of it
-    // has arrived, so the next record's parts are issued one per phase instead.
-    u32x4 rk[RAWV], rq[RAWV], rb[RAWV], rl[RAWV], rw[RAWW], rv[RAWW];
-    // Gate modes (GateMode): KDA and GDN carry one b per (token, value head) in b, which also
-    // serves as w, and GDN one decay per (token, value head); FG2 carries beta [..][DK] in b
-    // (k <- sqrt(beta) k, b <- 1 and w <- sqrt(beta), applied in phase 0b), FG2+ also
-    // beta_v in w (w <- sqrt(beta_v)).
-    constexpr bool b_scalar = GM == GATES_KDA || GM == GATES_GDN;
-    constexpr bool la_scalar = GM == GATES_GDN;
-    constexpr bool fg2 = GM == GATES_FG2 || GM == GATES_FG2_PLUS;
-    // a 16-byte vector of VEC copies of one element
-    auto bcast = [](const T *x) {
-        uint32_t u;
-        if constexpr (sizeof(T) == 4) u = __float_as_uint(io<T>::ld(x));
-        else u = static_cast<uint32_t>(x->bits) * 0x10001u;
-        return u32x4{u, u, u, u};
-    };
-    // (`scalar` is uniform over the workgroup: one branch around the whole loop)
-    auto load_gate = [&](const PrepLoc &lc, const T *src, u32x4 *dst, bool scalar) {   // [C][H_v][DK]
-        if (scalar) {
-#pragma unroll
-            for (int e = 0; e < RAWV; ++e) {
-                const int r = (tid + NT * e) / VK;
-                dst[e] = u32x4{0u, 0u, 0u, 0u};
-                if (r < lc.L) dst[e] = bcast(src + static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h);
-            }
-            return;
-        }
-#pragma unroll
-        for (int e = 0; e < RAWV; ++e) {
-            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-            dst[e] = u32x4{0u, 0u, 0u, 0u};
-            if (r < lc.L)
-                dst[e] = *reinterpret_cast<const u32x4 *>(
-                    src + (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DK + cv * VEC);
-        }
-    };
-    auto load_qk = [&](const PrepLoc &lc) {                               // [C][H_k][DK]
-#pragma unroll
-        for (int e = 0; e < RAWV; ++e) {
-            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-            rk[e] = u32x4{0u, 0u, 0u, 0u};
-            rq[e] = rk[e];
-            if (r < lc.L) {
-                const size_t ok = (static_cast<size_t>(lc.t0 + r) * p.h_k + lc.hk) * DK + cv * VEC;
-                rk[e] = *reinterpret_cast<const u32x4 *>(kp + ok);
-                rq[e] = *reinterpret_cast<const u32x4 *>(qp + ok);
-            }
-        }
-    };
-    // w's source: w itself (GDN-2, FG2+), or b (KDA and GDN: the scalar; FG2: beta, whose
-    // [..][DK] rows index like w's [..][DV] rows since d_v = d_k there)
-    const T *wsrc = (b_scalar || GM == GATES_FG2) ? bp : wp;
-    auto load_wv = [&](const PrepLoc &lc) {                               // [C][H_v][DV]
-#pragma unroll
-        for (int e = 0; e < RAWW; ++e) {
-            const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
-            rw[e] = u32x4{0u, 0u, 0u, 0u};
-            rv[e] = rw[e];
-            if (r < lc.L) {
-                const size_t ov = (static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h) * DV + cv * VEC;
-                // a scalar b is [rows][H_v]: only the broadcast below may index it
-                if (!b_scalar) rw[e] = *reinterpret_cast<const u32x4 *>(wsrc + ov);
-                rv[e] = *reinterpret_cast<const u32x4 *>(vp + ov);
-            }
-        }
-        if (b_scalar) {                  // w = the scalar b (uniform branch)
-#pragma unroll
-            for (int e = 0; e < RAWW; ++e) {
-                const int r = (tid + NT * e) / VV;
-                if (r < lc.L) rw[e] = bcast(wsrc + static_cast<size_t>(lc.t0 + r) * p.h_v + lc.h);
-            }
-        }
-    };
-
-    int item = blockIdx.x;
-    PrepLoc cur;
-    if (item < nitems) {
-        locate(item, cur);
-        load_gate(cur, lap, rl, la_scalar);
-        load_qk(cur);
-        load_gate(cur, bp, rb, b_scalar);
-        load_wv(cur);
-    }
-    for (; item < nitems; item += gridDim.x) {
-        const int next = item + gridDim.x;
-        const bool has_next = next < nitems;
-        PrepLoc nxt = cur;
-        if (has_next) locate(next, nxt);
-        char *rec = p.rec + cur.rec * R_::bytes;
-
-        // ---- phase 0: cumulative log decay, in log2 units, into s_g ----
-        if constexpr (BF) {
-            // g^T = la^T L^T on the matrix cores (L: lower-triangular ones): raw log alpha
-            // staged in the (still free) Khat tile, read back as A operands by transpose
-            // reads; the 0/1 operand is built in registers; each output tile is one
-            // 16-byte store of four channels of one token
-#pragma unroll
-            for (int e = 0; e < RAWV; ++e) {
-                const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-                *reinterpret_cast<u32x4 *>(&s_kh[r * SK + cv * VEC]) = rl[e];
-            }
-            __syncthreads();
-            for (int t = wave; t < (DK / 16) * 4; t += NW) {
-                const int ct = t >> 2, R = t & 3;         // channel tile, token tile
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt) {
-                    if (kt * 32 > 16 * R + 15) break;
-                    const int k0 = kt * 32 + 8 * lg + (li >> 2);
-                    const u32x2 lo = lds_tr4(&s_kh[k0 * SK + 16 * ct + 4 * (li & 3)]);
-                    const u32x2 hi = lds_tr4(&s_kh[(k0 + 4) * SK + 16 * ct + 4 * (li & 3)]);
-                    const int tok = 16 * R + li;          // output token (column of L^T)
-                    u32x4 ones;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int k = kt * 32 + 8 * lg + 2 * q;
-                        ones[q] = (k <= tok ? 0x3F80u : 0u) | (k + 1 <= tok ? 0x3F800000u : 0u);
-                    }
-                    acc = mma_k32(u32x4{lo.x, lo.y, hi.x, hi.y}, ones, acc);
-                }
-                // lane: g^T[16 ct + 4 lg + ii][16 R + li] = g[token][channel]
-                *reinterpret_cast<f32x4 *>(&s_g[(16 * R + li) * SG + 16 * ct + 4 * lg]) =
-                    f32x4{acc[0] * kLog2e, acc[1] * kLog2e, acc[2] * kLog2e, acc[3] * kLog2e};
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < RAWV; ++e) {
-                const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-                float x[VEC];
-                unpack16<BF>(rl[e], x);
-#pragma unroll
-                for (int s = 0; s < VEC; s += 4)     // log2 units: every factor is one exp2
-                    *reinterpret_cast<f32x4 *>(&s_g[r * SG + cv * VEC + s]) =
-                        f32x4{x[s] * kLog2e, x[s + 1] * kLog2e, x[s + 2] * kLog2e, x[s + 3] * kLog2e};
-            }
-            __syncthreads();
-            const int c = tid % DK, part = tid / DK;
-            float x[RPP];
-            float acc = 0.f;
-#pragma unroll
-            for (int rr = 0; rr < RPP; ++rr) {
-                acc += s_g[(part * RPP + rr) * SG + c];
-                x[rr] = acc;
-            }
-            s_part[part * DK + c] = acc;
-            __syncthreads();
-            float pre = 0.f;
-            for (int pp = 0; pp < part; ++pp) pre += s_part[pp * DK + c];
-#pragma unroll
-            for (int rr = 0; rr < RPP; ++rr) s_g[(part * RPP + rr) * SG + c] = x[rr] + pre;
-        }
-        __syncthreads();
-
-        // ---- phase 0b: per-channel factors, operand tiles, gamma.q ----
-        for (int idx = tid; idx < 14 * DK; idx += NT) {
-            const int c = idx % DK, kind = idx / DK;
-            if (kind < 4) {
-                s_fmid[kind * DK + c] = exp2_hw(s_g[(16 * kind + 7) * SG + c]);
-            } else if (kind < 8) {
-                const int I = kind - 4;
-                s_fkg[I * DK + c] = exp2_hw(s_g[(C - 1) * SG + c] - s_g[(16 * I + 7) * SG + c]);
-            } else {
-                const int pi = kind - 8;        // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-                const int R = pi < 1 ? 1 : (pi < 3 ? 2 : 3);
-                const int I = pi - R * (R - 1) / 2;
-                s_foff[pi * DK + c] = exp2_hw(s_g[(16 * R + 7) * SG + c] - s_g[(16 * I + 7) * SG + c]);
-            }
-        }
-        if (tid < DK) st_rec<NTR>(&reinterpret_cast<float *>(rec + R_::gC)[tid], exp2_hw(s_g[(C - 1) * SG + tid]));
-        __syncthreads();                         // s_fmid is read by the tile loop below
-        char *qgrec = rec + R_::Qg;
-#pragma unroll
-        for (int e = 0; e < RAWV; ++e) {
-            const int vi = tid + NT * e, r = vi / VK, cv = vi - r * VK;
-            const int c0 = cv * VEC, mid = ((r >> 4) * 16 + 7) * SG;
-            float kk[VEC], qq[VEC], bb[VEC], kh[VEC], qh[VEC], kb[VEC], qg[VEC];
-            unpack16<BF>(rk[e], kk);
-            unpack16<BF>(rq[e], qq);
-            unpack16<BF>(rb[e], bb);
-            if (p.qkn) {
-                // L2-norm of the q and k rows: the VK lanes holding row r are consecutive
-                // and aligned, so the row sums are butterflies over them
-                float sk = 0.f, sq = 0.f;
-#pragma unroll
-                for (int s = 0; s < VEC; ++s) {
-                    sk += kk[s] * kk[s];
-                    sq += qq[s] * qq[s];
-                }
-#pragma unroll
-                for (int off = 1; off < VK; off <<= 1) {
-                    sk += __shfl_xor(sk, off);
-                    sq += __shfl_xor(sq, off);
-                }
-                const float fk = rsqrtf(sk + p.l2eps), fq = rsqrtf(sq + p.l2eps);
-#pragma unroll
-                for (int s = 0; s < VEC; ++s) {
-                    kk[s] *= fk;
-                    qq[s] *= fq;
-                }
-            }
-            if (fg2) {                              // k <- sqrt(beta) k, b <- 1
-#pragma unroll
-                for (int s = 0; s < VEC; ++s) {
-                    kk[s] *= sqrt_hw(bb[s]);
-                    bb[s] = 1.f;
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < VEC; ++s) {
-                const float gr = s_g[r * SG + c0 + s], gm = s_g[mid + c0 + s];
-                const float ef = exp2_hw(gr - gm), ei = exp2_hw(gm - gr);
-                kh[s] = bb[s] * kk[s] * ef;
-                qh[s] = qq[s] * ef;
-                kb[s] = kk[s] * ei;
-                qg[s] = qh[s] * s_fmid[(r >> 4) * DK + c0 + s];   // q exp(g_r)
-            }
-            *reinterpret_cast<u32x4 *>(&s_kh[r * SK + c0]) = pack16<BF>(kh);
-            *reinterpret_cast<u32x4 *>(&s_qh[r * SK + c0]) = pack16<BF>(qh);
-            *reinterpret_cast<u32x4 *>(&s_kb[r * SK + c0]) = pack16<BF>(kb);
-            // gamma.q in K2's fragment order: row tile r/16, k tile c/KT, lane 16 lg + r%16
-            if constexpr (BF) {
-#pragma unroll
-                for (int j4 = 0; j4 < 2; ++j4) {
-                    const int c = c0 + 4 * j4, kt = c / 32, q4 = c % 32;
-                    const int half = q4 >= 16 ? 1 : 0, lgq = (q4 & 15) >> 2;
-                    const size_t slot = ((static_cast<size_t>(r >> 4) * NKD + kt) * 64 + 16 * lgq +
-                                         (r & 15)) * 2 + half;
-                    st_rec<NTR>(&reinterpret_cast<u32x2 *>(qgrec)[slot],
-                                u32x2{pack_bf16x2(qg[4 * j4], qg[4 * j4 + 1]),
-                                      pack_bf16x2(qg[4 * j4 + 2], qg[4 * j4 + 3])});
-                }
-            } else {
-                const int kt = c0 / 16, lgq = (c0 & 15) >> 2;
-                st_rec<NTR>(&reinterpret_cast<f32x4 *>(qgrec)[((r >> 4) * NKD + kt) * 64 + 16 * lgq + (r & 15)],
-                            f32x4{qg[0], qg[1], qg[2], qg[3]});
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < RAWW; ++e) {
-            const int vi = tid + NT * e, r = vi / VV, cv = vi - r * VV;
-            float ww[VEC], vv[VEC], prod[VEC];
-            unpack16<BF>(rw[e], ww);
-            unpack16<BF>(rv[e], vv);
-#pragma unroll
-            for (int s = 0; s < VEC; ++s) prod[s] = (fg2 ? sqrt_hw(ww[s]) : ww[s]) * vv[s];
-            *reinterpret_cast<u32x4 *>(&s_wv[r * SV + cv * VEC]) = pack16<BF>(prod);
-        }
-        __syncthreads();
-        if (has_next) load_gate(nxt, lap, rl, la_scalar);   // next record's raw tiles: first part
-
-        // ---- phase 1: A^T and M^T blocks (R >= I); zero upper blocks of M ----
-        char *mrec = rec + R_::M;
-        // (R, I) block pairs: the six off-diagonal pairs (which also scale Kbar) go to six
-        // waves, the four cheaper diagonal pairs two each to the other two
-        static_assert(NW == 8, "pair schedule assumes eight waves");
-        for (int pr = wave; pr < 10; pr += NW) {
-            const int R = static_cast<int>((0x3233322110ull >> (4 * pr)) & 0xF);
-            const int I = static_cast<int>((0x3221010010ull >> (4 * pr)) & 0xF);
-            const bool diag = (R == I);
-            const int pi = diag ? 0 : R * (R - 1) / 2 + I;
-            const int ri = 16 * I + li;              // A operand: column-side token i
-            const int rr = 16 * R + li;              // B operand: row-side token r
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = accA;
-#pragma unroll
-            for (int kt = 0; kt < DK / KT; ++kt) {
-                const int c0 = kt * KT + KS * lg;
-                u32x4 kb = *reinterpret_cast<const u32x4 *>(&s_kb[ri * SK + c0]);
-                if (!diag) {
-                    float x[KS];
-                    unpack16<BF>(kb, x);
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) x[s] *= s_foff[pi * DK + c0 + s];
-                    kb = pack16<BF>(x);
-                }
-                const u32x4 kh = *reinterpret_cast<const u32x4 *>(&s_kh[rr * SK + c0]);
-                const u32x4 qh = *reinterpret_cast<const u32x4 *>(&s_qh[rr * SK + c0]);
-                if constexpr (BF) {
-                    accA = mma_k32(kb, kh, accA);
-                    accM = mma_k32(kb, qh, accM);
-                } else {
-                    const f32x4 a = __builtin_bit_cast(f32x4, kb);
-                    accA = mma_k16_f32(a, __builtin_bit_cast(f32x4, kh), accA);
-                    accM = mma_k16_f32(a, __builtin_bit_cast(f32x4, qh), accM);
-                }
-            }
-            // lane holds A[r = 16R + li][i = 16I + 4 lg + ii] (and M)
-            f32x4 a4, m4;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int il = 4 * lg + ii;
-                a4[ii] = (diag && il >= li) ? 0.f : accA[ii];
-                m4[ii] = (diag && il > li) ? 0.f : accM[ii];
-            }
-            *reinterpret_cast<f32x4 *>(&s_A[rr * SA + 16 * I + 4 * lg]) = a4;
-            if constexpr (BF) {
-                st_rec<NTR>(&reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)],
-                            f4_to_b16(m4));
-            } else {
-                st_rec<NTR>(&reinterpret_cast<f32x4 *>(mrec)[(R * NKC + I) * 64 + lane], m4);
-            }
-        }
-        for (int u = wave; u < 6; u += NW) {
-            // (R, I) with I > R, in the order (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-            const int R2 = u < 3 ? 0 : (u < 5 ? 1 : 2);
-            const int I2 = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
-            if constexpr (BF) {
-                const u32x2 z = {0u, 0u};
-                st_rec<NTR>(&reinterpret_cast<u32x2 *>(mrec)[(((R2 * NKC + (I2 >> 1)) * 64 + lane) << 1) + (I2 & 1)], z);
-            } else {
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                st_rec<NTR>(&reinterpret_cast<f32x4 *>(mrec)[(R2 * NKC + I2) * 64 + lane], z);
-            }
-        }
-        __syncthreads();
-
-        // ---- phase 2a: diagonal inverses (wave 0) || KgT (waves 1-7) ----
-        if (has_next) load_qk(nxt);
-        if (wave == 0) {
-            const int R = lane >> 4, jc = lane & 15;      // column jc of T_RR
-            const float *Ab = &s_A[16 * R * SA + 16 * R];
-            // column jc of (I + A_RR)^{-1} by forward substitution, right-looking: once x[m]
-            // is known it is folded into every later row's sum, so the dependent chain is
-            // one FMA per row
-            float x[16], acc[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                x[m] = m == jc ? 1.f : (m > jc ? -acc[m] : 0.f);
-#pragma unroll
-                for (int r = m + 1; r < 16; ++r) acc[r] += Ab[r * SA + m] * x[m];
-            }
-            float *Tb = &s_T[16 * R * SA + 16 * R];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Tb[r * SA + jc] = x[r];
-        } else if constexpr (BF) {
-            // KgT fragment (channel rows 16 rt + li, tokens in perm order) by transpose reads
-            // of Kbar: half h holds tokens 32 kt + 16 h + 4 lg + a, a = 0..3
-            constexpr int NBK = (DK / 16) * NKC;
-            u32x4 *kg = reinterpret_cast<u32x4 *>(rec + R_::KgT);
-            for (int b2 = wave - 1; b2 < NBK; b2 += NW - 1) {
-                const int rt = b2 / NKC, kt = b2 - rt * NKC;
-                const int ch = 16 * rt + li;
-                float vals[8];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int k0 = kt * 32 + 16 * h + 4 * lg;
-                    const u32x2 t = lds_tr4(&s_kb[(k0 + (li >> 2)) * SK + 16 * rt + 4 * (li & 3)]);
-                    const float f = s_fkg[(2 * kt + h) * DK + ch];
-                    vals[4 * h + 0] = bf16_lo(t.x) * f;
-                    vals[4 * h + 1] = bf16_hi(t.x) * f;
-                    vals[4 * h + 2] = bf16_lo(t.y) * f;
-                    vals[4 * h + 3] = bf16_hi(t.y) * f;
-                }
-                st_rec<NTR>(&kg[b2 * 64 + lane], pack16<true>(vals));
-            }
-        } else {
-            constexpr int NBK = (DK / 16) * NKC;            // KgT blocks
-            constexpr int EPL = Op<BF>::EPL;
-            u32x4 *kg = reinterpret_cast<u32x4 *>(rec + R_::KgT);
-            for (int idx = tid - 64; idx < NBK * 64; idx += NT - 64) {
-                const int b2 = idx >> 6, l = idx & 63, lli = l & 15, llg = l >> 4;
-                const int rt = b2 / NKC, kt = b2 - rt * NKC;
-                const int ch = 16 * rt + lli;
-                float vals[EPL];
-#pragma unroll
-                for (int jj = 0; jj < EPL; ++jj) {
-                    const int tok = kt * KT + perm_k<BF>(llg, jj);
-                    vals[jj] = io<T>::ld(&s_kb[tok * SK + ch]) * s_fkg[(tok >> 4) * DK + ch];
-                }
-                st_rec<NTR>(&kg[b2 * 64 + l], pack16<BF>(vals));
-            }
-        }
-        __syncthreads();
-
-        // ---- phase 2b: off-diagonal blocks of T by levels d = R - I ----
-        if (has_next) {
-            load_gate(nxt, bp, rb, b_scalar);
-            load_wv(nxt);
-        }
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            if (wave < 4 - d) {
-                const int R = d + wave, I = R - d;
-                f32x4 P = {0.f, 0.f, 0.f, 0.f};
-                for (int m = I; m < R; ++m) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(&s_A[(16 * R + li) * SA + 16 * m + 4 * lg]);
-                    f32x4 bT;                      // B operand: T_mI[4 lg + s][li]
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) bT[s] = s_T[(16 * m + 4 * lg + s) * SA + 16 * I + li];
-                    P = mma_k16_f32(a, bT, P);
-                }
-                const f32x4 tRR = *reinterpret_cast<const f32x4 *>(&s_T[(16 * R + li) * SA + 16 * R + 4 * lg]);
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 Tn = mma_k16_f32(tRR, P, zero);   // lane: (T_RR P)[4 lg + ii][li]
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) s_T[(16 * R + 4 * lg + ii) * SA + 16 * I + li] = -Tn[ii];
-            }
-            __syncthreads();
-        }
-        if constexpr (BF) {
-            // bf16 copy of T (zero above the block diagonal) in the s_A space, read by phase 3
-            bf16_t *s_Tb = reinterpret_cast<bf16_t *>(s_A);
-            for (int idx = tid; idx < C * C / 8; idx += NT) {
-                const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
-                float t8[8];
-                const bool live = (c8 >> 4) <= (r >> 4);
-#pragma unroll
-                for (int e = 0; e < 8; e += 4) {
-                    const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s_T[r * SA + c8 + e]);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) t8[e + q] = live ? t4[q] : 0.f;
-                }
-                *reinterpret_cast<u32x4 *>(&s_Tb[r * STB + c8]) = pack16<true>(t8);
-            }
-            __syncthreads();
-        }
-
-        // ---- phase 3: W~^T = X^T T^T (X = gamma.b.k) and U~ = T (w.v) ----
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            const bool isW = which == 0;
-            if (wave >= (isW ? DK : DV) / 16) continue;
-            const int ct = wave;
-            const int c = 16 * ct + li;
-            float xv[NKTC][KS];
-            u32x4 xb[NKTC];                  // bf16: tokens 32 kt + 8 lg .. + 7 of column c
-            if constexpr (BF) {
-                const T *tile = isW ? s_kh : s_wv;
-                const int ld = isW ? SK : SV;
-#pragma unroll
-                for (int kt = 0; kt < NKTC; ++kt) {
-                    const int k0 = kt * 32 + 8 * lg + (li >> 2);
-                    const u32x2 lo = lds_tr4(&tile[k0 * ld + 16 * ct + 4 * (li & 3)]);
-                    const u32x2 hi = lds_tr4(&tile[(k0 + 4) * ld + 16 * ct + 4 * (li & 3)]);
-                    xb[kt] = u32x4{lo.x, lo.y, hi.x, hi.y};
-                    if (isW) {                   // X = Khat exp(Mid): one block per 8 tokens
-                        const float f = s_fmid[(2 * kt + (lg >> 1)) * DK + c];
-                        float x8[8];
-                        unpack16<true>(xb[kt], x8);
-#pragma unroll
-                        for (int s = 0; s < 8; ++s) x8[s] *= f;
-                        xb[kt] = pack16<true>(x8);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < NKTC; ++kt)
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) {
-                        const int tok = kt * KT + KS * lg + s;
-                        xv[kt][s] = isW ? io<T>::ld(&s_kh[tok * SK + c]) * s_fmid[(tok >> 4) * DK + c]
-                                        : io<T>::ld(&s_wv[tok * SV + c]);
-                    }
-            }
-#pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kt = 0; kt < NKTC; ++kt) {
-                    if (kt * KT > 16 * R + 15) break;
-                    // T[16R + li][kt*KT + KS*lg + s]; the KS tokens share one 16-block
-                    const int tok0 = kt * KT + KS * lg;
-                    if constexpr (BF) {
-                        const u32x4 tb = *reinterpret_cast<const u32x4 *>(
-                            &reinterpret_cast<const bf16_t *>(s_A)[(16 * R + li) * STB + tok0]);
-                        if (isW) acc = mma_k32(xb[kt], tb, acc);
-                        else acc = mma_k32(tb, xb[kt], acc);
-                    } else {
-                        float tv[KS];
-                        const bool live = (tok0 >> 4) <= R;
-#pragma unroll
-                        for (int s = 0; s < KS; s += 4) {
-                            const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s_T[(16 * R + li) * SA + tok0 + s]);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) tv[s + e] = live ? t4[e] : 0.f;
-                        }
-#pragma unroll
-                        for (int s = 0; s < 4; ++s)
-                            acc = isW ? __builtin_amdgcn_mfma_f32_16x16x4f32(xv[kt][s], tv[s], acc, 0, 0, 0)
-                                      : __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s], xv[kt][s], acc, 0, 0, 0);
-                    }
-                }
-                if (isW) {
-                    // lane: W~[16R + li][16 ct + 4 lg + ii] -> -W~ in K2's fragment order
-                    const f32x4 wn = -acc;
-                    char *wr = rec + R_::Wn;
-                    if constexpr (BF) {
-                        st_rec<NTR>(&reinterpret_cast<u32x2 *>(wr)[(((R * NKD + (ct >> 1)) * 64 + lane) << 1) +
-                                                                   (ct & 1)], f4_to_b16(wn));
-                    } else {
-                        st_rec<NTR>(&reinterpret_cast<f32x4 *>(wr)[(R * NKD + ct) * 64 + lane], wn);
-                    }
-                } else {
-                    // lane: U~[16R + 4 lg + ii][16 ct + li], an output tile (D layout)
-                    char *ut = rec + R_::Ut + (static_cast<size_t>(ct) * 4 + R) * R_::UT_TILE;
-                    if constexpr (BF) st_rec<NTR>(&reinterpret_cast<u32x2 *>(ut)[lane], f4_to_b16(acc));
-                    else st_rec<NTR>(&reinterpret_cast<f32x4 *>(ut)[lane], acc);
-                }
-            }
-        }
-        __syncthreads();                       // LDS is reused by the next record
-        cur = nxt;
     }
 }
 
@@ -1447,10 +845,6 @@ static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v, bool 
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Records beyond the last-level cache size (MALL, 256 MB on MI355X) are written with
-// non-temporal stores.
-constexpr size_t kStreamRecordBytes = static_cast<size_t>(256) << 20;
-
 // Segment buffers: fp32 start states of segments 0 and 1 [pair][2][d_k][d_v], transitions
 // [pair][nseg-2] (d_k x d_k as matrix-core fragments, 4 bytes per element) and fp32
 // zero-start end states [pair][nseg-2][d_k][d_v]
@@ -1489,21 +883,6 @@ size_t chunk_workspace_bytes(int chunk, int batch, int seqlen, int num_seqs, int
 
 bool chunk_size_built(int chunk) { return chunk == 32 || chunk == 64 || chunk == 128; }
 
-// Compute units of the current device (the persistent prep kernel runs one workgroup per
-// CU). Queried once per device and cached.
-static int device_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        cached[dev] = cus;
-    }
-    return cached[dev];
-}
 
 template <typename T, bool BF, int DK, int DV, int NW>
 static hipError_t launch_state(ChunkParams p, int64_t units, hipStream_t st) {
@@ -1554,25 +933,9 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(64), 0, st, a.cu_seqlens,
                            reinterpret_cast<int32_t *>(a.workspace), N, kChunk);
     }
-    const int64_t nchunks = nrec;
-    if (nchunks > 0) {
-        const int64_t items = nchunks * a.h_v;
-        const int grid = static_cast<int>(items < device_cu_count() ? items : device_cu_count());
-        const bool ntr = static_cast<size_t>(items) * Rec<kChunk, DK, DV, BF>::bytes > kStreamRecordBytes;
-        // (the gate-mode instances keep the default stores at every size: fewer instances)
-        const dim3 g3(grid), b3(512);
-        switch (p.gmode) {
-        case GATES_KDA: hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_KDA>), g3, b3, 0, st, p); break;
-        case GATES_GDN: hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_GDN>), g3, b3, 0, st, p); break;
-        case GATES_FG2_PLUS: hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_FG2_PLUS>), g3, b3, 0, st, p); break;
-        case GATES_FG2:                       // d_v = d_k (refused otherwise before the launch)
-            if constexpr (DK == DV) hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_FG2>), g3, b3, 0, st, p);
-            else return hipErrorInvalidValue;
-            break;
-        default:
-            if (ntr) hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, true, GATES_GDN2>), g3, b3, 0, st, p);
-            else hipLaunchKernelGGL((chunk_prep_kernel<T, BF, DK, DV, false, GATES_GDN2>), g3, b3, 0, st, p);
-        }
+    if (nrec > 0) {
+        const hipError_t e = launch_prep(p, kChunk, DK, DV, BF, nrec * a.h_v, st);
+        if (e != hipSuccess) return e;
     }
     const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
     if (p.nseg > 1 && p.num_pairs > 0) {

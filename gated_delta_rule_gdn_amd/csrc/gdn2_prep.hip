@@ -62,31 +62,41 @@ __device__ __forceinline__ float row_scan16(float x) {
     return x;
 }
 
-template <typename T, bool BF, int C, int DK, int DV, int GM>
-__global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParams p) {
+// NWV waves per workgroup; CPR channel blocks (matrix-core k tiles) per round. Every item of
+// a round is one 16-token sub-chunk x one channel block; item it of round r covers
+// sub-chunk it % NS and block r CPR + it / NS, and wave w takes items w, w + NWV, ...
+template <typename T, bool BF, int C, int DK, int DV, int GM, int NWV, int CPR, bool NTR>
+__global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
     using R_ = Rec<C, DK, DV, BF>;
+    constexpr int NT = 64 * NWV;
     constexpr int NS = C / 16;                 // 16-token sub-chunks
     constexpr int VEC = 16 / sizeof(T);        // elements per 16-byte vector
-    constexpr int CB = 4 * VEC;                // channels per round: one k tile
+    constexpr int CB = 4 * VEC;                // channels per block: one k tile
     constexpr int KT = Op<BF>::KT;
-    static_assert(KT == CB, "a round is one matrix-core k tile");
+    static_assert(KT == CB, "a channel block is one matrix-core k tile");
     constexpr int NJ = DK / CB, NJV = DV / CB;
-    constexpr int NSW = (NS + 3) / 4;          // sub-chunks per wave
+    static_assert(NJ % CPR == 0 && NJV % CPR == 0, "whole rounds");
+    constexpr int NR = NJ / CPR, NRV = NJV / CPR;   // key and value rounds
+    constexpr int IPR = NS * CPR;              // items per round
+    constexpr int IPW = (IPR + NWV - 1) / NWV; // items per wave per round (at most)
     constexpr int NPAIR = NS * (NS + 1) / 2, NOFF = NS * (NS - 1) / 2;
-    constexpr int PPW = (NPAIR + 3) / 4;       // block pairs per wave (at most)
-    constexpr int SB = CB + VEC;               // tile row stride (elements), 16 B of padding
+    constexpr int PPW = (NPAIR + NWV - 1) / NWV;    // block pairs per wave (at most)
+    constexpr int RW = CPR * CB;               // channels per round
+    constexpr int SB = RW + VEC;               // tile row stride (elements), 16 B of padding
     constexpr int TILE = C * SB;
-    constexpr bool DBUF = C <= 64;             // double-buffered round tiles
+    constexpr bool DBUF = C <= 64 && NWV == 4; // double-buffered round tiles
     constexpr int NBUF = DBUF ? 2 : 1;
     constexpr int BSTR = 20, BS = 16 * BSTR;   // fp32 16x16 block: row stride, size (floats)
     constexpr int NKD = R_::NKT_DK, NKC = R_::NKT_C;
-    constexpr int CT = CB / 16;                // 16-channel tiles per round
+    constexpr int CT = CB / 16;                // 16-channel tiles per block
+    constexpr int RCT = CPR * CT;              // 16-channel tiles per round
     constexpr int STB = C + 8;                 // row stride of the bf16 copy of T
     constexpr bool b_scalar = GM == GATES_KDA || GM == GATES_GDN;
     constexpr bool la_scalar = GM == GATES_GDN;
     constexpr bool fg2 = GM == GATES_FG2 || GM == GATES_FG2_PLUS;
     static_assert(NBUF * 3 * TILE >= 2 * TILE, "two X / w.v tiles fit in the round tiles");
     static_assert(!BF || C * STB * 2 <= NPAIR * BS * 4, "bf16 T fits over A");
+    static_assert(NWV % RCT == 0, "the WY rounds deal whole channel tiles to the waves");
 
     __shared__ float s_tot[NS * DK];           // sum of the log2 decay over each sub-chunk
     __shared__ float s_cmid[NS * DK];          // in-sub-chunk cumsum at its middle token
@@ -113,10 +123,14 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
     const T *bp = static_cast<const T *>(p.b), *lap = static_cast<const T *>(p.log_alpha);
     const T *vp = static_cast<const T *>(p.v), *wp = static_cast<const T *>(p.w);
 
-    // rows of this lane: token 16 R_s + t of sub-chunk R_s = wave + 4 s
-    auto subR = [&](int s) { return wave + 4 * s; };
-    auto row_ok = [&](int s) { return subR(s) < NS && 16 * subR(s) + t < L; };
-    auto tok = [&](int s) { return t0 + 16 * subR(s) + t; };
+    // item m of this wave in a round: its index in the round (valid when < IPR), sub-chunk
+    // and channel block within the round
+    auto it_of = [&](int m) { return wave + NWV * m; };
+    auto live = [&](int m) { return it_of(m) < IPR; };
+    auto subR = [&](int m) { return it_of(m) % NS; };
+    auto blk = [&](int m) { return it_of(m) / NS; };
+    auto row_ok = [&](int m) { return live(m) && 16 * subR(m) + t < L; };
+    auto tok = [&](int m) { return t0 + 16 * subR(m) + t; };
     auto bcast = [](const T *x) {      // a 16-byte vector of VEC copies of one element
         uint32_t u;
         if constexpr (sizeof(T) == 4) u = __float_as_uint(io<T>::ld(x));
@@ -125,58 +139,64 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
     };
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-    // ---- k, q, b of a round (channels CB j + VEC gi ..), prefetched one round ahead ----
-    u32x4 rk[2][NSW], rq[2][NSW], rb[2][NSW];
-    auto load_round = [&](int j, int slot) {
+    // ---- k, q, b of a round, prefetched one round ahead ----
+    u32x4 rk[2][IPW], rq[2][IPW], rb[2][IPW];
+    auto load_round = [&](int r, int slot) {
 #pragma unroll
-        for (int s = 0; s < NSW; ++s) {
-            rk[slot][s] = zero4;
-            rq[slot][s] = zero4;
-            rb[slot][s] = zero4;
-            if (row_ok(s)) {
-                const size_t okq = (static_cast<size_t>(tok(s)) * p.h_k + hk) * DK + CB * j + VEC * gi;
-                rk[slot][s] = *reinterpret_cast<const u32x4 *>(kp + okq);
-                rq[slot][s] = *reinterpret_cast<const u32x4 *>(qp + okq);
+        for (int m = 0; m < IPW; ++m) {
+            rk[slot][m] = zero4;
+            rq[slot][m] = zero4;
+            rb[slot][m] = zero4;
+            if (row_ok(m)) {
+                const int c0 = CB * (r * CPR + blk(m)) + VEC * gi;
+                const size_t okq = (static_cast<size_t>(tok(m)) * p.h_k + hk) * DK + c0;
+                rk[slot][m] = *reinterpret_cast<const u32x4 *>(kp + okq);
+                rq[slot][m] = *reinterpret_cast<const u32x4 *>(qp + okq);
                 if constexpr (b_scalar)
-                    rb[slot][s] = bcast(bp + static_cast<size_t>(tok(s)) * p.h_v + h);
+                    rb[slot][m] = bcast(bp + static_cast<size_t>(tok(m)) * p.h_v + h);
                 else
-                    rb[slot][s] = *reinterpret_cast<const u32x4 *>(
-                        bp + (static_cast<size_t>(tok(s)) * p.h_v + h) * DK + CB * j + VEC * gi);
+                    rb[slot][m] = *reinterpret_cast<const u32x4 *>(
+                        bp + (static_cast<size_t>(tok(m)) * p.h_v + h) * DK + c0);
             }
         }
     };
     load_round(0, 0);
 
-    // ---- scan: in-sub-chunk cumulative log2 decay of every round's channels ----
-    float cs[NSW][NJ][VEC];
+    // ---- scan: in-sub-chunk cumulative log2 decay of every item of every round ----
+    float cs[NR][IPW][VEC];
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-        if (subR(s) >= NS) continue;               // uniform over the wave
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+        for (int m = 0; m < IPW; ++m) {
             u32x4 raw = zero4;
-            if (row_ok(s)) {
-                if constexpr (la_scalar) raw = bcast(lap + static_cast<size_t>(tok(s)) * p.h_v + h);
+            if (row_ok(m)) {
+                if constexpr (la_scalar) raw = bcast(lap + static_cast<size_t>(tok(m)) * p.h_v + h);
                 else raw = *reinterpret_cast<const u32x4 *>(
-                         lap + (static_cast<size_t>(tok(s)) * p.h_v + h) * DK + CB * j + VEC * gi);
+                         lap + (static_cast<size_t>(tok(m)) * p.h_v + h) * DK +
+                         CB * (r * CPR + blk(m)) + VEC * gi);
             }
-            unpack16<BF>(raw, cs[s][j]);
+            unpack16<BF>(raw, cs[r][m]);
         }
-    }
     // q/k L2-norm factors (a uniform branch): sums of squares over all d_k channels of the
-    // token, the VEC channels of each round in-lane, the four lane groups by butterflies
-    float fk[NSW], fq[NSW];
+    // token; a token's channels are spread over the items of one sub-chunk (in this wave
+    // and others), so the partial sums meet in LDS (s_A is free until the rounds end)
+    float fk[IPW], fq[IPW];
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) fk[s] = fq[s] = 1.f;
+    for (int m = 0; m < IPW; ++m) fk[m] = fq[m] = 1.f;
     if (p.qkn) {
+        float *s_nk = s_A, *s_nq = s_A + C;
+        for (int i = tid; i < 2 * C; i += NT) s_A[i] = 0.f;
+        lds_barrier();
 #pragma unroll
-        for (int s = 0; s < NSW; ++s) {
+        for (int m = 0; m < IPW; ++m) {
+            if (!live(m)) continue;
             float sk = 0.f, sq = 0.f;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
+            for (int r = 0; r < NR; ++r) {
                 u32x4 k4 = zero4, q4 = zero4;
-                if (row_ok(s)) {
-                    const size_t okq = (static_cast<size_t>(tok(s)) * p.h_k + hk) * DK + CB * j + VEC * gi;
+                if (row_ok(m)) {
+                    const size_t okq = (static_cast<size_t>(tok(m)) * p.h_k + hk) * DK +
+                                       CB * (r * CPR + blk(m)) + VEC * gi;
                     k4 = *reinterpret_cast<const u32x4 *>(kp + okq);
                     q4 = *reinterpret_cast<const u32x4 *>(qp + okq);
                 }
@@ -193,37 +213,45 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
             sk += __shfl_xor(sk, 32);
             sq += __shfl_xor(sq, 16);
             sq += __shfl_xor(sq, 32);
-            fk[s] = rsqrtf(sk + p.l2eps);
-            fq[s] = rsqrtf(sq + p.l2eps);
+            if (gi == 0) {
+                atomicAdd(&s_nk[16 * subR(m) + t], sk);
+                atomicAdd(&s_nq[16 * subR(m) + t], sq);
+            }
         }
+        lds_barrier();
+#pragma unroll
+        for (int m = 0; m < IPW; ++m) {
+            if (!live(m)) continue;
+            fk[m] = rsqrtf(s_nk[16 * subR(m) + t] + p.l2eps);
+            fq[m] = rsqrtf(s_nq[16 * subR(m) + t] + p.l2eps);
+        }
+        lds_barrier();                         // s_A is reused for A
     }
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-        if (subR(s) >= NS) continue;
-        const int R = subR(s);
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+        for (int m = 0; m < IPW; ++m) {
+            if (!live(m)) continue;            // uniform over the wave
+            const int R = subR(m), c0 = CB * (r * CPR + blk(m)) + VEC * gi;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) cs[s][j][e] = row_scan16(cs[s][j][e] * kLog2e);
-            const int c0 = CB * j + VEC * gi;
+            for (int e = 0; e < VEC; ++e) cs[r][m][e] = row_scan16(cs[r][m][e] * kLog2e);
             if (t == 15) {
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4)
                     *reinterpret_cast<f32x4 *>(&s_tot[R * DK + c0 + e]) =
-                        f32x4{cs[s][j][e], cs[s][j][e + 1], cs[s][j][e + 2], cs[s][j][e + 3]};
+                        f32x4{cs[r][m][e], cs[r][m][e + 1], cs[r][m][e + 2], cs[r][m][e + 3]};
             }
             if (t == 7) {
 #pragma unroll
                 for (int e = 0; e < VEC; e += 4)
                     *reinterpret_cast<f32x4 *>(&s_cmid[R * DK + c0 + e]) =
-                        f32x4{cs[s][j][e], cs[s][j][e + 1], cs[s][j][e + 2], cs[s][j][e + 3]};
+                        f32x4{cs[r][m][e], cs[r][m][e + 1], cs[r][m][e + 2], cs[r][m][e + 3]};
             }
         }
-    }
     lds_barrier();
 
     // ---- per-channel factors (one thread per channel) and gamma_C ----
-    for (int c = tid; c < DK; c += 256) {
+    for (int c = tid; c < DK; c += NT) {
         float gmid[NS];
         float run = 0.f;
 #pragma unroll
@@ -231,7 +259,7 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
             gmid[R] = run + s_cmid[R * DK + c];
             run += s_tot[R * DK + c];
         }
-        reinterpret_cast<float *>(rec + R_::gC)[c] = exp2_hw(run);
+        st_rec<NTR>(&reinterpret_cast<float *>(rec + R_::gC)[c], exp2_hw(run));
 #pragma unroll
         for (int R = 0; R < NS; ++R) s_fkg[R * DK + c] = exp2_hw(run - gmid[R]);
 #pragma unroll
@@ -242,27 +270,26 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
     }
     // this lane's values relative to its sub-chunk's middle token: cs <- c_r - c_mid
 #pragma unroll
-    for (int s = 0; s < NSW; ++s) {
-        if (subR(s) >= NS) continue;
-        const int R = subR(s);
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int m = 0; m < IPW; ++m) {
+            if (!live(m)) continue;
+            const int R = subR(m), c0 = CB * (r * CPR + blk(m)) + VEC * gi;
 #pragma unroll
             for (int e = 0; e < VEC; e += 4) {
-                const f32x4 cm = *reinterpret_cast<const f32x4 *>(&s_cmid[R * DK + CB * j + VEC * gi + e]);
+                const f32x4 cm = *reinterpret_cast<const f32x4 *>(&s_cmid[R * DK + c0 + e]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) cs[s][j][e + q] -= cm[q];
+                for (int q = 0; q < 4; ++q) cs[r][m][e + q] -= cm[q];
             }
-    }
-    // 2^(g at the middle token of sub-chunk R) for this lane's channels of round j (the same
-    // sums in the same order as the per-channel factors above)
-    auto fmid_of = [&](int R, int j, float *out) {
+        }
+    // 2^(g at the middle token of sub-chunk R) for channels c0 .. c0 + VEC - 1 (the same sums
+    // in the same order as the per-channel factors above)
+    auto fmid_of = [&](int R, int c0, float *out) {
 #pragma unroll
         for (int e = 0; e < VEC; e += 4) {
-            const int c = CB * j + VEC * gi + e;
             f32x4 run = {0.f, 0.f, 0.f, 0.f};
-            for (int R2 = 0; R2 < R; ++R2) run += *reinterpret_cast<const f32x4 *>(&s_tot[R2 * DK + c]);
-            const f32x4 cm = *reinterpret_cast<const f32x4 *>(&s_cmid[R * DK + c]);
+            for (int R2 = 0; R2 < R; ++R2) run += *reinterpret_cast<const f32x4 *>(&s_tot[R2 * DK + c0 + e]);
+            const f32x4 cm = *reinterpret_cast<const f32x4 *>(&s_cmid[R * DK + c0 + e]);
 #pragma unroll
             for (int q = 0; q < 4; ++q) out[e + q] = exp2_hw(run[q] + cm[q]);
         }
@@ -272,35 +299,36 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
     f32x4 accA[PPW], accM[PPW];
 #pragma unroll
     for (int pi = 0; pi < PPW; ++pi) accA[pi] = accM[pi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 X[NSW][NJ];                          // gamma . b . k of this lane, for the WY pass
+    u32x4 X[NR][IPW];                          // gamma . b . k of this lane, for the WY pass
     char *qgrec = rec + R_::Qg;
     u32x4 *kgrec = reinterpret_cast<u32x4 *>(rec + R_::KgT);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int slot = j & 1, buf = DBUF ? (j & 1) : 0;
-        if (j + 1 < NJ) load_round(j + 1, slot ^ 1);
+    for (int r = 0; r < NR; ++r) {
+        const int slot = r & 1, buf = DBUF ? (r & 1) : 0;
+        if (r + 1 < NR) load_round(r + 1, slot ^ 1);
         T *tkh = s_tile + buf * 3 * TILE, *tqh = tkh + TILE, *tkb = tkh + 2 * TILE;
         if constexpr (!DBUF) {
-            if (j > 0) lds_barrier();        // the previous round's products are done
+            if (r > 0) lds_barrier();          // the previous round's products are done
         }
 #pragma unroll
-        for (int s = 0; s < NSW; ++s) {
-            if (subR(s) >= NS) continue;
-            const int r = 16 * subR(s) + t;
+        for (int m = 0; m < IPW; ++m) {
+            if (!live(m)) continue;
+            const int R = subR(m), row = 16 * R + t, j = r * CPR + blk(m);
+            const int c0 = CB * j + VEC * gi;
             float kk[VEC], qq[VEC], bb[VEC], kh[VEC], qh[VEC], kb[VEC], xx[VEC], qg[VEC], fm[VEC];
-            fmid_of(subR(s), j, fm);
-            unpack16<BF>(rk[slot][s], kk);
-            unpack16<BF>(rq[slot][s], qq);
-            unpack16<BF>(rb[slot][s], bb);
+            fmid_of(R, c0, fm);
+            unpack16<BF>(rk[slot][m], kk);
+            unpack16<BF>(rq[slot][m], qq);
+            unpack16<BF>(rb[slot][m], bb);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                kk[e] *= fk[s];
-                qq[e] *= fq[s];
+                kk[e] *= fk[m];
+                qq[e] *= fq[m];
                 if constexpr (fg2) {           // k <- sqrt(beta) k, b <- 1
                     kk[e] *= sqrt_hw(bb[e]);
                     bb[e] = 1.f;
                 }
-                const float d = cs[s][j][e];
+                const float d = cs[r][m][e];
                 const float ef = exp2_hw(d), ei = exp2_hw(-d);
                 kh[e] = bb[e] * kk[e] * ef;
                 qh[e] = qq[e] * ef;
@@ -308,58 +336,62 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
                 xx[e] = kh[e] * fm[e];
                 qg[e] = qh[e] * fm[e];
             }
-            const int col = VEC * gi;
-            *reinterpret_cast<u32x4 *>(&tkh[r * SB + col]) = pack16<BF>(kh);
-            *reinterpret_cast<u32x4 *>(&tqh[r * SB + col]) = pack16<BF>(qh);
-            *reinterpret_cast<u32x4 *>(&tkb[r * SB + col]) = pack16<BF>(kb);
-            X[s][j] = pack16<BF>(xx);
-            // gamma . q in the record's fragment order: row tile r / 16, k tile j
+            const int col = CB * blk(m) + VEC * gi;    // column within the round's tiles
+            *reinterpret_cast<u32x4 *>(&tkh[row * SB + col]) = pack16<BF>(kh);
+            *reinterpret_cast<u32x4 *>(&tqh[row * SB + col]) = pack16<BF>(qh);
+            *reinterpret_cast<u32x4 *>(&tkb[row * SB + col]) = pack16<BF>(kb);
+            X[r][m] = pack16<BF>(xx);
+            // gamma . q in the record's fragment order: row tile row / 16, k tile j
             if constexpr (BF) {
 #pragma unroll
                 for (int h4 = 0; h4 < 2; ++h4) {
                     const int q4 = 8 * gi + 4 * h4, half = q4 >= 16 ? 1 : 0, lgq = (q4 & 15) >> 2;
-                    const size_t sl = ((static_cast<size_t>(r >> 4) * NKD + j) * 64 + 16 * lgq + (r & 15)) * 2 + half;
-                    reinterpret_cast<u32x2 *>(qgrec)[sl] =
-                        u32x2{pack_bf16x2(qg[4 * h4], qg[4 * h4 + 1]), pack_bf16x2(qg[4 * h4 + 2], qg[4 * h4 + 3])};
+                    const size_t sl = ((static_cast<size_t>(row >> 4) * NKD + j) * 64 + 16 * lgq + (row & 15)) * 2 + half;
+                    st_rec<NTR>(&reinterpret_cast<u32x2 *>(qgrec)[sl],
+                                u32x2{pack_bf16x2(qg[4 * h4], qg[4 * h4 + 1]), pack_bf16x2(qg[4 * h4 + 2], qg[4 * h4 + 3])});
                 }
             } else {
-                reinterpret_cast<f32x4 *>(qgrec)[((r >> 4) * NKD + j) * 64 + 16 * gi + (r & 15)] =
-                    f32x4{qg[0], qg[1], qg[2], qg[3]};
+                st_rec<NTR>(&reinterpret_cast<f32x4 *>(qgrec)[((row >> 4) * NKD + j) * 64 + 16 * gi + (row & 15)],
+                            f32x4{qg[0], qg[1], qg[2], qg[3]});
             }
         }
-        lds_barrier();                       // round j's tiles are written
-        // A^T and M^T of the block pairs (lane: A[16R + li][16I + 4 lg + ii])
+        lds_barrier();                         // round r's tiles are written
+        // A^T and M^T of the block pairs (lane: A[16R + li][16I + 4 lg + ii]), one k tile
+        // per block of the round
 #pragma unroll
         for (int pi = 0; pi < PPW; ++pi) {
-            const int idx = wave + 4 * pi;
+            const int idx = wave + NWV * pi;
             if (idx >= NPAIR) break;
             int R, I;
             pair_of(idx, NS, R, I);
-            u32x4 kbv = *reinterpret_cast<const u32x4 *>(&tkb[(16 * I + li) * SB + VEC * lg]);
-            if (R != I) {
-                const float *f = &s_foff[(R * (R - 1) / 2 + I) * DK + CB * j + VEC * lg];
-                float x[VEC];
-                unpack16<BF>(kbv, x);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) x[e] *= f[e];
-                kbv = pack16<BF>(x);
-            }
-            const u32x4 khv = *reinterpret_cast<const u32x4 *>(&tkh[(16 * R + li) * SB + VEC * lg]);
-            const u32x4 qhv = *reinterpret_cast<const u32x4 *>(&tqh[(16 * R + li) * SB + VEC * lg]);
-            if constexpr (BF) {
-                accA[pi] = mma_k32(kbv, khv, accA[pi]);
-                accM[pi] = mma_k32(kbv, qhv, accM[pi]);
-            } else {
-                const f32x4 a = __builtin_bit_cast(f32x4, kbv);
-                accA[pi] = mma_k16_f32(a, __builtin_bit_cast(f32x4, khv), accA[pi]);
-                accM[pi] = mma_k16_f32(a, __builtin_bit_cast(f32x4, qhv), accM[pi]);
+            for (int jl = 0; jl < CPR; ++jl) {
+                u32x4 kbv = *reinterpret_cast<const u32x4 *>(&tkb[(16 * I + li) * SB + CB * jl + VEC * lg]);
+                if (R != I) {
+                    const float *f = &s_foff[(R * (R - 1) / 2 + I) * DK + CB * (r * CPR + jl) + VEC * lg];
+                    float x[VEC];
+                    unpack16<BF>(kbv, x);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) x[e] *= f[e];
+                    kbv = pack16<BF>(x);
+                }
+                const u32x4 khv = *reinterpret_cast<const u32x4 *>(&tkh[(16 * R + li) * SB + CB * jl + VEC * lg]);
+                const u32x4 qhv = *reinterpret_cast<const u32x4 *>(&tqh[(16 * R + li) * SB + CB * jl + VEC * lg]);
+                if constexpr (BF) {
+                    accA[pi] = mma_k32(kbv, khv, accA[pi]);
+                    accM[pi] = mma_k32(kbv, qhv, accM[pi]);
+                } else {
+                    const f32x4 a = __builtin_bit_cast(f32x4, kbv);
+                    accA[pi] = mma_k16_f32(a, __builtin_bit_cast(f32x4, khv), accA[pi]);
+                    accM[pi] = mma_k16_f32(a, __builtin_bit_cast(f32x4, qhv), accM[pi]);
+                }
             }
         }
         // KgT fragments of this round's channel tiles: (channel tile, token k tile) blocks
-        for (int f = wave; f < CT * NKC; f += 4) {
-            const int ctl = f / NKC, kt = f - ctl * NKC;
-            const int rt = CT * j + ctl;                 // channel tile of the record
-            const int ch = CB * j + 16 * ctl + li;       // this lane's channel
+        for (int f = wave; f < RCT * NKC; f += NWV) {
+            const int ctl = f / NKC, kt = f - ctl * NKC;     // channel tile within the round
+            const int rt = RCT * r + ctl;                    // channel tile of the record
+            const int ch = 16 * rt + li;                     // this lane's channel
             float vals[Op<BF>::EPL];
             if constexpr (BF) {
 #pragma unroll
@@ -379,28 +411,29 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
                     vals[jj] = io<T>::ld(&tkb[tk * SB + 16 * ctl + li]) * s_fkg[(tk >> 4) * DK + ch];
                 }
             }
-            kgrec[(rt * NKC + kt) * 64 + lane] = pack16<BF>(vals);
+            st_rec<NTR>(&kgrec[(rt * NKC + kt) * 64 + lane], pack16<BF>(vals));
         }
     }
 
     // ---- w and v (issued now, consumed after the solve) ----
-    u32x4 rw[NSW][NJV], rv[NSW][NJV];
+    u32x4 rw[NRV][IPW], rv[NRV][IPW];
 #pragma unroll
-    for (int s = 0; s < NSW; ++s)
+    for (int r = 0; r < NRV; ++r)
 #pragma unroll
-        for (int jv = 0; jv < NJV; ++jv) {
-            rw[s][jv] = zero4;
-            rv[s][jv] = zero4;
-            if (row_ok(s)) {
-                const size_t ov = (static_cast<size_t>(tok(s)) * p.h_v + h) * DV + CB * jv + VEC * gi;
-                rv[s][jv] = *reinterpret_cast<const u32x4 *>(vp + ov);
+        for (int m = 0; m < IPW; ++m) {
+            rw[r][m] = zero4;
+            rv[r][m] = zero4;
+            if (row_ok(m)) {
+                const size_t ov = (static_cast<size_t>(tok(m)) * p.h_v + h) * DV +
+                                  CB * (r * CPR + blk(m)) + VEC * gi;
+                rv[r][m] = *reinterpret_cast<const u32x4 *>(vp + ov);
                 if constexpr (b_scalar) {
-                    rw[s][jv] = bcast(bp + static_cast<size_t>(tok(s)) * p.h_v + h);
+                    rw[r][m] = bcast(bp + static_cast<size_t>(tok(m)) * p.h_v + h);
                 } else if constexpr (GM == GATES_FG2) {
                     // beta [.., d_k] indexes like w [.., d_v] (d_v = d_k)
-                    rw[s][jv] = *reinterpret_cast<const u32x4 *>(bp + ov);
+                    rw[r][m] = *reinterpret_cast<const u32x4 *>(bp + ov);
                 } else {
-                    rw[s][jv] = *reinterpret_cast<const u32x4 *>(wp + ov);
+                    rw[r][m] = *reinterpret_cast<const u32x4 *>(wp + ov);
                 }
             }
         }
@@ -409,7 +442,7 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
     char *mrec = rec + R_::M;
 #pragma unroll
     for (int pi = 0; pi < PPW; ++pi) {
-        const int idx = wave + 4 * pi;
+        const int idx = wave + NWV * pi;
         if (idx >= NPAIR) break;
         int R, I;
         pair_of(idx, NS, R, I);
@@ -423,11 +456,11 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
         }
         *reinterpret_cast<f32x4 *>(&s_A[tri_blk(R, I) * BS + li * BSTR + 4 * lg]) = a4;
         if constexpr (BF) {
-            reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)] = f4_to_b16(m4);
+            st_rec<NTR>(&reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (I >> 1)) * 64 + lane) << 1) + (I & 1)], f4_to_b16(m4));
             if (dg && !(R & 1) && R + 1 < NS)    // the upper half of a k tile on the diagonal
-                reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (R >> 1)) * 64 + lane) << 1) + 1] = u32x2{0u, 0u};
+                st_rec<NTR>(&reinterpret_cast<u32x2 *>(mrec)[(((R * NKC + (R >> 1)) * 64 + lane) << 1) + 1], u32x2{0u, 0u});
         } else {
-            reinterpret_cast<f32x4 *>(mrec)[(R * NKC + I) * 64 + lane] = m4;
+            st_rec<NTR>(&reinterpret_cast<f32x4 *>(mrec)[(R * NKC + I) * 64 + lane], m4);
         }
     }
     lds_barrier();
@@ -453,7 +486,7 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
     // off-diagonal blocks by levels d = R - I: T_RI = -T_RR sum_{I <= m < R} A_Rm T_mI
 #pragma unroll
     for (int d = 1; d < NS; ++d) {
-        for (int b = wave; b < NS - d; b += 4) {
+        for (int b = wave; b < NS - d; b += NWV) {
             const int R = b + d, I = b;
             f32x4 P = {0.f, 0.f, 0.f, 0.f};
             for (int m = I; m < R; ++m) {
@@ -473,7 +506,7 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
     if constexpr (BF) {
         // bf16 copy of T, row-major [C][STB], zero above the diagonal blocks, over A
         bf16_t *s_Tb = reinterpret_cast<bf16_t *>(s_A);
-        for (int idx = tid; idx < C * C / 8; idx += 256) {
+        for (int idx = tid; idx < C * C / 8; idx += NT) {
             const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
             const int R = r >> 4, I = c8 >> 4;
             float t8[8];
@@ -489,38 +522,39 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
         }
     }
 
-    // ---- W~^T = X^T T^T per channel round, U~ = T (w.v) per value round ----
-    // wave roles: channel tile ctl = wave % CT within the round, row tiles R = wave / CT + k
-    // (4 / CT); with CT = 2 the even and the odd row tiles carry equal k ranges
-    const int ctl = wave % CT, rg = wave / CT;
-    constexpr int RSTEP = 4 / CT;
+    // ---- W~^T = X^T T^T per key round, U~ = T (w.v) per value round ----
+    // wave roles: channel tile ctl = wave % RCT of the round, row tiles R = wave / RCT + k
+    // (NWV / RCT); with two row-tile groups the even and the odd row tiles carry equal k
+    // ranges
+    const int ctl = wave % RCT, rg = wave / RCT;
+    constexpr int RSTEP = NWV / RCT;
     const bf16_t *s_Tb = reinterpret_cast<const bf16_t *>(s_A);
     char *wrec = rec + R_::Wn;
 #pragma unroll
-    for (int rnd = 0; rnd < NJ + NJV; ++rnd) {
-        const bool isW = rnd < NJ;
-        const int j = isW ? rnd : rnd - NJ;
+    for (int rnd = 0; rnd < NR + NRV; ++rnd) {
+        const bool isW = rnd < NR;
+        const int r = isW ? rnd : rnd - NR;
         T *xt = s_tile + (rnd & 1) * TILE;
-        // this lane's rows of X (W rounds) or of w.v (U rounds)
+        // this lane's rows of X (key rounds) or of w.v (value rounds)
 #pragma unroll
-        for (int s = 0; s < NSW; ++s) {
-            if (subR(s) >= NS) continue;
-            const int r = 16 * subR(s) + t;
+        for (int m = 0; m < IPW; ++m) {
+            if (!live(m)) continue;
+            const int row = 16 * subR(m) + t;
             u32x4 v4;
             if (isW) {
-                v4 = X[s][j < NJ ? j : 0];
+                v4 = X[r < NR ? r : 0][m];
             } else {
                 float ww[VEC], vv[VEC], pr[VEC];
-                unpack16<BF>(rw[s][j < NJV ? j : 0], ww);
-                unpack16<BF>(rv[s][j < NJV ? j : 0], vv);
+                unpack16<BF>(rw[r < NRV ? r : 0][m], ww);
+                unpack16<BF>(rv[r < NRV ? r : 0][m], vv);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) pr[e] = (fg2 ? sqrt_hw(ww[e]) : ww[e]) * vv[e];
                 v4 = pack16<BF>(pr);
             }
-            *reinterpret_cast<u32x4 *>(&xt[r * SB + VEC * gi]) = v4;
+            *reinterpret_cast<u32x4 *>(&xt[row * SB + CB * blk(m) + VEC * gi]) = v4;
         }
-        lds_barrier();                       // this round's tile (and, first time, T) is ready
-        const int ct = CT * j + ctl;           // channel (or value column) tile of the record
+        lds_barrier();                         // this round's tile (and, first time, T) is ready
+        const int ct = RCT * r + ctl;          // channel (or value column) tile of the record
         if constexpr (BF) {
             u32x4 xb[NKC];                     // k = tokens 32 kt + 8 lg + 0..7 of column 16 ctl + li
 #pragma unroll
@@ -539,11 +573,11 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
                     acc = isW ? mma_k32(xb[kt], tb, acc) : mma_k32(tb, xb[kt], acc);
                 }
                 if (isW) {   // lane: W~[16R + li][16 ct + 4 lg + ii] -> -W~ fragments
-                    reinterpret_cast<u32x2 *>(wrec)[(((R * NKD + (ct >> 1)) * 64 + lane) << 1) + (ct & 1)] =
-                        f4_to_b16(-acc);
+                    st_rec<NTR>(&reinterpret_cast<u32x2 *>(wrec)[(((R * NKD + (ct >> 1)) * 64 + lane) << 1) + (ct & 1)],
+                                f4_to_b16(-acc));
                 } else {     // lane: U~[16R + 4 lg + ii][16 ct + li], a D-layout tile
-                    reinterpret_cast<u32x2 *>(rec + R_::Ut + (static_cast<size_t>(ct) * NS + R) * R_::UT_TILE)[lane] =
-                        f4_to_b16(acc);
+                    st_rec<NTR>(&reinterpret_cast<u32x2 *>(rec + R_::Ut + (static_cast<size_t>(ct) * NS + R) * R_::UT_TILE)[lane],
+                                f4_to_b16(acc));
                 }
             }
         } else {
@@ -561,26 +595,44 @@ __global__ __launch_bounds__(256, (C <= 64 ? 2 : 1)) void prep_kernel(ChunkParam
                         acc = isW ? __builtin_amdgcn_mfma_f32_16x16x4f32(xv[kt][s2], tv[s2], acc, 0, 0, 0)
                                   : __builtin_amdgcn_mfma_f32_16x16x4f32(tv[s2], xv[kt][s2], acc, 0, 0, 0);
                 }
-                if (isW) reinterpret_cast<f32x4 *>(wrec)[(R * NKD + ct) * 64 + lane] = -acc;
-                else reinterpret_cast<f32x4 *>(rec + R_::Ut + (static_cast<size_t>(ct) * NS + R) * R_::UT_TILE)[lane] = acc;
+                if (isW) st_rec<NTR>(&reinterpret_cast<f32x4 *>(wrec)[(R * NKD + ct) * 64 + lane], -acc);
+                else st_rec<NTR>(&reinterpret_cast<f32x4 *>(rec + R_::Ut + (static_cast<size_t>(ct) * NS + R) * R_::UT_TILE)[lane], acc);
             }
         }
     }
 }
 
+// Waves per workgroup and channel blocks per round: eight waves over two blocks where a
+// round then gives every wave a sub-chunk (64-token chunks) and the LDS of two workgroups
+// still fits a CU; four waves over one block otherwise.
+template <bool BF, int C, int DK, int DV> struct PrepShape {
+    static constexpr int NJ = DK / (BF ? 32 : 16), NJV = DV / (BF ? 32 : 16);
+    static constexpr bool WIDE = C == 64 && NJ % 2 == 0 && NJV % 2 == 0;
+    static constexpr int NWV = WIDE ? 8 : 4, CPR = WIDE ? 2 : 1;
+};
+
+// Records beyond the last-level cache (MALL, 256 MB on MI355X) are written with
+// non-temporal stores (gate-mode instances keep the default stores: fewer instances).
+constexpr size_t kStreamRecordBytes = static_cast<size_t>(256) << 20;
+
 template <typename T, bool BF, int C, int DK, int DV>
 hipError_t launch_prep_t(const ChunkParams &p, int64_t items, hipStream_t st) {
     if (items <= 0) return hipSuccess;
-    const dim3 g(static_cast<unsigned>(items)), b(256);
+    using PS = PrepShape<BF, C, DK, DV>;
+    constexpr int W = PS::NWV, R = PS::CPR;
+    const dim3 g(static_cast<unsigned>(items)), b(64 * W);
+    const bool ntr = static_cast<size_t>(items) * Rec<C, DK, DV, BF>::bytes > kStreamRecordBytes;
     switch (p.gmode) {
-    case GATES_KDA: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_KDA>), g, b, 0, st, p); break;
-    case GATES_GDN: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN>), g, b, 0, st, p); break;
-    case GATES_FG2_PLUS: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2_PLUS>), g, b, 0, st, p); break;
+    case GATES_KDA: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_KDA, W, R, false>), g, b, 0, st, p); break;
+    case GATES_GDN: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN, W, R, false>), g, b, 0, st, p); break;
+    case GATES_FG2_PLUS: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2_PLUS, W, R, false>), g, b, 0, st, p); break;
     case GATES_FG2:
-        if constexpr (DK == DV) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2>), g, b, 0, st, p);
+        if constexpr (DK == DV) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2, W, R, false>), g, b, 0, st, p);
         else return hipErrorInvalidValue;
         break;
-    default: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2>), g, b, 0, st, p);
+    default:
+        if (ntr) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2, W, R, true>), g, b, 0, st, p);
+        else hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2, W, R, false>), g, b, 0, st, p);
     }
     return hipGetLastError();
 }
