@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(OUT_DIR, "libgdn2.so")
 SOURCES = ["gdn2_api.cpp", "gdn2_decode.hip", "gdn2_chunk.hip", "gdn2_gates.hip", "gdn2_bwd.hip",
-           "gdn2_noalloc.hip", "gdn2_prep.hip", "gdn2_state.hip"]
+           "gdn2_noalloc.hip", "gdn2_prep.hip", "gdn2_state.hip", "gdn2_bwd16.hip"]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of generated code (hipcc's host pass warns that it
 # does not know the feature; that warning is harmless).

@@ -890,6 +890,7 @@ hipError_t launch_bwd_dt(const BwdArgs &a, hipStream_t st) {
 
 size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
                                  bool bf16, bool packed) {
+    if (bf16) return chunk_bwd16_workspace_bytes(batch, seqlen, num_seqs, h_v, d_k, d_v, packed);
     const int64_t nrec = chunk_upper_bound(kChunk, batch, seqlen, num_seqs, packed) * h_v;
     // (the floats of BLay<d_k, d_v>)
     const size_t per = 4 * (14 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * d_v +
@@ -901,7 +902,7 @@ size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, i
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t st) {
-    return a.bf16 ? launch_bwd_dt<bf16_t>(a, st) : launch_bwd_dt<float>(a, st);
+    return a.bf16 ? launch_chunk_bwd16(a, st) : launch_bwd_dt<float>(a, st);
 }
 
 }  // namespace gdn2

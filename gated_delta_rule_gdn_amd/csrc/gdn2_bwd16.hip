@@ -1,0 +1,1040 @@
+// gdn2_bwd16.hip -- chunked backward of Gated DeltaNet-2 for bf16 inputs, on bf16 matrix
+// cores.
+//
+// The algebra is that of gdn2_bwd.hip: the chunked WY form of the burn-gdn2 docs page,
+// section "Architecture" (Chunk mode), differentiated chunk by chunk. Within a chunk of
+// C = 64 tokens entering with state S and leaving with S' (record operands of the chunked
+// forward: Wn = -W~, Qg = gamma.q, Kg = (gamma_C / gamma).k, M, U~, gamma_C; T = (I + A)^-1;
+// X = w.v, Y = gamma.b.k), given dO and dS' = dL/dS':
+//   dU = M^T dO + Kg dS',   dS = gamma_C dS' + Qg^T dO + Wn^T dU     (to the chunk before)
+//   U = U~ + Wn S,  dQg = dO S^T,  dW~ = -dU S^T,  dKg = U dS'^T,  dM = lower(dO U^T),
+//   dX = T^T dU,  dY = T^T dW~,  dT = dU X^T + dW~ Y^T,  dA = strictly-lower(-T^T dT T^T),
+// then the chain rule through the decay factors to q, k, b and log alpha.
+//
+// Every product here takes bf16 operands from LDS (or from the forward's records) and
+// accumulates in fp32; the reverse state pass keeps dS in fp32 registers. Kernels of one call:
+//   (forward re-run)    the chunked forward, also writing the state entering every chunk and
+//                       T of every record
+//   bwd_pre_kernel      per record: Kg and Wn^T as matrix-core fragments, E1 = M^T dO and
+//                       E2 = Qg^T dO, all from the forward's record and dO
+//   bwd_rchain_kernel   per (sequence, value head, 32 state columns), from the last chunk:
+//                       dU = E1 + Kg dS' and dS = gamma_C dS' + E2 + Wn^T dU; writes dS' and dU
+//                       of every chunk (bf16) and dS0 (fp32)
+//   bwd_g1_kernel       per record: U, dQg, dW~, dKg, dM, dX (-> dv, dw), dU X^T, and
+//                       dgamma_C = sum_col dS' . S
+//   bwd_g2_kernel       per record: dY, dT, dA, the decay sums, dq, dk, db and dlog_alpha
+#include "gdn2_chunk.h"
+
+namespace gdn2 {
+
+namespace {
+
+constexpr int C = 64;
+constexpr int NKC = C / 32;        // bf16 k tiles over the chunk
+constexpr int NRC = C / 16;        // 16-row tiles over the chunk
+
+// Row strides (bf16 elements) of LDS tiles with rows of 64 or 128 elements. The 16 rows of
+// a fragment read (8 bytes per lane) fall on distinct banks, and so do the four rows of a
+// transposing read.
+template <int K> struct Pad { static constexpr int S = K == 64 ? 72 : 152; };
+
+// Per-record buffers (bytes).
+template <int DK, int DV>
+struct BL16 {
+    // bwd_pre_kernel -> bwd_rchain_kernel
+    static constexpr size_t KgA = 0;                                      // Kg, A fragments [C][DK]
+    static constexpr size_t WnT = KgA + static_cast<size_t>(C) * DK * 2;  // Wn^T, A fragments [DK][C]
+    static constexpr size_t OPS = WnT + static_cast<size_t>(DK) * C * 2;
+    static constexpr size_t E1 = OPS;                                     // fp32 D tiles [slice][C/16]
+    static constexpr size_t E2 = E1 + static_cast<size_t>(C) * DV * 4;    // fp32 D tiles [slice][DK/16]
+    static constexpr size_t CREC = E2 + static_cast<size_t>(DK) * DV * 4;
+    // bwd_rchain_kernel -> bwd_g1_kernel, bf16 D tiles
+    static constexpr size_t DSN = 0;                                      // dS' [slice][DK/16]
+    static constexpr size_t DU = DSN + static_cast<size_t>(DK) * DV * 2;  // dU [slice][C/16]
+    static constexpr size_t COUT = DU + static_cast<size_t>(C) * DV * 2;
+    // bwd_g1_kernel -> bwd_g2_kernel; [C][DK] products as D tiles (row tile B, column tile ct)
+    // at B * DK/16 + ct, [C][C] ones at R * C/16 + I
+    static constexpr size_t DQG = 0;                                      // fp32
+    static constexpr size_t DKG = DQG + static_cast<size_t>(C) * DK * 4;  // fp32
+    static constexpr size_t DW = DKG + static_cast<size_t>(C) * DK * 4;   // bf16
+    static constexpr size_t DM = DW + static_cast<size_t>(C) * DK * 2;    // bf16
+    static constexpr size_t DT1 = DM + static_cast<size_t>(C) * C * 2;    // fp32
+    static constexpr size_t DGL = DT1 + static_cast<size_t>(C) * C * 4;   // fp32 [DK]
+    static constexpr size_t GIO = (DGL + DK * 4 + 255) / 256 * 256;
+};
+
+struct B16Params {
+    const bf16_t *q, *k, *v, *la, *b, *w, *dO;
+    const float *dS_T;                 // [N][h_v][DK][DV], or NULL
+    const int32_t *cu, *map;           // packed batches: offsets and chunk map, else NULL
+    const char *rec;                   // records of the forward re-run
+    const bf16_t *tmat;                // T per record, [C][C]
+    const float *ck;                   // state entering every chunk, [record][DK][DV]
+    char *crec, *cout, *gio;
+    float *dq, *dk, *dv, *dw, *dla, *db, *dS0;
+    int num_seqs, seqlen, nc_dense, h_k, h_v, group, num_pairs;
+};
+
+__device__ __forceinline__ bool locate16(const B16Params &p, int chunk, int &n, int &j,
+                                         int64_t &start, int64_t &end) {
+    if (p.cu == nullptr) {
+        n = chunk / p.nc_dense;
+        j = chunk - n * p.nc_dense;
+        start = static_cast<int64_t>(n) * p.seqlen;
+        end = start + p.seqlen;
+        return n < p.num_seqs;
+    }
+    if (chunk >= p.map[p.num_seqs]) return false;
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.map[mid] <= chunk) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    j = chunk - p.map[n];
+    start = p.cu[n];
+    end = p.cu[n + 1];
+    return true;
+}
+
+// Fragment (perm order, gdn2_mfma.h) whose k index runs along the columns of a row-major
+// bf16 LDS tile: lane (li, lg) receives t[r0 + li][k0 + perm(lg, jj)].
+__device__ __forceinline__ u32x4 row_frag(const bf16_t *t, int stride, int r0, int k0, int li, int lg) {
+    const bf16_t *q = t + (r0 + li) * stride + k0 + 4 * lg;
+    const u32x2 a = *reinterpret_cast<const u32x2 *>(q);
+    const u32x2 b = *reinterpret_cast<const u32x2 *>(q + 16);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+// Fragment whose k index runs along the rows: lane (li, lg) receives t[k0 + perm(lg, jj)][c0 + li]
+// (two transposing reads).
+__device__ __forceinline__ u32x4 col_frag(const bf16_t *t, int stride, int k0, int c0, int li, int lg) {
+    const bf16_t *q = t + (k0 + 4 * lg + (li >> 2)) * stride + c0 + 4 * (li & 3);
+    const u32x2 a = lds_tr4(q);
+    const u32x2 b = lds_tr4(q + 16 * stride);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+// An A fragment block of a record (16 rows x 32 k) back into a row-major tile.
+__device__ __forceinline__ void frag_to_rows(bf16_t *t, int stride, int r0, int k0, u32x4 f, int li, int lg) {
+    bf16_t *q = t + (r0 + li) * stride + k0 + 4 * lg;
+    *reinterpret_cast<u32x2 *>(q) = u32x2{f.x, f.y};
+    *reinterpret_cast<u32x2 *>(q + 16) = u32x2{f.z, f.w};
+}
+// One lane's part of a 16x16 output tile (rows r0 + 4 lg + ii, column c0 + li) into a
+// row-major bf16 tile, from fp32 or from bf16 already rounded.
+__device__ __forceinline__ void put_tile(bf16_t *t, int stride, int r0, int c0, f32x4 v, int li, int lg) {
+    bf16_t *q = t + (r0 + 4 * lg) * stride + c0 + li;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) q[ii * stride].bits = f32_to_bf16_bits(v[ii]);
+}
+__device__ __forceinline__ void put_tile16(bf16_t *t, int stride, int r0, int c0, u32x2 v, int li, int lg) {
+    bf16_t *q = t + (r0 + 4 * lg) * stride + c0 + li;
+    q[0].bits = static_cast<uint16_t>(v.x & 0xffffu);
+    q[stride].bits = static_cast<uint16_t>(v.x >> 16);
+    q[2 * stride].bits = static_cast<uint16_t>(v.y & 0xffffu);
+    q[3 * stride].bits = static_cast<uint16_t>(v.y >> 16);
+}
+__device__ __forceinline__ f32x4 b16_to_f4(u32x2 v) {
+    return f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+}
+__device__ __forceinline__ float f32of(const bf16_t *p) { return bf16_to_f32(p->bits); }
+// Four fp32 values as a bf16 operand hi = bf16(x) and its remainder lo = bf16(x - hi)
+// (hi + lo keeps about 16 significant bits).
+__device__ __forceinline__ void split4(const float (&x)[4], u32x2 &hi, u32x2 &lo) {
+    hi.x = pack_bf16x2(x[0], x[1]);
+    hi.y = pack_bf16x2(x[2], x[3]);
+    lo.x = pack_bf16x2(x[0] - bf16_lo(hi.x), x[1] - bf16_hi(hi.x));
+    lo.y = pack_bf16x2(x[2] - bf16_lo(hi.y), x[3] - bf16_hi(hi.y));
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_pre_kernel: per record, the reverse pass's operands. The forward record's Wn, Qg, KgT
+// and M fragments are put back into row-major LDS tiles (blocks of M above the diagonal,
+// which the forward never writes, as zeros); transposing reads then give the fragments of
+// Kg, Wn^T, M^T and Qg^T, and dO is staged the same way.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(B16Params p) {
+    using R_ = Rec<C, DK, DV, true>;
+    using L_ = BL16<DK, DV>;
+    constexpr int SK = Pad<DK>::S, SC = Pad<C>::S, SV = Pad<DV>::S;
+    constexpr int NKD = DK / 32, NRK = DK / 16, NSL = DV / 16;
+    constexpr int NBW = NRC * NKD, NBK = NRK * NKC, NBM = NRC * NKC, NOV = C * DV / 8 / 256;
+    static_assert(NBW % 4 == 0 && NBK % 4 == 0 && NBM % 4 == 0 && NOV >= 1, "even split");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    bf16_t *Wl = reinterpret_cast<bf16_t *>(smem);     // [C][SK]  Wn
+    bf16_t *Ql = Wl + C * SK;                          // [C][SK]  Qg
+    bf16_t *KTl = Ql + C * SK;                         // [DK][SC] KgT
+    bf16_t *Ml = KTl + DK * SC;                        // [C][SC]  M
+    bf16_t *Ol = Ml + C * SC;                          // [C][SV]  dO
+
+    const int item = blockIdx.x, chunk = item / p.h_v, h = item - chunk * p.h_v;
+    int n, j;
+    int64_t start, end;
+    if (!locate16(p, chunk, n, j, start, end)) return;
+    const int64_t t0 = start + static_cast<int64_t>(j) * C;
+    const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const char *rec = p.rec + static_cast<size_t>(item) * R_::bytes;
+    char *cr = p.crec + static_cast<size_t>(item) * L_::CREC;
+    const u32x4 *wn = reinterpret_cast<const u32x4 *>(rec + R_::Wn);
+    const u32x4 *qg = reinterpret_cast<const u32x4 *>(rec + R_::Qg);
+    const u32x4 *kgt = reinterpret_cast<const u32x4 *>(rec + R_::KgT);
+    const u32x4 *mm = reinterpret_cast<const u32x4 *>(rec + R_::M);
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    u32x4 fw[NBW / 4], fq[NBW / 4], fk[NBK / 4], fm[NBM / 4], fo[NOV];
+#pragma unroll
+    for (int i = 0; i < NBW / 4; ++i) {
+        fw[i] = wn[(wave + 4 * i) * 64 + lane];
+        fq[i] = qg[(wave + 4 * i) * 64 + lane];
+    }
+#pragma unroll
+    for (int i = 0; i < NBK / 4; ++i) fk[i] = kgt[(wave + 4 * i) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < NBM / 4; ++i) {
+        const int blk = wave + 4 * i, R = blk / NKC, kt = blk - R * NKC;
+        fm[i] = 32 * kt <= 16 * R + 15 ? mm[blk * 64 + lane] : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < NOV; ++i) {
+        const int e = tid + 256 * i, r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+        fo[i] = r < Lr ? *reinterpret_cast<const u32x4 *>(
+                             p.dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c8)
+                       : zero4;
+    }
+#pragma unroll
+    for (int i = 0; i < NBW / 4; ++i) {
+        const int blk = wave + 4 * i, rt = blk / NKD, kt = blk - rt * NKD;
+        frag_to_rows(Wl, SK, 16 * rt, 32 * kt, fw[i], li, lg);
+        frag_to_rows(Ql, SK, 16 * rt, 32 * kt, fq[i], li, lg);
+    }
+#pragma unroll
+    for (int i = 0; i < NBK / 4; ++i) {
+        const int blk = wave + 4 * i, rt = blk / NKC, kt = blk - rt * NKC;
+        frag_to_rows(KTl, SC, 16 * rt, 32 * kt, fk[i], li, lg);
+    }
+#pragma unroll
+    for (int i = 0; i < NBM / 4; ++i) {
+        const int blk = wave + 4 * i, R = blk / NKC, kt = blk - R * NKC;
+        frag_to_rows(Ml, SC, 16 * R, 32 * kt, fm[i], li, lg);
+    }
+#pragma unroll
+    for (int i = 0; i < NOV; ++i) {
+        const int e = tid + 256 * i, r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+        *reinterpret_cast<u32x4 *>(&Ol[r * SV + c8]) = fo[i];
+    }
+    lds_barrier();
+
+    // Kg (rows: tokens, k: channels) and Wn^T (rows: channels, k: tokens) fragments
+    u32x4 *kga = reinterpret_cast<u32x4 *>(cr + L_::KgA);
+    u32x4 *wnt = reinterpret_cast<u32x4 *>(cr + L_::WnT);
+    for (int blk = wave; blk < NRC * NKD; blk += 4) {
+        const int ut = blk / NKD, kt = blk - ut * NKD;
+        kga[blk * 64 + lane] = col_frag(KTl, SC, 32 * kt, 16 * ut, li, lg);
+    }
+    for (int blk = wave; blk < NRK * NKC; blk += 4) {
+        const int rt = blk / NKC, kt = blk - rt * NKC;
+        wnt[blk * 64 + lane] = col_frag(Wl, SK, 32 * kt, 16 * rt, li, lg);
+    }
+    // E1 = M^T dO and E2 = Qg^T dO, one 16-column value slice at a time
+    f32x4 *e1 = reinterpret_cast<f32x4 *>(cr + L_::E1);
+    f32x4 *e2 = reinterpret_cast<f32x4 *>(cr + L_::E2);
+    for (int s = wave; s < NSL; s += 4) {
+        u32x4 ob[NKC];
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt) ob[kt] = col_frag(Ol, SV, 32 * kt, 16 * s, li, lg);
+#pragma unroll
+        for (int ut = 0; ut < NRC; ++ut) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(col_frag(Ml, SC, 32 * kt, 16 * ut, li, lg), ob[kt], acc);
+            e1[(s * NRC + ut) * 64 + lane] = acc;
+        }
+#pragma unroll
+        for (int rt = 0; rt < NRK; ++rt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(col_frag(Ql, SK, 32 * kt, 16 * rt, li, lg), ob[kt], acc);
+            e2[(s * NRK + rt) * 64 + lane] = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_rchain_kernel: the reverse state pass. A workgroup owns NWS 16-column slices of dS of
+// one (sequence, value head): one chain wave per slice holds its d_k x 16 slice in fp32
+// registers, and two copy waves stage each chunk's Kg and Wn^T fragments, gamma_C and the
+// slices' E1 and E2 tiles in LDS one chunk ahead (double-buffered, direct global-to-LDS
+// loads). The chain waves issue no global loads, so they never wait on memory: their stores
+// of dS' and dU stay in flight. The workgroups of one (sequence, head) are placed on one XCD
+// (blocks are dispatched to the XCDs round-robin), where they share the records in L2.
+template <int DK, int DV, int NWS>
+struct RChain {
+    static constexpr int NCP = 2;
+    static constexpr int OPS = static_cast<int>(BL16<DK, DV>::OPS);
+    static constexpr int EB = (C + DK) * 16 * 4;            // E1 and E2 tiles of one slice
+    static constexpr int STAGE = OPS + DK * 4 + NWS * EB;
+    static constexpr int LDS = 2 * STAGE;
+    static constexpr int G = DV / 16 / NWS;                 // workgroups per (sequence, head)
+};
+
+template <int DK, int DV, int NWS>
+__global__ __launch_bounds__(64 * (NWS + 2)) void bwd_rchain_kernel(B16Params p) {
+    using R_ = Rec<C, DK, DV, true>;
+    using L_ = BL16<DK, DV>;
+    using RC = RChain<DK, DV, NWS>;
+    constexpr int RT = DK / 16, NKD = DK / 32, NCP = RC::NCP, OPS = RC::OPS, EB = RC::EB;
+    constexpr int STAGE = RC::STAGE, G = RC::G;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int bid = blockIdx.x, idx = bid >> 3;
+    const int pair = (idx / G) * 8 + (bid & 7), part = idx - (idx / G) * G;
+    if (pair >= p.num_pairs) return;                        // uniform over the workgroup
+    const int n = pair / p.h_v, h = pair - n * p.h_v;
+    int64_t start, end;
+    int cbase;
+    if (p.cu == nullptr) {
+        start = static_cast<int64_t>(n) * p.seqlen;
+        end = start + p.seqlen;
+        cbase = n * p.nc_dense;
+    } else {
+        start = p.cu[n];
+        end = p.cu[n + 1];
+        cbase = p.map[n];
+    }
+    const int nchunks = static_cast<int>((end - start + C - 1) / C);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    const bool chain = wave < NWS;
+    const int s = part * NWS + wave;                        // value slice of a chain wave
+    auto recno = [&](int c) { return static_cast<size_t>(cbase + c) * p.h_v + h; };
+    auto stage = [&](int c, char *dst) {                    // copy waves
+        const int cw = wave - NWS;
+        const char *cr = p.crec + recno(c) * L_::CREC;
+        for (int blk = cw; blk < OPS / 1024; blk += NCP) dma16(cr + blk * 1024 + lane * 16, dst + blk * 1024);
+        if (cw == 0 && lane < DK / 4)
+            dma16(p.rec + recno(c) * R_::bytes + R_::gC + lane * 16, dst + OPS);
+#pragma unroll
+        for (int q = 0; q < NWS; ++q) {
+            const int sl = part * NWS + q;
+            const char *e1 = cr + L_::E1 + static_cast<size_t>(sl) * NRC * 1024;
+            const char *e2 = cr + L_::E2 + static_cast<size_t>(sl) * RT * 1024;
+            char *d = dst + OPS + DK * 4 + q * EB;
+            for (int blk = cw; blk < NRC + RT; blk += NCP) {
+                const char *src = blk < NRC ? e1 + blk * 1024 : e2 + (blk - NRC) * 1024;
+                dma16(src + lane * 16, d + blk * 1024);
+            }
+        }
+    };
+
+    f32x4 D[RT];                                            // dS' rows 16 rt + 4 lg + ii, column 16 s + li
+    const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * DK * DV;
+    if (chain) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                D[rt][ii] = p.dS_T ? p.dS_T[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + 16 * s + li] : 0.f;
+    }
+    if (nchunks > 0) {
+        if (!chain) stage(nchunks - 1, smem);
+        wait_vmem();
+        __syncthreads();
+    }
+    for (int c = nchunks - 1; c >= 0; --c) {
+        const char *buf = smem + ((nchunks - 1 - c) & 1) * STAGE;
+        if (!chain) {
+            if (c > 0) stage(c - 1, smem + ((nchunks - c) & 1) * STAGE);
+            wait_vmem();
+        } else {
+            const u32x4 *kga = reinterpret_cast<const u32x4 *>(buf);
+            const u32x4 *wnt = kga + C * DK / 8;
+            const float *gam = reinterpret_cast<const float *>(buf + OPS);
+            const f32x4 *e1 = reinterpret_cast<const f32x4 *>(buf + OPS + DK * 4 + wave * EB);
+            const f32x4 *e2 = e1 + NRC * 64;
+            char *co = p.cout + recno(c) * L_::COUT;
+            u32x2 *dsn = reinterpret_cast<u32x2 *>(co + L_::DSN) + s * RT * 64 + lane;
+            u32x2 *du = reinterpret_cast<u32x2 *>(co + L_::DU) + s * NRC * 64 + lane;
+            u32x4 Dp[NKD];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) dsn[rt * 64] = f4_to_b16(D[rt]);
+#pragma unroll
+            for (int kt = 0; kt < NKD; ++kt) Dp[kt] = dpair_to_b32(D[2 * kt], D[2 * kt + 1]);
+            f32x4 U[NRC];
+#pragma unroll
+            for (int ut = 0; ut < NRC; ++ut) {
+                f32x4 acc = e1[ut * 64 + lane];
+#pragma unroll
+                for (int kt = 0; kt < NKD; ++kt) acc = mma_k32(kga[(ut * NKD + kt) * 64 + lane], Dp[kt], acc);
+                U[ut] = acc;
+                du[ut * 64] = f4_to_b16(acc);
+            }
+            u32x4 Up[NKC];
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) Up[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&gam[16 * rt + 4 * lg]);
+                f32x4 acc = e2[rt * 64 + lane];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) acc[ii] += g4[ii] * D[rt][ii];
+#pragma unroll
+                for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(wnt[(rt * NKC + kt) * 64 + lane], Up[kt], acc);
+                D[rt] = acc;
+            }
+        }
+        lds_barrier();
+    }
+    if (chain) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                p.dS0[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + 16 * s + li] = D[rt][ii];
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_g1_kernel: per record, the products with S, dS', dO and dU. [C][DK] outputs are
+// formed in (row tile B, channel tile ct) tiles t = wave + 8 j; [C][DV] ones in (row tile
+// wave / 2, column tiles of half wave % 2); [C][C] ones in tiles wave and wave + 8.
+template <int DK, int DV>
+struct G1Lay {
+    static constexpr int SV = Pad<DV>::S, SC = Pad<C>::S;
+    static constexpr int LDS = 2 * (DK * SV + 5 * C * SV + C * SC) + DK * 4;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
+    using R_ = Rec<C, DK, DV, true>;
+    using L_ = BL16<DK, DV>;
+    constexpr int SV = Pad<DV>::S, SC = Pad<C>::S;
+    constexpr int NKD = DK / 32, NKV = DV / 32, RT = DK / 16, CT = DK / 16, VT = DV / 16;
+    constexpr int TPW = NRC * CT / 8, UPW = NRC * VT / 8;
+    constexpr int NSV = DK * DV / 4 / 512, NOV = C * DV / 8 / 512;
+    constexpr int NUT = NRC * VT / 8, NDT = RT * VT / 8;
+    static_assert(TPW >= 1 && UPW >= 1 && NSV >= 1 && NOV >= 1 && NUT >= 1 && NDT >= 1, "split");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    bf16_t *Sl = reinterpret_cast<bf16_t *>(smem);          // [DK][SV]: S, then dS'
+    bf16_t *Ol = Sl + DK * SV;                              // [C][SV]  dO
+    bf16_t *dUl = Ol + C * SV;                              // [C][SV]  dU
+    bf16_t *Ul = dUl + C * SV;                              // [C][SV]  U
+    bf16_t *wl = Ul + C * SV, *vl = wl + C * SV;            // [C][SV]  w, v
+    bf16_t *Tl = vl + C * SV;                               // [C][SC]  T
+    float *dgl = reinterpret_cast<float *>(Tl + C * SC);    // [DK]
+
+    const int item = blockIdx.x, chunk = item / p.h_v, h = item - chunk * p.h_v;
+    int n, j;
+    int64_t start, end;
+    if (!locate16(p, chunk, n, j, start, end)) return;
+    const int64_t t0 = start + static_cast<int64_t>(j) * C;
+    const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const char *rec = p.rec + static_cast<size_t>(item) * R_::bytes;
+    const float *S = p.ck + static_cast<size_t>(item) * DK * DV;
+    const char *co = p.cout + static_cast<size_t>(item) * L_::COUT;
+    char *gio = p.gio + static_cast<size_t>(item) * L_::GIO;
+    const bf16_t *Tg = p.tmat + static_cast<size_t>(item) * C * C;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    // every global load first
+    f32x4 sv[NSV];
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) sv[i] = reinterpret_cast<const f32x4 *>(S)[tid + 512 * i];
+    u32x4 ov[NOV], wv[NOV], vv[NOV];
+#pragma unroll
+    for (int i = 0; i < NOV; ++i) {
+        const int e = tid + 512 * i, r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+        ov[i] = wv[i] = vv[i] = zero4;
+        if (r < Lr) {
+            const size_t off = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c8;
+            ov[i] = *reinterpret_cast<const u32x4 *>(p.dO + off);
+            wv[i] = *reinterpret_cast<const u32x4 *>(p.w + off);
+            vv[i] = *reinterpret_cast<const u32x4 *>(p.v + off);
+        }
+    }
+    const u32x4 tv = reinterpret_cast<const u32x4 *>(Tg)[tid];
+    u32x2 duv[NUT], dsv[NDT];
+#pragma unroll
+    for (int i = 0; i < NUT; ++i) duv[i] = reinterpret_cast<const u32x2 *>(co + L_::DU)[(wave + 8 * i) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) dsv[i] = reinterpret_cast<const u32x2 *>(co + L_::DSN)[(wave + 8 * i) * 64 + lane];
+    const int urt = wave >> 1, uct0 = (wave & 1) * UPW;
+    u32x4 wnf[NKD];
+#pragma unroll
+    for (int kt = 0; kt < NKD; ++kt) wnf[kt] = reinterpret_cast<const u32x4 *>(rec + R_::Wn)[(urt * NKD + kt) * 64 + lane];
+    u32x2 utv[UPW];
+#pragma unroll
+    for (int jj = 0; jj < UPW; ++jj)
+        utv[jj] = reinterpret_cast<const u32x2 *>(rec + R_::Ut + static_cast<size_t>((uct0 + jj) * NRC + urt) * R_::UT_TILE)[lane];
+
+    if (tid < DK) dgl[tid] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSV; ++i) {
+        const int e = tid + 512 * i, row = e / (DV / 4), c4 = (e - row * (DV / 4)) * 4;
+        *reinterpret_cast<u32x2 *>(&Sl[row * SV + c4]) = f4_to_b16(sv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < NOV; ++i) {
+        const int e = tid + 512 * i, r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+        *reinterpret_cast<u32x4 *>(&Ol[r * SV + c8]) = ov[i];
+        *reinterpret_cast<u32x4 *>(&wl[r * SV + c8]) = wv[i];
+        *reinterpret_cast<u32x4 *>(&vl[r * SV + c8]) = vv[i];
+    }
+    {
+        const int r = tid / (C / 8), c8 = (tid - r * (C / 8)) * 8;
+        *reinterpret_cast<u32x4 *>(&Tl[r * SC + c8]) = tv;
+    }
+#pragma unroll
+    for (int i = 0; i < NUT; ++i) {
+        const int ti = wave + 8 * i, s = ti / NRC, ut = ti - s * NRC;
+        put_tile16(dUl, SV, 16 * ut, 16 * s, duv[i], li, lg);
+    }
+    lds_barrier();
+
+    // U = U~ + Wn S
+#pragma unroll
+    for (int jj = 0; jj < UPW; ++jj) {
+        const int ct = uct0 + jj;
+        f32x4 acc = b16_to_f4(utv[jj]);
+#pragma unroll
+        for (int kt = 0; kt < NKD; ++kt) acc = mma_k32(wnf[kt], col_frag(Sl, SV, 32 * kt, 16 * ct, li, lg), acc);
+        put_tile(Ul, SV, 16 * urt, 16 * ct, acc, li, lg);
+    }
+    // dQg = dO S^T, dW~ = -dU S^T
+    f32x4 *dqg = reinterpret_cast<f32x4 *>(gio + L_::DQG);
+    u32x2 *dwo = reinterpret_cast<u32x2 *>(gio + L_::DW);
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT;
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+#pragma unroll
+        for (int kt = 0; kt < NKV; ++kt) {
+            const u32x4 sb = row_frag(Sl, SV, 16 * ct, 32 * kt, li, lg);
+            a1 = mma_k32(row_frag(Ol, SV, 16 * B, 32 * kt, li, lg), sb, a1);
+            a2 = mma_k32(row_frag(dUl, SV, 16 * B, 32 * kt, li, lg), sb, a2);
+        }
+        dqg[t * 64 + lane] = a1;
+        dwo[t * 64 + lane] = f4_to_b16(-a2);
+    }
+    // dgamma_C (before exp): sum over the columns of dS' . S
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+        const int ti = wave + 8 * i, s = ti / RT, rt = ti - s * RT;
+        const f32x4 d4 = b16_to_f4(dsv[i]);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            float x = d4[ii] * f32of(&Sl[(16 * rt + 4 * lg + ii) * SV + 16 * s + li]);
+            x += __shfl_xor(x, 1);
+            x += __shfl_xor(x, 2);
+            x += __shfl_xor(x, 4);
+            x += __shfl_xor(x, 8);
+            if (li == 0) atomicAdd(&dgl[16 * rt + 4 * lg + ii], x);
+        }
+    }
+    lds_barrier();                                  // S no longer read; U written
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) {
+        const int ti = wave + 8 * i, s = ti / RT, rt = ti - s * RT;
+        put_tile16(Sl, SV, 16 * rt, 16 * s, dsv[i], li, lg);
+    }
+    lds_barrier();
+
+    // dKg = U dS'^T
+    f32x4 *dkg = reinterpret_cast<f32x4 *>(gio + L_::DKG);
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < NKV; ++kt)
+            acc = mma_k32(row_frag(Ul, SV, 16 * B, 32 * kt, li, lg), row_frag(Sl, SV, 16 * ct, 32 * kt, li, lg), acc);
+        dkg[t * 64 + lane] = acc;
+    }
+    // dM = lower(dO U^T) and dT1 = dU X^T, X = w.v
+    u32x2 *dmo = reinterpret_cast<u32x2 *>(gio + L_::DM);
+    f32x4 *dt1 = reinterpret_cast<f32x4 *>(gio + L_::DT1);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q, R = t >> 2, I = t & 3;
+        f32x4 am = {0.f, 0.f, 0.f, 0.f}, at = am;
+#pragma unroll
+        for (int kt = 0; kt < NKV; ++kt) {
+            if (I <= R)
+                am = mma_k32(row_frag(Ol, SV, 16 * R, 32 * kt, li, lg), row_frag(Ul, SV, 16 * I, 32 * kt, li, lg), am);
+            const u32x4 xw = row_frag(wl, SV, 16 * I, 32 * kt, li, lg), xv = row_frag(vl, SV, 16 * I, 32 * kt, li, lg);
+            u32x4 xb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                xb[e] = pack_bf16x2(bf16_lo(xw[e]) * bf16_lo(xv[e]), bf16_hi(xw[e]) * bf16_hi(xv[e]));
+            at = mma_k32(row_frag(dUl, SV, 16 * R, 32 * kt, li, lg), xb, at);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            if (16 * I + li > 16 * R + 4 * lg + ii) am[ii] = 0.f;
+        dmo[t * 64 + lane] = f4_to_b16(am);
+        dt1[t * 64 + lane] = at;
+    }
+    // dX = T^T dU, then dv = w dX and dw = v dX
+#pragma unroll
+    for (int jj = 0; jj < UPW; ++jj) {
+        const int ct = uct0 + jj;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt)
+            acc = mma_k32(col_frag(Tl, SC, 32 * kt, 16 * urt, li, lg), col_frag(dUl, SV, 32 * kt, 16 * ct, li, lg), acc);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int x = 16 * urt + 4 * lg + ii, col = 16 * ct + li;
+            if (x < Lr) {
+                const size_t off = (static_cast<size_t>(t0 + x) * p.h_v + h) * DV + col;
+                p.dv[off] = f32of(&wl[x * SV + col]) * acc[ii];
+                p.dw[off] = f32of(&vl[x * SV + col]) * acc[ii];
+            }
+        }
+    }
+    lds_barrier();                                  // the dgamma_C sums are complete
+    if (tid < DK) reinterpret_cast<float *>(gio + L_::DGL)[tid] = dgl[tid];
+}
+
+// ---------------------------------------------------------------------------------------
+// bwd_g2_kernel: per record, the products through T and the decay factors. The cumulative
+// log decay is rebuilt from log alpha (log2 units, fp32). The decay sums
+//   P1[x] = sum_{i<x} dA[x,i] k_i E[x,i],   P3[x] = sum_{i<=x} dM[x,i] k_i E[x,i]
+//   P2[x] = sum_{r>x} dA[r,x] bk_r E[r,x],  P4[x] = sum_{r>=x} dM[r,x] q_r E[r,x]
+// (E[r,i] = exp(g_r - g_i) per channel) run on the matrix cores per 16-row block B with the
+// block's middle row rho as reference, E[x,i] = exp(g_x - g_rho) exp(g_rho - g_i): every
+// factor spans at most 8 tokens of decay or is <= 1. The factor operands are split into bf16
+// hi and lo parts (two products each): P1 and P2 (and P3 and P4) enter dg with opposite
+// signs and cancel over the chunk, and a single bf16 rounding of their operands would
+// leave d log alpha about ten times less accurate than the other gradients. The wave that owns channel tile ct of
+// row block B also holds that tile of dQg, dKg and dY, and takes the elementwise chain rule
+// to dq, dk, db and the decay gradient dg there; d log alpha is the reverse cumulative sum
+// of dg over the chunk plus the gamma_C terms, which reach every row.
+template <int DK, int DV>
+struct G2Lay {
+    static constexpr int SK = Pad<DK>::S, SC = Pad<C>::S, SG = DK + 4;
+    static constexpr int LDS = 4 * (C * SG + 2 * NRC * DK) + 2 * (4 * C * SK + 3 * C * SC);
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
+    using L_ = BL16<DK, DV>;
+    constexpr int SK = Pad<DK>::S, SC = Pad<C>::S, SG = DK + 4;
+    constexpr int NKD = DK / 32, CT = DK / 16, TPW = NRC * CT / 8, NKV8 = C * DK / 8 / 512;
+    constexpr int PARTS = 512 / DK, RP = C / PARTS;
+    static_assert(TPW >= 1 && NKV8 >= 1 && PARTS * DK == 512, "split");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float *gl = reinterpret_cast<float *>(smem);            // [C][SG] cumulative log2 decay
+    float *tot = gl + C * SG;                               // [2][C/16][DK] column sums per row tile
+    bf16_t *kl = reinterpret_cast<bf16_t *>(tot + 2 * NRC * DK);   // [C][SK] k
+    bf16_t *bl = kl + C * SK, *ql = bl + C * SK;            // [C][SK] b, q
+    bf16_t *dWl = ql + C * SK;                              // [C][SK] dW~
+    bf16_t *Tl = dWl + C * SK;                              // [C][SC] T
+    bf16_t *dTl = Tl + C * SC;                              // [C][SC] dT, then Z, then dA
+    bf16_t *dMl = dTl + C * SC;                             // [C][SC] dM
+
+    const int item = blockIdx.x, chunk = item / p.h_v, h = item - chunk * p.h_v;
+    int n, j;
+    int64_t start, end;
+    if (!locate16(p, chunk, n, j, start, end)) return;
+    const int64_t t0 = start + static_cast<int64_t>(j) * C;
+    const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
+    const int hk = h / p.group;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const char *gio = p.gio + static_cast<size_t>(item) * L_::GIO;
+    const bf16_t *Tg = p.tmat + static_cast<size_t>(item) * C * C;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    // every global load first
+    const u32x4 tv = reinterpret_cast<const u32x4 *>(Tg)[tid];
+    u32x4 kv[NKV8], bv[NKV8], qv[NKV8];
+#pragma unroll
+    for (int i = 0; i < NKV8; ++i) {
+        const int e = tid + 512 * i, r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+        kv[i] = bv[i] = qv[i] = zero4;
+        if (r < Lr) {
+            const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c8;
+            kv[i] = *reinterpret_cast<const u32x4 *>(p.k + ok);
+            qv[i] = *reinterpret_cast<const u32x4 *>(p.q + ok);
+            bv[i] = *reinterpret_cast<const u32x4 *>(p.b + (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c8);
+        }
+    }
+    const int gc = tid / PARTS, gpart = tid - gc * PARTS;   // cumulative decay: channel, row part
+    float la[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+        const int row = gpart * RP + r;
+        la[r] = row < Lr ? f32of(p.la + (static_cast<size_t>(t0 + row) * p.h_v + h) * DK + gc) : 0.f;
+    }
+    u32x2 dwv[TPW], dmv[2];
+    f32x4 dqg[TPW], dkg[TPW], dt1[2];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj;
+        dwv[jj] = reinterpret_cast<const u32x2 *>(gio + L_::DW)[t * 64 + lane];
+        dqg[jj] = reinterpret_cast<const f32x4 *>(gio + L_::DQG)[t * 64 + lane];
+        dkg[jj] = reinterpret_cast<const f32x4 *>(gio + L_::DKG)[t * 64 + lane];
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        dmv[q] = reinterpret_cast<const u32x2 *>(gio + L_::DM)[(wave + 8 * q) * 64 + lane];
+        dt1[q] = reinterpret_cast<const f32x4 *>(gio + L_::DT1)[(wave + 8 * q) * 64 + lane];
+    }
+    float dglv[TPW];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj, ct = t % CT;
+        dglv[jj] = reinterpret_cast<const float *>(gio + L_::DGL)[16 * ct + li];
+    }
+
+    {
+        const int r = tid / (C / 8), c8 = (tid - r * (C / 8)) * 8;
+        *reinterpret_cast<u32x4 *>(&Tl[r * SC + c8]) = tv;
+    }
+#pragma unroll
+    for (int i = 0; i < NKV8; ++i) {
+        const int e = tid + 512 * i, r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+        *reinterpret_cast<u32x4 *>(&kl[r * SK + c8]) = kv[i];
+        *reinterpret_cast<u32x4 *>(&bl[r * SK + c8]) = bv[i];
+        *reinterpret_cast<u32x4 *>(&ql[r * SK + c8]) = qv[i];
+    }
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT;
+        put_tile16(dWl, SK, 16 * B, 16 * ct, dwv[jj], li, lg);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q;
+        put_tile16(dMl, SC, 16 * (t >> 2), 16 * (t & 3), dmv[q], li, lg);
+    }
+    {   // g: the PARTS lanes of a channel are adjacent; exclusive prefix of the part sums
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            run += la[r] * kLog2e;
+            la[r] = run;
+        }
+        float pre = 0.f;
+#pragma unroll
+        for (int q = 0; q < PARTS - 1; ++q) {
+            const float o = __shfl(run, (lane & ~(PARTS - 1)) + q);
+            if (q < gpart) pre += o;
+        }
+#pragma unroll
+        for (int r = 0; r < RP; ++r) gl[(gpart * RP + r) * SG + gc] = la[r] + pre;
+    }
+    lds_barrier();
+
+    // dY = T^T dW~ (own tiles)
+    f32x4 dy[TPW];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt)
+            acc = mma_k32(col_frag(Tl, SC, 32 * kt, 16 * B, li, lg), col_frag(dWl, SK, 32 * kt, 16 * ct, li, lg), acc);
+        dy[jj] = acc;
+    }
+    // dT = dU X^T + dW~ Y^T, Y = gamma . b . k built per fragment
+    f32x4 tt[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q, R = t >> 2, I = t & 3, i = 16 * I + li;
+        f32x4 acc = dt1[q];
+#pragma unroll
+        for (int kt = 0; kt < NKD; ++kt) {
+            const u32x4 kb = row_frag(kl, SK, 16 * I, 32 * kt, li, lg), bb = row_frag(bl, SK, 16 * I, 32 * kt, li, lg);
+            const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&gl[i * SG + 32 * kt + 4 * lg]);
+            const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&gl[i * SG + 32 * kt + 16 + 4 * lg]);
+            u32x4 yb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ga = exp2_hw(e < 2 ? g0[2 * e] : g1[2 * e - 4]);
+                const float gb = exp2_hw(e < 2 ? g0[2 * e + 1] : g1[2 * e - 3]);
+                yb[e] = pack_bf16x2(ga * bf16_lo(bb[e]) * bf16_lo(kb[e]), gb * bf16_hi(bb[e]) * bf16_hi(kb[e]));
+            }
+            acc = mma_k32(row_frag(dWl, SK, 16 * R, 32 * kt, li, lg), yb, acc);
+        }
+        tt[q] = acc;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q;
+        put_tile(dTl, SC, 16 * (t >> 2), 16 * (t & 3), tt[q], li, lg);
+    }
+    lds_barrier();
+    // Z = T^T dT
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q, R = t >> 2, I = t & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt)
+            acc = mma_k32(col_frag(Tl, SC, 32 * kt, 16 * R, li, lg), col_frag(dTl, SC, 32 * kt, 16 * I, li, lg), acc);
+        tt[q] = acc;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q;
+        put_tile(dTl, SC, 16 * (t >> 2), 16 * (t & 3), tt[q], li, lg);
+    }
+    lds_barrier();
+    // dA = strictly-lower(-Z T^T)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q, R = t >> 2, I = t & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt)
+            acc = mma_k32(row_frag(dTl, SC, 16 * R, 32 * kt, li, lg), row_frag(Tl, SC, 16 * I, 32 * kt, li, lg), acc);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) acc[ii] = 16 * I + li < 16 * R + 4 * lg + ii ? -acc[ii] : 0.f;
+        tt[q] = acc;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = wave + 8 * q;
+        put_tile(dTl, SC, 16 * (t >> 2), 16 * (t & 3), tt[q], li, lg);
+    }
+    lds_barrier();
+
+    // the decay sums and the elementwise chain rule on the own tiles
+    const bf16_t *dAl = dTl;
+    float dgv[TPW][4], own[TPW];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT, c = 16 * ct + li, rho = 16 * B + 7;
+        const float grho = gl[rho * SG + c];
+        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1, a4 = a1;
+        for (int kb = 0; kb <= B; ++kb) {       // P1, P3 over i in blocks 0 .. B
+            const u32x2 d1 = *reinterpret_cast<const u32x2 *>(&dAl[(16 * B + li) * SC + 16 * kb + 4 * lg]);
+            const u32x2 d3 = *reinterpret_cast<const u32x2 *>(&dMl[(16 * B + li) * SC + 16 * kb + 4 * lg]);
+            float f[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * kb + 4 * lg + e;
+                f[e] = f32of(&kl[i * SK + c]) * exp2_hw(grho - gl[i * SG + c]);
+            }
+            u32x2 fh, fl;
+            split4(f, fh, fl);
+            a1 = mma_k16_bf16(d1, fl, mma_k16_bf16(d1, fh, a1));
+            a3 = mma_k16_bf16(d3, fl, mma_k16_bf16(d3, fh, a3));
+        }
+        for (int kb = B; kb < NRC; ++kb) {      // P2, P4 over r in blocks B .. C/16 - 1
+            const int ofs = (16 * kb + 4 * lg + (li >> 2)) * SC + 16 * B + 4 * (li & 3);
+            const u32x2 d2 = lds_tr4(&dAl[ofs]);
+            const u32x2 d4 = lds_tr4(&dMl[ofs]);
+            float f2[4], f4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * kb + 4 * lg + e;
+                const float ex = exp2_hw(gl[r * SG + c] - grho);
+                f2[e] = f32of(&bl[r * SK + c]) * f32of(&kl[r * SK + c]) * ex;
+                f4[e] = f32of(&ql[r * SK + c]) * ex;
+            }
+            u32x2 h2, l2, h4, l4;
+            split4(f2, h2, l2);
+            split4(f4, h4, l4);
+            a2 = mma_k16_bf16(d2, l2, mma_k16_bf16(d2, h2, a2));
+            a4 = mma_k16_bf16(d4, l4, mma_k16_bf16(d4, h4, a4));
+        }
+        const float gL = gl[(C - 1) * SG + c];
+        float sg = 0.f, sk = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int x = 16 * B + 4 * lg + ii;
+            const float gx = gl[x * SG + c];
+            const float f0 = exp2_hw(gx - grho), f1 = exp2_hw(grho - gx);
+            const float p1 = a1[ii] * f0, p3 = a3[ii] * f0, p2 = a2[ii] * f1, p4 = a4[ii] * f1;
+            const float ga = exp2_hw(gx), fk = exp2_hw(gL - gx);
+            const float kk = f32of(&kl[x * SK + c]), qq = f32of(&ql[x * SK + c]), bb = f32of(&bl[x * SK + c]);
+            const float bk = bb * kk;
+            const float dyv = dy[jj][ii], dq_ = dqg[jj][ii], dk_ = dkg[jj][ii];
+            const float dbk = p1 + ga * dyv;
+            const float kd = fk * kk * dk_;
+            const float g_ = bk * p1 - kk * p2 + qq * p3 - kk * p4 + ga * bk * dyv + ga * qq * dq_ - kd;
+            dgv[jj][ii] = g_;
+            sg += g_;
+            sk += kd;
+            if (x < Lr) {
+                const size_t ok = (static_cast<size_t>(t0 + x) * p.h_k + hk) * DK + c;
+                const size_t og = (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c;
+                const float vq = p3 + ga * dq_, vk = p4 + p2 + fk * dk_ + bb * dbk;
+                if (p.group == 1) {
+                    p.dq[ok] = vq;
+                    p.dk[ok] = vk;
+                } else {
+                    atomicAdd(p.dq + ok, vq);
+                    atomicAdd(p.dk + ok, vk);
+                }
+                p.db[og] = kk * dbk;
+            }
+        }
+        own[jj] = sg;
+        sg += __shfl_xor(sg, 16);
+        sg += __shfl_xor(sg, 32);
+        sk += __shfl_xor(sk, 16);
+        sk += __shfl_xor(sk, 32);
+        if (lg == 0) {
+            tot[B * DK + c] = sg;
+            tot[(NRC + B) * DK + c] = sk;
+        }
+    }
+    lds_barrier();
+    // d log alpha[x] = gamma_C dgamma_C + sum_all kd + sum_{x' >= x} dg[x']
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT, c = 16 * ct + li;
+        float all = 0.f, later = 0.f;
+#pragma unroll
+        for (int b2 = 0; b2 < NRC; ++b2) {
+            all += tot[(NRC + b2) * DK + c];
+            if (b2 > B) later += tot[b2 * DK + c];
+        }
+        const float o1 = __shfl(own[jj], li + 16), o2 = __shfl(own[jj], li + 32), o3 = __shfl(own[jj], li + 48);
+        const float below = (lg < 1 ? o1 : 0.f) + (lg < 2 ? o2 : 0.f) + (lg < 3 ? o3 : 0.f);
+        float acc = exp2_hw(gl[(C - 1) * SG + c]) * dglv[jj] + all + later + below;
+#pragma unroll
+        for (int ii = 3; ii >= 0; --ii) {
+            acc += dgv[jj][ii];
+            const int x = 16 * B + 4 * lg + ii;
+            if (x < Lr) p.dla[(static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c] = acc;
+        }
+    }
+}
+
+__global__ void zero2_kernel(float *a, float *b, int64_t n) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        a[i] = 0.f;
+        b[i] = 0.f;
+    }
+}
+
+constexpr int kChainSlices = 2;     // value slices per reverse-pass workgroup
+
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the bf16 backward: the forward's (map, records, segment buffers), then the
+// state entering every chunk, a scratch o, T per record, and the per-record buffers of BL16.
+struct B16Ws {
+    size_t ck, o, tm, crec, cout, gio, total;
+};
+static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v, bool packed) {
+    const int64_t nrec = chunk_upper_bound(C, batch, seqlen, num_seqs, packed) * h_v;
+    const size_t crec = 4 * static_cast<size_t>(C) * d_k + 4 * static_cast<size_t>(C) * d_v +
+                        4 * static_cast<size_t>(d_k) * d_v;
+    const size_t cout = 2 * static_cast<size_t>(d_k) * d_v + 2 * static_cast<size_t>(C) * d_v;
+    const size_t gio = al256(10 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * C + 4 * d_k);
+    B16Ws w;
+    w.ck = al256(chunk_workspace_bytes(C, batch, seqlen, num_seqs, h_v, d_k, d_v, true, packed));
+    w.o = al256(w.ck + static_cast<size_t>(nrec) * d_k * d_v * 4);
+    w.tm = al256(w.o + static_cast<size_t>(batch) * seqlen * h_v * d_v * 2);
+    w.crec = al256(w.tm + static_cast<size_t>(nrec) * C * C * 2);
+    w.cout = al256(w.crec + static_cast<size_t>(nrec) * crec);
+    w.gio = al256(w.cout + static_cast<size_t>(nrec) * cout);
+    w.total = w.gio + static_cast<size_t>(nrec) * gio;
+    return w;
+}
+
+template <typename K>
+static hipError_t set_lds(K kern, int bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
+    using L_ = BL16<DK, DV>;
+    static_assert(L_::CREC == 4 * static_cast<size_t>(C) * DK + 4 * static_cast<size_t>(C) * DV +
+                                  4 * static_cast<size_t>(DK) * DV &&
+                      L_::COUT == 2 * static_cast<size_t>(DK) * DV + 2 * static_cast<size_t>(C) * DV &&
+                      L_::GIO == (10 * static_cast<size_t>(C) * DK + 6 * static_cast<size_t>(C) * C + 4 * DK + 255) / 256 * 256,
+                  "the per-record buffers match bwd16_ws");
+    using RC = RChain<DK, DV, kChainSlices>;
+    static_assert(RC::LDS <= 160 * 1024 && G1Lay<DK, DV>::LDS <= 160 * 1024 && G2Lay<DK, DV>::LDS <= 160 * 1024,
+                  "LDS");
+    const bool packed = a.cu_seqlens != nullptr;
+    const int N = packed ? a.num_seqs : a.batch;
+    const int64_t nrec = chunk_upper_bound(C, a.batch, a.seqlen, a.num_seqs, packed) * a.h_v;
+    const B16Ws ws = bwd16_ws(a.batch, a.seqlen, a.num_seqs, a.h_v, DK, DV, packed);
+    char *base = a.workspace;
+
+    ChunkArgs f;
+    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.b = a.b; f.w = a.w;
+    f.S0 = a.S0; f.cu_seqlens = a.cu_seqlens; f.o = base + ws.o; f.S_T = nullptr;
+    f.workspace = base;
+    f.batch = a.batch; f.seqlen = a.seqlen; f.num_seqs = a.num_seqs;
+    f.h_k = a.h_k; f.h_v = a.h_v; f.d_k = DK; f.d_v = DV; f.bf16 = true;
+    f.chunk = C;
+    f.fu = Fusion{};
+    f.fu.cks = reinterpret_cast<float *>(base + ws.ck);
+    f.fu.tmat = base + ws.tm;
+    hipError_t e = launch_chunk_fwd(f, st);
+    if (e != hipSuccess) return e;
+
+    B16Params p;
+    p.q = static_cast<const bf16_t *>(a.q); p.k = static_cast<const bf16_t *>(a.k);
+    p.v = static_cast<const bf16_t *>(a.v); p.la = static_cast<const bf16_t *>(a.log_alpha);
+    p.b = static_cast<const bf16_t *>(a.b); p.w = static_cast<const bf16_t *>(a.w);
+    p.dO = static_cast<const bf16_t *>(a.dO);
+    p.dS_T = a.dS_T;
+    p.cu = a.cu_seqlens;
+    p.map = packed ? reinterpret_cast<const int32_t *>(base) : nullptr;
+    p.rec = base + chunk_map_bytes(a.num_seqs, packed);
+    p.tmat = reinterpret_cast<const bf16_t *>(base + ws.tm);
+    p.ck = reinterpret_cast<const float *>(base + ws.ck);
+    p.crec = base + ws.crec;
+    p.cout = base + ws.cout;
+    p.gio = base + ws.gio;
+    p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dw = a.dw; p.dla = a.dla; p.db = a.db; p.dS0 = a.dS0;
+    p.num_seqs = N; p.seqlen = a.seqlen;
+    p.nc_dense = (a.seqlen + C - 1) / C;
+    p.h_k = a.h_k; p.h_v = a.h_v; p.group = a.h_v / a.h_k;
+    p.num_pairs = N * a.h_v;
+
+    const int64_t qk = static_cast<int64_t>(a.batch) * a.seqlen * a.h_k * DK;
+    if (qk > 0 && p.group > 1) {
+        const int64_t blocks = (qk + 255) / 256;
+        hipLaunchKernelGGL(zero2_kernel, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
+                           a.dq, a.dk, qk);
+    }
+    constexpr int pre_lds = 2 * (2 * C * Pad<DK>::S + DK * Pad<C>::S + C * Pad<C>::S + C * Pad<DV>::S);
+    static_assert(pre_lds <= 160 * 1024, "LDS");
+    if ((e = set_lds(bwd_pre_kernel<DK, DV>, pre_lds)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_rchain_kernel<DK, DV, kChainSlices>, RC::LDS)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_g1_kernel<DK, DV>, G1Lay<DK, DV>::LDS)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_g2_kernel<DK, DV>, G2Lay<DK, DV>::LDS)) != hipSuccess) return e;
+    if (nrec > 0)
+        hipLaunchKernelGGL((bwd_pre_kernel<DK, DV>), dim3(nrec), dim3(256), pre_lds, st, p);
+    if (p.num_pairs > 0) {
+        const int64_t blocks = static_cast<int64_t>((p.num_pairs + 7) / 8) * 8 * RC::G;
+        hipLaunchKernelGGL((bwd_rchain_kernel<DK, DV, kChainSlices>), dim3(blocks),
+                           dim3(64 * (kChainSlices + RC::NCP)), RC::LDS, st, p);
+    }
+    if (nrec > 0) {
+        constexpr int g1_lds = G1Lay<DK, DV>::LDS, g2_lds = G2Lay<DK, DV>::LDS;
+        hipLaunchKernelGGL((bwd_g1_kernel<DK, DV>), dim3(nrec), dim3(512), g1_lds, st, p);
+        hipLaunchKernelGGL((bwd_g2_kernel<DK, DV>), dim3(nrec), dim3(512), g2_lds, st, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t chunk_bwd16_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
+                                   bool packed) {
+    return bwd16_ws(batch, seqlen, num_seqs, h_v, d_k, d_v, packed).total;
+}
+
+hipError_t launch_chunk_bwd16(const BwdArgs &a, hipStream_t st) {
+    if (a.d_k == 128 && a.d_v == 128) return launch_bwd16_t<128, 128>(a, st);
+    if (a.d_k == 64 && a.d_v == 64) return launch_bwd16_t<64, 64>(a, st);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bwd16_t<128, 64>(a, st);
+    if (a.d_k == 64 && a.d_v == 128) return launch_bwd16_t<64, 128>(a, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn2

@@ -55,6 +55,7 @@ struct ChunkParams {
     float *S_T;
     float *S_ck;         // state entering every chunk [chunk][h_v][DK][DV], or NULL
     char *rec;           // first per-(chunk, head) record
+    void *tmat;          // bf16 inputs: T = (I + A)^-1 per record, [C][C] row-major, or NULL
     // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of
     // every pair are split into nseg segments of seg_len chunks that run concurrently.
     float *seg_S;        // [pair][2][DK][DV]       states entering segments 0 (copy of S0) and 1

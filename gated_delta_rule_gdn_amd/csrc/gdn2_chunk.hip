@@ -904,9 +904,9 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     static_assert(Rec<kChunk, DK, DV, BF>::bytes > 0, "");
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
-    ChunkParams p;
+    ChunkParams p{};
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.b = a.b; p.w = a.w;
-    p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks;
+    p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks; p.tmat = a.fu.tmat;
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
     p.rec = a.workspace + mapb;
@@ -991,7 +991,7 @@ static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
     const int C = a.chunk;
     ChunkParams p{};
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.b = a.b; p.w = a.w;
-    p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks;
+    p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks; p.tmat = a.fu.tmat;
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
     p.rec = a.workspace + mapb;

@@ -26,6 +26,7 @@ struct Fusion {
     bool csilu = false;
     int gmode = 0;                   // GateMode of the b / w arguments (0: GDN-2 gates)
     float *cks = nullptr;            // chunked forward: state entering every chunk, or NULL
+    void *tmat = nullptr;            // chunked forward, bf16: T = (I + A)^-1 per record, or NULL
 };
 
 struct DecodeArgs {
@@ -78,6 +79,10 @@ struct BwdArgs {
 size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
                                  bool bf16, bool packed);
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t st);
+// bf16 inputs (gdn2_bwd16.hip): the backward on bf16 matrix cores, with its own workspace.
+size_t chunk_bwd16_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
+                                   bool packed);
+hipError_t launch_chunk_bwd16(const BwdArgs &a, hipStream_t st);
 
 // Gate mappings of other delta-rule variants onto the GDN-2 inputs (gdn2_map_gates).
 enum GateMode { GATES_GDN2 = 0, GATES_KDA = 1, GATES_FG2 = 2, GATES_FG2_PLUS = 3, GATES_GDN = 4 };

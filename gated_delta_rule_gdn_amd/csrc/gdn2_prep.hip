@@ -522,6 +522,19 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
         }
     }
 
+    if constexpr (BF) {
+        if (p.tmat != nullptr) {               // T for the chunked backward
+            lds_barrier();
+            const bf16_t *s_Tb = reinterpret_cast<const bf16_t *>(s_A);
+            bf16_t *dst = static_cast<bf16_t *>(p.tmat) + static_cast<size_t>(item) * C * C;
+            for (int idx = tid; idx < C * C / 8; idx += NT) {
+                const int r = idx / (C / 8), c8 = (idx % (C / 8)) * 8;
+                *reinterpret_cast<u32x4 *>(&dst[r * C + c8]) =
+                    *reinterpret_cast<const u32x4 *>(&s_Tb[r * STB + c8]);
+            }
+        }
+    }
+
     // ---- W~^T = X^T T^T per key round, U~ = T (w.v) per value round ----
     // wave roles: channel tile ctl = wave % RCT of the round, row tiles R = wave / RCT + k
     // (NWV / RCT); with two row-tile groups the even and the odd row tiles carry equal k
