@@ -20,9 +20,8 @@
 //   bwd_rchain_kernel   per (sequence, value head, 32 state columns), from the last chunk:
 //                       dU = E1 + Kg dS' and dS = gamma_C dS' + E2 + Wn^T dU; writes dS' and dU
 //                       of every chunk (bf16) and dS0 (fp32)
-//   bwd_g1_kernel       per record: U, dQg, dW~, dKg, dM, dX (-> dv, dw), dU X^T, and
-//                       dgamma_C = sum_col dS' . S
-//   bwd_g2_kernel       per record: dY, dT, dA, the decay sums, dq, dk, db and dlog_alpha
+//   bwd_grads16_kernel  per record, every gradient of the chunk: U, dQg, dW~, dKg, dM,
+//                       dX (-> dv, dw), dT, dA, the decay sums, dq, dk, db and dlog_alpha
 #include "gdn2_chunk.h"
 
 namespace gdn2 {
@@ -45,22 +44,13 @@ struct BL16 {
     static constexpr size_t KgA = 0;                                      // Kg, A fragments [C][DK]
     static constexpr size_t WnT = KgA + static_cast<size_t>(C) * DK * 2;  // Wn^T, A fragments [DK][C]
     static constexpr size_t OPS = WnT + static_cast<size_t>(DK) * C * 2;
-    static constexpr size_t E1 = OPS;                                     // fp32 D tiles [slice][C/16]
-    static constexpr size_t E2 = E1 + static_cast<size_t>(C) * DV * 4;    // fp32 D tiles [slice][DK/16]
-    static constexpr size_t CREC = E2 + static_cast<size_t>(DK) * DV * 4;
-    // bwd_rchain_kernel -> bwd_g1_kernel, bf16 D tiles
+    static constexpr size_t E1 = OPS;                                     // bf16 D tiles [slice][C/16]
+    static constexpr size_t E2 = E1 + static_cast<size_t>(C) * DV * 2;    // bf16 D tiles [slice][DK/16]
+    static constexpr size_t CREC = E2 + static_cast<size_t>(DK) * DV * 2;
+    // bwd_rchain_kernel -> bwd_grads16_kernel, bf16 D tiles
     static constexpr size_t DSN = 0;                                      // dS' [slice][DK/16]
     static constexpr size_t DU = DSN + static_cast<size_t>(DK) * DV * 2;  // dU [slice][C/16]
     static constexpr size_t COUT = DU + static_cast<size_t>(C) * DV * 2;
-    // bwd_g1_kernel -> bwd_g2_kernel; [C][DK] products as D tiles (row tile B, column tile ct)
-    // at B * DK/16 + ct, [C][C] ones at R * C/16 + I
-    static constexpr size_t DQG = 0;                                      // fp32
-    static constexpr size_t DKG = DQG + static_cast<size_t>(C) * DK * 4;  // fp32
-    static constexpr size_t DW = DKG + static_cast<size_t>(C) * DK * 4;   // bf16
-    static constexpr size_t DM = DW + static_cast<size_t>(C) * DK * 2;    // bf16
-    static constexpr size_t DT1 = DM + static_cast<size_t>(C) * C * 2;    // fp32
-    static constexpr size_t DGL = DT1 + static_cast<size_t>(C) * C * 4;   // fp32 [DK]
-    static constexpr size_t GIO = (DGL + DK * 4 + 255) / 256 * 256;
 };
 
 struct B16Params {
@@ -70,7 +60,7 @@ struct B16Params {
     const char *rec;                   // records of the forward re-run
     const bf16_t *tmat;                // T per record, [C][C]
     const float *ck;                   // state entering every chunk, [record][DK][DV]
-    char *crec, *cout, *gio;
+    char *crec, *cout;
     float *dq, *dk, *dv, *dw, *dla, *db, *dS0;
     int num_seqs, seqlen, nc_dense, h_k, h_v, group, num_pairs;
 };
@@ -147,12 +137,14 @@ __device__ __forceinline__ void split4(const float (&x)[4], u32x2 &hi, u32x2 &lo
 }
 
 // ---------------------------------------------------------------------------------------
-// bwd_pre_kernel: per record, the reverse pass's operands. The forward record's Wn, Qg, KgT
+// bwd_pre_kernel: per record, the reverse pass's operands (one workgroup per CU by its LDS,
+// hence the register budget of one wave per SIMD). The forward record's Wn, Qg, KgT
 // and M fragments are put back into row-major LDS tiles (blocks of M above the diagonal,
 // which the forward never writes, as zeros); transposing reads then give the fragments of
 // Kg, Wn^T, M^T and Qg^T, and dO is staged the same way.
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(B16Params p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_pre_kernel(B16Params p) {
     using R_ = Rec<C, DK, DV, true>;
     using L_ = BL16<DK, DV>;
     constexpr int SK = Pad<DK>::S, SC = Pad<C>::S, SV = Pad<DV>::S;
@@ -236,8 +228,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(B16Params p) {
         wnt[blk * 64 + lane] = col_frag(Wl, SK, 32 * kt, 16 * rt, li, lg);
     }
     // E1 = M^T dO and E2 = Qg^T dO, one 16-column value slice at a time
-    f32x4 *e1 = reinterpret_cast<f32x4 *>(cr + L_::E1);
-    f32x4 *e2 = reinterpret_cast<f32x4 *>(cr + L_::E2);
+    u32x2 *e1 = reinterpret_cast<u32x2 *>(cr + L_::E1);
+    u32x2 *e2 = reinterpret_cast<u32x2 *>(cr + L_::E2);
     for (int s = wave; s < NSL; s += 4) {
         u32x4 ob[NKC];
 #pragma unroll
@@ -247,14 +239,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(B16Params p) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(col_frag(Ml, SC, 32 * kt, 16 * ut, li, lg), ob[kt], acc);
-            e1[(s * NRC + ut) * 64 + lane] = acc;
+            e1[(s * NRC + ut) * 64 + lane] = f4_to_b16(acc);
         }
 #pragma unroll
         for (int rt = 0; rt < NRK; ++rt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(col_frag(Ql, SK, 32 * kt, 16 * rt, li, lg), ob[kt], acc);
-            e2[(s * NRK + rt) * 64 + lane] = acc;
+            e2[(s * NRK + rt) * 64 + lane] = f4_to_b16(acc);
         }
     }
 }
@@ -263,27 +255,39 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(B16Params p) {
 // bwd_rchain_kernel: the reverse state pass. A workgroup owns NWS 16-column slices of dS of
 // one (sequence, value head): one chain wave per slice holds its d_k x 16 slice in fp32
 // registers, and two copy waves stage each chunk's Kg and Wn^T fragments, gamma_C and the
-// slices' E1 and E2 tiles in LDS one chunk ahead (double-buffered, direct global-to-LDS
-// loads). The chain waves issue no global loads, so they never wait on memory: their stores
-// of dS' and dU stay in flight. The workgroups of one (sequence, head) are placed on one XCD
-// (blocks are dispatched to the XCDs round-robin), where they share the records in L2.
+// slices' E1 and E2 tiles in LDS NBUF - 1 chunks ahead (direct global-to-LDS loads), so that
+// a chunk's staging latency overlaps several chunk steps. Each chunk step first issues all
+// of its LDS operand reads, then the products. The chain waves issue no global loads and
+// never wait on memory: their stores of dS' and dU stay in flight. The workgroups of one
+// (sequence, head) are placed on one XCD (blocks are dispatched to the XCDs round-robin),
+// where they share the records in L2.
 template <int DK, int DV, int NWS>
 struct RChain {
     static constexpr int NCP = 2;
     static constexpr int OPS = static_cast<int>(BL16<DK, DV>::OPS);
-    static constexpr int EB = (C + DK) * 16 * 4;            // E1 and E2 tiles of one slice
+    static constexpr int NRT = DK / 16;
+    static constexpr int EB = (C + DK) * 16 * 2;            // E1 and E2 tiles of one slice
     static constexpr int STAGE = OPS + DK * 4 + NWS * EB;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int NBUF = 4 * STAGE <= 160 * 1024 ? 4 : 3;
+    static constexpr int LDS = NBUF * STAGE;
     static constexpr int G = DV / 16 / NWS;                 // workgroups per (sequence, head)
+    // direct loads one copy wave issues per stage (copy wave 0 also loads gamma_C)
+    static constexpr int per(int cw) {
+        return (OPS / 1024 - cw + NCP - 1) / NCP + (cw == 0 ? 1 : 0) +
+               NWS * ((EB / 1024 - cw + NCP - 1) / NCP);
+    }
 };
 
+// (one workgroup per CU by its LDS: the register budget of one wave per SIMD)
 template <int DK, int DV, int NWS>
-__global__ __launch_bounds__(64 * (NWS + 2)) void bwd_rchain_kernel(B16Params p) {
+__global__ __launch_bounds__(64 * (NWS + 2)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_rchain_kernel(B16Params p) {
     using R_ = Rec<C, DK, DV, true>;
     using L_ = BL16<DK, DV>;
     using RC = RChain<DK, DV, NWS>;
     constexpr int RT = DK / 16, NKD = DK / 32, NCP = RC::NCP, OPS = RC::OPS, EB = RC::EB;
-    constexpr int STAGE = RC::STAGE, G = RC::G;
+    constexpr int STAGE = RC::STAGE, G = RC::G, NBUF = RC::NBUF;
+    static_assert(NCP == 2 && (NBUF - 2) * RC::per(0) < 64 && EB % 1024 == 0, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int bid = blockIdx.x, idx = bid >> 3;
     const int pair = (idx / G) * 8 + (bid & 7), part = idx - (idx / G) * G;
@@ -303,10 +307,12 @@ __global__ __launch_bounds__(64 * (NWS + 2)) void bwd_rchain_kernel(B16Params p)
     const int nchunks = static_cast<int>((end - start + C - 1) / C);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const bool chain = wave < NWS;
+    const int cw = wave - NWS;                              // copy wave index
     const int s = part * NWS + wave;                        // value slice of a chain wave
     auto recno = [&](int c) { return static_cast<size_t>(cbase + c) * p.h_v + h; };
-    auto stage = [&](int c, char *dst) {                    // copy waves
-        const int cw = wave - NWS;
+    auto slot = [&](int c) { return smem + (c % NBUF) * STAGE; };
+    auto stage = [&](int c) {                               // copy waves: chunk c into its slot
+        char *dst = slot(c);
         const char *cr = p.crec + recno(c) * L_::CREC;
         for (int blk = cw; blk < OPS / 1024; blk += NCP) dma16(cr + blk * 1024 + lane * 16, dst + blk * 1024);
         if (cw == 0 && lane < DK / 4)
@@ -314,13 +320,23 @@ __global__ __launch_bounds__(64 * (NWS + 2)) void bwd_rchain_kernel(B16Params p)
 #pragma unroll
         for (int q = 0; q < NWS; ++q) {
             const int sl = part * NWS + q;
-            const char *e1 = cr + L_::E1 + static_cast<size_t>(sl) * NRC * 1024;
-            const char *e2 = cr + L_::E2 + static_cast<size_t>(sl) * RT * 1024;
+            const char *e1 = cr + L_::E1 + static_cast<size_t>(sl) * NRC * 512;
+            const char *e2 = cr + L_::E2 + static_cast<size_t>(sl) * RT * 512;
             char *d = dst + OPS + DK * 4 + q * EB;
-            for (int blk = cw; blk < NRC + RT; blk += NCP) {
-                const char *src = blk < NRC ? e1 + blk * 1024 : e2 + (blk - NRC) * 1024;
+            for (int blk = cw; blk < EB / 1024; blk += NCP) {
+                const char *src = blk < NRC / 2 ? e1 + blk * 1024 : e2 + (blk - NRC / 2) * 1024;
                 dma16(src + lane * 16, d + blk * 1024);
             }
+        }
+    };
+    // copy waves: wait until the stage of chunk c has landed, with `newer` later-issued
+    // stages allowed to stay in flight
+    auto wait_stage = [&](int newer) {
+        if (newer <= 0) wait_vmem();
+        else if (newer == 1) {
+            if (cw == 0) wait_vmem_n<RC::per(0)>(); else wait_vmem_n<RC::per(1)>();
+        } else {
+            if (cw == 0) wait_vmem_n<(NBUF - 2) * RC::per(0)>(); else wait_vmem_n<(NBUF - 2) * RC::per(1)>();
         }
     };
 
@@ -334,53 +350,76 @@ __global__ __launch_bounds__(64 * (NWS + 2)) void bwd_rchain_kernel(B16Params p)
                 D[rt][ii] = p.dS_T ? p.dS_T[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + 16 * s + li] : 0.f;
     }
     if (nchunks > 0) {
-        if (!chain) stage(nchunks - 1, smem);
-        wait_vmem();
-        __syncthreads();
+        if (!chain) {
+            for (int c = nchunks - 1; c >= 0 && c > nchunks - NBUF; --c) stage(c);
+            wait_stage(min(nchunks - 1, NBUF - 2));
+        }
+        lds_barrier();
     }
     for (int c = nchunks - 1; c >= 0; --c) {
-        const char *buf = smem + ((nchunks - 1 - c) & 1) * STAGE;
         if (!chain) {
-            if (c > 0) stage(c - 1, smem + ((nchunks - c) & 1) * STAGE);
-            wait_vmem();
+            if (c >= NBUF - 1) stage(c - (NBUF - 1));
+            if (c >= 1) wait_stage(min(c - 1, NBUF - 2));   // chunk c - 1 has landed
         } else {
+            const char *buf = slot(c);
             const u32x4 *kga = reinterpret_cast<const u32x4 *>(buf);
             const u32x4 *wnt = kga + C * DK / 8;
             const float *gam = reinterpret_cast<const float *>(buf + OPS);
-            const f32x4 *e1 = reinterpret_cast<const f32x4 *>(buf + OPS + DK * 4 + wave * EB);
-            const f32x4 *e2 = e1 + NRC * 64;
+            const u32x2 *e1 = reinterpret_cast<const u32x2 *>(buf + OPS + DK * 4 + wave * EB);
+            const u32x2 *e2 = e1 + NRC * 64;
+            // every LDS operand of the step first
+            u32x4 ka[NRC][NKD], wa[RT][NKC];
+            u32x2 e1v[NRC], e2v[RT];
+            f32x4 g4[RT];
+#pragma unroll
+            for (int ut = 0; ut < NRC; ++ut) {
+                e1v[ut] = e1[ut * 64 + lane];
+#pragma unroll
+                for (int kt = 0; kt < NKD; ++kt) ka[ut][kt] = kga[(ut * NKD + kt) * 64 + lane];
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                e2v[rt] = e2[rt * 64 + lane];
+                g4[rt] = *reinterpret_cast<const f32x4 *>(&gam[16 * rt + 4 * lg]);
+#pragma unroll
+                for (int kt = 0; kt < NKC; ++kt) wa[rt][kt] = wnt[(rt * NKC + kt) * 64 + lane];
+            }
+            asm volatile("" ::: "memory");
             char *co = p.cout + recno(c) * L_::COUT;
             u32x2 *dsn = reinterpret_cast<u32x2 *>(co + L_::DSN) + s * RT * 64 + lane;
             u32x2 *du = reinterpret_cast<u32x2 *>(co + L_::DU) + s * NRC * 64 + lane;
             u32x4 Dp[NKD];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) dsn[rt * 64] = f4_to_b16(D[rt]);
-#pragma unroll
             for (int kt = 0; kt < NKD; ++kt) Dp[kt] = dpair_to_b32(D[2 * kt], D[2 * kt + 1]);
             f32x4 U[NRC];
 #pragma unroll
             for (int ut = 0; ut < NRC; ++ut) {
-                f32x4 acc = e1[ut * 64 + lane];
+                f32x4 acc = b16_to_f4(e1v[ut]);
 #pragma unroll
-                for (int kt = 0; kt < NKD; ++kt) acc = mma_k32(kga[(ut * NKD + kt) * 64 + lane], Dp[kt], acc);
+                for (int kt = 0; kt < NKD; ++kt) acc = mma_k32(ka[ut][kt], Dp[kt], acc);
                 U[ut] = acc;
-                du[ut * 64] = f4_to_b16(acc);
             }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) dsn[rt * 64] = f4_to_b16(D[rt]);
             u32x4 Up[NKC];
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) Up[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&gam[16 * rt + 4 * lg]);
-                f32x4 acc = e2[rt * 64 + lane];
+                f32x4 acc = b16_to_f4(e2v[rt]);
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) acc[ii] += g4[ii] * D[rt][ii];
+                for (int ii = 0; ii < 4; ++ii) acc[ii] += g4[rt][ii] * D[rt][ii];
 #pragma unroll
-                for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(wnt[(rt * NKC + kt) * 64 + lane], Up[kt], acc);
+                for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(wa[rt][kt], Up[kt], acc);
                 D[rt] = acc;
             }
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) {
+                du[(2 * kt) * 64] = Up[kt].xy;
+                du[(2 * kt + 1) * 64] = Up[kt].zw;
+            }
         }
-        lds_barrier();
+        lds_barrier();                                      // slot(c) free; slot(c - 1) ready
     }
     if (chain) {
 #pragma unroll
@@ -392,33 +431,87 @@ __global__ __launch_bounds__(64 * (NWS + 2)) void bwd_rchain_kernel(B16Params p)
 }
 
 // ---------------------------------------------------------------------------------------
-// bwd_g1_kernel: per record, the products with S, dS', dO and dU. [C][DK] outputs are
-// formed in (row tile B, channel tile ct) tiles t = wave + 8 j; [C][DV] ones in (row tile
-// wave / 2, column tiles of half wave % 2); [C][C] ones in tiles wave and wave + 8.
+// bwd_grads16_kernel: per record, every gradient of the chunk, in two phases that share one
+// LDS allocation (one workgroup of eight waves per CU by its LDS: the register budget of two
+// waves per SIMD).
+//
+// Phase 1, the products with S, dS', dO and dU:
+//   U = U~ + Wn S,  dQg = dO S^T,  dW~ = -dU S^T,  dKg = U dS'^T,  dM = lower(dO U^T),
+//   dT1 = dU X^T,  dX = T^T dU (-> dv = w dX, dw = v dX),  dgamma_C = sum_col dS' . S.
+// [C][DK] products are formed in (row tile B, channel tile ct) tiles t = wave + 8 j, [C][DV]
+// ones in (row tile wave / 2, column tiles of half wave % 2), [C][C] ones in tiles wave and
+// wave + 8; the [C][DK] and [C][C] results stay in registers for phase 2, which uses the
+// same tiles. Phase 2's inputs (k, q, b, log alpha) are loaded with phase 1's and wait in
+// registers.
+//
+// Phase 2, the products through T and the decay factors: the cumulative log decay is rebuilt
+// from log alpha (log2 units, fp32); dY = T^T dW~, dT = dT1 + dW~ Y^T, dA = strictly-lower(
+// -T^T dT T^T). The decay sums
+//   P1[x] = sum_{i<x} dA[x,i] k_i E[x,i],   P3[x] = sum_{i<=x} dM[x,i] k_i E[x,i]
+//   P2[x] = sum_{r>x} dA[r,x] bk_r E[r,x],  P4[x] = sum_{r>=x} dM[r,x] q_r E[r,x]
+// (E[r,i] = exp(g_r - g_i) per channel) run on the matrix cores per 16-row block B with the
+// block's middle row rho as reference, E[x,i] = exp(g_x - g_rho) exp(g_rho - g_i): every
+// factor spans at most 8 tokens of decay or is <= 1. The factor operands are split into bf16
+// hi and lo parts (two products each): P1 and P2 (and P3 and P4) enter dg with opposite
+// signs and cancel over the chunk, and a single bf16 rounding of their operands would leave
+// d log alpha about ten times less accurate than the other gradients. The wave that owns
+// channel tile ct of row block B holds that tile of dQg, dKg and dY and takes the
+// elementwise chain rule to dq, dk, db and the decay gradient dg there; d log alpha is the
+// reverse cumulative sum of dg over the chunk plus the gamma_C terms, which reach every row.
 template <int DK, int DV>
-struct G1Lay {
-    static constexpr int SV = Pad<DV>::S, SC = Pad<C>::S;
-    static constexpr int LDS = 2 * (DK * SV + 5 * C * SV + C * SC) + DK * 4;
+struct GLay {
+    static constexpr int SV = Pad<DV>::S, SK = Pad<DK>::S, SC = Pad<C>::S;
+    static constexpr int SQ = DK + 8;          // k, b, q, log alpha: rows or single elements only
+    static constexpr int SG = DK + 4;          // fp32 cumulative decay
+    // both phases: T [C][SC] bf16, dgamma_C [DK] fp32
+    static constexpr int T_ = 0, DGL = T_ + 2 * C * SC, BASE = DGL + 4 * DK;
+    // phase 1 (bf16 tiles)
+    static constexpr int S_ = BASE;                       // [DK][SV]: S, then dS'
+    static constexpr int O_ = S_ + 2 * DK * SV;           // [C][SV] dO
+    static constexpr int DU = O_ + 2 * C * SV;            // [C][SV] dU
+    static constexpr int U_ = DU + 2 * C * SV;            // [C][SV] U
+    static constexpr int W_ = U_ + 2 * C * SV;            // [C][SV] w
+    static constexpr int V_ = W_ + 2 * C * SV;            // [C][SV] v
+    static constexpr int END1 = V_ + 2 * C * SV;
+    // phase 2
+    static constexpr int G_ = BASE;                       // [C][SG] fp32
+    static constexpr int TOT = G_ + 4 * C * SG;           // [2][C/16][DK] fp32
+    static constexpr int K_ = TOT + 4 * 2 * NRC * DK;     // [C][SQ] bf16 each: k, b, q, log alpha
+    static constexpr int B_ = K_ + 2 * C * SQ, Q_ = B_ + 2 * C * SQ, LA = Q_ + 2 * C * SQ;
+    static constexpr int DW = LA + 2 * C * SQ;            // [C][SK] dW~
+    static constexpr int DT = DW + 2 * C * SK;            // [C][SC] dT, then Z, then dA
+    static constexpr int DM = DT + 2 * C * SC;            // [C][SC] dM
+    static constexpr int END2 = DM + 2 * C * SC;
+    static constexpr int LDS = END1 > END2 ? END1 : END2;
+    static_assert(BASE % 16 == 0 && O_ % 16 == 0 && DU % 16 == 0 && U_ % 16 == 0 && W_ % 16 == 0 &&
+                      V_ % 16 == 0 && TOT % 16 == 0 && K_ % 16 == 0 && B_ % 16 == 0 && Q_ % 16 == 0 &&
+                      LA % 16 == 0 && DW % 16 == 0 && DT % 16 == 0 && DM % 16 == 0,
+                  "16-byte aligned regions");
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_grads16_kernel(B16Params p) {
     using R_ = Rec<C, DK, DV, true>;
     using L_ = BL16<DK, DV>;
-    constexpr int SV = Pad<DV>::S, SC = Pad<C>::S;
+    using GL = GLay<DK, DV>;
+    constexpr int SV = GL::SV, SK = GL::SK, SC = GL::SC, SQ = GL::SQ, SG = GL::SG;
     constexpr int NKD = DK / 32, NKV = DV / 32, RT = DK / 16, CT = DK / 16, VT = DV / 16;
     constexpr int TPW = NRC * CT / 8, UPW = NRC * VT / 8;
-    constexpr int NSV = DK * DV / 4 / 512, NOV = C * DV / 8 / 512;
+    constexpr int NSV = DK * DV / 4 / 512, NOV = C * DV / 8 / 512, NKV8 = C * DK / 8 / 512;
     constexpr int NUT = NRC * VT / 8, NDT = RT * VT / 8;
-    static_assert(TPW >= 1 && UPW >= 1 && NSV >= 1 && NOV >= 1 && NUT >= 1 && NDT >= 1, "split");
+    constexpr int PARTS = 512 / DK, RP = C / PARTS;
+    static_assert(TPW >= 1 && UPW >= 1 && NSV >= 1 && NOV >= 1 && NUT >= 1 && NDT >= 1 && NKV8 >= 1 &&
+                      PARTS * DK == 512 && 8 % RT == 0, "split");
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    bf16_t *Sl = reinterpret_cast<bf16_t *>(smem);          // [DK][SV]: S, then dS'
-    bf16_t *Ol = Sl + DK * SV;                              // [C][SV]  dO
-    bf16_t *dUl = Ol + C * SV;                              // [C][SV]  dU
-    bf16_t *Ul = dUl + C * SV;                              // [C][SV]  U
-    bf16_t *wl = Ul + C * SV, *vl = wl + C * SV;            // [C][SV]  w, v
-    bf16_t *Tl = vl + C * SV;                               // [C][SC]  T
-    float *dgl = reinterpret_cast<float *>(Tl + C * SC);    // [DK]
+    bf16_t *Tl = reinterpret_cast<bf16_t *>(smem + GL::T_);
+    float *dgl = reinterpret_cast<float *>(smem + GL::DGL);
+    bf16_t *Sl = reinterpret_cast<bf16_t *>(smem + GL::S_);
+    bf16_t *Ol = reinterpret_cast<bf16_t *>(smem + GL::O_);
+    bf16_t *dUl = reinterpret_cast<bf16_t *>(smem + GL::DU);
+    bf16_t *Ul = reinterpret_cast<bf16_t *>(smem + GL::U_);
+    bf16_t *wl = reinterpret_cast<bf16_t *>(smem + GL::W_);
+    bf16_t *vl = reinterpret_cast<bf16_t *>(smem + GL::V_);
 
     const int item = blockIdx.x, chunk = item / p.h_v, h = item - chunk * p.h_v;
     int n, j;
@@ -426,15 +519,15 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
     if (!locate16(p, chunk, n, j, start, end)) return;
     const int64_t t0 = start + static_cast<int64_t>(j) * C;
     const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
+    const int hk = h / p.group;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const char *rec = p.rec + static_cast<size_t>(item) * R_::bytes;
     const float *S = p.ck + static_cast<size_t>(item) * DK * DV;
     const char *co = p.cout + static_cast<size_t>(item) * L_::COUT;
-    char *gio = p.gio + static_cast<size_t>(item) * L_::GIO;
     const bf16_t *Tg = p.tmat + static_cast<size_t>(item) * C * C;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-    // every global load first
+    // every global load of both phases first
     f32x4 sv[NSV];
 #pragma unroll
     for (int i = 0; i < NSV; ++i) sv[i] = reinterpret_cast<const f32x4 *>(S)[tid + 512 * i];
@@ -464,7 +557,22 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
 #pragma unroll
     for (int jj = 0; jj < UPW; ++jj)
         utv[jj] = reinterpret_cast<const u32x2 *>(rec + R_::Ut + static_cast<size_t>((uct0 + jj) * NRC + urt) * R_::UT_TILE)[lane];
+    u32x4 kv[NKV8], bv[NKV8], qv[NKV8], av[NKV8];
+#pragma unroll
+    for (int i = 0; i < NKV8; ++i) {
+        const int e = tid + 512 * i, r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+        kv[i] = bv[i] = qv[i] = av[i] = zero4;
+        if (r < Lr) {
+            const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c8;
+            const size_t og = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c8;
+            kv[i] = *reinterpret_cast<const u32x4 *>(p.k + ok);
+            qv[i] = *reinterpret_cast<const u32x4 *>(p.q + ok);
+            bv[i] = *reinterpret_cast<const u32x4 *>(p.b + og);
+            av[i] = *reinterpret_cast<const u32x4 *>(p.la + og);
+        }
+    }
 
+    // ---- phase 1 ----
     if (tid < DK) dgl[tid] = 0.f;
 #pragma unroll
     for (int i = 0; i < NSV; ++i) {
@@ -498,9 +606,9 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
         for (int kt = 0; kt < NKD; ++kt) acc = mma_k32(wnf[kt], col_frag(Sl, SV, 32 * kt, 16 * ct, li, lg), acc);
         put_tile(Ul, SV, 16 * urt, 16 * ct, acc, li, lg);
     }
-    // dQg = dO S^T, dW~ = -dU S^T
-    f32x4 *dqg = reinterpret_cast<f32x4 *>(gio + L_::DQG);
-    u32x2 *dwo = reinterpret_cast<u32x2 *>(gio + L_::DW);
+    // dQg = dO S^T, dW~ = -dU S^T (kept for phase 2)
+    f32x4 dqg[TPW];
+    u32x2 dwv[TPW];
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) {
         const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT;
@@ -511,17 +619,24 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
             a1 = mma_k32(row_frag(Ol, SV, 16 * B, 32 * kt, li, lg), sb, a1);
             a2 = mma_k32(row_frag(dUl, SV, 16 * B, 32 * kt, li, lg), sb, a2);
         }
-        dqg[t * 64 + lane] = a1;
-        dwo[t * 64 + lane] = f4_to_b16(-a2);
+        dqg[jj] = a1;
+        dwv[jj] = f4_to_b16(-a2);
     }
-    // dgamma_C (before exp): sum over the columns of dS' . S
+    // dgamma_C (before exp): sum over the columns of dS' . S. The wave's dS' tiles all lie in
+    // row tile wave % (d_k / 16): sum over them, then over the 16 columns of a tile.
+    {
+        const int rt = wave % RT;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < NDT; ++i) {
-        const int ti = wave + 8 * i, s = ti / RT, rt = ti - s * RT;
-        const f32x4 d4 = b16_to_f4(dsv[i]);
+        for (int i = 0; i < NDT; ++i) {
+            const int s = (wave + 8 * i) / RT;
+            const f32x4 d4 = b16_to_f4(dsv[i]);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[ii] += d4[ii] * f32of(&Sl[(16 * rt + 4 * lg + ii) * SV + 16 * s + li]);
+        }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            float x = d4[ii] * f32of(&Sl[(16 * rt + 4 * lg + ii) * SV + 16 * s + li]);
+            float x = acc[ii];
             x += __shfl_xor(x, 1);
             x += __shfl_xor(x, 2);
             x += __shfl_xor(x, 4);
@@ -537,8 +652,8 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
     }
     lds_barrier();
 
-    // dKg = U dS'^T
-    f32x4 *dkg = reinterpret_cast<f32x4 *>(gio + L_::DKG);
+    // dKg = U dS'^T (kept for phase 2)
+    f32x4 dkg[TPW];
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) {
         const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT;
@@ -546,11 +661,11 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
 #pragma unroll
         for (int kt = 0; kt < NKV; ++kt)
             acc = mma_k32(row_frag(Ul, SV, 16 * B, 32 * kt, li, lg), row_frag(Sl, SV, 16 * ct, 32 * kt, li, lg), acc);
-        dkg[t * 64 + lane] = acc;
+        dkg[jj] = acc;
     }
-    // dM = lower(dO U^T) and dT1 = dU X^T, X = w.v
-    u32x2 *dmo = reinterpret_cast<u32x2 *>(gio + L_::DM);
-    f32x4 *dt1 = reinterpret_cast<f32x4 *>(gio + L_::DT1);
+    // dM = lower(dO U^T) and dT1 = dU X^T, X = w.v (kept for phase 2)
+    u32x2 dmv[2];
+    f32x4 dt1[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int t = wave + 8 * q, R = t >> 2, I = t & 3;
@@ -569,8 +684,8 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
             if (16 * I + li > 16 * R + 4 * lg + ii) am[ii] = 0.f;
-        dmo[t * 64 + lane] = f4_to_b16(am);
-        dt1[t * 64 + lane] = at;
+        dmv[q] = f4_to_b16(am);
+        dt1[q] = at;
     }
     // dX = T^T dU, then dv = w dX and dw = v dX
 #pragma unroll
@@ -590,111 +705,25 @@ __global__ __launch_bounds__(512) void bwd_g1_kernel(B16Params p) {
             }
         }
     }
-    lds_barrier();                                  // the dgamma_C sums are complete
-    if (tid < DK) reinterpret_cast<float *>(gio + L_::DGL)[tid] = dgl[tid];
-}
+    lds_barrier();                                  // phase 1's tiles are no longer read
 
-// ---------------------------------------------------------------------------------------
-// bwd_g2_kernel: per record, the products through T and the decay factors. The cumulative
-// log decay is rebuilt from log alpha (log2 units, fp32). The decay sums
-//   P1[x] = sum_{i<x} dA[x,i] k_i E[x,i],   P3[x] = sum_{i<=x} dM[x,i] k_i E[x,i]
-//   P2[x] = sum_{r>x} dA[r,x] bk_r E[r,x],  P4[x] = sum_{r>=x} dM[r,x] q_r E[r,x]
-// (E[r,i] = exp(g_r - g_i) per channel) run on the matrix cores per 16-row block B with the
-// block's middle row rho as reference, E[x,i] = exp(g_x - g_rho) exp(g_rho - g_i): every
-// factor spans at most 8 tokens of decay or is <= 1. The factor operands are split into bf16
-// hi and lo parts (two products each): P1 and P2 (and P3 and P4) enter dg with opposite
-// signs and cancel over the chunk, and a single bf16 rounding of their operands would
-// leave d log alpha about ten times less accurate than the other gradients. The wave that owns channel tile ct of
-// row block B also holds that tile of dQg, dKg and dY, and takes the elementwise chain rule
-// to dq, dk, db and the decay gradient dg there; d log alpha is the reverse cumulative sum
-// of dg over the chunk plus the gamma_C terms, which reach every row.
-template <int DK, int DV>
-struct G2Lay {
-    static constexpr int SK = Pad<DK>::S, SC = Pad<C>::S, SG = DK + 4;
-    static constexpr int LDS = 4 * (C * SG + 2 * NRC * DK) + 2 * (4 * C * SK + 3 * C * SC);
-};
-
-template <int DK, int DV>
-__global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
-    using L_ = BL16<DK, DV>;
-    constexpr int SK = Pad<DK>::S, SC = Pad<C>::S, SG = DK + 4;
-    constexpr int NKD = DK / 32, CT = DK / 16, TPW = NRC * CT / 8, NKV8 = C * DK / 8 / 512;
-    constexpr int PARTS = 512 / DK, RP = C / PARTS;
-    static_assert(TPW >= 1 && NKV8 >= 1 && PARTS * DK == 512, "split");
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    float *gl = reinterpret_cast<float *>(smem);            // [C][SG] cumulative log2 decay
-    float *tot = gl + C * SG;                               // [2][C/16][DK] column sums per row tile
-    bf16_t *kl = reinterpret_cast<bf16_t *>(tot + 2 * NRC * DK);   // [C][SK] k
-    bf16_t *bl = kl + C * SK, *ql = bl + C * SK;            // [C][SK] b, q
-    bf16_t *dWl = ql + C * SK;                              // [C][SK] dW~
-    bf16_t *Tl = dWl + C * SK;                              // [C][SC] T
-    bf16_t *dTl = Tl + C * SC;                              // [C][SC] dT, then Z, then dA
-    bf16_t *dMl = dTl + C * SC;                             // [C][SC] dM
-
-    const int item = blockIdx.x, chunk = item / p.h_v, h = item - chunk * p.h_v;
-    int n, j;
-    int64_t start, end;
-    if (!locate16(p, chunk, n, j, start, end)) return;
-    const int64_t t0 = start + static_cast<int64_t>(j) * C;
-    const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
-    const int hk = h / p.group;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-    const char *gio = p.gio + static_cast<size_t>(item) * L_::GIO;
-    const bf16_t *Tg = p.tmat + static_cast<size_t>(item) * C * C;
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-    // every global load first
-    const u32x4 tv = reinterpret_cast<const u32x4 *>(Tg)[tid];
-    u32x4 kv[NKV8], bv[NKV8], qv[NKV8];
+    // ---- phase 2 ----
+    float *gl = reinterpret_cast<float *>(smem + GL::G_);
+    float *tot = reinterpret_cast<float *>(smem + GL::TOT);
+    bf16_t *kl = reinterpret_cast<bf16_t *>(smem + GL::K_);
+    bf16_t *bl = reinterpret_cast<bf16_t *>(smem + GL::B_);
+    bf16_t *ql = reinterpret_cast<bf16_t *>(smem + GL::Q_);
+    bf16_t *lal = reinterpret_cast<bf16_t *>(smem + GL::LA);
+    bf16_t *dWl = reinterpret_cast<bf16_t *>(smem + GL::DW);
+    bf16_t *dTl = reinterpret_cast<bf16_t *>(smem + GL::DT);
+    bf16_t *dMl = reinterpret_cast<bf16_t *>(smem + GL::DM);
 #pragma unroll
     for (int i = 0; i < NKV8; ++i) {
         const int e = tid + 512 * i, r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
-        kv[i] = bv[i] = qv[i] = zero4;
-        if (r < Lr) {
-            const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c8;
-            kv[i] = *reinterpret_cast<const u32x4 *>(p.k + ok);
-            qv[i] = *reinterpret_cast<const u32x4 *>(p.q + ok);
-            bv[i] = *reinterpret_cast<const u32x4 *>(p.b + (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c8);
-        }
-    }
-    const int gc = tid / PARTS, gpart = tid - gc * PARTS;   // cumulative decay: channel, row part
-    float la[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-        const int row = gpart * RP + r;
-        la[r] = row < Lr ? f32of(p.la + (static_cast<size_t>(t0 + row) * p.h_v + h) * DK + gc) : 0.f;
-    }
-    u32x2 dwv[TPW], dmv[2];
-    f32x4 dqg[TPW], dkg[TPW], dt1[2];
-#pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) {
-        const int t = wave + 8 * jj;
-        dwv[jj] = reinterpret_cast<const u32x2 *>(gio + L_::DW)[t * 64 + lane];
-        dqg[jj] = reinterpret_cast<const f32x4 *>(gio + L_::DQG)[t * 64 + lane];
-        dkg[jj] = reinterpret_cast<const f32x4 *>(gio + L_::DKG)[t * 64 + lane];
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        dmv[q] = reinterpret_cast<const u32x2 *>(gio + L_::DM)[(wave + 8 * q) * 64 + lane];
-        dt1[q] = reinterpret_cast<const f32x4 *>(gio + L_::DT1)[(wave + 8 * q) * 64 + lane];
-    }
-    float dglv[TPW];
-#pragma unroll
-    for (int jj = 0; jj < TPW; ++jj) {
-        const int t = wave + 8 * jj, ct = t % CT;
-        dglv[jj] = reinterpret_cast<const float *>(gio + L_::DGL)[16 * ct + li];
-    }
-
-    {
-        const int r = tid / (C / 8), c8 = (tid - r * (C / 8)) * 8;
-        *reinterpret_cast<u32x4 *>(&Tl[r * SC + c8]) = tv;
-    }
-#pragma unroll
-    for (int i = 0; i < NKV8; ++i) {
-        const int e = tid + 512 * i, r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
-        *reinterpret_cast<u32x4 *>(&kl[r * SK + c8]) = kv[i];
-        *reinterpret_cast<u32x4 *>(&bl[r * SK + c8]) = bv[i];
-        *reinterpret_cast<u32x4 *>(&ql[r * SK + c8]) = qv[i];
+        *reinterpret_cast<u32x4 *>(&kl[r * SQ + c8]) = kv[i];
+        *reinterpret_cast<u32x4 *>(&bl[r * SQ + c8]) = bv[i];
+        *reinterpret_cast<u32x4 *>(&ql[r * SQ + c8]) = qv[i];
+        *reinterpret_cast<u32x4 *>(&lal[r * SQ + c8]) = av[i];
     }
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) {
@@ -706,7 +735,12 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
         const int t = wave + 8 * q;
         put_tile16(dMl, SC, 16 * (t >> 2), 16 * (t & 3), dmv[q], li, lg);
     }
+    lds_barrier();
     {   // g: the PARTS lanes of a channel are adjacent; exclusive prefix of the part sums
+        const int gc = tid / PARTS, gpart = tid - gc * PARTS;
+        float la[RP];
+#pragma unroll
+        for (int r = 0; r < RP; ++r) la[r] = f32of(&lal[(gpart * RP + r) * SQ + gc]);
         float run = 0.f;
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
@@ -722,8 +756,6 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
 #pragma unroll
         for (int r = 0; r < RP; ++r) gl[(gpart * RP + r) * SG + gc] = la[r] + pre;
     }
-    lds_barrier();
-
     // dY = T^T dW~ (own tiles)
     f32x4 dy[TPW];
 #pragma unroll
@@ -735,6 +767,7 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
             acc = mma_k32(col_frag(Tl, SC, 32 * kt, 16 * B, li, lg), col_frag(dWl, SK, 32 * kt, 16 * ct, li, lg), acc);
         dy[jj] = acc;
     }
+    lds_barrier();                                  // g is complete
     // dT = dU X^T + dW~ Y^T, Y = gamma . b . k built per fragment
     f32x4 tt[2];
 #pragma unroll
@@ -743,7 +776,7 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
         f32x4 acc = dt1[q];
 #pragma unroll
         for (int kt = 0; kt < NKD; ++kt) {
-            const u32x4 kb = row_frag(kl, SK, 16 * I, 32 * kt, li, lg), bb = row_frag(bl, SK, 16 * I, 32 * kt, li, lg);
+            const u32x4 kb = row_frag(kl, SQ, 16 * I, 32 * kt, li, lg), bb = row_frag(bl, SQ, 16 * I, 32 * kt, li, lg);
             const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&gl[i * SG + 32 * kt + 4 * lg]);
             const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&gl[i * SG + 32 * kt + 16 + 4 * lg]);
             u32x4 yb;
@@ -815,7 +848,7 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * kb + 4 * lg + e;
-                f[e] = f32of(&kl[i * SK + c]) * exp2_hw(grho - gl[i * SG + c]);
+                f[e] = f32of(&kl[i * SQ + c]) * exp2_hw(grho - gl[i * SG + c]);
             }
             u32x2 fh, fl;
             split4(f, fh, fl);
@@ -831,8 +864,8 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * kb + 4 * lg + e;
                 const float ex = exp2_hw(gl[r * SG + c] - grho);
-                f2[e] = f32of(&bl[r * SK + c]) * f32of(&kl[r * SK + c]) * ex;
-                f4[e] = f32of(&ql[r * SK + c]) * ex;
+                f2[e] = f32of(&bl[r * SQ + c]) * f32of(&kl[r * SQ + c]) * ex;
+                f4[e] = f32of(&ql[r * SQ + c]) * ex;
             }
             u32x2 h2, l2, h4, l4;
             split4(f2, h2, l2);
@@ -849,7 +882,7 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
             const float f0 = exp2_hw(gx - grho), f1 = exp2_hw(grho - gx);
             const float p1 = a1[ii] * f0, p3 = a3[ii] * f0, p2 = a2[ii] * f1, p4 = a4[ii] * f1;
             const float ga = exp2_hw(gx), fk = exp2_hw(gL - gx);
-            const float kk = f32of(&kl[x * SK + c]), qq = f32of(&ql[x * SK + c]), bb = f32of(&bl[x * SK + c]);
+            const float kk = f32of(&kl[x * SQ + c]), qq = f32of(&ql[x * SQ + c]), bb = f32of(&bl[x * SQ + c]);
             const float bk = bb * kk;
             const float dyv = dy[jj][ii], dq_ = dqg[jj][ii], dk_ = dkg[jj][ii];
             const float dbk = p1 + ga * dyv;
@@ -895,7 +928,7 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
         }
         const float o1 = __shfl(own[jj], li + 16), o2 = __shfl(own[jj], li + 32), o3 = __shfl(own[jj], li + 48);
         const float below = (lg < 1 ? o1 : 0.f) + (lg < 2 ? o2 : 0.f) + (lg < 3 ? o3 : 0.f);
-        float acc = exp2_hw(gl[(C - 1) * SG + c]) * dglv[jj] + all + later + below;
+        float acc = exp2_hw(gl[(C - 1) * SG + c]) * dgl[c] + all + later + below;
 #pragma unroll
         for (int ii = 3; ii >= 0; --ii) {
             acc += dgv[jj][ii];
@@ -905,6 +938,7 @@ __global__ __launch_bounds__(512) void bwd_g2_kernel(B16Params p) {
     }
 }
 
+
 __global__ void zero2_kernel(float *a, float *b, int64_t n) {
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
@@ -913,29 +947,27 @@ __global__ void zero2_kernel(float *a, float *b, int64_t n) {
     }
 }
 
-constexpr int kChainSlices = 2;     // value slices per reverse-pass workgroup
+constexpr int kChainSlices = 1;     // value slices per reverse-pass workgroup
 
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace of the bf16 backward: the forward's (map, records, segment buffers), then the
 // state entering every chunk, a scratch o, T per record, and the per-record buffers of BL16.
 struct B16Ws {
-    size_t ck, o, tm, crec, cout, gio, total;
+    size_t ck, o, tm, crec, cout, total;
 };
 static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v, bool packed) {
     const int64_t nrec = chunk_upper_bound(C, batch, seqlen, num_seqs, packed) * h_v;
-    const size_t crec = 4 * static_cast<size_t>(C) * d_k + 4 * static_cast<size_t>(C) * d_v +
-                        4 * static_cast<size_t>(d_k) * d_v;
+    const size_t crec = 4 * static_cast<size_t>(C) * d_k + 2 * static_cast<size_t>(C) * d_v +
+                        2 * static_cast<size_t>(d_k) * d_v;
     const size_t cout = 2 * static_cast<size_t>(d_k) * d_v + 2 * static_cast<size_t>(C) * d_v;
-    const size_t gio = al256(10 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * C + 4 * d_k);
     B16Ws w;
     w.ck = al256(chunk_workspace_bytes(C, batch, seqlen, num_seqs, h_v, d_k, d_v, true, packed));
     w.o = al256(w.ck + static_cast<size_t>(nrec) * d_k * d_v * 4);
     w.tm = al256(w.o + static_cast<size_t>(batch) * seqlen * h_v * d_v * 2);
     w.crec = al256(w.tm + static_cast<size_t>(nrec) * C * C * 2);
     w.cout = al256(w.crec + static_cast<size_t>(nrec) * crec);
-    w.gio = al256(w.cout + static_cast<size_t>(nrec) * cout);
-    w.total = w.gio + static_cast<size_t>(nrec) * gio;
+    w.total = w.cout + static_cast<size_t>(nrec) * cout;
     return w;
 }
 
@@ -948,14 +980,12 @@ static hipError_t set_lds(K kern, int bytes) {
 template <int DK, int DV>
 hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     using L_ = BL16<DK, DV>;
-    static_assert(L_::CREC == 4 * static_cast<size_t>(C) * DK + 4 * static_cast<size_t>(C) * DV +
-                                  4 * static_cast<size_t>(DK) * DV &&
-                      L_::COUT == 2 * static_cast<size_t>(DK) * DV + 2 * static_cast<size_t>(C) * DV &&
-                      L_::GIO == (10 * static_cast<size_t>(C) * DK + 6 * static_cast<size_t>(C) * C + 4 * DK + 255) / 256 * 256,
+    static_assert(L_::CREC == 4 * static_cast<size_t>(C) * DK + 2 * static_cast<size_t>(C) * DV +
+                                  2 * static_cast<size_t>(DK) * DV &&
+                      L_::COUT == 2 * static_cast<size_t>(DK) * DV + 2 * static_cast<size_t>(C) * DV,
                   "the per-record buffers match bwd16_ws");
     using RC = RChain<DK, DV, kChainSlices>;
-    static_assert(RC::LDS <= 160 * 1024 && G1Lay<DK, DV>::LDS <= 160 * 1024 && G2Lay<DK, DV>::LDS <= 160 * 1024,
-                  "LDS");
+    static_assert(RC::LDS <= 160 * 1024 && GLay<DK, DV>::LDS <= 160 * 1024, "LDS");
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
     const int64_t nrec = chunk_upper_bound(C, a.batch, a.seqlen, a.num_seqs, packed) * a.h_v;
@@ -988,7 +1018,6 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     p.ck = reinterpret_cast<const float *>(base + ws.ck);
     p.crec = base + ws.crec;
     p.cout = base + ws.cout;
-    p.gio = base + ws.gio;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dw = a.dw; p.dla = a.dla; p.db = a.db; p.dS0 = a.dS0;
     p.num_seqs = N; p.seqlen = a.seqlen;
     p.nc_dense = (a.seqlen + C - 1) / C;
@@ -1005,8 +1034,7 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     static_assert(pre_lds <= 160 * 1024, "LDS");
     if ((e = set_lds(bwd_pre_kernel<DK, DV>, pre_lds)) != hipSuccess) return e;
     if ((e = set_lds(bwd_rchain_kernel<DK, DV, kChainSlices>, RC::LDS)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_g1_kernel<DK, DV>, G1Lay<DK, DV>::LDS)) != hipSuccess) return e;
-    if ((e = set_lds(bwd_g2_kernel<DK, DV>, G2Lay<DK, DV>::LDS)) != hipSuccess) return e;
+    if ((e = set_lds(bwd_grads16_kernel<DK, DV>, GLay<DK, DV>::LDS)) != hipSuccess) return e;
     if (nrec > 0)
         hipLaunchKernelGGL((bwd_pre_kernel<DK, DV>), dim3(nrec), dim3(256), pre_lds, st, p);
     if (p.num_pairs > 0) {
@@ -1015,9 +1043,8 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
                            dim3(64 * (kChainSlices + RC::NCP)), RC::LDS, st, p);
     }
     if (nrec > 0) {
-        constexpr int g1_lds = G1Lay<DK, DV>::LDS, g2_lds = G2Lay<DK, DV>::LDS;
-        hipLaunchKernelGGL((bwd_g1_kernel<DK, DV>), dim3(nrec), dim3(512), g1_lds, st, p);
-        hipLaunchKernelGGL((bwd_g2_kernel<DK, DV>), dim3(nrec), dim3(512), g2_lds, st, p);
+        constexpr int g_lds = GLay<DK, DV>::LDS;
+        hipLaunchKernelGGL((bwd_grads16_kernel<DK, DV>), dim3(nrec), dim3(512), g_lds, st, p);
     }
     return hipGetLastError();
 }
