@@ -60,6 +60,13 @@ def decode_alg(wl):
     return 2 * st + vec, 2 * st, 7 * wl.num_seqs * wl.h_v * wl.d_k * wl.d_v
 
 
+# Sources of the 64-token chunked forward and of the bf16 chunked backward (a stored counter
+# reading is used only while these are unchanged)
+CHUNK_SRC = ("gdn2_chunk.hip", "gdn2_prep.hip", "gdn2_chunk.h", "gdn2_mfma.h", "gdn2_common.h")
+BWD_SRC = ("gdn2_bwd16.hip", "gdn2_chunk.hip", "gdn2_prep.hip", "gdn2_chunk.h", "gdn2_mfma.h",
+           "gdn2_common.h")
+
+
 def source_hash(*names):
     h = hashlib.sha256()
     for n in names:
@@ -362,8 +369,7 @@ def bench_chunk_bwd(steps, warmup, seed=11):
     states = 3 * x["S0"].numel() * 4                                          # S0, dS_T, dS0
     nbytes = tok_in + grads + states
     del x, ws, dO, dST
-    bsrc = source_hash("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h",
-                       "gdn2_common.h")
+    bsrc = source_hash(*BWD_SRC)
     return {"workload": f"{wl.name}_bwd", "us_per_call": t * 1e6, "tokens_per_s": T * B / t,
             "alg_bytes": nbytes, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
             "traffic": measured_traffic("chunk_bwd_t4096", bsrc)}
@@ -669,10 +675,12 @@ def pmc_summary(fetch_dir, write_dir):
             continue
         name = kernel_short(k)
         base = name.split("<")[0]
-        if base in ("chunk_prep_kernel", "chunk_seg_kernel", "chunk_state_kernel"):
+        targs = name[name.index("<") + 1:name.rindex(">")].split(", ") if "<" in name else []
+        c64_bf16 = base == "prep_kernel" and targs[2] == "64" and "bf16" in targs[0]
+        if base in ("chunk_seg_kernel", "chunk_state_kernel") or c64_bf16:
             parts = [("chunk_fwd_t4096", 0, 5), ("chunk_bwd_t4096", 5, 8)]
         elif base in ("prep_kernel", "panel_state_kernel"):
-            parts = [("chunk_fwd_f32_t4096" if "<float" in name else "chunk_fwd_t4096_c128", 0, 2)]
+            parts = [("chunk_fwd_f32_t4096" if "float" in targs[0] else "chunk_fwd_t4096_c128", 0, 2)]
         elif base.startswith("bwd_"):
             parts = [("chunk_bwd_t4096", 0, 3)]
         elif base == "recurrent_fwd_kernel":
@@ -692,11 +700,10 @@ def pmc_summary(fetch_dir, write_dir):
             print(f"| {name} | {gname} | {rw[0] / 1e6:.1f} MB | {rw[1] / 1e6:.1f} MB | {sum(rw) / 1e6:.1f} MB |")
     out = {"_note": f"HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE (x{ff}) and "
                     f"WRITE_SIZE (x{wf}); commands and calibration in hbm_traffic_counters.md"}
-    csrc = source_hash("gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h", "gdn2_common.h")
+    csrc = source_hash(*CHUNK_SRC)
     gsrc = source_hash("gdn2_prep.hip", "gdn2_state.hip", "gdn2_chunk.h", "gdn2_mfma.h",
                        "gdn2_common.h")
-    bsrc = source_hash("gdn2_bwd.hip", "gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h",
-                       "gdn2_common.h")
+    bsrc = source_hash(*BWD_SRC)
     for gname, items in groups.items():
         src = {"chunk_fwd_t4096": csrc, "chunk_bwd_t4096": bsrc}.get(gname, gsrc)
         out[gname] = {"source_hash": src, "bytes_per_launch": int(sum(sum(rw) for _, rw in items)),
@@ -757,7 +764,7 @@ def main():
         wl, x, gout, t_warm, t_cold = bench_chunk(args.steps, args.warmup)
         B, T = x["q"].shape[:2]
         nbytes, flops = chunk_alg(wl, B * T, B)
-        src = source_hash("gdn2_chunk.hip", "gdn2_chunk.h", "gdn2_mfma.h", "gdn2_common.h")
+        src = source_hash(*CHUNK_SRC)
         out.update({
             "value": B * T / t_warm, "unit": "tokens/s", "ms_per_step": t_warm * 1e3,
             "config": {"workload": wl.name, "batch": B, "seq_len": T, "h_k": wl.h_k,

@@ -24,10 +24,10 @@
 //   bwd_grads_kernel    per record, in parallel: every input gradient of the chunk
 // The record kernels keep their intermediates in a per-record fp32 scratch of the workspace
 // and stage each product's operands in LDS; their products are fp32 matrix-core tiles
-// (16x16x4). With bf16 inputs the reverse pass takes three bf16 products of hi/lo-split
-// operands, which the factors kernel splits once per record. q and k gradients of value
-// heads that share a key head are summed with fp32 atomics; with one value head per key
-// head they are stored.
+// (16x16x4), as are the reverse pass's. This is the path for fp32 inputs (built at
+// d_k = d_v = 64); bf16 inputs take gdn2_bwd16.hip. q and k gradients of value heads that
+// share a key head are summed with fp32 atomics; with one value head per key head they are
+// stored.
 #include "gdn2_common.h"
 #include "gdn2_internal.h"
 #include "gdn2_mfma.h"
@@ -58,10 +58,7 @@ struct BLay {
                             DT = A + 4 * CC, TMP = A + 5 * CC, DA = A + 6 * CC;
     // [DK]
     static constexpr size_t GL = A + 7 * CC, DGL = GL + DK;
-    // bf16 inputs: the reverse pass's W~ and Kg operands, split into bf16 hi and lo parts
-    // (2 CK floats of u32x4 fragments: W~ hi, W~ lo, Kg hi, Kg lo)
-    static constexpr size_t OPS = DGL + DK;
-    static constexpr size_t FLOATS = OPS + 2 * CK;
+    static constexpr size_t FLOATS = DGL + DK;
 };
 
 // LDS copies of g, k, q and b.k of one record with row stride SP floats (DK + 1 where the
@@ -178,28 +175,6 @@ __device__ void block_mm_lds(float *lds, FA a, FB b, FS store) {
     block_mm<M, N, K>([&](int m, int k) { return As[m * SA + k]; },
                       [&](int k, int n) { return Bs[k * SB + n]; }, store);
     __syncthreads();
-}
-
-// Eight fp32 values -> a bf16 matrix-core operand in the order of mma_k32 (slots 0-3 and
-// 4-7 as given) as hi = bf16(x) and lo = bf16(x - hi): hi*hi + hi*lo + lo*hi keeps about 16
-// significant bits of a product.
-__device__ __forceinline__ void split_op(const float (&x)[8], u32x4 &hi, u32x4 &lo) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t h = pack_bf16x2(x[2 * j], x[2 * j + 1]);
-        hi[j] = h;
-        lo[j] = pack_bf16x2(x[2 * j] - bf16_lo(h), x[2 * j + 1] - bf16_hi(h));
-    }
-}
-__device__ __forceinline__ f32x4 mma3(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
-    c = mma_k32(ah, bh, c);
-    c = mma_k32(ah, bl, c);
-    return mma_k32(al, bh, c);
-}
-// two D tiles (k rows 0-15 and 16-31) as a split B operand
-__device__ __forceinline__ void split_dpair(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &lo) {
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    split_op(x, hi, lo);
 }
 
 // Clears the atomically accumulated dq and dk.
@@ -377,37 +352,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_factors_kernel(BwdParams p) {
              [&](int m, int nn, float x) { s[L_::E1 + m * DV + nn] = x; });
     block_mm_lds<DK, DV, C, true, false>(lf, [&](int m, int kk) { return sc[L_::QG + kk * DK + m]; }, dO_at,
              [&](int m, int nn, float x) { s[L_::E2 + m * DV + nn] = x; });
-    if constexpr (sizeof(T) == 2) {
-        // The reverse pass's bf16 operands, split here once rather than by every wave at
-        // every step: -W~^T tiles (A operands of dS) and Kg tiles (A operands of dU), each
-        // as the u32x4 fragment lane (li, lg) passes to mma_k32, hi parts then lo parts.
-        constexpr int UT = C / 16, RT = DK / 16, NOP = UT * (RT / 2) * 64;
-        u32x4 *ops = reinterpret_cast<u32x4 *>(s + L_::OPS);
-        for (int e = tid; e < NOP; e += kBwdThreads) {
-            const int lane = e & 63, li = lane & 15, lg = lane >> 4, t = e >> 6;
-            float xa[8];
-            u32x4 hi, lo;
-            const int rt = t / (UT / 2), kw = t - rt * (UT / 2);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                xa[q] = -sc[L_::WT + (32 * kw + 4 * lg + q) * DK + 16 * rt + li];
-                xa[4 + q] = -sc[L_::WT + (32 * kw + 16 + 4 * lg + q) * DK + 16 * rt + li];
-            }
-            split_op(xa, hi, lo);
-            ops[e] = hi;
-            ops[NOP + e] = lo;
-            const int ut = t / (RT / 2), kk = t - ut * (RT / 2);
-            const float *row = sc + L_::KG + (16 * ut + li) * DK + 32 * kk + 4 * lg;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                xa[q] = row[q];
-                xa[4 + q] = row[16 + q];
-            }
-            split_op(xa, hi, lo);
-            ops[2 * NOP + e] = hi;
-            ops[3 * NOP + e] = lo;
-        }
-    }
 }
 
 __device__ __forceinline__ void dma16(const void *src, void *lds_dst) {
@@ -428,10 +372,8 @@ struct ChainStage {
 // Four waves per workgroup, each owning 16 state columns of one (sequence, value head);
 // the workgroup stages each chunk's W~, Kg and g_L in LDS (double-buffered, direct
 // global-to-LDS loads issued one chunk ahead), and each wave prefetches its columns of
-// M^T dO and Qg^T dO into registers one chunk ahead. BF (bf16 inputs): the products are
-// three bf16 products of split operands (about 16 significant bits); fp32 inputs keep
-// fp32 products.
-template <int DK, int DV, bool BF>
+// M^T dO and Qg^T dO into registers one chunk ahead. The products are fp32 matrix-core tiles.
+template <int DK, int DV>
 __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
     using L_ = BLay<DK, DV>;
     using CS = ChainStage<DK>;
@@ -458,7 +400,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
         return p.scr + (static_cast<size_t>(cbase + c) * p.h_v + h) * L_::FLOATS;
     };
     auto stage = [&](int c, char *dst) {            // this wave's share of chunk c's copies
-        const char *src = reinterpret_cast<const char *>(scratch(c) + (BF ? L_::OPS : L_::WT));
+        const char *src = reinterpret_cast<const char *>(scratch(c) + L_::WT);
         for (int blk = wave; blk < CS::TILES / 1024; blk += 4)
             dma16(src + blk * 1024 + lane * 16, dst + blk * 1024);
         if (wave == 3 && lane < DK / 4)
@@ -508,8 +450,6 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
         }
         const float *wt = reinterpret_cast<const float *>(buf);
         const float *kg = wt + C * DK;
-        constexpr int NOP = UT * (RT / 2) * 64;
-        const u32x4 *ops = reinterpret_cast<const u32x4 *>(buf);      // bf16 inputs
         const float *gl = wt + 2 * C * DK;
         float *s = scratch(c);
 #pragma unroll
@@ -519,57 +459,31 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdParams p) {
                 s[L_::DSN + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = D[rt][ii];
         // dU = M^T dO + Kg dS'
         f32x4 U4[UT];
-        u32x4 dbh[BF ? RT / 2 : 1], dbl[BF ? RT / 2 : 1];      // dS' as split B operands
-        if constexpr (BF) {
-#pragma unroll
-            for (int k2 = 0; k2 < RT / 2; ++k2) split_dpair(D[2 * k2], D[2 * k2 + 1], dbh[k2], dbl[k2]);
-        }
 #pragma unroll
         for (int ut = 0; ut < UT; ++ut) {
             f32x4 acc = {e1[ut][0], e1[ut][1], e1[ut][2], e1[ut][3]};
-            if constexpr (BF) {
 #pragma unroll
-                for (int k2 = 0; k2 < RT / 2; ++k2) {
-                    const int o = (ut * (RT / 2) + k2) * 64 + lane;
-                    acc = mma3(ops[2 * NOP + o], ops[3 * NOP + o], dbh[k2], dbl[k2], acc);
-                }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < RT; ++kt) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(&kg[(16 * ut + li) * DK + 16 * kt + 4 * lg]);
-                    acc = mma_k16_f32(av, D[kt], acc);
-                }
+            for (int kt = 0; kt < RT; ++kt) {
+                const f32x4 av = *reinterpret_cast<const f32x4 *>(&kg[(16 * ut + li) * DK + 16 * kt + 4 * lg]);
+                acc = mma_k16_f32(av, D[kt], acc);
             }
             U4[ut] = acc;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) s[L_::DU + (16 * ut + 4 * lg + ii) * DV + col] = acc[ii];
         }
         // dS = gamma_L dS' + Qg^T dO - W~^T dU
-        u32x4 ubh[BF ? UT / 2 : 1], ubl[BF ? UT / 2 : 1];      // dU as split B operands
-        if constexpr (BF) {
-#pragma unroll
-            for (int k2 = 0; k2 < UT / 2; ++k2) split_dpair(U4[2 * k2], U4[2 * k2 + 1], ubh[k2], ubl[k2]);
-        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             f32x4 acc;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 acc[ii] = __expf(gl[16 * rt + 4 * lg + ii]) * D[rt][ii] + e2[rt][ii];
-            if constexpr (BF) {
 #pragma unroll
-                for (int k2 = 0; k2 < UT / 2; ++k2) {
-                    const int o = (rt * (UT / 2) + k2) * 64 + lane;
-                    acc = mma3(ops[o], ops[NOP + o], ubh[k2], ubl[k2], acc);
-                }
-            } else {
+            for (int kt = 0; kt < UT; ++kt) {
+                f32x4 av;
 #pragma unroll
-                for (int kt = 0; kt < UT; ++kt) {
-                    f32x4 av;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) av[e] = -wt[(16 * kt + 4 * lg + e) * DK + 16 * rt + li];
-                    acc = mma_k16_f32(av, U4[kt], acc);
-                }
+                for (int e = 0; e < 4; ++e) av[e] = -wt[(16 * kt + 4 * lg + e) * DK + 16 * rt + li];
+                acc = mma_k16_f32(av, U4[kt], acc);
             }
             D[rt] = acc;
         }
@@ -803,7 +717,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_grads_kernel(BwdParams p) {
 
 template <typename T, int DK, int DV>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
-    static_assert(BLay<DK, DV>::FLOATS == 14 * static_cast<size_t>(C) * DK + 6 * static_cast<size_t>(C) * DV +
+    static_assert(BLay<DK, DV>::FLOATS == 12 * static_cast<size_t>(C) * DK + 6 * static_cast<size_t>(C) * DV +
                       2 * static_cast<size_t>(DK) * DV + 7 * static_cast<size_t>(C) * C + 2 * DK,
                   "the per-record scratch matches chunk_bwd_workspace_bytes");
     const bool packed = a.cu_seqlens != nullptr;
@@ -866,11 +780,10 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     const int64_t units = static_cast<int64_t>(N) * a.h_v * (DV / 64);
     if (units > 0) {
         const int lds = 2 * ChainStage<DK>::BYTES;
-        constexpr bool BF = sizeof(T) == 2;
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_chain_kernel<DK, DV, BF>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_chain_kernel<DK, DV>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV, BF>), dim3(units), dim3(256), lds, st, p);
+        hipLaunchKernelGGL((bwd_chain_kernel<DK, DV>), dim3(units), dim3(256), lds, st, p);
     }
     if (nrec > 0) {
         hipLaunchKernelGGL((bwd_grads_kernel<T, DK, DV>), dim3(nrec), dim3(kBwdThreads), glds, st, p);
@@ -878,13 +791,6 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_bwd_dt(const BwdArgs &a, hipStream_t st) {
-    if (a.d_k == 128 && a.d_v == 128) return launch_bwd_t<T, 128, 128>(a, st);
-    if (a.d_k == 64 && a.d_v == 64) return launch_bwd_t<T, 64, 64>(a, st);
-    if (a.d_k == 128 && a.d_v == 64) return launch_bwd_t<T, 128, 64>(a, st);
-    return launch_bwd_t<T, 64, 128>(a, st);
-}
 
 }  // namespace
 
@@ -893,7 +799,7 @@ size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, i
     if (bf16) return chunk_bwd16_workspace_bytes(batch, seqlen, num_seqs, h_v, d_k, d_v, packed);
     const int64_t nrec = chunk_upper_bound(kChunk, batch, seqlen, num_seqs, packed) * h_v;
     // (the floats of BLay<d_k, d_v>)
-    const size_t per = 4 * (14 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * d_v +
+    const size_t per = 4 * (12 * static_cast<size_t>(C) * d_k + 6 * static_cast<size_t>(C) * d_v +
                             2 * static_cast<size_t>(d_k) * d_v + 7 * static_cast<size_t>(C) * C + 2 * d_k);
     const size_t o_bytes = (static_cast<size_t>(batch) * seqlen * h_v * d_v * (bf16 ? 2 : 4) + 255) / 256 * 256;
     const size_t head = (chunk_workspace_bytes(kChunk, batch, seqlen, num_seqs, h_v, d_k, d_v, bf16, packed) +
@@ -902,7 +808,9 @@ size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, i
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t st) {
-    return a.bf16 ? launch_chunk_bwd16(a, st) : launch_bwd_dt<float>(a, st);
+    if (a.bf16) return launch_chunk_bwd16(a, st);
+    if (a.d_k == 64 && a.d_v == 64) return launch_bwd_t<float, 64, 64>(a, st);
+    return hipErrorInvalidValue;            // refused by the API layer before the launch
 }
 
 }  // namespace gdn2
