@@ -774,7 +774,7 @@ def main():
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": nbytes / t_warm / 1e9 / HBM_PEAK_GBPS,
                          "traffic": measured_traffic("chunk_fwd_t4096", src),
-                         "kernel": "one gdn2_chunk_fwd call: chunk_prep_kernel, chunk_seg_kernel, chunk_state_kernel",
+                         "kernel": "one gdn2_chunk_fwd call: prep_kernel, chunk_seg_kernel, chunk_state_kernel",
                          "alg_bytes": nbytes, "alg_flops": flops,
                          "mfma_frac_bf16": flops / t_warm / 1e12 / BF16_MFMA_PEAK_TFLOPS},
             "cold_cache": {"us_per_call": t_cold * 1e6, "tokens_per_s": B * T / t_cold,

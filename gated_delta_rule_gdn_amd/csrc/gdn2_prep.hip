@@ -10,9 +10,11 @@
 //   KgT = ((gamma_C / gamma) . k)^T,  gamma_C
 // (the record layout of gdn2_chunk.h).
 //
-// One 256-thread workgroup per record, small enough in LDS that two records run on a CU
-// at once for C <= 64 (the rounds of one hide the latency of the other's). The key
-// channels are processed in rounds of one matrix-core k tile (32 bf16 / 16 fp32 channels):
+// One workgroup per record, small enough in LDS that two records run on a CU at once for
+// C <= 64 (the rounds of one hide the latency of the other's): eight waves at C = 64, where
+// a round covers two matrix-core k tiles and every wave holds one sub-chunk of each, four
+// waves over one k tile per round otherwise (PrepShape below). The key channels are
+// processed in rounds of k tiles (32 bf16 / 16 fp32 channels each):
 //   scan    every lane holds one token of a 16-token sub-chunk and 8 (bf16) or 4 (fp32)
 //           channels; the cumulative log decay inside each sub-chunk is an in-row scan of the
 //           16 lanes (DPP row shifts), in log2 units; sub-chunk sums go through LDS
@@ -33,7 +35,7 @@ namespace gdn2 {
 
 // The (R, I) block pairs of the lower triangle (R >= I) of NS 16-token sub-chunks, numbered
 // off-diagonal pairs first ((1,0), (2,0), (2,1), (3,0), ...), then the diagonal; wave w
-// takes pairs w, w + 4, ...
+// takes pairs w, w + NWV, ...
 __device__ __forceinline__ void pair_of(int idx, int ns, int &R, int &I) {
     const int noff = ns * (ns - 1) / 2;
     if (idx >= noff) {
