@@ -254,7 +254,7 @@ void bwd_pre_kernel(B16Params p) {
 // ---------------------------------------------------------------------------------------
 // bwd_rchain_kernel: the reverse state pass. A workgroup owns NWS 16-column slices of dS of
 // one (sequence, value head): one chain wave per slice holds its d_k x 16 slice in fp32
-// registers, and two copy waves stage each chunk's Kg and Wn^T fragments, gamma_C and the
+// registers, and four copy waves stage each chunk's Kg and Wn^T fragments, gamma_C and the
 // slices' E1 and E2 tiles in LDS NBUF - 1 chunks ahead (direct global-to-LDS loads), so that
 // a chunk's staging latency overlaps several chunk steps. Each chunk step first issues all
 // of its LDS operand reads, then the products. The chain waves issue no global loads and
@@ -263,7 +263,7 @@ void bwd_pre_kernel(B16Params p) {
 // where they share the records in L2.
 template <int DK, int DV, int NWS>
 struct RChain {
-    static constexpr int NCP = 2;
+    static constexpr int NCP = 4;
     static constexpr int OPS = static_cast<int>(BL16<DK, DV>::OPS);
     static constexpr int NRT = DK / 16;
     static constexpr int EB = (C + DK) * 16 * 2;            // E1 and E2 tiles of one slice
@@ -280,14 +280,14 @@ struct RChain {
 
 // (one workgroup per CU by its LDS: the register budget of one wave per SIMD)
 template <int DK, int DV, int NWS>
-__global__ __launch_bounds__(64 * (NWS + 2)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * (NWS + 4)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_rchain_kernel(B16Params p) {
     using R_ = Rec<C, DK, DV, true>;
     using L_ = BL16<DK, DV>;
     using RC = RChain<DK, DV, NWS>;
     constexpr int RT = DK / 16, NKD = DK / 32, NCP = RC::NCP, OPS = RC::OPS, EB = RC::EB;
     constexpr int STAGE = RC::STAGE, G = RC::G, NBUF = RC::NBUF;
-    static_assert(NCP == 2 && (NBUF - 2) * RC::per(0) < 64 && EB % 1024 == 0, "vmcnt range");
+    static_assert(NCP == 4 && (NBUF - 2) * RC::per(0) < 64 && EB % 1024 == 0, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int bid = blockIdx.x, idx = bid >> 3;
     const int pair = (idx / G) * 8 + (bid & 7), part = idx - (idx / G) * G;
@@ -332,11 +332,16 @@ void bwd_rchain_kernel(B16Params p) {
     // copy waves: wait until the stage of chunk c has landed, with `newer` later-issued
     // stages allowed to stay in flight
     auto wait_stage = [&](int newer) {
-        if (newer <= 0) wait_vmem();
-        else if (newer == 1) {
-            if (cw == 0) wait_vmem_n<RC::per(0)>(); else wait_vmem_n<RC::per(1)>();
-        } else {
-            if (cw == 0) wait_vmem_n<(NBUF - 2) * RC::per(0)>(); else wait_vmem_n<(NBUF - 2) * RC::per(1)>();
+        if (newer <= 0) {
+            wait_vmem();
+            return;
+        }
+        const bool one = newer == 1;
+        switch (cw) {          // each copy wave counts its own loads per stage
+        case 0: if (one) wait_vmem_n<RC::per(0)>(); else wait_vmem_n<(NBUF - 2) * RC::per(0)>(); break;
+        case 1: if (one) wait_vmem_n<RC::per(1)>(); else wait_vmem_n<(NBUF - 2) * RC::per(1)>(); break;
+        case 2: if (one) wait_vmem_n<RC::per(2)>(); else wait_vmem_n<(NBUF - 2) * RC::per(2)>(); break;
+        default: if (one) wait_vmem_n<RC::per(3)>(); else wait_vmem_n<(NBUF - 2) * RC::per(3)>(); break;
         }
     };
 
