@@ -66,6 +66,40 @@ def test_chunk_forward_replays_in_a_graph():
         assert torch.equal(o, o_e) and torch.equal(S_T, S_e) and torch.equal(ck, ck_e)
 
 
+def test_chunk_backward_replays_in_a_graph():
+    """The bf16 chunked backward (its forward re-run, the reverse pass and the gradient
+    kernels), captured once: every replay equals the eager call bit for bit (one value head
+    per key head, so no atomics; a ragged last chunk)."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=700, h_k=2, h_v=2, d_k=128,
+                            d_v=128, neg_eig=True, s0_std=0.1)
+    x = {n: t.cuda() if isinstance(t, torch.Tensor) else t
+         for n, t in inputs.chunk_inputs(wl, seed=53).items()}
+    args = [x[n] for n in NAMES]
+    gen = torch.Generator().manual_seed(53)
+    dO = torch.randn(1, 700, 2, 128, generator=gen).to(torch.bfloat16).cuda()
+    dST = torch.randn(1, 2, 128, 128, generator=gen).cuda()
+    nbytes = g.chunk_bwd_workspace_bytes(1, 700, 2, 2, 128, 128, torch.bfloat16)
+    ref = g.chunk_bwd(*args, dO, S0=x["S0"], dS_T=dST,
+                      workspace=torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    box = {}
+
+    def call():
+        box["out"] = g.chunk_bwd(*args, dO, S0=x["S0"], dS_T=dST, workspace=ws)
+
+    graph = capture(call)
+    out = box["out"]
+    for rep in range(3):
+        for t in out.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] chunk backward replay {rep}", flush=True)
+        for n in ref:
+            assert torch.equal(out[n], ref[n]), n
+
+
 def test_decode_steps_replay_in_a_graph():
     """Four in-place decode steps on one state pool, captured once: every replay advances
     the state by the same four steps as the eager calls."""
