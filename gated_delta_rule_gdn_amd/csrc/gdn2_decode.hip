@@ -9,7 +9,7 @@
 //     u   = w . v - y
 //     S   = S' + k u^T                          (= (I - k (b.k)^T) S' + k (w.v)^T)
 //     o   = S^T q = z + (k . q) u
-// The llama.cpp decode notes (LocalAI mirror, section 2) describe the same fused
+// The GDN decode verify page (LocalAI mirror), section 2, describes the same fused
 // read-update-write of a persistent state, with the state held in registers across the
 // tokens of one call; section 4 notes that the step is bound by the traffic of the fp32
 // state and names a bf16 state as a way to cut it. This kernel therefore moves each state
@@ -18,7 +18,7 @@
 //
 // Optional fusions (burn-gdn2 "Architecture": ShortConv and L2-Norm before the recurrence,
 // Gated RMS Norm with a SiLU gate after it): a causal depthwise convolution of width 4 over
-// q, k and v with its three-input state in the cache (llama.cpp decode notes, sections 1
+// q, k and v with its three-input state in the cache (GDN decode verify page, sections 1
 // and 2), q and k divided by their L2 norms, and each output row replaced by
 // o / sqrt(mean o^2 + eps) * weight * silu(gate).
 //

@@ -14,7 +14,7 @@
  *                          prefill; chunk_size defaults to 64 on that page);
  *   - gdn2_recurrent_step  one fused token-by-token step ("FusedRecurrent" mode, decode),
  *                          which reads and writes a persistent state in place as the
- *                          llama.cpp decode notes (LocalAI mirror, section 2) describe.
+ *                          GDN decode verify page (LocalAI mirror), section 2, describes.
  *
  * Conventions (the pages are silent on these; this is the reading the library implements):
  *   - o_t reads the state AFTER the update of token t.
@@ -98,7 +98,7 @@ typedef enum gdn2_state_dtype {
  *   norm_eps     >= 0
  *
  * gdn2_recurrent_fwd only: the short causal depthwise convolution that the same diagram
- * puts before the L2-Norm (burn-gdn2 use_short_conv; the llama.cpp decode notes, section 1,
+ * puts before the L2-Norm (burn-gdn2 use_short_conv; the GDN decode verify page, section 1,
  * give its kernel width 4, and section 2 its state of the last 3 inputs per channel, kept
  * in the recurrent cache and read and written back every step). The convolved channels are
  * q, k and v, C = 2 h_k d_k + h_v d_v of them in that order (q of key head 0..h_k-1, then
@@ -241,11 +241,13 @@ size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
 
 /*
  * Gradients of gdn2_chunk_fwd (without fusion options, GDN-2 gates) with respect to every
- * input and the initial state (built for chunk_size 64, bf16 at any head dims and fp32 at
- * d_k = d_v = 64; other configurations return GDN2_ERR_UNSUPPORTED), taken through the chunked form of the burn-gdn2 docs page
+ * input and the initial state, taken through the chunked form of the burn-gdn2 docs page
  * ("Architecture", Chunk mode; its Chunk WY training path): the forward is re-run to store
  * the state entering every chunk, then one pass runs the state gradient backward over the
- * chunks, and one pass per chunk forms the input gradients.
+ * chunks, and one pass per chunk forms the input gradients. Built for chunk_size 64, with
+ * bf16 inputs at every supported head-dim pair (bf16 matrix-core products, fp32
+ * accumulation) and with fp32 inputs at d_k = d_v = 64 (fp32 products); other
+ * configurations return GDN2_ERR_UNSUPPORTED.
  *
  *   q .. w, S0, cu_seqlens, chunk_size, dims   as for gdn2_chunk_fwd
  *   dO          device [B, T, h_v, d_v] in the input dtype: dL/do
@@ -271,7 +273,7 @@ gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v,
 
 /*
  * One decode step for N sequences, one token each (burn-gdn2 "FusedRecurrent" mode; the
- * llama.cpp decode notes, section 2, describe the same fused state read-update-write).
+ * GDN decode verify page, section 2, describes the same fused state read-update-write).
  *
  *   q, k          device [N, h_k, d_k]   (dims->batch = N, dims->seqlen = 1)
  *   v, w          device [N, h_v, d_v]
@@ -287,7 +289,7 @@ gdn2_status gdn2_recurrent_step(const void *q, const void *k, const void *v,
 
 /*
  * Multi-token recurrent forward against a state cache (burn-gdn2 "FusedRecurrent" mode run
- * over T tokens). The llama.cpp decode notes (LocalAI mirror) describe, in section 2, the
+ * over T tokens). The GDN decode verify page (LocalAI mirror) describes, in section 2, the
  * recurrent cache whose slots hold one state per sequence and are read and written back
  * every step, and a fused kernel that keeps its share of a state in registers across the
  * tokens of the call; section 4 names a bf16 state as the way to cut the state traffic.

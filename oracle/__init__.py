@@ -11,7 +11,7 @@ Two independent evaluations of the method live here:
   (section "Architecture"), written out in plain C (``gdn2_oracle.c``), fp64, one
   (sequence, value head) pair at a time. ``decode_step`` is one token of it, and
   ``recurrent_cache`` runs it over a pool of stored states (the recurrent cache of the
-  llama.cpp decode notes, LocalAI mirror, section 2), optionally stored in bfloat16
+  GDN decode verify page, LocalAI mirror, section 2), optionally stored in bfloat16
   (section 4 of the same notes), with ``round_to_bf16`` the rounding of the stored state.
 * ``short_conv`` / ``conv_qkv``, ``l2_normalize`` and ``gated_rms_norm`` -- the stages
   the burn-gdn2 "Architecture" diagram draws around the recurrence (ShortConv and the
@@ -351,8 +351,8 @@ def gated_rms_norm(o, gate, weight, eps):
 def short_conv(x, weight, state, silu=False):
     """Causal depthwise convolution of width 4 along the token axis, one sequence.
 
-    The ShortConv stage of the burn-gdn2 "Architecture" diagram; the llama.cpp decode notes
-    give its width 4 (section 1) and its state, the last three inputs of every channel
+    The ShortConv stage of the burn-gdn2 "Architecture" diagram; the GDN decode verify page
+    gives its width 4 (section 1) and its state, the last three inputs of every channel
     (section 2). x [T, C] the inputs; weight [C, 4], tap 3 on the current token and tap 0
     on the input three tokens back; state [3, C] the three inputs before x, oldest first.
     With ``silu`` the output passes through y / (1 + exp(-y)) (the pages name no

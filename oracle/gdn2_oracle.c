@@ -17,7 +17,7 @@
  * alpha_t the channel-wise decay on the key axis. Readings taken where the page is
  * silent:
  *   - o_t reads the state after the update of token t (the equation names S with
- *     no index; the llama.cpp decode notes, section 2, read out after the rank-1
+ *     no index; the GDN decode verify page, section 2, reads out after the rank-1
  *     update).
  *   - the decay is passed as log(alpha_t) <= 0 and exponentiated here (the llama.cpp
  *     notes, section 2, carry the decay as g and apply exp(g)).

@@ -161,7 +161,7 @@ def test_exact_retrieval():
     assert np.max(np.abs(o[:, 0] - v[:, 0])) < 1e-13 * 10
 
 
-# ---- P5: the scalar-gate rule of the llama.cpp decode notes (section 2) ----------------
+# ---- P5: the scalar-gate rule of the GDN decode verify page (section 2) ----------------
 
 def test_scalar_gate_rule_of_llama_cpp_notes():
     """Decay s *= exp(g); sk = S^T k; delta d = (v - sk) * beta; s += k d^T; o = S^T q."""
@@ -344,7 +344,7 @@ def test_identity_token_leaves_state_unchanged():
 
 
 # ---- the recurrent cache: slots, padding entries, bf16-stored states ---------------------
-# (llama.cpp decode notes, LocalAI mirror: section 2 for the slot cache read and written back
+# (GDN decode verify page, LocalAI mirror: section 2 for the slot cache read and written back
 # every step, section 4 for a bf16 state)
 
 def test_round_to_bf16_closed_forms_and_torch_cast():
