@@ -13,11 +13,12 @@
 //
 // Every product here takes bf16 operands from LDS (or from the forward's records) and
 // accumulates in fp32; the reverse state pass keeps dS in fp32 registers. Kernels of one call:
-//   (forward re-run)    the chunked forward, also writing the state entering every chunk and
-//                       T of every record
+//   (forward re-run)    the chunked forward, also writing the state entering every chunk,
+//                       rounded to bf16 (the precision every product below takes it in), and T
+//                       of every record
 //   bwd_pre_kernel      per record: Kg and Wn^T as matrix-core fragments, E1 = M^T dO and
 //                       E2 = Qg^T dO, all from the forward's record and dO
-//   bwd_rchain_kernel   per (sequence, value head, 32 state columns), from the last chunk:
+//   bwd_rchain_kernel   per (sequence, value head, 16 state columns), from the last chunk:
 //                       dU = E1 + Kg dS' and dS = gamma_C dS' + E2 + Wn^T dU; writes dS' and dU
 //                       of every chunk (bf16) and dS0 (fp32)
 //   bwd_grads16_kernel  per record, every gradient of the chunk: U, dQg, dW~, dKg, dM,
@@ -59,7 +60,8 @@ struct B16Params {
     const int32_t *cu, *map;           // packed batches: offsets and chunk map, else NULL
     const char *rec;                   // records of the forward re-run
     const bf16_t *tmat;                // T per record, [C][C]
-    const float *ck;                   // state entering every chunk, [record][DK][DV]
+    const u32x4 *ck;                   // state entering every chunk: bf16 B fragments of the
+                                       // state pass, [record][DV/16][DK/32][64 lanes]
     char *crec, *cout;
     float *dq, *dk, *dv, *dw, *dla, *db, *dS0;
     int num_seqs, seqlen, nc_dense, h_k, h_v, group, num_pairs;
@@ -503,10 +505,10 @@ void bwd_grads16_kernel(B16Params p) {
     constexpr int SV = GL::SV, SK = GL::SK, SC = GL::SC, SQ = GL::SQ, SG = GL::SG;
     constexpr int NKD = DK / 32, NKV = DV / 32, RT = DK / 16, CT = DK / 16, VT = DV / 16;
     constexpr int TPW = NRC * CT / 8, UPW = NRC * VT / 8;
-    constexpr int NSV = DK * DV / 4 / 512, NOV = C * DV / 8 / 512, NKV8 = C * DK / 8 / 512;
+    constexpr int NSF = DK * DV / 8 / 512, NOV = C * DV / 8 / 512, NKV8 = C * DK / 8 / 512;
     constexpr int NUT = NRC * VT / 8, NDT = RT * VT / 8;
     constexpr int PARTS = 512 / DK, RP = C / PARTS;
-    static_assert(TPW >= 1 && UPW >= 1 && NSV >= 1 && NOV >= 1 && NUT >= 1 && NDT >= 1 && NKV8 >= 1 &&
+    static_assert(TPW >= 1 && UPW >= 1 && NSF >= 1 && NOV >= 1 && NUT >= 1 && NDT >= 1 && NKV8 >= 1 &&
                       PARTS * DK == 512 && 8 % RT == 0, "split");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     bf16_t *Tl = reinterpret_cast<bf16_t *>(smem + GL::T_);
@@ -527,15 +529,15 @@ void bwd_grads16_kernel(B16Params p) {
     const int hk = h / p.group;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const char *rec = p.rec + static_cast<size_t>(item) * R_::bytes;
-    const float *S = p.ck + static_cast<size_t>(item) * DK * DV;
+    const u32x4 *S = p.ck + static_cast<size_t>(item) * (DK * DV / 8);
     const char *co = p.cout + static_cast<size_t>(item) * L_::COUT;
     const bf16_t *Tg = p.tmat + static_cast<size_t>(item) * C * C;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     // every global load of both phases first
-    f32x4 sv[NSV];
+    u32x4 sv[NSF];
 #pragma unroll
-    for (int i = 0; i < NSV; ++i) sv[i] = reinterpret_cast<const f32x4 *>(S)[tid + 512 * i];
+    for (int i = 0; i < NSF; ++i) sv[i] = S[tid + 512 * i];
     u32x4 ov[NOV], wv[NOV], vv[NOV];
 #pragma unroll
     for (int i = 0; i < NOV; ++i) {
@@ -580,9 +582,10 @@ void bwd_grads16_kernel(B16Params p) {
     // ---- phase 1 ----
     if (tid < DK) dgl[tid] = 0.f;
 #pragma unroll
-    for (int i = 0; i < NSV; ++i) {
-        const int e = tid + 512 * i, row = e / (DV / 4), c4 = (e - row * (DV / 4)) * 4;
-        *reinterpret_cast<u32x2 *>(&Sl[row * SV + c4]) = f4_to_b16(sv[i]);
+    for (int i = 0; i < NSF; ++i) {          // fragment (column tile, k tile) = two D tiles
+        const int f = (tid >> 6) + 8 * i, ct = f / NKD, kt = f - ct * NKD;
+        put_tile16(Sl, SV, 32 * kt, 16 * ct, u32x2{sv[i].x, sv[i].y}, li, lg);
+        put_tile16(Sl, SV, 32 * kt + 16, 16 * ct, u32x2{sv[i].z, sv[i].w}, li, lg);
     }
 #pragma unroll
     for (int i = 0; i < NOV; ++i) {
@@ -957,9 +960,9 @@ constexpr int kChainSlices = 1;     // value slices per reverse-pass workgroup
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace of the bf16 backward: the forward's (map, records, segment buffers), then the
-// state entering every chunk, a scratch o, T per record, and the per-record buffers of BL16.
+// state entering every chunk (bf16), T per record, and the per-record buffers of BL16.
 struct B16Ws {
-    size_t ck, o, tm, crec, cout, total;
+    size_t ck, tm, crec, cout, total;
 };
 static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v, bool packed) {
     const int64_t nrec = chunk_upper_bound(C, batch, seqlen, num_seqs, packed) * h_v;
@@ -968,8 +971,7 @@ static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int
     const size_t cout = 2 * static_cast<size_t>(d_k) * d_v + 2 * static_cast<size_t>(C) * d_v;
     B16Ws w;
     w.ck = al256(chunk_workspace_bytes(C, batch, seqlen, num_seqs, h_v, d_k, d_v, true, packed));
-    w.o = al256(w.ck + static_cast<size_t>(nrec) * d_k * d_v * 4);
-    w.tm = al256(w.o + static_cast<size_t>(batch) * seqlen * h_v * d_v * 2);
+    w.tm = al256(w.ck + static_cast<size_t>(nrec) * d_k * d_v * 2);
     w.crec = al256(w.tm + static_cast<size_t>(nrec) * C * C * 2);
     w.cout = al256(w.crec + static_cast<size_t>(nrec) * crec);
     w.total = w.cout + static_cast<size_t>(nrec) * cout;
@@ -999,13 +1001,13 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
 
     ChunkArgs f;
     f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.b = a.b; f.w = a.w;
-    f.S0 = a.S0; f.cu_seqlens = a.cu_seqlens; f.o = base + ws.o; f.S_T = nullptr;
+    f.S0 = a.S0; f.cu_seqlens = a.cu_seqlens; f.o = nullptr; f.S_T = nullptr;   // states only
     f.workspace = base;
     f.batch = a.batch; f.seqlen = a.seqlen; f.num_seqs = a.num_seqs;
     f.h_k = a.h_k; f.h_v = a.h_v; f.d_k = DK; f.d_v = DV; f.bf16 = true;
     f.chunk = C;
     f.fu = Fusion{};
-    f.fu.cks = reinterpret_cast<float *>(base + ws.ck);
+    f.fu.cks16 = base + ws.ck;
     f.fu.tmat = base + ws.tm;
     hipError_t e = launch_chunk_fwd(f, st);
     if (e != hipSuccess) return e;
@@ -1020,7 +1022,7 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     p.map = packed ? reinterpret_cast<const int32_t *>(base) : nullptr;
     p.rec = base + chunk_map_bytes(a.num_seqs, packed);
     p.tmat = reinterpret_cast<const bf16_t *>(base + ws.tm);
-    p.ck = reinterpret_cast<const float *>(base + ws.ck);
+    p.ck = reinterpret_cast<const u32x4 *>(base + ws.ck);
     p.crec = base + ws.crec;
     p.cout = base + ws.cout;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dw = a.dw; p.dla = a.dla; p.db = a.db; p.dS0 = a.dS0;

@@ -54,6 +54,8 @@ struct ChunkParams {
     void *o;
     float *S_T;
     float *S_ck;         // state entering every chunk [chunk][h_v][DK][DV], or NULL
+    void *S_ck16;        // the same states as bf16 B fragments, [chunk][h_v][DV/16][DK/32][64]
+                         // x 16 B (64-token path, bf16 records only), or NULL
     char *rec;           // first per-(chunk, head) record
     void *tmat;          // bf16 inputs: T = (I + A)^-1 per record, [C][C] row-major, or NULL
     // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of

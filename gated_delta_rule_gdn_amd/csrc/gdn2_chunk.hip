@@ -281,10 +281,15 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
     // copy waves (wave >= 2 NW): stage chunk c's record part into a stage buffer; chunk c
     // of the workgroup's segment uses buffer (c - cb) & 1
     const int ldr = wave - 2 * NW;
+    // Without outputs (p.o == NULL: only the chunk states are wanted) Qg and M stay unstaged.
+    const bool outputs = p.o != nullptr;
     auto issue = [&](int c, char *dst) {
         const char *rec = record(c);
-        for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += NCOPY)
-            dma16(rec + blk * 1024 + lane * 16, dst + blk * 1024);
+        for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += NCOPY) {
+            const size_t off = static_cast<size_t>(blk) * 1024;
+            if (!outputs && ((off >= R_::Qg && off < R_::KgT) || off >= R_::M)) continue;
+            dma16(rec + off + lane * 16, dst + off);
+        }
         if (ldr == NCOPY - 1 && lane < static_cast<int>(SL::GCB / 16))
             dma16(rec + R_::gC + lane * 16, dst + SL::SHARED);
         // the slices' U~: column tiles slice*NW .. slice*NW + NW - 1 are contiguous in the
@@ -342,9 +347,9 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii)
                     R[j][ii] = Rg[static_cast<size_t>(16 * (r0 + j) + 4 * lg + ii) * DV + col];
-        } else if (CL::EARLY && g == 1 && ce > cb) {
+        } else if (CL::EARLY && g == 1 && ce > cb && outputs) {
             // P_1 has landed once no more than the first chunk's loads (issued after it; at
-            // least CB_MIN per copy wave) are outstanding
+            // least CB_MIN per copy wave with outputs) are outstanding
             wait_vmem_n<CB_MIN>();
         } else {
             wait_vmem();
@@ -420,13 +425,22 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
                     U[rt] = reinterpret_cast<const f32x4 *>(ut + rt * R_::UT_TILE)[lane];
                 }
             }
-            // publish S (chunk entry) as B operands, then its counter
+            // publish S (chunk entry) as B operands, then its counter; with S_ck16 the same
+            // bf16 fragments go to memory ([DV/16][DK/32][64 lanes] per record)
             u32x4 SB[NKD];
+            u32x4 *ck16 = nullptr;
+            if constexpr (BF) {
+                if (p.S_ck16)
+                    ck16 = static_cast<u32x4 *>(p.S_ck16) +
+                           (static_cast<size_t>(cbase + c) * p.h_v + h) * (DK * DV / 8) +
+                           static_cast<size_t>(ct) * NKD * 64;
+            }
 #pragma unroll
             for (int kt = 0; kt < NKD; ++kt) {
                 if constexpr (BF) SB[kt] = dpair_to_b32(S[2 * kt], S[2 * kt + 1]);
                 else SB[kt] = __builtin_bit_cast(u32x4, S[kt]);
-                xS[kt * 64 + lane] = SB[kt];
+                if (outputs) xS[kt * 64 + lane] = SB[kt];
+                if (ck16) ck16[kt * 64 + lane] = SB[kt];
             }
             if (lane == 0) *flagS = c + 1;
             __builtin_amdgcn_sched_barrier(0);
@@ -452,7 +466,7 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
             for (int kt = 0; kt < NKC; ++kt) {
                 if constexpr (BF) UB[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
                 else UB[kt] = __builtin_bit_cast(u32x4, U[kt]);
-                xU[kt * 64 + lane] = UB[kt];
+                if (outputs) xU[kt * 64 + lane] = UB[kt];
             }
             if (lane == 0) *flagU = c + 1;
             // S = gamma_C S + KgT U
@@ -476,6 +490,10 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
     }
 
     // ---- output wave ----
+    if (!outputs) {                         // states only: meet the chunk barriers, nothing else
+        for (int c = cb; c < ce; ++c) raw_barrier();
+        return;
+    }
     for (int c = cb; c < ce; ++c) {
         const char *cur = smem + ((c - cb) & 1) * BUF;
         raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
@@ -907,6 +925,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     ChunkParams p{};
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.b = a.b; p.w = a.w;
     p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks; p.tmat = a.fu.tmat;
+    p.S_ck16 = a.fu.cks16;
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
     p.rec = a.workspace + mapb;
@@ -986,6 +1005,7 @@ static hipError_t launch_chunk_dt(const ChunkArgs &a, hipStream_t st) {
 // Generic path: any built chunk size, both dtypes, all head dims; the state pass walks each
 // chunk in row panels and runs every (sequence, head) from its start (no segments).
 static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
+    if (a.fu.cks16 != nullptr) return hipErrorInvalidValue;   // written by the 64-token pass only
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
     const int C = a.chunk;
