@@ -533,18 +533,23 @@ void bwd_grads16_kernel(B16Params p) {
     const char *co = p.cout + static_cast<size_t>(item) * L_::COUT;
     const bf16_t *Tg = p.tmat + static_cast<size_t>(item) * C * C;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // token strides (elements) of the [.., h, d] gradient layouts
+    const int tsv = p.h_v * DV, tsk = p.h_k * DK, tsg = p.h_v * DK;
 
     // every global load of both phases first
     u32x4 sv[NSF];
 #pragma unroll
     for (int i = 0; i < NSF; ++i) sv[i] = S[tid + 512 * i];
+    // row r0 + (512 / (d / 8)) i and columns c8 .. c8 + 7 of the [C][d] tiles for this thread
+    const int rv0 = tid / (DV / 8), cv8 = (tid - rv0 * (DV / 8)) * 8;
+    const size_t ov0 = (static_cast<size_t>(t0 + rv0) * p.h_v + h) * DV + cv8;
     u32x4 ov[NOV], wv[NOV], vv[NOV];
 #pragma unroll
     for (int i = 0; i < NOV; ++i) {
-        const int e = tid + 512 * i, r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+        const int r = rv0 + (512 / (DV / 8)) * i;
         ov[i] = wv[i] = vv[i] = zero4;
         if (r < Lr) {
-            const size_t off = (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c8;
+            const size_t off = ov0 + static_cast<size_t>((512 / (DV / 8)) * i) * tsv;
             ov[i] = *reinterpret_cast<const u32x4 *>(p.dO + off);
             wv[i] = *reinterpret_cast<const u32x4 *>(p.w + off);
             vv[i] = *reinterpret_cast<const u32x4 *>(p.v + off);
@@ -564,14 +569,17 @@ void bwd_grads16_kernel(B16Params p) {
 #pragma unroll
     for (int jj = 0; jj < UPW; ++jj)
         utv[jj] = reinterpret_cast<const u32x2 *>(rec + R_::Ut + static_cast<size_t>((uct0 + jj) * NRC + urt) * R_::UT_TILE)[lane];
+    const int rk0 = tid / (DK / 8), ck8 = (tid - rk0 * (DK / 8)) * 8;
+    const size_t ok0 = (static_cast<size_t>(t0 + rk0) * p.h_k + hk) * DK + ck8;
+    const size_t og0 = (static_cast<size_t>(t0 + rk0) * p.h_v + h) * DK + ck8;
     u32x4 kv[NKV8], bv[NKV8], qv[NKV8], av[NKV8];
 #pragma unroll
     for (int i = 0; i < NKV8; ++i) {
-        const int e = tid + 512 * i, r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+        const int r = rk0 + (512 / (DK / 8)) * i;
         kv[i] = bv[i] = qv[i] = av[i] = zero4;
         if (r < Lr) {
-            const size_t ok = (static_cast<size_t>(t0 + r) * p.h_k + hk) * DK + c8;
-            const size_t og = (static_cast<size_t>(t0 + r) * p.h_v + h) * DK + c8;
+            const size_t ok = ok0 + static_cast<size_t>((512 / (DK / 8)) * i) * tsk;
+            const size_t og = og0 + static_cast<size_t>((512 / (DK / 8)) * i) * tsg;
             kv[i] = *reinterpret_cast<const u32x4 *>(p.k + ok);
             qv[i] = *reinterpret_cast<const u32x4 *>(p.q + ok);
             bv[i] = *reinterpret_cast<const u32x4 *>(p.b + og);
@@ -703,11 +711,13 @@ void bwd_grads16_kernel(B16Params p) {
 #pragma unroll
         for (int kt = 0; kt < NKC; ++kt)
             acc = mma_k32(col_frag(Tl, SC, 32 * kt, 16 * urt, li, lg), col_frag(dUl, SV, 32 * kt, 16 * ct, li, lg), acc);
+        const int x0 = 16 * urt + 4 * lg, col = 16 * ct + li;
+        const size_t o0 = (static_cast<size_t>(t0 + x0) * p.h_v + h) * DV + col;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int x = 16 * urt + 4 * lg + ii, col = 16 * ct + li;
+            const int x = x0 + ii;
             if (x < Lr) {
-                const size_t off = (static_cast<size_t>(t0 + x) * p.h_v + h) * DV + col;
+                const size_t off = o0 + static_cast<size_t>(ii) * tsv;
                 p.dv[off] = f32of(&wl[x * SV + col]) * acc[ii];
                 p.dw[off] = f32of(&vl[x * SV + col]) * acc[ii];
             }
@@ -883,9 +893,12 @@ void bwd_grads16_kernel(B16Params p) {
         }
         const float gL = gl[(C - 1) * SG + c];
         float sg = 0.f, sk = 0.f;
+        const int x0 = 16 * B + 4 * lg;
+        const size_t okx = (static_cast<size_t>(t0 + x0) * p.h_k + hk) * DK + c;
+        const size_t ogx = (static_cast<size_t>(t0 + x0) * p.h_v + h) * DK + c;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int x = 16 * B + 4 * lg + ii;
+            const int x = x0 + ii;
             const float gx = gl[x * SG + c];
             const float f0 = exp2_hw(gx - grho), f1 = exp2_hw(grho - gx);
             const float p1 = a1[ii] * f0, p3 = a3[ii] * f0, p2 = a2[ii] * f1, p4 = a4[ii] * f1;
@@ -900,8 +913,8 @@ void bwd_grads16_kernel(B16Params p) {
             sg += g_;
             sk += kd;
             if (x < Lr) {
-                const size_t ok = (static_cast<size_t>(t0 + x) * p.h_k + hk) * DK + c;
-                const size_t og = (static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c;
+                const size_t ok = okx + static_cast<size_t>(ii) * tsk;
+                const size_t og = ogx + static_cast<size_t>(ii) * tsg;
                 const float vq = p3 + ga * dq_, vk = p4 + p2 + fk * dk_ + bb * dbk;
                 if (p.group == 1) {
                     p.dq[ok] = vq;
@@ -937,11 +950,11 @@ void bwd_grads16_kernel(B16Params p) {
         const float o1 = __shfl(own[jj], li + 16), o2 = __shfl(own[jj], li + 32), o3 = __shfl(own[jj], li + 48);
         const float below = (lg < 1 ? o1 : 0.f) + (lg < 2 ? o2 : 0.f) + (lg < 3 ? o3 : 0.f);
         float acc = exp2_hw(gl[(C - 1) * SG + c]) * dgl[c] + all + later + below;
+        float *dla0 = p.dla + (static_cast<size_t>(t0 + 16 * B + 4 * lg) * p.h_v + h) * DK + c;
 #pragma unroll
         for (int ii = 3; ii >= 0; --ii) {
             acc += dgv[jj][ii];
-            const int x = 16 * B + 4 * lg + ii;
-            if (x < Lr) p.dla[(static_cast<size_t>(t0 + x) * p.h_v + h) * DK + c] = acc;
+            if (16 * B + 4 * lg + ii < Lr) dla0[static_cast<size_t>(ii) * tsg] = acc;
         }
     }
 }
