@@ -851,46 +851,78 @@ void bwd_grads16_kernel(B16Params p) {
     }
     lds_barrier();
 
-    // the decay sums and the elementwise chain rule on the own tiles
+    // The decay sums of the own tiles. All of a wave's tiles lie in channel tile wave % CT
+    // (8 % CT == 0), so the factor operands are formed once per 16-row block kb, relative to
+    // that block's middle row: F = k 2^(g_mid(kb) - g_i) (P1, P3), G2 = bk 2^(g_r - g_mid(kb))
+    // and G4 = q 2^(g_r - g_mid(kb)) (P2, P4). A tile of row block B takes block kb's products
+    // scaled by 2^(g_mid(B) - g_mid(kb)) (kb < B) or 2^(g_mid(kb) - g_mid(B)) (kb > B), both
+    // <= 1 and one per channel, i.e. per lane; at kb = B the factor is 1.
     const bf16_t *dAl = dTl;
+    const int cw = 16 * (wave % CT) + li;
+    f32x4 A1[TPW], A2[TPW], A3[TPW], A4[TPW];
+    float gmB[TPW];
+#pragma unroll
+    for (int jj = 0; jj < TPW; ++jj) {
+        const int B = (wave + 8 * jj) / CT;
+        gmB[jj] = gl[(16 * B + 7) * SG + cw];
+        A1[jj] = A2[jj] = A3[jj] = A4[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kb = 0; kb < NRC; ++kb) {
+        const float gm = gl[(16 * kb + 7) * SG + cw];
+        float f[4], f2[4], f4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * kb + 4 * lg + e;
+            const float gi = gl[i * SG + cw], kk = f32of(&kl[i * SQ + cw]);
+            const float ex = exp2_hw(gi - gm);
+            f[e] = kk * exp2_hw(gm - gi);
+            f2[e] = f32of(&bl[i * SQ + cw]) * kk * ex;
+            f4[e] = f32of(&ql[i * SQ + cw]) * ex;
+        }
+        u32x2 fh, fl, h2, l2, h4, l4;
+        split4(f, fh, fl);
+        split4(f2, h2, l2);
+        split4(f4, h4, l4);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) {
+            const int B = (wave + 8 * jj) / CT;
+            if (kb <= B) {                      // P1, P3: i in block kb
+                const u32x2 d1 = *reinterpret_cast<const u32x2 *>(&dAl[(16 * B + li) * SC + 16 * kb + 4 * lg]);
+                const u32x2 d3 = *reinterpret_cast<const u32x2 *>(&dMl[(16 * B + li) * SC + 16 * kb + 4 * lg]);
+                if (kb == B) {
+                    A1[jj] = mma_k16_bf16(d1, fl, mma_k16_bf16(d1, fh, A1[jj]));
+                    A3[jj] = mma_k16_bf16(d3, fl, mma_k16_bf16(d3, fh, A3[jj]));
+                } else {
+                    const float sc = exp2_hw(gmB[jj] - gm);
+                    A1[jj] += sc * mma_k16_bf16(d1, fl, mma_k16_bf16(d1, fh, z));
+                    A3[jj] += sc * mma_k16_bf16(d3, fl, mma_k16_bf16(d3, fh, z));
+                }
+            }
+            if (kb >= B) {                      // P2, P4: r in block kb
+                const int ofs = (16 * kb + 4 * lg + (li >> 2)) * SC + 16 * B + 4 * (li & 3);
+                const u32x2 d2 = lds_tr4(&dAl[ofs]);
+                const u32x2 d4 = lds_tr4(&dMl[ofs]);
+                if (kb == B) {
+                    A2[jj] = mma_k16_bf16(d2, l2, mma_k16_bf16(d2, h2, A2[jj]));
+                    A4[jj] = mma_k16_bf16(d4, l4, mma_k16_bf16(d4, h4, A4[jj]));
+                } else {
+                    const float sc = exp2_hw(gm - gmB[jj]);
+                    A2[jj] += sc * mma_k16_bf16(d2, l2, mma_k16_bf16(d2, h2, z));
+                    A4[jj] += sc * mma_k16_bf16(d4, l4, mma_k16_bf16(d4, h4, z));
+                }
+            }
+        }
+    }
+
+    // the elementwise chain rule on the own tiles
     float dgv[TPW][4], own[TPW];
 #pragma unroll
     for (int jj = 0; jj < TPW; ++jj) {
-        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT, c = 16 * ct + li, rho = 16 * B + 7;
-        const float grho = gl[rho * SG + c];
-        f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1, a3 = a1, a4 = a1;
-        for (int kb = 0; kb <= B; ++kb) {       // P1, P3 over i in blocks 0 .. B
-            const u32x2 d1 = *reinterpret_cast<const u32x2 *>(&dAl[(16 * B + li) * SC + 16 * kb + 4 * lg]);
-            const u32x2 d3 = *reinterpret_cast<const u32x2 *>(&dMl[(16 * B + li) * SC + 16 * kb + 4 * lg]);
-            float f[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * kb + 4 * lg + e;
-                f[e] = f32of(&kl[i * SQ + c]) * exp2_hw(grho - gl[i * SG + c]);
-            }
-            u32x2 fh, fl;
-            split4(f, fh, fl);
-            a1 = mma_k16_bf16(d1, fl, mma_k16_bf16(d1, fh, a1));
-            a3 = mma_k16_bf16(d3, fl, mma_k16_bf16(d3, fh, a3));
-        }
-        for (int kb = B; kb < NRC; ++kb) {      // P2, P4 over r in blocks B .. C/16 - 1
-            const int ofs = (16 * kb + 4 * lg + (li >> 2)) * SC + 16 * B + 4 * (li & 3);
-            const u32x2 d2 = lds_tr4(&dAl[ofs]);
-            const u32x2 d4 = lds_tr4(&dMl[ofs]);
-            float f2[4], f4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * kb + 4 * lg + e;
-                const float ex = exp2_hw(gl[r * SG + c] - grho);
-                f2[e] = f32of(&bl[r * SQ + c]) * f32of(&kl[r * SQ + c]) * ex;
-                f4[e] = f32of(&ql[r * SQ + c]) * ex;
-            }
-            u32x2 h2, l2, h4, l4;
-            split4(f2, h2, l2);
-            split4(f4, h4, l4);
-            a2 = mma_k16_bf16(d2, l2, mma_k16_bf16(d2, h2, a2));
-            a4 = mma_k16_bf16(d4, l4, mma_k16_bf16(d4, h4, a4));
-        }
+        const int t = wave + 8 * jj, B = t / CT, ct = t - B * CT, c = 16 * ct + li;
+        const float grho = gmB[jj];
+        const f32x4 a1 = A1[jj], a2 = A2[jj], a3 = A3[jj], a4 = A4[jj];
         const float gL = gl[(C - 1) * SG + c];
         float sg = 0.f, sk = 0.f;
         const int x0 = 16 * B + 4 * lg;
