@@ -13,9 +13,9 @@
 //
 // Every product here takes bf16 operands from LDS (or from the forward's records) and
 // accumulates in fp32; the reverse state pass keeps dS in fp32 registers. Kernels of one call:
-//   (forward re-run)    the chunked forward, also writing the state entering every chunk,
-//                       rounded to bf16 (the precision every product below takes it in), and T
-//                       of every record
+//   (forward re-run)    the chunked forward without o, also writing the state entering every
+//                       chunk and U = U~ + Wn S of every chunk as bf16 fragments (the precision
+//                       every product below takes them in), and T of every record
 //   bwd_pre_kernel      per record: Kg and Wn^T as matrix-core fragments, E1 = M^T dO and
 //                       E2 = Qg^T dO, all from the forward's record and dO
 //   bwd_rchain_kernel   per (sequence, value head, 16 state columns), from the last chunk:
@@ -62,6 +62,8 @@ struct B16Params {
     const bf16_t *tmat;                // T per record, [C][C]
     const u32x4 *ck;                   // state entering every chunk: bf16 B fragments of the
                                        // state pass, [record][DV/16][DK/32][64 lanes]
+    const u32x4 *uck;                  // U = U~ + Wn S of every chunk, the same fragments
+                                       // [record][DV/16][C/32][64 lanes]
     char *crec, *cout;
     float *dq, *dk, *dv, *dw, *dla, *db, *dS0;
     int num_seqs, seqlen, nc_dense, h_k, h_v, group, num_pairs;
@@ -499,16 +501,16 @@ struct GLay {
 template <int DK, int DV>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_grads16_kernel(B16Params p) {
-    using R_ = Rec<C, DK, DV, true>;
     using L_ = BL16<DK, DV>;
     using GL = GLay<DK, DV>;
     constexpr int SV = GL::SV, SK = GL::SK, SC = GL::SC, SQ = GL::SQ, SG = GL::SG;
     constexpr int NKD = DK / 32, NKV = DV / 32, RT = DK / 16, CT = DK / 16, VT = DV / 16;
     constexpr int TPW = NRC * CT / 8, UPW = NRC * VT / 8;
-    constexpr int NSF = DK * DV / 8 / 512, NOV = C * DV / 8 / 512, NKV8 = C * DK / 8 / 512;
+    constexpr int NSF = DK * DV / 8 / 512, NUF = C * DV / 8 / 512, NOV = C * DV / 8 / 512,
+                  NKV8 = C * DK / 8 / 512;
     constexpr int NUT = NRC * VT / 8, NDT = RT * VT / 8;
     constexpr int PARTS = 512 / DK, RP = C / PARTS;
-    static_assert(TPW >= 1 && UPW >= 1 && NSF >= 1 && NOV >= 1 && NUT >= 1 && NDT >= 1 && NKV8 >= 1 &&
+    static_assert(TPW >= 1 && UPW >= 1 && NSF >= 1 && NUF >= 1 && NOV >= 1 && NUT >= 1 && NDT >= 1 && NKV8 >= 1 &&
                       PARTS * DK == 512 && 8 % RT == 0, "split");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     bf16_t *Tl = reinterpret_cast<bf16_t *>(smem + GL::T_);
@@ -528,7 +530,6 @@ void bwd_grads16_kernel(B16Params p) {
     const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
     const int hk = h / p.group;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-    const char *rec = p.rec + static_cast<size_t>(item) * R_::bytes;
     const u32x4 *S = p.ck + static_cast<size_t>(item) * (DK * DV / 8);
     const char *co = p.cout + static_cast<size_t>(item) * L_::COUT;
     const bf16_t *Tg = p.tmat + static_cast<size_t>(item) * C * C;
@@ -562,13 +563,9 @@ void bwd_grads16_kernel(B16Params p) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) dsv[i] = reinterpret_cast<const u32x2 *>(co + L_::DSN)[(wave + 8 * i) * 64 + lane];
     const int urt = wave >> 1, uct0 = (wave & 1) * UPW;
-    u32x4 wnf[NKD];
+    u32x4 uf[NUF];                      // U of the forward's state pass
 #pragma unroll
-    for (int kt = 0; kt < NKD; ++kt) wnf[kt] = reinterpret_cast<const u32x4 *>(rec + R_::Wn)[(urt * NKD + kt) * 64 + lane];
-    u32x2 utv[UPW];
-#pragma unroll
-    for (int jj = 0; jj < UPW; ++jj)
-        utv[jj] = reinterpret_cast<const u32x2 *>(rec + R_::Ut + static_cast<size_t>((uct0 + jj) * NRC + urt) * R_::UT_TILE)[lane];
+    for (int i = 0; i < NUF; ++i) uf[i] = p.uck[static_cast<size_t>(item) * (C * DV / 8) + tid + 512 * i];
     const int rk0 = tid / (DK / 8), ck8 = (tid - rk0 * (DK / 8)) * 8;
     const size_t ok0 = (static_cast<size_t>(t0 + rk0) * p.h_k + hk) * DK + ck8;
     const size_t og0 = (static_cast<size_t>(t0 + rk0) * p.h_v + h) * DK + ck8;
@@ -611,17 +608,14 @@ void bwd_grads16_kernel(B16Params p) {
         const int ti = wave + 8 * i, s = ti / NRC, ut = ti - s * NRC;
         put_tile16(dUl, SV, 16 * ut, 16 * s, duv[i], li, lg);
     }
+#pragma unroll
+    for (int i = 0; i < NUF; ++i) {          // fragment (column tile, token k tile) = two D tiles
+        const int f = (tid >> 6) + 8 * i, ct = f / NKC, kt = f - ct * NKC;
+        put_tile16(Ul, SV, 32 * kt, 16 * ct, u32x2{uf[i].x, uf[i].y}, li, lg);
+        put_tile16(Ul, SV, 32 * kt + 16, 16 * ct, u32x2{uf[i].z, uf[i].w}, li, lg);
+    }
     lds_barrier();
 
-    // U = U~ + Wn S
-#pragma unroll
-    for (int jj = 0; jj < UPW; ++jj) {
-        const int ct = uct0 + jj;
-        f32x4 acc = b16_to_f4(utv[jj]);
-#pragma unroll
-        for (int kt = 0; kt < NKD; ++kt) acc = mma_k32(wnf[kt], col_frag(Sl, SV, 32 * kt, 16 * ct, li, lg), acc);
-        put_tile(Ul, SV, 16 * urt, 16 * ct, acc, li, lg);
-    }
     // dQg = dO S^T, dW~ = -dU S^T (kept for phase 2)
     f32x4 dqg[TPW];
     u32x2 dwv[TPW];
@@ -1005,9 +999,10 @@ constexpr int kChainSlices = 1;     // value slices per reverse-pass workgroup
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace of the bf16 backward: the forward's (map, records, segment buffers), then the
-// state entering every chunk (bf16), T per record, and the per-record buffers of BL16.
+// state entering every chunk and U of every chunk (bf16 fragments), T per record, and the
+// per-record buffers of BL16.
 struct B16Ws {
-    size_t ck, tm, crec, cout, total;
+    size_t ck, cu, tm, crec, cout, total;
 };
 static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v, bool packed) {
     const int64_t nrec = chunk_upper_bound(C, batch, seqlen, num_seqs, packed) * h_v;
@@ -1016,7 +1011,8 @@ static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int
     const size_t cout = 2 * static_cast<size_t>(d_k) * d_v + 2 * static_cast<size_t>(C) * d_v;
     B16Ws w;
     w.ck = al256(chunk_workspace_bytes(C, batch, seqlen, num_seqs, h_v, d_k, d_v, true, packed));
-    w.tm = al256(w.ck + static_cast<size_t>(nrec) * d_k * d_v * 2);
+    w.cu = al256(w.ck + static_cast<size_t>(nrec) * d_k * d_v * 2);
+    w.tm = al256(w.cu + static_cast<size_t>(nrec) * C * d_v * 2);
     w.crec = al256(w.tm + static_cast<size_t>(nrec) * C * C * 2);
     w.cout = al256(w.crec + static_cast<size_t>(nrec) * crec);
     w.total = w.cout + static_cast<size_t>(nrec) * cout;
@@ -1053,6 +1049,7 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     f.chunk = C;
     f.fu = Fusion{};
     f.fu.cks16 = base + ws.ck;
+    f.fu.cku16 = base + ws.cu;
     f.fu.tmat = base + ws.tm;
     hipError_t e = launch_chunk_fwd(f, st);
     if (e != hipSuccess) return e;
@@ -1068,6 +1065,7 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     p.rec = base + chunk_map_bytes(a.num_seqs, packed);
     p.tmat = reinterpret_cast<const bf16_t *>(base + ws.tm);
     p.ck = reinterpret_cast<const u32x4 *>(base + ws.ck);
+    p.uck = reinterpret_cast<const u32x4 *>(base + ws.cu);
     p.crec = base + ws.crec;
     p.cout = base + ws.cout;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dw = a.dw; p.dla = a.dla; p.db = a.db; p.dS0 = a.dS0;

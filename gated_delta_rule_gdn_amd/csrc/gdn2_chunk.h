@@ -56,6 +56,8 @@ struct ChunkParams {
     float *S_ck;         // state entering every chunk [chunk][h_v][DK][DV], or NULL
     void *S_ck16;        // the same states as bf16 B fragments, [chunk][h_v][DV/16][DK/32][64]
                          // x 16 B (64-token path, bf16 records only), or NULL
+    void *U_ck16;        // U = U~ + Wn S of every chunk as bf16 B fragments, [chunk][h_v]
+                         // [DV/16][C/32][64] x 16 B (same paths), or NULL
     char *rec;           // first per-(chunk, head) record
     void *tmat;          // bf16 inputs: T = (I + A)^-1 per record, [C][C] row-major, or NULL
     // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of

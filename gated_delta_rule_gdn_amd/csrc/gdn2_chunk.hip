@@ -460,13 +460,21 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
                 for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
-            // publish U as B operands, then its counter
+            // publish U as B operands, then its counter (and, with U_ck16, to memory)
             u32x4 UB[NKC];
+            u32x4 *cku = nullptr;
+            if constexpr (BF) {
+                if (p.U_ck16)
+                    cku = static_cast<u32x4 *>(p.U_ck16) +
+                          (static_cast<size_t>(cbase + c) * p.h_v + h) * (C * DV / 8) +
+                          static_cast<size_t>(ct) * NKC * 64;
+            }
 #pragma unroll
             for (int kt = 0; kt < NKC; ++kt) {
                 if constexpr (BF) UB[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
                 else UB[kt] = __builtin_bit_cast(u32x4, U[kt]);
                 if (outputs) xU[kt * 64 + lane] = UB[kt];
+                if (cku) cku[kt * 64 + lane] = UB[kt];
             }
             if (lane == 0) *flagU = c + 1;
             // S = gamma_C S + KgT U
@@ -926,6 +934,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.q = a.q; p.k = a.k; p.v = a.v; p.log_alpha = a.log_alpha; p.b = a.b; p.w = a.w;
     p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks; p.tmat = a.fu.tmat;
     p.S_ck16 = a.fu.cks16;
+    p.U_ck16 = a.fu.cku16;
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
     p.rec = a.workspace + mapb;
@@ -1005,7 +1014,7 @@ static hipError_t launch_chunk_dt(const ChunkArgs &a, hipStream_t st) {
 // Generic path: any built chunk size, both dtypes, all head dims; the state pass walks each
 // chunk in row panels and runs every (sequence, head) from its start (no segments).
 static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
-    if (a.fu.cks16 != nullptr) return hipErrorInvalidValue;   // written by the 64-token pass only
+    if (a.fu.cks16 || a.fu.cku16) return hipErrorInvalidValue;   // written by the 64-token pass only
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
     const int C = a.chunk;

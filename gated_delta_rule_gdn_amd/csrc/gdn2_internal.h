@@ -27,6 +27,7 @@ struct Fusion {
     int gmode = 0;                   // GateMode of the b / w arguments (0: GDN-2 gates)
     float *cks = nullptr;            // chunked forward: state entering every chunk, or NULL
     void *cks16 = nullptr;           // the same as bf16 fragments (64-token path), or NULL
+    void *cku16 = nullptr;           // U of every chunk as bf16 fragments (64-token path), or NULL
     void *tmat = nullptr;            // chunked forward, bf16: T = (I + A)^-1 per record, or NULL
 };
 
