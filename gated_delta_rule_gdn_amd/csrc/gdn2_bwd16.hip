@@ -15,13 +15,14 @@
 // accumulates in fp32; the reverse state pass keeps dS in fp32 registers. Kernels of one call:
 //   (forward re-run)    the chunked forward without o, also writing the state entering every
 //                       chunk and U = U~ + Wn S of every chunk as bf16 fragments (the precision
-//                       every product below takes them in), and T of every record
-//   bwd_pre_kernel      per record: Kg and Wn^T as matrix-core fragments, E1 = M^T dO and
-//                       E2 = Qg^T dO, all from the forward's record and dO
+//                       every product below takes them in) and T of every record; its state
+//                       pass's output waves form the reverse pass's operands from each staged
+//                       record and dO: Kg and Wn^T as matrix-core fragments, E1 = M^T dO and
+//                       E2 = Qg^T dO (BwdOps)
 //   bwd_rchain_kernel   per (sequence, value head, 16 state columns), from the last chunk:
 //                       dU = E1 + Kg dS' and dS = gamma_C dS' + E2 + Wn^T dU; writes dS' and dU
 //                       of every chunk (bf16) and dS0 (fp32)
-//   bwd_grads16_kernel  per record, every gradient of the chunk: U, dQg, dW~, dKg, dM,
+//   bwd_grads16_kernel  per record, every gradient of the chunk: dQg, dW~, dKg, dM,
 //                       dX (-> dv, dw), dT, dA, the decay sums, dq, dk, db and dlog_alpha
 #include "gdn2_chunk.h"
 
@@ -41,13 +42,14 @@ template <int K> struct Pad { static constexpr int S = K == 64 ? 72 : 152; };
 // Per-record buffers (bytes).
 template <int DK, int DV>
 struct BL16 {
-    // bwd_pre_kernel -> bwd_rchain_kernel
-    static constexpr size_t KgA = 0;                                      // Kg, A fragments [C][DK]
-    static constexpr size_t WnT = KgA + static_cast<size_t>(C) * DK * 2;  // Wn^T, A fragments [DK][C]
-    static constexpr size_t OPS = WnT + static_cast<size_t>(DK) * C * 2;
-    static constexpr size_t E1 = OPS;                                     // bf16 D tiles [slice][C/16]
-    static constexpr size_t E2 = E1 + static_cast<size_t>(C) * DV * 2;    // bf16 D tiles [slice][DK/16]
-    static constexpr size_t CREC = E2 + static_cast<size_t>(DK) * DV * 2;
+    // the forward re-run's state pass -> bwd_rchain_kernel (BwdOps, gdn2_chunk.h)
+    using BO = BwdOps<DK, DV>;
+    static constexpr size_t KgA = BO::KgA;                                // Kg, A fragments [C][DK]
+    static constexpr size_t WnT = BO::WnT;                                // Wn^T, A fragments [DK][C]
+    static constexpr size_t OPS = BO::E1;
+    static constexpr size_t E1 = BO::E1;                                  // bf16 D tiles [slice][C/16]
+    static constexpr size_t E2 = BO::E2;                                  // bf16 D tiles [slice][DK/16]
+    static constexpr size_t CREC = BO::bytes;
     // bwd_rchain_kernel -> bwd_grads16_kernel, bf16 D tiles
     static constexpr size_t DSN = 0;                                      // dS' [slice][DK/16]
     static constexpr size_t DU = DSN + static_cast<size_t>(DK) * DV * 2;  // dU [slice][C/16]
@@ -107,12 +109,6 @@ __device__ __forceinline__ u32x4 col_frag(const bf16_t *t, int stride, int k0, i
     const u32x2 b = lds_tr4(q + 16 * stride);
     return u32x4{a.x, a.y, b.x, b.y};
 }
-// An A fragment block of a record (16 rows x 32 k) back into a row-major tile.
-__device__ __forceinline__ void frag_to_rows(bf16_t *t, int stride, int r0, int k0, u32x4 f, int li, int lg) {
-    bf16_t *q = t + (r0 + li) * stride + k0 + 4 * lg;
-    *reinterpret_cast<u32x2 *>(q) = u32x2{f.x, f.y};
-    *reinterpret_cast<u32x2 *>(q + 16) = u32x2{f.z, f.w};
-}
 // One lane's part of a 16x16 output tile (rows r0 + 4 lg + ii, column c0 + li) into a
 // row-major bf16 tile, from fp32 or from bf16 already rounded.
 __device__ __forceinline__ void put_tile(bf16_t *t, int stride, int r0, int c0, f32x4 v, int li, int lg) {
@@ -138,121 +134,6 @@ __device__ __forceinline__ void split4(const float (&x)[4], u32x2 &hi, u32x2 &lo
     hi.y = pack_bf16x2(x[2], x[3]);
     lo.x = pack_bf16x2(x[0] - bf16_lo(hi.x), x[1] - bf16_hi(hi.x));
     lo.y = pack_bf16x2(x[2] - bf16_lo(hi.y), x[3] - bf16_hi(hi.y));
-}
-
-// ---------------------------------------------------------------------------------------
-// bwd_pre_kernel: per record, the reverse pass's operands (one workgroup per CU by its LDS,
-// hence the register budget of one wave per SIMD). The forward record's Wn, Qg, KgT
-// and M fragments are put back into row-major LDS tiles (blocks of M above the diagonal,
-// which the forward never writes, as zeros); transposing reads then give the fragments of
-// Kg, Wn^T, M^T and Qg^T, and dO is staged the same way.
-template <int DK, int DV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_pre_kernel(B16Params p) {
-    using R_ = Rec<C, DK, DV, true>;
-    using L_ = BL16<DK, DV>;
-    constexpr int SK = Pad<DK>::S, SC = Pad<C>::S, SV = Pad<DV>::S;
-    constexpr int NKD = DK / 32, NRK = DK / 16, NSL = DV / 16;
-    constexpr int NBW = NRC * NKD, NBK = NRK * NKC, NBM = NRC * NKC, NOV = C * DV / 8 / 256;
-    static_assert(NBW % 4 == 0 && NBK % 4 == 0 && NBM % 4 == 0 && NOV >= 1, "even split");
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    bf16_t *Wl = reinterpret_cast<bf16_t *>(smem);     // [C][SK]  Wn
-    bf16_t *Ql = Wl + C * SK;                          // [C][SK]  Qg
-    bf16_t *KTl = Ql + C * SK;                         // [DK][SC] KgT
-    bf16_t *Ml = KTl + DK * SC;                        // [C][SC]  M
-    bf16_t *Ol = Ml + C * SC;                          // [C][SV]  dO
-
-    const int item = blockIdx.x, chunk = item / p.h_v, h = item - chunk * p.h_v;
-    int n, j;
-    int64_t start, end;
-    if (!locate16(p, chunk, n, j, start, end)) return;
-    const int64_t t0 = start + static_cast<int64_t>(j) * C;
-    const int Lr = static_cast<int>(min<int64_t>(C, end - t0));
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-    const char *rec = p.rec + static_cast<size_t>(item) * R_::bytes;
-    char *cr = p.crec + static_cast<size_t>(item) * L_::CREC;
-    const u32x4 *wn = reinterpret_cast<const u32x4 *>(rec + R_::Wn);
-    const u32x4 *qg = reinterpret_cast<const u32x4 *>(rec + R_::Qg);
-    const u32x4 *kgt = reinterpret_cast<const u32x4 *>(rec + R_::KgT);
-    const u32x4 *mm = reinterpret_cast<const u32x4 *>(rec + R_::M);
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-    u32x4 fw[NBW / 4], fq[NBW / 4], fk[NBK / 4], fm[NBM / 4], fo[NOV];
-#pragma unroll
-    for (int i = 0; i < NBW / 4; ++i) {
-        fw[i] = wn[(wave + 4 * i) * 64 + lane];
-        fq[i] = qg[(wave + 4 * i) * 64 + lane];
-    }
-#pragma unroll
-    for (int i = 0; i < NBK / 4; ++i) fk[i] = kgt[(wave + 4 * i) * 64 + lane];
-#pragma unroll
-    for (int i = 0; i < NBM / 4; ++i) {
-        const int blk = wave + 4 * i, R = blk / NKC, kt = blk - R * NKC;
-        fm[i] = 32 * kt <= 16 * R + 15 ? mm[blk * 64 + lane] : zero4;
-    }
-#pragma unroll
-    for (int i = 0; i < NOV; ++i) {
-        const int e = tid + 256 * i, r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
-        fo[i] = r < Lr ? *reinterpret_cast<const u32x4 *>(
-                             p.dO + (static_cast<size_t>(t0 + r) * p.h_v + h) * DV + c8)
-                       : zero4;
-    }
-#pragma unroll
-    for (int i = 0; i < NBW / 4; ++i) {
-        const int blk = wave + 4 * i, rt = blk / NKD, kt = blk - rt * NKD;
-        frag_to_rows(Wl, SK, 16 * rt, 32 * kt, fw[i], li, lg);
-        frag_to_rows(Ql, SK, 16 * rt, 32 * kt, fq[i], li, lg);
-    }
-#pragma unroll
-    for (int i = 0; i < NBK / 4; ++i) {
-        const int blk = wave + 4 * i, rt = blk / NKC, kt = blk - rt * NKC;
-        frag_to_rows(KTl, SC, 16 * rt, 32 * kt, fk[i], li, lg);
-    }
-#pragma unroll
-    for (int i = 0; i < NBM / 4; ++i) {
-        const int blk = wave + 4 * i, R = blk / NKC, kt = blk - R * NKC;
-        frag_to_rows(Ml, SC, 16 * R, 32 * kt, fm[i], li, lg);
-    }
-#pragma unroll
-    for (int i = 0; i < NOV; ++i) {
-        const int e = tid + 256 * i, r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
-        *reinterpret_cast<u32x4 *>(&Ol[r * SV + c8]) = fo[i];
-    }
-    lds_barrier();
-
-    // Kg (rows: tokens, k: channels) and Wn^T (rows: channels, k: tokens) fragments
-    u32x4 *kga = reinterpret_cast<u32x4 *>(cr + L_::KgA);
-    u32x4 *wnt = reinterpret_cast<u32x4 *>(cr + L_::WnT);
-    for (int blk = wave; blk < NRC * NKD; blk += 4) {
-        const int ut = blk / NKD, kt = blk - ut * NKD;
-        kga[blk * 64 + lane] = col_frag(KTl, SC, 32 * kt, 16 * ut, li, lg);
-    }
-    for (int blk = wave; blk < NRK * NKC; blk += 4) {
-        const int rt = blk / NKC, kt = blk - rt * NKC;
-        wnt[blk * 64 + lane] = col_frag(Wl, SK, 32 * kt, 16 * rt, li, lg);
-    }
-    // E1 = M^T dO and E2 = Qg^T dO, one 16-column value slice at a time
-    u32x2 *e1 = reinterpret_cast<u32x2 *>(cr + L_::E1);
-    u32x2 *e2 = reinterpret_cast<u32x2 *>(cr + L_::E2);
-    for (int s = wave; s < NSL; s += 4) {
-        u32x4 ob[NKC];
-#pragma unroll
-        for (int kt = 0; kt < NKC; ++kt) ob[kt] = col_frag(Ol, SV, 32 * kt, 16 * s, li, lg);
-#pragma unroll
-        for (int ut = 0; ut < NRC; ++ut) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(col_frag(Ml, SC, 32 * kt, 16 * ut, li, lg), ob[kt], acc);
-            e1[(s * NRC + ut) * 64 + lane] = f4_to_b16(acc);
-        }
-#pragma unroll
-        for (int rt = 0; rt < NRK; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(col_frag(Ql, SK, 32 * kt, 16 * rt, li, lg), ob[kt], acc);
-            e2[(s * NRK + rt) * 64 + lane] = f4_to_b16(acc);
-        }
-    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1050,6 +931,8 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     f.fu = Fusion{};
     f.fu.cks16 = base + ws.ck;
     f.fu.cku16 = base + ws.cu;
+    f.fu.bops = base + ws.crec;
+    f.fu.bdo = a.dO;
     f.fu.tmat = base + ws.tm;
     hipError_t e = launch_chunk_fwd(f, st);
     if (e != hipSuccess) return e;
@@ -1080,13 +963,8 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(zero2_kernel, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
                            a.dq, a.dk, qk);
     }
-    constexpr int pre_lds = 2 * (2 * C * Pad<DK>::S + DK * Pad<C>::S + C * Pad<C>::S + C * Pad<DV>::S);
-    static_assert(pre_lds <= 160 * 1024, "LDS");
-    if ((e = set_lds(bwd_pre_kernel<DK, DV>, pre_lds)) != hipSuccess) return e;
     if ((e = set_lds(bwd_rchain_kernel<DK, DV, kChainSlices>, RC::LDS)) != hipSuccess) return e;
     if ((e = set_lds(bwd_grads16_kernel<DK, DV>, GLay<DK, DV>::LDS)) != hipSuccess) return e;
-    if (nrec > 0)
-        hipLaunchKernelGGL((bwd_pre_kernel<DK, DV>), dim3(nrec), dim3(256), pre_lds, st, p);
     if (p.num_pairs > 0) {
         const int64_t blocks = static_cast<int64_t>((p.num_pairs + 7) / 8) * 8 * RC::G;
         hipLaunchKernelGGL((bwd_rchain_kernel<DK, DV, kChainSlices>), dim3(blocks),

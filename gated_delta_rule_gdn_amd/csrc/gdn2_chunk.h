@@ -46,6 +46,20 @@ struct Rec {
     static constexpr size_t UT_TILE = 64 * 4 * E;      // one D-layout tile
 };
 
+// Per-record operands of the chunked backward's reverse state pass (64-token chunks, bf16):
+//   KgA  Kg = (KgT)^T as A fragment blocks [C/16][DK/32]
+//   WnT  Wn^T as A fragment blocks         [DK/16][C/32]
+//   E1   M^T dO as bf16 D tiles            [DV/16 slice][C/16]
+//   E2   Qg^T dO as bf16 D tiles           [DV/16 slice][DK/16]
+template <int DK, int DV>
+struct BwdOps {
+    static constexpr size_t KgA = 0;
+    static constexpr size_t WnT = KgA + static_cast<size_t>(kChunk) * DK * 2;
+    static constexpr size_t E1 = WnT + static_cast<size_t>(DK) * kChunk * 2;
+    static constexpr size_t E2 = E1 + static_cast<size_t>(kChunk) * DV * 2;
+    static constexpr size_t bytes = E2 + static_cast<size_t>(DK) * DV * 2;
+};
+
 struct ChunkParams {
     const void *q, *k, *v, *log_alpha, *b, *w;
     const float *S0;
@@ -58,6 +72,9 @@ struct ChunkParams {
                          // x 16 B (64-token path, bf16 records only), or NULL
     void *U_ck16;        // U = U~ + Wn S of every chunk as bf16 B fragments, [chunk][h_v]
                          // [DV/16][C/32][64] x 16 B (same paths), or NULL
+    char *bops;          // with o == NULL: the chunked backward's per-record reverse-pass
+                         // operands (BwdOps), formed by the output waves, or NULL
+    const void *dO;      // gradient of o, [.., h_v, DV] (with bops)
     char *rec;           // first per-(chunk, head) record
     void *tmat;          // bf16 inputs: T = (I + A)^-1 per record, [C][C] row-major, or NULL
     // Segmented state pass (dense batches with few (sequence, head) pairs): the chunks of
@@ -139,6 +156,19 @@ __device__ __forceinline__ u32x2 lds_tr4(const void *p) {
         (__attribute__((address_space(3))) s16x4v *)(p));
     return __builtin_bit_cast(u32x2, r);
 }
+// A fragment of X^T read from X stored as A fragment blocks (the record layout above; X has
+// nkx k tiles): the block of X^T at row tile ry and k tile ky, i.e. lane (li, lg) receives
+// X[32 ky + perm(lg, jj)][16 ry + li]. Each lane names the 8-byte run of four consecutive
+// columns of X that the transposing read distributes (see lds_tr4).
+__device__ __forceinline__ u32x4 frag_t(const char *x, int nkx, int ry, int ky, int li, int lg) {
+    const int r = 32 * ky + 4 * lg + (li >> 2), c = 16 * ry + 4 * (li & 3);
+    const int off = ((((r >> 4) * nkx + (c >> 5)) * 64 + ((c & 15) >> 2) * 16 + (r & 15)) << 4) +
+                    ((c & 31) >> 4) * 8;
+    const u32x2 lo = lds_tr4(x + off);
+    const u32x2 hi = lds_tr4(x + off + nkx * 1024);   // rows r + 16: the next row tile of X
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
 // 2^x on the transcendental unit (the prep kernel keeps its cumulative decay in log2 units)
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

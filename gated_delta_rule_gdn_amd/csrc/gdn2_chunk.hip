@@ -219,6 +219,84 @@ struct CarryLayout {
     static_assert(LDS <= 159 * 1024, "carry fits in LDS");
 };
 
+// The backward's reverse-pass operands (BwdOps) of every chunk of a state-pass workgroup,
+// formed by an output wave of the states-only pass (64-token chunks, bf16 records) from the
+// staged record: E1 = M^T dO and E2 = Qg^T dO for its 16-column slice ct of dO, and its
+// share of the Kg and Wn^T fragment blocks (blocks ow, ow + now, ...). The transposes come
+// from transposing LDS reads of the staged fragments (frag_t); the slice of dO goes through
+// the wave's own LDS area (row-major, 16 + 8 columns), prefetched a chunk ahead in registers
+// (rows past the sequence as zeros). Meets the chunk barriers of the state pass.
+template <int DK, int DV>
+__device__ void bwd_operands(const ChunkParams &p, char *smem, size_t buf_bytes, char *own,
+                             int cb, int ce, int64_t start, int64_t end, int cbase, int h, int ct,
+                             int ow, int now) {
+    using R_ = Rec<kChunk, DK, DV, true>;
+    using BO = BwdOps<DK, DV>;
+    constexpr int C = kChunk, NKD = DK / 32, NKC = C / 32, NRC = C / 16, NRK = DK / 16;
+    constexpr int NF = NRC * NKD + NRK * NKC;         // Kg blocks, then Wn^T blocks
+    constexpr int OS = 24;                            // row stride of the dO slice (elements)
+    const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+    bf16_t *od = reinterpret_cast<bf16_t *>(own);
+    const bf16_t *dO = static_cast<const bf16_t *>(p.dO);
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    u32x4 d0 = zero4, d1 = zero4;                     // this lane's row of the next chunk's slice
+    auto load = [&](int c) {
+        const int64_t t0 = start + static_cast<int64_t>(c) * C;
+        d0 = d1 = zero4;
+        if (t0 + lane < end) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                dO + (static_cast<size_t>(t0 + lane) * p.h_v + h) * DV + 16 * ct);
+            d0 = src[0];
+            d1 = src[1];
+        }
+    };
+    if (ce > cb) load(cb);
+    for (int c = cb; c < ce; ++c) {
+        const char *cur = smem + ((c - cb) & 1) * buf_bytes;
+        raw_barrier();                      // chunk c is staged; chunk c-1 fully consumed
+        *reinterpret_cast<u32x4 *>(&od[lane * OS]) = d0;
+        *reinterpret_cast<u32x4 *>(&od[lane * OS + 8]) = d1;
+        if (c + 1 < ce) load(c + 1);
+        wait_lds();
+        asm volatile("" ::: "memory");
+        char *ob = p.bops + (static_cast<size_t>(cbase + c) * p.h_v + h) * BO::bytes;
+        u32x4 db[NKC];                      // dO as B fragments: k = tokens, n = the slice
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt) {
+            const bf16_t *q = od + (32 * kt + 4 * lg + (li >> 2)) * OS + 4 * (li & 3);
+            const u32x2 a = lds_tr4(q), b = lds_tr4(q + 16 * OS);
+            db[kt] = u32x4{a.x, a.y, b.x, b.y};
+        }
+        u32x2 *e1 = reinterpret_cast<u32x2 *>(ob + BO::E1) + static_cast<size_t>(ct) * NRC * 64;
+#pragma unroll
+        for (int ut = 0; ut < NRC; ++ut) {  // E1 = M^T dO (M^T blocks of zeros skipped)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt)
+                if (32 * kt + 31 >= 16 * ut) acc = mma_k32(frag_t(cur + R_::M, NKC, ut, kt, li, lg), db[kt], acc);
+            e1[ut * 64 + lane] = f4_to_b16(acc);
+        }
+        u32x2 *e2 = reinterpret_cast<u32x2 *>(ob + BO::E2) + static_cast<size_t>(ct) * NRK * 64;
+#pragma unroll
+        for (int rt = 0; rt < NRK; ++rt) {  // E2 = Qg^T dO
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(frag_t(cur + R_::Qg, NKD, rt, kt, li, lg), db[kt], acc);
+            e2[rt * 64 + lane] = f4_to_b16(acc);
+        }
+        for (int f = ow; f < NF; f += now) {
+            if (f < NRC * NKD) {            // Kg block (token tile, channel k tile)
+                const int ut = f / NKD, kt = f - ut * NKD;
+                reinterpret_cast<u32x4 *>(ob + BO::KgA)[f * 64 + lane] = frag_t(cur + R_::KgT, NKC, ut, kt, li, lg);
+            } else {                        // Wn^T block (channel tile, token k tile)
+                const int g = f - NRC * NKD, rt = g / NKC, kt = g - rt * NKC;
+                reinterpret_cast<u32x4 *>(ob + BO::WnT)[g * 64 + lane] = frag_t(cur + R_::Wn, NKD, rt, kt, li, lg);
+            }
+        }
+        wait_lds();                         // every read of chunk c's stage has completed
+    }
+}
+
 // copy waves per state-pass workgroup: six, four with four slices (the register budget of
 // twelve waves)
 template <int NW> struct StateWaves {
@@ -281,13 +359,15 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
     // copy waves (wave >= 2 NW): stage chunk c's record part into a stage buffer; chunk c
     // of the workgroup's segment uses buffer (c - cb) & 1
     const int ldr = wave - 2 * NW;
-    // Without outputs (p.o == NULL: only the chunk states are wanted) Qg and M stay unstaged.
+    // Without outputs (p.o == NULL: only the chunk states are wanted) Qg and M stay unstaged,
+    // unless the output waves form the backward's operands (p.bops).
     const bool outputs = p.o != nullptr;
+    const bool stage_qm = outputs || p.bops != nullptr;
     auto issue = [&](int c, char *dst) {
         const char *rec = record(c);
         for (int blk = ldr; blk < static_cast<int>(SL::SHARED / 1024); blk += NCOPY) {
             const size_t off = static_cast<size_t>(blk) * 1024;
-            if (!outputs && ((off >= R_::Qg && off < R_::KgT) || off >= R_::M)) continue;
+            if (!stage_qm && ((off >= R_::Qg && off < R_::KgT) || off >= R_::M)) continue;
             dma16(rec + off + lane * 16, dst + off);
         }
         if (ldr == NCOPY - 1 && lane < static_cast<int>(SL::GCB / 16))
@@ -347,9 +427,9 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii)
                     R[j][ii] = Rg[static_cast<size_t>(16 * (r0 + j) + 4 * lg + ii) * DV + col];
-        } else if (CL::EARLY && g == 1 && ce > cb && outputs) {
+        } else if (CL::EARLY && g == 1 && ce > cb && stage_qm) {
             // P_1 has landed once no more than the first chunk's loads (issued after it; at
-            // least CB_MIN per copy wave with outputs) are outstanding
+            // least CB_MIN per copy wave when Qg and M are staged) are outstanding
             wait_vmem_n<CB_MIN>();
         } else {
             wait_vmem();
@@ -498,8 +578,15 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
     }
 
     // ---- output wave ----
-    if (!outputs) {                         // states only: meet the chunk barriers, nothing else
-        for (int c = cb; c < ce; ++c) raw_barrier();
+    if (!outputs) {
+        if constexpr (BF) {
+            if (p.bops != nullptr) {
+                bwd_operands<DK, DV>(p, smem, BUF, xch_base + sl * SL::XCH, cb, ce, start, end, cbase, h,
+                                     ct, slice * NW + sl, p.nslices * NW);
+                return;
+            }
+        }
+        for (int c = cb; c < ce; ++c) raw_barrier();   // states only: meet the chunk barriers
         return;
     }
     for (int c = cb; c < ce; ++c) {
@@ -935,6 +1022,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks; p.tmat = a.fu.tmat;
     p.S_ck16 = a.fu.cks16;
     p.U_ck16 = a.fu.cku16;
+    p.bops = BF && a.o == nullptr ? a.fu.bops : nullptr;
+    p.dO = a.fu.bdo;
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
     p.rec = a.workspace + mapb;
@@ -1014,7 +1103,7 @@ static hipError_t launch_chunk_dt(const ChunkArgs &a, hipStream_t st) {
 // Generic path: any built chunk size, both dtypes, all head dims; the state pass walks each
 // chunk in row panels and runs every (sequence, head) from its start (no segments).
 static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
-    if (a.fu.cks16 || a.fu.cku16) return hipErrorInvalidValue;   // written by the 64-token pass only
+    if (a.fu.cks16 || a.fu.cku16 || a.fu.bops) return hipErrorInvalidValue;   // 64-token pass only
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
     const int C = a.chunk;

@@ -28,6 +28,8 @@ struct Fusion {
     float *cks = nullptr;            // chunked forward: state entering every chunk, or NULL
     void *cks16 = nullptr;           // the same as bf16 fragments (64-token path), or NULL
     void *cku16 = nullptr;           // U of every chunk as bf16 fragments (64-token path), or NULL
+    char *bops = nullptr;            // with o == NULL: the backward's reverse-pass operands
+    const void *bdo = nullptr;       // dO for bops
     void *tmat = nullptr;            // chunked forward, bf16: T = (I + A)^-1 per record, or NULL
 };
 
