@@ -11,9 +11,9 @@
 // (the record layout of gdn2_chunk.h).
 //
 // One workgroup per record, small enough in LDS that two records run on a CU at once for
-// C <= 64 (the rounds of one hide the latency of the other's): eight waves at C = 64, where
-// a round covers two matrix-core k tiles and every wave holds one sub-chunk of each, four
-// waves over one k tile per round otherwise (PrepShape below). The key channels are
+// C <= 64 (the rounds of one hide the latency of the other's): eight waves at C = 64 (and
+// for bf16 records at C = 128), where a round covers two matrix-core k tiles, four waves
+// over one k tile per round otherwise (PrepShape below). The key channels are
 // processed in rounds of k tiles (32 bf16 / 16 fp32 channels each):
 //   scan    every lane holds one token of a 16-token sub-chunk and 8 (bf16) or 4 (fp32)
 //           channels; the cumulative log decay inside each sub-chunk is an in-row scan of the
@@ -106,7 +106,13 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
     __shared__ float s_foff[(NOFF > 0 ? NOFF : 1) * DK];   // 2^(g_mid_R - g_mid_I), R > I
     __shared__ __attribute__((aligned(16))) T s_tile[NBUF * 3 * TILE];
     __shared__ __attribute__((aligned(16))) float s_A[NPAIR * BS];
-    __shared__ __attribute__((aligned(16))) float s_T[NPAIR * BS];
+    // bf16 records at C = 128 keep the fp32 T over the round tiles (dead between the last
+    // round and the WY rounds) so that eight waves fit the LDS; the WY rounds read the bf16
+    // copy of T only
+    constexpr bool TALIAS = BF && C == 128;
+    static_assert(!TALIAS || NBUF * 3 * TILE * sizeof(T) >= NPAIR * BS * sizeof(float), "T fits the tiles");
+    __shared__ __attribute__((aligned(16))) float s_Tst[TALIAS ? 4 : NPAIR * BS];
+    float *const s_T = TALIAS ? reinterpret_cast<float *>(s_tile) : s_Tst;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 15, lg = lane >> 4;   // matrix-core lane roles (= t, gi below)
@@ -524,6 +530,7 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
         }
     }
 
+    if constexpr (TALIAS) lds_barrier();     // every read of the fp32 T is done
     if constexpr (BF) {
         if (p.tmat != nullptr) {               // T for the chunked backward
             lds_barrier();
@@ -618,11 +625,12 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
 }
 
 // Waves per workgroup and channel blocks per round: eight waves over two blocks where a
-// round then gives every wave a sub-chunk (64-token chunks) and the LDS of two workgroups
-// still fits a CU; four waves over one block otherwise.
+// round then gives every wave a sub-chunk (64-token chunks; the LDS of two workgroups still
+// fits a CU) or two (128-token chunks of bf16 records, one workgroup per CU with the fp32 T
+// over the round tiles); four waves over one block otherwise.
 template <bool BF, int C, int DK, int DV> struct PrepShape {
     static constexpr int NJ = DK / (BF ? 32 : 16), NJV = DV / (BF ? 32 : 16);
-    static constexpr bool WIDE = C == 64 && NJ % 2 == 0 && NJV % 2 == 0;
+    static constexpr bool WIDE = (C == 64 || (C == 128 && BF)) && NJ % 2 == 0 && NJV % 2 == 0;
     static constexpr int NWV = WIDE ? 8 : 4, CPR = WIDE ? 2 : 1;
 };
 
