@@ -235,12 +235,128 @@ __device__ __forceinline__ bool wait_flag(lds_flag *flag, int want) {
     return ok;
 }
 
+// Segment transitions P (d_k x d_k; the segmented state passes of gdn2_chunk.hip and gdn2_state.hip) as the segment pass
+// writes them and the state pass reads them: matrix-core A operands, so that the product
+// P S needs no transposition. Fragment (rt, kt) covers rows 16 rt .. 16 rt + 15 and one k
+// tile of columns; lane li + 16 lg holds row 16 rt + li at the k slots of group lg (the perm
+// order of mma_k32 for bf16 records, k = 4 lg + s for fp32 ones).
+//   bf16 records: two planes hi = bf16(P) and lo = bf16(P - hi), each [RT][DK/32][64][8]
+//                 bf16; P S is formed as hi S_hi + hi S_lo + lo S_hi, which keeps about 16
+//                 significant bits of the fp32 operands;
+//   fp32 records: one plane [RT][RT][64][4] fp32.
+template <int DK, bool BF>
+struct SegPFrag {
+    static constexpr int RT = DK / 16, NK = BF ? DK / 32 : DK / 16;
+    static constexpr size_t PLANE = static_cast<size_t>(RT) * NK * 64 * 16;   // bytes
+    static constexpr size_t BYTES = BF ? 2 * PLANE : PLANE;
+    static_assert(BYTES == static_cast<size_t>(DK) * DK * 4, "the size of an fp32 P");
+    // stores element P[r][c]
+    __device__ static void put(char *base, int r, int c, float x) {
+        const int rt = r >> 4, lane = (r & 15) + 16 * ((c & 15) >> 2);
+        if constexpr (BF) {
+            const int kt = c >> 5, slot = 4 * ((c >> 4) & 1) + (c & 3);
+            const size_t off = ((static_cast<size_t>(rt) * NK + kt) * 64 + lane) * 16 + slot * 2;
+            const __bf16 hi = static_cast<__bf16>(x);
+            const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+            *reinterpret_cast<__bf16 *>(base + off) = hi;
+            *reinterpret_cast<__bf16 *>(base + PLANE + off) = lo;
+        } else {
+            const int kt = c >> 4, slot = c & 3;
+            const size_t off = ((static_cast<size_t>(rt) * NK + kt) * 64 + lane) * 16 + slot * 4;
+            *reinterpret_cast<float *>(base + off) = x;
+        }
+    }
+    // Row tiles R0 .. R0 + RT/2 - 1 of P S + R, for the 16 columns of S a wave holds in D
+    // layout (lane: rows 16 rt + 4 lg + ii of its column), written over those tiles of S and
+    // into the exchange `xch` ([rt][lane]); P staged in LDS at `pl`, R (these tiles) in D
+    // layout. The fragments of the next row tile are read while the products of one run.
+    template <int R0>
+    __device__ static void carry_half(const char *pl, const f32x4 (&R)[RT / 2], f32x4 (&S)[RT],
+                                      f32x4 *xch) {
+        constexpr int H = RT / 2;
+        const int lane = threadIdx.x & 63;
+        // this lane's LDS address in the staged P, kept opaque so that the compiler folds only
+        // the fragment offsets (< 64 KB) into the LDS instructions instead of keeping one
+        // address register per fragment
+        uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                            (__attribute__((address_space(3))) const char *)pl)) + lane * 16;
+        asm volatile("" : "+v"(base));
+        auto frag = [&](uint32_t off) {
+            return *(__attribute__((address_space(3))) const u32x4 *)(static_cast<uintptr_t>(base + off));
+        };
+        f32x4 acc[H];
+#pragma unroll
+        for (int j = 0; j < H; ++j) acc[j] = R[j];
+        if constexpr (BF) {
+            u32x4 sh[NK], sl[NK];
+#pragma unroll
+            for (int kt = 0; kt < NK; ++kt) {
+                const f32x4 a = S[2 * kt], b = S[2 * kt + 1];
+                sh[kt] = dpair_to_b32(a, b);
+                const f32x4 ar = {bf16_lo(sh[kt].x), bf16_hi(sh[kt].x), bf16_lo(sh[kt].y), bf16_hi(sh[kt].y)};
+                const f32x4 br = {bf16_lo(sh[kt].z), bf16_hi(sh[kt].z), bf16_lo(sh[kt].w), bf16_hi(sh[kt].w)};
+                sl[kt] = dpair_to_b32(a - ar, b - br);
+            }
+            u32x4 fh[2][NK], fl[2][NK];
+#pragma unroll
+            for (int kt = 0; kt < NK; ++kt) {
+                fh[0][kt] = frag((R0 * NK + kt) * 1024);
+                fl[0][kt] = frag(PLANE + (R0 * NK + kt) * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const int cb = j & 1, nb = cb ^ 1;
+                if (j + 1 < H) {
+#pragma unroll
+                    for (int kt = 0; kt < NK; ++kt) {
+                        fh[nb][kt] = frag(((R0 + j + 1) * NK + kt) * 1024);
+                        fl[nb][kt] = frag(PLANE + ((R0 + j + 1) * NK + kt) * 1024);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kt = 0; kt < NK; ++kt) {
+                    acc[j] = mma_k32(fh[cb][kt], sh[kt], acc[j]);
+                    acc[j] = mma_k32(fh[cb][kt], sl[kt], acc[j]);
+                    acc[j] = mma_k32(fl[cb][kt], sh[kt], acc[j]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            f32x4 f[2][NK];
+#pragma unroll
+            for (int kt = 0; kt < NK; ++kt) f[0][kt] = __builtin_bit_cast(f32x4, frag((R0 * NK + kt) * 1024));
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const int cb = j & 1, nb = cb ^ 1;
+                if (j + 1 < H) {
+#pragma unroll
+                    for (int kt = 0; kt < NK; ++kt)
+                        f[nb][kt] = __builtin_bit_cast(f32x4, frag(((R0 + j + 1) * NK + kt) * 1024));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kt = 0; kt < NK; ++kt) acc[j] = mma_k16_f32(f[cb][kt], S[kt], acc[j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+            S[R0 + j] = acc[j];
+            xch[(R0 + j) * 64 + lane] = acc[j];
+        }
+    }
+};
+
 // The intra-chunk pass (gdn2_prep.hip): one record per (chunk, value head) item, for the
 // chunk sizes and dims it is built for.
 hipError_t launch_prep(const ChunkParams &p, int chunk, int dk, int dv, bool bf16, int64_t items,
                        hipStream_t st);
-// The panel state pass (gdn2_state.hip) over the records of launch_prep.
+// The panel state pass (gdn2_state.hip) over the records of launch_prep, its segment pass
+// (nothing to do when p.nseg == 1) and the 16-column slices per state-pass workgroup.
 hipError_t launch_panel_state(const ChunkParams &p, int chunk, int dk, int dv, bool bf16,
                               hipStream_t st);
+hipError_t launch_panel_seg(const ChunkParams &p, int chunk, int dk, int dv, bool bf16, hipStream_t st);
+int panel_slices(int chunk, int dk, int dv, bool bf16);
 
 }  // namespace gdn2

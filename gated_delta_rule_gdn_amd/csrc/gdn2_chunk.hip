@@ -92,119 +92,6 @@ struct StageLayout {
     static_assert(lds_bytes(1) <= 160 * 1024, "stage must fit in LDS");
 };
 
-// Segment transitions P (d_k x d_k, see the segmented state pass below) as the segment pass
-// writes them and the state pass reads them: matrix-core A operands, so that the product
-// P S needs no transposition. Fragment (rt, kt) covers rows 16 rt .. 16 rt + 15 and one k
-// tile of columns; lane li + 16 lg holds row 16 rt + li at the k slots of group lg (the perm
-// order of mma_k32 for bf16 records, k = 4 lg + s for fp32 ones).
-//   bf16 records: two planes hi = bf16(P) and lo = bf16(P - hi), each [RT][DK/32][64][8]
-//                 bf16; P S is formed as hi S_hi + hi S_lo + lo S_hi, which keeps about 16
-//                 significant bits of the fp32 operands;
-//   fp32 records: one plane [RT][RT][64][4] fp32.
-template <int DK, bool BF>
-struct SegPFrag {
-    static constexpr int RT = DK / 16, NK = BF ? DK / 32 : DK / 16;
-    static constexpr size_t PLANE = static_cast<size_t>(RT) * NK * 64 * 16;   // bytes
-    static constexpr size_t BYTES = BF ? 2 * PLANE : PLANE;
-    static_assert(BYTES == static_cast<size_t>(DK) * DK * 4, "the size of an fp32 P");
-    // stores element P[r][c]
-    __device__ static void put(char *base, int r, int c, float x) {
-        const int rt = r >> 4, lane = (r & 15) + 16 * ((c & 15) >> 2);
-        if constexpr (BF) {
-            const int kt = c >> 5, slot = 4 * ((c >> 4) & 1) + (c & 3);
-            const size_t off = ((static_cast<size_t>(rt) * NK + kt) * 64 + lane) * 16 + slot * 2;
-            const __bf16 hi = static_cast<__bf16>(x);
-            const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
-            *reinterpret_cast<__bf16 *>(base + off) = hi;
-            *reinterpret_cast<__bf16 *>(base + PLANE + off) = lo;
-        } else {
-            const int kt = c >> 4, slot = c & 3;
-            const size_t off = ((static_cast<size_t>(rt) * NK + kt) * 64 + lane) * 16 + slot * 4;
-            *reinterpret_cast<float *>(base + off) = x;
-        }
-    }
-    // Row tiles R0 .. R0 + RT/2 - 1 of P S + R, for the 16 columns of S a wave holds in D
-    // layout (lane: rows 16 rt + 4 lg + ii of its column), written over those tiles of S and
-    // into the exchange `xch` ([rt][lane]); P staged in LDS at `pl`, R (these tiles) in D
-    // layout. The fragments of the next row tile are read while the products of one run.
-    template <int R0>
-    __device__ static void carry_half(const char *pl, const f32x4 (&R)[RT / 2], f32x4 (&S)[RT],
-                                      f32x4 *xch) {
-        constexpr int H = RT / 2;
-        const int lane = threadIdx.x & 63;
-        // this lane's LDS address in the staged P, kept opaque so that the compiler folds only
-        // the fragment offsets (< 64 KB) into the LDS instructions instead of keeping one
-        // address register per fragment
-        uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-                            (__attribute__((address_space(3))) const char *)pl)) + lane * 16;
-        asm volatile("" : "+v"(base));
-        auto frag = [&](uint32_t off) {
-            return *(__attribute__((address_space(3))) const u32x4 *)(static_cast<uintptr_t>(base + off));
-        };
-        f32x4 acc[H];
-#pragma unroll
-        for (int j = 0; j < H; ++j) acc[j] = R[j];
-        if constexpr (BF) {
-            u32x4 sh[NK], sl[NK];
-#pragma unroll
-            for (int kt = 0; kt < NK; ++kt) {
-                const f32x4 a = S[2 * kt], b = S[2 * kt + 1];
-                sh[kt] = dpair_to_b32(a, b);
-                const f32x4 ar = {bf16_lo(sh[kt].x), bf16_hi(sh[kt].x), bf16_lo(sh[kt].y), bf16_hi(sh[kt].y)};
-                const f32x4 br = {bf16_lo(sh[kt].z), bf16_hi(sh[kt].z), bf16_lo(sh[kt].w), bf16_hi(sh[kt].w)};
-                sl[kt] = dpair_to_b32(a - ar, b - br);
-            }
-            u32x4 fh[2][NK], fl[2][NK];
-#pragma unroll
-            for (int kt = 0; kt < NK; ++kt) {
-                fh[0][kt] = frag((R0 * NK + kt) * 1024);
-                fl[0][kt] = frag(PLANE + (R0 * NK + kt) * 1024);
-            }
-#pragma unroll
-            for (int j = 0; j < H; ++j) {
-                const int cb = j & 1, nb = cb ^ 1;
-                if (j + 1 < H) {
-#pragma unroll
-                    for (int kt = 0; kt < NK; ++kt) {
-                        fh[nb][kt] = frag(((R0 + j + 1) * NK + kt) * 1024);
-                        fl[nb][kt] = frag(PLANE + ((R0 + j + 1) * NK + kt) * 1024);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int kt = 0; kt < NK; ++kt) {
-                    acc[j] = mma_k32(fh[cb][kt], sh[kt], acc[j]);
-                    acc[j] = mma_k32(fh[cb][kt], sl[kt], acc[j]);
-                    acc[j] = mma_k32(fl[cb][kt], sh[kt], acc[j]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            f32x4 f[2][NK];
-#pragma unroll
-            for (int kt = 0; kt < NK; ++kt) f[0][kt] = __builtin_bit_cast(f32x4, frag((R0 * NK + kt) * 1024));
-#pragma unroll
-            for (int j = 0; j < H; ++j) {
-                const int cb = j & 1, nb = cb ^ 1;
-                if (j + 1 < H) {
-#pragma unroll
-                    for (int kt = 0; kt < NK; ++kt)
-                        f[nb][kt] = __builtin_bit_cast(f32x4, frag(((R0 + j + 1) * NK + kt) * 1024));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int kt = 0; kt < NK; ++kt) acc[j] = mma_k16_f32(f[cb][kt], S[kt], acc[j]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < H; ++j) {
-            S[R0 + j] = acc[j];
-            xch[(R0 + j) * 64 + lane] = acc[j];
-        }
-    }
-};
-
 // LDS of the segment carry in the state pass: P_g, then the exchange of the carried state
 // ([slice][rt][lane] f32x4), placed after stage buffer 0 when the workgroup's LDS can grow to
 // hold them there, so that the first chunk is staged into buffer 0 during the carry.
@@ -943,9 +830,9 @@ static int state_slices(int d_v, bool bf16, int64_t pairs) {
     return ctiles % 2 == 0 ? 2 : 1;
 }
 
-static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v, bool bf16) {
+// per_unit: state-pass workgroups per (sequence, head, segment) unit
+static SegPlan seg_plan(bool packed, int64_t pairs, int nc, int64_t per_unit) {
     SegPlan sp{1, nc};
-    const int64_t per_unit = (d_v / 16) / state_slices(d_v, bf16, pairs);   // WGs per unit
     if (packed || pairs <= 0 || nc < 8 || per_unit <= 0) return sp;
     int64_t G = kSegTargetWGs / (pairs * per_unit);
     if (G > nc / 4) G = nc / 4;
@@ -954,6 +841,10 @@ static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v, bool 
     sp.nseg = (nc + L - 1) / L;
     sp.seg_len = L;
     return sp;
+}
+
+static SegPlan chunk_seg_plan(bool packed, int64_t pairs, int nc, int d_v, bool bf16) {
+    return seg_plan(packed, pairs, nc, (d_v / 16) / state_slices(d_v, bf16, pairs));
 }
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -978,13 +869,20 @@ static bool tuned_path(int chunk, int d_k, int d_v, bool bf16) {
     return chunk == kChunk && (bf16 || (d_k == 64 && d_v == 64));
 }
 
+// The segment plan of either path (the generic path's state pass has its own slices per
+// workgroup).
+static SegPlan path_seg_plan(int chunk, int d_k, int d_v, bool bf16, bool packed, int64_t pairs, int nc) {
+    if (tuned_path(chunk, d_k, d_v, bf16)) return chunk_seg_plan(packed, pairs, nc, d_v, bf16);
+    return seg_plan(packed, pairs, nc, (d_v / 16) / panel_slices(chunk, d_k, d_v, bf16));
+}
+
 size_t chunk_workspace_bytes(int chunk, int batch, int seqlen, int num_seqs, int h_v, int d_k,
                              int d_v, bool bf16, bool packed) {
     const int64_t nc = (static_cast<int64_t>(seqlen) + chunk - 1) / chunk;
     const int64_t pairs = static_cast<int64_t>(packed ? num_seqs : batch) * h_v;
     size_t segb = 0;
-    if (tuned_path(chunk, d_k, d_v, bf16)) {
-        const SegPlan sp = chunk_seg_plan(packed, pairs, static_cast<int>(nc), d_v, bf16);
+    {
+        const SegPlan sp = path_seg_plan(chunk, d_k, d_v, bf16, packed, pairs, static_cast<int>(nc));
         size_t off[3];
         seg_area(sp, pairs, d_k, d_v, off, &segb);
     }
@@ -1117,16 +1015,27 @@ static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
     p.group = a.h_v / a.h_k;
     p.nc_dense = (a.seqlen + C - 1) / C;
     p.num_pairs = N * a.h_v;
-    p.nseg = 1;
-    p.seg_len = p.nc_dense;
     p.qkn = a.fu.qk_norm ? 1 : 0;
     p.l2eps = a.fu.l2eps;
     p.gmode = a.fu.gmode;
+    const int64_t nrec = chunk_upper_bound(C, a.batch, a.seqlen, N, packed);
+    const SegPlan sp = path_seg_plan(C, a.d_k, a.d_v, a.bf16, packed, p.num_pairs, p.nc_dense);
+    p.nseg = sp.nseg;
+    p.seg_len = sp.seg_len;
+    {
+        size_t off[3], segb;
+        seg_area(sp, p.num_pairs, a.d_k, a.d_v, off, &segb);
+        char *seg_base = p.rec + static_cast<size_t>(nrec) * a.h_v * chunk_record_bytes(C, a.d_k, a.d_v, a.bf16);
+        p.seg_S = reinterpret_cast<float *>(seg_base + off[0]);
+        p.seg_P = reinterpret_cast<float *>(seg_base + off[1]);
+        p.seg_R = reinterpret_cast<float *>(seg_base + off[2]);
+    }
     if (packed)
         hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(64), 0, st, a.cu_seqlens,
                            reinterpret_cast<int32_t *>(a.workspace), N, C);
-    const int64_t nrec = chunk_upper_bound(C, a.batch, a.seqlen, N, packed);
     hipError_t e = launch_prep(p, C, a.d_k, a.d_v, a.bf16, nrec * a.h_v, st);
+    if (e != hipSuccess) return e;
+    e = launch_panel_seg(p, C, a.d_k, a.d_v, a.bf16, st);
     if (e != hipSuccess) return e;
     e = launch_panel_state(p, C, a.d_k, a.d_v, a.bf16, st);
     if (e != hipSuccess || !a.fu.gate) return e;

@@ -200,14 +200,21 @@ def test_workspace_size_formula(L):
     d = Dims(8, 2048, 0, 8, 8, 128, 128, 1)         # 64 pairs: enough work, no segments
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 8 * 32 * 8 * rec
     # chunk sizes 32 and 128, and fp32 records at d = 128: records of
-    # E*(3*C*dk + C*C + C*dv) + 4*dk bytes, no segment area
+    # E*(3*C*dk + C*C + C*dv) + 4*dk bytes; dense batches with few pairs add the same
+    # segment area, planned for the panel state pass (two 16-column slices per workgroup at
+    # these shapes: 16 pairs x 4 workgroups -> 4 segments)
     def rec_c(C, E, dk, dv):
         return (E * (3 * C * dk + C * C + C * dv) + 4 * dk + 255) // 256 * 256
     d = Dims(1, 4096, 0, 16, 16, 128, 128, 1)
-    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 32 * 16 * rec_c(128, 2, 128, 128)
-    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 32) == 128 * 16 * rec_c(32, 2, 128, 128)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == \
+        32 * 16 * rec_c(128, 2, 128, 128) + seg_bytes(16, 4, 128, 128)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 32) == \
+        128 * 16 * rec_c(32, 2, 128, 128) + seg_bytes(16, 4, 128, 128)
     d = Dims(1, 4096, 0, 16, 16, 128, 128, 0)
-    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 64 * 16 * rec_c(64, 4, 128, 128)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == \
+        64 * 16 * rec_c(64, 4, 128, 128) + seg_bytes(16, 4, 128, 128)
+    d = Dims(8, 4096, 0, 8, 8, 128, 128, 1)         # 64 pairs at chunk 128: no segments
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 8 * 32 * 8 * rec_c(128, 2, 128, 128)
     d = Dims(1, 1000, 5, 1, 2, 128, 64, 0)          # packed, fp32, 128-token chunks
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 256 + (8 + 5) * 2 * rec_c(128, 4, 128, 64)
     assert L.gdn2_chunk_fwd_workspace_bytes(None, 64) == 0
