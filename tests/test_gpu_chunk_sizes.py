@@ -56,6 +56,22 @@ def test_fp32_b1_t4096_h16_d128():
     assert_chunk_parity(x, torch.float32, label="fp32 B1 T4096 H16 d128", worst=True)
 
 
+@pytest.mark.parametrize("C,dtype,dk,dv,T", [
+    (32, torch.bfloat16, 128, 128, 1000),   # 32 chunks over 2 pairs -> 8 segments of 4
+    (128, torch.bfloat16, 128, 64, 2000),   # 16 chunks -> 4 segments
+    (64, torch.float32, 128, 128, 1500),    # 24 chunks -> 6 segments
+    (32, torch.float32, 64, 64, 700),       # 22 chunks -> 5 segments, a ragged last one
+])
+def test_segmented_panel_pass(C, dtype, dk, dv, T):
+    """Dense batches with two (sequence, head) pairs: the panel state pass is cut into many
+    segments, so most segment starts are carried over several transitions (random S0,
+    ragged tail)."""
+    wl = inputs.small_chunk(dtype=dtype, batch=1, seqlen=T, h_k=2, h_v=2, d_k=dk, d_v=dv,
+                            neg_eig=True, s0_std=0.1)
+    x = inputs.chunk_inputs(wl, seed=T + C + dk)
+    assert_chunk_parity(x, dtype, label=f"segmented C={C} {dtype} {dk}x{dv} T={T}", chunk_size=C)
+
+
 @pytest.mark.parametrize("C", [32, 128])
 def test_bf16_b1_t4096_h16_d128_chunk_sizes(C):
     """The timed workload (bf16, B=1, T=4096, 16 heads, d=128, random S0, negative
