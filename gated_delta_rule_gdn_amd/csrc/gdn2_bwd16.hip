@@ -19,9 +19,12 @@
 //                       pass's output waves form the reverse pass's operands from each staged
 //                       record and dO: Kg and Wn^T as matrix-core fragments, E1 = M^T dO and
 //                       E2 = Qg^T dO (BwdOps)
-//   bwd_rchain_kernel   per (sequence, value head, 16 state columns), from the last chunk:
-//                       dU = E1 + Kg dS' and dS = gamma_C dS' + E2 + Wn^T dU; writes dS' and dU
-//                       of every chunk (bf16) and dS0 (fp32)
+//   bwd_rseg_kernel     (dense batches with few pairs only) per later segment of chunks:
+//                       its gradient transition Q and zero-start result R, and the gradient
+//                       entering the segment before the last
+//   bwd_rchain_kernel   per (sequence, value head, 16 state columns[, segment]), from the
+//                       last chunk: dU = E1 + Kg dS' and dS = gamma_C dS' + E2 + Wn^T dU;
+//                       writes dS' and dU of every chunk (bf16) and dS0 (fp32)
 //   bwd_grads16_kernel  per record, every gradient of the chunk: dQg, dW~, dKg, dM,
 //                       dX (-> dv, dw), dT, dA, the decay sums, dq, dk, db and dlog_alpha
 #include "gdn2_chunk.h"
@@ -68,7 +71,11 @@ struct B16Params {
                                        // [record][DV/16][C/32][64 lanes]
     char *crec, *cout;
     float *dq, *dk, *dv, *dw, *dla, *db, *dS0;
+    // segmented reverse pass (nseg > 1): the gradient entering segment nseg-2 [pair][DK][DV],
+    // transitions Q [pair][nseg-2] (SegPFrag) and zero-start results R [pair][nseg-2][DK][DV]
+    float *rseg_S, *rseg_Q, *rseg_R;
     int num_seqs, seqlen, nc_dense, h_k, h_v, group, num_pairs;
+    int nseg, seg_len;
 };
 
 __device__ __forceinline__ bool locate16(const B16Params &p, int chunk, int &n, int &j,
@@ -174,9 +181,11 @@ void bwd_rchain_kernel(B16Params p) {
     constexpr int STAGE = RC::STAGE, G = RC::G, NBUF = RC::NBUF;
     static_assert(NCP == 4 && (NBUF - 2) * RC::per(0) < 64 && EB % 1024 == 0, "vmcnt range");
     extern __shared__ __attribute__((aligned(16))) char smem[];
+    // unit = (pair, segment in reverse order rg); its G workgroups share an XCD
     const int bid = blockIdx.x, idx = bid >> 3;
-    const int pair = (idx / G) * 8 + (bid & 7), part = idx - (idx / G) * G;
-    if (pair >= p.num_pairs) return;                        // uniform over the workgroup
+    const int unit = (idx / G) * 8 + (bid & 7), part = idx - (idx / G) * G;
+    if (unit >= p.num_pairs * p.nseg) return;               // uniform over the workgroup
+    const int pair = unit / p.nseg, rg = unit - pair * p.nseg;
     const int n = pair / p.h_v, h = pair - n * p.h_v;
     int64_t start, end;
     int cbase;
@@ -190,6 +199,10 @@ void bwd_rchain_kernel(B16Params p) {
         cbase = p.map[n];
     }
     const int nchunks = static_cast<int>((end - start + C - 1) / C);
+    // this workgroup's chunks [cb, ce), taken from ce - 1 down to cb (segment g = nseg-1-rg)
+    const int g = p.nseg - 1 - rg;
+    const int cb = p.nseg > 1 ? g * p.seg_len : 0;
+    const int ce = p.nseg > 1 ? min(nchunks, cb + p.seg_len) : nchunks;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
     const bool chain = wave < NWS;
     const int cw = wave - NWS;                              // copy wave index
@@ -230,26 +243,71 @@ void bwd_rchain_kernel(B16Params p) {
         }
     };
 
-    f32x4 D[RT];                                            // dS' rows 16 rt + 4 lg + ii, column 16 s + li
+    // dS' rows 16 rt + 4 lg + ii, column 16 s + li: from dS_T for the last segment, else from
+    // the gradient entering segment nseg - 2, carried over segments rg' = 1 .. rg - 1 for
+    // rg >= 2 (dS <- Q dS + R, Q staged at the start of the LDS before any chunk)
+    f32x4 D[RT];
     const size_t sbase = (static_cast<size_t>(n) * p.h_v + h) * DK * DV;
     if (chain) {
+        const float *Din = rg == 0 ? p.dS_T : p.rseg_S;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
-                D[rt][ii] = p.dS_T ? p.dS_T[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + 16 * s + li] : 0.f;
+                D[rt][ii] = Din ? Din[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + 16 * s + li] : 0.f;
     }
-    if (nchunks > 0) {
+    {
+        using PF = SegPFrag<DK, true>;
+        constexpr int H = RT / 2, NBLK = static_cast<int>(PF::BYTES / 1024);
+        static_assert(PF::BYTES + NWS * RT * 1024 <= static_cast<size_t>(RC::LDS), "carry fits");
+        const int nq = p.nseg - 2;
+        for (int hq = 1; hq < rg; ++hq) {   // rg >= 2 only; uniform over the workgroup
+            if (!chain) {
+                const char *Qh = reinterpret_cast<const char *>(p.rseg_Q) +
+                                 (static_cast<size_t>(pair) * nq + hq - 1) * PF::BYTES;
+                for (int blk = cw; blk < NBLK; blk += NCP) dma16(Qh + blk * 1024 + lane * 16, smem + blk * 1024);
+                wait_vmem();
+            }
+            f32x4 Rl[H], Rh[H];
+            if (chain) {
+                const float *Rq = p.rseg_R + (static_cast<size_t>(pair) * nq + hq - 1) * DK * DV;
+#pragma unroll
+                for (int j = 0; j < H; ++j)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        Rl[j][ii] = Rq[static_cast<size_t>(16 * j + 4 * lg + ii) * DV + 16 * s + li];
+                        Rh[j][ii] = Rq[static_cast<size_t>(16 * (H + j) + 4 * lg + ii) * DV + 16 * s + li];
+                    }
+            }
+            raw_barrier();                  // Q staged
+            if (chain) {                    // both halves from the same dS (the products pack it first)
+                f32x4 A[RT], B[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) A[rt] = B[rt] = D[rt];
+                f32x4 *xd = reinterpret_cast<f32x4 *>(smem + PF::BYTES) + wave * RT * 64;
+                PF::template carry_half<0>(smem, Rl, A, xd);
+                PF::template carry_half<H>(smem, Rh, B, xd);
+#pragma unroll
+                for (int j = 0; j < H; ++j) {
+                    D[j] = A[j];
+                    D[H + j] = B[H + j];
+                }
+            }
+            wait_lds();
+            raw_barrier();                  // every read of Q done before the LDS is restaged
+        }
+    }
+    if (ce > cb) {
         if (!chain) {
-            for (int c = nchunks - 1; c >= 0 && c > nchunks - NBUF; --c) stage(c);
-            wait_stage(min(nchunks - 1, NBUF - 2));
+            for (int c = ce - 1; c >= cb && c > ce - NBUF; --c) stage(c);
+            wait_stage(min(ce - 1 - cb, NBUF - 2));
         }
         lds_barrier();
     }
-    for (int c = nchunks - 1; c >= 0; --c) {
+    for (int c = ce - 1; c >= cb; --c) {
         if (!chain) {
-            if (c >= NBUF - 1) stage(c - (NBUF - 1));
-            if (c >= 1) wait_stage(min(c - 1, NBUF - 2));   // chunk c - 1 has landed
+            if (c - cb >= NBUF - 1) stage(c - (NBUF - 1));
+            if (c - cb >= 1) wait_stage(min(c - cb - 1, NBUF - 2));   // chunk c - 1 has landed
         } else {
             const char *buf = slot(c);
             const u32x4 *kga = reinterpret_cast<const u32x4 *>(buf);
@@ -311,13 +369,212 @@ void bwd_rchain_kernel(B16Params p) {
         }
         lds_barrier();                                      // slot(c) free; slot(c - 1) ready
     }
-    if (chain) {
+    if (chain && g == 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 p.dS0[sbase + static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + 16 * s + li] = D[rt][ii];
     }
+}
+
+// ---------------------------------------------------------------------------------------
+// Segmented reverse pass (dense batches with few (sequence, value head) pairs). The reverse
+// recursion is affine in the state gradient: dS_before = (diag(gamma_C) + Wn^T Kg) dS_after
+// + (E2 + Wn^T E1), so over a segment of chunks dS_in = Q dS_out + R. Segments are taken in
+// reverse order, rg = nseg - 1 - g for segment g of chunks [g L, (g + 1) L):
+//   bwd_rseg_kernel   rg = 0 (the last segment): the true run from dS_T, whose result is
+//                     the gradient entering segment nseg - 2 from above; rg = 1 .. nseg - 2:
+//                     R (from zero) and Q (the chain run on the columns of the identity
+//                     without E1 and E2). Only the chain is computed.
+//   bwd_rchain_kernel every segment from its own start, with outputs; segment rg >= 2 first
+//                     carries the gradient entering segment nseg - 2 over rg = 1 .. rg - 1,
+//                     dS <- Q dS + R.
+// ---------------------------------------------------------------------------------------
+constexpr int kRSegWaves = 4;    // chain waves per reverse segment-pass workgroup
+constexpr int kRSegCopy = 4;
+constexpr int kRSegRSlices = 2;  // R slices per workgroup (their E1 and E2 tiles are staged too)
+
+// Q workgroups (up to kRSegWaves slices of Q) stage Kg, Wn^T and gamma_C per chunk; R
+// workgroups (kRSegRSlices slices of R) also their slices' E1 and E2 tiles. Each kind takes
+// as many stages (<= 4) as fit in the LDS, so that up to three chunks are in flight.
+template <int DK, int DV>
+struct RSegLayout {
+    using L_ = BL16<DK, DV>;
+    static constexpr int OPS = static_cast<int>(L_::OPS);             // Kg, Wn^T fragments
+    static constexpr int EB = (C + DK) * 16 * 2;                      // E1 and E2 tiles of a slice
+    static constexpr int GC = OPS;                                    // gamma_C, fp32 [DK]
+    static constexpr int EO = GC + DK * 4;                            // [slice] E1, E2 tiles
+    static constexpr int QBUF = EO, RBUF = EO + kRSegRSlices * EB;
+    static constexpr int QN = QBUF * 4 <= 160 * 1024 ? 4 : 160 * 1024 / QBUF;
+    static constexpr int RN = RBUF * 4 <= 160 * 1024 ? 4 : 160 * 1024 / RBUF;
+    static constexpr int LDS = QN * QBUF > RN * RBUF ? QN * QBUF : RN * RBUF;
+    static constexpr int NQ = DK / 16, NR = DV / 16;                  // Q and R column slices
+    static constexpr int QG = (NQ + kRSegWaves - 1) / kRSegWaves;
+    static constexpr int GROUPS = QG + (NR + kRSegRSlices - 1) / kRSegRSlices;
+    static_assert(QN >= 2 && RN >= 2 && EB % 1024 == 0, "reverse segment stages");
+};
+
+// s_waitcnt vmcnt(min(n, 63)), n chosen at run time (copy waves only, off the critical path)
+template <int N = 63>
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+    if constexpr (N == 0) {
+        wait_vmem_n<0>();
+    } else {
+        if (n >= N) wait_vmem_n<N>();
+        else wait_vmem_upto<N - 1>(n);
+    }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * (kRSegWaves + kRSegCopy)) void bwd_rseg_kernel(B16Params p) {
+    using R_ = Rec<C, DK, DV, true>;
+    using L_ = BL16<DK, DV>;
+    using SG = RSegLayout<DK, DV>;
+    constexpr int RT = DK / 16, NKD = DK / 32;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+
+    const int bid = blockIdx.x, xcd = bid & 7, rest = bid >> 3;
+    const int grp = rest % SG::GROUPS;
+    const int unit = (rest / SG::GROUPS) * 8 + xcd;
+    const int nsa = p.nseg - 1;
+    if (unit >= p.num_pairs * nsa) return;
+    const int pair = unit / nsa, rg = unit - pair * nsa;
+    const bool qgrp = grp < SG::QG;
+    if (qgrp && rg == 0) return;                  // the last segment needs no Q (uniform)
+    const int n = pair / p.h_v, h = pair - n * p.h_v;
+    // this workgroup's slices [v0, v1) of Q (qgrp) or of R
+    const int v0 = qgrp ? grp * kRSegWaves : (grp - SG::QG) * kRSegRSlices;
+    const int v1 = qgrp ? min(v0 + kRSegWaves, SG::NQ) : min(v0 + kRSegRSlices, SG::NR);
+    const int nb = qgrp ? SG::QN : SG::RN, sb = qgrp ? SG::QBUF : SG::RBUF;
+    const int g = p.nseg - 1 - rg;
+    const int cb = g * p.seg_len;
+    const int ce = min(p.nc_dense, cb + p.seg_len);
+    const int nst = ce - cb;                      // chunks, taken from ce - 1 down to cb
+    const int cbase = n * p.nc_dense;
+    auto recno = [&](int c) { return static_cast<size_t>(cbase + c) * p.h_v + h; };
+    auto slot = [&](int i) { return smem + (i % nb) * sb; };
+
+    if (wave >= kRSegWaves) {
+        // ---- copy waves: up to nb - 1 steps in flight; step i is chunk ce - 1 - i
+        const int cw = wave - kRSegWaves;
+        const int ner = qgrp ? 0 : v1 - v0;       // R slices whose E1, E2 are staged
+        auto issue = [&](int i) {
+            char *dst = slot(i);
+            const int c = ce - 1 - i;
+            const char *cr = p.crec + recno(c) * L_::CREC;
+            for (int blk = cw; blk < SG::OPS / 1024; blk += kRSegCopy) dma16(cr + blk * 1024 + lane * 16, dst + blk * 1024);
+            if (cw == kRSegCopy - 1 && lane < DK / 4)
+                dma16(p.rec + recno(c) * R_::bytes + R_::gC + lane * 16, dst + SG::GC);
+            for (int r = 0; r < ner; ++r) {
+                const char *e1 = cr + L_::E1 + static_cast<size_t>(v0 + r) * NRC * 512;
+                const char *e2 = cr + L_::E2 + static_cast<size_t>(v0 + r) * RT * 512;
+                char *d = dst + SG::EO + r * SG::EB;
+                for (int blk = cw; blk < SG::EB / 1024; blk += kRSegCopy) {
+                    const char *src = blk < NRC / 2 ? e1 + blk * 1024 : e2 + (blk - NRC / 2) * 1024;
+                    dma16(src + lane * 16, d + blk * 1024);
+                }
+            }
+        };
+        // direct loads this wave issues per step (the loops of issue())
+        const int per = (SG::OPS / 1024 - cw + kRSegCopy - 1) / kRSegCopy + (cw == kRSegCopy - 1 ? 1 : 0) +
+                        ner * ((SG::EB / 1024 - cw + kRSegCopy - 1) / kRSegCopy);
+        int issued = 0;
+        for (; issued < nst && issued < nb - 1; ++issued) issue(issued);
+        for (int i = 0; i < nst; ++i) {
+            wait_vmem_upto((issued - 1 - i) * per);   // step i has landed
+            raw_barrier();                  // step i is staged; step i-1 fully consumed
+            if (issued < nst) issue(issued++);   // into the slot of step i-1
+        }
+        return;
+    }
+
+    // ---- chain waves ----
+    const int v = v0 + wave;
+    const bool active = v < v1;                   // uniform per wave
+    const int col = 16 * v + li;
+    f32x4 D[RT];
+    const size_t sbase = static_cast<size_t>(pair) * DK * DV;
+    const bool fromT = active && !qgrp && rg == 0 && p.dS_T != nullptr;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int row = 16 * rt + 4 * lg + ii;
+            D[rt][ii] = fromT ? p.dS_T[sbase + static_cast<size_t>(row) * DV + col]
+                              : (qgrp && row == col ? 1.f : 0.f);
+        }
+    for (int i = 0; i < nst; ++i) {
+        const char *buf = slot(i);
+        raw_barrier();                      // step i is staged; step i-1 fully consumed
+        if (!active) continue;
+        const u32x4 *kga = reinterpret_cast<const u32x4 *>(buf);
+        const u32x4 *wnt = kga + C * DK / 8;
+        const float *gam = reinterpret_cast<const float *>(buf + SG::GC);
+        const u32x2 *e1 = reinterpret_cast<const u32x2 *>(buf + SG::EO + wave * SG::EB);
+        const u32x2 *e2 = e1 + NRC * 64;
+        // the products' LDS operands first (no E1, E2 on Q columns)
+        u32x4 ka[NRC][NKD], wa[RT][NKC];
+        u32x2 e1v[NRC], e2v[RT];
+#pragma unroll
+        for (int ut = 0; ut < NRC; ++ut) {
+            if (!qgrp) e1v[ut] = e1[ut * 64 + lane];
+#pragma unroll
+            for (int kt = 0; kt < NKD; ++kt) ka[ut][kt] = kga[(ut * NKD + kt) * 64 + lane];
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (!qgrp) e2v[rt] = e2[rt * 64 + lane];
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) wa[rt][kt] = wnt[(rt * NKC + kt) * 64 + lane];
+        }
+        u32x4 Dp[NKD];
+#pragma unroll
+        for (int kt = 0; kt < NKD; ++kt) Dp[kt] = dpair_to_b32(D[2 * kt], D[2 * kt + 1]);
+        // dU = E1 + Kg dS'
+        f32x4 U[NRC];
+#pragma unroll
+        for (int ut = 0; ut < NRC; ++ut) {
+            f32x4 acc = qgrp ? f32x4{0.f, 0.f, 0.f, 0.f} : b16_to_f4(e1v[ut]);
+#pragma unroll
+            for (int kt = 0; kt < NKD; ++kt) acc = mma_k32(ka[ut][kt], Dp[kt], acc);
+            U[ut] = acc;
+        }
+        u32x4 Up[NKC];
+#pragma unroll
+        for (int kt = 0; kt < NKC; ++kt) Up[kt] = dpair_to_b32(U[2 * kt], U[2 * kt + 1]);
+        // dS = E2 + gamma_C dS' + Wn^T dU
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            f32x4 acc = qgrp ? f32x4{0.f, 0.f, 0.f, 0.f} : b16_to_f4(e2v[rt]);
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&gam[16 * rt + 4 * lg]);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[ii] += g4[ii] * D[rt][ii];
+#pragma unroll
+            for (int kt = 0; kt < NKC; ++kt) acc = mma_k32(wa[rt][kt], Up[kt], acc);
+            D[rt] = acc;
+        }
+        wait_lds();
+    }
+    if (!active) return;
+    if (qgrp) {
+        char *dst = reinterpret_cast<char *>(p.rseg_Q) +
+                    (static_cast<size_t>(pair) * (nsa - 1) + rg - 1) * SegPFrag<DK, true>::BYTES;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                SegPFrag<DK, true>::put(dst, 16 * rt + 4 * lg + ii, col, D[rt][ii]);
+        return;
+    }
+    float *dst = rg == 0 ? p.rseg_S + static_cast<size_t>(pair) * DK * DV   // entering segment nseg-2
+                         : p.rseg_R + (static_cast<size_t>(pair) * (nsa - 1) + rg - 1) * DK * DV;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            dst[static_cast<size_t>(16 * rt + 4 * lg + ii) * DV + col] = D[rt][ii];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -876,17 +1133,40 @@ __global__ void zero2_kernel(float *a, float *b, int64_t n) {
 }
 
 constexpr int kChainSlices = 1;     // value slices per reverse-pass workgroup
+constexpr int kSegChainSlices = 2;  // the same when the reverse pass is segmented
+constexpr int64_t kRSegTargetWGs = 256;
 
 static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Segmentation of the reverse pass: dense batches whose reverse pass would leave at least
+// half of the CUs idle, in at least three segments of at least four chunks, aiming at about
+// kRSegTargetWGs workgroups of kSegChainSlices slices. With nseg segments the serial depth is
+// about two segments plus nseg - 2 carries instead of every chunk.
+struct RSegPlan {
+    int nseg, seg_len;
+};
+static RSegPlan rseg_plan(bool packed, int64_t pairs, int nc, int d_v) {
+    const RSegPlan one{1, nc};
+    const int64_t g1 = d_v / 16 / kChainSlices, g2 = d_v / 16 / kSegChainSlices;
+    if (packed || pairs <= 0 || nc < 12 || 2 * pairs * g1 > kRSegTargetWGs) return one;
+    int64_t G = kRSegTargetWGs / (pairs * g2);
+    if (G > nc / 4) G = nc / 4;
+    if (G < 3) return one;
+    const int L = static_cast<int>((nc + G - 1) / G);
+    const RSegPlan sp{(nc + L - 1) / L, L};
+    return sp.nseg >= 3 ? sp : one;
+}
+
 // Workspace of the bf16 backward: the forward's (map, records, segment buffers), then the
-// state entering every chunk and U of every chunk (bf16 fragments), T per record, and the
-// per-record buffers of BL16.
+// state entering every chunk and U of every chunk (bf16 fragments), T per record, the
+// per-record buffers of BL16 and the reverse pass's segment buffers (B16Params).
 struct B16Ws {
-    size_t ck, cu, tm, crec, cout, total;
+    size_t ck, cu, tm, crec, cout, rs, rq, rr, total;
+    RSegPlan sp;
 };
 static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v, bool packed) {
     const int64_t nrec = chunk_upper_bound(C, batch, seqlen, num_seqs, packed) * h_v;
+    const int64_t pairs = static_cast<int64_t>(packed ? num_seqs : batch) * h_v;
     const size_t crec = 4 * static_cast<size_t>(C) * d_k + 2 * static_cast<size_t>(C) * d_v +
                         2 * static_cast<size_t>(d_k) * d_v;
     const size_t cout = 2 * static_cast<size_t>(d_k) * d_v + 2 * static_cast<size_t>(C) * d_v;
@@ -896,7 +1176,12 @@ static B16Ws bwd16_ws(int batch, int seqlen, int num_seqs, int h_v, int d_k, int
     w.tm = al256(w.cu + static_cast<size_t>(nrec) * C * d_v * 2);
     w.crec = al256(w.tm + static_cast<size_t>(nrec) * C * C * 2);
     w.cout = al256(w.crec + static_cast<size_t>(nrec) * crec);
-    w.total = w.cout + static_cast<size_t>(nrec) * cout;
+    w.sp = rseg_plan(packed, pairs, (seqlen + C - 1) / C, d_v);
+    const size_t nPR = w.sp.nseg > 2 ? static_cast<size_t>(w.sp.nseg - 2) : 0;
+    w.rs = al256(w.cout + static_cast<size_t>(nrec) * cout);
+    w.rq = al256(w.rs + (w.sp.nseg > 1 ? static_cast<size_t>(pairs) * d_k * d_v * 4 : 0));
+    w.rr = al256(w.rq + static_cast<size_t>(pairs) * nPR * d_k * d_k * 4);
+    w.total = w.rr + static_cast<size_t>(pairs) * nPR * d_k * d_v * 4;
     return w;
 }
 
@@ -914,7 +1199,9 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
                       L_::COUT == 2 * static_cast<size_t>(DK) * DV + 2 * static_cast<size_t>(C) * DV,
                   "the per-record buffers match bwd16_ws");
     using RC = RChain<DK, DV, kChainSlices>;
-    static_assert(RC::LDS <= 160 * 1024 && GLay<DK, DV>::LDS <= 160 * 1024, "LDS");
+    using RC2 = RChain<DK, DV, kSegChainSlices>;
+    using SG = RSegLayout<DK, DV>;
+    static_assert(RC::LDS <= 160 * 1024 && RC2::LDS <= 160 * 1024 && GLay<DK, DV>::LDS <= 160 * 1024, "LDS");
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
     const int64_t nrec = chunk_upper_bound(C, a.batch, a.seqlen, a.num_seqs, packed) * a.h_v;
@@ -956,6 +1243,11 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     p.nc_dense = (a.seqlen + C - 1) / C;
     p.h_k = a.h_k; p.h_v = a.h_v; p.group = a.h_v / a.h_k;
     p.num_pairs = N * a.h_v;
+    p.nseg = ws.sp.nseg;
+    p.seg_len = ws.sp.seg_len;
+    p.rseg_S = p.nseg > 1 ? reinterpret_cast<float *>(base + ws.rs) : nullptr;
+    p.rseg_Q = p.nseg > 2 ? reinterpret_cast<float *>(base + ws.rq) : nullptr;
+    p.rseg_R = p.nseg > 2 ? reinterpret_cast<float *>(base + ws.rr) : nullptr;
 
     const int64_t qk = static_cast<int64_t>(a.batch) * a.seqlen * a.h_k * DK;
     if (qk > 0 && p.group > 1) {
@@ -963,9 +1255,19 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(zero2_kernel, dim3(blocks < 4096 ? blocks : 4096), dim3(256), 0, st,
                            a.dq, a.dk, qk);
     }
-    if ((e = set_lds(bwd_rchain_kernel<DK, DV, kChainSlices>, RC::LDS)) != hipSuccess) return e;
     if ((e = set_lds(bwd_grads16_kernel<DK, DV>, GLay<DK, DV>::LDS)) != hipSuccess) return e;
-    if (p.num_pairs > 0) {
+    if (p.num_pairs > 0 && p.nseg > 1) {
+        // the segment pass over segments rg = 0 .. nseg - 2, then every segment with its carry
+        if ((e = set_lds(bwd_rseg_kernel<DK, DV>, SG::LDS)) != hipSuccess) return e;
+        if ((e = set_lds(bwd_rchain_kernel<DK, DV, kSegChainSlices>, RC2::LDS)) != hipSuccess) return e;
+        const int64_t su = static_cast<int64_t>(p.num_pairs) * (p.nseg - 1);
+        hipLaunchKernelGGL((bwd_rseg_kernel<DK, DV>), dim3((su + 7) / 8 * 8 * SG::GROUPS),
+                           dim3(64 * (kRSegWaves + kRSegCopy)), SG::LDS, st, p);
+        const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
+        hipLaunchKernelGGL((bwd_rchain_kernel<DK, DV, kSegChainSlices>), dim3((units + 7) / 8 * 8 * RC2::G),
+                           dim3(64 * (kSegChainSlices + RC2::NCP)), RC2::LDS, st, p);
+    } else if (p.num_pairs > 0) {
+        if ((e = set_lds(bwd_rchain_kernel<DK, DV, kChainSlices>, RC::LDS)) != hipSuccess) return e;
         const int64_t blocks = static_cast<int64_t>((p.num_pairs + 7) / 8) * 8 * RC::G;
         hipLaunchKernelGGL((bwd_rchain_kernel<DK, DV, kChainSlices>), dim3(blocks),
                            dim3(64 * (kChainSlices + RC::NCP)), RC::LDS, st, p);

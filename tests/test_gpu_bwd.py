@@ -2,8 +2,10 @@
 adjoint of the recurrence (oracle.recurrent_bwd), every gradient by relative L2: 1e-4 for
 fp32 inputs, 2e-2 for bf16 inputs. Cases: ragged tails, grouped value heads (2 and 3 per
 key head, and 4 over 32 pairs), every built head shape, packed batches with an empty
-sequence, zero initial state and zero dS_T, and the timed chunk shape (whose forward takes
-the segmented state pass); bit-equal repeated calls when no value heads share a key head."""
+sequence, zero initial state and zero dS_T, the timed chunk shape (whose forward takes
+the segmented state pass and whose reverse pass is segmented too), dense batches of few pairs
+in 3 to 8 reverse segments (a ragged last segment, grouped heads); bit-equal repeated calls
+when no value heads share a key head."""
 import numpy as np
 import pytest
 import torch
@@ -144,3 +146,19 @@ def test_bwd_extreme_decay(dtype, dk, dv):
     wl = inputs.small_chunk(dtype=dtype, batch=1, seqlen=300, h_k=2, h_v=2, d_k=dk, d_v=dv,
                             neg_eig=True, s0_std=0.1)
     run_case(inputs.chunk_inputs(wl, seed=65, decay_mu=3.0), f"extreme decay {dtype} {dk}x{dv}", 9)
+
+
+@pytest.mark.parametrize("batch,seqlen,h_k,h_v,dk,dv,label", [
+    (1, 1300, 1, 2, 128, 128, "5 segments of 5 chunks, the last one a single ragged chunk"),
+    (2, 900, 1, 2, 64, 64, "3 segments of 5 chunks"),
+    (1, 2000, 2, 4, 128, 64, "8 segments of 4 chunks, two value heads per key head"),
+    (1, 1000, 1, 2, 64, 128, "4 segments of 4 chunks"),
+])
+def test_bwd_segmented_reverse_pass(batch, seqlen, h_k, h_v, dk, dv, label):
+    """Dense batches with few (sequence, value head) pairs take the segmented reverse pass:
+    the segment pass forms, per later segment, the gradient transition and the zero-start
+    result, and every segment's reverse chain starts from the carried gradient."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=batch, seqlen=seqlen, h_k=h_k, h_v=h_v,
+                            d_k=dk, d_v=dv, neg_eig=True)
+    run_case(inputs.chunk_inputs(wl, seed=80 + seqlen % 17), f"bf16 {dk}x{dv} B={batch} "
+             f"T={seqlen} H_k={h_k} H_v={h_v}: {label}", 9)
