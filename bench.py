@@ -679,7 +679,7 @@ def pmc_summary(fetch_dir, write_dir):
         c64_bf16 = base == "prep_kernel" and targs[2] == "64" and "bf16" in targs[0]
         if base in ("chunk_seg_kernel", "chunk_state_kernel") or c64_bf16:
             parts = [("chunk_fwd_t4096", 0, 5), ("chunk_bwd_t4096", 5, 8)]
-        elif base in ("prep_kernel", "panel_state_kernel"):
+        elif base in ("prep_kernel", "panel_seg_kernel", "panel_state_kernel"):
             parts = [("chunk_fwd_f32_t4096" if "float" in targs[0] else "chunk_fwd_t4096_c128", 0, 2)]
         elif base.startswith("bwd_"):
             parts = [("chunk_bwd_t4096", 0, 3)]
