@@ -341,12 +341,11 @@ def bench_chunk_states(steps, warmup, seed=10):
     return res
 
 
-def bench_chunk_bwd(steps, warmup, seed=11):
-    """The chunked backward (gdn2_chunk_bwd) on the timed chunk workload: the forward re-run
-    that stores the chunk states, the reverse state pass and the per-chunk gradients.
-    Algorithmic bytes: the forward inputs, dO, S0 and dS_T read once, the fp32 gradients
-    written once."""
-    wl = inputs.CHUNK_BF16_T4096
+def bench_chunk_bwd(steps, warmup, seed=11, wl=inputs.CHUNK_BF16_T4096):
+    """The chunked backward (gdn2_chunk_bwd) on a chunk workload (the timed one by default):
+    the forward re-run that stores the chunk states, the reverse state pass and the per-chunk
+    gradients. Algorithmic bytes: the forward inputs, dO, S0 and dS_T read once, the fp32
+    gradients written once."""
     x = inputs.chunk_inputs_device(wl, seed)
     B, T = x["q"].shape[:2]
     gen = torch.Generator(device="cuda")
@@ -363,16 +362,17 @@ def bench_chunk_bwd(steps, warmup, seed=11):
     for _ in range(warmup):
         call()
     t = time_region(call, steps, torch.cuda.current_stream())
-    e = 2
+    e = 2 if wl.dtype == torch.bfloat16 else 4
     tok_in = T * (2 * wl.h_k * wl.d_k + wl.h_v * (2 * wl.d_k + 3 * wl.d_v)) * e   # q k, la b, v w dO
     grads = T * (2 * wl.h_k * wl.d_k + wl.h_v * (2 * wl.d_k + 2 * wl.d_v)) * 4
     states = 3 * x["S0"].numel() * 4                                          # S0, dS_T, dS0
     nbytes = tok_in + grads + states
     del x, ws, dO, dST
     bsrc = source_hash(*BWD_SRC)
+    timed = wl is inputs.CHUNK_BF16_T4096
     return {"workload": f"{wl.name}_bwd", "us_per_call": t * 1e6, "tokens_per_s": T * B / t,
             "alg_bytes": nbytes, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
-            "traffic": measured_traffic("chunk_bwd_t4096", bsrc)}
+            "traffic": measured_traffic("chunk_bwd_t4096", bsrc) if timed else None}
 
 
 def bench_fused(steps, warmup, seed=8):
@@ -820,9 +820,11 @@ def main():
         out["gate_variants"] = bench_gate_variants(max(10, args.steps // 4), 3)
         out["chunk_states"] = bench_chunk_states(max(10, args.steps // 4), 3)
         out["chunk_bwd"] = bench_chunk_bwd(max(5, args.steps // 10), 2)
+    t4096_f32 = dataclasses.replace(inputs.CHUNK_BF16_T4096, dtype=torch.float32,
+                                    name="chunk_f32_b1_t4096_h16_d128_negeig")
+    if args.only == "all" and not args.no_other_workloads:
+        out["chunk_bwd_f32"] = bench_chunk_bwd(5, 2, wl=t4096_f32)
     if args.only in ("chunk", "all") and not args.no_other_workloads:
-        t4096_f32 = dataclasses.replace(inputs.CHUNK_BF16_T4096, dtype=torch.float32,
-                                        name="chunk_f32_b1_t4096_h16_d128_negeig")
         out["other_chunk_workloads"] = [
             bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed, chunk)
             for wl, seed, chunk in ((inputs.CHUNK_F32_SMALL, 2000, 64),

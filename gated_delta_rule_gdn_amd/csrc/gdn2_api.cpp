@@ -110,14 +110,13 @@ const char *gdn2_status_string(int32_t s) {
 
 const char *gdn2_last_error(void) { return g_last_error; }
 
-// The chunked backward is built for 64-token chunks, bf16 records at any supported head dims
-// and fp32 records at d_k = d_v = 64.
+// The chunked backward takes the chunk size of the forward whose gradients it forms (32, 64
+// or 128). The gradients do not depend on it, and every chunk size is computed with 64-token
+// chunks, for both dtypes at every supported head-dim pair.
 static gdn2_status check_bwd_built(const gdn2_dims *d, int32_t chunk_size) {
     if (!d) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
-    if (chunk_size != gdn2::kChunk)
-        return fail(GDN2_ERR_UNSUPPORTED, "the chunked backward is built for chunk_size 64");
-    if (d->dtype == GDN2_F32 && (d->d_k != 64 || d->d_v != 64))
-        return fail(GDN2_ERR_UNSUPPORTED, "the fp32 chunked backward is built for d_k = d_v = 64");
+    if (!gdn2::chunk_size_built(chunk_size))
+        return fail(GDN2_ERR_UNSUPPORTED, "chunk_size must be 32, 64 or 128");
     return GDN2_OK;
 }
 

@@ -24,8 +24,8 @@
 //   bwd_grads_kernel    per record, in parallel: every input gradient of the chunk
 // The record kernels keep their intermediates in a per-record fp32 scratch of the workspace
 // and stage each product's operands in LDS; their products are fp32 matrix-core tiles
-// (16x16x4), as are the reverse pass's. This is the path for fp32 inputs (built at
-// d_k = d_v = 64); bf16 inputs take gdn2_bwd16.hip. q and k gradients of value heads that
+// (16x16x4), as are the reverse pass's. This is the path for fp32 inputs (every head-dim
+// pair); bf16 inputs take gdn2_bwd16.hip. q and k gradients of value heads that
 // share a key head are summed with fp32 atomics; with one value head per key head they are
 // stored.
 #include "gdn2_common.h"
@@ -810,6 +810,9 @@ size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, i
 hipError_t launch_chunk_bwd(const BwdArgs &a, hipStream_t st) {
     if (a.bf16) return launch_chunk_bwd16(a, st);
     if (a.d_k == 64 && a.d_v == 64) return launch_bwd_t<float, 64, 64>(a, st);
+    if (a.d_k == 128 && a.d_v == 128) return launch_bwd_t<float, 128, 128>(a, st);
+    if (a.d_k == 128 && a.d_v == 64) return launch_bwd_t<float, 128, 64>(a, st);
+    if (a.d_k == 64 && a.d_v == 128) return launch_bwd_t<float, 64, 128>(a, st);
     return hipErrorInvalidValue;            // refused by the API layer before the launch
 }
 

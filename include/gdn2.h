@@ -244,12 +244,15 @@ size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
  * input and the initial state, taken through the chunked form of the burn-gdn2 docs page
  * ("Architecture", Chunk mode; its Chunk WY training path): the forward is re-run to store
  * the state entering every chunk, then one pass runs the state gradient backward over the
- * chunks, and one pass per chunk forms the input gradients. Built for chunk_size 64, with
- * bf16 inputs at every supported head-dim pair (bf16 matrix-core products, fp32
- * accumulation) and with fp32 inputs at d_k = d_v = 64 (fp32 products); other
- * configurations return GDN2_ERR_UNSUPPORTED.
+ * chunks, and one pass per chunk forms the input gradients. Built for bf16 inputs (bf16
+ * matrix-core products, fp32 accumulation) and fp32 inputs (fp32 products) at every
+ * supported head-dim pair.
  *
- *   q .. w, S0, cu_seqlens, chunk_size, dims   as for gdn2_chunk_fwd
+ *   q .. w, S0, cu_seqlens, dims   as for gdn2_chunk_fwd
+ *   chunk_size  32, 64 or 128: the chunk size of the forward call whose gradients these are.
+ *               The chunked form computes the same function at every chunk size, so the
+ *               gradients do not depend on it; all three are computed with 64-token chunks
+ *               (the same bits). Other values return GDN2_ERR_UNSUPPORTED.
  *   dO          device [B, T, h_v, d_v] in the input dtype: dL/do
  *   dS_T        device fp32 [N, h_v, d_k, d_v]: dL/dS_T, or NULL for zero
  *   dq, dk      device fp32 [B, T, h_k, d_k]   (value heads that share a key head add up,

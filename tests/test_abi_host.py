@@ -309,17 +309,22 @@ def test_chunk_bwd_validation(L):
     need = L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 64)
     assert need > L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64)
     assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(Dims(2, 100, 0, 2, 4, 32, 128, 1)), 64) == 0
-    # the backward is built for 64-token chunks, and in fp32 for d_k = d_v = 64
-    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 128) == 0
-    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(Dims(2, 100, 0, 2, 4, 128, 128, 0)), 64) == 0
+    # every built chunk size is computed with 64-token chunks (the same workspace); others
+    # are refused
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 128) == need
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 32) == need
+    assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(d), 48) == 0
+    # fp32 at every head-dim pair
+    for dk, dv in ((64, 64), (128, 128), (128, 64), (64, 128)):
+        assert L.gdn2_chunk_bwd_workspace_bytes(ctypes.byref(Dims(2, 100, 0, 2, 4, dk, dv, 0)), 64) > 0
 
-    def call(dims=d, outs=None, ws=P[19], ws_bytes=None, dO=P[8]):
+    def call(dims=d, outs=None, ws=P[19], ws_bytes=None, dO=P[8], chunk=64):
         o = P[10:17] if outs is None else outs
-        return L.gdn2_chunk_bwd(P[0], P[1], P[2], P[3], P[4], P[5], None, None, 64, dO, None,
+        return L.gdn2_chunk_bwd(P[0], P[1], P[2], P[3], P[4], P[5], None, None, chunk, dO, None,
                                 *o, ctypes.byref(dims), ws, need if ws_bytes is None else ws_bytes,
                                 None)
     assert call(dims=Dims(2, 100, 0, 2, 4, 128, 128, 7)) == 3          # dtype
-    assert call(dims=Dims(2, 100, 0, 2, 4, 128, 128, 0)) == 3          # fp32 at d = 128
+    assert call(chunk=48) == 3                                         # chunk size not built
     assert call(dims=Dims(2, 100, 0, 2, 5, 128, 128, 1)) == 2          # h_v not a multiple of h_k
     assert call(dO=None) == 1
     assert call(outs=[None] + P[11:17]) == 1

@@ -26,7 +26,7 @@ def setup_module(module):
     g.lib()
 
 
-def run_case(x, label, seed, with_states=True):
+def run_case(x, label, seed, with_states=True, chunk_size=64):
     dtype = x["q"].dtype
     d = to_gpu(x)
     B, T = x["q"].shape[:2]
@@ -38,7 +38,7 @@ def run_case(x, label, seed, with_states=True):
     print(f"[case] chunk_bwd {label}", flush=True)
     got = g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO.cuda(),
                       S0=d["S0"], cu_seqlens=d["cu_seqlens"],
-                      dS_T=None if dST is None else dST.cuda())
+                      dS_T=None if dST is None else dST.cuda(), chunk_size=chunk_size)
     torch.cuda.synchronize()
     f, cu, S0 = flat_inputs(x)
     ref = oracle.recurrent_bwd(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"],
@@ -53,6 +53,7 @@ def run_case(x, label, seed, with_states=True):
           flush=True)
     assert all(np.isfinite(list(errs.values())))
     assert max(errs.values()) <= TOL[dtype], errs
+    return got
 
 
 def test_bwd_fp32_gva_ragged():
@@ -162,3 +163,28 @@ def test_bwd_segmented_reverse_pass(batch, seqlen, h_k, h_v, dk, dv, label):
                             d_k=dk, d_v=dv, neg_eig=True)
     run_case(inputs.chunk_inputs(wl, seed=80 + seqlen % 17), f"bf16 {dk}x{dv} B={batch} "
              f"T={seqlen} H_k={h_k} H_v={h_v}: {label}", 9)
+
+
+@pytest.mark.parametrize("dk,dv,h_k,h_v,seqlen", [(128, 128, 1, 2, 200), (128, 64, 1, 2, 150),
+                                                  (64, 128, 2, 4, 130)])
+def test_bwd_fp32_every_head_dim_pair(dk, dv, h_k, h_v, seqlen):
+    """fp32 inputs at d = 128 and at the mixed head dims (fp32 products throughout), ragged
+    tails and grouped value heads, at the fp32 bar."""
+    wl = inputs.small_chunk(dtype=torch.float32, batch=2, seqlen=seqlen, h_k=h_k, h_v=h_v,
+                            d_k=dk, d_v=dv, neg_eig=True)
+    run_case(inputs.chunk_inputs(wl, seed=90 + dk // 64 + dv // 32), f"fp32 {dk}x{dv} B=2 "
+             f"T={seqlen} H_k={h_k} H_v={h_v}", 10)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_bwd_chunk_size_does_not_change_the_gradients(dtype):
+    """chunk_size names the forward's chunking; the gradients do not depend on it. Calls at
+    chunk sizes 32 and 128 match the oracle and give the bits of the chunk-64 call."""
+    wl = inputs.small_chunk(dtype=dtype, batch=1, seqlen=300, h_k=2, h_v=2, d_k=128, d_v=128,
+                            neg_eig=True)      # (no grouped heads: no atomics, the same bits)
+    x = inputs.chunk_inputs(wl, seed=95)
+    ref = run_case(x, f"{dtype} 128x128 T=300, chunk_size 64", 11)
+    for cs in (32, 128):
+        got = run_case(x, f"{dtype} 128x128 T=300, chunk_size {cs}", 11, chunk_size=cs)
+        for n in ref:
+            assert torch.equal(got[n], ref[n]), (cs, n)
