@@ -26,7 +26,8 @@ Two independent evaluations of the method live here:
 * ``variant_sequence`` / ``variant`` -- the update rules of the neighbouring delta-rule
   models the pages name (the scalar-gate KDA that the "Architecture" section says b and w
   replace, a scalar-decay GDN, and FG2-GDN and FG2-GDN+ of the FG2-GDN summary, section 2),
-  each written from its own formula in numpy fp64.
+  each written from its own formula in numpy fp64. ``map_gates`` gives the GDN-2 inputs of
+  each variant and ``map_gates_bwd`` the chain rule back through them.
 * ``chunked_sequence_bwd`` -- the gradient taken through that chunked form, step by step
   (the backward pass chunked kernels follow), checked against ``recurrent_bwd``.
 * ``chunked`` -- the chunked WY form named on the same page (the "Chunk" training
@@ -601,6 +602,64 @@ def variant(mode, q, k, v, log_alpha, beta, S0=None, beta_v=None, pairs=None):
             np.asarray(beta)[n, :, h], S_init,
             None if beta_v is None else np.asarray(beta_v)[n, :, h])
     return o, S_T
+
+
+def map_gates(mode, q, k, v, log_alpha, beta, beta_v=None):
+    """The GDN-2 inputs under which the GDN-2 recurrence (``sequence``) is the variant
+    ``mode`` of ``variant_sequence``, for one (sequence, value head) pair. The burn-gdn2
+    "Architecture" section says the channel-wise b and w replace KDA's scalar gate; the FG2
+    modes fold sqrt(beta) into the keys and values (FG2-GDN summary, section 2):
+
+    * ``"kda"``: b = beta 1 [T, d_k], w = beta 1 [T, d_v]; q, k, v, log_alpha unchanged;
+    * ``"gdn"``: as kda, log_alpha [T] broadcast over d_k;
+    * ``"fg2"``: k' = sqrt(beta) k, v' = sqrt(beta) v, b = w = 1;
+    * ``"fg2+"``: k' = sqrt(beta) k, b = 1, w = sqrt(beta_v), v unchanged.
+
+    Shapes as in ``variant_sequence``. Returns (q', k', v', log_alpha', b, w) fp64."""
+    q, k, v, la, beta = (_f64(x) for x in (q, k, v, log_alpha, beta))
+    T, d_k = k.shape
+    d_v = v.shape[1]
+    if mode in ("kda", "gdn"):
+        b = np.repeat(beta[:, None], d_k, axis=1)
+        w = np.repeat(beta[:, None], d_v, axis=1)
+        la2 = np.repeat(la[:, None], d_k, axis=1) if mode == "gdn" else la
+        return q, k, v, la2, b, w
+    if mode == "fg2":
+        return q, np.sqrt(beta) * k, np.sqrt(beta) * v, la, np.ones((T, d_k)), np.ones((T, d_v))
+    if mode == "fg2+":
+        return q, np.sqrt(beta) * k, v, la, np.ones((T, d_k)), np.sqrt(_f64(beta_v))
+    raise ValueError(f"unknown mode {mode!r}")
+
+
+def map_gates_bwd(mode, q, k, v, log_alpha, beta, grads, beta_v=None):
+    """The chain rule through ``map_gates`` for one pair: ``grads`` holds the gradients of
+    a loss with respect to the mapped inputs (the keys of ``sequence_bwd``: dq, dk, dv,
+    dlog_alpha, db, dw); returns the gradients with respect to the variant's own inputs,
+    dict dq, dk, dv, dlog_alpha, dbeta (and dbeta_v for ``"fg2+"``), fp64, in the shapes of
+    ``variant_sequence``'s inputs. b and w are constants in the FG2 modes, so their gradients
+    end there. The derivative of sqrt(beta) is 1 / (2 sqrt(beta)): beta must be > 0 there."""
+    q, k, v, la, beta = (_f64(x) for x in (q, k, v, log_alpha, beta))
+    g = {n: _f64(x) for n, x in grads.items()}
+    out = {"dq": g["dq"], "dv": g["dv"], "dlog_alpha": g["dlog_alpha"]}
+    if mode in ("kda", "gdn"):
+        # b and w are beta in every channel: dbeta sums their gradients over the channels
+        out["dk"] = g["dk"]
+        out["dbeta"] = g["db"].sum(axis=1) + g["dw"].sum(axis=1)
+        if mode == "gdn":
+            out["dlog_alpha"] = g["dlog_alpha"].sum(axis=1)
+        return out
+    if mode not in ("fg2", "fg2+"):
+        raise ValueError(f"unknown mode {mode!r}")
+    sb = np.sqrt(beta)
+    out["dk"] = sb * g["dk"]                              # k' = sqrt(beta) k
+    dbeta = g["dk"] * k / (2.0 * sb)
+    if mode == "fg2":
+        out["dv"] = sb * g["dv"]                          # v' = sqrt(beta) v
+        dbeta = dbeta + g["dv"] * v / (2.0 * sb)
+    else:
+        out["dbeta_v"] = g["dw"] / (2.0 * np.sqrt(_f64(beta_v)))   # w = sqrt(beta_v)
+    out["dbeta"] = dbeta
+    return out
 
 
 def rel_l2(x, ref) -> float:

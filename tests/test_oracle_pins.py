@@ -685,6 +685,60 @@ def test_variant_fg2_plus_with_equal_scales_is_fg2():
     assert close(o1, o2) and close(S1, S2)
 
 
+# ---- the gate mappings onto GDN-2 inputs and their chain rule (oracle.map_gates[_bwd]) ---
+
+@pytest.mark.parametrize("mode", ["kda", "gdn", "fg2", "fg2+"])
+def test_map_gates_gives_the_variant(mode):
+    """The GDN-2 recurrence on the mapped inputs is the variant's own update rule."""
+    rng = np.random.default_rng(36)
+    T, dk = 9, 5
+    dv = dk if mode == "fg2" else 3
+    q, k, v, la, beta, beta_v = variant_case(rng, T, dk, dv, mode)
+    S0 = rng.standard_normal((dk, dv))
+    o, ST = oracle.variant_sequence(mode, q, k, v, la, beta, S0, beta_v)
+    q2, k2, v2, la2, b, w = oracle.map_gates(mode, q, k, v, la, beta, beta_v)
+    o2, S2 = oracle.sequence(q2, k2, v2, w, la2, b, S0)
+    assert close(o, o2) and close(ST, S2)
+
+
+@pytest.mark.parametrize("mode", ["kda", "gdn", "fg2", "fg2+"])
+def test_map_gates_bwd_matches_finite_differences(mode):
+    """Gradients of L = <dO, o> + <dS_T, S_T> of the variant with respect to each of its own
+    inputs: the composition map_gates -> sequence_bwd -> map_gates_bwd against central
+    differences of variant_sequence (the variant's own rule), every element."""
+    rng = np.random.default_rng(37)
+    T, dk = 4, 3
+    dv = dk if mode == "fg2" else 2
+    q, k, v, la, beta, beta_v = variant_case(rng, T, dk, dv, mode)
+    S0 = rng.standard_normal((dk, dv))
+    dO = rng.standard_normal((T, dv))
+    dST = rng.standard_normal((dk, dv))
+    m = oracle.map_gates(mode, q, k, v, la, beta, beta_v)
+    gm = oracle.sequence_bwd(m[0], m[1], m[2], m[5], m[3], m[4], S0, dO, dST)
+    got = oracle.map_gates_bwd(mode, q, k, v, la, beta, gm, beta_v)
+    x = {"q": q, "k": k, "v": v, "log_alpha": la, "beta": beta}
+    if mode == "fg2+":
+        x["beta_v"] = beta_v
+
+    def loss(xx):
+        o, ST = oracle.variant_sequence(mode, xx["q"], xx["k"], xx["v"], xx["log_alpha"],
+                                        xx["beta"], S0, xx.get("beta_v"))
+        return float(np.sum(dO * o) + np.sum(dST * ST))
+
+    eps = 1e-6
+    for name in x:
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {n: a.copy() for n, a in x.items()}
+            xm = {n: a.copy() for n, a in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+        g = got["d" + name]
+        assert g.shape == fd.shape, name
+        assert np.allclose(g, fd, rtol=1e-6, atol=1e-7), (name, np.abs(g - fd).max())
+
+
 # ---- the parity metric and the key-head map of the variant rules ---------------------------
 
 def test_rel_l2_closed_forms():
