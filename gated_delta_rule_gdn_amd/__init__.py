@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.gdn2_check_cu_seqlens.argtypes = [vp, i32, i32]
         L.gdn2_map_gates.restype = i32
         L.gdn2_map_gates.argtypes = [i32, dp] + [vp] * 13
+        L.gdn2_map_gates_bwd.restype = i32
+        L.gdn2_map_gates_bwd.argtypes = [i32, dp] + [vp] * 17
         L.gdn2_chunk_fwd_noalloc.restype = i32
         L.gdn2_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i32, vp, vp, dp, fp, vp]
         L.gdn2_chunk_bwd_workspace_bytes.restype = sz
@@ -509,6 +511,63 @@ def map_gates(mode: str, q, k, v, log_alpha, beta, beta_v=None):
                               stream)
     _raise_on(st)
     return q2, k2, v2, la2, b, w
+
+
+def map_gates_bwd(mode: str, k, v, beta, grads: dict, beta_v=None) -> dict:
+    """The chain rule back through map_gates, on the GPU (gdn2_map_gates_bwd). k, v, beta and
+    beta_v are map_gates' inputs; grads holds the fp32 gradients of the mapped inputs (the
+    dq, dk, dv, dlog_alpha, db, dw of chunk_bwd run on map_gates' outputs). Returns the
+    gradients with respect to the variant's own inputs: dq, dk, dv, dlog_alpha, dbeta (and
+    dbeta_v for "fg2+"), fp32, in the shapes of map_gates' inputs; those the mapping does not
+    change are the tensors of grads themselves."""
+    if mode not in GATE_MODES:
+        raise ValueError(f"mode must be one of {sorted(GATE_MODES)}")
+    code = GATE_MODES[mode]
+    dev = k.device
+    lead, Hk, dk = tuple(k.shape[:-2]), k.shape[-2], k.shape[-1]
+    Hv, dv = v.shape[-2], v.shape[-1]
+    fg2 = mode in ("fg2", "fg2+")
+    for name, t in (("k", k), ("v", v), ("beta", beta), ("beta_v", beta_v)):
+        if t is not None:
+            _need_gpu(name, t, dev)
+            if t.dtype != k.dtype:
+                raise TypeError(f"{name} has dtype {t.dtype}, expected {k.dtype}")
+    want = {"dq": lead + ((Hv,) if fg2 else (Hk,)) + (dk,), "dk": lead + ((Hv,) if fg2 else (Hk,)) + (dk,),
+            "dv": lead + (Hv, dv), "dw": lead + (Hv, dv), "dlog_alpha": lead + (Hv, dk),
+            "db": lead + (Hv, dk)}
+    for n, shape in want.items():
+        t = grads[n]
+        _need_gpu(n, t, dev)
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"grads[{n!r}] must be contiguous fp32 {list(shape)}")
+    rows = 1
+    for x in lead:
+        rows *= x
+    dims = Dims(rows, 1, 0, Hk, Hv, dk, dv, _dtype_code(k.dtype))
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": grads["dq"], "dk": grads["dk"], "dv": grads["dv"], "dlog_alpha": grads["dlog_alpha"]}
+    dq = dk_ = dv_ = dla = dbv = None
+    if fg2:
+        dk_ = out["dk"] = torch.empty(*lead, Hk, dk, **f32)
+        if Hv > Hk:
+            dq = out["dq"] = torch.empty(*lead, Hk, dk, **f32)
+        else:
+            out["dq"] = grads["dq"].view(*lead, Hk, dk)
+    if mode == "fg2":
+        dv_ = out["dv"] = torch.empty(*lead, Hv, dv, **f32)
+    if mode == "gdn":
+        dla = out["dlog_alpha"] = torch.empty(*lead, Hv, **f32)
+    dbeta = out["dbeta"] = torch.empty(*(lead + ((Hv,) if mode in ("kda", "gdn") else (Hv, dk))), **f32)
+    if mode == "fg2+":
+        dbv = out["dbeta_v"] = torch.empty(*lead, Hv, dv, **f32)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib().gdn2_map_gates_bwd(code, ctypes.byref(dims), _ptr(k), _ptr(v), _ptr(beta),
+                                  _ptr(beta_v), _ptr(grads["dq"]), _ptr(grads["dk"]),
+                                  _ptr(grads["dv"]), _ptr(grads["dlog_alpha"]), _ptr(grads["db"]),
+                                  _ptr(grads["dw"]), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla),
+                                  _ptr(dbeta), _ptr(dbv), stream)
+    _raise_on(st)
+    return out
 
 
 def _fg2_fusion_check(mode, kw):

@@ -403,6 +403,65 @@ gdn2_status gdn2_map_gates(int32_t mode, const gdn2_dims *dims, const void *q, c
     return GDN2_OK;
 }
 
+gdn2_status gdn2_map_gates_bwd(int32_t mode, const gdn2_dims *dims, const void *k,
+                               const void *v, const void *beta, const void *beta_v,
+                               const float *dq_m, const float *dk_m, const float *dv_m,
+                               const float *dla_m, const float *db_m, const float *dw_m,
+                               float *dq, float *dk, float *dv, float *dlog_alpha, float *dbeta,
+                               float *dbeta_v, void *stream) {
+    if (!dims) return fail(GDN2_ERR_NULL_ARG, "dims is NULL");
+    gdn2_status st = check_heads(dims);
+    if (st != GDN2_OK) return st;
+    if (mode != GDN2_GATES_KDA && mode != GDN2_GATES_FG2 && mode != GDN2_GATES_FG2_PLUS &&
+        mode != GDN2_GATES_GDN)
+        return fail(GDN2_ERR_UNSUPPORTED, "mode must be a gdn2_gate_mode");
+    const bool fg2 = mode == GDN2_GATES_FG2 || mode == GDN2_GATES_FG2_PLUS;
+    if (mode == GDN2_GATES_FG2 && dims->d_v != dims->d_k)
+        return fail(GDN2_ERR_BAD_SHAPE, "GDN2_GATES_FG2 scales v by sqrt(beta): d_v must equal d_k");
+    if (dims->batch < 0 || dims->seqlen < 0) return fail(GDN2_ERR_BAD_SHAPE, "batch and seqlen must be >= 0");
+    const int64_t rows = static_cast<int64_t>(dims->batch) * dims->seqlen;
+    const int64_t hd = static_cast<int64_t>(dims->h_v) * (dims->d_k > dims->d_v ? dims->d_k : dims->d_v);
+    if (rows > INT32_MAX || rows * hd > kMaxElems) return fail(GDN2_ERR_BAD_SHAPE, "tensors too large");
+    if (rows == 0) {
+        g_last_error[0] = '\0';
+        return GDN2_OK;
+    }
+    const bool share = dims->h_v > dims->h_k;
+    // what each mode reads and writes
+    const void *ins[10] = {k, v, beta, beta_v, dq_m, dk_m, dv_m, dla_m, db_m, dw_m};
+    const bool need_in[10] = {fg2, mode == GDN2_GATES_FG2, fg2, mode == GDN2_GATES_FG2_PLUS,
+                              fg2 && share, fg2, mode == GDN2_GATES_FG2, mode == GDN2_GATES_GDN,
+                              !fg2, !fg2 || mode == GDN2_GATES_FG2_PLUS};
+    float *outs[6] = {fg2 && share ? dq : nullptr, fg2 ? dk : nullptr,
+                      mode == GDN2_GATES_FG2 ? dv : nullptr, mode == GDN2_GATES_GDN ? dlog_alpha : nullptr,
+                      dbeta, mode == GDN2_GATES_FG2_PLUS ? dbeta_v : nullptr};
+    const bool need_out[6] = {fg2 && share, fg2, mode == GDN2_GATES_FG2, mode == GDN2_GATES_GDN, true,
+                              mode == GDN2_GATES_FG2_PLUS};
+    for (int i = 0; i < 10; ++i)
+        if (need_in[i] && !ins[i]) return fail(GDN2_ERR_NULL_ARG, "an input this mode reads is NULL");
+    for (int i = 0; i < 6; ++i)
+        if (need_out[i] && !outs[i]) return fail(GDN2_ERR_NULL_ARG, "an output this mode writes is NULL");
+    for (int i = 0; i < 6; ++i) {
+        if (!outs[i]) continue;
+        for (int j = 0; j < 10; ++j)
+            if (need_in[j] && static_cast<const void *>(outs[i]) == ins[j])
+                return fail(GDN2_ERR_BAD_SHAPE, "an output aliases an input");
+        for (int j = i + 1; j < 6; ++j)
+            if (outs[i] == outs[j]) return fail(GDN2_ERR_BAD_SHAPE, "two outputs are the same buffer");
+    }
+    gdn2::GateBwdArgs a;
+    a.mode = mode;
+    a.k = k; a.v = v; a.beta = beta; a.beta_v = beta_v;
+    a.dq_m = dq_m; a.dk_m = dk_m; a.dv_m = dv_m; a.dla_m = dla_m; a.db_m = db_m; a.dw_m = dw_m;
+    a.dq = outs[0]; a.dk = outs[1]; a.dv = outs[2]; a.dla = outs[3]; a.dbeta = outs[4]; a.dbeta_v = outs[5];
+    a.rows = rows; a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
+    a.bf16 = dims->dtype == GDN2_BF16;
+    const hipError_t e = gdn2::launch_map_gates_bwd(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail_hip(e, "gdn2_map_gates_bwd launch");
+    g_last_error[0] = '\0';
+    return GDN2_OK;
+}
+
 gdn2_status gdn2_check_cu_seqlens(const int32_t *cu, int32_t num_seqs, int32_t total_tokens) {
     if (!cu) return fail(GDN2_ERR_NULL_ARG, "cu_seqlens is NULL");
     if (num_seqs < 1) return fail(GDN2_ERR_BAD_SHAPE, "num_seqs must be >= 1");

@@ -100,8 +100,21 @@ struct GateArgs {
     bool bf16;
 };
 
+// The chain rule back through a gate mapping (gdn2_map_gates_bwd): the forward's k, v,
+// beta, beta_v (input dtype), the fp32 gradients of the mapped inputs, the fp32 outputs.
+struct GateBwdArgs {
+    int mode;
+    const void *k, *v, *beta, *beta_v;
+    const float *dq_m, *dk_m, *dv_m, *dla_m, *db_m, *dw_m;
+    float *dq, *dk, *dv, *dla, *dbeta, *dbeta_v;
+    int64_t rows;
+    int h_k, h_v, d_k, d_v;
+    bool bf16;
+};
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_map_gates(const GateArgs &a, hipStream_t st);
+hipError_t launch_map_gates_bwd(const GateBwdArgs &a, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkArgs &a, hipStream_t st);
 
 }  // namespace gdn2

@@ -371,6 +371,43 @@ gdn2_status gdn2_map_gates(int32_t mode, const gdn2_dims *dims, const void *q, c
                            void *log_alpha_out, void *b_out, void *w_out, void *stream);
 
 /*
+ * Gradients through gdn2_map_gates: the chain rule of its mapping (the mappings are those
+ * of gdn2_map_gates, after the burn-gdn2 "Architecture" section and the FG2-GDN summary,
+ * section 2). Given the gradients of a loss with respect to the GDN-2 inputs the mapping
+ * wrote (for instance from gdn2_chunk_bwd run on them), it writes the gradients with
+ * respect to the variant's own inputs. Only the gradients the mapping changes are written;
+ * every other gradient of the variant is the mapped one itself:
+ *   GDN2_GATES_KDA       dbeta [rows, h_v] = sum over d_k of db_m + sum over d_v of dw_m;
+ *                        dq, dk, dv, dlog_alpha are dq_m, dk_m, dv_m, dla_m
+ *   GDN2_GATES_GDN       as KDA, and dlog_alpha [rows, h_v] = sum over d_k of dla_m
+ *   GDN2_GATES_FG2       dk [rows, h_k, d_k] = sum over the key head's value heads of
+ *                        sqrt(beta) . dk_m; dv [rows, h_v, d_v] = sqrt(beta) . dv_m;
+ *                        dbeta [rows, h_v, d_k] = (dk_m . k + dv_m . v) / (2 sqrt(beta));
+ *                        dq [rows, h_k, d_k] = sum over the value heads of dq_m when
+ *                        h_v > h_k (when h_v = h_k, dq is dq_m); dlog_alpha is dla_m;
+ *                        db_m and dw_m are not read (b = w = 1 are constants)
+ *   GDN2_GATES_FG2_PLUS  dk and dq as FG2; dbeta = dk_m . k / (2 sqrt(beta));
+ *                        dbeta_v [rows, h_v, d_v] = dw_m / (2 sqrt(beta_v)); dv and
+ *                        dlog_alpha are dv_m and dla_m
+ *
+ *   mode, dims          as for gdn2_map_gates (rows = dims->batch x dims->seqlen)
+ *   k, v, beta, beta_v  the forward's inputs of gdn2_map_gates, device, dims->dtype
+ *   dq_m, dk_m          device fp32 [rows, h', d_k]: dL/dq', dL/dk' of the mapped inputs
+ *                       (h' = h_v in the FG2 modes, whose mapped keys are per value head)
+ *   dv_m, dw_m          device fp32 [rows, h_v, d_v];  dla_m, db_m  device fp32 [rows, h_v, d_k]
+ *   dq .. dbeta_v       device fp32 outputs, in the shapes listed above
+ * Pointers a mode does not read or write are ignored. In the FG2 modes beta (and beta_v)
+ * must be > 0 (the derivative of the square root); a zero gives inf or NaN there. Outputs
+ * must not alias the inputs or each other. One elementwise pass on `stream` (HBM-bound).
+ */
+gdn2_status gdn2_map_gates_bwd(int32_t mode, const gdn2_dims *dims, const void *k,
+                               const void *v, const void *beta, const void *beta_v,
+                               const float *dq_m, const float *dk_m, const float *dv_m,
+                               const float *dla_m, const float *db_m, const float *dw_m,
+                               float *dq, float *dk, float *dv, float *dlog_alpha,
+                               float *dbeta, float *dbeta_v, void *stream);
+
+/*
  * Host helper: checks a HOST copy of cu_seqlens (N+1 entries) against total tokens T.
  * Returns GDN2_OK when cu[0] = 0, cu is non-decreasing and cu[N] = T, else
  * GDN2_ERR_BAD_SHAPE (GDN2_ERR_NULL_ARG for a NULL pointer). Touches no device.

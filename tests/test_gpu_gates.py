@@ -170,3 +170,111 @@ def test_native_variants_at_the_decode_shape(mode):
     eo, es = oracle.rel_l2(np64(o_n), np64(o_m)), oracle.rel_l2(np64(s_n), np64(s_m))
     print(f"[parity] native vs mapped {mode} decode: o={eo:.2e} S={es:.2e}", flush=True)
     assert eo <= tol and es <= tol
+
+
+# ---- training the variants: the chain rule back through the mapping (gdn2_map_gates_bwd) ---
+
+def _pair_args(mode, f, n, h, G):
+    hk = h // G
+    args = (f["q"][n, :, hk], f["k"][n, :, hk], f["v"][n, :, h], f["log_alpha"][n, :, h],
+            f["beta"][n, :, h])
+    return args, (f["beta_v"][n, :, h] if mode == "fg2+" else None)
+
+
+def _assemble(mode, f, per_pair):
+    """Per-pair gradients of the variant's inputs -> tensors in the inputs' shapes; q and k
+    gradients of the value heads of a key head add up."""
+    N, T, Hk, dk = f["k"].shape
+    Hv = f["v"].shape[2]
+    G = Hv // Hk
+    out = {"dq": np.zeros(f["q"].shape), "dk": np.zeros(f["k"].shape),
+           "dv": np.zeros(f["v"].shape), "dlog_alpha": np.zeros(f["log_alpha"].shape),
+           "dbeta": np.zeros(f["beta"].shape)}
+    if mode == "fg2+":
+        out["dbeta_v"] = np.zeros(f["beta_v"].shape)
+    for (n, h), r in per_pair.items():
+        out["dq"][n, :, h // G] += r["dq"]
+        out["dk"][n, :, h // G] += r["dk"]
+        for name in ("dv", "dlog_alpha", "dbeta") + (("dbeta_v",) if mode == "fg2+" else ()):
+            out[name][n, :, h] = r[name]
+    return out
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("mode", MODES)
+def test_map_gates_bwd_against_the_oracle_chain_rule(mode, dtype):
+    """gdn2_map_gates_bwd on random gradients of the mapped inputs against
+    oracle.map_gates_bwd per (sequence, value head) pair (fp32 arithmetic on both sides'
+    inputs: relative L2 <= 1e-5 on every output)."""
+    dk, dv = (128, 128) if mode == "fg2" else (128, 64)
+    x = inputs.variant_inputs(mode, dtype, 2, 33, 2, 4, dk, dv, seed=110 + MODES.index(mode))
+    d = {n: t.cuda() for n, t in x.items()}
+    f = {n: np64(t) for n, t in x.items()}
+    N, T, Hk = 2, 33, 2
+    Hv = 4
+    hq = Hv if mode in ("fg2", "fg2+") else Hk     # the mapped keys are per value head in FG2
+    gen = torch.Generator().manual_seed(7)
+    grads = {"dq": torch.randn(N, T, hq, dk, generator=gen), "dk": torch.randn(N, T, hq, dk, generator=gen),
+             "dv": torch.randn(N, T, Hv, dv, generator=gen), "dw": torch.randn(N, T, Hv, dv, generator=gen),
+             "dlog_alpha": torch.randn(N, T, Hv, dk, generator=gen),
+             "db": torch.randn(N, T, Hv, dk, generator=gen)}
+    print(f"[case] map_gates_bwd {mode} {dtype}", flush=True)
+    got = g.map_gates_bwd(mode, d["k"], d["v"], d["beta"], {n: t.cuda() for n, t in grads.items()},
+                          beta_v=d.get("beta_v"))
+    torch.cuda.synchronize()
+    gf = {n: t.double().numpy() for n, t in grads.items()}
+    per_pair = {}
+    for n in range(N):
+        for h in range(Hv):
+            args, bv = _pair_args(mode, f, n, h, Hv // Hk)
+            hm = h if hq == Hv else h // (Hv // Hk)
+            gm = {"dq": gf["dq"][n, :, hm], "dk": gf["dk"][n, :, hm], "dv": gf["dv"][n, :, h],
+                  "dw": gf["dw"][n, :, h], "dlog_alpha": gf["dlog_alpha"][n, :, h],
+                  "db": gf["db"][n, :, h]}
+            per_pair[(n, h)] = oracle.map_gates_bwd(mode, *args, gm, bv)
+    ref = _assemble(mode, f, per_pair)
+    if hq == Hk:       # dq, dk pass through per key head: not summed over the value heads
+        ref["dq"], ref["dk"] = gf["dq"], gf["dk"]
+    errs = {n: oracle.rel_l2(np64(got[n]).reshape(ref[n].shape), ref[n]) for n in ref}
+    print(f"[parity] map_gates_bwd {mode} {dtype}: " + " ".join(f"{n}={e:.1e}" for n, e in errs.items()),
+          flush=True)
+    assert max(errs.values()) <= 1e-5, errs
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("mode", MODES)
+def test_variant_training_gradients(mode, dtype):
+    """The gradients of a variant's loss with respect to its own inputs, on the GPU:
+    map_gates -> chunk_bwd -> map_gates_bwd, against the oracle's map_gates -> sequence_bwd
+    -> map_gates_bwd per pair (itself pinned against finite differences of the variant's own
+    rule). Relative L2 per gradient tensor at the forward's bars."""
+    dk, dv = (128, 128) if mode == "fg2" else (128, 64)
+    x = inputs.variant_inputs(mode, dtype, 2, 150, 2, 4, dk, dv, seed=120 + MODES.index(mode))
+    d = {n: t.cuda() for n, t in x.items()}
+    f = {n: np64(t) for n, t in x.items()}
+    N, T, Hv = 2, 150, 4
+    gen = torch.Generator().manual_seed(8)
+    dO = torch.randn(N, T, Hv, dv, generator=gen).to(dtype)
+    dST = torch.randn(N, Hv, dk, dv, generator=gen)
+    print(f"[case] variant training gradients {mode} {dtype}", flush=True)
+    m = g.map_gates(mode, d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d.get("beta_v"))
+    gm = g.chunk_bwd(*m, dO.cuda(), S0=d["S"], dS_T=dST.cuda())
+    got = g.map_gates_bwd(mode, d["k"], d["v"], d["beta"], gm, beta_v=d.get("beta_v"))
+    torch.cuda.synchronize()
+    dO64, dST64 = np64(dO), np64(dST)
+    per_pair, dS0 = {}, np.zeros((N, Hv, dk, dv))
+    for n in range(N):
+        for h in range(Hv):
+            args, bv = _pair_args(mode, f, n, h, 2)
+            mm = oracle.map_gates(mode, *args, bv)
+            gp = oracle.sequence_bwd(mm[0], mm[1], mm[2], mm[5], mm[3], mm[4], f["S"][n, h],
+                                     dO64[n, :, h], dST64[n, h])
+            per_pair[(n, h)] = oracle.map_gates_bwd(mode, *args, gp, bv)
+            dS0[n, h] = gp["dS0"]
+    ref = _assemble(mode, f, per_pair)
+    errs = {n: oracle.rel_l2(np64(got[n]).reshape(ref[n].shape), ref[n]) for n in ref}
+    errs["dS0"] = oracle.rel_l2(np64(gm["dS0"]), dS0)
+    print(f"[parity] variant grads {mode} {dtype} {dk}x{dv}: " +
+          " ".join(f"{n}={e:.1e}" for n, e in errs.items()), flush=True)
+    assert all(np.isfinite(list(errs.values())))
+    assert max(errs.values()) <= TOL[dtype], errs
