@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 7
+#define GDN2_ABI_VERSION 8
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
