@@ -66,19 +66,55 @@ def test_chunk_forward_replays_in_a_graph():
         assert torch.equal(o, o_e) and torch.equal(S_T, S_e) and torch.equal(ck, ck_e)
 
 
-def test_chunk_backward_replays_in_a_graph():
+@pytest.mark.parametrize("dtype,chunk", [(torch.bfloat16, 128), (torch.bfloat16, 32),
+                                         (torch.float32, 64)])
+def test_generic_chunk_path_replays_in_a_graph(dtype, chunk):
+    """The generic path (prep kernel, panel segment pass, panel state pass) at chunks of 128
+    and 32 and in fp32 at d = 128, segmented (4 pairs), captured once: every replay equals
+    the eager call bit for bit."""
+    wl = inputs.small_chunk(dtype=dtype, batch=1, seqlen=2048, h_k=2, h_v=4, d_k=128, d_v=128,
+                            neg_eig=True)
+    x = {n: t.cuda() if isinstance(t, torch.Tensor) else t
+         for n, t in inputs.chunk_inputs(wl, seed=52).items()}
+    args = [x[n] for n in NAMES]
+    B, T = 1, 2048
+    nbytes = g.chunk_fwd_workspace_bytes(B, T, 2, 4, 128, 128, dtype, chunk_size=chunk)
+
+    def buffers():
+        return (torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+                torch.empty(B, T, 4, 128, dtype=dtype, device="cuda"),
+                torch.empty(1, 4, 128, 128, dtype=torch.float32, device="cuda"))
+
+    ws_e, o_e, S_e = buffers()
+    g.chunk_fwd(*args, S0=x["S0"], chunk_size=chunk, workspace=ws_e, out=o_e, final_state=S_e)
+    ws, o, S_T = buffers()
+    graph = capture(lambda: g.chunk_fwd(*args, S0=x["S0"], chunk_size=chunk, workspace=ws, out=o,
+                                        final_state=S_T))
+    for rep in range(3):
+        o.fill_(float("nan"))
+        S_T.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] generic path {dtype} chunk {chunk} replay {rep}", flush=True)
+        assert torch.equal(o, o_e) and torch.equal(S_T, S_e)
+
+
+@pytest.mark.parametrize("seqlen", [700, 1000])
+def test_chunk_backward_replays_in_a_graph(seqlen):
     """The bf16 chunked backward (its forward re-run, the reverse pass and the gradient
     kernels), captured once: every replay equals the eager call bit for bit (one value head
-    per key head, so no atomics; a ragged last chunk)."""
-    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=700, h_k=2, h_v=2, d_k=128,
+    per key head, so no atomics; a ragged last chunk). At T = 1000 (16 chunks, two pairs)
+    the forward re-run's state pass and the reverse pass are both segmented."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=seqlen, h_k=2, h_v=2, d_k=128,
                             d_v=128, neg_eig=True, s0_std=0.1)
     x = {n: t.cuda() if isinstance(t, torch.Tensor) else t
          for n, t in inputs.chunk_inputs(wl, seed=53).items()}
     args = [x[n] for n in NAMES]
     gen = torch.Generator().manual_seed(53)
-    dO = torch.randn(1, 700, 2, 128, generator=gen).to(torch.bfloat16).cuda()
+    dO = torch.randn(1, seqlen, 2, 128, generator=gen).to(torch.bfloat16).cuda()
     dST = torch.randn(1, 2, 128, 128, generator=gen).cuda()
-    nbytes = g.chunk_bwd_workspace_bytes(1, 700, 2, 2, 128, 128, torch.bfloat16)
+    nbytes = g.chunk_bwd_workspace_bytes(1, seqlen, 2, 2, 128, 128, torch.bfloat16)
     ref = g.chunk_bwd(*args, dO, S0=x["S0"], dS_T=dST,
                       workspace=torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
