@@ -165,6 +165,17 @@ def test_bwd_segmented_reverse_pass(batch, seqlen, h_k, h_v, dk, dv, label):
              f"T={seqlen} H_k={h_k} H_v={h_v}: {label}", 9)
 
 
+def test_bwd_segmented_without_initial_state_or_final_gradient():
+    """The segmented reverse pass (4 segments) with S0 = 0 and dS_T = 0: the last segment's
+    chain starts from zero in both the segment pass and the pass over every segment."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=1000, h_k=1, h_v=2, d_k=128,
+                            d_v=128, neg_eig=True, s0_std=0.0)
+    x = inputs.chunk_inputs(wl, seed=97)
+    x["S0"] = None
+    run_case(x, "bf16 128x128 T=1000, 4 reverse segments, S0 = 0, dS_T = 0", 12,
+             with_states=False)
+
+
 @pytest.mark.parametrize("dk,dv,h_k,h_v,seqlen", [(128, 128, 1, 2, 200), (128, 64, 1, 2, 150),
                                                   (64, 128, 2, 4, 130)])
 def test_bwd_fp32_every_head_dim_pair(dk, dv, h_k, h_v, seqlen):
