@@ -23,17 +23,18 @@ def setup_module(module):
     g.lib()
 
 
-def run_both(x):
+def run_both(x, chunk_size=64):
     d = to_gpu(x)
     args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
-    o_ref, S_ref = g.chunk_fwd(*args, S0=d["S0"], cu_seqlens=d["cu_seqlens"])
-    o_na, S_na = g.chunk_fwd_noalloc(*args, S0=d["S0"], cu_seqlens=d["cu_seqlens"])
+    o_ref, S_ref = g.chunk_fwd(*args, S0=d["S0"], cu_seqlens=d["cu_seqlens"], chunk_size=chunk_size)
+    o_na, S_na = g.chunk_fwd_noalloc(*args, S0=d["S0"], cu_seqlens=d["cu_seqlens"],
+                                     chunk_size=chunk_size)
     torch.cuda.synchronize()
     return np64(o_ref), np64(S_ref), np64(o_na), np64(S_na)
 
 
-def check(x, dtype, label):
-    o_ref, S_ref, o_na, S_na = run_both(x)
+def check(x, dtype, label, chunk_size=64):
+    o_ref, S_ref, o_na, S_na = run_both(x, chunk_size)
     assert np.array_equal(o_na, o_ref) and np.array_equal(S_na, S_ref), label
     o_r, S_r = oracle_chunk(x)
     B, T = x["q"].shape[:2]
@@ -53,6 +54,18 @@ def test_static_workspace_two_calls_second_smaller():
                             len_lo=1, len_hi=200, s0_std=0.1)
     x2 = inputs.chunk_inputs(wl, seed=99)
     check(x2, torch.float32, "fp32 packed 3 seqs, 2 heads, d=64")
+
+
+def test_static_workspace_generic_path():
+    """The generic path over the static array: 128-token chunks (segmented panel passes),
+    then fp32 at d = 128, each smaller than the call before it."""
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=2000, h_k=2, h_v=4, d_k=128,
+                            d_v=128, neg_eig=True)
+    check(inputs.chunk_inputs(wl, seed=1003), torch.bfloat16, "bf16 chunk 128 B=1 T=2000 H=4",
+          chunk_size=128)
+    wl = inputs.small_chunk(dtype=torch.float32, batch=1, seqlen=700, h_k=1, h_v=2, d_k=128,
+                            d_v=128, neg_eig=True)
+    check(inputs.chunk_inputs(wl, seed=1004), torch.float32, "fp32 d=128 B=1 T=700 H=2")
 
 
 def test_static_workspace_refuses_oversized_calls():
