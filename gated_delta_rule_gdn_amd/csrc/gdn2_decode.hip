@@ -47,9 +47,10 @@ constexpr int kTokBlock = 8;          // tokens staged in LDS at a time
 // next step reads them from the cache.
 constexpr size_t kStreamStateBytes = static_cast<size_t>(256) << 20;
 
-// 16-byte state vectors: 4 fp32 or 8 bf16 columns, widened to fp32 in registers.
-template <typename ST> struct svec;
-template <> struct svec<float> {
+// State vectors: 4 fp32 or 8 bf16 columns (16 bytes), or 4 bf16 columns (8 bytes), widened
+// to fp32 in registers.
+template <typename ST, int N = 16 / static_cast<int>(sizeof(ST))> struct svec;
+template <> struct svec<float, 4> {
     static constexpr int N = 4;
     static __device__ __forceinline__ void ld(const float *p, float *x) {
         const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
@@ -62,7 +63,7 @@ template <> struct svec<float> {
         else *reinterpret_cast<f32x4 *>(p) = v;
     }
 };
-template <> struct svec<bf16_t> {
+template <> struct svec<bf16_t, 8> {
     static constexpr int N = 8;
     static __device__ __forceinline__ void ld(const bf16_t *p, float *x) {
         const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
@@ -79,6 +80,20 @@ template <> struct svec<bf16_t> {
         for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);   // RNE
         if constexpr (NTS) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
         else *reinterpret_cast<u32x4 *>(p) = v;
+    }
+};
+template <> struct svec<bf16_t, 4> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ void ld(const bf16_t *p, float *x) {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+        x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+        x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    }
+    template <bool NTS>
+    static __device__ __forceinline__ void st(bf16_t *p, const float *x) {
+        const u32x2 v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};   // RNE
+        if constexpr (NTS) __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p));
+        else *reinterpret_cast<u32x2 *>(p) = v;
     }
 };
 
@@ -135,7 +150,10 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     const T *__restrict__ gate, const float *__restrict__ nw, float neps,
     const float *__restrict__ cw, float *__restrict__ cst, int csilu, int gmode) {
     constexpr int NT = kDecodeThreads, NW = NT / 64;
-    constexpr int VN = svec<ST>::N;   // columns per lane (one 16-byte vector)
+    // columns per lane: one 16-byte vector; four columns for a bf16 state in multi-token
+    // calls, whose per-token reductions then run over fewer values and lanes
+    constexpr int VN = COLW ? 4 : svec<ST>::N;
+    using SV = svec<ST, VN>;
     using Gm = Geom<DK, DV, VN, COLW>;
     constexpr int CG = Gm::CG, RG = Gm::RG, RPT = Gm::RPT;
     // The row split serves single-token calls only (the launch picks it for T = 1), so its
@@ -285,7 +303,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
-            svec<ST>::ld(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
+            SV::ld(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
         __builtin_amdgcn_sched_barrier(0);
         // one token: taps 0-2 read the conv state, tap 3 the token itself
         auto conv1 = [&](f32x4 wt, const float *old, float x) {
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     } else {
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
-            svec<ST>::ld(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
+            SV::ld(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
     }
 
     for (int t0 = 0; t0 < nt; t0 += TB) {
@@ -484,7 +502,7 @@ __global__ __launch_bounds__(kDecodeThreads) void recurrent_fwd_kernel(
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        svec<ST>::template st<NTS>(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
+        SV::template st<NTS>(Sp + static_cast<size_t>(rg + RG * i) * DV + c0, s[i]);
 
 }
 
