@@ -561,11 +561,7 @@ __global__ __launch_bounds__(64 * (kRSegWaves + kRSegCopy)) void bwd_rseg_kernel
     if (qgrp) {
         char *dst = reinterpret_cast<char *>(p.rseg_Q) +
                     (static_cast<size_t>(pair) * (nsa - 1) + rg - 1) * SegPFrag<DK, true>::BYTES;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                SegPFrag<DK, true>::put(dst, 16 * rt + 4 * lg + ii, col, D[rt][ii]);
+        SegPFrag<DK, true>::put_slice(dst, v, D);
         return;
     }
     float *dst = rg == 0 ? p.rseg_S + static_cast<size_t>(pair) * DK * DV   // entering segment nseg-2

@@ -266,6 +266,43 @@ struct SegPFrag {
             *reinterpret_cast<float *>(base + off) = x;
         }
     }
+    // Stores the 16 columns 16 v .. 16 v + 15 of P that a wave holds in D layout (lane
+    // (li, lg): rows 16 rt + 4 lg + ii of column 16 v + li, in S[rt][ii]). Each group of four
+    // lanes transposes its 4 x 4 blocks with lane shuffles, so that every lane then holds
+    // four consecutive columns of one row: one 8-byte piece per bf16 plane (or one 16-byte
+    // fp32 piece) instead of four 2-byte (4-byte) element stores. Whole wave.
+    __device__ static void put_slice(char *base, int v, const f32x4 (&S)[RT]) {
+        const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+        const int q = li & 3, m = li >> 2;
+        const int lanep = 4 * lg + q + 16 * m;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            // round d: send row (q + d) & 3, receive from lane (q - d) & 3 of the group its
+            // row q, i.e. column 4 m + ((q - d) & 3) of row 4 lg + q
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int si = (q + d) & 3, pi = (q - d) & 3;
+                const float send = si == 0 ? S[rt][0] : si == 1 ? S[rt][1] : si == 2 ? S[rt][2] : S[rt][3];
+                const float recv = __shfl(send, (lane & ~3) | pi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = pi == e ? recv : o[e];
+            }
+            if constexpr (BF) {
+                const size_t off = ((static_cast<size_t>(rt) * NK + (v >> 1)) * 64 + lanep) * 16 + 8 * (v & 1);
+                u32x2 hi, lo;
+                hi.x = pack_bf16x2(o[0], o[1]);
+                hi.y = pack_bf16x2(o[2], o[3]);
+                lo.x = pack_bf16x2(o[0] - bf16_lo(hi.x), o[1] - bf16_hi(hi.x));
+                lo.y = pack_bf16x2(o[2] - bf16_lo(hi.y), o[3] - bf16_hi(hi.y));
+                *reinterpret_cast<u32x2 *>(base + off) = hi;
+                *reinterpret_cast<u32x2 *>(base + PLANE + off) = lo;
+            } else {
+                const size_t off = ((static_cast<size_t>(rt) * NK + v) * 64 + lanep) * 16;
+                *reinterpret_cast<f32x4 *>(base + off) = f32x4{o[0], o[1], o[2], o[3]};
+            }
+        }
+    }
     // Row tiles R0 .. R0 + RT/2 - 1 of P S + R, for the 16 columns of S a wave holds in D
     // layout (lane: rows 16 rt + 4 lg + ii of its column), written over those tiles of S and
     // into the exchange `xch` ([rt][lane]); P staged in LDS at `pl`, R (these tiles) in D

@@ -557,11 +557,7 @@ __global__ __launch_bounds__(64 * (kPSegWaves + kPSegCopy)) void panel_seg_kerne
     if (isP) {
         char *dst = reinterpret_cast<char *>(p.seg_P) +
                     (static_cast<size_t>(pair) * (nsa - 1) + g - 1) * SegPFrag<DK, BF>::BYTES;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                SegPFrag<DK, BF>::put(dst, 16 * rt + 4 * lg + ii, col, S[rt][ii]);
+        SegPFrag<DK, BF>::put_slice(dst, v, S);
         return;
     }
     float *dst = g == 0 ? segS + static_cast<size_t>(DK) * DV   // state entering segment 1
