@@ -341,11 +341,12 @@ def bench_chunk_states(steps, warmup, seed=10):
     return res
 
 
-def bench_chunk_bwd(steps, warmup, seed=11, wl=inputs.CHUNK_BF16_T4096):
+def bench_chunk_bwd(steps, warmup, seed=11, wl=inputs.CHUNK_BF16_T4096, from_states=False):
     """The chunked backward (gdn2_chunk_bwd) on a chunk workload (the timed one by default):
     the forward re-run that stores the chunk states, the reverse state pass and the per-chunk
     gradients. Algorithmic bytes: the forward inputs, dO, S0 and dS_T read once, the fp32
-    gradients written once."""
+    gradients written once. from_states: gdn2_chunk_bwd_states, given the chunk states a
+    forward wrote (written once, untimed; their reading is counted)."""
     x = inputs.chunk_inputs_device(wl, seed)
     B, T = x["q"].shape[:2]
     gen = torch.Generator(device="cuda")
@@ -354,10 +355,16 @@ def bench_chunk_bwd(steps, warmup, seed=11, wl=inputs.CHUNK_BF16_T4096):
     dST = torch.randn_like(x["S0"])
     ws = torch.empty(g.chunk_bwd_workspace_bytes(B, T, wl.h_k, wl.h_v, wl.d_k, wl.d_v, wl.dtype),
                      dtype=torch.uint8, device="cuda")
+    ck = None
+    if from_states:
+        ck = torch.empty(g.num_chunks(T, B), wl.h_v, wl.d_k, wl.d_v, dtype=torch.float32,
+                         device="cuda")
+        g.chunk_fwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], S0=x["S0"],
+                    chunk_states=ck)
 
     def call():
         g.chunk_bwd(x["q"], x["k"], x["v"], x["log_alpha"], x["b"], x["w"], dO, S0=x["S0"],
-                    dS_T=dST, workspace=ws)
+                    dS_T=dST, workspace=ws, chunk_states=ck)
 
     for _ in range(warmup):
         call()
@@ -366,11 +373,12 @@ def bench_chunk_bwd(steps, warmup, seed=11, wl=inputs.CHUNK_BF16_T4096):
     tok_in = T * (2 * wl.h_k * wl.d_k + wl.h_v * (2 * wl.d_k + 3 * wl.d_v)) * e   # q k, la b, v w dO
     grads = T * (2 * wl.h_k * wl.d_k + wl.h_v * (2 * wl.d_k + 2 * wl.d_v)) * 4
     states = 3 * x["S0"].numel() * 4                                          # S0, dS_T, dS0
-    nbytes = tok_in + grads + states
-    del x, ws, dO, dST
+    nbytes = tok_in + grads + states + (ck.numel() * 4 if from_states else 0)
+    del x, ws, dO, dST, ck
     bsrc = source_hash(*BWD_SRC)
-    timed = wl is inputs.CHUNK_BF16_T4096
-    return {"workload": f"{wl.name}_bwd", "us_per_call": t * 1e6, "tokens_per_s": T * B / t,
+    timed = wl is inputs.CHUNK_BF16_T4096 and not from_states
+    return {"workload": f"{wl.name}_bwd" + ("_from_states" if from_states else ""),
+            "us_per_call": t * 1e6, "tokens_per_s": T * B / t,
             "alg_bytes": nbytes, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
             "traffic": measured_traffic("chunk_bwd_t4096", bsrc) if timed else None}
 
@@ -755,6 +763,7 @@ def main():
         return
     if args.only == "bwd":
         print(json.dumps(bench_chunk_bwd(max(5, args.steps // 10), 2)))
+        print(json.dumps(bench_chunk_bwd(max(5, args.steps // 10), 2, from_states=True)))
         return
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -824,6 +833,7 @@ def main():
                                     name="chunk_f32_b1_t4096_h16_d128_negeig")
     if args.only == "all" and not args.no_other_workloads:
         out["chunk_bwd_f32"] = bench_chunk_bwd(5, 2, wl=t4096_f32)
+        out["chunk_bwd_from_states"] = bench_chunk_bwd(max(5, args.steps // 10), 2, from_states=True)
     if args.only in ("chunk", "all") and not args.no_other_workloads:
         out["other_chunk_workloads"] = [
             bench_chunk_workload(wl, max(10, args.steps // 4), 3, seed, chunk)

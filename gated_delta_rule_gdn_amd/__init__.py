@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.gdn2_chunk_bwd_workspace_bytes.argtypes = [dp, i32]
         L.gdn2_chunk_bwd.restype = i32
         L.gdn2_chunk_bwd.argtypes = [vp] * 8 + [i32] + [vp] * 9 + [dp, vp, sz, vp]
+        L.gdn2_chunk_bwd_states.restype = i32
+        L.gdn2_chunk_bwd_states.argtypes = [vp] * 8 + [i32] + [vp] * 10 + [dp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -291,10 +293,13 @@ def chunk_bwd_workspace_bytes(batch: int, seqlen: int, h_k: int, h_v: int, d_k: 
 
 
 def chunk_bwd(q, k, v, log_alpha, b, w, dO, S0=None, cu_seqlens=None, dS_T=None,
-              chunk_size: int = CHUNK_SIZE, workspace: Optional[torch.Tensor] = None) -> dict:
+              chunk_size: int = CHUNK_SIZE, workspace: Optional[torch.Tensor] = None,
+              chunk_states: Optional[torch.Tensor] = None) -> dict:
     """Gradients of chunk_fwd (GDN-2 gates, no fusion options) given dO = dL/do and
     dS_T = dL/dS_T (None: zero). Returns fp32 tensors: dq, dk [B,T,H_k,d_k]; dv, dw
-    [B,T,H_v,d_v]; dlog_alpha, db [B,T,H_v,d_k]; dS0 [N,H_v,d_k,d_v]."""
+    [B,T,H_v,d_v]; dlog_alpha, db [B,T,H_v,d_k]; dS0 [N,H_v,d_k,d_v]. chunk_states: the
+    chunk_states a chunk_size-64 chunk_fwd of the same inputs wrote (gdn2_chunk_bwd_states:
+    the serial pass over the chunks is not re-run)."""
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("b", b), ("w", w),
                     ("dO", dO)):
@@ -331,11 +336,22 @@ def chunk_bwd(q, k, v, log_alpha, b, w, dO, S0=None, cu_seqlens=None, dS_T=None,
            "dlog_alpha": torch.empty(B, T, Hv, dk_, **f32), "db": torch.empty(B, T, Hv, dk_, **f32),
            "dS0": torch.empty(N, Hv, dk_, dv_, **f32)}
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib().gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
-                              _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(dO), _ptr(dS_T),
-                              *(_ptr(out[n]) for n in ("dq", "dk", "dv", "dw", "dlog_alpha", "db",
-                                                       "dS0")),
-                              ctypes.byref(dims), _ptr(workspace), workspace.numel(), stream)
+    grads = [_ptr(out[n]) for n in ("dq", "dk", "dv", "dw", "dlog_alpha", "db", "dS0")]
+    if chunk_states is None:
+        st = lib().gdn2_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b), _ptr(w),
+                                  _ptr(S0), _ptr(cu_seqlens), chunk_size, _ptr(dO), _ptr(dS_T),
+                                  *grads, ctypes.byref(dims), _ptr(workspace), workspace.numel(),
+                                  stream)
+    else:
+        _need_gpu("chunk_states", chunk_states, dev)
+        nc = num_chunks(T if cu_seqlens is None else cu_seqlens, B, chunk_size)
+        if chunk_states.dtype != torch.float32 or chunk_states.shape != (nc, Hv, dk_, dv_):
+            raise ValueError(f"chunk_states must be fp32 [{nc},{Hv},{dk_},{dv_}]")
+        st = lib().gdn2_chunk_bwd_states(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(b),
+                                         _ptr(w), _ptr(S0), _ptr(cu_seqlens), chunk_size,
+                                         _ptr(chunk_states), _ptr(dO), _ptr(dS_T), *grads,
+                                         ctypes.byref(dims), _ptr(workspace), workspace.numel(),
+                                         stream)
     _raise_on(st)
     return out
 

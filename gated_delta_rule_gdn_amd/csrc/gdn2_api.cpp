@@ -227,25 +227,29 @@ size_t gdn2_chunk_bwd_workspace_bytes(const gdn2_dims *dims, int32_t chunk_size)
     return dense > pk ? dense : pk;
 }
 
-gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
-                           const void *b, const void *w, const float *S0,
-                           const int32_t *cu_seqlens, int32_t chunk_size, const void *dO,
-                           const float *dS_T, float *dq, float *dk, float *dv, float *dw,
-                           float *dlog_alpha, float *db, float *dS0, const gdn2_dims *dims,
-                           void *workspace, size_t workspace_bytes, void *stream) {
+static gdn2_status chunk_bwd_common(const void *q, const void *k, const void *v,
+                                    const void *log_alpha, const void *b, const void *w,
+                                    const float *S0, const int32_t *cu_seqlens, int32_t chunk_size,
+                                    const float *chunk_states, bool given, const void *dO,
+                                    const float *dS_T, float *dq, float *dk, float *dv, float *dw,
+                                    float *dlog_alpha, float *db, float *dS0, const gdn2_dims *dims,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
     const bool packed = cu_seqlens != nullptr;
     gdn2_status st = check_chunk_dims(dims, chunk_size, packed);
     if (st != GDN2_OK) return st;
     st = check_bwd_built(dims, chunk_size);
     if (st != GDN2_OK) return st;
+    if (given && chunk_size != gdn2::kChunk)
+        return fail(GDN2_ERR_UNSUPPORTED, "chunk_states are those of a chunk_size 64 forward");
     const int64_t tokens = static_cast<int64_t>(dims->batch) * dims->seqlen;
     const int N = packed ? dims->num_seqs : dims->batch;
     if (tokens > 0 && (!q || !k || !v || !log_alpha || !b || !w || !dO || !dq || !dk || !dv ||
                        !dw || !dlog_alpha || !db))
         return fail(GDN2_ERR_NULL_ARG, "the inputs, dO and every token gradient are required");
     if (N > 0 && !dS0) return fail(GDN2_ERR_NULL_ARG, "dS0 is required");
+    if (given && tokens > 0 && !chunk_states) return fail(GDN2_ERR_NULL_ARG, "chunk_states is NULL");
     const void *outs[] = {dq, dk, dv, dw, dlog_alpha, db, dS0};
-    const void *ins[] = {q, k, v, log_alpha, b, w, S0, cu_seqlens, dO, dS_T, workspace};
+    const void *ins[] = {q, k, v, log_alpha, b, w, S0, cu_seqlens, dO, dS_T, workspace, chunk_states};
     for (const void *x : outs) {
         if (!x) continue;
         for (const void *y : ins)
@@ -270,10 +274,34 @@ gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const vo
     a.batch = dims->batch; a.seqlen = dims->seqlen; a.num_seqs = packed ? dims->num_seqs : 0;
     a.h_k = dims->h_k; a.h_v = dims->h_v; a.d_k = dims->d_k; a.d_v = dims->d_v;
     a.bf16 = bf;
+    a.ck_in = given && bf ? chunk_states : nullptr;   // fp32 inputs recompute them
     const hipError_t e = gdn2::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail_hip(e, "gdn2_chunk_bwd launch");
     g_last_error[0] = '\0';
     return GDN2_OK;
+}
+
+gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v, const void *log_alpha,
+                           const void *b, const void *w, const float *S0,
+                           const int32_t *cu_seqlens, int32_t chunk_size, const void *dO,
+                           const float *dS_T, float *dq, float *dk, float *dv, float *dw,
+                           float *dlog_alpha, float *db, float *dS0, const gdn2_dims *dims,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+    return chunk_bwd_common(q, k, v, log_alpha, b, w, S0, cu_seqlens, chunk_size, nullptr, false,
+                            dO, dS_T, dq, dk, dv, dw, dlog_alpha, db, dS0, dims, workspace,
+                            workspace_bytes, stream);
+}
+
+gdn2_status gdn2_chunk_bwd_states(const void *q, const void *k, const void *v,
+                                  const void *log_alpha, const void *b, const void *w,
+                                  const float *S0, const int32_t *cu_seqlens, int32_t chunk_size,
+                                  const float *chunk_states, const void *dO, const float *dS_T,
+                                  float *dq, float *dk, float *dv, float *dw, float *dlog_alpha,
+                                  float *db, float *dS0, const gdn2_dims *dims, void *workspace,
+                                  size_t workspace_bytes, void *stream) {
+    return chunk_bwd_common(q, k, v, log_alpha, b, w, S0, cu_seqlens, chunk_size, chunk_states,
+                            true, dO, dS_T, dq, dk, dv, dw, dlog_alpha, db, dS0, dims, workspace,
+                            workspace_bytes, stream);
 }
 
 static gdn2_status recurrent_common(const void *q, const void *k, const void *v,

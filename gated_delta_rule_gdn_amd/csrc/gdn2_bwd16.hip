@@ -1217,6 +1217,7 @@ hipError_t launch_bwd16_t(const BwdArgs &a, hipStream_t st) {
     f.fu.bops = base + ws.crec;
     f.fu.bdo = a.dO;
     f.fu.tmat = base + ws.tm;
+    f.fu.ck_in = a.ck_in;
     hipError_t e = launch_chunk_fwd(f, st);
     if (e != hipSuccess) return e;
 

@@ -68,6 +68,8 @@ struct ChunkParams {
     void *o;
     float *S_T;
     float *S_ck;         // state entering every chunk [chunk][h_v][DK][DV], or NULL
+    const float *S_in;   // with bops: the state entering every chunk, given (the layout of
+                         // S_ck); the chain then only forms U, and nothing is carried
     void *S_ck16;        // the same states as bf16 B fragments, [chunk][h_v][DV/16][DK/32][64]
                          // x 16 B (64-token path, bf16 records only), or NULL
     void *U_ck16;        // U = U~ + Wn S of every chunk as bf16 B fragments, [chunk][h_v]

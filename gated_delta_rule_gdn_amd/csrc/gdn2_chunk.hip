@@ -191,7 +191,7 @@ template <int NW> struct StateWaves {
     static constexpr int ALL = 2 * NW + COPY;
 };
 
-template <typename T, bool BF, int DK, int DV, int NW>
+template <typename T, bool BF, int DK, int DV, int NW, bool GIVEN>
 __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(ChunkParams p) {
     using R_ = Rec<kChunk, DK, DV, BF>;
     using SL = StageLayout<DK, DV, BF>;
@@ -283,11 +283,23 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
                            static_cast<int>(NW * SL::UTS / 1024) / NCOPY;   // see issue()
     char *pslot = smem + CL::PSLOT;
     f32x4 *xch = reinterpret_cast<f32x4 *>(pslot + PF::BYTES) + sl * RT * 64;
-    const bool carry = seg >= 2;
+    // Given states (GIVEN: p.S_in, the backward's forward re-run): every chunk starts from its
+    // own state, so nothing is carried and the chain waves only form U.
+    constexpr bool given = GIVEN;
+    const bool carry = seg >= 2 && !given;
     const bool holds = wave < 2 * NW;                     // chain and output waves
     f32x4 S[RT];
     const size_t sbase = static_cast<size_t>(pair) * DK * DV;
-    if (carry ? holds : chain) {
+    auto given_state = [&](int c, f32x4 (&X)[RT]) {       // this wave's columns of S_in[chunk c]
+        const float *g = p.S_in + (static_cast<size_t>(cbase + c) * p.h_v + h) * (DK * DV) + col;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) X[rt][ii] = g[static_cast<size_t>(16 * rt + 4 * lg + ii) * DV];
+    };
+    if (given) {
+        if (chain && ce > cb) given_state(cb, S);
+    } else if (carry ? holds : chain) {
         const float *Sin = p.nseg == 1 ? p.S0 : p.seg_S + (sbase << 1) + (seg > 0 ? DK * DV : 0);
         const size_t ibase = p.nseg == 1 ? sbase : 0;
 #pragma unroll
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
     };
     if (carry && !holds) stage_P(1);      // ahead of the first chunk, which is needed later
     if (CL::EARLY && !holds && ce > cb) issue(cb, smem);
-    for (int g = 1; g < seg; ++g) {
+    for (int g = 1; carry && g < seg; ++g) {
         f32x4 R[H];                         // this wave's half of R_g
         if (holds) {
             const float *Rg = p.seg_R + (static_cast<size_t>(pair) * (p.nseg - 2) + g - 1) * DK * DV;
@@ -410,6 +422,9 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
                 if (ck16) ck16[kt * 64 + lane] = SB[kt];
             }
             if (lane == 0) *flagS = c + 1;
+            // given states: S is dead once packed; the next chunk's state is loaded into it
+            // now and lands during this chunk's step
+            if (given && c + 1 < ce) given_state(c + 1, S);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kt = 0; kt < NKD; ++kt)
@@ -421,12 +436,14 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
             __builtin_amdgcn_sched_barrier(0);
             // KgT operands and the decay of S, while the last U products drain
             u32x4 ak[RT][NKC];
+            if (!given) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+                for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
+                    for (int kt = 0; kt < NKC; ++kt) ak[rt][kt] = kg[(rt * NKC + kt) * 64 + lane];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
+                for (int rt = 0; rt < RT; ++rt) S[rt] *= *reinterpret_cast<const f32x4 *>(gc + 16 * rt + 4 * lg);
+            }
             // publish U as B operands, then its counter (and, with U_ck16, to memory)
             u32x4 UB[NKC];
             u32x4 *cku = nullptr;
@@ -445,13 +462,15 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
             }
             if (lane == 0) *flagU = c + 1;
             // S = gamma_C S + KgT U
+            if (!given) {
 #pragma unroll
-            for (int kt = 0; kt < NKC; ++kt)
+                for (int kt = 0; kt < NKC; ++kt)
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    if constexpr (BF) S[rt] = mma_k32(ak[rt][kt], UB[kt], S[rt]);
-                    else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, ak[rt][kt]), U[kt], S[rt]);
-                }
+                    for (int rt = 0; rt < RT; ++rt) {
+                        if constexpr (BF) S[rt] = mma_k32(ak[rt][kt], UB[kt], S[rt]);
+                        else S[rt] = mma_k16_f32(__builtin_bit_cast(f32x4, ak[rt][kt]), U[kt], S[rt]);
+                    }
+            }
             wait_lds();                     // this chunk's LDS reads and writes are done
         }
         if (p.S_T && seg == p.nseg - 1) {
@@ -891,11 +910,11 @@ size_t chunk_workspace_bytes(int chunk, int batch, int seqlen, int num_seqs, int
 bool chunk_size_built(int chunk) { return chunk == 32 || chunk == 64 || chunk == 128; }
 
 
-template <typename T, bool BF, int DK, int DV, int NW>
+template <typename T, bool BF, int DK, int DV, int NW, bool GIVEN = false>
 static hipError_t launch_state(ChunkParams p, int64_t units, hipStream_t st) {
     p.nslices = DV / 16 / NW;
     const size_t lds = CarryLayout<DK, DV, BF, NW>::LDS;
-    auto kern = chunk_state_kernel<T, BF, DK, DV, NW>;
+    auto kern = chunk_state_kernel<T, BF, DK, DV, NW, GIVEN>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
@@ -918,6 +937,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     p.U_ck16 = a.fu.cku16;
     p.bops = BF && a.o == nullptr ? a.fu.bops : nullptr;
     p.dO = a.fu.bdo;
+    p.S_in = p.bops ? a.fu.ck_in : nullptr;
+    if (a.fu.ck_in && !p.S_in) return hipErrorInvalidValue;   // given states: backward only
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
     p.rec = a.workspace + mapb;
@@ -949,8 +970,8 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     const int64_t units = static_cast<int64_t>(p.num_pairs) * p.nseg;
-    if (p.nseg > 1 && p.num_pairs > 0) {
-        // segment pass
+    if (p.nseg > 1 && p.num_pairs > 0 && !p.S_in) {
+        // segment pass (not needed when the state entering every chunk is given)
         using SGy = SegLayout<DK, DV, BF>;
         auto skern = chunk_seg_kernel<T, BF, DK, DV>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(skern),
@@ -966,7 +987,11 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     hipError_t e;
     if constexpr (BF) {
         const int nw = state_slices(DV, BF, p.num_pairs);
-        if (nw == 4) e = launch_state<T, BF, DK, DV, 4>(p, units, st);
+        if (p.S_in) {
+            if (nw == 4) e = launch_state<T, BF, DK, DV, 4, true>(p, units, st);
+            else if (nw == 2) e = launch_state<T, BF, DK, DV, 2, true>(p, units, st);
+            else e = launch_state<T, BF, DK, DV, 1, true>(p, units, st);
+        } else if (nw == 4) e = launch_state<T, BF, DK, DV, 4>(p, units, st);
         else if (nw == 2) e = launch_state<T, BF, DK, DV, 2>(p, units, st);
         else e = launch_state<T, BF, DK, DV, 1>(p, units, st);
     } else {
@@ -997,7 +1022,7 @@ static hipError_t launch_chunk_dt(const ChunkArgs &a, hipStream_t st) {
 // Generic path: any built chunk size, both dtypes, all head dims; the state pass walks each
 // chunk in row panels and runs every (sequence, head) from its start (no segments).
 static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
-    if (a.fu.cks16 || a.fu.cku16 || a.fu.bops) return hipErrorInvalidValue;   // 64-token pass only
+    if (a.fu.cks16 || a.fu.cku16 || a.fu.bops || a.fu.ck_in) return hipErrorInvalidValue;   // 64-token pass only
     const bool packed = a.cu_seqlens != nullptr;
     const int N = packed ? a.num_seqs : a.batch;
     const int C = a.chunk;

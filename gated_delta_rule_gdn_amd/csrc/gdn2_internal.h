@@ -31,6 +31,8 @@ struct Fusion {
     char *bops = nullptr;            // with o == NULL: the backward's reverse-pass operands
     const void *bdo = nullptr;       // dO for bops
     void *tmat = nullptr;            // chunked forward, bf16: T = (I + A)^-1 per record, or NULL
+    const float *ck_in = nullptr;    // with bops (64-token path): the state entering every chunk,
+                                     // given (fp32, the layout of cks): no chain, no segment pass
 };
 
 struct DecodeArgs {
@@ -79,6 +81,8 @@ struct BwdArgs {
     char *workspace;
     int batch, seqlen, num_seqs, h_k, h_v, d_k, d_v;
     bool bf16;
+    const float *ck_in = nullptr;    // the state entering every 64-token chunk, from the forward
+                                     // (bf16 inputs: used instead of the re-run's chain), or NULL
 };
 size_t chunk_bwd_workspace_bytes(int batch, int seqlen, int num_seqs, int h_v, int d_k, int d_v,
                                  bool bf16, bool packed);

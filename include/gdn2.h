@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 8
+#define GDN2_ABI_VERSION 9
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -273,6 +273,27 @@ gdn2_status gdn2_chunk_bwd(const void *q, const void *k, const void *v,
                            float *dw, float *dlog_alpha, float *db, float *dS0,
                            const gdn2_dims *dims, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * gdn2_chunk_bwd for a forward that saved the state entering every chunk (its
+ * gdn2_fusion.chunk_states, taken with chunk_size 64 on the same inputs, S0 and layout):
+ * the chunked form hands exactly that state from one chunk to the next (burn-gdn2 docs page,
+ * "Architecture", Chunk WY training path), so the backward uses it instead of re-running
+ * the serial pass over the chunks. Gradients equal gdn2_chunk_bwd's (the same bits when no
+ * value heads share a key head). chunk_size must be 64 (GDN2_ERR_UNSUPPORTED otherwise);
+ * with fp32 inputs the states are recomputed and chunk_states is only checked.
+ *
+ *   chunk_states  device fp32 [num_chunks][h_v][d_k][d_v], the layout of
+ *                 gdn2_fusion.chunk_states; read only; must not alias an output
+ *   other arguments, the workspace size and the error behaviour as for gdn2_chunk_bwd
+ */
+gdn2_status gdn2_chunk_bwd_states(const void *q, const void *k, const void *v,
+                                  const void *log_alpha, const void *b, const void *w,
+                                  const float *S0, const int32_t *cu_seqlens, int32_t chunk_size,
+                                  const float *chunk_states, const void *dO, const float *dS_T,
+                                  float *dq, float *dk, float *dv, float *dw, float *dlog_alpha,
+                                  float *db, float *dS0, const gdn2_dims *dims, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * One decode step for N sequences, one token each (burn-gdn2 "FusedRecurrent" mode; the

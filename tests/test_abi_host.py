@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.gdn2_abi_version() == 8
+    assert L.gdn2_abi_version() == 9
     assert L.gdn2_status_string(0) == b"ok"
     assert b"workspace" in L.gdn2_status_string(4)
     assert L.gdn2_status_string(99) == b"unknown status"
@@ -332,6 +332,15 @@ def test_chunk_bwd_validation(L):
     assert call(outs=[P[10], P[10]] + P[12:17]) == 2                   # dq and dk alias
     assert call(ws_bytes=need - 1) == 4
     assert call(ws=ctypes.c_void_p(0x10001)) == 4                      # misaligned workspace
+
+    # the entry point that takes the forward's chunk states
+    def call_states(ck=P[18], chunk=64, outs=None):
+        o = P[10:17] if outs is None else outs
+        return L.gdn2_chunk_bwd_states(P[0], P[1], P[2], P[3], P[4], P[5], None, None, chunk, ck,
+                                       P[8], None, *o, ctypes.byref(d), P[19], need, None)
+    assert call_states(ck=None) == 1                                   # chunk_states required
+    assert call_states(chunk=128) == 3                                 # states of a chunk-64 forward
+    assert call_states(outs=[P[18]] + P[11:17]) == 2                   # dq aliases chunk_states
 
 
 def test_chunk_fwd_noalloc_rejects_without_touching_a_device(L):

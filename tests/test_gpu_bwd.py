@@ -199,3 +199,67 @@ def test_bwd_chunk_size_does_not_change_the_gradients(dtype):
         got = run_case(x, f"{dtype} 128x128 T=300, chunk_size {cs}", 11, chunk_size=cs)
         for n in ref:
             assert torch.equal(got[n], ref[n]), (cs, n)
+
+
+@pytest.mark.parametrize("label,kw", [
+    ("bf16 128x128 B=1 T=4096 H=16 (the timed shape, 4 segments)", dict(wl="t4096")),
+    ("bf16 64x64 B=3 T=700", dict(dtype=torch.bfloat16, batch=3, seqlen=700, h_k=2, h_v=2, d_k=64, d_v=64)),
+    ("bf16 128x64 packed with an empty sequence, G=2", dict(packed=True)),
+    ("fp32 64x64 B=2 T=150 G=2 (states recomputed)", dict(dtype=torch.float32, batch=2, seqlen=150, h_k=2, h_v=4, d_k=64, d_v=64)),
+])
+def test_bwd_from_forward_states(label, kw):
+    """gdn2_chunk_bwd_states with the chunk states a chunk-64 forward of the same inputs
+    wrote: the same gradients as gdn2_chunk_bwd (the same bits without grouped heads, within
+    the bars with them), and within the bars of the oracle's token adjoint."""
+    kw = dict(kw)
+    if kw.pop("wl", None) == "t4096":
+        x = inputs.chunk_inputs(inputs.CHUNK_BF16_T4096, seed=71)
+    elif kw.pop("packed", False):
+        wl = inputs.small_chunk(dtype=torch.bfloat16, h_k=2, h_v=4, d_k=128, d_v=64, num_seqs=4,
+                                len_lo=2, len_hi=200)
+        x = inputs.chunk_inputs(wl, seed=72)
+        cu = x["cu_seqlens"].clone()
+        lens = (cu[1:] - cu[:-1]).tolist()
+        lens[2] = 0
+        cu[1:] = torch.cumsum(torch.tensor(lens), 0).to(torch.int32)
+        T = int(cu[-1])
+        for n in ("q", "k", "v", "log_alpha", "b", "w"):
+            x[n] = x[n][:, :T].contiguous()
+        x["cu_seqlens"] = cu
+    else:
+        x = inputs.chunk_inputs(inputs.small_chunk(neg_eig=True, **kw), seed=73)
+    d = to_gpu(x)
+    dtype = x["q"].dtype
+    B, T = x["q"].shape[:2]
+    Hv, dv, dk = x["v"].shape[2], x["v"].shape[3], x["k"].shape[3]
+    N = B if x["cu_seqlens"] is None else x["cu_seqlens"].numel() - 1
+    gen = torch.Generator().manual_seed(74)
+    dO = torch.randn(B, T, Hv, dv, generator=gen).to(dtype).cuda()
+    dST = torch.randn(N, Hv, dk, dv, generator=gen).cuda()
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"])
+    nc = g.num_chunks(T if d["cu_seqlens"] is None else x["cu_seqlens"], B)
+    ck = torch.empty(nc, Hv, dk, dv, dtype=torch.float32, device="cuda")
+    print(f"[case] chunk_bwd_states {label}", flush=True)
+    g.chunk_fwd(*args, S0=d["S0"], cu_seqlens=d["cu_seqlens"], chunk_states=ck)
+    ref = g.chunk_bwd(*args, dO, S0=d["S0"], cu_seqlens=d["cu_seqlens"], dS_T=dST)
+    got = g.chunk_bwd(*args, dO, S0=d["S0"], cu_seqlens=d["cu_seqlens"], dS_T=dST, chunk_states=ck)
+    torch.cuda.synchronize()
+    grouped = x["q"].shape[2] != Hv
+    for n in ref:
+        if grouped:
+            e = oracle.rel_l2(np64(got[n]), np64(ref[n]))
+            assert e <= 1e-5, (n, e)
+        else:
+            assert torch.equal(got[n], ref[n]), n
+    if T <= 1000:
+        f, cu, S0 = flat_inputs(x)
+        o_ref = oracle.recurrent_bwd(f["q"], f["k"], f["v"], f["log_alpha"], f["b"], f["w"],
+                                     np64(dO).reshape(B * T, Hv, dv), S0=S0, dS_T=np64(dST),
+                                     cu_seqlens=cu, threads=ORACLE_THREADS)
+        errs = {n: oracle.rel_l2(np64(got[n]).reshape(o_ref[n].shape), o_ref[n]) for n in GRADS}
+        errs["dS0"] = oracle.rel_l2(np64(got["dS0"]), o_ref["dS0"])
+        print(f"[parity] chunk_bwd_states {label}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()),
+              flush=True)
+        assert max(errs.values()) <= TOL[dtype], errs
+    else:
+        print(f"[parity] chunk_bwd_states {label}: equal to gdn2_chunk_bwd", flush=True)
