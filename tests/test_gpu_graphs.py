@@ -100,12 +100,13 @@ def test_generic_chunk_path_replays_in_a_graph(dtype, chunk):
         assert torch.equal(o, o_e) and torch.equal(S_T, S_e)
 
 
-@pytest.mark.parametrize("seqlen", [700, 1000])
-def test_chunk_backward_replays_in_a_graph(seqlen):
+@pytest.mark.parametrize("seqlen,from_states", [(700, False), (1000, False), (1000, True)])
+def test_chunk_backward_replays_in_a_graph(seqlen, from_states):
     """The bf16 chunked backward (its forward re-run, the reverse pass and the gradient
     kernels), captured once: every replay equals the eager call bit for bit (one value head
     per key head, so no atomics; a ragged last chunk). At T = 1000 (16 chunks, two pairs)
-    the forward re-run's state pass and the reverse pass are both segmented."""
+    the forward re-run's state pass and the reverse pass are both segmented; from_states
+    runs gdn2_chunk_bwd_states on the chunk states of an eager forward."""
     wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=seqlen, h_k=2, h_v=2, d_k=128,
                             d_v=128, neg_eig=True, s0_std=0.1)
     x = {n: t.cuda() if isinstance(t, torch.Tensor) else t
@@ -115,13 +116,17 @@ def test_chunk_backward_replays_in_a_graph(seqlen):
     dO = torch.randn(1, seqlen, 2, 128, generator=gen).to(torch.bfloat16).cuda()
     dST = torch.randn(1, 2, 128, 128, generator=gen).cuda()
     nbytes = g.chunk_bwd_workspace_bytes(1, seqlen, 2, 2, 128, 128, torch.bfloat16)
-    ref = g.chunk_bwd(*args, dO, S0=x["S0"], dS_T=dST,
+    ck = None
+    if from_states:
+        ck = torch.empty(g.num_chunks(seqlen, 1), 2, 128, 128, dtype=torch.float32, device="cuda")
+        g.chunk_fwd(*args, S0=x["S0"], chunk_states=ck)
+    ref = g.chunk_bwd(*args, dO, S0=x["S0"], dS_T=dST, chunk_states=ck,
                       workspace=torch.empty(nbytes, dtype=torch.uint8, device="cuda"))
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     box = {}
 
     def call():
-        box["out"] = g.chunk_bwd(*args, dO, S0=x["S0"], dS_T=dST, workspace=ws)
+        box["out"] = g.chunk_bwd(*args, dO, S0=x["S0"], dS_T=dST, workspace=ws, chunk_states=ck)
 
     graph = capture(call)
     out = box["out"]
