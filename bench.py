@@ -376,11 +376,12 @@ def bench_chunk_bwd(steps, warmup, seed=11, wl=inputs.CHUNK_BF16_T4096, from_sta
     nbytes = tok_in + grads + states + (ck.numel() * 4 if from_states else 0)
     del x, ws, dO, dST, ck
     bsrc = source_hash(*BWD_SRC)
-    timed = wl is inputs.CHUNK_BF16_T4096 and not from_states
+    timed = wl is inputs.CHUNK_BF16_T4096
     return {"workload": f"{wl.name}_bwd" + ("_from_states" if from_states else ""),
             "us_per_call": t * 1e6, "tokens_per_s": T * B / t,
             "alg_bytes": nbytes, "hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBPS,
-            "traffic": measured_traffic("chunk_bwd_t4096", bsrc) if timed else None}
+            "traffic": measured_traffic("chunk_bwd_from_states_t4096" if from_states
+                                        else "chunk_bwd_t4096", bsrc) if timed else None}
 
 
 def bench_fused(steps, warmup, seed=8):
@@ -556,7 +557,8 @@ def cpu_baseline_decode(wl, pairs=1024):
 def profile_driver():
     """Short fixed sequence for hardware-counter runs: 5 chunk forwards (bf16, B=1 T=4096
     H=16 d=128, chunk 64), 2 at chunk 128, 2 fp32 forwards of that shape, 3 chunked
-    backwards, 20 decode steps with an fp32 state and 20 with a bf16 state, and 3 copies of
+    backwards, one forward that writes the chunk states and 3 backwards from them
+    (gdn2_chunk_bwd_states), 20 decode steps with an fp32 state and 20 with a bf16 state, and 3 copies of
     256 MiB (the copy calibrates the FETCH_SIZE / WRITE_SIZE counters)."""
     wl = inputs.CHUNK_BF16_T4096
     x = inputs.chunk_inputs(wl, seed=1002)
@@ -577,8 +579,15 @@ def profile_driver():
     for _ in range(3):
         g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO, S0=d["S0"],
                     dS_T=torch.ones_like(d["S0"]))
+    ck = torch.empty(g.num_chunks(wl.seqlen, 1), wl.h_v, wl.d_k, wl.d_v, dtype=torch.float32,
+                     device="cuda")
+    g.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], S0=d["S0"],
+                chunk_states=ck)
+    for _ in range(3):
+        g.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], dO, S0=d["S0"],
+                    dS_T=torch.ones_like(d["S0"]), chunk_states=ck)
     torch.cuda.synchronize()
-    del dO
+    del dO, ck
     torch.cuda.empty_cache()
     dw = inputs.DECODE_F32
     y = inputs.decode_inputs(dw, seed=3, steps=1)
@@ -646,7 +655,10 @@ def pmc_summary(fetch_dir, write_dir):
     Each counter is scaled by what it reads for the 256 MiB copy of the driver. Launches of
     one kernel are kept in dispatch order, so the chunk-forward kernels of the 5 plain
     forwards (the first 5 launches) are told apart from the forward re-run inside the 3
-    backwards (the next 3). Prints the per-launch rows of the traffic table."""
+    backwards (the next 3); the forward that writes the chunk states (launch 9) is left out,
+    and the 3 backwards from those states follow it (their prep launches 10-12, their
+    given-states state pass and backward kernels as their own launches). Prints the
+    per-launch rows of the traffic table."""
     import csv
     import glob
     from collections import defaultdict
@@ -676,7 +688,7 @@ def pmc_summary(fetch_dir, write_dir):
         return float(np.mean(fv)) * ff * 1024, float(np.mean(wv)) * wf * 1024 if wv else 0.0
 
     groups = {"chunk_fwd_t4096": [], "chunk_fwd_t4096_c128": [], "chunk_fwd_f32_t4096": [],
-              "chunk_bwd_t4096": []}
+              "chunk_bwd_t4096": [], "chunk_bwd_from_states_t4096": []}
     dec = {}
     for k in F:
         if "gdn2" not in k:
@@ -685,12 +697,17 @@ def pmc_summary(fetch_dir, write_dir):
         base = name.split("<")[0]
         targs = name[name.index("<") + 1:name.rindex(">")].split(", ") if "<" in name else []
         c64_bf16 = base == "prep_kernel" and targs[2] == "64" and "bf16" in targs[0]
-        if base in ("chunk_seg_kernel", "chunk_state_kernel") or c64_bf16:
+        if base == "chunk_state_kernel" and targs[-1] == "true":      # given states
+            parts = [("chunk_bwd_from_states_t4096", 0, 3)]
+        elif c64_bf16:
+            parts = [("chunk_fwd_t4096", 0, 5), ("chunk_bwd_t4096", 5, 8),
+                     ("chunk_bwd_from_states_t4096", 9, 12)]
+        elif base in ("chunk_seg_kernel", "chunk_state_kernel"):
             parts = [("chunk_fwd_t4096", 0, 5), ("chunk_bwd_t4096", 5, 8)]
         elif base in ("prep_kernel", "panel_seg_kernel", "panel_state_kernel"):
             parts = [("chunk_fwd_f32_t4096" if "float" in targs[0] else "chunk_fwd_t4096_c128", 0, 2)]
         elif base.startswith("bwd_"):
-            parts = [("chunk_bwd_t4096", 0, 3)]
+            parts = [("chunk_bwd_t4096", 0, 3), ("chunk_bwd_from_states_t4096", 3, 6)]
         elif base == "recurrent_fwd_kernel":
             key = ("decode_step_bf16state_n64_hv48" if "float, bf16_t" in name
                    else "decode_step_n64_hv48")
@@ -713,7 +730,8 @@ def pmc_summary(fetch_dir, write_dir):
                        "gdn2_common.h")
     bsrc = source_hash(*BWD_SRC)
     for gname, items in groups.items():
-        src = {"chunk_fwd_t4096": csrc, "chunk_bwd_t4096": bsrc}.get(gname, gsrc)
+        src = {"chunk_fwd_t4096": csrc, "chunk_bwd_t4096": bsrc,
+               "chunk_bwd_from_states_t4096": bsrc}.get(gname, gsrc)
         out[gname] = {"source_hash": src, "bytes_per_launch": int(sum(sum(rw) for _, rw in items)),
                       "kernels": {n: int(sum(rw)) for n, rw in items}}
     dsrc = source_hash("gdn2_decode.hip", "gdn2_common.h")
