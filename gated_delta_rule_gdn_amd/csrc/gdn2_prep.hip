@@ -103,6 +103,7 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
     __shared__ float s_tot[NS * DK];           // sum of the log2 decay over each sub-chunk
     __shared__ float s_cmid[NS * DK];          // in-sub-chunk cumsum at its middle token
     __shared__ float s_fkg[NS * DK];           // 2^(g_C - g_mid_R)
+    __shared__ float s_fmid[NS * DK];          // 2^(g_mid_R)
     __shared__ float s_foff[(NOFF > 0 ? NOFF : 1) * DK];   // 2^(g_mid_R - g_mid_I), R > I
     __shared__ __attribute__((aligned(16))) T s_tile[NBUF * 3 * TILE];
     __shared__ __attribute__((aligned(16))) float s_A[NPAIR * BS];
@@ -269,7 +270,10 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
         }
         st_rec<NTR>(&reinterpret_cast<float *>(rec + R_::gC)[c], exp2_hw(run));
 #pragma unroll
-        for (int R = 0; R < NS; ++R) s_fkg[R * DK + c] = exp2_hw(run - gmid[R]);
+        for (int R = 0; R < NS; ++R) {
+            s_fkg[R * DK + c] = exp2_hw(run - gmid[R]);
+            s_fmid[R * DK + c] = exp2_hw(gmid[R]);
+        }
 #pragma unroll
         for (int R = 1; R < NS; ++R)
 #pragma unroll
@@ -290,16 +294,14 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
                 for (int q = 0; q < 4; ++q) cs[r][m][e + q] -= cm[q];
             }
         }
-    // 2^(g at the middle token of sub-chunk R) for channels c0 .. c0 + VEC - 1 (the same sums
-    // in the same order as the per-channel factors above)
+    lds_barrier();                             // the per-channel factors are written
+    // 2^(g at the middle token of sub-chunk R) for channels c0 .. c0 + VEC - 1
     auto fmid_of = [&](int R, int c0, float *out) {
 #pragma unroll
         for (int e = 0; e < VEC; e += 4) {
-            f32x4 run = {0.f, 0.f, 0.f, 0.f};
-            for (int R2 = 0; R2 < R; ++R2) run += *reinterpret_cast<const f32x4 *>(&s_tot[R2 * DK + c0 + e]);
-            const f32x4 cm = *reinterpret_cast<const f32x4 *>(&s_cmid[R * DK + c0 + e]);
+            const f32x4 f = *reinterpret_cast<const f32x4 *>(&s_fmid[R * DK + c0 + e]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) out[e + q] = exp2_hw(run[q] + cm[q]);
+            for (int q = 0; q < 4; ++q) out[e + q] = f[q];
         }
     };
 
@@ -328,10 +330,15 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
             unpack16<BF>(rk[slot][m], kk);
             unpack16<BF>(rq[slot][m], qq);
             unpack16<BF>(rb[slot][m], bb);
+            if (p.qkn) {                       // uniform
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    kk[e] *= fk[m];
+                    qq[e] *= fq[m];
+                }
+            }
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                kk[e] *= fk[m];
-                qq[e] *= fq[m];
                 if constexpr (fg2) {           // k <- sqrt(beta) k, b <- 1
                     kk[e] *= sqrt_hw(bb[e]);
                     bb[e] = 1.f;
