@@ -15,6 +15,18 @@
  *   - gdn2_recurrent_step  one fused token-by-token step ("FusedRecurrent" mode, decode),
  *                          which reads and writes a persistent state in place as the
  *                          GDN decode verify page (LocalAI mirror), section 2, describes.
+ * Around them (each declared below with its own description):
+ *   - gdn2_recurrent_fwd        several tokens per call against a pool of fp32 or bf16
+ *                               states, with optional fused prologue and epilogue;
+ *   - gdn2_chunk_bwd, gdn2_chunk_bwd_states
+ *                               the gradients of the chunked forward (recomputing the
+ *                               chunk states, or from those a training forward saved);
+ *   - gdn2_map_gates, gdn2_map_gates_bwd
+ *                               the inputs of other delta-rule variants (KDA, GDN,
+ *                               FG2-GDN, FG2-GDN+) mapped onto these, and their gradients
+ *                               mapped back;
+ *   - gdn2_chunk_fwd_noalloc    the chunked forward on a static device workspace, for
+ *                               callers that cannot allocate.
  *
  * Conventions (the pages are silent on these; this is the reading the library implements):
  *   - o_t reads the state AFTER the update of token t.
