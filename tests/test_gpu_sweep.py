@@ -7,6 +7,8 @@ segments) or a packed one (1-4 sequences of 1-200 tokens), the number of key hea
 value heads per key head (1-3), an initial state or none, and a negative-eigenvalue erase
 gate or not. The draws are fixed by their seeds, so every run checks the same cases.
 """
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -93,3 +95,50 @@ def test_backward_sweep(seed):
           " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
     assert all(np.isfinite(list(errs.values())))
     assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_recurrent_sweep(seed):
+    """gdn2_recurrent_fwd on drawn configurations: dtype, stored-state dtype, head-dim pair,
+    1-24 tokens per call, 1-5 sequences on a pool of up to twice as many slots (a random
+    slot per sequence, sometimes a padding entry), 1-2 key heads with 1-3 value heads each,
+    against the oracle's state cache; slots no sequence names must come back unchanged."""
+    rng = np.random.default_rng(5000 + seed)
+    dtype = (torch.bfloat16, torch.float32)[int(rng.integers(2))]
+    sdt = (torch.bfloat16, torch.float32)[int(rng.integers(2))]
+    dk, dv = DIMS[int(rng.integers(len(DIMS)))]
+    T, N = int(rng.integers(1, 25)), int(rng.integers(1, 6))
+    hk, G = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    slots = N + int(rng.integers(0, N + 1))
+    idx = [int(s) for s in rng.permutation(slots)[:N]]
+    if N > 1 and rng.random() < 0.5:
+        idx[int(rng.integers(N))] = -1                   # a padding entry
+    label = (f"{'bf16' if dtype == torch.bfloat16 else 'fp32'} inputs, "
+             f"{'bf16' if sdt == torch.bfloat16 else 'fp32'} state, {dk}x{dv} T={T} N={N} "
+             f"slots={slots} idx={idx} h_k={hk} G={G}")
+    print(f"[case] sweep recurrent seed={seed}: {label}", flush=True)
+    wl = inputs.DecodeWorkload("recurrent_sweep", dtype, N, hk, hk * G, dk, dv, steps=T)
+    x = inputs.decode_inputs(wl, seed=6000 + seed)
+    y = {n: x[n].transpose(0, 1).contiguous() for n in ("q", "k", "v", "log_alpha", "b", "w")}
+    pool = inputs.decode_inputs(replace(wl, num_seqs=slots), seed=7000 + seed, steps=1)["S"]
+    pool = pool.to(sdt)
+    d = {n: t.cuda() for n, t in y.items()}
+    P = pool.cuda()
+    o = g.recurrent_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["b"], d["w"], P,
+                        state_idx=torch.tensor(idx, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    o_r, P_r = oracle.recurrent_cache(*(np64(y[n]) for n in ("q", "k", "v", "log_alpha", "b", "w")),
+                                      np64(pool), idx, bf16_state=sdt == torch.bfloat16,
+                                      threads=ORACLE_THREADS)
+    live = [n for n in range(N) if idx[n] >= 0]
+    for n in range(N):
+        if idx[n] < 0:
+            assert torch.all(o[n] == 0)
+    for s in set(range(slots)) - {idx[n] for n in live}:
+        assert torch.equal(P[s].cpu(), pool[s])
+    o_g = np64(o)
+    eo = oracle.rel_l2(o_g[live], o_r[live])
+    es = oracle.rel_l2(np64(P)[[idx[n] for n in live]], P_r[[idx[n] for n in live]])
+    bar = 1e-4 if dtype == torch.float32 and sdt == torch.float32 else 2e-2
+    print(f"[parity] sweep recurrent {seed}: {label}: o={eo:.2e} S={es:.2e} tol={bar:g}", flush=True)
+    assert eo <= bar and es <= bar
