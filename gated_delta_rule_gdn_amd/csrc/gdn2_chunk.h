@@ -89,6 +89,9 @@ struct ChunkParams {
     int qkn;             // nonzero: q and k rows are L2-normalised in K1
     float l2eps;
     int gmode;           // GateMode: how b (and w, log_alpha) carry the gates
+    int xgroup;          // prep kernel: the value heads per key head when block b maps to the
+                         // record that puts a key head's G value heads on one XCD back to
+                         // back (items a multiple of 8 G), else 0 (record b)
 };
 
 // Locates chunk `chunk` of the batch: sequence n, its chunk index j, and token range.

@@ -119,7 +119,14 @@ __global__ __launch_bounds__(64 * NWV) void prep_kernel(ChunkParams p) {
     const int li = lane & 15, lg = lane >> 4;   // matrix-core lane roles (= t, gi below)
     const int t = li, gi = lg;                  // elementwise roles: token in sub-chunk, group
 
-    const int item = blockIdx.x;
+    // Records in (chunk, value head) order. With grouped heads (xgroup = G), blocks of one
+    // XCD (b mod 8) take the G records of a (chunk, key head) one after another, so that
+    // their q and k rows are fetched into that XCD's L2 once (a bijection on the records).
+    int item = blockIdx.x;
+    if (p.xgroup > 1) {
+        const int xr = item >> 3;
+        item = ((xr / p.xgroup) * 8 + (item & 7)) * p.xgroup + xr % p.xgroup;
+    }
     const int chunk = item / p.h_v, h = item - chunk * p.h_v, hk = h / p.group;
     int n, jc;
     int64_t start, end;
@@ -648,21 +655,23 @@ constexpr size_t kStreamRecordBytes = static_cast<size_t>(256) << 20;
 template <typename T, bool BF, int C, int DK, int DV>
 hipError_t launch_prep_t(const ChunkParams &p, int64_t items, hipStream_t st) {
     if (items <= 0) return hipSuccess;
+    ChunkParams q = p;
+    q.xgroup = p.group > 1 && items % (8 * p.group) == 0 ? p.group : 0;
     using PS = PrepShape<BF, C, DK, DV>;
     constexpr int W = PS::NWV, R = PS::CPR;
     const dim3 g(static_cast<unsigned>(items)), b(64 * W);
     const bool ntr = static_cast<size_t>(items) * Rec<C, DK, DV, BF>::bytes > kStreamRecordBytes;
     switch (p.gmode) {
-    case GATES_KDA: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_KDA, W, R, false>), g, b, 0, st, p); break;
-    case GATES_GDN: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN, W, R, false>), g, b, 0, st, p); break;
-    case GATES_FG2_PLUS: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2_PLUS, W, R, false>), g, b, 0, st, p); break;
+    case GATES_KDA: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_KDA, W, R, false>), g, b, 0, st, q); break;
+    case GATES_GDN: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN, W, R, false>), g, b, 0, st, q); break;
+    case GATES_FG2_PLUS: hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2_PLUS, W, R, false>), g, b, 0, st, q); break;
     case GATES_FG2:
-        if constexpr (DK == DV) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2, W, R, false>), g, b, 0, st, p);
+        if constexpr (DK == DV) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_FG2, W, R, false>), g, b, 0, st, q);
         else return hipErrorInvalidValue;
         break;
     default:
-        if (ntr) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2, W, R, true>), g, b, 0, st, p);
-        else hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2, W, R, false>), g, b, 0, st, p);
+        if (ntr) hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2, W, R, true>), g, b, 0, st, q);
+        else hipLaunchKernelGGL((prep_kernel<T, BF, C, DK, DV, GATES_GDN2, W, R, false>), g, b, 0, st, q);
     }
     return hipGetLastError();
 }
