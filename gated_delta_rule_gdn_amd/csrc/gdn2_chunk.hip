@@ -38,18 +38,38 @@
 
 namespace gdn2 {
 
-// K0: chunk offsets of a packed batch, map[n] = sum_{m<n} ceil(len_m / chunk).
-__global__ void chunk_map_kernel(const int32_t *__restrict__ cu, int32_t *__restrict__ map,
-                                 int num_seqs, int chunk) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
+// K0: chunk offsets of a packed batch, map[n] = sum_{m<n} ceil(len_m / chunk), and the
+// order in which the state pass takes the sequences: order[r] = the sequence of rank r by
+// decreasing chunk count (ties by index), so that the longest chains are dispatched first
+// and the short ones fill in behind them (up to kOrderSeqs sequences; more keep their own
+// order). One workgroup of kMapThreads threads.
+constexpr int kMapThreads = 256, kOrderSeqs = 256;
+__global__ __launch_bounds__(kMapThreads) void chunk_map_kernel(const int32_t *__restrict__ cu,
+                                                                int32_t *__restrict__ map,
+                                                                int32_t *__restrict__ order,
+                                                                int num_seqs, int chunk) {
+    __shared__ int s_nc[kOrderSeqs];
+    if (threadIdx.x == 0) {
         int acc = 0;
         map[0] = 0;
         for (int n = 0; n < num_seqs; ++n) {
             int len = cu[n + 1] - cu[n];
             len = len < 0 ? 0 : len;
-            acc += (len + chunk - 1) / chunk;
+            const int nc = (len + chunk - 1) / chunk;
+            if (n < kOrderSeqs) s_nc[n] = nc;
+            acc += nc;
             map[n + 1] = acc;
         }
+    }
+    __syncthreads();
+    for (int n = threadIdx.x; n < num_seqs; n += kMapThreads) {
+        int r = n;
+        if (num_seqs <= kOrderSeqs) {
+            const int c = s_nc[n];
+            r = 0;
+            for (int m = 0; m < num_seqs; ++m) r += s_nc[m] > c || (s_nc[m] == c && m < n);
+        }
+        order[r] = n;
     }
 }
 
@@ -217,7 +237,10 @@ __global__ __launch_bounds__(64 * StateWaves<NW>::ALL) void chunk_state_kernel(C
     const int slice = rest % p.nslices;
     const int unit = (rest / p.nslices) * 8 + xcd;
     if (unit >= p.num_pairs * p.nseg) return;
-    const int pair = unit / p.nseg, seg = unit - pair * p.nseg;
+    const int upair = unit / p.nseg, seg = unit - upair * p.nseg;
+    // packed batches take the sequences longest first (the chunk-map kernel's order), so
+    // that the short chains fill in behind the long ones
+    const int pair = p.order ? p.order[upair / p.h_v] * p.h_v + upair % p.h_v : upair;
     const int n = pair / p.h_v, h = pair - n * p.h_v;
 
     int64_t start, end;
@@ -823,8 +846,14 @@ int64_t chunk_upper_bound(int chunk, int batch, int seqlen, int num_seqs, bool p
     return packed ? per + num_seqs : per * batch;
 }
 
+// chunk map [num_seqs + 1] and the state pass's sequence order [num_seqs] (chunk_map_kernel)
 size_t chunk_map_bytes(int num_seqs, bool packed) {
-    return packed ? (static_cast<size_t>(num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
+    return packed ? (static_cast<size_t>(num_seqs + 1) * 4 + 255) / 256 * 256 +
+                        (static_cast<size_t>(num_seqs) * 4 + 255) / 256 * 256
+                  : 0;
+}
+static size_t chunk_order_offset(int num_seqs) {
+    return (static_cast<size_t>(num_seqs + 1) * 4 + 255) / 256 * 256;
 }
 
 // Segmentation of the state pass: dense batches only, aiming at about kSegTargetWGs
@@ -941,6 +970,7 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
     if (a.fu.ck_in && !p.S_in) return hipErrorInvalidValue;   // given states: backward only
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
+    p.order = packed ? reinterpret_cast<const int32_t *>(a.workspace + chunk_order_offset(N)) : nullptr;
     p.rec = a.workspace + mapb;
     p.seqlen = a.seqlen; p.num_seqs = N; p.h_k = a.h_k; p.h_v = a.h_v;
     p.group = a.h_v / a.h_k;
@@ -962,8 +992,9 @@ static hipError_t launch_chunk_t(const ChunkArgs &a, hipStream_t st) {
         p.seg_R = reinterpret_cast<float *>(seg_base + off[2]);
     }
     if (packed) {
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(64), 0, st, a.cu_seqlens,
-                           reinterpret_cast<int32_t *>(a.workspace), N, kChunk);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, st, a.cu_seqlens,
+                           reinterpret_cast<int32_t *>(a.workspace),
+                           reinterpret_cast<int32_t *>(a.workspace + chunk_order_offset(N)), N, kChunk);
     }
     if (nrec > 0) {
         const hipError_t e = launch_prep(p, kChunk, DK, DV, BF, nrec * a.h_v, st);
@@ -1052,8 +1083,9 @@ static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
         p.seg_R = reinterpret_cast<float *>(seg_base + off[2]);
     }
     if (packed)
-        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(64), 0, st, a.cu_seqlens,
-                           reinterpret_cast<int32_t *>(a.workspace), N, C);
+        hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(kMapThreads), 0, st, a.cu_seqlens,
+                           reinterpret_cast<int32_t *>(a.workspace),
+                           reinterpret_cast<int32_t *>(a.workspace + chunk_order_offset(N)), N, C);
     hipError_t e = launch_prep(p, C, a.d_k, a.d_v, a.bf16, nrec * a.h_v, st);
     if (e != hipSuccess) return e;
     e = launch_panel_seg(p, C, a.d_k, a.d_v, a.bf16, st);

@@ -170,10 +170,11 @@ def test_workspace_size_formula(L):
     d = Dims(2, 100, 0, 2, 4, 128, 128, 1)
     rec = (2 * (3 * 64 * 128 + 64 * 64 + 64 * 128) + 4 * 128 + 255) // 256 * 256
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 2 * 2 * 4 * rec
-    # packed: ceil(T/64) + N chunks plus the chunk map
+    # packed: ceil(T/64) + N chunks, plus the chunk map [N + 1] and the state pass's
+    # sequence order [N] (int32 each, 256-byte aligned)
     d = Dims(1, 1000, 5, 1, 2, 64, 64, 0)
     rec = (4 * (3 * 64 * 64 + 64 * 64 + 64 * 64) + 4 * 64 + 255) // 256 * 256
-    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 256 + (16 + 5) * 2 * rec
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 64) == 512 + (16 + 5) * 2 * rec
     # a dense batch with few (sequence, head) pairs: the state pass is split into segments
     # (about 256 workgroups of two 16-column slices, at least 4 chunks per segment) and the
     # workspace adds fp32 states entering segments 0 and 1 [pair][2][dk][dv], transitions
@@ -216,7 +217,7 @@ def test_workspace_size_formula(L):
     d = Dims(8, 4096, 0, 8, 8, 128, 128, 1)         # 64 pairs at chunk 128: no segments
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 8 * 32 * 8 * rec_c(128, 2, 128, 128)
     d = Dims(1, 1000, 5, 1, 2, 128, 64, 0)          # packed, fp32, 128-token chunks
-    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 256 + (8 + 5) * 2 * rec_c(128, 4, 128, 64)
+    assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(d), 128) == 512 + (8 + 5) * 2 * rec_c(128, 4, 128, 64)
     assert L.gdn2_chunk_fwd_workspace_bytes(None, 64) == 0
     assert L.gdn2_chunk_fwd_workspace_bytes(ctypes.byref(Dims(1, 10, 0, 1, 1, 96, 64, 1)),
                                             64) == 0
