@@ -174,6 +174,29 @@ def test_packed_with_empty_and_short_sequences(dtype):
     assert np.array_equal(S_g[2], np64(x["S0"][2]))      # empty sequence: S_T = S0
 
 
+# Packed batches are taken longest first by the state pass (the chunk-map kernel ranks up to
+# 256 sequences by chunk count; more keep their own order): 200 sequences with many equal
+# chunk counts (ranked, ties by index) and 300 (not ranked), empty ones included.
+@pytest.mark.parametrize("num_seqs", [200, 300])
+def test_packed_many_sequences_state_order(num_seqs):
+    wl = inputs.small_chunk(dtype=torch.bfloat16, h_k=1, h_v=2, d_k=64, d_v=64,
+                            num_seqs=num_seqs, len_lo=1, len_hi=200)
+    x = inputs.chunk_inputs(wl, seed=30 + num_seqs)
+    cu = x["cu_seqlens"].clone()
+    lens = (cu[1:] - cu[:-1]).tolist()
+    for n in range(0, num_seqs, 37):
+        lens[n] = 0                               # empty sequences among them
+    cu[1:] = torch.cumsum(torch.tensor(lens), 0).to(torch.int32)
+    T = int(cu[-1])
+    for n in ("q", "k", "v", "log_alpha", "b", "w"):
+        x[n] = x[n][:, :T].contiguous()
+    x["cu_seqlens"] = cu
+    assert_chunk_parity(x, torch.bfloat16, label=f"packed {num_seqs} sequences", worst=True)
+    _, S_g = gpu_chunk(x)
+    for n in range(0, num_seqs, 37):
+        assert np.array_equal(S_g[n], np64(x["S0"][n]))   # empty sequence: S_T = S0
+
+
 def test_chunk_extreme_decay_stress():
     wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=300, h_k=2, h_v=2, d_k=128,
                             d_v=128, neg_eig=True)
