@@ -197,6 +197,18 @@ def test_packed_many_sequences_state_order(num_seqs):
         assert np.array_equal(S_g[n], np64(x["S0"][n]))   # empty sequence: S_T = S0
 
 
+# With grouped heads the prep kernel maps blocks to records so that the G value heads of a
+# key head run back to back on one XCD, when the record count is a multiple of 8 G: shapes
+# chosen so that it is (G = 2, 3, 4), against the oracle on every pair.
+@pytest.mark.parametrize("G,T", [(2, 256), (3, 512), (4, 128)])
+def test_grouped_heads_record_mapping(G, T):
+    wl = inputs.small_chunk(dtype=torch.bfloat16, batch=2, seqlen=T, h_k=2, h_v=2 * G, d_k=128,
+                            d_v=128, neg_eig=True)
+    assert (2 * ((T + 63) // 64) * 2 * G) % (8 * G) == 0
+    x = inputs.chunk_inputs(wl, seed=40 + G)
+    assert_chunk_parity(x, torch.bfloat16, label=f"grouped heads G={G} T={T}", worst=True)
+
+
 def test_chunk_extreme_decay_stress():
     wl = inputs.small_chunk(dtype=torch.bfloat16, batch=1, seqlen=300, h_k=2, h_v=2, d_k=128,
                             d_v=128, neg_eig=True)
