@@ -65,7 +65,7 @@ struct ChunkParams {
     const float *S0;
     const int32_t *cu;
     const int32_t *map;
-    const int32_t *order;  // packed batches, 64-token state pass: sequence of each rank (longest
+    const int32_t *order;  // packed batches, state passes: sequence of each rank (longest
                            // first, chunk_map_kernel), or NULL
     void *o;
     float *S_T;

@@ -1062,6 +1062,7 @@ static hipError_t launch_chunk_generic(const ChunkArgs &a, hipStream_t st) {
     p.S0 = a.S0; p.cu = a.cu_seqlens; p.o = a.o; p.S_T = a.S_T; p.S_ck = a.fu.cks; p.tmat = a.fu.tmat;
     const size_t mapb = chunk_map_bytes(a.num_seqs, packed);
     p.map = packed ? reinterpret_cast<const int32_t *>(a.workspace) : nullptr;
+    p.order = packed ? reinterpret_cast<const int32_t *>(a.workspace + chunk_order_offset(N)) : nullptr;
     p.rec = a.workspace + mapb;
     p.seqlen = a.seqlen; p.num_seqs = N; p.h_k = a.h_k; p.h_v = a.h_v;
     p.group = a.h_v / a.h_k;

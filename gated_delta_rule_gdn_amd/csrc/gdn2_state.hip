@@ -79,7 +79,9 @@ __global__ __launch_bounds__(64 * (2 * NW + 4)) void panel_state_kernel(ChunkPar
     const int slice = rest % p.nslices;
     const int unit = (rest / p.nslices) * 8 + xcd;
     if (unit >= p.num_pairs * p.nseg) return;
-    const int pair = unit / p.nseg, seg = unit - pair * p.nseg;
+    const int upair = unit / p.nseg, seg = unit - upair * p.nseg;
+    // packed batches take the sequences longest first (the chunk-map kernel's order)
+    const int pair = p.order ? p.order[upair / p.h_v] * p.h_v + upair % p.h_v : upair;
     const int n = pair / p.h_v, h = pair - n * p.h_v;
     int64_t start, end;
     int cbase;

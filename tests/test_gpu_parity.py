@@ -174,11 +174,13 @@ def test_packed_with_empty_and_short_sequences(dtype):
     assert np.array_equal(S_g[2], np64(x["S0"][2]))      # empty sequence: S_T = S0
 
 
-# Packed batches are taken longest first by the state pass (the chunk-map kernel ranks up to
-# 256 sequences by chunk count; more keep their own order): 200 sequences with many equal
-# chunk counts (ranked, ties by index) and 300 (not ranked), empty ones included.
+# Packed batches are taken longest first by the state passes (the chunk-map kernel ranks up
+# to 256 sequences by chunk count; more keep their own order): 200 sequences with many equal
+# chunk counts (ranked, ties by index) and 300 (not ranked), empty ones included, at every
+# chunk size (64: the 64-token state pass; 32 and 128: the panel state pass).
 @pytest.mark.parametrize("num_seqs", [200, 300])
-def test_packed_many_sequences_state_order(num_seqs):
+@pytest.mark.parametrize("C", [32, 64, 128])
+def test_packed_many_sequences_state_order(num_seqs, C):
     wl = inputs.small_chunk(dtype=torch.bfloat16, h_k=1, h_v=2, d_k=64, d_v=64,
                             num_seqs=num_seqs, len_lo=1, len_hi=200)
     x = inputs.chunk_inputs(wl, seed=30 + num_seqs)
@@ -191,8 +193,9 @@ def test_packed_many_sequences_state_order(num_seqs):
     for n in ("q", "k", "v", "log_alpha", "b", "w"):
         x[n] = x[n][:, :T].contiguous()
     x["cu_seqlens"] = cu
-    assert_chunk_parity(x, torch.bfloat16, label=f"packed {num_seqs} sequences", worst=True)
-    _, S_g = gpu_chunk(x)
+    assert_chunk_parity(x, torch.bfloat16, label=f"packed {num_seqs} sequences C={C}",
+                        worst=True, chunk_size=C)
+    _, S_g = gpu_chunk(x, chunk_size=C)
     for n in range(0, num_seqs, 37):
         assert np.array_equal(S_g[n], np64(x["S0"][n]))   # empty sequence: S_T = S0
 
