@@ -57,7 +57,7 @@ def draw(seed, long_ok=True):
     return wl, C, label
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(64))
 def test_forward_sweep(seed):
     wl, C, label = draw(seed)
     print(f"[case] sweep forward seed={seed}: {label}", flush=True)
@@ -65,7 +65,7 @@ def test_forward_sweep(seed):
     assert_chunk_parity(x, wl.dtype, label=f"sweep {seed}: {label}", worst=True, chunk_size=C)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(32))
 def test_backward_sweep(seed):
     """Every gradient of a drawn configuration against the oracle's token adjoint (dense
     draws stay at most 300 tokens long)."""
